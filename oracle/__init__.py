@@ -1,0 +1,177 @@
+"""ctypes wrapper around the C oracle (``sage_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY.  The oracle is the slow CPU reference that the GPU path is
+checked against; only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` import it.  The product package never does.
+
+Arrays cross the boundary as numpy arrays; 16-bit inputs are passed as their raw bit
+patterns (``uint16``) with a flag that says whether they are fp16 or bf16.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "sage_oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+BQ, BK = 128, 64
+
+SMOOTH_V = 0x0001
+NO_SMOOTH_K = 0x0002
+NO_SMOOTH_Q = 0x0004
+QK_IDENTITY = 0x0010
+QK_PER_BLOCK = 0x0020
+QK_PER_TOKEN = 0x0040
+QK_PER_TENSOR = 0x0080
+PV_IDENTITY = 0x0100
+PV_E5M2 = 0x0200
+PV_INT8 = 0x0400
+MXFP4 = 0x1000
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (plain C11, no fast-math, no FP contraction)."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+               "-fno-fast-math", SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, LIB)
+    return LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build(force=True)
+        L = ctypes.CDLL(LIB)
+        P = ctypes.c_void_p
+        i, u, dbl = ctypes.c_int, ctypes.c_uint, ctypes.c_double
+        L.orc_preprocess_head.argtypes = [P, P, P, i, i, i, i, u] + [P] * 10
+        L.orc_preprocess_head.restype = i
+        L.orc_forward_head.argtypes = [P, P, P, i, i, i, i, i, dbl, u, P, i, P]
+        L.orc_forward_head.restype = i
+        L.orc_exact_head.argtypes = [P, P, P, i, i, i, i, i, dbl, P, i, P]
+        L.orc_exact_head.restype = i
+        L.orc_exact_f64.argtypes = [P, P, P, i, i, i, i, dbl, P]
+        L.orc_exact_f64.restype = i
+        L.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+        L.orc_e4m3_decode.restype = dbl
+        L.orc_e4m3_encode.argtypes = [dbl]
+        L.orc_e4m3_encode.restype = ctypes.c_uint8
+        L.orc_e5m2_decode.argtypes = [ctypes.c_uint8]
+        L.orc_e5m2_decode.restype = dbl
+        L.orc_e5m2_encode.argtypes = [dbl]
+        L.orc_e5m2_encode.restype = ctypes.c_uint8
+        L.orc_e2m1_decode.argtypes = [ctypes.c_uint8]
+        L.orc_e2m1_decode.restype = dbl
+        L.orc_e2m1_encode.argtypes = [dbl]
+        L.orc_e2m1_encode.restype = ctypes.c_uint8
+        L.orc_e8m0_exponent.argtypes = [dbl]
+        L.orc_e8m0_exponent.restype = i
+        L.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.orc_bf16_to_f32.restype = ctypes.c_float
+        L.orc_fp16_to_f32.argtypes = [ctypes.c_uint16]
+        L.orc_fp16_to_f32.restype = ctypes.c_float
+        L.orc_k_group.argtypes = [i]
+        L.orc_k_group.restype = i
+        L.orc_num_threads.argtypes = []
+        L.orc_num_threads.restype = i
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def _u16(x):
+    x = np.ascontiguousarray(x)
+    assert x.dtype == np.uint16, x.dtype
+    return x
+
+
+def preprocess_head(q, k, v, fp16: bool, flags: int = 0) -> dict:
+    """Quantized tensors and scales of one head, in natural layouts (see sage_oracle.h)."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    N, d = q.shape
+    M = k.shape[0]
+    nqb, nkt = -(-N // BQ), -(-M // BK)
+    o = dict(kmean=np.zeros(d, np.float32), vmean=np.zeros(d, np.float32),
+             khat=np.zeros((M, d), np.int8), dk=np.zeros((nkt, 4), np.float32),
+             vhat=np.zeros((M, d), np.uint8), dv=np.zeros(d, np.float32),
+             qhat=np.zeros((N, d), np.int8), dq=np.zeros(N, np.float32),
+             qmean=np.zeros((nqb, d), np.float32), ds=np.zeros((nqb, M), np.float64))
+    rc = lib().orc_preprocess_head(_ptr(q), _ptr(k), _ptr(v), int(fp16), N, M, d, flags,
+                                   *[_ptr(o[n]) for n in ("kmean", "vmean", "khat", "dk", "vhat",
+                                                          "dv", "qhat", "dq", "qmean", "ds")])
+    if rc != 0:
+        raise ValueError("orc_preprocess_head rejected its arguments")
+    return o
+
+
+def forward_head(q, k, v, fp16: bool, causal: bool, sm_scale: float, flags: int = 0, rows=None):
+    """The quantized forward of one head in FP64: [len(rows) or N, d]."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    N, d = q.shape
+    M = k.shape[0]
+    if rows is None:
+        nrows, rp = N, None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int32)
+        nrows, rp = len(rows), rows
+    out = np.zeros((nrows, d), np.float64)
+    rc = lib().orc_forward_head(_ptr(q), _ptr(k), _ptr(v), int(fp16), N, M, d, int(causal),
+                                float(sm_scale), flags, _ptr(rp), nrows, _ptr(out))
+    if rc != 0:
+        raise ValueError("orc_forward_head rejected its arguments")
+    return out
+
+
+def exact_head(q, k, v, fp16: bool, causal: bool, sm_scale: float, rows=None):
+    """softmax(Q K^T * sm_scale) V in FP64 on the widened inputs."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    N, d = q.shape
+    M = k.shape[0]
+    if rows is None:
+        nrows, rp = N, None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int32)
+        nrows, rp = len(rows), rows
+    out = np.zeros((nrows, d), np.float64)
+    rc = lib().orc_exact_head(_ptr(q), _ptr(k), _ptr(v), int(fp16), N, M, d, int(causal),
+                              float(sm_scale), _ptr(rp), nrows, _ptr(out))
+    if rc != 0:
+        raise ValueError("orc_exact_head rejected its arguments")
+    return out
+
+
+def exact_f64(q, k, v, causal: bool, sm_scale: float):
+    q = np.ascontiguousarray(q, np.float64)
+    k = np.ascontiguousarray(k, np.float64)
+    v = np.ascontiguousarray(v, np.float64)
+    N, d = q.shape
+    M = k.shape[0]
+    out = np.zeros((N, v.shape[1]), np.float64)
+    assert v.shape[1] == d
+    rc = lib().orc_exact_f64(_ptr(q), _ptr(k), _ptr(v), N, M, d, int(causal), float(sm_scale), _ptr(out))
+    if rc != 0:
+        raise ValueError("orc_exact_f64 rejected its arguments")
+    return out
+
+
+def e4m3_decode_table() -> np.ndarray:
+    return np.array([lib().orc_e4m3_decode(c) for c in range(256)])
+
+
+def num_threads() -> int:
+    return lib().orc_num_threads()

@@ -1,0 +1,108 @@
+/*
+ * sage_oracle.h -- CPU oracle for the SageAttention2-style quantized attention forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This library is the plain, slow reference that the GPU
+ * path is checked against.  It is called from the test-suite, from the package's smoke
+ * check and from the benchmark's CPU-baseline leg -- never from the product path.  It
+ * shares no code with the HIP library.
+ *
+ * Sources (the pages this follows, cited by title and section):
+ *   [SA2]  "SageAttention2 Technical Report: Accurate 4 Bit Attention for Plug-and-play
+ *          Inference Acceleration" (structured summary of arXiv 2411.10958), section 3.4:
+ *          "Smoothing Q", "Per-Thread INT4 Quantization", "FP8 Quantization for P~V",
+ *          "Two-Level Accumulation", "Optional Smoothing of V", "The Complete Algorithm
+ *          (Algorithm 1)".
+ *   [SA2R] "SageAttention2: Efficient Attention with Thorough Outlier Smoothing and
+ *          Per-thread INT4 Quantization" (paper review blog), "core formulas" and the
+ *          forward-pass algorithm listing.
+ *   [SA3]  "SageAttention3 ..." summary (arXiv 2505.11594), section 3.4 "The NVFP4
+ *          Microscaling Format and Quantization Operator" (E2M1 value set, 1x32 E8M0
+ *          blocks for MXFP4).
+ *   [QA]   "Quantization for Attention, in depth" blog: "The datapath and its quantize
+ *          points", "Worked example: what smoothing buys at INT8", "Failure modes".
+ *
+ * Conventions: tensors of one (batch, head) are row-major [tokens][d]; inputs arrive as
+ * raw bf16 or fp16 bit patterns and are widened exactly to FP32.  Every quantity the
+ * method keeps in full precision is computed here in FP64; the preprocessing is FP32/FP64
+ * with a pinned evaluation order so that the quantized tensors and scales have exactly one
+ * correct value (see sage_oracle.c for each step and the reading it takes).
+ */
+#ifndef SAGE_ORACLE_H
+#define SAGE_ORACLE_H
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORC_BQ 128 /* Q smoothing block (FlashAttention query tile) */
+#define ORC_BK 64  /* KV tile: running-max step and two-level accumulation granularity */
+
+/* ---- option bits (default 0 = the method as the pages define it) ---- */
+#define ORC_SMOOTH_V      0x0001u /* V' = V - mean_t(V), O += V_m            [SA2 optional V smoothing] */
+#define ORC_NO_SMOOTH_K   0x0002u /* ablation: skip K - mean(K)                                          */
+#define ORC_NO_SMOOTH_Q   0x0004u /* ablation: skip per-block Q mean / Delta S                           */
+#define ORC_QK_IDENTITY   0x0010u /* no Q/K quantization, smoothing done in FP64                         */
+#define ORC_QK_PER_BLOCK  0x0020u /* ablation: one scale per Q block (128) and per K tile (64)           */
+#define ORC_QK_PER_TOKEN  0x0040u /* ablation: one scale per Q token and per K token                     */
+#define ORC_QK_PER_TENSOR 0x0080u /* ablation: one scale for all of Q (per head), one for all of K       */
+#define ORC_PV_IDENTITY   0x0100u /* no P/V quantization (448*P~ and V'/dV kept exact)                   */
+#define ORC_PV_E5M2       0x0200u /* ablation: P~ and V in E5M2 (static scale 1/57344, per-channel V)    */
+#define ORC_PV_INT8       0x0400u /* ablation: naive INT8 P~ (static 1/127) and per-channel INT8 V       */
+#define ORC_MXFP4         0x1000u /* MX variant: E2M1 values, E8M0 scale per 32 along the reduction dim  */
+
+/* ---- scalar formats ---- */
+float   orc_bf16_to_f32(uint16_t h);
+float   orc_fp16_to_f32(uint16_t h);
+double  orc_e4m3_decode(uint8_t code);  /* OCP E4M3FN: bias 7, max 448, no Inf, S.1111.111 = NaN */
+uint8_t orc_e4m3_encode(double x);      /* round-to-nearest-even, saturate to +-448, NaN -> 0x7F */
+double  orc_e5m2_decode(uint8_t code);  /* OCP E5M2: bias 15, max 57344                           */
+uint8_t orc_e5m2_encode(double x);      /* RNE, saturate to +-57344                               */
+double  orc_e2m1_decode(uint8_t code);  /* 4-bit E2M1: {0, .5, 1, 1.5, 2, 3, 4, 6} and negatives   */
+uint8_t orc_e2m1_encode(double x);      /* RNE (ties to even mantissa), saturate to +-6           */
+int     orc_e8m0_exponent(double amax); /* smallest e with amax <= 6*2^e, clamped to [-127,127]   */
+
+/* Quantization group of key t inside its 64-key tile (0..3), see sage_oracle.c step 3. */
+int orc_k_group(int t);
+
+/* ---- whole-head preprocessing (the quantities the GPU must reproduce bit for bit) ----
+ * q: [N][d], k, v: [M][d] raw 16-bit codes; in_fp16 selects fp16 (else bf16).
+ * Outputs (natural layouts, all caller-allocated):
+ *   kmean[d], vmean[d] (zeros unless ORC_SMOOTH_V), khat[M][d], dk[ceil(M/64)][4],
+ *   vhat[M][d] (E4M3 codes), dv[d], qhat[N][d], dq[N], qmean[ceil(N/128)][d],
+ *   ds[ceil(N/128)][M] (FP64 Delta S).
+ * Only the default quantizers (per-thread INT8 QK, E4M3 PV) are written by this call;
+ * flags may hold ORC_SMOOTH_V, ORC_NO_SMOOTH_K, ORC_NO_SMOOTH_Q and ORC_QK_PER_BLOCK (the
+ * per-block ablation; dk then repeats the tile scale).  Returns 0, or -1 on a
+ * bad argument. */
+int orc_preprocess_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, int in_fp16,
+                        int N, int M, int d, unsigned flags,
+                        float* kmean, float* vmean, int8_t* khat, float* dk,
+                        uint8_t* vhat, float* dv, int8_t* qhat, float* dq,
+                        float* qmean, double* ds);
+
+/* ---- forward of one head: the quantized method, FP64 everywhere it is not quantized ----
+ * rows: the query rows to produce (NULL with nrows = N means all rows in order);
+ * out: [nrows][d] in FP64.  causal requires N == M (mask key t > row r).
+ * Returns 0, or -1 on a bad argument. */
+int orc_forward_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, int in_fp16,
+                     int N, int M, int d, int causal, double sm_scale, unsigned flags,
+                     const int* rows, int nrows, double* out);
+
+/* ---- textbook attention softmax(Q K^T * sm_scale) V in FP64 on the widened inputs ---- */
+int orc_exact_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, int in_fp16,
+                   int N, int M, int d, int causal, double sm_scale,
+                   const int* rows, int nrows, double* out);
+
+/* Same, on FP64 inputs (used by the pins that build exactly representable cases). */
+int orc_exact_f64(const double* q, const double* k, const double* v, int N, int M, int d,
+                  int causal, double sm_scale, double* out);
+
+/* Number of threads the OpenMP loops use (1 when built without OpenMP). */
+int orc_num_threads(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
