@@ -306,7 +306,8 @@ static int setup_k(head_t* h) {
       float s = int8_scale(am);
       for (int t = u * ORC_BK; t < M && t < (u + 1) * ORC_BK; t++) h->dk_key[t] = s;
     }
-  } else { /* per-thread groups (default) */
+  } else { /* per-thread groups (default); a group with no valid key (ragged last tile)
+            * has amax 0 and so the floor scale 1e-8/127 */
     for (int u = 0; u < h->nkt; u++) {
       float am[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       for (int t = u * ORC_BK; t < M && t < (u + 1) * ORC_BK; t++) {
@@ -667,7 +668,12 @@ int orc_preprocess_head(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   if (vmean) memcpy(vmean, h.vmean, sizeof(float) * d);
   if (khat) memcpy(khat, h.khat, (size_t)M * d);
   if (dk) { /* the scale of each (tile, group); with ORC_QK_PER_BLOCK all four are equal */
-    for (int t = 0; t < M; t++) dk[(size_t)(t / ORC_BK) * 4 + orc_k_group(t)] = h.dk_key[t];
+    if (flags & ORC_QK_PER_BLOCK) {
+      for (int u = 0; u < h.nkt; u++)
+        for (int g = 0; g < 4; g++) dk[(size_t)u * 4 + g] = h.dk_key[(size_t)u * ORC_BK];
+    } else {
+      memcpy(dk, h.dk_grp, sizeof(float) * 4 * h.nkt);
+    }
   }
   if (vhat) memcpy(vhat, h.vhat, (size_t)M * d);
   if (dv) memcpy(dv, h.dv, sizeof(float) * d);

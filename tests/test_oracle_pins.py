@@ -272,3 +272,14 @@ def test_quantizer_invariants_and_means():
     rel = np.abs(dec[p["vhat"]] * p["dv"][None, :] - vp) / np.maximum(np.abs(vp), 1e-30)
     normal = np.abs(vp) / p["dv"][None, :] >= 2.0 ** -6
     assert rel[normal].max() <= 2.0 ** -4 * (1 + 1e-6)
+
+
+def test_empty_key_group_has_floor_scale():
+    """M = 600: the last tile holds 24 keys, all in its first 32-key half, so groups 2, 3
+    are empty and take amax 0 -> scale max(0, 1e-8) / 127."""
+    cfg = sy.CONFIGS["n4k"].with_shape(H=1, N=128, M=600)
+    q, k, v = [x[0, 0] for x in sy.make_qkv(cfg)]
+    p = oracle.preprocess_head(q, k, v, fp16=False)
+    floor = np.float32(1e-8) / np.float32(127.0)
+    assert p["dk"][-1, 2] == floor and p["dk"][-1, 3] == floor
+    assert p["dk"][-1, 0] > 1e-3 and p["dk"][-1, 1] > 1e-3
