@@ -1,0 +1,203 @@
+#!/usr/bin/env python3
+"""Benchmark of the quantized attention forward on one MI355X.
+
+One step = one whole forward pass (preprocessing: means, INT8/FP8 quantization, Delta S;
+then the fused attention kernel) over one batch of seeded synthetic input already
+resident in HBM, through the C ABI (sage_attn_fwd_ws with a preallocated workspace).
+
+Metric: attention TOPS = 4 N^2 d H B / time, causal counted as half (the pages'
+convention: "Quantization for Attention, in depth", "When attention compute is worth
+quantizing"; "SageAttention2 Technical Report", kernel speed figures).  The default
+workload is the LLM-prefill shape B=1, H=32, N=M=32768, d=128, bf16, causal.
+
+Printed: ONE JSON line with the metric, a roofline object for the dominant kernel (the
+fused attention kernel, timed with HIP events recorded on its stream around every launch
+in the timed region) and a cpu_baseline object (the CPU oracle on a bounded sample of the
+same workload, rank 0, N=1 only).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TOPS = 5000.0  # MI355X dense INT8 / OCP-FP8 MFMA peak, 5.0 POPS
+
+# Kernel-level HBM traffic measured with rocprofv3 counters (FETCH_SIZE, WRITE_SIZE per
+# dispatch of the fused attention kernel on this workload, scaled by a copy-kernel
+# calibration); None until measured for the current kernel.
+TRAFFIC_BYTES = {}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill32k",
+                    help="one of: n4k, prefill32k, video17k (default prefill32k)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class Hip:
+    """The few HIP runtime calls the timing needs (events), via ctypes."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.lib.hipEventCreate(ctypes.byref(e)) == 0
+        return e
+
+    def elapsed(self, a, b):
+        ms = ctypes.c_float()
+        assert self.lib.hipEventSynchronize(b) == 0
+        assert self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(e)
+
+
+def counted_ops(cfg) -> float:
+    ops = 4.0 * cfg.N * cfg.M * cfg.d * cfg.H * cfg.B
+    return ops / 2 if cfg.causal else ops
+
+
+def cpu_baseline(cfg, budget_s: float) -> dict:
+    """The oracle (as it stands) on head 0 of the workload: batches of seeded random query
+    rows until the time budget is spent; ops counted with the same convention per row
+    (4 d x keys the row attends to)."""
+    import oracle
+    from quantized_attention_amd import synthetic as sy
+    q, k, v = sy.make_qkv(cfg, heads=[0])
+    rng = np.random.default_rng(7)
+    s = 1.0 / math.sqrt(cfg.d)
+    flags = oracle.SMOOTH_V if cfg.smooth_v else 0
+    ops, t_used, nrows, batch = 0.0, 0.0, 0, 8
+    while t_used < budget_s:
+        rows = np.sort(rng.integers(0, cfg.N, batch))
+        t0 = time.perf_counter()
+        oracle.forward_head(q[0], k[0], v[0], cfg.fp16, cfg.causal, s, flags, rows=rows)
+        dt = time.perf_counter() - t0
+        t_used += dt
+        nrows += batch
+        ops += sum(4.0 * cfg.d * ((int(r) + 1) if cfg.causal else cfg.M) for r in rows)
+        if dt < budget_s / 8:
+            batch *= 2
+    return {"value": ops / t_used / 1e12, "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"head 0 of {cfg.B * cfg.H}, {nrows} seeded random query rows of N={cfg.N} "
+                      f"(per-head preprocessing and Delta S rows included), {t_used:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); heads are independent, "
+              "so a multi-GPU run would shard heads with no communication -- not measured here.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import quantized_attention_amd as qa
+    from quantized_attention_amd import synthetic as sy
+
+    cfg = sy.CONFIGS[args.workload]
+    qa.load_library()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {cfg.name} B={cfg.B} H={cfg.H} N={cfg.N} d={cfg.d}", file=sys.stderr, flush=True)
+    qb, kb, vb = sy.make_qkv(cfg)
+    dt = torch.float16 if cfg.fp16 else torch.bfloat16
+    q, k, v = (torch.from_numpy(x.view(np.int16)).view(dt).to(dev) for x in (qb, kb, vb))
+    del qb, kb, vb
+    out = torch.empty((cfg.B, cfg.H, cfg.N, cfg.d), dtype=dt, device=dev)
+    var = (qa.SAGE_IN_FP16 if cfg.fp16 else qa.SAGE_IN_BF16) | (qa.SAGE_SMOOTH_V if cfg.smooth_v else 0)
+    ws_bytes = qa.sage_attn_workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.M, cfg.d, cfg.causal, var)
+    ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
+    ws_ptr = (ws.data_ptr() + 255) // 256 * 256
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    scale = 1.0 / math.sqrt(cfg.d)
+    hip = Hip()
+
+    def step(evs=None):
+        if evs is not None:
+            qa.sage_attn_set_profile_events(evs[0], evs[1])
+        rc = qa.sage_attn_fwd_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), cfg.B, cfg.H,
+                                 cfg.N, cfg.M, cfg.d, cfg.causal, scale, var, ws_ptr, ws_bytes, stream)
+        if rc != qa.SAGE_OK:
+            raise qa.SageError(rc, "sage_attn_fwd_ws")
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    kev = [(hip.event(), hip.event()) for _ in range(args.steps)]
+    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        step(kev[i])
+    t_stop.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_stop)
+    kern_ms = [hip.elapsed(a, b) for a, b in kev]
+    for a, b in kev:
+        hip.destroy(a)
+        hip.destroy(b)
+    ms = total_ms / args.steps
+    kms = float(np.mean(kern_ms))
+    ops = counted_ops(cfg)
+    value = ops / (ms * 1e-3) / 1e12
+    achieved = ops / (kms * 1e-3) / 1e12
+    traffic = TRAFFIC_BYTES.get(cfg.name)
+    line = {
+        "metric": "attention TOPS (4*N^2*d*H*B/time, causal counted as half) at N=32k d=128, % of INT8/FP8 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8(QK)+fp8e4m3(PV), fp32 softmax/accumulate",
+        "data": "synthetic (seeded Gaussian + per-channel offsets)",
+        "config": {"workload": f"{cfg.name}: B={cfg.B} H={cfg.H} N=M={cfg.N} d={cfg.d} {cfg.dtype} "
+                               f"{'causal' if cfg.causal else 'non-causal'}"
+                               f"{' smooth_v' if cfg.smooth_v else ''}",
+                   "global_batch": cfg.B, "seq_len": cfg.N, "heads": cfg.H, "head_dim": cfg.d,
+                   "parallelism": "single GPU"},
+        "frac_of_peak": round(value / PEAK_TOPS, 4),
+        "attn_kernel_ms": round(kms, 4),
+        "preprocess_ms": round(ms - kms, 4),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TOPS, "unit": "TOPS",
+                     "frac": round(achieved / PEAK_TOPS, 4), "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] cpu baseline ({args.cpu_seconds:.0f} s budget)", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

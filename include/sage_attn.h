@@ -1,0 +1,140 @@
+/*
+ * sage_attn.h -- C ABI of the MI355X (gfx950) quantized attention forward.
+ *
+ * The operation is the SageAttention2 forward pass, INT8-QK / FP8-PV variant:
+ *   "SageAttention2 Technical Report: Accurate 4 Bit Attention for Plug-and-play Inference
+ *   Acceleration" (summary of arXiv 2411.10958), section 3.4, "The Complete Algorithm
+ *   (Algorithm 1)": K is smoothed by its token mean, each 128-query block of Q by its own
+ *   mean with the GEMV correction Delta S = q_i gamma(K)^T ("Smoothing Q"), smoothed Q and K
+ *   are quantized to INT8 with one scale per thread fragment ("Per-Thread INT4
+ *   Quantization", here per query token and per 16-key group), P~ = exp(S - m) is cast to
+ *   FP8 E4M3 with the static scale 1/448 and V per channel to E4M3 ("FP8 Quantization for
+ *   P~V"), the online softmax runs in FP32, and each 64-key tile's P^ V^ is accumulated
+ *   into an FP32 output buffer ("Two-Level Accumulation"); the epilogue is O / l / 448 * dV
+ *   (+ V_m with the optional V smoothing, "Optional Smoothing of V").  The drop-in API the
+ *   pages describe replaces scaled-dot-product attention: softmax(Q K^T * sm_scale) V
+ *   ("SageAttention Guide": API usage; "Quantization for Attention, in depth").
+ *
+ * Conventions for every entry point
+ *   - Q is [B][H][N][d], K and V are [B][H][M][d], out is [B][H][N][d]; all contiguous,
+ *     row-major, 16-byte aligned device pointers on the current HIP device.  Inputs are bf16
+ *     or fp16 (SAGE_IN_*); out is the input type, or FP32 with SAGE_OUT_FP32.
+ *   - d is 64 or 128; B, H, N, M >= 1; B*H*max(N,M)*d < 2^40.  causal masks key t > query r
+ *     (top-left alignment) and needs N == M.
+ *   - sm_scale <= 0 or not finite selects 1/sqrt(d).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue work on it and
+ *     never synchronize the host; the caller keeps every buffer alive until the stream has
+ *     passed the call.  Buffers must not overlap (out may not alias an input).
+ *   - Argument errors are detected before anything is enqueued and return a negative
+ *     sage_status.  A failed launch returns SAGE_ERR_LAUNCH; faults inside kernels surface
+ *     at the caller's next synchronization.
+ *   - NaN inputs propagate to the output rows that attend to them.
+ */
+#ifndef SAGE_ATTN_H
+#define SAGE_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SAGE_OK = 0,
+  SAGE_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, bad variant bits      */
+  SAGE_ERR_UNSUPPORTED = -2, /* valid request this build does not serve (d, causal N!=M,
+                                non-gfx950 device)                                         */
+  SAGE_ERR_NO_MEMORY = -3,   /* workspace allocation failed, or a given workspace is small */
+  SAGE_ERR_LAUNCH = -4,      /* a kernel launch or stream call failed                      */
+  SAGE_ERR_DEVICE = -5       /* no usable HIP device                                       */
+} sage_status;
+
+/* ---- variant bit-field ---- */
+#define SAGE_PATH_I8F8  0x0000u /* INT8 QK (per-token Q, 4 groups / 64 keys K), FP8 E4M3 PV   */
+#define SAGE_SMOOTH_V   0x0010u /* V' = V - mean_t(V) before quantization, O += V_m           */
+#define SAGE_IN_BF16    0x0000u
+#define SAGE_IN_FP16    0x0100u
+#define SAGE_OUT_SAME   0x0000u
+#define SAGE_OUT_FP32   0x1000u /* write FP32 output (removes output rounding from checks)    */
+
+/* Tile constants of the method (query smoothing block, key/value tile). */
+#define SAGE_BQ 128
+#define SAGE_BK 64
+
+/*
+ * sage_attn_fwd -- the whole forward pass: preprocessing (means, quantization, Delta S)
+ * followed by the fused attention kernel, on `stream`.
+ * Workspace: allocated and released on the stream (stream-ordered hipMallocAsync /
+ * hipFreeAsync); sage_attn_workspace_bytes() tells its size.
+ * Returns SAGE_OK or a negative sage_status.
+ */
+int sage_attn_fwd(const void* q, const void* k, const void* v, void* out,
+                  int B, int H, int N, int M, int d, int causal, float sm_scale,
+                  unsigned variant, void* stream);
+
+/* Bytes of device workspace sage_attn_fwd_ws needs for this problem (0 on bad arguments). */
+size_t sage_attn_workspace_bytes(int B, int H, int N, int M, int d, int causal, unsigned variant);
+
+/* As sage_attn_fwd, with a caller-owned device workspace of ws_bytes bytes (256-byte
+ * aligned).  Returns SAGE_ERR_NO_MEMORY if ws_bytes is too small. */
+int sage_attn_fwd_ws(const void* q, const void* k, const void* v, void* out,
+                     int B, int H, int N, int M, int d, int causal, float sm_scale,
+                     unsigned variant, void* workspace, size_t ws_bytes, void* stream);
+
+/*
+ * sage_attn_quantize -- the preprocessing step alone, written into caller buffers (device
+ * pointers; any may be NULL to skip it).  Layouts, with BH = B*H, nqb = ceil(N/128),
+ * nkt = ceil(M/64), Np = 128*nqb, Mp = 64*nkt:
+ *   q_hat   int8  [BH][Np][d]   smoothed, quantized Q; rows >= N are 0
+ *   k_hat   int8  [BH][Mp][d]   smoothed, quantized K; keys >= M are 0
+ *   v_hat   uint8 [BH][nkt][d][64]  E4M3 codes of V (or V'), transposed per 64-key tile;
+ *           byte p = 32h + b of channel c holds key 64*tile + kperm(h, b) with
+ *           kperm(h, b) = 32*(b/16) + 8*((b%16)/4) + 4*h + b%4 (the order in which a
+ *           lane half h of the FP8 MFMA consumes the keys of its P fragment); keys >= M are 0
+ *   dq      float [BH][Np]      per-token Q scale (1.0 for rows >= N)
+ *   dk      float [BH][nkt][4]  K scale of (tile, group); group of key t in its tile is
+ *           2*((t%64)/32) + (((t%32)>>2)&1)
+ *   dv      float [BH][d]       per-channel V scale (max|V'| / 448)
+ *   k_mean  float [BH][d]       token mean of K
+ *   v_mean  float [BH][d]       token mean of V (0 unless SAGE_SMOOTH_V)
+ *   q_mean  float [BH][nqb][d]  per-block mean of Q
+ *   delta_s float [BH][nqb][Mp] Delta S_i[t] = q_i . gamma(K)[t] (FP32); with causal only
+ *           t < 128*(i+1) is written
+ * Returns SAGE_OK or a negative sage_status.
+ */
+typedef struct {
+  void* q_hat;
+  void* k_hat;
+  void* v_hat;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* k_mean;
+  float* v_mean;
+  float* q_mean;
+  float* delta_s;
+} sage_quant_views;
+
+int sage_attn_quantize(const void* q, const void* k, const void* v,
+                       int B, int H, int N, int M, int d, int causal, unsigned variant,
+                       const sage_quant_views* dst, void* stream);
+
+/*
+ * sage_attn_set_profile_events -- measurement hook.  With both arguments non-NULL (two
+ * hipEvent_t handles), the next sage_attn_fwd / sage_attn_fwd_ws call on this thread
+ * records `start` on its stream just before the fused attention kernel and `stop` just
+ * after it, then forgets both (one call, one pair).  NULL, NULL clears a pending pair.
+ * Only the caller's events are touched; no state is shared between threads.
+ */
+void sage_attn_set_profile_events(void* start, void* stop);
+
+/* Human-readable text of a sage_status (static storage). */
+const char* sage_attn_status_string(int status);
+
+/* Library version: major*10000 + minor*100 + patch. */
+int sage_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SAGE_ATTN_H */

@@ -1,0 +1,174 @@
+"""MI355X-native quantized attention forward (SageAttention2 INT8-QK / FP8-PV method).
+
+Thin Python binding over the C ABI of ``libsage_attn.so`` (declared in
+``include/sage_attn.h``).  Every step of the computation runs in the library's HIP
+kernels; this module only marshals arguments.  PyTorch, where used, supplies device
+memory and the current stream.
+
+The raw entry points take integers (device addresses, sizes) and return the library's
+status code; ``sage_attn`` is the convenience wrapper over torch tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "SAGE_OK", "SAGE_ERR_INVALID_ARG", "SAGE_ERR_UNSUPPORTED", "SAGE_ERR_NO_MEMORY",
+    "SAGE_ERR_LAUNCH", "SAGE_ERR_DEVICE", "SAGE_PATH_I8F8", "SAGE_SMOOTH_V", "SAGE_IN_BF16",
+    "SAGE_IN_FP16", "SAGE_OUT_SAME", "SAGE_OUT_FP32", "SAGE_BQ", "SAGE_BK", "SageError",
+    "library_path", "load_library", "sage_attn_fwd", "sage_attn_fwd_ws",
+    "sage_attn_workspace_bytes", "sage_attn_quantize", "sage_attn_status_string",
+    "sage_attn_version", "sage_attn_set_profile_events", "sage_attn", "QuantViews",
+]
+
+SAGE_OK = 0
+SAGE_ERR_INVALID_ARG = -1
+SAGE_ERR_UNSUPPORTED = -2
+SAGE_ERR_NO_MEMORY = -3
+SAGE_ERR_LAUNCH = -4
+SAGE_ERR_DEVICE = -5
+
+SAGE_PATH_I8F8 = 0x0000
+SAGE_SMOOTH_V = 0x0010
+SAGE_IN_BF16 = 0x0000
+SAGE_IN_FP16 = 0x0100
+SAGE_OUT_SAME = 0x0000
+SAGE_OUT_FP32 = 0x1000
+
+SAGE_BQ = 128
+SAGE_BK = 64
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "lib", "libsage_attn.so")
+_lib = None
+
+
+class SageError(RuntimeError):
+    """A non-zero status from the library."""
+
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {sage_attn_status_string(status)} (status {status})")
+        self.status = status
+
+
+class QuantViews(ctypes.Structure):
+    """Mirror of ``sage_quant_views`` (device pointers; 0 skips a field)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("q_hat", "k_hat", "v_hat", "dq", "dk", "dv", "k_mean", "v_mean", "q_mean", "delta_s")]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libsage_attn.so; raise if it has not been built (there is no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with `python -m quantized_attention_amd.build` "
+                           "(the quantized attention has no non-HIP implementation)")
+    L = ctypes.CDLL(_LIB_PATH)
+    P, i, u, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint, ctypes.c_float, ctypes.c_size_t
+    L.sage_attn_fwd.argtypes = [P, P, P, P, i, i, i, i, i, i, f, u, P]
+    L.sage_attn_fwd.restype = i
+    L.sage_attn_fwd_ws.argtypes = [P, P, P, P, i, i, i, i, i, i, f, u, P, sz, P]
+    L.sage_attn_fwd_ws.restype = i
+    L.sage_attn_workspace_bytes.argtypes = [i, i, i, i, i, i, u]
+    L.sage_attn_workspace_bytes.restype = sz
+    L.sage_attn_quantize.argtypes = [P, P, P, i, i, i, i, i, i, u, ctypes.POINTER(QuantViews), P]
+    L.sage_attn_quantize.restype = i
+    L.sage_attn_status_string.argtypes = [i]
+    L.sage_attn_status_string.restype = ctypes.c_char_p
+    L.sage_attn_set_profile_events.argtypes = [P, P]
+    L.sage_attn_set_profile_events.restype = None
+    L.sage_attn_version.argtypes = []
+    L.sage_attn_version.restype = i
+    _lib = L
+    return L
+
+
+# ---------------------------------------------------------------- raw C ABI (same names)
+def sage_attn_fwd(q, k, v, out, B, H, N, M, d, causal, sm_scale, variant, stream) -> int:
+    return load_library().sage_attn_fwd(q, k, v, out, B, H, N, M, d, int(causal), float(sm_scale),
+                                        variant, stream)
+
+
+def sage_attn_fwd_ws(q, k, v, out, B, H, N, M, d, causal, sm_scale, variant, workspace, ws_bytes,
+                     stream) -> int:
+    return load_library().sage_attn_fwd_ws(q, k, v, out, B, H, N, M, d, int(causal), float(sm_scale),
+                                           variant, workspace, ws_bytes, stream)
+
+
+def sage_attn_workspace_bytes(B, H, N, M, d, causal, variant) -> int:
+    return load_library().sage_attn_workspace_bytes(B, H, N, M, d, int(causal), variant)
+
+
+def sage_attn_quantize(q, k, v, B, H, N, M, d, causal, variant, views: QuantViews, stream) -> int:
+    return load_library().sage_attn_quantize(q, k, v, B, H, N, M, d, int(causal), variant,
+                                             ctypes.byref(views), stream)
+
+
+def sage_attn_set_profile_events(start, stop) -> None:
+    load_library().sage_attn_set_profile_events(start, stop)
+
+
+def sage_attn_status_string(status: int) -> str:
+    try:
+        return load_library().sage_attn_status_string(status).decode()
+    except RuntimeError:
+        return f"status {status}"
+
+
+def sage_attn_version() -> int:
+    return load_library().sage_attn_version()
+
+
+# ---------------------------------------------------------------- torch convenience
+def _variant_for(q, smooth_v: bool, out_fp32: bool) -> int:
+    import torch
+    if q.dtype == torch.bfloat16:
+        var = SAGE_IN_BF16
+    elif q.dtype == torch.float16:
+        var = SAGE_IN_FP16
+    else:
+        raise TypeError(f"q, k, v must be bf16 or fp16, got {q.dtype}")
+    if smooth_v:
+        var |= SAGE_SMOOTH_V
+    if out_fp32:
+        var |= SAGE_OUT_FP32
+    return var
+
+
+def sage_attn(q, k, v, causal: bool = False, sm_scale: float | None = None, smooth_v: bool = False,
+              out_fp32: bool = False, out=None):
+    """softmax(Q K^T * sm_scale) V with the quantized method, for [B, H, N, d] tensors.
+
+    q: [B, H, N, d], k/v: [B, H, M, d], all the same dtype (bf16/fp16), contiguous, on the
+    current device.  Returns out [B, H, N, d] in the input dtype (FP32 with out_fp32).
+    """
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, T, d]")
+    B, H, N, d = q.shape
+    M = k.shape[2]
+    if tuple(k.shape) != (B, H, M, d) or tuple(v.shape) != (B, H, M, d):
+        raise ValueError("k and v must be [B, H, M, d] matching q")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    var = _variant_for(q, smooth_v, out_fp32)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.float32 if out_fp32 else q.dtype, device=q.device)
+    scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(d)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = sage_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, M, d,
+                       causal, scale, var, stream)
+    if rc != SAGE_OK:
+        raise SageError(rc, "sage_attn_fwd")
+    return out

@@ -1,0 +1,255 @@
+// sage_attn.hip -- C ABI entry points: argument checks, workspace, launch sequence.
+//
+// The sequence is the pages' forward pass ("SageAttention2 Technical Report" summary,
+// 3.4 "The Complete Algorithm (Algorithm 1)" and 3.2 "Big-Picture Architecture"):
+// preprocessing (K mean and K^, V scale and V^, Q block means and Q^, Delta S) as separate
+// launches writing a device workspace, then one fused attention kernel.  All argument
+// checks run before anything is enqueued; nothing here synchronizes the host.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+
+#include "sage_common.hpp"
+
+namespace sage {
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t workspace_layout(const Problem& p, size_t* sizes) {
+  const size_t BH = (size_t)p.BH, d = (size_t)p.d;
+  size_t s[13];
+  s[0] = BH * p.Np * d;                      // qhat
+  s[1] = BH * p.Mp * d;                      // khat
+  s[2] = BH * p.nkt * d * kBK;               // vhat
+  s[3] = BH * p.Np * sizeof(float);          // dq
+  s[4] = BH * p.nkt * 4 * sizeof(float);     // dk
+  s[5] = BH * d * sizeof(float);             // dv
+  s[6] = BH * d * sizeof(float);             // kmean
+  s[7] = BH * d * sizeof(float);             // vmean
+  s[8] = BH * p.nqb * d * sizeof(float);     // qmean
+  s[9] = BH * p.nqb * (size_t)p.Mp * sizeof(float);  // ds
+  s[10] = BH * p.nkt * d * sizeof(double);   // kpart
+  s[11] = BH * p.nkt * d * sizeof(double);   // vpart
+  s[12] = BH * p.nkt * d * sizeof(float);    // vamax
+  size_t tot = 0;
+  for (int i = 0; i < 13; i++) {
+    if (sizes) sizes[i] = s[i];
+    tot += align256(s[i]);
+  }
+  return tot;
+}
+
+void carve_workspace(const Problem& p, void* base, Workspace* w) {
+  size_t s[13];
+  workspace_layout(p, s);
+  char* b = static_cast<char*>(base);
+  void* ptr[13];
+  for (int i = 0; i < 13; i++) {
+    ptr[i] = b;
+    b += align256(s[i]);
+  }
+  w->qhat = (int8_t*)ptr[0];
+  w->khat = (int8_t*)ptr[1];
+  w->vhat = (uint8_t*)ptr[2];
+  w->dq = (float*)ptr[3];
+  w->dk = (float*)ptr[4];
+  w->dv = (float*)ptr[5];
+  w->kmean = (float*)ptr[6];
+  w->vmean = (float*)ptr[7];
+  w->qmean = (float*)ptr[8];
+  w->ds = (float*)ptr[9];
+  w->kpart = (double*)ptr[10];
+  w->vpart = (double*)ptr[11];
+  w->vamax = (float*)ptr[12];
+}
+
+namespace {
+
+constexpr unsigned kKnownBits = SAGE_SMOOTH_V | SAGE_IN_FP16 | SAGE_OUT_FP32;
+
+// Per-device "is gfx950" cache, filled once per device under a mutex.
+int device_check() {
+  static std::mutex mu;
+  static signed char ok[64];
+  static bool init = false;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SAGE_ERR_DEVICE;
+  if (dev < 0 || dev >= 64) return SAGE_ERR_DEVICE;
+  std::lock_guard<std::mutex> g(mu);
+  if (!init) {
+    std::memset(ok, -1, sizeof(ok));
+    init = true;
+  }
+  if (ok[dev] < 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return SAGE_ERR_DEVICE;
+    ok[dev] = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 0;
+  }
+  return ok[dev] ? SAGE_OK : SAGE_ERR_UNSUPPORTED;
+}
+
+int make_problem(int B, int H, int N, int M, int d, int causal, float sm_scale, unsigned variant,
+                 Problem* p) {
+  if (B < 1 || H < 1 || N < 1 || M < 1) return SAGE_ERR_INVALID_ARG;
+  if (variant & ~kKnownBits) return SAGE_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return SAGE_ERR_UNSUPPORTED;
+  if (causal && N != M) return SAGE_ERR_UNSUPPORTED;
+  const double big = (double)B * H * (double)(N > M ? N : M) * d;
+  if (big >= 1099511627776.0) return SAGE_ERR_INVALID_ARG;  // 2^40 elements
+  if ((long long)B * H > (1LL << 30)) return SAGE_ERR_INVALID_ARG;
+  p->B = B; p->H = H; p->N = N; p->M = M; p->d = d;
+  p->causal = causal ? 1 : 0;
+  p->sm_scale = (sm_scale > 0.0f && std::isfinite(sm_scale)) ? sm_scale : 1.0f / std::sqrt((float)d);
+  p->variant = variant;
+  p->BH = B * H;
+  p->nqb = (N + kBQ - 1) / kBQ;
+  p->nkt = (M + kBK - 1) / kBK;
+  p->Np = p->nqb * kBQ;
+  p->Mp = p->nkt * kBK;
+  p->fp16 = (variant & SAGE_IN_FP16) != 0;
+  p->out_fp32 = (variant & SAGE_OUT_FP32) != 0;
+  p->smooth_v = (variant & SAGE_SMOOTH_V) != 0;
+  // grid limits: y = B*H for every kernel, x = blocks/tiles
+  if (p->BH > 65535 || p->nkt > (1 << 30)) return SAGE_ERR_INVALID_ARG;
+  return SAGE_OK;
+}
+
+bool aligned16(const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) == 0; }
+
+// The preprocessing launches; ds goes to ds_out scaled by ds_scale.
+int run_preprocess(const Problem& p, const void* q, const void* k, const void* v, const Workspace& w,
+                   float ds_scale, float* ds_out, hipStream_t s) {
+  if (launch_k_stats(p, k, v, w, s) != hipSuccess) return SAGE_ERR_LAUNCH;
+  if (launch_k_finalize(p, w, s) != hipSuccess) return SAGE_ERR_LAUNCH;
+  if (launch_k_quant(p, k, v, w, s) != hipSuccess) return SAGE_ERR_LAUNCH;
+  if (p.smooth_v && launch_v_scale(p, w, s) != hipSuccess) return SAGE_ERR_LAUNCH;
+  if (launch_v_quant(p, v, w, s) != hipSuccess) return SAGE_ERR_LAUNCH;
+  if (launch_q_prep(p, q, w, s) != hipSuccess) return SAGE_ERR_LAUNCH;
+  if (ds_out && launch_delta_s(p, k, w, ds_scale, ds_out, s) != hipSuccess) return SAGE_ERR_LAUNCH;
+  return SAGE_OK;
+}
+
+// Events of the measurement hook (per thread, consumed by the next forward call).
+thread_local hipEvent_t t_prof_start = nullptr, t_prof_stop = nullptr;
+
+int fwd_impl(const void* q, const void* k, const void* v, void* out, const Problem& p, void* ws,
+             hipStream_t s) {
+  Workspace w;
+  carve_workspace(p, ws, &w);
+  hipEvent_t e0 = t_prof_start, e1 = t_prof_stop;
+  t_prof_start = t_prof_stop = nullptr;
+  int rc = run_preprocess(p, q, k, v, w, p.sm_scale * 1.4426950408889634f, w.ds, s);
+  if (rc != SAGE_OK) return rc;
+  if (e0 && hipEventRecord(e0, s) != hipSuccess) return SAGE_ERR_LAUNCH;
+  if (launch_attn_fwd(p, w, out, s) != hipSuccess) return SAGE_ERR_LAUNCH;
+  if (e1 && hipEventRecord(e1, s) != hipSuccess) return SAGE_ERR_LAUNCH;
+  return SAGE_OK;
+}
+
+int check_io(const void* q, const void* k, const void* v, const void* out) {
+  if (!q || !k || !v || !out) return SAGE_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return SAGE_ERR_INVALID_ARG;
+  return SAGE_OK;
+}
+
+}  // namespace
+}  // namespace sage
+
+using namespace sage;
+
+extern "C" {
+
+size_t sage_attn_workspace_bytes(int B, int H, int N, int M, int d, int causal, unsigned variant) {
+  Problem p;
+  if (make_problem(B, H, N, M, d, causal, 0.0f, variant, &p) != SAGE_OK) return 0;
+  return workspace_layout(p, nullptr);
+}
+
+int sage_attn_fwd_ws(const void* q, const void* k, const void* v, void* out, int B, int H, int N,
+                     int M, int d, int causal, float sm_scale, unsigned variant, void* workspace,
+                     size_t ws_bytes, void* stream) {
+  Problem p;
+  int rc = make_problem(B, H, N, M, d, causal, sm_scale, variant, &p);
+  if (rc != SAGE_OK) return rc;
+  if ((rc = check_io(q, k, v, out)) != SAGE_OK) return rc;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return SAGE_ERR_INVALID_ARG;
+  if (ws_bytes < workspace_layout(p, nullptr)) return SAGE_ERR_NO_MEMORY;
+  if ((rc = device_check()) != SAGE_OK) return rc;
+  return fwd_impl(q, k, v, out, p, workspace, (hipStream_t)stream);
+}
+
+int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int M,
+                  int d, int causal, float sm_scale, unsigned variant, void* stream) {
+  Problem p;
+  int rc = make_problem(B, H, N, M, d, causal, sm_scale, variant, &p);
+  if (rc != SAGE_OK) return rc;
+  if ((rc = check_io(q, k, v, out)) != SAGE_OK) return rc;
+  if ((rc = device_check()) != SAGE_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, workspace_layout(p, nullptr), s) != hipSuccess || !ws) {
+    (void)hipGetLastError();
+    return SAGE_ERR_NO_MEMORY;
+  }
+  rc = fwd_impl(q, k, v, out, p, ws, s);
+  if (hipFreeAsync(ws, s) != hipSuccess && rc == SAGE_OK) rc = SAGE_ERR_LAUNCH;
+  return rc;
+}
+
+int sage_attn_quantize(const void* q, const void* k, const void* v, int B, int H, int N, int M, int d,
+                       int causal, unsigned variant, const sage_quant_views* dst, void* stream) {
+  Problem p;
+  int rc = make_problem(B, H, N, M, d, causal, 0.0f, variant, &p);
+  if (rc != SAGE_OK) return rc;
+  if (!dst || !q || !k || !v) return SAGE_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return SAGE_ERR_INVALID_ARG;
+  if ((rc = device_check()) != SAGE_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, workspace_layout(p, nullptr), s) != hipSuccess || !ws) {
+    (void)hipGetLastError();
+    return SAGE_ERR_NO_MEMORY;
+  }
+  Workspace w;
+  carve_workspace(p, ws, &w);
+  rc = run_preprocess(p, q, k, v, w, 1.0f, dst->delta_s, s);
+  size_t sz[13];
+  workspace_layout(p, sz);
+  struct Copy { void* dst; const void* src; size_t n; } copies[] = {
+      {dst->q_hat, w.qhat, sz[0]}, {dst->k_hat, w.khat, sz[1]}, {dst->v_hat, w.vhat, sz[2]},
+      {dst->dq, w.dq, sz[3]},      {dst->dk, w.dk, sz[4]},      {dst->dv, w.dv, sz[5]},
+      {dst->k_mean, w.kmean, sz[6]}, {dst->v_mean, w.vmean, sz[7]}, {dst->q_mean, w.qmean, sz[8]}};
+  for (const Copy& c : copies) {
+    if (rc != SAGE_OK) break;
+    if (c.dst && hipMemcpyAsync(c.dst, c.src, c.n, hipMemcpyDeviceToDevice, s) != hipSuccess) rc = SAGE_ERR_LAUNCH;
+  }
+  if (hipFreeAsync(ws, s) != hipSuccess && rc == SAGE_OK) rc = SAGE_ERR_LAUNCH;
+  return rc;
+}
+
+void sage_attn_set_profile_events(void* start, void* stop) {
+  if (start && stop) {
+    t_prof_start = (hipEvent_t)start;
+    t_prof_stop = (hipEvent_t)stop;
+  } else {
+    t_prof_start = t_prof_stop = nullptr;
+  }
+}
+
+const char* sage_attn_status_string(int status) {
+  switch (status) {
+    case SAGE_OK: return "ok";
+    case SAGE_ERR_INVALID_ARG: return "invalid argument";
+    case SAGE_ERR_UNSUPPORTED: return "unsupported (head dim, causal with N != M, or non-gfx950 device)";
+    case SAGE_ERR_NO_MEMORY: return "workspace allocation failed or workspace too small";
+    case SAGE_ERR_LAUNCH: return "kernel launch failed";
+    case SAGE_ERR_DEVICE: return "no usable HIP device";
+    default: return "unknown status";
+  }
+}
+
+int sage_attn_version(void) { return 100; }
+
+}  // extern "C"

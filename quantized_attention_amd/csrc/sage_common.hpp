@@ -1,0 +1,117 @@
+// sage_common.hpp -- shared definitions of the HIP library (gfx950 only).
+//
+// Problem description, workspace carving and the small device helpers the preprocessing
+// and attention kernels share.  Nothing here is shared with the CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "sage_attn.h"
+
+namespace sage {
+
+constexpr int kBQ = SAGE_BQ;  // query block: Q smoothing and the attention work-group tile
+constexpr int kBK = SAGE_BK;  // key/value tile: running-max step and two-level accumulation
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// Resolved problem: sizes, padded sizes and the variant bits.
+struct Problem {
+  int B, H, N, M, d;
+  int causal;
+  float sm_scale;
+  unsigned variant;
+  int BH, nqb, nkt, Np, Mp;
+  bool fp16, out_fp32, smooth_v;
+};
+
+// Device workspace (all 256-byte aligned slices of one allocation).
+struct Workspace {
+  int8_t* qhat;    // [BH][Np][d]
+  int8_t* khat;    // [BH][Mp][d]
+  uint8_t* vhat;   // [BH][nkt][d][64], keys permuted (see sage_attn.h)
+  float* dq;       // [BH][Np]
+  float* dk;       // [BH][nkt][4]
+  float* dv;       // [BH][d]
+  float* kmean;    // [BH][d]
+  float* vmean;    // [BH][d]
+  float* qmean;    // [BH][nqb][d]
+  float* ds;       // [BH][nqb][Mp], Delta S (pre-multiplied by ds_scale)
+  double* kpart;   // [BH][nkt][d] FP64 chunk sums of K
+  double* vpart;   // [BH][nkt][d] FP64 chunk sums of V (V smoothing)
+  float* vamax;    // [BH][nkt][d] chunk max |V| (or |V'|)
+};
+
+// Bytes of each workspace slice, in carving order.
+size_t workspace_layout(const Problem& p, size_t* sizes /* [13] or null */);
+void carve_workspace(const Problem& p, void* base, Workspace* w);
+
+// The key a lane half h consumes at byte b of its 32-byte FP8 P fragment: the S^T
+// accumulator of the two 32-key halves (T = b / 16) holds, for accumulator register
+// r = b % 16, key 8*(r/4) + 4*h + r%4 of that half.
+__host__ __device__ inline int kperm(int h, int b) {
+  return 32 * (b >> 4) + 8 * ((b & 15) >> 2) + 4 * h + (b & 3);
+}
+
+// Scale group (0..3) of key t inside its 64-key tile: the lane half of the S^T accumulator
+// that holds it, within its 32-key half.
+__host__ __device__ inline int kgroup(int t) {
+  int u = t & 63;
+  return 2 * (u >> 5) + ((u >> 2) & 1);
+}
+
+__device__ inline float load_in(const uint16_t* p, size_t i, bool fp16) {
+  uint16_t h = p[i];
+  if (fp16) return static_cast<float>(__builtin_bit_cast(_Float16, h));
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// FP32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ inline uint32_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// FP32 -> fp16 bits, round to nearest even (hardware conversion).
+__device__ inline uint32_t f32_to_fp16_bits(float x) {
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(x)));
+}
+
+// |x| max that ignores NaN (a NaN element does not set a scale).
+__device__ inline float amax_upd(float m, float x) {
+  float a = fabsf(x);
+  return (a > m) ? a : m;
+}
+
+// Symmetric INT8 code: RNE of x / scale (IEEE FP32 division), clamped to +-127; NaN -> 0.
+__device__ inline int8_t int8_code(float x, float scale) {
+  float y = rintf(__fdiv_rn(x, scale));
+  if (!(y == y)) return 0;
+  y = y > 127.0f ? 127.0f : (y < -127.0f ? -127.0f : y);
+  return static_cast<int8_t>(static_cast<int>(y));
+}
+
+__device__ inline float int8_scale(float amax) {
+  float a = amax > 1e-8f ? amax : 1e-8f;
+  return __fdiv_rn(a, 127.0f);
+}
+
+// Launchers (one per kernel file); each returns hipSuccess or the launch error.
+hipError_t launch_k_stats(const Problem& p, const void* k, const void* v, const Workspace& w, hipStream_t s);
+hipError_t launch_k_finalize(const Problem& p, const Workspace& w, hipStream_t s);
+hipError_t launch_k_quant(const Problem& p, const void* k, const void* v, const Workspace& w, hipStream_t s);
+hipError_t launch_v_scale(const Problem& p, const Workspace& w, hipStream_t s);
+hipError_t launch_v_quant(const Problem& p, const void* v, const Workspace& w, hipStream_t s);
+hipError_t launch_q_prep(const Problem& p, const void* q, const Workspace& w, hipStream_t s);
+hipError_t launch_delta_s(const Problem& p, const void* k, const Workspace& w, float ds_scale,
+                          float* ds_out, hipStream_t s);
+hipError_t launch_attn_fwd(const Problem& p, const Workspace& w, void* out, hipStream_t s);
+
+}  // namespace sage

@@ -17,7 +17,8 @@ Arrays are returned as raw 16-bit patterns (uint16), shape [B, H, T, d].
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field, replace
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, replace
 
 import numpy as np
 
@@ -85,9 +86,13 @@ CONFIGS = {
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round FP32 to bf16 (nearest, ties to even) and return the 16-bit patterns."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    r = ((u >> 16) & 1) + np.uint32(0x7FFF)
-    return ((u + r) >> 16).astype(np.uint16)
+    u = np.array(x, dtype=np.float32, copy=True).view(np.uint32)
+    r = u >> 16
+    r &= 1
+    r += np.uint32(0x7FFF)
+    u += r
+    u >>= 16
+    return u.astype(np.uint16)
 
 
 def f32_to_fp16_bits(x: np.ndarray) -> np.ndarray:
@@ -117,22 +122,32 @@ def _head(cfg: Config, tensor: int, b: int, h: int, T: int) -> np.ndarray:
         off = (rng.standard_normal(d) * dist.v_bias_std).astype(np.float32)
     x = rng.standard_normal((T, d), dtype=np.float32)
     x += off[None, :]
-    return f32_to_fp16_bits(x) if cfg.fp16 else f32_to_bf16_bits(x)
+    if cfg.fp16:
+        return f32_to_fp16_bits(x)
+    u = x.view(np.uint32)  # x is owned here: round to bf16 in place
+    r = u >> 16
+    r &= 1
+    r += np.uint32(0x7FFF)
+    u += r
+    u >>= 16
+    return u.astype(np.uint16)
 
 
 def make_tensor(cfg: Config, tensor: int, heads=None) -> np.ndarray:
     """One of Q, K, V as uint16 bits [B, H, T, d] (or [len(heads), T, d] for a subset of
     flattened (b*H + h) head indices)."""
     T = cfg.N if tensor == TENSOR_Q else cfg.M
-    if heads is None:
-        out = np.empty((cfg.B, cfg.H, T, cfg.d), np.uint16)
-        for b in range(cfg.B):
-            for h in range(cfg.H):
-                out[b, h] = _head(cfg, tensor, b, h, T)
-        return out
-    out = np.empty((len(heads), T, cfg.d), np.uint16)
-    for i, bh in enumerate(heads):
+    idx = list(range(cfg.B * cfg.H)) if heads is None else list(heads)
+    out = np.empty((len(idx), T, cfg.d), np.uint16)
+
+    def fill(i):  # each head has its own generator, so threads do not change the values
+        bh = idx[i]
         out[i] = _head(cfg, tensor, bh // cfg.H, bh % cfg.H, T)
+
+    with ThreadPoolExecutor(max_workers=min(8, len(idx))) as ex:
+        list(ex.map(fill, range(len(idx))))
+    if heads is None:
+        return out.reshape(cfg.B, cfg.H, T, cfg.d)
     return out
 
 

@@ -1,0 +1,72 @@
+"""Helpers of the GPU parity tests: move seeded inputs to the device, call the C ABI
+through the binding, and bring results back in the oracle's natural layouts.
+
+The only layout knowledge here is what include/sage_attn.h documents for the quantize
+views (padding, the per-tile transposed V^ with its key order); nothing is imported from
+the HIP sources or the oracle."""
+import numpy as np
+import torch
+
+import quantized_attention_amd as qa
+
+BQ, BK = qa.SAGE_BQ, qa.SAGE_BK
+
+
+def to_dev(bits: np.ndarray, fp16: bool) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.float16 if fp16 else torch.bfloat16).cuda()
+
+
+def doc_kperm(h: int, b: int) -> int:
+    """Key order of the transposed V^ tile, as the header documents it."""
+    return 32 * (b // 16) + 8 * ((b % 16) // 4) + 4 * h + b % 4
+
+
+INV_PERM = np.array([doc_kperm(p // 32, p % 32) for p in range(64)])
+
+
+def fwd(q, k, v, fp16, causal, sm_scale, smooth_v=False, out_fp32=True):
+    """q, k, v: uint16 bits [B, H, T, d] on the host; returns the output as a host array."""
+    B, H, N, d = q.shape
+    M = k.shape[2]
+    tq, tk, tv = to_dev(q, fp16), to_dev(k, fp16), to_dev(v, fp16)
+    out = qa.sage_attn(tq, tk, tv, causal=causal, sm_scale=sm_scale, smooth_v=smooth_v, out_fp32=out_fp32)
+    torch.cuda.synchronize()
+    return out
+
+
+def quantize(q, k, v, fp16, causal, smooth_v=False):
+    """Preprocessing through sage_attn_quantize, returned per head in natural layouts."""
+    B, H, N, d = q.shape
+    M = k.shape[2]
+    BH = B * H
+    nqb, nkt = -(-N // BQ), -(-M // BK)
+    Np, Mp = nqb * BQ, nkt * BK
+    dev = torch.device("cuda")
+    bufs = dict(
+        q_hat=torch.empty((BH, Np, d), dtype=torch.int8, device=dev),
+        k_hat=torch.empty((BH, Mp, d), dtype=torch.int8, device=dev),
+        v_hat=torch.empty((BH, nkt, d, 64), dtype=torch.uint8, device=dev),
+        dq=torch.empty((BH, Np), dtype=torch.float32, device=dev),
+        dk=torch.empty((BH, nkt, 4), dtype=torch.float32, device=dev),
+        dv=torch.empty((BH, d), dtype=torch.float32, device=dev),
+        k_mean=torch.empty((BH, d), dtype=torch.float32, device=dev),
+        v_mean=torch.empty((BH, d), dtype=torch.float32, device=dev),
+        q_mean=torch.empty((BH, nqb, d), dtype=torch.float32, device=dev),
+        delta_s=torch.full((BH, nqb, Mp), float("nan"), dtype=torch.float32, device=dev),
+    )
+    views = qa.QuantViews(**{n: t.data_ptr() for n, t in bufs.items()})
+    tq, tk, tv = to_dev(q, fp16), to_dev(k, fp16), to_dev(v, fp16)
+    var = (qa.SAGE_IN_FP16 if fp16 else qa.SAGE_IN_BF16) | (qa.SAGE_SMOOTH_V if smooth_v else 0)
+    rc = qa.sage_attn_quantize(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), B, H, N, M, d, causal, var,
+                               views, torch.cuda.current_stream().cuda_stream)
+    assert rc == qa.SAGE_OK, qa.sage_attn_status_string(rc)
+    torch.cuda.synchronize()
+    h = {n: t.cpu().numpy() for n, t in bufs.items()}
+    # V^: [BH][nkt][d][64] (permuted keys) -> [BH][Mp][d]
+    vt = h["v_hat"]
+    vnat = np.zeros((BH, Mp, d), np.uint8)
+    for u in range(nkt):
+        vnat[:, u * 64 + INV_PERM, :] = vt[:, u].transpose(0, 2, 1)
+    h["v_nat"] = vnat
+    return h

@@ -1,0 +1,64 @@
+"""The C-ABI library loads, exports every symbol include/sage_attn.h declares, and rejects
+bad arguments before touching a device (CPU-only; no compute calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_attention_amd as qa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "sage_attn.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\**\s*(sage_attn_[a-z_]+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert names == sorted(["sage_attn_fwd", "sage_attn_fwd_ws", "sage_attn_workspace_bytes",
+                            "sage_attn_quantize", "sage_attn_set_profile_events",
+                            "sage_attn_status_string", "sage_attn_version"])
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(qa.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert hasattr(qa, name), name  # the binding keeps the same names
+
+
+def test_status_strings_and_version():
+    assert qa.sage_attn_version() >= 100
+    for s in (qa.SAGE_OK, qa.SAGE_ERR_INVALID_ARG, qa.SAGE_ERR_UNSUPPORTED, qa.SAGE_ERR_NO_MEMORY,
+              qa.SAGE_ERR_LAUNCH, qa.SAGE_ERR_DEVICE):
+        assert qa.sage_attn_status_string(s)
+    assert qa.sage_attn_status_string(123) == "unknown status"
+
+
+def test_argument_errors_are_reported_before_any_device_work():
+    f = qa.sage_attn_fwd
+    A = 256  # a 16-byte aligned stand-in address; never dereferenced on these paths
+    assert f(0, A, A, A, 1, 1, 64, 64, 64, 0, 0.0, 0, 0) == qa.SAGE_ERR_INVALID_ARG   # null q
+    assert f(A + 2, A, A, A, 1, 1, 64, 64, 64, 0, 0.0, 0, 0) == qa.SAGE_ERR_INVALID_ARG  # misaligned
+    assert f(A, A, A, A, 0, 1, 64, 64, 64, 0, 0.0, 0, 0) == qa.SAGE_ERR_INVALID_ARG   # B = 0
+    assert f(A, A, A, A, 1, 1, 0, 64, 64, 0, 0.0, 0, 0) == qa.SAGE_ERR_INVALID_ARG   # N = 0
+    assert f(A, A, A, A, 1, 1, 64, 64, 96, 0, 0.0, 0, 0) == qa.SAGE_ERR_UNSUPPORTED  # d = 96
+    assert f(A, A, A, A, 1, 1, 64, 65, 64, 1, 0.0, 0, 0) == qa.SAGE_ERR_UNSUPPORTED  # causal N != M
+    assert f(A, A, A, A, 1, 1, 64, 64, 64, 0, 0.0, 0x8, 0) == qa.SAGE_ERR_INVALID_ARG  # unknown bit
+    ws = qa.sage_attn_workspace_bytes(1, 1, 64, 64, 64, 0, 0)
+    assert ws > 0
+    assert qa.sage_attn_fwd_ws(A, A, A, A, 1, 1, 64, 64, 64, 0, 0.0, 0, A, ws - 1, 0) == qa.SAGE_ERR_NO_MEMORY
+    assert qa.sage_attn_fwd_ws(A, A, A, A, 1, 1, 64, 64, 64, 0, 0.0, 0, A + 16, ws, 0) == qa.SAGE_ERR_INVALID_ARG
+    assert qa.sage_attn_workspace_bytes(1, 1, 64, 64, 80, 0, 0) == 0
+    assert qa.sage_attn_quantize(0, A, A, 1, 1, 64, 64, 64, 0, 0, qa.QuantViews(), 0) == qa.SAGE_ERR_INVALID_ARG
+
+
+def test_workspace_grows_with_problem():
+    a = qa.sage_attn_workspace_bytes(1, 32, 4096, 4096, 128, 0, 0)
+    b = qa.sage_attn_workspace_bytes(1, 32, 32768, 32768, 128, 1, 0)
+    assert 0 < a < b
+    # dominated by Delta S (nqb * Mp floats per head) and the three quantized tensors
+    assert b < 2 * 1024 ** 3

@@ -1,0 +1,188 @@
+"""GPU parity of the HIP path against the CPU oracle (needs an MI355X).
+
+Bars (stated by the method's acceptance criteria): quantized tensors, scales and means
+bit-exact; the output within max |err| <= 1e-2 and mean |err| <= 1e-3 of the oracle
+(FP32 output, so output rounding is not part of the error) and cosine >= 0.999 against
+textbook FP64 attention.  Delta S is FP32 on the GPU and FP64 in the oracle, so it is
+compared with a relative tolerance.
+
+Sizes: small cases the oracle finishes in seconds that span several tiles with ragged
+tails; the full workload shapes in the launch configuration the benchmark times, checked
+on sampled rows the oracle computes one by one.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_attention_amd import synthetic as sy
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS, MEAN_ABS, MIN_COS = 1e-2, 1e-3, 0.999
+
+
+def say(msg):
+    print(f"[gpu-test] {msg}", file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import quantized_attention_amd  # noqa: F401  (fails loudly if the library is missing)
+    quantized_attention_amd.load_library()
+
+
+from tests import gpu_util as gu  # noqa: E402
+
+
+def small(name, **kw):
+    return sy.CONFIGS[name].with_shape(**kw)
+
+
+SMALL_CASES = [
+    ("tiny", sy.CONFIGS["tiny"]),
+    ("n4k-ragged", small("n4k", H=2, N=600, M=600)),
+    ("prefill-causal", small("prefill32k", H=2, N=700, M=700)),
+    ("video-smoothv", small("video17k", B=2, H=1, N=333, M=333)),
+    ("video-nosmooth", small("video17k", B=1, H=2, N=333, M=333, smooth_v=False)),
+    ("fp16-d128-N!=M", sy.Config("fp16x", 1, 2, 300, 1000, 128, "fp16", False,
+                                 sy.Dist(q_off_std=1.0, k_off_std=2.0, v_bias_std=0.5), 77)),
+    ("bf16-d64-causal", sy.Config("bf16c", 1, 1, 250, 250, 64, "bf16", True,
+                                  sy.Dist(k_off_std=3.0, k_spike=8.0, k_spike_channels=sy.spike_channels(64)), 78)),
+    ("one-token", sy.Config("one", 1, 1, 1, 1, 64, "bf16", False, sy.Dist(), 79)),
+    ("few-tokens", sy.Config("few", 1, 3, 5, 3, 128, "fp16", False, sy.Dist(k_off_std=1.0), 80)),
+]
+
+
+def oracle_head(cfg, q, k, v, bh, flags=0, rows=None):
+    b, h = bh // cfg.H, bh % cfg.H
+    return oracle.forward_head(q[b, h], k[b, h], v[b, h], cfg.fp16, cfg.causal, 1 / math.sqrt(cfg.d),
+                               flags | (oracle.SMOOTH_V if cfg.smooth_v else 0), rows=rows)
+
+
+@pytest.mark.parametrize("name,cfg", SMALL_CASES, ids=[c[0] for c in SMALL_CASES])
+def test_preprocess_bit_exact(name, cfg):
+    q, k, v = sy.make_qkv(cfg)
+    say(f"quantize {name} B={cfg.B} H={cfg.H} N={cfg.N} M={cfg.M} d={cfg.d}")
+    g = gu.quantize(q, k, v, cfg.fp16, cfg.causal, cfg.smooth_v)
+    N, M = cfg.N, cfg.M
+    for bh in range(cfg.B * cfg.H):
+        b, h = bh // cfg.H, bh % cfg.H
+        o = oracle.preprocess_head(q[b, h], k[b, h], v[b, h], cfg.fp16,
+                                   oracle.SMOOTH_V if cfg.smooth_v else 0)
+        assert np.array_equal(g["k_mean"][bh].view(np.uint32), o["kmean"].view(np.uint32))
+        assert np.array_equal(g["v_mean"][bh].view(np.uint32), o["vmean"].view(np.uint32))
+        assert np.array_equal(g["q_mean"][bh].view(np.uint32), o["qmean"].view(np.uint32))
+        assert np.array_equal(g["dq"][bh, :N].view(np.uint32), o["dq"].view(np.uint32))
+        assert np.array_equal(g["dk"][bh].view(np.uint32), o["dk"].view(np.uint32))
+        assert np.array_equal(g["dv"][bh].view(np.uint32), o["dv"].view(np.uint32))
+        assert np.array_equal(g["q_hat"][bh, :N], o["qhat"])
+        assert not g["q_hat"][bh, N:].any()
+        assert np.array_equal(g["k_hat"][bh, :M], o["khat"])
+        assert not g["k_hat"][bh, M:].any()
+        assert np.array_equal(g["v_nat"][bh, :M], o["vhat"])
+        assert not g["v_nat"][bh, M:].any()
+        ds, ref = g["delta_s"][bh][:, :M].astype(np.float64), o["ds"]
+        if cfg.causal:
+            mask = np.arange(M)[None, :] < 128 * (np.arange(ds.shape[0])[:, None] + 1)
+            ds, ref = ds[mask], ref[mask]
+        assert np.abs(ds - ref).max() <= 1e-5 * max(1.0, np.abs(ref).max())
+
+
+def check_output(got, ref, exact=None):
+    err = np.abs(got - ref)
+    assert np.isfinite(got).all()
+    assert err.max() <= MAX_ABS, f"max abs err {err.max()}"
+    assert err.mean() <= MEAN_ABS, f"mean abs err {err.mean()}"
+    if exact is not None:
+        cos = (got * exact).sum() / math.sqrt((got * got).sum() * (exact * exact).sum())
+        assert cos >= MIN_COS, f"cosine {cos}"
+
+
+@pytest.mark.parametrize("name,cfg", SMALL_CASES, ids=[c[0] for c in SMALL_CASES])
+def test_forward_parity_small(name, cfg):
+    q, k, v = sy.make_qkv(cfg)
+    say(f"forward {name} B={cfg.B} H={cfg.H} N={cfg.N} M={cfg.M} d={cfg.d} causal={cfg.causal}")
+    out = gu.fwd(q, k, v, cfg.fp16, cfg.causal, None, cfg.smooth_v).cpu().numpy()
+    s = 1 / math.sqrt(cfg.d)
+    allg, allr, alle = [], [], []
+    for bh in range(cfg.B * cfg.H):
+        b, h = bh // cfg.H, bh % cfg.H
+        allg.append(out[b, h].astype(np.float64))
+        allr.append(oracle_head(cfg, q, k, v, bh))
+        alle.append(oracle.exact_head(q[b, h], k[b, h], v[b, h], cfg.fp16, cfg.causal, s))
+    g, r, e = np.stack(allg), np.stack(allr), np.stack(alle)
+    check_output(g, r, e if cfg.N > 1 else None)
+
+
+def test_output_dtype_is_rounded_fp32():
+    cfg = small("n4k", H=2, N=300, M=300)
+    q, k, v = sy.make_qkv(cfg)
+    say("bf16 vs fp32 output")
+    o32 = gu.fwd(q, k, v, False, False, None, out_fp32=True).cpu()
+    o16 = gu.fwd(q, k, v, False, False, None, out_fp32=False).cpu()
+    assert o16.dtype == torch.bfloat16
+    assert torch.equal(o32.to(torch.bfloat16).view(torch.int16), o16.view(torch.int16))
+
+
+def test_deterministic():
+    cfg = small("prefill32k", H=2, N=1000, M=1000)
+    q, k, v = sy.make_qkv(cfg)
+    say("determinism")
+    a = gu.fwd(q, k, v, False, True, None).cpu()
+    b = gu.fwd(q, k, v, False, True, None).cpu()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def test_nan_propagates():
+    cfg = small("n4k", H=1, N=200, M=200)
+    q, k, v = sy.make_qkv(cfg)
+    v = v.copy()
+    v[0, 0, 3, :] = 0x7FC0  # bf16 quiet NaN in one value row
+    say("nan propagation")
+    out = gu.fwd(q, k, v, False, False, None).cpu().numpy()
+    assert np.isnan(out).all(axis=-1).all()
+
+
+def test_sm_scale_argument():
+    cfg = small("n4k", H=1, N=256, M=256)
+    q, k, v = sy.make_qkv(cfg)
+    say("explicit sm_scale")
+    out = gu.fwd(q, k, v, False, False, 0.05).cpu().numpy()[0, 0].astype(np.float64)
+    ref = oracle.forward_head(q[0, 0], k[0, 0], v[0, 0], False, False, 0.05)
+    check_output(out, ref)
+
+
+# ---------------------------------------------------------------- full workload shapes
+FULL = ["n4k", "prefill32k", "video17k"]
+
+
+def sample_rows(N, seed):
+    rng = np.random.default_rng(seed)
+    edge = [0, 1, 127, 128, N // 2, N - 129, N - 128, N - 2, N - 1]
+    rows = sorted(set([r for r in edge if 0 <= r < N] + list(rng.integers(0, N, 24))))
+    return np.array(rows)
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    cfg = sy.CONFIGS[name]
+    q, k, v = sy.make_qkv(cfg)
+    say(f"full-size forward {name} B={cfg.B} H={cfg.H} N={cfg.N} d={cfg.d} causal={cfg.causal}")
+    out = gu.fwd(q, k, v, cfg.fp16, cfg.causal, None, cfg.smooth_v)
+    BH = cfg.B * cfg.H
+    heads = sorted({0, BH - 1, BH // 2})
+    s = 1 / math.sqrt(cfg.d)
+    for bh in heads:
+        b, h = bh // cfg.H, bh % cfg.H
+        rows = sample_rows(cfg.N, 100 + bh)
+        got = out[b, h, torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+        ref = oracle_head(cfg, q, k, v, bh, rows=rows)
+        ex = oracle.exact_head(q[b, h], k[b, h], v[b, h], cfg.fp16, cfg.causal, s, rows=rows)
+        say(f"  head {bh}: max abs {np.abs(got - ref).max():.3g}")
+        check_output(got, ref, ex)
