@@ -56,6 +56,9 @@ typedef enum {
 #define SAGE_IN_FP16    0x0100u
 #define SAGE_OUT_SAME   0x0000u
 #define SAGE_OUT_FP32   0x1000u /* write FP32 output (removes output rounding from checks)    */
+#define SAGE_ACC_VALU   0x2000u /* two-level accumulation in its literal form: each tile's
+                                   P^V^ from a zero MFMA accumulator, added to O by a VALU FMA
+                                   (default: the tile sum enters O through the MFMA C operand) */
 
 /* Tile constants of the method (query smoothing block, key/value tile). */
 #define SAGE_BQ 128

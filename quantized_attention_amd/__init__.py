@@ -17,7 +17,7 @@ import os
 __all__ = [
     "SAGE_OK", "SAGE_ERR_INVALID_ARG", "SAGE_ERR_UNSUPPORTED", "SAGE_ERR_NO_MEMORY",
     "SAGE_ERR_LAUNCH", "SAGE_ERR_DEVICE", "SAGE_PATH_I8F8", "SAGE_SMOOTH_V", "SAGE_IN_BF16",
-    "SAGE_IN_FP16", "SAGE_OUT_SAME", "SAGE_OUT_FP32", "SAGE_BQ", "SAGE_BK", "SageError",
+    "SAGE_IN_FP16", "SAGE_OUT_SAME", "SAGE_OUT_FP32", "SAGE_ACC_VALU", "SAGE_BQ", "SAGE_BK", "SageError",
     "library_path", "load_library", "sage_attn_fwd", "sage_attn_fwd_ws",
     "sage_attn_workspace_bytes", "sage_attn_quantize", "sage_attn_status_string",
     "sage_attn_version", "sage_attn_set_profile_events", "sage_attn", "QuantViews",
@@ -36,6 +36,7 @@ SAGE_IN_BF16 = 0x0000
 SAGE_IN_FP16 = 0x0100
 SAGE_OUT_SAME = 0x0000
 SAGE_OUT_FP32 = 0x1000
+SAGE_ACC_VALU = 0x2000
 
 SAGE_BQ = 128
 SAGE_BK = 64
@@ -128,7 +129,7 @@ def sage_attn_version() -> int:
 
 
 # ---------------------------------------------------------------- torch convenience
-def _variant_for(q, smooth_v: bool, out_fp32: bool) -> int:
+def _variant_for(q, smooth_v: bool, out_fp32: bool, acc_valu: bool = False) -> int:
     import torch
     if q.dtype == torch.bfloat16:
         var = SAGE_IN_BF16
@@ -140,11 +141,13 @@ def _variant_for(q, smooth_v: bool, out_fp32: bool) -> int:
         var |= SAGE_SMOOTH_V
     if out_fp32:
         var |= SAGE_OUT_FP32
+    if acc_valu:
+        var |= SAGE_ACC_VALU
     return var
 
 
 def sage_attn(q, k, v, causal: bool = False, sm_scale: float | None = None, smooth_v: bool = False,
-              out_fp32: bool = False, out=None):
+              out_fp32: bool = False, out=None, acc_valu: bool = False):
     """softmax(Q K^T * sm_scale) V with the quantized method, for [B, H, N, d] tensors.
 
     q: [B, H, N, d], k/v: [B, H, M, d], all the same dtype (bf16/fp16), contiguous, on the
@@ -162,7 +165,7 @@ def sage_attn(q, k, v, causal: bool = False, sm_scale: float | None = None, smoo
     for t in (q, k, v):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous device tensors")
-    var = _variant_for(q, smooth_v, out_fp32)
+    var = _variant_for(q, smooth_v, out_fp32, acc_valu)
     if out is None:
         out = torch.empty((B, H, N, d), dtype=torch.float32 if out_fp32 else q.dtype, device=q.device)
     scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(d)

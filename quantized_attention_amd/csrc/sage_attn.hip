@@ -67,7 +67,7 @@ void carve_workspace(const Problem& p, void* base, Workspace* w) {
 
 namespace {
 
-constexpr unsigned kKnownBits = SAGE_SMOOTH_V | SAGE_IN_FP16 | SAGE_OUT_FP32;
+constexpr unsigned kKnownBits = SAGE_SMOOTH_V | SAGE_IN_FP16 | SAGE_OUT_FP32 | SAGE_ACC_VALU;
 
 // Per-device "is gfx950" cache, filled once per device under a mutex.
 int device_check() {

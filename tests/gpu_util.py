@@ -25,12 +25,13 @@ def doc_kperm(h: int, b: int) -> int:
 INV_PERM = np.array([doc_kperm(p // 32, p % 32) for p in range(64)])
 
 
-def fwd(q, k, v, fp16, causal, sm_scale, smooth_v=False, out_fp32=True):
+def fwd(q, k, v, fp16, causal, sm_scale, smooth_v=False, out_fp32=True, acc_valu=False):
     """q, k, v: uint16 bits [B, H, T, d] on the host; returns the output as a host array."""
     B, H, N, d = q.shape
     M = k.shape[2]
     tq, tk, tv = to_dev(q, fp16), to_dev(k, fp16), to_dev(v, fp16)
-    out = qa.sage_attn(tq, tk, tv, causal=causal, sm_scale=sm_scale, smooth_v=smooth_v, out_fp32=out_fp32)
+    out = qa.sage_attn(tq, tk, tv, causal=causal, sm_scale=sm_scale, smooth_v=smooth_v, out_fp32=out_fp32,
+                       acc_valu=acc_valu)
     torch.cuda.synchronize()
     return out
 

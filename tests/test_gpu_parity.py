@@ -120,6 +120,25 @@ def test_forward_parity_small(name, cfg):
     check_output(g, r, e if cfg.N > 1 else None)
 
 
+@pytest.mark.parametrize("name", ["n4k-ragged", "prefill-causal", "video-smoothv"])
+def test_forward_parity_literal_two_level(name):
+    """The SAGE_ACC_VALU variant (tile sum from a zero accumulator, VALU add into O) meets
+    the same bars, and differs from the default only by FP32 rounding."""
+    cfg = dict(SMALL_CASES)[name]
+    q, k, v = sy.make_qkv(cfg)
+    say(f"forward literal two-level {name}")
+    out = gu.fwd(q, k, v, cfg.fp16, cfg.causal, None, cfg.smooth_v, acc_valu=True).cpu().numpy()
+    dflt = gu.fwd(q, k, v, cfg.fp16, cfg.causal, None, cfg.smooth_v).cpu().numpy()
+    s = 1 / math.sqrt(cfg.d)
+    g = np.stack([out[bh // cfg.H, bh % cfg.H].astype(np.float64) for bh in range(cfg.B * cfg.H)])
+    r = np.stack([oracle_head(cfg, q, k, v, bh) for bh in range(cfg.B * cfg.H)])
+    e = np.stack([oracle.exact_head(q[bh // cfg.H, bh % cfg.H], k[bh // cfg.H, bh % cfg.H],
+                                    v[bh // cfg.H, bh % cfg.H], cfg.fp16, cfg.causal, s)
+                  for bh in range(cfg.B * cfg.H)])
+    check_output(g, r, e)
+    assert np.abs(out - dflt).max() <= 1e-5 * max(1.0, np.abs(dflt).max())
+
+
 def test_output_dtype_is_rounded_fp32():
     cfg = small("n4k", H=2, N=300, M=300)
     q, k, v = sy.make_qkv(cfg)
