@@ -1,8 +1,9 @@
-// preprocess.hip -- smoothing and quantization of Q, K, V (gfx950).
+// preprocess.hip -- smoothing, quantization and the Delta S correction (gfx950).
 //
 // "SageAttention2 Technical Report" summary, 3.4:
 //   * "Smoothing Q": k = mean(K) over all tokens of the head, gamma(K) = K - k; for each
-//     128-query block q_i = mean(Q_i), gamma(Q_i) = Q_i - q_i.
+//     128-query block q_i = mean(Q_i), gamma(Q_i) = Q_i - q_i, and the GEMV correction
+//     Delta S_ij = q_i gamma(K_j)^T added back after dequantization.
 //   * "Per-Thread INT4 Quantization" (here INT8): one scale per thread fragment of the
 //     S^T = K^ Q^T MFMA -- per query token for Q, per 16-key group for K.
 //   * "FP8 Quantization for P~V": dV[c] = max_t |V[t,c]| / 448, V^ = E4M3(V / dV).
@@ -10,223 +11,157 @@
 // "Quantization for Attention, in depth", "Failure modes": means and scales cover valid
 // tokens only.
 //
-// The values are pinned: FP64 sums in a fixed order (64-token chunks in token order, chunk
-// sums in chunk order, one FP64 division, one rounding to FP32), IEEE FP32 division for
-// every scale and code, round-half-even, so Q^, K^, V^, the scales and the means have
-// exactly one correct value.  Every kernel here is HBM-bound; none needs MFMA.
+// Pinned values: FP64 sums in a fixed order (64-token chunks in token order, chunk sums in
+// chunk order, one FP64 division, one rounding to FP32), IEEE FP32 division for every scale
+// and code, round-half-even -- so Q^, K^, V^, the scales and the means have exactly one
+// correct value.  max_t |V' [t,c]| comes from the per-channel max and min of V: FP32
+// subtraction of a fixed V_m is monotone, so max |fp32(V - V_m)| = max(fp32(max V - V_m),
+// fp32(V_m - min V)) exactly, and V is read twice, not three times.
+//
+// Launches (all HBM-bound): kv_stats (K, V chunk statistics) and q_prep (Q blocks) read the
+// inputs once; kv_finalize turns chunk statistics into means and the V scale; kv_quant reads
+// K and V once more and writes K^, V^ and Delta S.  Delta S_i[t] = q_i . gamma(K)[t] for one
+// 64-key tile against every query block is a small GEMM done on the bf16 MFMA with both
+// operands split into a bf16 head and tail (x = hi + lo, exact to 2^-16 relative), three
+// products accumulated in FP32 -- FP32-class accuracy at matrix-core speed.
 #include "sage_common.hpp"
 
 namespace sage {
 namespace {
 
-// ---- K (and V) chunk statistics: one thread per channel, 64 tokens in order ----
-__global__ void k_stats_kernel(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-                               double* __restrict__ kpart, double* __restrict__ vpart,
-                               float* __restrict__ vamax, int M, int d, int nkt, bool fp16,
-                               bool smooth_v) {
-  const int u = blockIdx.x, bh = blockIdx.y, c = threadIdx.x;
-  if (c >= d) return;
-  const size_t base = (size_t)bh * M * d;
-  const int t0 = u * kBK, t1 = min(t0 + kBK, M);
-  double ks = 0.0, vs = 0.0;
-  float va = 0.0f;
-  for (int t = t0; t < t1; t++) {
-    ks += (double)load_in(K, base + (size_t)t * d + c, fp16);
-    float x = load_in(V, base + (size_t)t * d + c, fp16);
-    if (smooth_v)
-      vs += (double)x;
-    else
-      va = amax_upd(va, x);
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// 8 consecutive 16-bit inputs widened to FP32.
+__device__ __forceinline__ void widen8(const v4i& raw, bool fp16, float (&x)[8]) {
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    const uint32_t u = static_cast<uint32_t>(raw[e]);
+    const uint16_t lo = static_cast<uint16_t>(u & 0xffffu), hi = static_cast<uint16_t>(u >> 16);
+    if (fp16) {
+      x[2 * e] = static_cast<float>(__builtin_bit_cast(_Float16, lo));
+      x[2 * e + 1] = static_cast<float>(__builtin_bit_cast(_Float16, hi));
+    } else {
+      x[2 * e] = __uint_as_float(u << 16);
+      x[2 * e + 1] = __uint_as_float(u & 0xffff0000u);
+    }
   }
-  const size_t o = ((size_t)bh * nkt + u) * d + c;
-  kpart[o] = ks;
-  if (smooth_v)
-    vpart[o] = vs;
-  else
-    vamax[o] = va;
 }
 
-// ---- chunk sums -> means (and the V scale when V is not smoothed) ----
-__global__ void k_finalize_kernel(const double* __restrict__ kpart, const double* __restrict__ vpart,
-                                  const float* __restrict__ vamax, float* __restrict__ kmean,
-                                  float* __restrict__ vmean, float* __restrict__ dv, int M, int d,
-                                  int nkt, bool smooth_v) {
+// ---- K and V chunk statistics: tile staged in LDS with 16-byte loads; one thread per
+// channel adds the chunk's tokens in order (FP64); V max / min (and sum when smoothing) ----
+template <int D>
+__global__ __launch_bounds__(256) void kv_stats_kernel(const uint16_t* __restrict__ K,
+                                                       const uint16_t* __restrict__ V,
+                                                       double* __restrict__ kpart, double* __restrict__ vpart,
+                                                       float* __restrict__ vmaxp, float* __restrict__ vminp,
+                                                       int M, int nkt, bool fp16, bool smooth_v) {
+  constexpr int RS = D + 8;  // LDS row stride (16-bit elements), 16-byte aligned rows
+  __shared__ __attribute__((aligned(16))) uint16_t sk[kBK * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t sv[kBK * RS];
+  const int u = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int t0 = u * kBK, n = min(kBK, M - t0);
+  const size_t base = ((size_t)bh * M + t0) * D;
+#pragma unroll
+  for (int i = 0; i < kBK * D / 8 / 256; i++) {
+    const int x = tid + 256 * i, row = x / (D / 8), c0 = (x % (D / 8)) * 8;
+    if (row < n) {
+      *reinterpret_cast<v4i*>(&sk[row * RS + c0]) = *reinterpret_cast<const v4i*>(K + base + (size_t)row * D + c0);
+      *reinterpret_cast<v4i*>(&sv[row * RS + c0]) = *reinterpret_cast<const v4i*>(V + base + (size_t)row * D + c0);
+    }
+  }
+  __syncthreads();
+  const size_t o = ((size_t)bh * nkt + u) * D;
+  if (tid < D) {
+    double s = 0.0;
+    for (int t = 0; t < n; t++) s += (double)load_in(sk, (size_t)t * RS + tid, fp16);
+    kpart[o + tid] = s;
+  } else if (tid >= 128 && tid - 128 < D) {
+    const int c = tid - 128;
+    double s = 0.0;
+    float mx = -INFINITY, mn = INFINITY;
+    for (int t = 0; t < n; t++) {
+      const float x = load_in(sv, (size_t)t * RS + c, fp16);
+      if (smooth_v) s += (double)x;
+      mx = x > mx ? x : mx;  // NaN ignored
+      mn = x < mn ? x : mn;
+    }
+    if (smooth_v) vpart[o + c] = s;
+    vmaxp[o + c] = mx;
+    vminp[o + c] = mn;
+  }
+}
+
+// ---- chunk statistics -> k mean, V_m (when smoothing) and the V scale ----
+__global__ void kv_finalize_kernel(const double* __restrict__ kpart, const double* __restrict__ vpart,
+                                   const float* __restrict__ vmaxp, const float* __restrict__ vminp,
+                                   float* __restrict__ kmean, float* __restrict__ vmean, float* __restrict__ dv,
+                                   int M, int d, int nkt, bool smooth_v) {
   const int bh = blockIdx.x, c = threadIdx.x;
   if (c >= d) return;
+  constexpr int U = 8;  // loads in flight; the sums themselves stay in chunk order
   double ks = 0.0, vs = 0.0;
-  float va = 0.0f;
-  for (int u = 0; u < nkt; u++) {
-    const size_t o = ((size_t)bh * nkt + u) * d + c;
-    ks += kpart[o];
-    if (smooth_v)
-      vs += vpart[o];
-    else
-      va = va > vamax[o] ? va : vamax[o];
+  float mx = -INFINITY, mn = INFINITY;
+  for (int u0 = 0; u0 < nkt; u0 += U) {
+    double kb[U], vb[U];
+    float xb[U], nb[U];
+#pragma unroll
+    for (int i = 0; i < U; i++) {
+      const size_t o = ((size_t)bh * nkt + min(u0 + i, nkt - 1)) * d + c;
+      kb[i] = kpart[o];
+      vb[i] = smooth_v ? vpart[o] : 0.0;
+      xb[i] = vmaxp[o];
+      nb[i] = vminp[o];
+    }
+#pragma unroll
+    for (int i = 0; i < U; i++) {
+      if (u0 + i < nkt) {
+        ks += kb[i];
+        if (smooth_v) vs += vb[i];
+        mx = xb[i] > mx ? xb[i] : mx;
+        mn = nb[i] < mn ? nb[i] : mn;
+      }
+    }
   }
   kmean[(size_t)bh * d + c] = (float)(ks / (double)M);
-  if (smooth_v) {
-    vmean[(size_t)bh * d + c] = (float)(vs / (double)M);
-  } else {
-    vmean[(size_t)bh * d + c] = 0.0f;
-    float a = va > 1e-8f ? va : 1e-8f;
-    dv[(size_t)bh * d + c] = __fdiv_rn(a, 448.0f);
-  }
-}
-
-// ---- K: gamma(K), per-group scale, INT8 codes; V' chunk max when V is smoothed ----
-// 256 threads, one 64-key tile.  Each thread owns 4 consecutive channels of a key.
-template <int D>
-__global__ __launch_bounds__(256) void k_quant_kernel(const uint16_t* __restrict__ K,
-                                                      const uint16_t* __restrict__ V,
-                                                      const float* __restrict__ kmean,
-                                                      const float* __restrict__ vmean,
-                                                      int8_t* __restrict__ khat, float* __restrict__ dk,
-                                                      float* __restrict__ vamax, int M, int Mp, int nkt,
-                                                      bool fp16, bool smooth_v) {
-  constexpr int QUADS = kBK * D / 4;          // 4-channel groups in the tile
-  constexpr int PER = QUADS / 256;            // per thread
-  __shared__ float gmax[4][4];                // [group][wave]
-  __shared__ float sdk[4];
-  const int u = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const size_t in_base = (size_t)bh * M * D;
-  const float* km = kmean + (size_t)bh * D;
-  float g[PER][4];
-  float am[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < PER; i++) {
-    const int qd = tid + 256 * i;
-    const int t = qd / (D / 4), c0 = (qd % (D / 4)) * 4;
-    const int key = u * kBK + t;
-    const int grp = kgroup(t);
-#pragma unroll
-    for (int e = 0; e < 4; e++) {
-      float x = 0.0f;
-      if (key < M) x = load_in(K, in_base + (size_t)key * D + c0 + e, fp16) - km[c0 + e];
-      g[i][e] = x;
-      // group index is a runtime value; update all four under a select
-#pragma unroll
-      for (int q = 0; q < 4; q++)
-        if (q == grp) am[q] = amax_upd(am[q], x);
-    }
-  }
-  // wave reduction of the four maxima, then across the four waves (max is exact)
-#pragma unroll
-  for (int q = 0; q < 4; q++) {
-    float m = am[q];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      float o = __shfl_xor(m, off);
-      m = o > m ? o : m;
-    }
-    if (lane == 0) gmax[q][wave] = m;
-  }
-  __syncthreads();
-  if (tid < 4) {
-    float m = gmax[tid][0];
-    for (int w = 1; w < 4; w++) m = gmax[tid][w] > m ? gmax[tid][w] : m;
-    const float s = int8_scale(m);
-    sdk[tid] = s;
-    dk[((size_t)bh * nkt + u) * 4 + tid] = s;
-  }
-  __syncthreads();
-  int8_t* kout = khat + ((size_t)bh * Mp + (size_t)u * kBK) * D;
-#pragma unroll
-  for (int i = 0; i < PER; i++) {
-    const int qd = tid + 256 * i;
-    const int t = qd / (D / 4), c0 = (qd % (D / 4)) * 4;
-    const int key = u * kBK + t;
-    const float s = sdk[kgroup(t)];
-    uint32_t word = 0;
-    if (key < M) {
-#pragma unroll
-      for (int e = 0; e < 4; e++) word |= (uint32_t)(uint8_t)int8_code(g[i][e], s) << (8 * e);
-    }
-    *reinterpret_cast<uint32_t*>(kout + (size_t)t * D + c0) = word;
-  }
-  if (smooth_v && tid < D) {
-    const float vm = vmean[(size_t)bh * D + tid];
-    float va = 0.0f;
-    for (int t = u * kBK; t < min(u * kBK + kBK, M); t++)
-      va = amax_upd(va, load_in(V, in_base + (size_t)t * D + tid, fp16) - vm);
-    vamax[((size_t)bh * nkt + u) * D + tid] = va;
-  }
-}
-
-// ---- V scale after smoothing: max over the chunk maxima ----
-__global__ void v_scale_kernel(const float* __restrict__ vamax, float* __restrict__ dv, int d, int nkt) {
-  const int bh = blockIdx.x, c = threadIdx.x;
-  if (c >= d) return;
-  float va = 0.0f;
-  for (int u = 0; u < nkt; u++) {
-    const float x = vamax[((size_t)bh * nkt + u) * d + c];
-    va = va > x ? va : x;
-  }
-  const float a = va > 1e-8f ? va : 1e-8f;
+  const float vm = smooth_v ? (float)(vs / (double)M) : 0.0f;
+  vmean[(size_t)bh * d + c] = vm;
+  const float a1 = mx - vm, a2 = vm - mn;  // max |fp32(V - V_m)| over the tokens
+  const float am = a1 > a2 ? a1 : a2;
+  const float a = am > 1e-8f ? am : 1e-8f;
   dv[(size_t)bh * d + c] = __fdiv_rn(a, 448.0f);
 }
 
-// ---- V: E4M3 codes, transposed per tile with the P-fragment key order ----
-template <int D>
-__global__ __launch_bounds__(256) void v_quant_kernel(const uint16_t* __restrict__ V,
-                                                      const float* __restrict__ vmean,
-                                                      const float* __restrict__ dv,
-                                                      uint8_t* __restrict__ vhat, int M, int nkt,
-                                                      bool fp16) {
-  __shared__ float sv[kBK][D + 1];
-  const int u = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  const size_t in_base = (size_t)bh * M * D;
-  const float* vm = vmean + (size_t)bh * D;
-  const float* sc = dv + (size_t)bh * D;
-  // coalesced load of the tile: V' = V - V_m (FP32), then V' / dV (IEEE division)
-  for (int x = tid; x < kBK * D; x += 256) {
-    const int t = x / D, c = x % D;
-    const int key = u * kBK + t;
-    float y = 0.0f;
-    if (key < M) {
-      const float vp = load_in(V, in_base + (size_t)key * D + c, fp16) - vm[c];
-      y = __fdiv_rn(vp, sc[c]);
-      // saturate to the E4M3 range (the conversion itself does not); NaN stays NaN
-      y = y > 448.0f ? 448.0f : (y < -448.0f ? -448.0f : y);
-    }
-    sv[t][c] = y;
-  }
-  __syncthreads();
-  // each thread writes 4-byte words: channel c, bytes p0..p0+3 of its 64-byte row
-  uint8_t* vout = vhat + ((size_t)bh * nkt + u) * (size_t)D * kBK;
-  for (int x = tid; x < D * (kBK / 4); x += 256) {
-    const int c = x / (kBK / 4), p0 = (x % (kBK / 4)) * 4;
-    const int h = p0 >> 5, b0 = p0 & 31;
-    int w = 0;
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(sv[kperm(h, b0)][c], sv[kperm(h, b0 + 1)][c], w, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(sv[kperm(h, b0 + 2)][c], sv[kperm(h, b0 + 3)][c], w, true);
-    *reinterpret_cast<int*>(vout + (size_t)c * kBK + p0) = w;
-  }
-}
-
-// ---- Q: block mean, gamma(Q), per-token scale, INT8 codes ----
+// ---- Q: block mean (and its bf16 head/tail), gamma(Q), per-token scale, INT8 codes ----
 template <int D>
 __global__ __launch_bounds__(256) void q_prep_kernel(const uint16_t* __restrict__ Q,
                                                      int8_t* __restrict__ qhat, float* __restrict__ dq,
-                                                     float* __restrict__ qmean, int N, int Np, int nqb,
+                                                     float* __restrict__ qmean, uint16_t* __restrict__ qm_hi,
+                                                     uint16_t* __restrict__ qm_lo, int N, int Np, int nqb,
                                                      bool fp16) {
-  __shared__ uint16_t sq[kBQ][D + 2];  // raw 16-bit inputs of the block
+  constexpr int RS = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t sq[kBQ * RS];
   __shared__ float sm[D];
   const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int r0 = i * kBQ, n = min(kBQ, N - r0);
-  const size_t in_base = (size_t)bh * N * D;
-  for (int x = tid; x < kBQ * D; x += 256) {
-    const int r = x / D, c = x % D;
-    sq[r][c] = (r < n) ? Q[in_base + (size_t)(r0 + r) * D + c] : (uint16_t)0;
+  const size_t in_base = ((size_t)bh * N + r0) * D;
+#pragma unroll
+  for (int k = 0; k < kBQ * D / 8 / 256; k++) {
+    const int x = tid + 256 * k, r = x / (D / 8), c0 = (x % (D / 8)) * 8;
+    if (r < n)
+      *reinterpret_cast<v4i*>(&sq[r * RS + c0]) = *reinterpret_cast<const v4i*>(Q + in_base + (size_t)r * D + c0);
   }
   __syncthreads();
   if (tid < D) {
     double s = 0.0;  // rows in order, FP64
-    for (int r = 0; r < n; r++) s += (double)load_in(&sq[r][0], tid, fp16);
+    for (int r = 0; r < n; r++) s += (double)load_in(sq, (size_t)r * RS + tid, fp16);
     const float m = (float)(s / (double)n);
     sm[tid] = m;
-    qmean[((size_t)bh * nqb + i) * D + tid] = m;
+    const size_t o = ((size_t)bh * nqb + i) * D + tid;
+    qmean[o] = m;
+    const uint16_t hb = bf16_rn(m);
+    qm_hi[o] = hb;
+    qm_lo[o] = bf16_rn(m - bf16_val(hb));
   }
   __syncthreads();
   // each wave takes 32 rows; a lane holds D/64 channels of the row
@@ -238,7 +173,7 @@ __global__ __launch_bounds__(256) void q_prep_kernel(const uint16_t* __restrict_
 #pragma unroll
     for (int e = 0; e < CPL; e++) {
       const int c = lane * CPL + e;
-      g[e] = (r < n) ? load_in(&sq[r][0], c, fp16) - sm[c] : 0.0f;
+      g[e] = (r < n) ? load_in(sq, (size_t)r * RS + c, fp16) - sm[c] : 0.0f;
       am = amax_upd(am, g[e]);
     }
 #pragma unroll
@@ -260,55 +195,241 @@ __global__ __launch_bounds__(256) void q_prep_kernel(const uint16_t* __restrict_
   }
 }
 
+struct KVArgs {
+  const uint16_t* K;
+  const uint16_t* V;
+  const float* kmean;
+  const float* vmean;
+  const float* dv;
+  const uint16_t* qm_hi;
+  const uint16_t* qm_lo;
+  int8_t* khat;
+  float* dk;
+  uint8_t* vhat;
+  float* ds;  // null: no Delta S
+  float ds_scale;
+  int M, Mp, nkt, nqb, causal;
+  bool fp16;
+};
+
+// ---- one 64-key tile: gamma(K), group scales, K^; Delta S against every query block;
+// V' / dV -> E4M3, transposed in the P-fragment key order ----
+template <int D>
+__global__ __launch_bounds__(256) void kv_quant_kernel(KVArgs a) {
+  constexpr int RS = D + 8;                 // bf16 split of gamma(K), 16-byte aligned rows
+  constexpr int CH = kBK * D / 8 / 256;     // 8-element chunks per thread
+  __shared__ __attribute__((aligned(16))) uint16_t sAh[kBK * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t sAl[kBK * RS];
+  __shared__ float sv[kBK][D + 1];
+  __shared__ float gmax[4][4];
+  __shared__ float sdk[4];
+  const int u = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int t0 = u * kBK, n = min(kBK, a.M - t0);
+  const size_t in_base = ((size_t)bh * a.M + t0) * D;
+  const float* km = a.kmean + (size_t)bh * D;
+
+  // ---- gamma(K) = K - k (FP32), its bf16 split into LDS, group maxima ----
+  float g[CH][8];
+  float am[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < CH; i++) {
+    const int x = tid + 256 * i, row = x / (D / 8), c0 = (x % (D / 8)) * 8;
+    if (row < n) {
+      float w[8];
+      widen8(*reinterpret_cast<const v4i*>(a.K + in_base + (size_t)row * D + c0), a.fp16, w);
+#pragma unroll
+      for (int e = 0; e < 8; e++) g[i][e] = w[e] - km[c0 + e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; e++) g[i][e] = 0.0f;
+    }
+    const int grp = kgroup(row);
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; e++) m = amax_upd(m, g[i][e]);
+#pragma unroll
+    for (int q = 0; q < 4; q++)
+      if (q == grp) am[q] = m > am[q] ? m : am[q];
+    v4i hv, lv;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const uint16_t h0 = bf16_rn(g[i][2 * e]), h1 = bf16_rn(g[i][2 * e + 1]);
+      const uint16_t l0 = bf16_rn(g[i][2 * e] - bf16_val(h0)), l1 = bf16_rn(g[i][2 * e + 1] - bf16_val(h1));
+      hv[e] = (int)((uint32_t)h0 | ((uint32_t)h1 << 16));
+      lv[e] = (int)((uint32_t)l0 | ((uint32_t)l1 << 16));
+    }
+    *reinterpret_cast<v4i*>(&sAh[row * RS + c0]) = hv;
+    *reinterpret_cast<v4i*>(&sAl[row * RS + c0]) = lv;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; q++) {
+    float m = am[q];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float o = __shfl_xor(m, off);
+      m = o > m ? o : m;
+    }
+    if (lane == 0) gmax[q][wave] = m;
+  }
+  __syncthreads();
+  if (tid < 4) {
+    float m = gmax[tid][0];
+    for (int w = 1; w < 4; w++) m = gmax[tid][w] > m ? gmax[tid][w] : m;
+    const float s = int8_scale(m);
+    sdk[tid] = s;
+    a.dk[((size_t)bh * a.nkt + u) * 4 + tid] = s;
+  }
+  __syncthreads();
+
+  // ---- K^ codes (keys >= M stay 0) ----
+  {
+    int8_t* kout = a.khat + ((size_t)bh * a.Mp + t0) * D;
+#pragma unroll
+    for (int i = 0; i < CH; i++) {
+      const int x = tid + 256 * i, row = x / (D / 8), c0 = (x % (D / 8)) * 8;
+      const float s = sdk[kgroup(row)];
+      uint32_t w0 = 0, w1 = 0;
+      if (row < n) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          w0 |= (uint32_t)(uint8_t)int8_code(g[i][e], s) << (8 * e);
+          w1 |= (uint32_t)(uint8_t)int8_code(g[i][4 + e], s) << (8 * e);
+        }
+      }
+      *reinterpret_cast<uint2*>(kout + (size_t)row * D + c0) = make_uint2(w0, w1);
+    }
+  }
+
+  // ---- Delta S^T[key][block] = gamma(K) q^T on the bf16 MFMA, split operands ----
+  if (a.ds) {
+    const int h = lane >> 5, col = lane & 31;
+    const int T = wave & 1;
+    const int ilo = a.causal ? u / 2 : 0;  // block i needs keys < 128 (i + 1)
+    for (int gidx = wave >> 1; 32 * gidx < a.nqb; gidx += 2) {
+      if (32 * gidx + 31 < ilo) continue;
+      const int blk = 32 * gidx + col;
+      const bool bv = blk < a.nqb;
+      v16f acc;
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[r] = 0.0f;
+      const size_t qo = ((size_t)bh * a.nqb + (bv ? blk : 0)) * D;
+#pragma unroll
+      for (int s = 0; s < D / 16; s++) {
+        const v8bf ah = *reinterpret_cast<const v8bf*>(&sAh[(32 * T + col) * RS + 16 * s + 8 * h]);
+        const v8bf al = *reinterpret_cast<const v8bf*>(&sAl[(32 * T + col) * RS + 16 * s + 8 * h]);
+        v8bf bq = *reinterpret_cast<const v8bf*>(a.qm_hi + qo + 16 * s + 8 * h);
+        v8bf bl = *reinterpret_cast<const v8bf*>(a.qm_lo + qo + 16 * s + 8 * h);
+        if (!bv) {
+          bq = v8bf{};
+          bl = v8bf{};
+        }
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bq, acc, 0, 0, 0);  // small terms first
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bq, acc, 0, 0, 0);
+      }
+      if (bv && blk >= ilo) {
+        float* dst = a.ds + ((size_t)bh * a.nqb + blk) * a.Mp + t0 + 32 * T + 4 * h;
+#pragma unroll
+        for (int b = 0; b < 4; b++)
+          *reinterpret_cast<float4*>(dst + 8 * b) =
+              make_float4(acc[4 * b] * a.ds_scale, acc[4 * b + 1] * a.ds_scale, acc[4 * b + 2] * a.ds_scale,
+                          acc[4 * b + 3] * a.ds_scale);
+      }
+    }
+  }
+
+  // ---- V: V' / dV (IEEE division), saturated to the E4M3 range, staged in LDS ----
+  {
+    const float* vm = a.vmean + (size_t)bh * D;
+    const float* sc = a.dv + (size_t)bh * D;
+#pragma unroll
+    for (int i = 0; i < CH; i++) {
+      const int x = tid + 256 * i, row = x / (D / 8), c0 = (x % (D / 8)) * 8;
+      float w[8];
+      if (row < n) {
+        widen8(*reinterpret_cast<const v4i*>(a.V + in_base + (size_t)row * D + c0), a.fp16, w);
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          float y = __fdiv_rn(w[e] - vm[c0 + e], sc[c0 + e]);
+          y = y > 448.0f ? 448.0f : (y < -448.0f ? -448.0f : y);  // NaN stays NaN
+          w[e] = y;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; e++) w[e] = 0.0f;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; e++) sv[row][c0 + e] = w[e];
+    }
+  }
+  __syncthreads();
+  uint8_t* vout = a.vhat + ((size_t)bh * a.nkt + u) * (size_t)D * kBK;
+  for (int x = tid; x < D * (kBK / 4); x += 256) {
+    const int c = x / (kBK / 4), p0 = (x % (kBK / 4)) * 4;
+    const int h = p0 >> 5, b0 = p0 & 31;
+    int wd = __builtin_amdgcn_cvt_pk_fp8_f32(sv[kperm(h, b0)][c], sv[kperm(h, b0 + 1)][c], 0, false);
+    wd = __builtin_amdgcn_cvt_pk_fp8_f32(sv[kperm(h, b0 + 2)][c], sv[kperm(h, b0 + 3)][c], wd, true);
+    *reinterpret_cast<int*>(vout + (size_t)c * kBK + p0) = wd;
+  }
+}
+
 }  // namespace
 
-hipError_t launch_k_stats(const Problem& p, const void* k, const void* v, const Workspace& w, hipStream_t s) {
-  hipLaunchKernelGGL(k_stats_kernel, dim3(p.nkt, p.BH), dim3(p.d), 0, s,
-                     (const uint16_t*)k, (const uint16_t*)v, w.kpart, w.vpart, w.vamax, p.M, p.d,
-                     p.nkt, p.fp16, p.smooth_v);
+hipError_t launch_kv_stats(const Problem& p, const void* k, const void* v, const Workspace& w, hipStream_t s) {
+  const dim3 grid(p.nkt, p.BH);
+  if (p.d == 128)
+    hipLaunchKernelGGL(kv_stats_kernel<128>, grid, dim3(256), 0, s, (const uint16_t*)k, (const uint16_t*)v,
+                       w.kpart, w.vpart, w.vmaxp, w.vminp, p.M, p.nkt, p.fp16, p.smooth_v);
+  else
+    hipLaunchKernelGGL(kv_stats_kernel<64>, grid, dim3(256), 0, s, (const uint16_t*)k, (const uint16_t*)v,
+                       w.kpart, w.vpart, w.vmaxp, w.vminp, p.M, p.nkt, p.fp16, p.smooth_v);
   return hipGetLastError();
 }
 
-hipError_t launch_k_finalize(const Problem& p, const Workspace& w, hipStream_t s) {
-  hipLaunchKernelGGL(k_finalize_kernel, dim3(p.BH), dim3(p.d), 0, s, w.kpart, w.vpart, w.vamax,
+hipError_t launch_kv_finalize(const Problem& p, const Workspace& w, hipStream_t s) {
+  hipLaunchKernelGGL(kv_finalize_kernel, dim3(p.BH), dim3(p.d), 0, s, w.kpart, w.vpart, w.vmaxp, w.vminp,
                      w.kmean, w.vmean, w.dv, p.M, p.d, p.nkt, p.smooth_v);
   return hipGetLastError();
 }
 
-hipError_t launch_k_quant(const Problem& p, const void* k, const void* v, const Workspace& w, hipStream_t s) {
-  if (p.d == 128)
-    hipLaunchKernelGGL(k_quant_kernel<128>, dim3(p.nkt, p.BH), dim3(256), 0, s, (const uint16_t*)k,
-                       (const uint16_t*)v, w.kmean, w.vmean, w.khat, w.dk, w.vamax, p.M, p.Mp, p.nkt,
-                       p.fp16, p.smooth_v);
-  else
-    hipLaunchKernelGGL(k_quant_kernel<64>, dim3(p.nkt, p.BH), dim3(256), 0, s, (const uint16_t*)k,
-                       (const uint16_t*)v, w.kmean, w.vmean, w.khat, w.dk, w.vamax, p.M, p.Mp, p.nkt,
-                       p.fp16, p.smooth_v);
-  return hipGetLastError();
-}
-
-hipError_t launch_v_scale(const Problem& p, const Workspace& w, hipStream_t s) {
-  hipLaunchKernelGGL(v_scale_kernel, dim3(p.BH), dim3(p.d), 0, s, w.vamax, w.dv, p.d, p.nkt);
-  return hipGetLastError();
-}
-
-hipError_t launch_v_quant(const Problem& p, const void* v, const Workspace& w, hipStream_t s) {
-  if (p.d == 128)
-    hipLaunchKernelGGL(v_quant_kernel<128>, dim3(p.nkt, p.BH), dim3(256), 0, s, (const uint16_t*)v,
-                       w.vmean, w.dv, w.vhat, p.M, p.nkt, p.fp16);
-  else
-    hipLaunchKernelGGL(v_quant_kernel<64>, dim3(p.nkt, p.BH), dim3(256), 0, s, (const uint16_t*)v,
-                       w.vmean, w.dv, w.vhat, p.M, p.nkt, p.fp16);
-  return hipGetLastError();
-}
-
 hipError_t launch_q_prep(const Problem& p, const void* q, const Workspace& w, hipStream_t s) {
+  const dim3 grid(p.nqb, p.BH);
   if (p.d == 128)
-    hipLaunchKernelGGL(q_prep_kernel<128>, dim3(p.nqb, p.BH), dim3(256), 0, s, (const uint16_t*)q,
-                       w.qhat, w.dq, w.qmean, p.N, p.Np, p.nqb, p.fp16);
+    hipLaunchKernelGGL(q_prep_kernel<128>, grid, dim3(256), 0, s, (const uint16_t*)q, w.qhat, w.dq, w.qmean,
+                       w.qm_hi, w.qm_lo, p.N, p.Np, p.nqb, p.fp16);
   else
-    hipLaunchKernelGGL(q_prep_kernel<64>, dim3(p.nqb, p.BH), dim3(256), 0, s, (const uint16_t*)q,
-                       w.qhat, w.dq, w.qmean, p.N, p.Np, p.nqb, p.fp16);
+    hipLaunchKernelGGL(q_prep_kernel<64>, grid, dim3(256), 0, s, (const uint16_t*)q, w.qhat, w.dq, w.qmean,
+                       w.qm_hi, w.qm_lo, p.N, p.Np, p.nqb, p.fp16);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_quant(const Problem& p, const void* k, const void* v, const Workspace& w,
+                           float ds_scale, float* ds_out, hipStream_t s) {
+  KVArgs a;
+  a.K = (const uint16_t*)k;
+  a.V = (const uint16_t*)v;
+  a.kmean = w.kmean;
+  a.vmean = w.vmean;
+  a.dv = w.dv;
+  a.qm_hi = w.qm_hi;
+  a.qm_lo = w.qm_lo;
+  a.khat = w.khat;
+  a.dk = w.dk;
+  a.vhat = w.vhat;
+  a.ds = ds_out;
+  a.ds_scale = ds_scale;
+  a.M = p.M;
+  a.Mp = p.Mp;
+  a.nkt = p.nkt;
+  a.nqb = p.nqb;
+  a.causal = p.causal;
+  a.fp16 = p.fp16;
+  const dim3 grid(p.nkt, p.BH);
+  if (p.d == 128)
+    hipLaunchKernelGGL(kv_quant_kernel<128>, grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(kv_quant_kernel<64>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -19,22 +19,25 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t workspace_layout(const Problem& p, size_t* sizes) {
   const size_t BH = (size_t)p.BH, d = (size_t)p.d;
-  size_t s[13];
-  s[0] = BH * p.Np * d;                      // qhat
-  s[1] = BH * p.Mp * d;                      // khat
-  s[2] = BH * p.nkt * d * kBK;               // vhat
-  s[3] = BH * p.Np * sizeof(float);          // dq
-  s[4] = BH * p.nkt * 4 * sizeof(float);     // dk
-  s[5] = BH * d * sizeof(float);             // dv
-  s[6] = BH * d * sizeof(float);             // kmean
-  s[7] = BH * d * sizeof(float);             // vmean
-  s[8] = BH * p.nqb * d * sizeof(float);     // qmean
+  size_t s[kWsSlices];
+  s[0] = BH * p.Np * d;                              // qhat
+  s[1] = BH * p.Mp * d;                              // khat
+  s[2] = BH * p.nkt * d * kBK;                       // vhat
+  s[3] = BH * p.Np * sizeof(float);                  // dq
+  s[4] = BH * p.nkt * 4 * sizeof(float);             // dk
+  s[5] = BH * d * sizeof(float);                     // dv
+  s[6] = BH * d * sizeof(float);                     // kmean
+  s[7] = BH * d * sizeof(float);                     // vmean
+  s[8] = BH * p.nqb * d * sizeof(float);             // qmean
   s[9] = BH * p.nqb * (size_t)p.Mp * sizeof(float);  // ds
-  s[10] = BH * p.nkt * d * sizeof(double);   // kpart
-  s[11] = BH * p.nkt * d * sizeof(double);   // vpart
-  s[12] = BH * p.nkt * d * sizeof(float);    // vamax
+  s[10] = BH * p.nkt * d * sizeof(double);           // kpart
+  s[11] = BH * p.nkt * d * sizeof(double);           // vpart
+  s[12] = BH * p.nkt * d * sizeof(float);            // vmaxp
+  s[13] = BH * p.nkt * d * sizeof(float);            // vminp
+  s[14] = BH * p.nqb * d * sizeof(uint16_t);         // qm_hi
+  s[15] = BH * p.nqb * d * sizeof(uint16_t);         // qm_lo
   size_t tot = 0;
-  for (int i = 0; i < 13; i++) {
+  for (int i = 0; i < kWsSlices; i++) {
     if (sizes) sizes[i] = s[i];
     tot += align256(s[i]);
   }
@@ -42,11 +45,11 @@ size_t workspace_layout(const Problem& p, size_t* sizes) {
 }
 
 void carve_workspace(const Problem& p, void* base, Workspace* w) {
-  size_t s[13];
+  size_t s[kWsSlices];
   workspace_layout(p, s);
   char* b = static_cast<char*>(base);
-  void* ptr[13];
-  for (int i = 0; i < 13; i++) {
+  void* ptr[kWsSlices];
+  for (int i = 0; i < kWsSlices; i++) {
     ptr[i] = b;
     b += align256(s[i]);
   }
@@ -62,7 +65,10 @@ void carve_workspace(const Problem& p, void* base, Workspace* w) {
   w->ds = (float*)ptr[9];
   w->kpart = (double*)ptr[10];
   w->vpart = (double*)ptr[11];
-  w->vamax = (float*)ptr[12];
+  w->vmaxp = (float*)ptr[12];
+  w->vminp = (float*)ptr[13];
+  w->qm_hi = (uint16_t*)ptr[14];
+  w->qm_lo = (uint16_t*)ptr[15];
 }
 
 namespace {
@@ -121,13 +127,10 @@ bool aligned16(const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) ==
 // The preprocessing launches; ds goes to ds_out scaled by ds_scale.
 int run_preprocess(const Problem& p, const void* q, const void* k, const void* v, const Workspace& w,
                    float ds_scale, float* ds_out, hipStream_t s) {
-  if (launch_k_stats(p, k, v, w, s) != hipSuccess) return SAGE_ERR_LAUNCH;
-  if (launch_k_finalize(p, w, s) != hipSuccess) return SAGE_ERR_LAUNCH;
-  if (launch_k_quant(p, k, v, w, s) != hipSuccess) return SAGE_ERR_LAUNCH;
-  if (p.smooth_v && launch_v_scale(p, w, s) != hipSuccess) return SAGE_ERR_LAUNCH;
-  if (launch_v_quant(p, v, w, s) != hipSuccess) return SAGE_ERR_LAUNCH;
+  if (launch_kv_stats(p, k, v, w, s) != hipSuccess) return SAGE_ERR_LAUNCH;
   if (launch_q_prep(p, q, w, s) != hipSuccess) return SAGE_ERR_LAUNCH;
-  if (ds_out && launch_delta_s(p, k, w, ds_scale, ds_out, s) != hipSuccess) return SAGE_ERR_LAUNCH;
+  if (launch_kv_finalize(p, w, s) != hipSuccess) return SAGE_ERR_LAUNCH;
+  if (launch_kv_quant(p, k, v, w, ds_scale, ds_out, s) != hipSuccess) return SAGE_ERR_LAUNCH;
   return SAGE_OK;
 }
 
@@ -215,7 +218,7 @@ int sage_attn_quantize(const void* q, const void* k, const void* v, int B, int H
   Workspace w;
   carve_workspace(p, ws, &w);
   rc = run_preprocess(p, q, k, v, w, 1.0f, dst->delta_s, s);
-  size_t sz[13];
+  size_t sz[kWsSlices];
   workspace_layout(p, sz);
   struct Copy { void* dst; const void* src; size_t n; } copies[] = {
       {dst->q_hat, w.qhat, sz[0]}, {dst->k_hat, w.khat, sz[1]}, {dst->v_hat, w.vhat, sz[2]},

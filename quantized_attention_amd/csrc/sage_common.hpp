@@ -33,23 +33,27 @@ struct Problem {
 
 // Device workspace (all 256-byte aligned slices of one allocation).
 struct Workspace {
-  int8_t* qhat;    // [BH][Np][d]
-  int8_t* khat;    // [BH][Mp][d]
-  uint8_t* vhat;   // [BH][nkt][d][64], keys permuted (see sage_attn.h)
-  float* dq;       // [BH][Np]
-  float* dk;       // [BH][nkt][4]
-  float* dv;       // [BH][d]
-  float* kmean;    // [BH][d]
-  float* vmean;    // [BH][d]
-  float* qmean;    // [BH][nqb][d]
-  float* ds;       // [BH][nqb][Mp], Delta S (pre-multiplied by ds_scale)
-  double* kpart;   // [BH][nkt][d] FP64 chunk sums of K
-  double* vpart;   // [BH][nkt][d] FP64 chunk sums of V (V smoothing)
-  float* vamax;    // [BH][nkt][d] chunk max |V| (or |V'|)
+  int8_t* qhat;     // [BH][Np][d]
+  int8_t* khat;     // [BH][Mp][d]
+  uint8_t* vhat;    // [BH][nkt][d][64], keys permuted (see sage_attn.h)
+  float* dq;        // [BH][Np]
+  float* dk;        // [BH][nkt][4]
+  float* dv;        // [BH][d]
+  float* kmean;     // [BH][d]
+  float* vmean;     // [BH][d]
+  float* qmean;     // [BH][nqb][d]
+  float* ds;        // [BH][nqb][Mp], Delta S (pre-multiplied by ds_scale)
+  double* kpart;    // [BH][nkt][d] FP64 chunk sums of K
+  double* vpart;    // [BH][nkt][d] FP64 chunk sums of V (V smoothing)
+  float* vmaxp;     // [BH][nkt][d] chunk max of V
+  float* vminp;     // [BH][nkt][d] chunk min of V
+  uint16_t* qm_hi;  // [BH][nqb][d] bf16 head of the block mean (Delta S operand)
+  uint16_t* qm_lo;  // [BH][nqb][d] bf16 tail: q_mean - hi, rounded to bf16
 };
+constexpr int kWsSlices = 16;
 
 // Bytes of each workspace slice, in carving order.
-size_t workspace_layout(const Problem& p, size_t* sizes /* [13] or null */);
+size_t workspace_layout(const Problem& p, size_t* sizes /* [kWsSlices] or null */);
 void carve_workspace(const Problem& p, void* base, Workspace* w);
 
 // The key a lane half h consumes at byte b of its 32-byte FP8 P fragment: the S^T
@@ -103,15 +107,19 @@ __device__ inline float int8_scale(float amax) {
   return __fdiv_rn(a, 127.0f);
 }
 
-// Launchers (one per kernel file); each returns hipSuccess or the launch error.
-hipError_t launch_k_stats(const Problem& p, const void* k, const void* v, const Workspace& w, hipStream_t s);
-hipError_t launch_k_finalize(const Problem& p, const Workspace& w, hipStream_t s);
-hipError_t launch_k_quant(const Problem& p, const void* k, const void* v, const Workspace& w, hipStream_t s);
-hipError_t launch_v_scale(const Problem& p, const Workspace& w, hipStream_t s);
-hipError_t launch_v_quant(const Problem& p, const void* v, const Workspace& w, hipStream_t s);
+// bf16 bits of an FP32 value, round to nearest even (hardware conversion).
+__device__ inline uint16_t bf16_rn(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+__device__ inline float bf16_val(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
+
+// Launchers; each returns hipSuccess or the launch error.
+hipError_t launch_kv_stats(const Problem& p, const void* k, const void* v, const Workspace& w, hipStream_t s);
+hipError_t launch_kv_finalize(const Problem& p, const Workspace& w, hipStream_t s);
 hipError_t launch_q_prep(const Problem& p, const void* q, const Workspace& w, hipStream_t s);
-hipError_t launch_delta_s(const Problem& p, const void* k, const Workspace& w, float ds_scale,
-                          float* ds_out, hipStream_t s);
+// K^, Delta S (into ds_out scaled by ds_scale; skipped when ds_out is null) and V^.
+hipError_t launch_kv_quant(const Problem& p, const void* k, const void* v, const Workspace& w,
+                           float ds_scale, float* ds_out, hipStream_t s);
 hipError_t launch_attn_fwd(const Problem& p, const Workspace& w, void* out, hipStream_t s);
 
 }  // namespace sage
