@@ -43,15 +43,44 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLog2_448 = 8.807354922057604f;  // log2(448)
 constexpr int kXCD = 8;
 
+// LDS tiles are unpadded; 16-byte chunks are XOR-swizzled within a row so that the 16
+// lanes a ds_read_b128 serves at once (16 consecutive rows, one chunk column) hit 16
+// distinct 16-byte bank groups.  Rows sharing a 256-byte bank line differ in the low row
+// bits, rows that alias differ in the swizzle.
 template <int D>
 struct Tiles {
-  static constexpr int KS = D + 16;    // padded K^ row (bytes): conflict-free 16-lane b128 reads
-  static constexpr int VS = kBK + 16;  // padded V^ channel row (bytes)
-  static constexpr int KBYTES = kBK * KS;
-  static constexpr int VBYTES = D * VS;
-  static constexpr int KLD = kBK * D / 16 / 256;  // 16-byte loads per thread per tile
-  static constexpr int VLD = D * kBK / 16 / 256;
+  static constexpr int KROW = D;                   // bytes per K^ row
+  static constexpr int KCH = D / 16;               // 16-byte chunks per K^ row
+  static constexpr int KRPL = 256 / D;             // K^ rows per 256-byte bank line
+  static constexpr int KBYTES = kBK * D;
+  static constexpr int VBYTES = D * kBK;           // V^ rows are channels, 64 bytes each
+  static constexpr int KDMA = KBYTES / 1024 / 4;   // 1 KiB LDS-DMA wave instructions per wave
+  static constexpr int VDMA = VBYTES / 1024 / 4;
+  __device__ static int kswz(int r) { return (r / KRPL) & (KCH - 1); }
+  __device__ static int vswz(int r) { return (r >> 2) & 3; }
+  __device__ static int koff(int r, int c) { return r * D + 16 * (c ^ kswz(r)); }
+  __device__ static int voff(int r, int c) { return r * kBK + 16 * (c ^ vswz(r)); }
 };
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS byte address of a __shared__ object, in an SGPR.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>((uintptr_t)(const lds_void*)p));
+}
+
+// Global -> LDS DMA of one 16-byte (or 4-byte) chunk per lane into LDS bytes
+// [lds + 16 lane, +16) (resp. [lds + 4 lane, +4)).  Issued from asm so that the compiler's
+// wait-count tracking does not treat every later LDS read as dependent on it; completion is
+// awaited explicitly (vmcnt) before the barrier that publishes the tile.
+__device__ __forceinline__ void dma16(uint32_t lds, const void* gbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds), "v"(voff), "s"(gbase) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(uint32_t lds, const void* gbase, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
+               :: "s"(lds), "v"(voff), "s"(gbase) : "memory", "m0");
+}
 
 struct AttnArgs {
   const int8_t* qhat;
@@ -80,27 +109,32 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// One 64-key tile for one wave: scores, online softmax, P^ V^ into O.  `masked` (wave-
-// uniform) selects the causal / ragged-tail mask; interior tiles skip it.
-template <int D, bool CAUSAL, bool ACC_VALU>
-__device__ __forceinline__ void tile_step(const int8_t* __restrict__ sK, const uint8_t* __restrict__ sV,
-                                          const float* __restrict__ sDS, const float* __restrict__ sDK,
-                                          const v4i (&qf)[D / 32], float dql, int h, int col, int key0,
-                                          int qrow, int M, bool masked, v16f (&O)[D / 32], float& m_run,
-                                          float& l_run) {
-  constexpr int KS = Tiles<D>::KS, VS = Tiles<D>::VS, NKS = D / 32;
-  // ---- S^T = K^ Q^T on the INT8 MFMA (exact INT32) ----
-  v16i acc[2];
+// S^T = K^ Q^T of one 64-key tile on the INT8 MFMA (exact INT32): two 32-key halves.
+template <int D>
+__device__ __forceinline__ void qk_tile(const int8_t* __restrict__ sK, const v4i (&qf)[D / 32], int h, int col,
+                                        v16i (&acc)[2]) {
+  constexpr int NKS = D / 32;
 #pragma unroll
   for (int T = 0; T < 2; T++) {
 #pragma unroll
     for (int r = 0; r < 16; r++) acc[T][r] = 0;
 #pragma unroll
     for (int s = 0; s < NKS; s++) {
-      const v4i kf = *reinterpret_cast<const v4i*>(&sK[(32 * T + col) * KS + 32 * s + 16 * h]);
+      const v4i kf = *reinterpret_cast<const v4i*>(&sK[Tiles<D>::koff(32 * T + col, 2 * s + h)]);
       acc[T] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[s], acc[T], 0, 0, 0);
     }
   }
+}
+
+// The rest of one tile for one wave, from its INT32 scores: dequantize, online softmax,
+// P^ V^ into O.  `masked` (wave-uniform) selects the causal / ragged-tail mask; interior
+// tiles skip it.
+template <int D, bool CAUSAL, bool ACC_VALU>
+__device__ __forceinline__ void softmax_pv(const v16i (&acc)[2], const uint8_t* __restrict__ sV,
+                                           const float* __restrict__ sDS, const float* __restrict__ sDK,
+                                           float dql, int h, int col, int key0, int qrow, int M, bool masked,
+                                           v16f (&O)[D / 32], float& m_run, float& l_run) {
+  constexpr int NKS = D / 32;
   // ---- dequantize (dQ dK sm_scale log2e) and add Delta S ----
   float sc[2][16];
 #pragma unroll
@@ -145,7 +179,8 @@ __device__ __forceinline__ void tile_step(const int8_t* __restrict__ sK, const u
       const float p2 = fast_exp2(sc[T][4 * q4 + 2] - base);
       const float p3 = fast_exp2(sc[T][4 * q4 + 3] - base);
       psum += (p0 + p1) + (p2 + p3);
-      int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+      // the instruction keeps the other half-word of its destination: seed it with p0's bits
+      int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __float_as_int(p0), false);
       wd = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
       pf[4 * T + q4] = wd;
     }
@@ -162,9 +197,8 @@ __device__ __forceinline__ void tile_step(const int8_t* __restrict__ sK, const u
   }
 #pragma unroll
   for (int c = 0; c < NKS; c++) {
-    const uint8_t* vp = &sV[(32 * c + col) * VS + 32 * h];
-    const v4i lo = *reinterpret_cast<const v4i*>(vp);
-    const v4i hi = *reinterpret_cast<const v4i*>(vp + 16);
+    const v4i lo = *reinterpret_cast<const v4i*>(&sV[Tiles<D>::voff(32 * c + col, 2 * h)]);
+    const v4i hi = *reinterpret_cast<const v4i*>(&sV[Tiles<D>::voff(32 * c + col, 2 * h + 1)]);
     const v8i vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     if (ACC_VALU) {
       v16f R;
@@ -182,11 +216,12 @@ __device__ __forceinline__ void tile_step(const int8_t* __restrict__ sK, const u
 template <int D, bool CAUSAL, int OUT, bool ACC_VALU>  // OUT: 0 bf16, 1 fp16, 2 fp32
 __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   using TL = Tiles<D>;
-  constexpr int KS = TL::KS, VS = TL::VS, NKS = D / 32;
-  __shared__ __attribute__((aligned(16))) int8_t sK[2][TL::KBYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t sV[2][TL::VBYTES];
-  __shared__ float sDS[2][kBK];
-  __shared__ float sDK[2][4];
+  constexpr int NKS = D / 32;
+  constexpr int NB = 4;  // LDS ring: tile j computed, j+1 read by the next QK, j+2 and j+3 arriving
+  __shared__ __attribute__((aligned(1024))) int8_t sK[NB][TL::KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV[NB][TL::VBYTES];
+  __shared__ __attribute__((aligned(256))) float sDS[NB][kBK];
+  __shared__ __attribute__((aligned(16))) float sDK[NB][4];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -232,49 +267,71 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   const float* dsbase = a.ds + ((size_t)bh * a.nqb + qb) * a.Mp;
   const float* dkbase = a.dk + (size_t)bh * a.nkt * 4;
 
-  // ---- staging: global -> registers (next tile) -> LDS ----
-  v4i kreg[TL::KLD], vreg[TL::VLD];
-  float dsreg = 0.0f, dkreg = 0.0f;
-  auto gload = [&](int j) {
+  // ---- staging: global -> LDS by DMA (global_load_lds), no registers, no LDS stores ----
+  // Per-lane source offsets inside a tile (the swizzle is the same for every tile).
+  int koffs[TL::KDMA], voffs[TL::VDMA];
+#pragma unroll
+  for (int i = 0; i < TL::KDMA; i++) {
+    const int q = (TL::KDMA * w + i) * 64 + lane;  // 16-byte LDS chunk this lane fills
+    const int r = q / TL::KCH;
+    koffs[i] = r * D + 16 * ((q % TL::KCH) ^ TL::kswz(r));
+  }
+#pragma unroll
+  for (int i = 0; i < TL::VDMA; i++) {
+    const int q = (TL::VDMA * w + i) * 64 + lane;
+    const int r = q >> 2;
+    voffs[i] = r * kBK + 16 * ((q & 3) ^ TL::vswz(r));
+  }
+  auto dma = [&](int j, int slot) {
     const int8_t* kt = kbase + (size_t)j * kBK * D;
     const uint8_t* vt = vbase + (size_t)j * D * kBK;
 #pragma unroll
-    for (int i = 0; i < TL::KLD; i++) kreg[i] = *reinterpret_cast<const v4i*>(kt + (tid + 256 * i) * 16);
+    for (int i = 0; i < TL::KDMA; i++) dma16(lds_addr(&sK[slot][(TL::KDMA * w + i) * 1024]), kt, koffs[i]);
 #pragma unroll
-    for (int i = 0; i < TL::VLD; i++) vreg[i] = *reinterpret_cast<const v4i*>(vt + (tid + 256 * i) * 16);
-    if (tid < kBK) dsreg = dsbase[(size_t)j * kBK + tid];
-    if (tid < 4) dkreg = dkbase[(size_t)j * 4 + tid];
+    for (int i = 0; i < TL::VDMA; i++) dma16(lds_addr(&sV[slot][(TL::VDMA * w + i) * 1024]), vt, voffs[i]);
+    if (w == 0) dma4(lds_addr(&sDS[slot][0]), dsbase + (size_t)j * kBK, 4 * lane);
+    if (w == 1 && lane < 4) dma4(lds_addr(&sDK[slot][0]), dkbase + (size_t)j * 4, 4 * lane);
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < TL::KLD; i++) {
-      const int x = tid + 256 * i, row = x / (D / 16), cc = (x % (D / 16)) * 16;
-      *reinterpret_cast<v4i*>(&sK[buf][row * KS + cc]) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < TL::VLD; i++) {
-      const int x = tid + 256 * i, row = x / (kBK / 16), cc = (x % (kBK / 16)) * 16;
-      *reinterpret_cast<v4i*>(&sV[buf][row * VS + cc]) = vreg[i];
-    }
-    if (tid < kBK) sDS[buf][tid] = dsreg;
-    if (tid < 4) sDK[buf][tid] = dkreg;
+  // Wait until this wave's DMAs of all tiles but the newest one have landed (the newest
+  // tile's instructions may stay in flight) and its own LDS reads are done, then barrier:
+  // the next tile is visible to all and the slot read last iteration may be refilled.
+  constexpr int kPerTile = TL::KDMA + TL::VDMA;  // DMA instructions per tile, waves 2 and 3
+  auto publish = [&](bool newest_in_flight) {
+    if (!newest_in_flight)
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if (w < 2)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kPerTile + 1) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kPerTile) : "memory");
   };
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int j = 0; j < jend; j++) {
-    const int buf = j & 1;
-    if (j + 1 < jend) gload(j + 1);
-    const int key0 = j * kBK;
-    // wave-uniform tile class: fully masked (skip), boundary (masked) or interior
-    const bool skip = CAUSAL && key0 > wq0 + 31;
-    const bool masked = (CAUSAL && key0 + kBK - 1 > wq0) || (key0 + kBK > a.M);
-    if (!skip)
-      tile_step<D, CAUSAL, ACC_VALU>(sK[buf], sV[buf], sDS[buf], sDK[buf], qf, dql, h, col, key0, qrow, a.M,
-                                     masked, O, m_run, l_run);
-    if (j + 1 < jend) lstore(buf ^ 1);
-    __syncthreads();
+  // Software pipeline per wave: the QK MFMAs of tile j+1 are issued before the softmax of
+  // tile j, so the matrix core works on j+1 while the VALU works on j.  Tile j+3 streams into
+  // the ring slot last read in the previous iteration; two tiles are always in flight, and one
+  // barrier per tile publishes the next.
+  auto skip_t = [&](int j) { return CAUSAL && j * kBK > wq0 + 31; };  // fully masked for this wave
+  auto body = [&](int j, v16i (&cur)[2], v16i (&nxt)[2]) {
+    if (j + 3 < jend) dma(j + 3, (j + 3) % NB);
+    if (j + 1 < jend && !skip_t(j + 1)) qk_tile<D>(sK[(j + 1) % NB], qf, h, col, nxt);
+    if (!skip_t(j)) {
+      const int key0 = j * kBK;
+      const bool masked = (CAUSAL && key0 + kBK - 1 > wq0) || (key0 + kBK > a.M);
+      const int b = j % NB;
+      softmax_pv<D, CAUSAL, ACC_VALU>(cur, sV[b], sDS[b], sDK[b], dql, h, col, key0, qrow, a.M, masked, O,
+                                      m_run, l_run);
+    }
+    publish(j + 3 < jend);  // tile j+2 must be complete; j+3 may still be arriving
+  };
+
+  dma(0, 0);
+  if (jend > 1) dma(1, 1);
+  if (jend > 2) dma(2, 2);
+  publish(jend > 2);  // tiles 0 and 1 landed; tile 2 may be arriving
+  v16i accA[2], accB[2];
+  qk_tile<D>(sK[0], qf, h, col, accA);  // tile 0 is never masked away
+  for (int j = 0; j < jend; j += 2) {
+    body(j, accA, accB);
+    if (j + 1 < jend) body(j + 1, accB, accA);
   }
 
   // ---- epilogue: O / l (l holds 448 * sum P~) * dV (+ V_m) ----
