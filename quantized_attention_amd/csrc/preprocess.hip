@@ -73,17 +73,31 @@ __global__ __launch_bounds__(256) void kv_stats_kernel(const uint16_t* __restric
   const size_t o = ((size_t)bh * nkt + u) * D;
   if (tid < D) {
     double s = 0.0;
-    for (int t = 0; t < n; t++) s += (double)load_in(sk, (size_t)t * RS + tid, fp16);
+    for (int t0b = 0; t0b < n; t0b += 8) {  // 8 LDS reads in flight; the adds stay in token order
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; e++) x[e] = load_in(sk, (size_t)min(t0b + e, kBK - 1) * RS + tid, fp16);
+#pragma unroll
+      for (int e = 0; e < 8; e++)
+        if (t0b + e < n) s += (double)x[e];
+    }
     kpart[o + tid] = s;
   } else if (tid >= 128 && tid - 128 < D) {
     const int c = tid - 128;
     double s = 0.0;
     float mx = -INFINITY, mn = INFINITY;
-    for (int t = 0; t < n; t++) {
-      const float x = load_in(sv, (size_t)t * RS + c, fp16);
-      if (smooth_v) s += (double)x;
-      mx = x > mx ? x : mx;  // NaN ignored
-      mn = x < mn ? x : mn;
+    for (int t0b = 0; t0b < n; t0b += 8) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; e++) x[e] = load_in(sv, (size_t)min(t0b + e, kBK - 1) * RS + c, fp16);
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        if (t0b + e < n) {
+          if (smooth_v) s += (double)x[e];
+          mx = x[e] > mx ? x[e] : mx;  // NaN ignored
+          mn = x[e] < mn ? x[e] : mn;
+        }
+      }
     }
     if (smooth_v) vpart[o + c] = s;
     vmaxp[o + c] = mx;
@@ -153,8 +167,15 @@ __global__ __launch_bounds__(256) void q_prep_kernel(const uint16_t* __restrict_
   }
   __syncthreads();
   if (tid < D) {
-    double s = 0.0;  // rows in order, FP64
-    for (int r = 0; r < n; r++) s += (double)load_in(sq, (size_t)r * RS + tid, fp16);
+    double s = 0.0;  // rows in order, FP64 (8 LDS reads in flight)
+    for (int rb = 0; rb < n; rb += 8) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; e++) x[e] = load_in(sq, (size_t)min(rb + e, kBQ - 1) * RS + tid, fp16);
+#pragma unroll
+      for (int e = 0; e < 8; e++)
+        if (rb + e < n) s += (double)x[e];
+    }
     const float m = (float)(s / (double)n);
     sm[tid] = m;
     const size_t o = ((size_t)bh * nqb + i) * D + tid;
@@ -229,6 +250,16 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(KVArgs a) {
   const size_t in_base = ((size_t)bh * a.M + t0) * D;
   const float* km = a.kmean + (size_t)bh * D;
 
+  // ---- all of this thread's K and V chunks in flight at once ----
+  v4i kraw[CH], vraw[CH];
+#pragma unroll
+  for (int i = 0; i < CH; i++) {
+    const int x = tid + 256 * i, row = x / (D / 8), c0 = (x % (D / 8)) * 8;
+    const size_t off = in_base + (size_t)min(row, n - 1) * D + c0;  // rows >= n are not used
+    kraw[i] = *reinterpret_cast<const v4i*>(a.K + off);
+    vraw[i] = *reinterpret_cast<const v4i*>(a.V + off);
+  }
+
   // ---- gamma(K) = K - k (FP32), its bf16 split into LDS, group maxima ----
   float g[CH][8];
   float am[4] = {0.f, 0.f, 0.f, 0.f};
@@ -237,7 +268,7 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(KVArgs a) {
     const int x = tid + 256 * i, row = x / (D / 8), c0 = (x % (D / 8)) * 8;
     if (row < n) {
       float w[8];
-      widen8(*reinterpret_cast<const v4i*>(a.K + in_base + (size_t)row * D + c0), a.fp16, w);
+      widen8(kraw[i], a.fp16, w);
 #pragma unroll
       for (int e = 0; e < 8; e++) g[i][e] = w[e] - km[c0 + e];
     } else {
@@ -314,19 +345,21 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(KVArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; r++) acc[r] = 0.0f;
       const size_t qo = ((size_t)bh * a.nqb + (bv ? blk : 0)) * D;
+      v8bf bq[D / 16], bl[D / 16];  // the block's q-mean head/tail, all loads in flight
+#pragma unroll
+      for (int s = 0; s < D / 16; s++) {
+        bq[s] = *reinterpret_cast<const v8bf*>(a.qm_hi + qo + 16 * s + 8 * h);
+        bl[s] = *reinterpret_cast<const v8bf*>(a.qm_lo + qo + 16 * s + 8 * h);
+      }
 #pragma unroll
       for (int s = 0; s < D / 16; s++) {
         const v8bf ah = *reinterpret_cast<const v8bf*>(&sAh[(32 * T + col) * RS + 16 * s + 8 * h]);
         const v8bf al = *reinterpret_cast<const v8bf*>(&sAl[(32 * T + col) * RS + 16 * s + 8 * h]);
-        v8bf bq = *reinterpret_cast<const v8bf*>(a.qm_hi + qo + 16 * s + 8 * h);
-        v8bf bl = *reinterpret_cast<const v8bf*>(a.qm_lo + qo + 16 * s + 8 * h);
-        if (!bv) {
-          bq = v8bf{};
-          bl = v8bf{};
-        }
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bq, acc, 0, 0, 0);  // small terms first
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bq, acc, 0, 0, 0);
+        const v8bf qh = bv ? bq[s] : v8bf{};
+        const v8bf ql = bv ? bl[s] : v8bf{};
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qh, acc, 0, 0, 0);  // small terms first
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, ql, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qh, acc, 0, 0, 0);
       }
       if (bv && blk >= ilo) {
         float* dst = a.ds + ((size_t)bh * a.nqb + blk) * a.Mp + t0 + 32 * T + 4 * h;
@@ -348,7 +381,7 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(KVArgs a) {
       const int x = tid + 256 * i, row = x / (D / 8), c0 = (x % (D / 8)) * 8;
       float w[8];
       if (row < n) {
-        widen8(*reinterpret_cast<const v4i*>(a.V + in_base + (size_t)row * D + c0), a.fp16, w);
+        widen8(vraw[i], a.fp16, w);
 #pragma unroll
         for (int e = 0; e < 8; e++) {
           float y = __fdiv_rn(w[e] - vm[c0 + e], sc[c0 + e]);
