@@ -32,10 +32,32 @@ sys.path.insert(0, ROOT)
 
 PEAK_TOPS = 5000.0  # MI355X dense INT8 / OCP-FP8 MFMA peak, 5.0 POPS
 
-# Kernel-level HBM traffic measured with rocprofv3 counters (FETCH_SIZE, WRITE_SIZE per
-# dispatch of the fused attention kernel on this workload, scaled by a copy-kernel
-# calibration); None until measured for the current kernel.
-TRAFFIC_BYTES = {}
+# Kernel-level HBM traffic of the fused attention kernel, one launch on the named workload:
+# rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (KiB per dispatch) scaled by what the same
+# counters read for a plain 1 GiB device copy (FETCH x2.000, WRITE x1.000).  Valid only for
+# the kernel source it was taken on: the hash of attn_fwd.hip + sage_common.hpp is checked,
+# and a changed kernel reports traffic null until the counters are taken again.
+TRAFFIC_BYTES = {
+    "prefill32k": {"source_sha256_16": "b0764badecc728d8",
+                   "fetch_bytes": 1598236629, "write_bytes": 268435558},
+}
+KERNEL_SOURCES = ("quantized_attention_amd/csrc/attn_fwd.hip", "quantized_attention_amd/csrc/sage_common.hpp")
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(name: str):
+    t = TRAFFIC_BYTES.get(name)
+    if t is None or t["source_sha256_16"] != kernel_source_hash():
+        return None
+    return t["fetch_bytes"] + t["write_bytes"]
 
 
 def parse():
@@ -47,6 +69,9 @@ def parse():
                     help="one of: n4k, prefill32k, video17k (default prefill32k)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="after the steps, copy a MIB-MiB device buffer twice (a plain copy kernel of "
+                         "known size, the reference point for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -168,7 +193,7 @@ def main():
     ops = counted_ops(cfg)
     value = ops / (ms * 1e-3) / 1e12
     achieved = ops / (kms * 1e-3) / 1e12
-    traffic = TRAFFIC_BYTES.get(cfg.name)
+    traffic = measured_traffic(cfg.name)
     line = {
         "metric": "attention TOPS (4*N^2*d*H*B/time, causal counted as half) at N=32k d=128, % of INT8/FP8 MFMA peak",
         "value": round(value, 2),
@@ -193,6 +218,15 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TOPS, "unit": "TOPS",
                      "frac": round(achieved / PEAK_TOPS, 4), "traffic": traffic},
     }
+    if args.copy_calibration > 0:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = n
+        del src, dst
     if not args.no_cpu_baseline:
         print(f"[bench] cpu baseline ({args.cpu_seconds:.0f} s budget)", file=sys.stderr, flush=True)
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
