@@ -58,6 +58,8 @@ def lib():
         i, u, dbl = ctypes.c_int, ctypes.c_uint, ctypes.c_double
         L.orc_preprocess_head.argtypes = [P, P, P, i, i, i, i, u] + [P] * 10
         L.orc_preprocess_head.restype = i
+        L.orc_preprocess_mx_head.argtypes = [P, P, P, i, i, i, i, u, P, P, P, P, P, P]
+        L.orc_preprocess_mx_head.restype = i
         L.orc_forward_head.argtypes = [P, P, P, i, i, i, i, i, dbl, u, P, i, P]
         L.orc_forward_head.restype = i
         L.orc_exact_head.argtypes = [P, P, P, i, i, i, i, i, dbl, P, i, P]
@@ -116,6 +118,21 @@ def preprocess_head(q, k, v, fp16: bool, flags: int = 0) -> dict:
                                                           "dv", "qhat", "dq", "qmean", "ds")])
     if rc != 0:
         raise ValueError("orc_preprocess_head rejected its arguments")
+    return o
+
+
+def preprocess_mx_head(q, k, v, fp16: bool, flags: int = 0) -> dict:
+    """MX-variant codes and exponents of one head (natural layouts, see sage_oracle.h)."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    N, d = q.shape
+    M = k.shape[0]
+    o = dict(qcode=np.zeros((N, d), np.uint8), qexp=np.zeros((N, d // 32), np.int32),
+             kcode=np.zeros((M, d), np.uint8), kexp=np.zeros((M, d // 32), np.int32),
+             vcode=np.zeros((M, d), np.uint8), vexp=np.zeros((-(-M // 32), d), np.int32))
+    rc = lib().orc_preprocess_mx_head(_ptr(q), _ptr(k), _ptr(v), int(fp16), N, M, d, flags & ~MXFP4,
+                                      *[_ptr(o[n]) for n in ("qcode", "qexp", "kcode", "kexp", "vcode", "vexp")])
+    if rc != 0:
+        raise ValueError("orc_preprocess_mx_head rejected its arguments")
     return o
 
 

@@ -688,6 +688,31 @@ int orc_preprocess_head(const uint16_t* q, const uint16_t* k, const uint16_t* v,
   return 0;
 }
 
+/* The MX variant's quantized tensors of one head, as codes: the E2M1 code (sign << 3 |
+ * magnitude index) of every element of gamma(Q) [N][d] and gamma(K) [M][d] with their E8M0
+ * exponents per 32 channels [N][d/32], [M][d/32]; the codes of V' [M][d] with one exponent
+ * per 32 tokens of each channel [ceil(M/32)][d] ([SA3] 3.4: 1x32 blocks along the reduction
+ * dimension of each product).  The E2M1 decode is injective (signed zeros included), so the
+ * codes are those the quantizer chose.  Any output may be NULL. */
+int orc_preprocess_mx_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, int in_fp16,
+                           int N, int M, int d, unsigned flags,
+                           uint8_t* qcode, int* qexp, uint8_t* kcode, int* kexp,
+                           uint8_t* vcode, int* vexp) {
+  if (!q || !k || !v) return -1;
+  if (flags & ~(ORC_SMOOTH_V | ORC_NO_SMOOTH_K | ORC_NO_SMOOTH_Q)) return -1;
+  head_t h;
+  if (head_setup(&h, q, k, v, in_fp16, N, M, d, flags | ORC_MXFP4)) { head_free(&h); return -1; }
+  int nb = d / 32, nvb = (M + 31) / 32;
+  if (qcode) for (size_t x = 0; x < (size_t)N * d; x++) qcode[x] = orc_e2m1_encode(h.qx[x]);
+  if (kcode) for (size_t x = 0; x < (size_t)M * d; x++) kcode[x] = orc_e2m1_encode(h.kx[x]);
+  if (vcode) for (size_t x = 0; x < (size_t)M * d; x++) vcode[x] = orc_e2m1_encode(h.vx[x]);
+  if (qexp) memcpy(qexp, h.qe, sizeof(int) * (size_t)N * nb);
+  if (kexp) memcpy(kexp, h.ke, sizeof(int) * (size_t)M * nb);
+  if (vexp) memcpy(vexp, h.ve, sizeof(int) * (size_t)nvb * d);
+  head_free(&h);
+  return 0;
+}
+
 /* Textbook attention: softmax(Q K^T * sm_scale) V, FP64, row by row. */
 static void exact_row(const double* qr, const double* K, const double* V, int M, int d, int lim,
                       double sm_scale, double* s, double* out) {

@@ -86,6 +86,13 @@ int orc_preprocess_head(const uint16_t* q, const uint16_t* k, const uint16_t* v,
  * rows: the query rows to produce (NULL with nrows = N means all rows in order);
  * out: [nrows][d] in FP64.  causal requires N == M (mask key t > row r).
  * Returns 0, or -1 on a bad argument. */
+/* MX variant (ORC_MXFP4 implied): E2M1 codes of gamma(Q) [N][d], gamma(K) [M][d], V' [M][d];
+ * E8M0 exponents (unbiased) [N][d/32], [M][d/32] per 32 channels and [ceil(M/32)][d] per 32
+ * tokens of each V channel.  flags: ORC_SMOOTH_V / ORC_NO_SMOOTH_K / ORC_NO_SMOOTH_Q. */
+int orc_preprocess_mx_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, int in_fp16,
+                           int N, int M, int d, unsigned flags,
+                           uint8_t* qcode, int* qexp, uint8_t* kcode, int* kexp,
+                           uint8_t* vcode, int* vexp);
 int orc_forward_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, int in_fp16,
                      int N, int M, int d, int causal, double sm_scale, unsigned flags,
                      const int* rows, int nrows, double* out);

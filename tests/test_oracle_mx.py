@@ -1,0 +1,160 @@
+"""Pins of the oracle's MXFP4 variant.
+
+Sources: "SageAttention3" summary, 3.4 "The NVFP4 Microscaling Format and Quantization
+Operator" (the E2M1 value set; one E8M0 power-of-two scale per 1x32 block along the
+reduction dimension of each product; P~ quantized per block of keys, V per block of
+tokens); "SageAttention2 Technical Report" summary, 3.4 ("Smoothing Q", "Optional Smoothing
+of V", "The Complete Algorithm").
+
+The lossless construction: fp16 inputs whose smoothed Q and K sit exactly on the E2M1 grid
+of their own 32-channel blocks (with a different exponent per token and block), V' exactly
+on the grid of each 32-token block of each channel, and scores that are multiples of ln 2,
+so that every P~ is a power of two within three octaves of its 32-key block's maximum.
+Then every quantizer in the MX forward is exact and the result must equal textbook FP64
+attention.  A mistake in the block axis of any operand, in the E8M0 rule (the smallest e
+with amax <= 6 * 2^e), in the scale arithmetic 2^(e_a + e_b), in the V smoothing
+add-back or in the P~ blocks (per 32 keys of the row, relative to the block maximum) breaks
+one of the equalities below.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+
+E2M1 = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def f16(x):
+    x = np.asarray(x, np.float64)
+    b = x.astype(np.float16)
+    assert np.array_equal(b.astype(np.float64), x), "construction is not fp16-exact"
+    return b.view(np.uint16)
+
+
+def grid_block(rng, n, e):
+    """n values on the E2M1 grid times 2^e whose largest magnitude is 4 or 6 times 2^e,
+    so that the block's E8M0 exponent is exactly e."""
+    z = rng.choice(E2M1, n) * rng.choice([-1.0, 1.0], n)
+    z[rng.integers(n)] = rng.choice([4.0, 6.0]) * rng.choice([-1.0, 1.0])
+    return z * 2.0 ** e
+
+
+def mx_lossless_case(seed, N, M, d, smooth_v):
+    assert N % 2 == 0 and M % 2 == 0
+    rng = np.random.default_rng(seed)
+    nb = d // 32
+    score_ch = [32 * b + 1 for b in range(nb)]                       # the only channels scores use
+    dead_ch = [32 * b + c for b in range(nb) for c in range(2, 10)]  # K constant there (gamma K = 0)
+    free_ch = [c for c in range(d) if c not in score_ch and c not in dead_ch]
+    # ---- K = kb + Y, Y paired (t, t+1) -> mean(K) = kb exactly
+    kb = 2.0 * rng.integers(-3, 4, d)
+    Y = np.zeros((M, d))
+    kexp = np.zeros((M, nb), int)
+    for t in range(0, M, 2):
+        for b in range(nb):
+            f = int(rng.integers(-2, 2))
+            kexp[t, b] = kexp[t + 1, b] = f
+            blk = [c for c in free_ch if c // 32 == b]
+            Y[t, blk] = grid_block(rng, len(blk), f)
+            Y[t, score_ch[b]] = rng.integers(-1, 2)  # 1 = 2^-f * 2^f is on every grid f in -2..1
+        Y[t + 1] = -Y[t]
+    # ---- Q = qb_i + Yq, Yq paired within each 128-row block; qb only on dead channels
+    nqb = -(-N // 128)
+    qb = np.zeros((nqb, d))
+    Yq = np.zeros((N, d))
+    qexp = np.zeros((N, nb), int)
+    for i in range(nqb):
+        qb[i, dead_ch] = 2.0 * rng.integers(-3, 4, len(dead_ch))
+        for r in range(128 * i, min(128 * i + 128, N), 2):
+            cr = int(rng.integers(nb))
+            for b in range(nb):
+                blk = [c for c in dead_ch if c // 32 == b]
+                g = int(rng.integers(1, 5)) if b == cr else int(rng.integers(-2, 5))
+                qexp[r, b] = qexp[r + 1, b] = g
+                Yq[r, blk] = grid_block(rng, len(blk), g)
+            Yq[r, score_ch[cr]] = 8.0 * rng.choice([-1.0, 1.0])  # 8 = (8 / 2^g) 2^g, g in 1..4
+            Yq[r + 1] = -Yq[r]
+    # ---- V = vm + Z; Z on the grid of each 32-token block (pairs keep mean(V) = vm)
+    nvb = -(-M // 32)
+    vm = 0.25 * rng.integers(-8, 9, d) if smooth_v else np.zeros(d)
+    Z = np.zeros((M, d))
+    vexp = np.zeros((nvb, d), int)
+    for vb in range(nvb):
+        toks = np.arange(32 * vb, min(32 * vb + 32, M))
+        for c in range(d):
+            h = int(rng.integers(-3, 1))
+            vexp[vb, c] = h
+            z = grid_block(rng, len(toks), h)
+            if smooth_v:
+                z[1::2] = -z[0::2]
+                z[0] = rng.choice([4.0, 6.0]) * 2.0 ** h
+                z[1] = -z[0]
+            Z[toks, c] = z
+    Q = np.repeat(qb, 128, axis=0)[:N] + Yq
+    K = kb[None, :] + Y
+    V = vm[None, :] + Z
+    c = dict(Y=Y, Yq=Yq, Z=Z, kexp=kexp, qexp=qexp, vexp=vexp, qb=qb, kb=kb, vm=vm)
+    return f16(Q), f16(K), f16(V), math.log(2.0) / 8.0, c
+
+
+def codes_of(x, e_per_elem):
+    """E2M1 codes of values on the grid; zeros are +0, as the smoothing subtraction leaves them."""
+    y = (x + 0.0) / 2.0 ** e_per_elem
+    mag = np.abs(y)
+    idx = np.array([np.flatnonzero(E2M1 == m)[0] for m in mag.ravel()]).reshape(y.shape)
+    return (np.signbit(y).astype(np.uint8) << 3) | idx.astype(np.uint8)
+
+
+@pytest.mark.parametrize("N,d,smooth_v", [(192, 128, False), (192, 64, True), (130, 128, True)])
+def test_mx_codes_and_exponents_match_construction(N, d, smooth_v):
+    q, k, v, _, c = mx_lossless_case(30 + N + d, N, N, d, smooth_v)
+    p = oracle.preprocess_mx_head(q, k, v, True, oracle.SMOOTH_V if smooth_v else 0)
+    nb = d // 32
+    qe = np.repeat(c["qexp"], 32, axis=1)
+    ke = np.repeat(c["kexp"], 32, axis=1)
+    ve = np.repeat(c["vexp"], 32, axis=0)[:N]
+    # blocks that are entirely zero take the floor exponent -127 (their codes are zeros)
+    zq = np.repeat(np.abs(c["Yq"]).reshape(N, nb, 32).max(axis=2) == 0, 32, axis=1)
+    zk = np.repeat(np.abs(c["Y"]).reshape(N, nb, 32).max(axis=2) == 0, 32, axis=1)
+    assert np.array_equal(p["qexp"], np.where(zq[:, ::32], -127, c["qexp"]))
+    assert np.array_equal(p["kexp"], np.where(zk[:, ::32], -127, c["kexp"]))
+    assert np.array_equal(p["vexp"], c["vexp"])
+    assert np.array_equal(p["qcode"], codes_of(c["Yq"], np.where(zq, 0, qe)))
+    assert np.array_equal(p["kcode"], codes_of(c["Y"], np.where(zk, 0, ke)))
+    assert np.array_equal(p["vcode"], codes_of(c["Z"], ve))
+
+
+@pytest.mark.parametrize("N,d,causal,smooth_v", [(192, 128, False, False), (192, 128, True, True),
+                                                 (160, 64, False, True), (130, 128, True, False)])
+def test_mx_lossless_construction_equals_textbook(N, d, causal, smooth_v):
+    q, k, v, s, c = mx_lossless_case(40 + N + d, N, N, d, smooth_v)
+    flags = oracle.MXFP4 | (oracle.SMOOTH_V if smooth_v else 0)
+    got = oracle.forward_head(q, k, v, True, causal, s, flags)
+    ex = oracle.exact_head(q, k, v, True, causal, s)
+    assert np.abs(got - ex).max() < 1e-11 * max(1.0, np.abs(ex).max())
+
+
+def test_mx_p_block_exponent_follows_block_max_not_row_max():
+    """One 64-key tile, scores (ln 2) * {-2 for keys 0..31 except -4 for key 3; 0 for keys
+    32..63}: row 0 sees P~ = 2^-2 and 2^-4 in its first 32-key block and 1 in the second.
+    With one exponent per 32-key block (e = -4 for block max 2^-2) both 2^-2 = 4 * 2^-4 and
+    2^-4 = 1 * 2^-4 are on the grid, and only key 3 carries a value, so O = exact attention.
+    A single exponent per row (e = -2 for row max 1) would put 2^-4 = 0.25 * 2^-2 on a tie
+    and round it to 0, losing the whole output.  K is left unsmoothed (its mean would move
+    the values off the grid); row 1 = -row 0 keeps the Q block mean at 0."""
+    d, M = 64, 64
+    Q = np.zeros((2, d)); Q[0, 0] = 1.0; Q[1, 0] = -1.0
+    K = np.zeros((M, d))
+    K[:32, 0] = -2.0
+    K[3, 0] = -4.0
+    V = np.zeros((M, d))
+    V[3, :] = 4.0
+    q, k, v = f16(Q), f16(K), f16(V)
+    s = math.log(2.0)
+    got = oracle.forward_head(q, k, v, True, False, s, oracle.MXFP4 | oracle.NO_SMOOTH_K)
+    ex = oracle.exact_head(q, k, v, True, False, s)
+    l0 = 31 * 2.0 ** -2 + 2.0 ** -4 + 32
+    assert abs(ex[0, 0] - 4 * 2.0 ** -4 / l0) < 1e-15
+    assert np.abs(got - ex).max() < 1e-12
