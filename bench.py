@@ -30,18 +30,20 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_TOPS = 5000.0  # MI355X dense INT8 / OCP-FP8 MFMA peak, 5.0 POPS
+PEAK_TOPS = 5000.0     # MI355X dense INT8 / OCP-FP8 MFMA peak, 5.0 POPS
+PEAK_TOPS_FP4 = 10100.0  # MI355X dense MXFP4 MFMA peak, 10.1 PFLOP/s (the MX variant's contractions)
 
 # Kernel-level HBM traffic of the fused attention kernel, one launch on the named workload:
 # rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (KiB per dispatch) scaled by what the same
 # counters read for a plain 1 GiB device copy (FETCH x2.000, WRITE x1.000).  Valid only for
-# the kernel source it was taken on: the hash of attn_fwd.hip + sage_common.hpp is checked,
+# the kernel source it was taken on: the hash of the fused kernel's sources is checked,
 # and a changed kernel reports traffic null until the counters are taken again.
 TRAFFIC_BYTES = {
-    "prefill32k": {"source_sha256_16": "b0764badecc728d8",
-                   "fetch_bytes": 1598236629, "write_bytes": 268435558},
+    "prefill32k": {"source_sha256_16": "6938d376c6324f23",
+                   "fetch_bytes": 1596341237, "write_bytes": 268439859},
 }
-KERNEL_SOURCES = ("quantized_attention_amd/csrc/attn_fwd.hip", "quantized_attention_amd/csrc/sage_common.hpp")
+KERNEL_SOURCES = ("quantized_attention_amd/csrc/attn_fwd.hip", "quantized_attention_amd/csrc/attn_device.hpp",
+                  "quantized_attention_amd/csrc/sage_common.hpp")
 
 
 def kernel_source_hash() -> str:
@@ -66,7 +68,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill32k",
-                    help="one of: n4k, prefill32k, video17k (default prefill32k)")
+                    help="one of: n4k, prefill32k, video17k, mxfp4_32k (default prefill32k)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -115,7 +117,7 @@ def cpu_baseline(cfg, budget_s: float) -> dict:
     q, k, v = sy.make_qkv(cfg, heads=[0])
     rng = np.random.default_rng(7)
     s = 1.0 / math.sqrt(cfg.d)
-    flags = oracle.SMOOTH_V if cfg.smooth_v else 0
+    flags = (oracle.SMOOTH_V if cfg.smooth_v else 0) | (oracle.MXFP4 if cfg.mxfp4 else 0)
     ops, t_used, nrows, batch = 0.0, 0.0, 0, 8
     while t_used < budget_s:
         rows = np.sort(rng.integers(0, cfg.N, batch))
@@ -155,6 +157,9 @@ def main():
     del qb, kb, vb
     out = torch.empty((cfg.B, cfg.H, cfg.N, cfg.d), dtype=dt, device=dev)
     var = (qa.SAGE_IN_FP16 if cfg.fp16 else qa.SAGE_IN_BF16) | (qa.SAGE_SMOOTH_V if cfg.smooth_v else 0)
+    if cfg.mxfp4:
+        var |= qa.SAGE_PATH_MXFP4
+    peak = PEAK_TOPS_FP4 if cfg.mxfp4 else PEAK_TOPS
     ws_bytes = qa.sage_attn_workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.M, cfg.d, cfg.causal, var)
     ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
     ws_ptr = (ws.data_ptr() + 255) // 256 * 256
@@ -194,8 +199,13 @@ def main():
     value = ops / (ms * 1e-3) / 1e12
     achieved = ops / (kms * 1e-3) / 1e12
     traffic = measured_traffic(cfg.name)
+    dtype = ("e2m1 + e8m0 1x32 blocks (QK, PV), fp32 softmax/accumulate" if cfg.mxfp4
+             else "int8(QK)+fp8e4m3(PV), fp32 softmax/accumulate")
+    metric = ("attention TOPS (4*N^2*d*H*B/time, causal counted as half) at N=32k d=128, % of INT8/FP8 MFMA peak"
+              if not cfg.mxfp4 else
+              "attention TOPS (4*N^2*d*H*B/time) at N=32k d=128, MXFP4 variant, % of FP4 MFMA peak")
     line = {
-        "metric": "attention TOPS (4*N^2*d*H*B/time, causal counted as half) at N=32k d=128, % of INT8/FP8 MFMA peak",
+        "metric": metric,
         "value": round(value, 2),
         "unit": "TOPS",
         "n_gpus": 1,
@@ -205,18 +215,18 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8(QK)+fp8e4m3(PV), fp32 softmax/accumulate",
+        "dtype": dtype,
         "data": "synthetic (seeded Gaussian + per-channel offsets)",
         "config": {"workload": f"{cfg.name}: B={cfg.B} H={cfg.H} N=M={cfg.N} d={cfg.d} {cfg.dtype} "
                                f"{'causal' if cfg.causal else 'non-causal'}"
                                f"{' smooth_v' if cfg.smooth_v else ''}",
                    "global_batch": cfg.B, "seq_len": cfg.N, "heads": cfg.H, "head_dim": cfg.d,
                    "parallelism": "single GPU"},
-        "frac_of_peak": round(value / PEAK_TOPS, 4),
+        "frac_of_peak": round(value / peak, 4),
         "attn_kernel_ms": round(kms, 4),
         "preprocess_ms": round(ms - kms, 4),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TOPS, "unit": "TOPS",
-                     "frac": round(achieved / PEAK_TOPS, 4), "traffic": traffic},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TOPS",
+                     "frac": round(achieved / peak, 4), "traffic": traffic},
     }
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20

@@ -28,7 +28,8 @@
  *   - Argument errors are detected before anything is enqueued and return a negative
  *     sage_status.  A failed launch returns SAGE_ERR_LAUNCH; faults inside kernels surface
  *     at the caller's next synchronization.
- *   - NaN inputs propagate to the output rows that attend to them.
+ *   - NaN inputs propagate to the output rows that attend to them (INT8/FP8 path; E2M1 has
+ *     no NaN code, and the MX variant codes a NaN element as the largest magnitude, 6).
  */
 #ifndef SAGE_ATTN_H
 #define SAGE_ATTN_H
@@ -51,6 +52,13 @@ typedef enum {
 
 /* ---- variant bit-field ---- */
 #define SAGE_PATH_I8F8  0x0000u /* INT8 QK (per-token Q, 4 groups / 64 keys K), FP8 E4M3 PV   */
+#define SAGE_PATH_MXFP4 0x0001u /* MXFP4 ("SageAttention3" summary, 3.4 "The NVFP4 Microscaling
+                                   Format and Quantization Operator"): smoothed Q and K, P~ and
+                                   V' in E2M1 with one E8M0 power-of-two scale per 32 elements
+                                   along each product's reduction dimension (Q, K: 32 channels
+                                   of a token; P~: 32 keys of a query row; V': 32 tokens of a
+                                   channel), on the block-scaled FP4 MFMA.  No 448 and no dV:
+                                   the epilogue is O / l (+ V_m).  Means and Delta S as above. */
 #define SAGE_SMOOTH_V   0x0010u /* V' = V - mean_t(V) before quantization, O += V_m           */
 #define SAGE_IN_BF16    0x0000u
 #define SAGE_IN_FP16    0x0100u
@@ -103,6 +111,25 @@ int sage_attn_fwd_ws(const void* q, const void* k, const void* v, void* out,
  *   q_mean  float [BH][nqb][d]  per-block mean of Q
  *   delta_s float [BH][nqb][Mp] Delta S_i[t] = q_i . gamma(K)[t] (FP32); with causal only
  *           t < 128*(i+1) is written
+ * With SAGE_PATH_MXFP4 the quantized tensors are E2M1 codes (sign << 3 | magnitude index
+ * into {0, 0.5, 1, 1.5, 2, 3, 4, 6}), two per byte, the lower-indexed element in the low
+ * nibble, and the scales are E8M0 bytes (2^(byte - 127)):
+ *   q_hat   uint8 [BH][Np][d/2]   gamma(Q) / 2^e per 32-channel block; rows >= N are 0
+ *   k_hat   uint8 [BH][Mp][d/2]   gamma(K) / 2^e per 32-channel block; keys >= M are 0
+ *   v_hat   uint8 [BH][nkt][d][32]  V' / 2^e per 32-token block, transposed per 64-key tile:
+ *           nibble p = 32h + j of channel c holds key 64*tile + vperm(h, j) with
+ *           vperm(h, j) = 32*h + 8*((j%16)/4) + 4*(j/16) + j%4 (the keys a lane half h of
+ *           the FP4 MFMA consumes after the P fragments of the two lane halves are swapped
+ *           so that half h holds the contiguous keys 32h..32h+31); keys >= M are 0
+ *   mx_scales_q uint8 [BH][Np][d/32]  E8M0 of (row, 32-channel block); rows >= N are 0
+ *   mx_scales_k uint8 [BH][nkt][64][4] byte 4*l + 2*T + c (c < d/64) of tile u holds the E8M0
+ *           of key 64u + 32T + l%32, channel block 2c + l/32 (the A-operand scale of MFMA lane
+ *           l); bytes with c >= d/64 are 0
+ *   mx_scales_v uint8 [BH][nkt][64][4] byte 4*l + g (g < d/32) of tile u holds the E8M0 of
+ *           channel 32g + l%32, tokens 64u + 32*(l/32) .. +31; bytes with g >= d/32 are 0
+ *   dq and dk are not written; dv is written (it is not used by the MX forward).
+ * The E8M0 exponent of a block is the smallest e with max|x| <= 6 * 2^e, clamped to
+ * [-127, 127] (an all-zero block has e = -127, byte 0).
  * Returns SAGE_OK or a negative sage_status.
  */
 typedef struct {
@@ -116,6 +143,9 @@ typedef struct {
   float* v_mean;
   float* q_mean;
   float* delta_s;
+  void* mx_scales_q; /* SAGE_PATH_MXFP4 only (ignored otherwise); NULL skips */
+  void* mx_scales_k;
+  void* mx_scales_v;
 } sage_quant_views;
 
 int sage_attn_quantize(const void* q, const void* k, const void* v,

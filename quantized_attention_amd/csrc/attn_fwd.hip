@@ -34,14 +34,14 @@
 // kept on one XCD (work-groups are dealt to the 8 XCDs round-robin), so a head's K^/V^
 // tiles are shared through that XCD's L2.  K^/V^ tiles are double-buffered in LDS; the
 // next tile's global loads are in flight while the current one is computed.
-#include "sage_common.hpp"
+#include "attn_device.hpp"
 
 namespace sage {
 namespace {
 
-constexpr float kLog2e = 1.4426950408889634f;
+using namespace attn;
+
 constexpr float kLog2_448 = 8.807354922057604f;  // log2(448)
-constexpr int kXCD = 8;
 
 // LDS tiles are unpadded; 16-byte chunks are XOR-swizzled within a row so that the 16
 // lanes a ds_read_b128 serves at once (16 consecutive rows, one chunk column) hit 16
@@ -62,26 +62,6 @@ struct Tiles {
   __device__ static int voff(int r, int c) { return r * kBK + 16 * (c ^ vswz(r)); }
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// LDS byte address of a __shared__ object, in an SGPR.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>((uintptr_t)(const lds_void*)p));
-}
-
-// Global -> LDS DMA of one 16-byte (or 4-byte) chunk per lane into LDS bytes
-// [lds + 16 lane, +16) (resp. [lds + 4 lane, +4)).  Issued from asm so that the compiler's
-// wait-count tracking does not treat every later LDS read as dependent on it; completion is
-// awaited explicitly (vmcnt) before the barrier that publishes the tile.
-__device__ __forceinline__ void dma16(uint32_t lds, const void* gbase, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :: "s"(lds), "v"(voff), "s"(gbase) : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(uint32_t lds, const void* gbase, uint32_t voff) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
-               :: "s"(lds), "v"(voff), "s"(gbase) : "memory", "m0");
-}
-
 struct AttnArgs {
   const int8_t* qhat;
   const int8_t* khat;
@@ -96,18 +76,6 @@ struct AttnArgs {
   float qk_scale;   // sm_scale * log2(e)
   int xcd_map;      // 1: heads grouped per XCD
 };
-
-__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// max over the two lanes that share a query (l and l ^ 32), on the VALU
-__device__ __forceinline__ float pair_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float pair_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 // S^T = K^ Q^T of one 64-key tile on the INT8 MFMA (exact INT32): two 32-key halves.
 template <int D>
@@ -349,19 +317,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       float o[4];
 #pragma unroll
       for (int k = 0; k < 4; k++) o[k] = fmaf(O[c][4 * b + k] * inv, dvp[ch + k], vmp[ch + k]);
-      if (OUT == 2) {
-        *reinterpret_cast<float4*>(reinterpret_cast<float*>(a.out) + orow + ch) = make_float4(o[0], o[1], o[2], o[3]);
-      } else if (OUT == 1) {
-        uint2 u;
-        u.x = f32_to_fp16_bits(o[0]) | (f32_to_fp16_bits(o[1]) << 16);
-        u.y = f32_to_fp16_bits(o[2]) | (f32_to_fp16_bits(o[3]) << 16);
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + orow + ch) = u;
-      } else {
-        uint2 u;
-        u.x = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
-        u.y = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
-        *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + orow + ch) = u;
-      }
+      store_out4<OUT>(a.out, orow + ch, o);
     }
   }
 }

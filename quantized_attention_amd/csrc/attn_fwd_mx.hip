@@ -1,0 +1,365 @@
+// attn_fwd_mx.hip -- fused quantized attention forward, MXFP4 variant (gfx950).
+//
+// "SageAttention3" summary, 3.4 "The NVFP4 Microscaling Format and Quantization Operator":
+// each operand of the two products is E2M1 with one power-of-two (E8M0) scale per 32
+// elements along the product's reduction dimension, and a product is the sum over blocks of
+// X_a X_b (a^ . b^)_blk.  With the smoothing of "SageAttention2 Technical Report" 3.4, per
+// 128-query block i and 64-key tile j:
+//   S   = sum_blk X_Q X_K (Q^ K^T)_blk + Delta S_ij
+//   m   = max(m, rowmax S);  P~ = exp(S - m);  l = e^{m_old - m} l + rowsum P~   (FP32)
+//   P^  = E2M1(P~ / X_P), X_P per 32 keys of the row (the smallest 2^e with max <= 6 * 2^e)
+//   O   = e^{m_old - m} O + sum_blk X_P X_V (P^ V^)_blk
+//   out = O / l (+ V_m)
+//
+// Mapping.  As in the INT8/FP8 kernel, S^T = K^ Q^T on the 32x32 MFMA gives each lane one
+// query and 16 keys of each 32-key half (keys 8b + 4h + k, h = lane / 32); here the MFMA is
+// v_mfma_scale_f32_32x32x64_f8f6f4 with both operands E2M1 (64 channels per instruction,
+// each lane half a 32-channel block whose E8M0 scale the lane supplies: byte-selected from
+// one scale word per tile for K, per kernel for Q).  The block scales are applied inside
+// the MFMA, so the FP32 scores need one FMA (sm_scale log2 e, Delta S) and no dequant.
+// The P~ block of a row is 32 contiguous keys: its maximum is exp2 of the block's largest
+// score (the same exp2 the element gets), which sets the E8M0 scale; the hardware
+// conversion takes that scale directly (v_cvt_scalef32_pk_fp4_f32 divides by the power of
+// two of the scale's exponent field and rounds to nearest even).  The FP4 PV MFMA consumes
+// 32 keys per lane half, so the two lane halves swap their packed fragments once
+// (v_permlane32_swap): afterwards half h holds the keys 32h..32h+31, the P block h and its
+// scale, and V^ was stored with its keys in that order (vperm_mx).  O^T = V^T P^T then
+// accumulates through the MFMA's FP32 C operand (lazy rescale when a row's maximum rises),
+// or, as a variant, from a zero accumulator with one VALU FMA into O.
+#include "attn_device.hpp"
+
+namespace sage {
+namespace {
+
+using namespace attn;
+
+// LDS tiles, unpadded, 16-byte chunks XOR-swizzled within a row so that the 16 lanes a
+// ds_read_b128 serves at once (16 consecutive rows, one chunk column) hit 16 distinct
+// 16-byte bank groups.
+template <int D>
+struct MxTiles {
+  static constexpr int KROW = D / 2;          // bytes per K^ row (two E2M1 codes per byte)
+  static constexpr int KCH = KROW / 16;       // 16-byte chunks per K^ row
+  static constexpr int KRPL = 256 / KROW;     // K^ rows per 256-byte bank line
+  static constexpr int KBYTES = kBK * KROW;
+  static constexpr int VROW = kBK / 2;        // V^ rows are channels: 64 keys, 32 bytes
+  static constexpr int VBYTES = D * VROW;
+  static constexpr int KDMA = KBYTES / 1024;  // 1 KiB LDS-DMA wave instructions per tile
+  static constexpr int VDMA = VBYTES / 1024;
+  __device__ static int kswz(int r) { return (r / KRPL) & (KCH - 1); }
+  __device__ static int vswz(int r) { return (r >> 3) & 1; }
+  __device__ static int koff(int r, int c) { return r * KROW + 16 * (c ^ kswz(r)); }
+  __device__ static int voff(int r, int c) { return r * VROW + 16 * (c ^ vswz(r)); }
+};
+
+struct MxArgs {
+  const uint8_t* qhat;  // [BH][Np][D/2]
+  const uint8_t* khat;  // [BH][Mp][D/2]
+  const uint8_t* vhat;  // [BH][nkt][D][32]
+  const uint8_t* qsc;   // [BH][Np][D/32]
+  const uint8_t* ksc;   // [BH][nkt][64][4]
+  const uint8_t* vsc;   // [BH][nkt][64][4]
+  const float* vmean;
+  const float* ds;      // Delta S * sm_scale * log2(e)
+  void* out;
+  int N, M, BH, nqb, nkt, Np, Mp;
+  float qk_scale;       // sm_scale * log2(e)
+  int xcd_map;
+};
+
+// One block-scaled FP4 MFMA: 32x32 output, 64-deep reduction; a and b carry 32 E2M1 codes
+// per lane (the operand's upper half is not read for FP4), sa / sb the lanes' scale words
+// with the E8M0 byte selected by OA / OB.
+template <int OA, int OB>
+__device__ __forceinline__ v16f mfma_fp4(const v4i& a, const v4i& b, const v16f& c, uint32_t sa, uint32_t sb) {
+  const v8i a8 = __builtin_shufflevector(a, a, 0, 1, 2, 3, -1, -1, -1, -1);
+  const v8i b8 = __builtin_shufflevector(b, b, 0, 1, 2, 3, -1, -1, -1, -1);
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, OA, (int)sa, OB, (int)sb);
+}
+
+// S^T = sum_blk X_K X_Q (K^ Q^T)_blk of one 64-key tile: two 32-key halves, D/64 MFMAs each.
+// The K scale word of lane l holds byte 2T + c for key 32T + l%32, channel block 2c + l/32;
+// the Q scale word byte c for channel block 2c + l/32.
+template <int D>
+__device__ __forceinline__ void qk_tile_mx(const uint8_t* __restrict__ sK, const v4i (&qf)[D / 64], uint32_t ks,
+                                           uint32_t qs, int h, int col, v16f (&acc)[2]) {
+  static_for<0, 2>([&](auto Tc) {
+    constexpr int T = decltype(Tc)::value;
+#pragma unroll
+    for (int r = 0; r < 16; r++) acc[T][r] = 0.0f;
+    static_for<0, D / 64>([&](auto Cc) {
+      constexpr int C = decltype(Cc)::value;
+      const v4i kf = *reinterpret_cast<const v4i*>(&sK[MxTiles<D>::koff(32 * T + col, 2 * C + h)]);
+      acc[T] = mfma_fp4<2 * T + C, C>(kf, qf[C], acc[T], ks, qs);
+    });
+  });
+}
+
+template <int D, bool CAUSAL, bool ACC_VALU>
+__device__ __forceinline__ void softmax_pv_mx(const v16f (&acc)[2], const uint8_t* __restrict__ sV,
+                                              const float* __restrict__ sDS, uint32_t vs, float qk_scale, int h,
+                                              int col, int key0, int qrow, int M, bool masked, v16f (&O)[D / 32],
+                                              float& m_run, float& l_run) {
+  // ---- scores: sm_scale log2(e) and Delta S (the block scales were applied by the MFMA) ----
+  float sc[2][16];
+#pragma unroll
+  for (int T = 0; T < 2; T++)
+#pragma unroll
+    for (int r = 0; r < 16; r++)
+      sc[T][r] = fmaf(acc[T][r], qk_scale, sDS[32 * T + 8 * (r >> 2) + 4 * h + (r & 3)]);
+  if (masked) {
+    asm volatile("" ::: "memory");  // keep this a real branch (interior tiles skip it)
+    int lim = M - 1 - key0;
+    if (CAUSAL) lim = min(lim, qrow - key0);
+    lim -= 4 * h;
+#pragma unroll
+    for (int T = 0; T < 2; T++)
+#pragma unroll
+      for (int r = 0; r < 16; r++)
+        sc[T][r] = (32 * T + 8 * (r >> 2) + (r & 3) <= lim) ? sc[T][r] : -INFINITY;
+  }
+  // ---- running max; each 32-key half's maximum is also its P block's ----
+  float mb[2];
+#pragma unroll
+  for (int T = 0; T < 2; T++) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; r++) m = fmaxf(m, sc[T][r]);
+    mb[T] = pair_max(m);
+  }
+  const float m_new = fmaxf(m_run, fmaxf(mb[0], mb[1]));
+  const float base = (m_new == -INFINITY) ? 0.0f : m_new;
+  const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile, exactly 1 if m is unchanged
+  m_run = m_new;
+  // E8M0 of each P block: from its largest P~ (0 for a fully masked block: code 0)
+  const uint32_t pc0 = e8m0_code(fast_exp2(mb[0] - base));
+  const uint32_t pc1 = e8m0_code(fast_exp2(mb[1] - base));
+  // ---- P~ (FP32), row sum of the unquantized values, E2M1 pack ----
+  float psum = 0.0f;
+  uint32_t pk[2][2];
+#pragma unroll
+  for (int T = 0; T < 2; T++) {
+    const float scl = __uint_as_float((T ? pc1 : pc0) << 23);
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+      float p[8];
+#pragma unroll
+      for (int e = 0; e < 8; e++) p[e] = fast_exp2(sc[T][8 * q + e] - base);
+      psum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      uint32_t wd = 0;
+      wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, p[0], p[1], scl, 0);
+      wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, p[2], p[3], scl, 1);
+      wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, p[4], p[5], scl, 2);
+      wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, p[6], p[7], scl, 3);
+      pk[T][q] = wd;
+    }
+  }
+  l_run = fmaf(l_run, alpha, psum);
+  // ---- regroup: lane half h takes the whole 32-key half T = h (half 0's keys first) ----
+#pragma unroll
+  for (int q = 0; q < 2; q++) {
+    const auto r = __builtin_amdgcn_permlane32_swap(pk[0][q], pk[1][q], false, false);
+    pk[0][q] = r[0];
+    pk[1][q] = r[1];
+  }
+  const v4i pf = {(int)pk[0][0], (int)pk[0][1], (int)pk[1][0], (int)pk[1][1]};
+  const uint32_t pcode = h ? pc1 : pc0;
+  // ---- O^T += sum_blk X_V X_P (V^T P^T)_blk per 32-channel sub-tile ----
+  if (!ACC_VALU) {
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int c = 0; c < D / 32; c++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) O[c][r] *= alpha;
+    }
+  }
+  static_for<0, D / 32>([&](auto gc) {
+    constexpr int g = decltype(gc)::value;
+    const v4i vf = *reinterpret_cast<const v4i*>(&sV[MxTiles<D>::voff(32 * g + col, h)]);
+    if (ACC_VALU) {
+      v16f R;
+#pragma unroll
+      for (int r = 0; r < 16; r++) R[r] = 0.0f;
+      R = mfma_fp4<g, 0>(vf, pf, R, vs, pcode);
+#pragma unroll
+      for (int r = 0; r < 16; r++) O[g][r] = fmaf(O[g][r], alpha, R[r]);
+    } else {
+      O[g] = mfma_fp4<g, 0>(vf, pf, O[g], vs, pcode);
+    }
+  });
+}
+
+template <int D, bool CAUSAL, int OUT, bool ACC_VALU>  // OUT: 0 bf16, 1 fp16, 2 fp32
+__global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(MxArgs a) {
+  using TL = MxTiles<D>;
+  constexpr int NG = D / 32;  // 32-channel sub-tiles of O
+  constexpr int NB = 4;       // LDS ring: tile j computed, j+1 read by the next QK, j+2, j+3 arriving
+  __shared__ __attribute__((aligned(1024))) uint8_t sK[NB][TL::KBYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sV[NB][TL::VBYTES];
+  __shared__ __attribute__((aligned(256))) float sDS[NB][kBK];
+  __shared__ __attribute__((aligned(256))) uint32_t sKS[NB][64];
+  __shared__ __attribute__((aligned(256))) uint32_t sVS[NB][64];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = lane >> 5, col = lane & 31;
+
+  int bh, qi;
+  {
+    const int L = blockIdx.x;
+    if (a.xcd_map) {  // XCD x gets heads x, x+8, ...; a head's blocks stay together
+      const int x = L % kXCD, r = L / kXCD;
+      bh = x + kXCD * (r / a.nqb);
+      qi = r % a.nqb;
+    } else {
+      bh = L / a.nqb;
+      qi = L % a.nqb;
+    }
+  }
+  const int qb = CAUSAL ? (a.nqb - 1 - qi) : qi;  // heavy blocks first
+  const int q0 = qb * kBQ;
+  const int wq0 = q0 + 32 * w;
+  const int qrow = wq0 + col;
+
+  // ---- Q^ fragments (B operand): query qrow, channels 64c + 32h .. +32; scale bytes ----
+  v4i qf[D / 64];
+  uint32_t qs = 0;
+  {
+    const size_t row = (size_t)bh * a.Np + qrow;
+    const uint8_t* qp = a.qhat + row * (D / 2) + 16 * h;
+#pragma unroll
+    for (int c = 0; c < D / 64; c++) qf[c] = *reinterpret_cast<const v4i*>(qp + 32 * c);
+    const uint8_t* sp = a.qsc + row * (D / 32);
+#pragma unroll
+    for (int c = 0; c < D / 64; c++) qs |= (uint32_t)sp[2 * c + h] << (8 * c);
+  }
+
+  v16f O[NG];
+#pragma unroll
+  for (int c = 0; c < NG; c++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) O[c][r] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  const int jend = CAUSAL ? min(a.nkt, (q0 + kBQ + kBK - 1) / kBK) : a.nkt;
+  const uint8_t* kbase = a.khat + (size_t)bh * a.Mp * (D / 2);
+  const uint8_t* vbase = a.vhat + (size_t)bh * a.nkt * TL::VBYTES;
+  const float* dsbase = a.ds + ((size_t)bh * a.nqb + qb) * a.Mp;
+  const uint8_t* ksbase = a.ksc + (size_t)bh * a.nkt * 256;
+  const uint8_t* vsbase = a.vsc + (size_t)bh * a.nkt * 256;
+
+  // ---- staging by LDS DMA.  D = 128: wave w moves K^ KiB w and V^ KiB w; D = 64: waves 0-1
+  // move K^, waves 2-3 move V^.  Waves 0, 1, 2 also move Delta S, the K scales, the V scales.
+  static_assert(TL::KDMA == TL::VDMA && (TL::KDMA == 4 || TL::KDMA == 2), "tile size");
+  const bool movesK = TL::KDMA == 4 || w < 2, movesV = TL::VDMA == 4 || w >= 2;
+  const int kchunk = movesK ? w : 0, vchunk = movesV ? (TL::VDMA == 4 ? w : w - 2) : 0;
+  int koffs = 0, voffs = 0;
+  {
+    const int q = kchunk * 64 + lane;  // 16-byte LDS chunk this lane fills
+    const int r = q / TL::KCH;
+    koffs = r * TL::KROW + 16 * ((q % TL::KCH) ^ TL::kswz(r));
+    const int qv = vchunk * 64 + lane;
+    const int rv = qv / 2;
+    voffs = rv * TL::VROW + 16 * ((qv & 1) ^ TL::vswz(rv));
+  }
+  auto dma = [&](int j, int slot) {
+    if (movesK) dma16(lds_addr(&sK[slot][kchunk * 1024]), kbase + (size_t)j * TL::KBYTES, koffs);
+    if (movesV) dma16(lds_addr(&sV[slot][vchunk * 1024]), vbase + (size_t)j * TL::VBYTES, voffs);
+    if (w == 0) dma4(lds_addr(&sDS[slot][0]), dsbase + (size_t)j * kBK, 4 * lane);
+    if (w == 1) dma4(lds_addr(&sKS[slot][0]), ksbase + (size_t)j * 256, 4 * lane);
+    if (w == 2) dma4(lds_addr(&sVS[slot][0]), vsbase + (size_t)j * 256, 4 * lane);
+  };
+  // DMA instructions per tile: waves 0-2 issue one more than wave 3 (the scale / Delta S line).
+  constexpr int kPer012 = (TL::KDMA == 4 ? 2 : 1) + 1, kPer3 = kPer012 - 1;
+  auto publish = [&](bool newest_in_flight) {
+    if (!newest_in_flight)
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if (w < 3)
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kPer012) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kPer3) : "memory");
+  };
+
+  auto skip_t = [&](int j) { return CAUSAL && j * kBK > wq0 + 31; };  // fully masked for this wave
+  auto body = [&](int j, v16f (&cur)[2], v16f (&nxt)[2]) {
+    if (j + 3 < jend) dma(j + 3, (j + 3) % NB);
+    if (j + 1 < jend && !skip_t(j + 1)) {
+      const int b1 = (j + 1) % NB;
+      qk_tile_mx<D>(sK[b1], qf, sKS[b1][lane], qs, h, col, nxt);
+    }
+    if (!skip_t(j)) {
+      const int key0 = j * kBK;
+      const bool masked = (CAUSAL && key0 + kBK - 1 > wq0) || (key0 + kBK > a.M);
+      const int b = j % NB;
+      softmax_pv_mx<D, CAUSAL, ACC_VALU>(cur, sV[b], sDS[b], sVS[b][lane], a.qk_scale, h, col, key0, qrow, a.M,
+                                         masked, O, m_run, l_run);
+    }
+    publish(j + 3 < jend);
+  };
+
+  dma(0, 0);
+  if (jend > 1) dma(1, 1);
+  if (jend > 2) dma(2, 2);
+  publish(jend > 2);
+  v16f accA[2], accB[2];
+  qk_tile_mx<D>(sK[0], qf, sKS[0][lane], qs, h, col, accA);  // tile 0 is never masked away
+  for (int j = 0; j < jend; j += 2) {
+    body(j, accA, accB);
+    if (j + 1 < jend) body(j + 1, accB, accA);
+  }
+
+  // ---- epilogue: O / l (+ V_m) ----
+  const float l_tot = pair_sum(l_run);
+  if (qrow >= a.N) return;
+  const float inv = 1.0f / l_tot;
+  const float* vmp = a.vmean + (size_t)bh * D;
+  const size_t orow = ((size_t)bh * a.N + qrow) * D;
+#pragma unroll
+  for (int c = 0; c < NG; c++) {
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      const int ch = 32 * c + 8 * b + 4 * h;
+      float o[4];
+#pragma unroll
+      for (int k = 0; k < 4; k++) o[k] = fmaf(O[c][4 * b + k], inv, vmp[ch + k]);
+      store_out4<OUT>(a.out, orow + ch, o);
+    }
+  }
+}
+
+template <int D, bool CAUSAL, bool ACC_VALU>
+hipError_t launch_d(const Problem& p, const MxArgs& a, hipStream_t s) {
+  dim3 grid(p.nqb * p.BH);
+  const int out = p.out_fp32 ? 2 : (p.fp16 ? 1 : 0);
+  if (out == 2)
+    hipLaunchKernelGGL((attn_fwd_mx_kernel<D, CAUSAL, 2, ACC_VALU>), grid, dim3(256), 0, s, a);
+  else if (out == 1)
+    hipLaunchKernelGGL((attn_fwd_mx_kernel<D, CAUSAL, 1, ACC_VALU>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_mx_kernel<D, CAUSAL, 0, ACC_VALU>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D, bool ACC_VALU>
+hipError_t launch_c(const Problem& p, const MxArgs& a, hipStream_t s) {
+  return p.causal ? launch_d<D, true, ACC_VALU>(p, a, s) : launch_d<D, false, ACC_VALU>(p, a, s);
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_mx(const Problem& p, const Workspace& w, void* out, hipStream_t s) {
+  MxArgs a;
+  a.qhat = reinterpret_cast<const uint8_t*>(w.qhat);
+  a.khat = reinterpret_cast<const uint8_t*>(w.khat);
+  a.vhat = w.vhat;
+  a.qsc = w.qsc; a.ksc = w.ksc; a.vsc = w.vsc;
+  a.vmean = w.vmean; a.ds = w.ds; a.out = out;
+  a.N = p.N; a.M = p.M; a.BH = p.BH; a.nqb = p.nqb; a.nkt = p.nkt; a.Np = p.Np; a.Mp = p.Mp;
+  a.qk_scale = p.sm_scale * kLog2e;
+  a.xcd_map = (p.BH % kXCD == 0) ? 1 : 0;
+  const bool valu = (p.variant & SAGE_ACC_VALU) != 0;
+  if (p.d == 128) return valu ? launch_c<128, true>(p, a, s) : launch_c<128, false>(p, a, s);
+  return valu ? launch_c<64, true>(p, a, s) : launch_c<64, false>(p, a, s);
+}
+
+}  // namespace sage

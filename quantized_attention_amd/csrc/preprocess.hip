@@ -146,9 +146,10 @@ __global__ void kv_finalize_kernel(const double* __restrict__ kpart, const doubl
 }
 
 // ---- Q: block mean (and its bf16 head/tail), gamma(Q), per-token scale, INT8 codes ----
-template <int D>
+template <int D, bool MX>
 __global__ __launch_bounds__(256) void q_prep_kernel(const uint16_t* __restrict__ Q,
                                                      int8_t* __restrict__ qhat, float* __restrict__ dq,
+                                                     uint8_t* __restrict__ qsc,
                                                      float* __restrict__ qmean, uint16_t* __restrict__ qm_hi,
                                                      uint16_t* __restrict__ qm_lo, int N, int Np, int nqb,
                                                      bool fp16) {
@@ -197,22 +198,41 @@ __global__ __launch_bounds__(256) void q_prep_kernel(const uint16_t* __restrict_
       g[e] = (r < n) ? load_in(sq, (size_t)r * RS + c, fp16) - sm[c] : 0.0f;
       am = amax_upd(am, g[e]);
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float o = __shfl_xor(am, off);
-      am = o > am ? o : am;
-    }
-    const float s = (r < n) ? int8_scale(am) : 1.0f;
     const size_t row = (size_t)bh * Np + r0 + r;
-    if (lane == 0) dq[row] = s;
-    uint32_t word = 0;
+    if constexpr (MX) {
+      // one E8M0 scale per 32 channels: the block's lanes are 32 / CPL consecutive lanes
 #pragma unroll
-    for (int e = 0; e < CPL; e++)
-      word |= (uint32_t)(uint8_t)((r < n) ? int8_code(g[e], s) : 0) << (8 * e);
-    if (CPL == 2)
-      *reinterpret_cast<uint16_t*>(qhat + row * D + lane * CPL) = (uint16_t)word;
-    else
-      qhat[row * D + lane] = (int8_t)word;
+      for (int off = 16 / CPL; off >= 1; off >>= 1) {
+        const float o = __shfl_xor(am, off);
+        am = o > am ? o : am;
+      }
+      const uint32_t code = e8m0_code(am);  // padded rows: amax 0 -> code 0, values 0
+      const float sc = __uint_as_float(code << 23);
+      uint8_t* qo = reinterpret_cast<uint8_t*>(qhat) + row * (D / 2);
+      if (CPL == 2) {
+        qo[lane] = (uint8_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, g[0], g[CPL - 1], sc, 0);
+      } else {
+        const float nb = __shfl_xor(g[0], 1);
+        if (!(lane & 1)) qo[lane >> 1] = (uint8_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, g[0], nb, sc, 0);
+      }
+      if ((lane & (32 / CPL - 1)) == 0) qsc[row * (D / 32) + lane / (32 / CPL)] = (uint8_t)code;
+    } else {
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const float o = __shfl_xor(am, off);
+        am = o > am ? o : am;
+      }
+      const float s = (r < n) ? int8_scale(am) : 1.0f;
+      if (lane == 0) dq[row] = s;
+      uint32_t word = 0;
+#pragma unroll
+      for (int e = 0; e < CPL; e++)
+        word |= (uint32_t)(uint8_t)((r < n) ? int8_code(g[e], s) : 0) << (8 * e);
+      if (CPL == 2)
+        *reinterpret_cast<uint16_t*>(qhat + row * D + lane * CPL) = (uint16_t)word;
+      else
+        qhat[row * D + lane] = (int8_t)word;
+    }
   }
 }
 
@@ -228,14 +248,17 @@ struct KVArgs {
   float* dk;
   uint8_t* vhat;
   float* ds;  // null: no Delta S
+  uint8_t* ksc;  // MX: E8M0 of gamma(K) blocks, [BH][nkt][64][4]
+  uint8_t* vsc;  // MX: E8M0 of V' blocks, [BH][nkt][64][4]
   float ds_scale;
   int M, Mp, nkt, nqb, causal;
   bool fp16;
 };
 
 // ---- one 64-key tile: gamma(K), group scales, K^; Delta S against every query block;
-// V' / dV -> E4M3, transposed in the P-fragment key order ----
-template <int D>
+// V' / dV -> E4M3, transposed in the P-fragment key order.  MX: gamma(K) and V' in E2M1
+// with an E8M0 scale per 32 channels of a key / per 32 tokens of a channel ----
+template <int D, bool MX>
 __global__ __launch_bounds__(256) void kv_quant_kernel(KVArgs a) {
   constexpr int RS = D + 8;                 // bf16 split of gamma(K), 16-byte aligned rows
   constexpr int CH = kBK * D / 8 / 256;     // 8-element chunks per thread
@@ -275,13 +298,15 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(KVArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; e++) g[i][e] = 0.0f;
     }
-    const int grp = kgroup(row);
-    float m = 0.0f;
+    if constexpr (!MX) {
+      const int grp = kgroup(row);
+      float m = 0.0f;
 #pragma unroll
-    for (int e = 0; e < 8; e++) m = amax_upd(m, g[i][e]);
+      for (int e = 0; e < 8; e++) m = amax_upd(m, g[i][e]);
 #pragma unroll
-    for (int q = 0; q < 4; q++)
-      if (q == grp) am[q] = m > am[q] ? m : am[q];
+      for (int q = 0; q < 4; q++)
+        if (q == grp) am[q] = m > am[q] ? m : am[q];
+    }
     v4i hv, lv;
 #pragma unroll
     for (int e = 0; e < 4; e++) {
@@ -293,6 +318,38 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(KVArgs a) {
     *reinterpret_cast<v4i*>(&sAh[row * RS + c0]) = hv;
     *reinterpret_cast<v4i*>(&sAl[row * RS + c0]) = lv;
   }
+  if constexpr (MX) {
+    // ---- K^ in E2M1: the 4 threads holding a key's 32-channel block are consecutive lanes ----
+    uint8_t* kout = reinterpret_cast<uint8_t*>(a.khat) + ((size_t)bh * a.Mp + t0) * (D / 2);
+    uint8_t* sco = a.ksc + ((size_t)bh * a.nkt + u) * 256;
+#pragma unroll
+    for (int i = 0; i < CH; i++) {
+      const int x = tid + 256 * i, row = x / (D / 8), c0 = (x % (D / 8)) * 8;
+      float m = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; e++) m = amax_upd(m, g[i][e]);
+      float o = __shfl_xor(m, 1);
+      m = o > m ? o : m;
+      o = __shfl_xor(m, 2);
+      m = o > m ? o : m;
+      const uint32_t code = e8m0_code(m);  // keys >= M: all zero -> code 0, codes 0
+      const float sc = __uint_as_float(code << 23);
+      uint32_t wd = 0;
+      wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, g[i][0], g[i][1], sc, 0);
+      wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, g[i][2], g[i][3], sc, 1);
+      wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, g[i][4], g[i][5], sc, 2);
+      wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, g[i][6], g[i][7], sc, 3);
+      *reinterpret_cast<uint32_t*>(kout + (size_t)row * (D / 2) + c0 / 2) = wd;
+      if ((x & 3) == 0) {
+        // A-operand scale of MFMA lane 32*(b%2) + row%32 (b = channel block), byte 2T + b/2
+        const int b = c0 >> 5, T = row >> 5, l = 32 * (b & 1) + (row & 31);
+        if (D == 128)
+          sco[4 * l + 2 * T + (b >> 1)] = (uint8_t)code;
+        else
+          *reinterpret_cast<uint16_t*>(sco + 4 * l + 2 * T) = (uint16_t)code;  // byte 2T+1 = 0
+      }
+    }
+  } else {
 #pragma unroll
   for (int q = 0; q < 4; q++) {
     float m = am[q];
@@ -331,6 +388,8 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(KVArgs a) {
       *reinterpret_cast<uint2*>(kout + (size_t)row * D + c0) = make_uint2(w0, w1);
     }
   }
+  }
+  __syncthreads();  // sAh / sAl complete before the Delta S MFMAs read them
 
   // ---- Delta S^T[key][block] = gamma(K) q^T on the bf16 MFMA, split operands ----
   if (a.ds) {
@@ -373,6 +432,7 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(KVArgs a) {
   }
 
   // ---- V: V' / dV (IEEE division), saturated to the E4M3 range, staged in LDS ----
+  // (MX: V' itself; the block scale comes from the staged values)
   {
     const float* vm = a.vmean + (size_t)bh * D;
     const float* sc = a.dv + (size_t)bh * D;
@@ -384,9 +444,13 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(KVArgs a) {
         widen8(vraw[i], a.fp16, w);
 #pragma unroll
         for (int e = 0; e < 8; e++) {
-          float y = __fdiv_rn(w[e] - vm[c0 + e], sc[c0 + e]);
-          y = y > 448.0f ? 448.0f : (y < -448.0f ? -448.0f : y);  // NaN stays NaN
-          w[e] = y;
+          if constexpr (MX) {
+            w[e] = w[e] - vm[c0 + e];
+          } else {
+            float y = __fdiv_rn(w[e] - vm[c0 + e], sc[c0 + e]);
+            y = y > 448.0f ? 448.0f : (y < -448.0f ? -448.0f : y);  // NaN stays NaN
+            w[e] = y;
+          }
         }
       } else {
 #pragma unroll
@@ -397,13 +461,43 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(KVArgs a) {
     }
   }
   __syncthreads();
-  uint8_t* vout = a.vhat + ((size_t)bh * a.nkt + u) * (size_t)D * kBK;
-  for (int x = tid; x < D * (kBK / 4); x += 256) {
-    const int c = x / (kBK / 4), p0 = (x % (kBK / 4)) * 4;
-    const int h = p0 >> 5, b0 = p0 & 31;
-    int wd = __builtin_amdgcn_cvt_pk_fp8_f32(sv[kperm(h, b0)][c], sv[kperm(h, b0 + 1)][c], 0, false);
-    wd = __builtin_amdgcn_cvt_pk_fp8_f32(sv[kperm(h, b0 + 2)][c], sv[kperm(h, b0 + 3)][c], wd, true);
-    *reinterpret_cast<int*>(vout + (size_t)c * kBK + p0) = wd;
+  if constexpr (MX) {
+    // one thread per (channel, 32-token half): scale, then 32 codes in the vperm_mx order
+    if (tid < 2 * D) {
+      const int c = tid % D, T = tid / D;
+      float m = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 32; k++) m = amax_upd(m, sv[32 * T + k][c]);
+      const uint32_t code = e8m0_code(m);
+      const float scf = __uint_as_float(code << 23);
+      v4i out;
+#pragma unroll
+      for (int q = 0; q < 4; q++) {
+        // byte e of word q holds nibbles j = 8q + 2e, j + 1: keys vperm_mx(T, j), + 1
+        const int k0 = vperm_mx(T, 8 * q), k1 = vperm_mx(T, 8 * q + 2);
+        const int k2 = vperm_mx(T, 8 * q + 4), k3 = vperm_mx(T, 8 * q + 6);
+        uint32_t wd = 0;
+        wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, sv[k0][c], sv[k0 + 1][c], scf, 0);
+        wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, sv[k1][c], sv[k1 + 1][c], scf, 1);
+        wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, sv[k2][c], sv[k2 + 1][c], scf, 2);
+        wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, sv[k3][c], sv[k3 + 1][c], scf, 3);
+        out[q] = (int)wd;
+      }
+      uint8_t* vout = a.vhat + (((size_t)bh * a.nkt + u) * D + c) * (kBK / 2) + 16 * T;
+      *reinterpret_cast<v4i*>(vout) = out;
+      uint8_t* sco = a.vsc + ((size_t)bh * a.nkt + u) * 256 + 4 * (32 * T + (c & 31));
+      sco[c >> 5] = (uint8_t)code;
+      if (D == 64 && (c >> 5) == 1) *reinterpret_cast<uint16_t*>(sco + 2) = 0;  // bytes g >= d/32
+    }
+  } else {
+    uint8_t* vout = a.vhat + ((size_t)bh * a.nkt + u) * (size_t)D * kBK;
+    for (int x = tid; x < D * (kBK / 4); x += 256) {
+      const int c = x / (kBK / 4), p0 = (x % (kBK / 4)) * 4;
+      const int h = p0 >> 5, b0 = p0 & 31;
+      int wd = __builtin_amdgcn_cvt_pk_fp8_f32(sv[kperm(h, b0)][c], sv[kperm(h, b0 + 1)][c], 0, false);
+      wd = __builtin_amdgcn_cvt_pk_fp8_f32(sv[kperm(h, b0 + 2)][c], sv[kperm(h, b0 + 3)][c], wd, true);
+      *reinterpret_cast<int*>(vout + (size_t)c * kBK + p0) = wd;
+    }
   }
 }
 
@@ -428,12 +522,14 @@ hipError_t launch_kv_finalize(const Problem& p, const Workspace& w, hipStream_t 
 
 hipError_t launch_q_prep(const Problem& p, const void* q, const Workspace& w, hipStream_t s) {
   const dim3 grid(p.nqb, p.BH);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, (const uint16_t*)q, w.qhat, w.dq, w.qsc, w.qmean, w.qm_hi,
+                       w.qm_lo, p.N, p.Np, p.nqb, p.fp16);
+  };
   if (p.d == 128)
-    hipLaunchKernelGGL(q_prep_kernel<128>, grid, dim3(256), 0, s, (const uint16_t*)q, w.qhat, w.dq, w.qmean,
-                       w.qm_hi, w.qm_lo, p.N, p.Np, p.nqb, p.fp16);
+    p.mx ? go(q_prep_kernel<128, true>) : go(q_prep_kernel<128, false>);
   else
-    hipLaunchKernelGGL(q_prep_kernel<64>, grid, dim3(256), 0, s, (const uint16_t*)q, w.qhat, w.dq, w.qmean,
-                       w.qm_hi, w.qm_lo, p.N, p.Np, p.nqb, p.fp16);
+    p.mx ? go(q_prep_kernel<64, true>) : go(q_prep_kernel<64, false>);
   return hipGetLastError();
 }
 
@@ -451,6 +547,8 @@ hipError_t launch_kv_quant(const Problem& p, const void* k, const void* v, const
   a.dk = w.dk;
   a.vhat = w.vhat;
   a.ds = ds_out;
+  a.ksc = w.ksc;
+  a.vsc = w.vsc;
   a.ds_scale = ds_scale;
   a.M = p.M;
   a.Mp = p.Mp;
@@ -459,10 +557,13 @@ hipError_t launch_kv_quant(const Problem& p, const void* k, const void* v, const
   a.causal = p.causal;
   a.fp16 = p.fp16;
   const dim3 grid(p.nkt, p.BH);
-  if (p.d == 128)
-    hipLaunchKernelGGL(kv_quant_kernel<128>, grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(kv_quant_kernel<64>, grid, dim3(256), 0, s, a);
+  if (p.d == 128) {
+    if (p.mx) hipLaunchKernelGGL((kv_quant_kernel<128, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((kv_quant_kernel<128, false>), grid, dim3(256), 0, s, a);
+  } else {
+    if (p.mx) hipLaunchKernelGGL((kv_quant_kernel<64, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((kv_quant_kernel<64, false>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

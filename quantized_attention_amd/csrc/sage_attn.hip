@@ -19,12 +19,13 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t workspace_layout(const Problem& p, size_t* sizes) {
   const size_t BH = (size_t)p.BH, d = (size_t)p.d;
+  const size_t qd = p.mx ? d / 2 : d;                // bytes per quantized row
   size_t s[kWsSlices];
-  s[0] = BH * p.Np * d;                              // qhat
-  s[1] = BH * p.Mp * d;                              // khat
-  s[2] = BH * p.nkt * d * kBK;                       // vhat
-  s[3] = BH * p.Np * sizeof(float);                  // dq
-  s[4] = BH * p.nkt * 4 * sizeof(float);             // dk
+  s[0] = BH * p.Np * qd;                             // qhat
+  s[1] = BH * p.Mp * qd;                             // khat
+  s[2] = BH * p.nkt * d * (p.mx ? kBK / 2 : kBK);    // vhat
+  s[3] = p.mx ? 0 : BH * p.Np * sizeof(float);       // dq
+  s[4] = p.mx ? 0 : BH * p.nkt * 4 * sizeof(float);  // dk
   s[5] = BH * d * sizeof(float);                     // dv
   s[6] = BH * d * sizeof(float);                     // kmean
   s[7] = BH * d * sizeof(float);                     // vmean
@@ -36,6 +37,9 @@ size_t workspace_layout(const Problem& p, size_t* sizes) {
   s[13] = BH * p.nkt * d * sizeof(float);            // vminp
   s[14] = BH * p.nqb * d * sizeof(uint16_t);         // qm_hi
   s[15] = BH * p.nqb * d * sizeof(uint16_t);         // qm_lo
+  s[16] = p.mx ? BH * p.Np * (d / 32) : 0;           // qsc
+  s[17] = p.mx ? BH * p.nkt * 256 : 0;               // ksc
+  s[18] = p.mx ? BH * p.nkt * 256 : 0;               // vsc
   size_t tot = 0;
   for (int i = 0; i < kWsSlices; i++) {
     if (sizes) sizes[i] = s[i];
@@ -69,11 +73,14 @@ void carve_workspace(const Problem& p, void* base, Workspace* w) {
   w->vminp = (float*)ptr[13];
   w->qm_hi = (uint16_t*)ptr[14];
   w->qm_lo = (uint16_t*)ptr[15];
+  w->qsc = (uint8_t*)ptr[16];
+  w->ksc = (uint8_t*)ptr[17];
+  w->vsc = (uint8_t*)ptr[18];
 }
 
 namespace {
 
-constexpr unsigned kKnownBits = SAGE_SMOOTH_V | SAGE_IN_FP16 | SAGE_OUT_FP32 | SAGE_ACC_VALU;
+constexpr unsigned kKnownBits = SAGE_PATH_MXFP4 | SAGE_SMOOTH_V | SAGE_IN_FP16 | SAGE_OUT_FP32 | SAGE_ACC_VALU;
 
 // Per-device "is gfx950" cache, filled once per device under a mutex.
 int device_check() {
@@ -117,6 +124,7 @@ int make_problem(int B, int H, int N, int M, int d, int causal, float sm_scale, 
   p->fp16 = (variant & SAGE_IN_FP16) != 0;
   p->out_fp32 = (variant & SAGE_OUT_FP32) != 0;
   p->smooth_v = (variant & SAGE_SMOOTH_V) != 0;
+  p->mx = (variant & SAGE_PATH_MXFP4) != 0;
   // grid limits: y = B*H for every kernel, x = blocks/tiles
   if (p->BH > 65535 || p->nkt > (1 << 30)) return SAGE_ERR_INVALID_ARG;
   return SAGE_OK;
@@ -146,7 +154,8 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, const Probl
   int rc = run_preprocess(p, q, k, v, w, p.sm_scale * 1.4426950408889634f, w.ds, s);
   if (rc != SAGE_OK) return rc;
   if (e0 && hipEventRecord(e0, s) != hipSuccess) return SAGE_ERR_LAUNCH;
-  if (launch_attn_fwd(p, w, out, s) != hipSuccess) return SAGE_ERR_LAUNCH;
+  if ((p.mx ? launch_attn_fwd_mx(p, w, out, s) : launch_attn_fwd(p, w, out, s)) != hipSuccess)
+    return SAGE_ERR_LAUNCH;
   if (e1 && hipEventRecord(e1, s) != hipSuccess) return SAGE_ERR_LAUNCH;
   return SAGE_OK;
 }
@@ -223,10 +232,11 @@ int sage_attn_quantize(const void* q, const void* k, const void* v, int B, int H
   struct Copy { void* dst; const void* src; size_t n; } copies[] = {
       {dst->q_hat, w.qhat, sz[0]}, {dst->k_hat, w.khat, sz[1]}, {dst->v_hat, w.vhat, sz[2]},
       {dst->dq, w.dq, sz[3]},      {dst->dk, w.dk, sz[4]},      {dst->dv, w.dv, sz[5]},
-      {dst->k_mean, w.kmean, sz[6]}, {dst->v_mean, w.vmean, sz[7]}, {dst->q_mean, w.qmean, sz[8]}};
+      {dst->k_mean, w.kmean, sz[6]}, {dst->v_mean, w.vmean, sz[7]}, {dst->q_mean, w.qmean, sz[8]},
+      {dst->mx_scales_q, w.qsc, sz[16]}, {dst->mx_scales_k, w.ksc, sz[17]}, {dst->mx_scales_v, w.vsc, sz[18]}};
   for (const Copy& c : copies) {
     if (rc != SAGE_OK) break;
-    if (c.dst && hipMemcpyAsync(c.dst, c.src, c.n, hipMemcpyDeviceToDevice, s) != hipSuccess) rc = SAGE_ERR_LAUNCH;
+    if (c.dst && c.n && hipMemcpyAsync(c.dst, c.src, c.n, hipMemcpyDeviceToDevice, s) != hipSuccess) rc = SAGE_ERR_LAUNCH;
   }
   if (hipFreeAsync(ws, s) != hipSuccess && rc == SAGE_OK) rc = SAGE_ERR_LAUNCH;
   return rc;

@@ -29,15 +29,18 @@ struct Problem {
   unsigned variant;
   int BH, nqb, nkt, Np, Mp;
   bool fp16, out_fp32, smooth_v;
+  bool mx;  // SAGE_PATH_MXFP4
 };
 
-// Device workspace (all 256-byte aligned slices of one allocation).
+// Device workspace (all 256-byte aligned slices of one allocation).  Layouts of the
+// quantized tensors and scales are those sage_attn.h documents for the quantize views
+// (INT8/FP8, or E2M1 codes with E8M0 scales for the MX variant).
 struct Workspace {
-  int8_t* qhat;     // [BH][Np][d]
-  int8_t* khat;     // [BH][Mp][d]
-  uint8_t* vhat;    // [BH][nkt][d][64], keys permuted (see sage_attn.h)
-  float* dq;        // [BH][Np]
-  float* dk;        // [BH][nkt][4]
+  int8_t* qhat;     // [BH][Np][d]            (MX: [BH][Np][d/2] E2M1 pairs)
+  int8_t* khat;     // [BH][Mp][d]            (MX: [BH][Mp][d/2])
+  uint8_t* vhat;    // [BH][nkt][d][64] keys permuted (MX: [BH][nkt][d][32])
+  float* dq;        // [BH][Np]   (not used by MX)
+  float* dk;        // [BH][nkt][4]   (not used by MX)
   float* dv;        // [BH][d]
   float* kmean;     // [BH][d]
   float* vmean;     // [BH][d]
@@ -49,8 +52,11 @@ struct Workspace {
   float* vminp;     // [BH][nkt][d] chunk min of V
   uint16_t* qm_hi;  // [BH][nqb][d] bf16 head of the block mean (Delta S operand)
   uint16_t* qm_lo;  // [BH][nqb][d] bf16 tail: q_mean - hi, rounded to bf16
+  uint8_t* qsc;     // MX: [BH][Np][d/32] E8M0 of gamma(Q) blocks
+  uint8_t* ksc;     // MX: [BH][nkt][64][4] E8M0 of gamma(K) blocks, MFMA A-operand lane order
+  uint8_t* vsc;     // MX: [BH][nkt][64][4] E8M0 of V' blocks, MFMA A-operand lane order
 };
-constexpr int kWsSlices = 16;
+constexpr int kWsSlices = 19;
 
 // Bytes of each workspace slice, in carving order.
 size_t workspace_layout(const Problem& p, size_t* sizes /* [kWsSlices] or null */);
@@ -68,6 +74,26 @@ __host__ __device__ inline int kperm(int h, int b) {
 __host__ __device__ inline int kgroup(int t) {
   int u = t & 63;
   return 2 * (u >> 5) + ((u >> 2) & 1);
+}
+
+// MX: the key (inside its 64-key tile) that lane half h of the FP4 PV MFMA consumes at
+// nibble j of its 32-nibble P fragment, once the two lane halves have swapped fragments so
+// that half h holds the keys 32h..32h+31: the fragment's first 16 nibbles come from
+// accumulator lane half 0 (keys 8*(r/4) + r%4), the last 16 from lane half 1 (+4).
+__host__ __device__ inline int vperm_mx(int h, int j) {
+  return 32 * h + 8 * ((j & 15) >> 2) + 4 * (j >> 4) + (j & 3);
+}
+
+// E8M0 byte of an MX block with largest magnitude amax (FP32, >= 0, NaN excluded): the
+// smallest e with amax <= 6 * 2^e, clamped to [-127, 127], biased by 127.  With
+// amax = (1 + f) 2^(E - 127): e = E - 129 if f <= 1/2, else E - 128; a subnormal or zero
+// amax gives e = -127; an infinite one e = 127.
+__device__ inline uint32_t e8m0_code(float amax) {
+  const uint32_t u = __float_as_uint(amax);
+  const int E = (int)(u >> 23);
+  if (E == 255) return 254u;
+  const int c = E - 2 + ((u & 0x7fffffu) > 0x400000u ? 1 : 0);
+  return c > 0 ? (uint32_t)c : 0u;
 }
 
 __device__ inline float load_in(const uint16_t* p, size_t i, bool fp16) {
@@ -121,5 +147,6 @@ hipError_t launch_q_prep(const Problem& p, const void* q, const Workspace& w, hi
 hipError_t launch_kv_quant(const Problem& p, const void* k, const void* v, const Workspace& w,
                            float ds_scale, float* ds_out, hipStream_t s);
 hipError_t launch_attn_fwd(const Problem& p, const Workspace& w, void* out, hipStream_t s);
+hipError_t launch_attn_fwd_mx(const Problem& p, const Workspace& w, void* out, hipStream_t s);
 
 }  // namespace sage
