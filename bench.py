@@ -201,9 +201,10 @@ def main():
     traffic = measured_traffic(cfg.name)
     dtype = ("e2m1 + e8m0 1x32 blocks (QK, PV), fp32 softmax/accumulate" if cfg.mxfp4
              else "int8(QK)+fp8e4m3(PV), fp32 softmax/accumulate")
-    metric = ("attention TOPS (4*N^2*d*H*B/time, causal counted as half) at N=32k d=128, % of INT8/FP8 MFMA peak"
+    shape = f"N={cfg.N} d={cfg.d}" + (" causal" if cfg.causal else "")
+    metric = (f"attention TOPS (4*N^2*d*H*B/time, causal counted as half) at {shape}, % of INT8/FP8 MFMA peak"
               if not cfg.mxfp4 else
-              "attention TOPS (4*N^2*d*H*B/time) at N=32k d=128, MXFP4 variant, % of FP4 MFMA peak")
+              f"attention TOPS (4*N^2*d*H*B/time) at {shape}, MXFP4 variant, % of FP4 MFMA peak")
     line = {
         "metric": metric,
         "value": round(value, 2),

@@ -147,13 +147,17 @@ __device__ __forceinline__ void softmax_pv(const v16i (&acc)[2], const uint8_t* 
       const float p2 = fast_exp2(sc[T][4 * q4 + 2] - base);
       const float p3 = fast_exp2(sc[T][4 * q4 + 3] - base);
       psum += (p0 + p1) + (p2 + p3);
-      // the instruction keeps the other half-word of its destination: seed it with p0's bits
-      int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __float_as_int(p0), false);
+      // the instruction keeps the other half-word of its destination: seed it with a dead
+      // register (the score p0 came from) so that no copy is needed
+      int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __float_as_int(sc[T][4 * q4 + 0]), false);
       wd = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, wd, true);
       pf[4 * T + q4] = wd;
     }
   }
   l_run = fmaf(l_run, alpha, psum);
+  // The packed P^ must exist before the rescale branch below: otherwise the exp work is sunk
+  // past it and a rescale waits on the previous tile's PV MFMAs instead of overlapping them.
+  asm volatile("" : "+v"(pf));
   // ---- O^T += V^T P^T per 32-channel sub-tile ----
   if (!ACC_VALU) {
     if (__any(alpha != 1.0f)) {
@@ -181,11 +185,15 @@ __device__ __forceinline__ void softmax_pv(const v16i (&acc)[2], const uint8_t* 
   }
 }
 
-template <int D, bool CAUSAL, int OUT, bool ACC_VALU>  // OUT: 0 bf16, 1 fp16, 2 fp32
-__global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
+// PIPE: the QK MFMAs of tile j+1 are issued before the softmax of tile j (one wave overlaps
+// its own matrix and vector work); otherwise the waves of other work-groups provide the
+// overlap.  NB: LDS ring slots.  OCC: work-groups per CU the register budget is sized for.
+template <int D, bool CAUSAL, int OUT, bool ACC_VALU, bool PIPE, int NB, int OCC>  // OUT: 0 bf16, 1 fp16, 2 fp32
+__global__ __launch_bounds__(256, OCC) void attn_fwd_kernel(AttnArgs a) {
   using TL = Tiles<D>;
   constexpr int NKS = D / 32;
-  constexpr int NB = 4;  // LDS ring: tile j computed, j+1 read by the next QK, j+2 and j+3 arriving
+  static_assert(!PIPE || NB == 4, "the pipelined loop uses a 4-slot ring");
+  static_assert(NB >= 2 && NB <= 4, "ring size");
   __shared__ __attribute__((aligned(1024))) int8_t sK[NB][TL::KBYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t sV[NB][TL::VBYTES];
   __shared__ __attribute__((aligned(256))) float sDS[NB][kBK];
@@ -273,33 +281,65 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kPerTile) : "memory");
   };
 
-  // Software pipeline per wave: the QK MFMAs of tile j+1 are issued before the softmax of
-  // tile j, so the matrix core works on j+1 while the VALU works on j.  Tile j+3 streams into
-  // the ring slot last read in the previous iteration; two tiles are always in flight, and one
-  // barrier per tile publishes the next.
   auto skip_t = [&](int j) { return CAUSAL && j * kBK > wq0 + 31; };  // fully masked for this wave
-  auto body = [&](int j, v16i (&cur)[2], v16i (&nxt)[2]) {
-    if (j + 3 < jend) dma(j + 3, (j + 3) % NB);
-    if (j + 1 < jend && !skip_t(j + 1)) qk_tile<D>(sK[(j + 1) % NB], qf, h, col, nxt);
-    if (!skip_t(j)) {
-      const int key0 = j * kBK;
-      const bool masked = (CAUSAL && key0 + kBK - 1 > wq0) || (key0 + kBK > a.M);
-      const int b = j % NB;
-      softmax_pv<D, CAUSAL, ACC_VALU>(cur, sV[b], sDS[b], sDK[b], dql, h, col, key0, qrow, a.M, masked, O,
-                                      m_run, l_run);
-    }
-    publish(j + 3 < jend);  // tile j+2 must be complete; j+3 may still be arriving
-  };
+  if constexpr (PIPE) {
+    // Software pipeline per wave: the QK MFMAs of tile j+1 are issued before the softmax of
+    // tile j, so the matrix core works on j+1 while the VALU works on j.  Tile j+3 streams into
+    // the ring slot last read in the previous iteration; two tiles are always in flight, and one
+    // barrier per tile publishes the next.
+    auto body = [&](int j, v16i (&cur)[2], v16i (&nxt)[2]) {
+      if (j + 3 < jend) dma(j + 3, (j + 3) % NB);
+      if (j + 1 < jend && !skip_t(j + 1)) qk_tile<D>(sK[(j + 1) % NB], qf, h, col, nxt);
+      if (!skip_t(j)) {
+        const int key0 = j * kBK;
+        const bool masked = (CAUSAL && key0 + kBK - 1 > wq0) || (key0 + kBK > a.M);
+        const int b = j % NB;
+        softmax_pv<D, CAUSAL, ACC_VALU>(cur, sV[b], sDS[b], sDK[b], dql, h, col, key0, qrow, a.M, masked, O,
+                                        m_run, l_run);
+      }
+      publish(j + 3 < jend);  // tile j+2 must be complete; j+3 may still be arriving
+    };
 
-  dma(0, 0);
-  if (jend > 1) dma(1, 1);
-  if (jend > 2) dma(2, 2);
-  publish(jend > 2);  // tiles 0 and 1 landed; tile 2 may be arriving
-  v16i accA[2], accB[2];
-  qk_tile<D>(sK[0], qf, h, col, accA);  // tile 0 is never masked away
-  for (int j = 0; j < jend; j += 2) {
-    body(j, accA, accB);
-    if (j + 1 < jend) body(j + 1, accB, accA);
+    dma(0, 0);
+    if (jend > 1) dma(1, 1);
+    if (jend > 2) dma(2, 2);
+    publish(jend > 2);  // tiles 0 and 1 landed; tile 2 may be arriving
+    v16i accA[2], accB[2];
+    qk_tile<D>(sK[0], qf, h, col, accA);  // tile 0 is never masked away
+    for (int j = 0; j < jend; j += 2) {
+      body(j, accA, accB);
+      if (j + 1 < jend) body(j + 1, accB, accA);
+    }
+  } else {
+    // Ring of NB slots: tile j is computed from slot j % NB while tiles j+1 .. j+NB-1 stream
+    // in; at the end of iteration j, tile j+1 must have landed and up to NB-2 newer tiles may
+    // still be in flight (n tiles -> n times this wave's DMA instructions per tile).
+    auto publish_n = [&](int n) {
+      if (n <= 0)
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else if (n == 1) {
+        if (w < 2) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kPerTile + 1) : "memory");
+        else asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kPerTile) : "memory");
+      } else {
+        if (w < 2) asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * kPerTile + 2) : "memory");
+        else asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * kPerTile) : "memory");
+      }
+    };
+    for (int t = 0; t < NB - 1 && t < jend; t++) dma(t, t);
+    publish_n(min(NB - 2, jend - 1));  // tile 0 landed
+    for (int j = 0; j < jend; j++) {
+      if (j + NB - 1 < jend) dma(j + NB - 1, (j + NB - 1) % NB);  // the slot tile j-1 left
+      if (!skip_t(j)) {
+        const int key0 = j * kBK;
+        const bool masked = (CAUSAL && key0 + kBK - 1 > wq0) || (key0 + kBK > a.M);
+        const int b = j % NB;
+        v16i acc[2];
+        qk_tile<D>(sK[b], qf, h, col, acc);
+        softmax_pv<D, CAUSAL, ACC_VALU>(acc, sV[b], sDS[b], sDK[b], dql, h, col, key0, qrow, a.M, masked, O,
+                                        m_run, l_run);
+      }
+      publish_n(min(NB - 2, jend - j - 2));
+    }
   }
 
   // ---- epilogue: O / l (l holds 448 * sum P~) * dV (+ V_m) ----
@@ -322,16 +362,36 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_kernel(AttnArgs a) {
   }
 }
 
+// Loop shape of the fused kernel.  Default (measured fastest at prefill 32k): the plain loop
+// with a 2-slot ring and registers budgeted for three work-groups per CU, so that three
+// waves per SIMD overlap one another's matrix and vector work.  The software-pipelined
+// 4-slot form (two work-groups per CU) stays selectable for comparison.
+#ifndef SAGE_ATTN_PIPE
+#define SAGE_ATTN_PIPE 0
+#endif
+#ifndef SAGE_ATTN_OCC
+#define SAGE_ATTN_OCC 0  // 0: per head dimension (d = 64 fits four work-groups per CU, d = 128 three)
+#endif
+#ifndef SAGE_ATTN_RING
+#define SAGE_ATTN_RING 2
+#endif
+constexpr bool kPipe = SAGE_ATTN_PIPE != 0;
+constexpr int kRing = kPipe ? 4 : SAGE_ATTN_RING;
+template <int D>
+constexpr int occ_for() {
+  return kPipe ? 2 : (SAGE_ATTN_OCC ? SAGE_ATTN_OCC : (D == 64 ? 4 : 3));
+}
+
 template <int D, bool CAUSAL, bool ACC_VALU>
 hipError_t launch_d(const Problem& p, const AttnArgs& a, hipStream_t s) {
   dim3 grid(p.nqb * p.BH);
   const int out = p.out_fp32 ? 2 : (p.fp16 ? 1 : 0);
   if (out == 2)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, 2, ACC_VALU>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, 2, ACC_VALU, kPipe, kRing, occ_for<D>()>), grid, dim3(256), 0, s, a);
   else if (out == 1)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, 1, ACC_VALU>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, 1, ACC_VALU, kPipe, kRing, occ_for<D>()>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, 0, ACC_VALU>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, 0, ACC_VALU, kPipe, kRing, occ_for<D>()>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

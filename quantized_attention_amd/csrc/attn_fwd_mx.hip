@@ -189,11 +189,14 @@ __device__ __forceinline__ void softmax_pv_mx(const v16f (&acc)[2], const uint8_
   });
 }
 
+// Registers are budgeted for OCC work-groups per CU (three waves per SIMD at d = 128, four at
+// d = 64), which overlap one another's matrix and vector work; the K/V tiles use a 2-slot
+// ring: tile j+1 streams in while tile j is computed.
 template <int D, bool CAUSAL, int OUT, bool ACC_VALU>  // OUT: 0 bf16, 1 fp16, 2 fp32
-__global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(MxArgs a) {
+__global__ __launch_bounds__(256, D == 64 ? 4 : 3) void attn_fwd_mx_kernel(MxArgs a) {
   using TL = MxTiles<D>;
   constexpr int NG = D / 32;  // 32-channel sub-tiles of O
-  constexpr int NB = 4;       // LDS ring: tile j computed, j+1 read by the next QK, j+2, j+3 arriving
+  constexpr int NB = 2;
   __shared__ __attribute__((aligned(1024))) uint8_t sK[NB][TL::KBYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t sV[NB][TL::VBYTES];
   __shared__ __attribute__((aligned(256))) float sDS[NB][kBK];
@@ -269,43 +272,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mx_kernel(MxArgs a) {
     if (w == 1) dma4(lds_addr(&sKS[slot][0]), ksbase + (size_t)j * 256, 4 * lane);
     if (w == 2) dma4(lds_addr(&sVS[slot][0]), vsbase + (size_t)j * 256, 4 * lane);
   };
-  // DMA instructions per tile: waves 0-2 issue one more than wave 3 (the scale / Delta S line).
-  constexpr int kPer012 = (TL::KDMA == 4 ? 2 : 1) + 1, kPer3 = kPer012 - 1;
-  auto publish = [&](bool newest_in_flight) {
-    if (!newest_in_flight)
-      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else if (w < 3)
-      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kPer012) : "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kPer3) : "memory");
-  };
+  // The slot of tile j+1 was last read in iteration j-1, which every wave left at the barrier
+  // that closed it; at the end of iteration j, tile j+1 must have landed for all waves.
+  auto publish = [&]() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
   auto skip_t = [&](int j) { return CAUSAL && j * kBK > wq0 + 31; };  // fully masked for this wave
-  auto body = [&](int j, v16f (&cur)[2], v16f (&nxt)[2]) {
-    if (j + 3 < jend) dma(j + 3, (j + 3) % NB);
-    if (j + 1 < jend && !skip_t(j + 1)) {
-      const int b1 = (j + 1) % NB;
-      qk_tile_mx<D>(sK[b1], qf, sKS[b1][lane], qs, h, col, nxt);
-    }
+  dma(0, 0);
+  publish();
+  for (int j = 0; j < jend; j++) {
+    if (j + 1 < jend) dma(j + 1, (j + 1) % NB);
     if (!skip_t(j)) {
       const int key0 = j * kBK;
       const bool masked = (CAUSAL && key0 + kBK - 1 > wq0) || (key0 + kBK > a.M);
       const int b = j % NB;
-      softmax_pv_mx<D, CAUSAL, ACC_VALU>(cur, sV[b], sDS[b], sVS[b][lane], a.qk_scale, h, col, key0, qrow, a.M,
+      v16f acc[2];
+      qk_tile_mx<D>(sK[b], qf, sKS[b][lane], qs, h, col, acc);
+      softmax_pv_mx<D, CAUSAL, ACC_VALU>(acc, sV[b], sDS[b], sVS[b][lane], a.qk_scale, h, col, key0, qrow, a.M,
                                          masked, O, m_run, l_run);
     }
-    publish(j + 3 < jend);
-  };
-
-  dma(0, 0);
-  if (jend > 1) dma(1, 1);
-  if (jend > 2) dma(2, 2);
-  publish(jend > 2);
-  v16f accA[2], accB[2];
-  qk_tile_mx<D>(sK[0], qf, sKS[0][lane], qs, h, col, accA);  // tile 0 is never masked away
-  for (int j = 0; j < jend; j += 2) {
-    body(j, accA, accB);
-    if (j + 1 < jend) body(j + 1, accB, accA);
+    publish();
   }
 
   // ---- epilogue: O / l (+ V_m) ----
