@@ -106,43 +106,65 @@ __global__ __launch_bounds__(256) void kv_stats_kernel(const uint16_t* __restric
 }
 
 // ---- chunk statistics -> k mean, V_m (when smoothing) and the V scale ----
-__global__ void kv_finalize_kernel(const double* __restrict__ kpart, const double* __restrict__ vpart,
-                                   const float* __restrict__ vmaxp, const float* __restrict__ vminp,
-                                   float* __restrict__ kmean, float* __restrict__ vmean, float* __restrict__ dv,
-                                   int M, int d, int nkt, bool smooth_v) {
-  const int bh = blockIdx.x, c = threadIdx.x;
-  if (c >= d) return;
-  constexpr int U = 8;  // loads in flight; the sums themselves stay in chunk order
+// One work-group per (head, 8 channels).  The partials of a stage of 256 chunks are staged in
+// LDS by all 256 threads at once (the loads overlap instead of forming a chain of round
+// trips); then one thread per channel adds them in chunk order, as the pinned order requires.
+constexpr int kFinCh = 8;       // channels per work-group
+constexpr int kFinStage = 256;  // chunks staged per round
+__global__ __launch_bounds__(256) void kv_finalize_kernel(const double* __restrict__ kpart,
+                                                          const double* __restrict__ vpart,
+                                                          const float* __restrict__ vmaxp,
+                                                          const float* __restrict__ vminp,
+                                                          float* __restrict__ kmean, float* __restrict__ vmean,
+                                                          float* __restrict__ dv, int M, int d, int nkt,
+                                                          bool smooth_v) {
+  __shared__ double sk[kFinStage][kFinCh];
+  __shared__ double svs[kFinStage][kFinCh];
+  __shared__ float smx[kFinStage][kFinCh];
+  __shared__ float smn[kFinStage][kFinCh];
+  const int bh = blockIdx.x, c0 = blockIdx.y * kFinCh, tid = threadIdx.x;
   double ks = 0.0, vs = 0.0;
   float mx = -INFINITY, mn = INFINITY;
-  for (int u0 = 0; u0 < nkt; u0 += U) {
-    double kb[U], vb[U];
-    float xb[U], nb[U];
+  for (int u0 = 0; u0 < nkt; u0 += kFinStage) {
+    const int ns = min(kFinStage, nkt - u0);
 #pragma unroll
-    for (int i = 0; i < U; i++) {
-      const size_t o = ((size_t)bh * nkt + min(u0 + i, nkt - 1)) * d + c;
-      kb[i] = kpart[o];
-      vb[i] = smooth_v ? vpart[o] : 0.0;
-      xb[i] = vmaxp[o];
-      nb[i] = vminp[o];
-    }
-#pragma unroll
-    for (int i = 0; i < U; i++) {
-      if (u0 + i < nkt) {
-        ks += kb[i];
-        if (smooth_v) vs += vb[i];
-        mx = xb[i] > mx ? xb[i] : mx;
-        mn = nb[i] < mn ? nb[i] : mn;
+    for (int i = 0; i < kFinStage * kFinCh / 256; i++) {
+      const int x = tid + 256 * i, uu = x / kFinCh, cc = x % kFinCh;
+      if (uu < ns) {
+        const size_t o = ((size_t)bh * nkt + u0 + uu) * d + c0 + cc;
+        sk[uu][cc] = kpart[o];
+        if (smooth_v) svs[uu][cc] = vpart[o];
+        smx[uu][cc] = vmaxp[o];
+        smn[uu][cc] = vminp[o];
       }
     }
+    __syncthreads();
+    if (tid < kFinCh) {
+      for (int uu = 0; uu < ns; uu++) ks += sk[uu][tid];
+    } else if (tid >= 64 && tid < 64 + kFinCh) {
+      const int cc = tid - 64;
+      for (int uu = 0; uu < ns; uu++) {
+        if (smooth_v) vs += svs[uu][cc];
+        mx = smx[uu][cc] > mx ? smx[uu][cc] : mx;  // NaN ignored
+        mn = smn[uu][cc] < mn ? smn[uu][cc] : mn;
+      }
+    }
+    __syncthreads();
   }
-  kmean[(size_t)bh * d + c] = (float)(ks / (double)M);
-  const float vm = smooth_v ? (float)(vs / (double)M) : 0.0f;
-  vmean[(size_t)bh * d + c] = vm;
-  const float a1 = mx - vm, a2 = vm - mn;  // max |fp32(V - V_m)| over the tokens
-  const float am = a1 > a2 ? a1 : a2;
-  const float a = am > 1e-8f ? am : 1e-8f;
-  dv[(size_t)bh * d + c] = __fdiv_rn(a, 448.0f);
+  // the K sum lives in threads 0..7, the V statistics in threads 64..71
+  if (tid < kFinCh) {
+    const float km = (float)(ks / (double)M);
+    kmean[(size_t)bh * d + c0 + tid] = km;
+  }
+  if (tid >= 64 && tid < 64 + kFinCh) {
+    const int c = c0 + tid - 64;
+    const float vm = smooth_v ? (float)(vs / (double)M) : 0.0f;
+    vmean[(size_t)bh * d + c] = vm;
+    const float a1 = mx - vm, a2 = vm - mn;  // max |fp32(V - V_m)| over the tokens
+    const float am = a1 > a2 ? a1 : a2;
+    const float a = am > 1e-8f ? am : 1e-8f;
+    dv[(size_t)bh * d + c] = __fdiv_rn(a, 448.0f);
+  }
 }
 
 // ---- Q: block mean (and its bf16 head/tail), gamma(Q), per-token scale, INT8 codes ----
@@ -186,52 +208,64 @@ __global__ __launch_bounds__(256) void q_prep_kernel(const uint16_t* __restrict_
     qm_lo[o] = bf16_rn(m - bf16_val(hb));
   }
   __syncthreads();
-  // each wave takes 32 rows; a lane holds D/64 channels of the row
-  constexpr int CPL = D / 64;
-  for (int rr = 0; rr < kBQ / 4; rr++) {
-    const int r = wave * (kBQ / 4) + rr;
-    float g[CPL];
+  // Each wave takes 32 rows.  A row is spread over LPR = D/8 lanes holding 8 consecutive
+  // channels each (one 16-byte LDS read); a wave quantizes 64/LPR rows per step, and the
+  // row / block maxima are short reductions inside each lane group.
+  constexpr int LPR = D / 8;          // lanes per row
+  constexpr int RPS = 64 / LPR;       // rows per wave step
+  const int sub = lane / LPR, cl = lane % LPR, c0 = 8 * cl;
+  float mch[8];
+#pragma unroll
+  for (int e = 0; e < 8; e++) mch[e] = sm[c0 + e];
+  for (int rr = 0; rr < kBQ / 4; rr += RPS) {
+    const int r = wave * (kBQ / 4) + rr + sub;
+    const size_t row = (size_t)bh * Np + r0 + r;
+    float g[8];
+    if (r < n) {
+      const v4i raw = *reinterpret_cast<const v4i*>(&sq[r * RS + c0]);
+      widen8(raw, fp16, g);
+#pragma unroll
+      for (int e = 0; e < 8; e++) g[e] = g[e] - mch[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; e++) g[e] = 0.0f;
+    }
     float am = 0.0f;
 #pragma unroll
-    for (int e = 0; e < CPL; e++) {
-      const int c = lane * CPL + e;
-      g[e] = (r < n) ? load_in(sq, (size_t)r * RS + c, fp16) - sm[c] : 0.0f;
-      am = amax_upd(am, g[e]);
-    }
-    const size_t row = (size_t)bh * Np + r0 + r;
+    for (int e = 0; e < 8; e++) am = amax_upd(am, g[e]);
     if constexpr (MX) {
-      // one E8M0 scale per 32 channels: the block's lanes are 32 / CPL consecutive lanes
+      // one E8M0 scale per 32 channels: 4 lanes
 #pragma unroll
-      for (int off = 16 / CPL; off >= 1; off >>= 1) {
+      for (int off = 2; off >= 1; off >>= 1) {
         const float o = __shfl_xor(am, off);
         am = o > am ? o : am;
       }
       const uint32_t code = e8m0_code(am);  // padded rows: amax 0 -> code 0, values 0
       const float sc = __uint_as_float(code << 23);
-      uint8_t* qo = reinterpret_cast<uint8_t*>(qhat) + row * (D / 2);
-      if (CPL == 2) {
-        qo[lane] = (uint8_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, g[0], g[CPL - 1], sc, 0);
-      } else {
-        const float nb = __shfl_xor(g[0], 1);
-        if (!(lane & 1)) qo[lane >> 1] = (uint8_t)__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, g[0], nb, sc, 0);
-      }
-      if ((lane & (32 / CPL - 1)) == 0) qsc[row * (D / 32) + lane / (32 / CPL)] = (uint8_t)code;
+      uint32_t wd = 0;
+      wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, g[0], g[1], sc, 0);
+      wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, g[2], g[3], sc, 1);
+      wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, g[4], g[5], sc, 2);
+      wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, g[6], g[7], sc, 3);
+      *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(qhat) + row * (D / 2) + c0 / 2) = wd;
+      if ((cl & 3) == 0) qsc[row * (D / 32) + cl / 4] = (uint8_t)code;
     } else {
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
+      for (int off = LPR / 2; off >= 1; off >>= 1) {
         const float o = __shfl_xor(am, off);
         am = o > am ? o : am;
       }
-      const float s = (r < n) ? int8_scale(am) : 1.0f;
-      if (lane == 0) dq[row] = s;
-      uint32_t word = 0;
+      const float sc = (r < n) ? int8_scale(am) : 1.0f;
+      if (cl == 0) dq[row] = sc;
+      uint32_t w0 = 0, w1 = 0;
+      if (r < n) {
 #pragma unroll
-      for (int e = 0; e < CPL; e++)
-        word |= (uint32_t)(uint8_t)((r < n) ? int8_code(g[e], s) : 0) << (8 * e);
-      if (CPL == 2)
-        *reinterpret_cast<uint16_t*>(qhat + row * D + lane * CPL) = (uint16_t)word;
-      else
-        qhat[row * D + lane] = (int8_t)word;
+        for (int e = 0; e < 4; e++) {
+          w0 |= (uint32_t)(uint8_t)int8_code(g[e], sc) << (8 * e);
+          w1 |= (uint32_t)(uint8_t)int8_code(g[4 + e], sc) << (8 * e);
+        }
+      }
+      *reinterpret_cast<uint2*>(qhat + row * D + c0) = make_uint2(w0, w1);
     }
   }
 }
@@ -259,12 +293,17 @@ struct KVArgs {
 // V' / dV -> E4M3, transposed in the P-fragment key order.  MX: gamma(K) and V' in E2M1
 // with an E8M0 scale per 32 channels of a key / per 32 tokens of a channel ----
 template <int D, bool MX>
-__global__ __launch_bounds__(256) void kv_quant_kernel(KVArgs a) {
+__global__ __launch_bounds__(256, 4) void kv_quant_kernel(KVArgs a) {
   constexpr int RS = D + 8;                 // bf16 split of gamma(K), 16-byte aligned rows
   constexpr int CH = kBK * D / 8 / 256;     // 8-element chunks per thread
-  __shared__ __attribute__((aligned(16))) uint16_t sAh[kBK * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t sAl[kBK * RS];
-  __shared__ float sv[kBK][D + 1];
+  // The bf16 split of gamma(K) (read by the Delta S MFMAs) and the staged V' (read by the
+  // transposing V^ writer) are live one after the other: they share one LDS buffer, which
+  // lets four work-groups share a CU.
+  constexpr int kSplitBytes = 2 * kBK * RS * 2, kVBytes = kBK * (D + 1) * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kSplitBytes > kVBytes ? kSplitBytes : kVBytes];
+  uint16_t* sAh = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* sAl = sAh + kBK * RS;
+  float (*sv)[D + 1] = reinterpret_cast<float (*)[D + 1]>(smem);
   __shared__ float gmax[4][4];
   __shared__ float sdk[4];
   const int u = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
@@ -392,44 +431,47 @@ __global__ __launch_bounds__(256) void kv_quant_kernel(KVArgs a) {
   __syncthreads();  // sAh / sAl complete before the Delta S MFMAs read them
 
   // ---- Delta S^T[key][block] = gamma(K) q^T on the bf16 MFMA, split operands ----
+  // A wave takes groups of 32 query blocks (gidx = wave, wave + 4, ...), loads their q-mean
+  // head/tail once and computes both 32-key halves of the tile against them.
   if (a.ds) {
     const int h = lane >> 5, col = lane & 31;
-    const int T = wave & 1;
     const int ilo = a.causal ? u / 2 : 0;  // block i needs keys < 128 (i + 1)
-    for (int gidx = wave >> 1; 32 * gidx < a.nqb; gidx += 2) {
+    for (int gidx = wave; 32 * gidx < a.nqb; gidx += 4) {
       if (32 * gidx + 31 < ilo) continue;
       const int blk = 32 * gidx + col;
       const bool bv = blk < a.nqb;
-      v16f acc;
-#pragma unroll
-      for (int r = 0; r < 16; r++) acc[r] = 0.0f;
       const size_t qo = ((size_t)bh * a.nqb + (bv ? blk : 0)) * D;
       v8bf bq[D / 16], bl[D / 16];  // the block's q-mean head/tail, all loads in flight
 #pragma unroll
       for (int s = 0; s < D / 16; s++) {
-        bq[s] = *reinterpret_cast<const v8bf*>(a.qm_hi + qo + 16 * s + 8 * h);
-        bl[s] = *reinterpret_cast<const v8bf*>(a.qm_lo + qo + 16 * s + 8 * h);
+        bq[s] = bv ? *reinterpret_cast<const v8bf*>(a.qm_hi + qo + 16 * s + 8 * h) : v8bf{};
+        bl[s] = bv ? *reinterpret_cast<const v8bf*>(a.qm_lo + qo + 16 * s + 8 * h) : v8bf{};
       }
 #pragma unroll
-      for (int s = 0; s < D / 16; s++) {
-        const v8bf ah = *reinterpret_cast<const v8bf*>(&sAh[(32 * T + col) * RS + 16 * s + 8 * h]);
-        const v8bf al = *reinterpret_cast<const v8bf*>(&sAl[(32 * T + col) * RS + 16 * s + 8 * h]);
-        const v8bf qh = bv ? bq[s] : v8bf{};
-        const v8bf ql = bv ? bl[s] : v8bf{};
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qh, acc, 0, 0, 0);  // small terms first
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, ql, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qh, acc, 0, 0, 0);
-      }
-      if (bv && blk >= ilo) {
-        float* dst = a.ds + ((size_t)bh * a.nqb + blk) * a.Mp + t0 + 32 * T + 4 * h;
+      for (int T = 0; T < 2; T++) {
+        v16f acc;
 #pragma unroll
-        for (int b = 0; b < 4; b++)
-          *reinterpret_cast<float4*>(dst + 8 * b) =
-              make_float4(acc[4 * b] * a.ds_scale, acc[4 * b + 1] * a.ds_scale, acc[4 * b + 2] * a.ds_scale,
-                          acc[4 * b + 3] * a.ds_scale);
+        for (int r = 0; r < 16; r++) acc[r] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < D / 16; s++) {
+          const v8bf ah = *reinterpret_cast<const v8bf*>(&sAh[(32 * T + col) * RS + 16 * s + 8 * h]);
+          const v8bf al = *reinterpret_cast<const v8bf*>(&sAl[(32 * T + col) * RS + 16 * s + 8 * h]);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bq[s], acc, 0, 0, 0);  // small terms first
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl[s], acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bq[s], acc, 0, 0, 0);
+        }
+        if (bv && blk >= ilo) {
+          float* dst = a.ds + ((size_t)bh * a.nqb + blk) * a.Mp + t0 + 32 * T + 4 * h;
+#pragma unroll
+          for (int b = 0; b < 4; b++)
+            *reinterpret_cast<float4*>(dst + 8 * b) =
+                make_float4(acc[4 * b] * a.ds_scale, acc[4 * b + 1] * a.ds_scale, acc[4 * b + 2] * a.ds_scale,
+                            acc[4 * b + 3] * a.ds_scale);
+        }
       }
     }
   }
+  __syncthreads();  // the split of gamma(K) is dead: its LDS now stages V'
 
   // ---- V: V' / dV (IEEE division), saturated to the E4M3 range, staged in LDS ----
   // (MX: V' itself; the block scale comes from the staged values)
@@ -515,8 +557,8 @@ hipError_t launch_kv_stats(const Problem& p, const void* k, const void* v, const
 }
 
 hipError_t launch_kv_finalize(const Problem& p, const Workspace& w, hipStream_t s) {
-  hipLaunchKernelGGL(kv_finalize_kernel, dim3(p.BH), dim3(p.d), 0, s, w.kpart, w.vpart, w.vmaxp, w.vminp,
-                     w.kmean, w.vmean, w.dv, p.M, p.d, p.nkt, p.smooth_v);
+  hipLaunchKernelGGL(kv_finalize_kernel, dim3(p.BH, p.d / kFinCh), dim3(256), 0, s, w.kpart, w.vpart, w.vmaxp,
+                     w.vminp, w.kmean, w.vmean, w.dv, p.M, p.d, p.nkt, p.smooth_v);
   return hipGetLastError();
 }
 
