@@ -327,18 +327,25 @@ __global__ __launch_bounds__(256, OCC) void attn_fwd_kernel(AttnArgs a) {
     };
     for (int t = 0; t < NB - 1 && t < jend; t++) dma(t, t);
     publish_n(min(NB - 2, jend - 1));  // tile 0 landed
-    for (int j = 0; j < jend; j++) {
-      if (j + NB - 1 < jend) dma(j + NB - 1, (j + NB - 1) % NB);  // the slot tile j-1 left
+    // One iteration; the slot is a compile-time constant so LDS addresses are immediates.
+    auto iter = [&](int j, auto slotc) {
+      constexpr int b = decltype(slotc)::value;
+      if (j + NB - 1 < jend) dma(j + NB - 1, (b + NB - 1) % NB);  // the slot tile j-1 left
       if (!skip_t(j)) {
         const int key0 = j * kBK;
         const bool masked = (CAUSAL && key0 + kBK - 1 > wq0) || (key0 + kBK > a.M);
-        const int b = j % NB;
         v16i acc[2];
         qk_tile<D>(sK[b], qf, h, col, acc);
         softmax_pv<D, CAUSAL, ACC_VALU>(acc, sV[b], sDS[b], sDK[b], dql, h, col, key0, qrow, a.M, masked, O,
                                         m_run, l_run);
       }
       publish_n(min(NB - 2, jend - j - 2));
+    };
+    for (int j0 = 0; j0 < jend; j0 += NB) {
+      static_for<0, NB>([&](auto slotc) {
+        const int j = j0 + decltype(slotc)::value;
+        if (j < jend) iter(j, slotc);
+      });
     }
   }
 

@@ -279,18 +279,25 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 3) void attn_fwd_mx_kernel(MxArg
   auto skip_t = [&](int j) { return CAUSAL && j * kBK > wq0 + 31; };  // fully masked for this wave
   dma(0, 0);
   publish();
-  for (int j = 0; j < jend; j++) {
-    if (j + 1 < jend) dma(j + 1, (j + 1) % NB);
+  // One iteration; the slot is a compile-time constant so LDS addresses are immediates.
+  auto iter = [&](int j, auto slotc) {
+    constexpr int b = decltype(slotc)::value;
+    if (j + 1 < jend) dma(j + 1, 1 - b);
     if (!skip_t(j)) {
       const int key0 = j * kBK;
       const bool masked = (CAUSAL && key0 + kBK - 1 > wq0) || (key0 + kBK > a.M);
-      const int b = j % NB;
       v16f acc[2];
       qk_tile_mx<D>(sK[b], qf, sKS[b][lane], qs, h, col, acc);
       softmax_pv_mx<D, CAUSAL, ACC_VALU>(acc, sV[b], sDS[b], sVS[b][lane], a.qk_scale, h, col, key0, qrow, a.M,
                                          masked, O, m_run, l_run);
     }
     publish();
+  };
+  for (int j0 = 0; j0 < jend; j0 += NB) {
+    static_for<0, NB>([&](auto slotc) {
+      const int j = j0 + decltype(slotc)::value;
+      if (j < jend) iter(j, slotc);
+    });
   }
 
   // ---- epilogue: O / l (+ V_m) ----

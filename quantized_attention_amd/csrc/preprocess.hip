@@ -140,13 +140,34 @@ __global__ __launch_bounds__(256) void kv_finalize_kernel(const double* __restri
     }
     __syncthreads();
     if (tid < kFinCh) {
-      for (int uu = 0; uu < ns; uu++) ks += sk[uu][tid];
+      for (int ub = 0; ub < ns; ub += 8) {  // 8 LDS reads in flight, adds in chunk order
+        double x[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) x[e] = sk[min(ub + e, kFinStage - 1)][tid];
+#pragma unroll
+        for (int e = 0; e < 8; e++)
+          if (ub + e < ns) ks += x[e];
+      }
     } else if (tid >= 64 && tid < 64 + kFinCh) {
       const int cc = tid - 64;
-      for (int uu = 0; uu < ns; uu++) {
-        if (smooth_v) vs += svs[uu][cc];
-        mx = smx[uu][cc] > mx ? smx[uu][cc] : mx;  // NaN ignored
-        mn = smn[uu][cc] < mn ? smn[uu][cc] : mn;
+      for (int ub = 0; ub < ns; ub += 8) {
+        double x[8];
+        float hx[8], lx[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          const int uu = min(ub + e, kFinStage - 1);
+          x[e] = smooth_v ? svs[uu][cc] : 0.0;
+          hx[e] = smx[uu][cc];
+          lx[e] = smn[uu][cc];
+        }
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          if (ub + e < ns) {
+            if (smooth_v) vs += x[e];
+            mx = hx[e] > mx ? hx[e] : mx;  // NaN ignored
+            mn = lx[e] < mn ? lx[e] : mn;
+          }
+        }
       }
     }
     __syncthreads();
