@@ -36,28 +36,33 @@ PEAK_TOPS_FP4 = 10100.0  # MI355X dense MXFP4 MFMA peak, 10.1 PFLOP/s (the MX va
 # Kernel-level HBM traffic of the fused attention kernel, one launch on the named workload:
 # rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (KiB per dispatch) scaled by what the same
 # counters read for a plain 1 GiB device copy (FETCH x2.000, WRITE x1.000).  Valid only for
-# the kernel source it was taken on: the hash of the fused kernel's sources is checked,
+# the kernel source it was taken on: the hash of that fused kernel's sources is checked,
 # and a changed kernel reports traffic null until the counters are taken again.
 TRAFFIC_BYTES = {
-    "prefill32k": {"source_sha256_16": "6938d376c6324f23",
-                   "fetch_bytes": 1596341237, "write_bytes": 268439859},
+    "prefill32k": {"source_sha256_16": "23808ae835617b4d",
+                   "fetch_bytes": 1779260565, "write_bytes": 268539584},
+    "mxfp4_32k": {"source_sha256_16": "4cd1ff8256f5b3ab",
+                  "fetch_bytes": 1694527628, "write_bytes": 201326592},
 }
-KERNEL_SOURCES = ("quantized_attention_amd/csrc/attn_fwd.hip", "quantized_attention_amd/csrc/attn_device.hpp",
-                  "quantized_attention_amd/csrc/sage_common.hpp")
+_COMMON_SOURCES = ("quantized_attention_amd/csrc/attn_device.hpp", "quantized_attention_amd/csrc/sage_common.hpp")
+KERNEL_SOURCES = {
+    False: ("quantized_attention_amd/csrc/attn_fwd.hip",) + _COMMON_SOURCES,    # INT8/FP8 path
+    True: ("quantized_attention_amd/csrc/attn_fwd_mx.hip",) + _COMMON_SOURCES,  # MXFP4 variant
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(mx: bool = False) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in KERNEL_SOURCES[mx]:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(name: str):
+def measured_traffic(name: str, mx: bool = False):
     t = TRAFFIC_BYTES.get(name)
-    if t is None or t["source_sha256_16"] != kernel_source_hash():
+    if t is None or t["source_sha256_16"] != kernel_source_hash(mx):
         return None
     return t["fetch_bytes"] + t["write_bytes"]
 
@@ -198,7 +203,7 @@ def main():
     ops = counted_ops(cfg)
     value = ops / (ms * 1e-3) / 1e12
     achieved = ops / (kms * 1e-3) / 1e12
-    traffic = measured_traffic(cfg.name)
+    traffic = measured_traffic(cfg.name, cfg.mxfp4)
     dtype = ("e2m1 + e8m0 1x32 blocks (QK, PV), fp32 softmax/accumulate" if cfg.mxfp4
              else "int8(QK)+fp8e4m3(PV), fp32 softmax/accumulate")
     shape = f"N={cfg.N} d={cfg.d}" + (" causal" if cfg.causal else "")
