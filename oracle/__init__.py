@@ -136,8 +136,9 @@ def preprocess_mx_head(q, k, v, fp16: bool, flags: int = 0) -> dict:
     return o
 
 
-def forward_head(q, k, v, fp16: bool, causal: bool, sm_scale: float, flags: int = 0, rows=None):
-    """The quantized forward of one head in FP64: [len(rows) or N, d]."""
+def forward_head(q, k, v, fp16: bool, causal: int, sm_scale: float, flags: int = 0, rows=None):
+    """The quantized forward of one head in FP64: [len(rows) or N, d].  causal: 0 none, 1 key t
+    visible to row r iff t <= r, 2 iff t <= r + M - N (needs N <= M)."""
     q, k, v = _u16(q), _u16(k), _u16(v)
     N, d = q.shape
     M = k.shape[0]
@@ -154,7 +155,7 @@ def forward_head(q, k, v, fp16: bool, causal: bool, sm_scale: float, flags: int 
     return out
 
 
-def exact_head(q, k, v, fp16: bool, causal: bool, sm_scale: float, rows=None):
+def exact_head(q, k, v, fp16: bool, causal: int, sm_scale: float, rows=None):
     """softmax(Q K^T * sm_scale) V in FP64 on the widened inputs."""
     q, k, v = _u16(q), _u16(k), _u16(v)
     N, d = q.shape
@@ -172,7 +173,7 @@ def exact_head(q, k, v, fp16: bool, causal: bool, sm_scale: float, rows=None):
     return out
 
 
-def exact_f64(q, k, v, causal: bool, sm_scale: float):
+def exact_f64(q, k, v, causal: int, sm_scale: float):
     q = np.ascontiguousarray(q, np.float64)
     k = np.ascontiguousarray(k, np.float64)
     v = np.ascontiguousarray(v, np.float64)

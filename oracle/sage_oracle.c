@@ -537,8 +537,19 @@ static double quant_p(const head_t* h, double p) {
   return orc_e4m3_decode(orc_e4m3_encode(h->pscale * p));
 }
 
+/* The causal mask: key t is visible to query row r iff t <= r + off.  causal = 1 aligns the
+ * first query with the first key (off = 0; the pages' reference code masks the upper
+ * triangle of the N x M score matrix); causal = 2 aligns the last query with the last key
+ * (off = M - N, the reading of K and V as a cache of M >= N earlier tokens that the N queries
+ * follow; needs N <= M so that no row is empty).  Returns -1 for other values. */
+static int causal_offset(int causal, int N, int M, int* off) {
+  if (causal == 0 || causal == 1) { *off = 0; return 0; }
+  if (causal == 2 && N <= M) { *off = M - N; return 0; }
+  return -1;
+}
+
 /* Steps 7-8 for one row: the tile loop and the epilogue. */
-static void forward_row(const head_t* h, int r, int causal, double sm_scale, const double* ds,
+static void forward_row(const head_t* h, int r, int causal, int off, double sm_scale, const double* ds,
                         double* S, double* Pt, double* Ph, double* R, double* out) {
   int d = h->d, M = h->M;
   double m = -INFINITY, l = 0.0;
@@ -547,13 +558,13 @@ static void forward_row(const head_t* h, int r, int causal, double sm_scale, con
     int t0 = j * ORC_BK;
     /* Causal: a tile whose first key is past row r is fully masked for this row; with its
      * row maximum at -inf it leaves m, l and O unchanged, so it is not visited. */
-    if (causal && t0 > r) break;
+    if (causal && t0 > r + off) break;
     int t1 = t0 + ORC_BK < M ? t0 + ORC_BK : M;
     int n = t1 - t0;
     double mt = -INFINITY;
     for (int x = 0; x < n; x++) {
       int t = t0 + x;
-      if (causal && t > r) { S[x] = -INFINITY; continue; }
+      if (causal && t > r + off) { S[x] = -INFINITY; continue; }
       S[x] = (qk_term(h, r, t) + ds[t]) * sm_scale; /* [SA2 Alg. 1] S = deq(QK) + Delta S */
       if (S[x] > mt) mt = S[x];
     }
@@ -610,8 +621,9 @@ static void forward_row(const head_t* h, int r, int causal, double sm_scale, con
 int orc_forward_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, int in_fp16,
                      int N, int M, int d, int causal, double sm_scale, unsigned flags,
                      const int* rows, int nrows, double* out) {
+  int off;
   if (!q || !k || !v || !out || nrows < 0) return -1;
-  if (causal && N != M) return -1;
+  if (causal_offset(causal, N, M, &off)) return -1;
   if ((flags & ORC_MXFP4) && (flags & (ORC_QK_IDENTITY | ORC_PV_IDENTITY | ORC_PV_E5M2 | ORC_PV_INT8))) return -1;
   if (!rows && nrows != N) return -1;
   head_t h;
@@ -643,7 +655,7 @@ int orc_forward_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, in
 #pragma omp for schedule(dynamic, 4)
       for (int x = 0; x < nrows; x++) {
         int r = rows ? rows[x] : x;
-        forward_row(&h, r, causal, sm_scale, dsr[r / ORC_BQ], S, Pt, Ph, R, out + (size_t)x * d);
+        forward_row(&h, r, causal, off, sm_scale, dsr[r / ORC_BQ], S, Pt, Ph, R, out + (size_t)x * d);
       }
       free(S); free(Pt); free(Ph); free(R);
     }
@@ -713,6 +725,9 @@ int orc_preprocess_mx_head(const uint16_t* q, const uint16_t* k, const uint16_t*
   return 0;
 }
 
+/* Number of keys row r sees under the causal mask t <= r + off (at most M). */
+static int visible(int r, int off, int M) { return r + off + 1 < M ? r + off + 1 : M; }
+
 /* Textbook attention: softmax(Q K^T * sm_scale) V, FP64, row by row. */
 static void exact_row(const double* qr, const double* K, const double* V, int M, int d, int lim,
                       double sm_scale, double* s, double* out) {
@@ -734,14 +749,15 @@ static void exact_row(const double* qr, const double* K, const double* V, int M,
 
 int orc_exact_f64(const double* q, const double* k, const double* v, int N, int M, int d,
                   int causal, double sm_scale, double* out) {
+  int off;
   if (!q || !k || !v || !out || N < 1 || M < 1 || d < 1) return -1;
-  if (causal && N != M) return -1;
+  if (causal_offset(causal, N, M, &off)) return -1;
 #pragma omp parallel
   {
     double* s = malloc(sizeof(double) * M);
 #pragma omp for schedule(dynamic, 4)
     for (int r = 0; r < N; r++)
-      exact_row(q + (size_t)r * d, k, v, M, d, causal ? r + 1 : M, sm_scale, s, out + (size_t)r * d);
+      exact_row(q + (size_t)r * d, k, v, M, d, causal ? visible(r, off, M) : M, sm_scale, s, out + (size_t)r * d);
     free(s);
   }
   return 0;
@@ -750,8 +766,9 @@ int orc_exact_f64(const double* q, const double* k, const double* v, int N, int 
 int orc_exact_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, int in_fp16,
                    int N, int M, int d, int causal, double sm_scale,
                    const int* rows, int nrows, double* out) {
+  int off;
   if (!q || !k || !v || !out || N < 1 || M < 1 || d < 1 || nrows < 0) return -1;
-  if (causal && N != M) return -1;
+  if (causal_offset(causal, N, M, &off)) return -1;
   if (!rows && nrows != N) return -1;
   double* K = malloc(sizeof(double) * (size_t)M * d);
   double* V = malloc(sizeof(double) * (size_t)M * d);
@@ -771,7 +788,7 @@ int orc_exact_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, int 
       if (r < 0 || r >= N) { bad = 1; continue; }
       for (int c = 0; c < d; c++)
         qr[c] = in_fp16 ? orc_fp16_to_f32(q[(size_t)r * d + c]) : orc_bf16_to_f32(q[(size_t)r * d + c]);
-      exact_row(qr, K, V, M, d, causal ? r + 1 : M, sm_scale, s, out + (size_t)x * d);
+      exact_row(qr, K, V, M, d, causal ? visible(r, off, M) : M, sm_scale, s, out + (size_t)x * d);
     }
     free(s);
     free(qr);

@@ -82,10 +82,6 @@ int orc_preprocess_head(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         uint8_t* vhat, float* dv, int8_t* qhat, float* dq,
                         float* qmean, double* ds);
 
-/* ---- forward of one head: the quantized method, FP64 everywhere it is not quantized ----
- * rows: the query rows to produce (NULL with nrows = N means all rows in order);
- * out: [nrows][d] in FP64.  causal requires N == M (mask key t > row r).
- * Returns 0, or -1 on a bad argument. */
 /* MX variant (ORC_MXFP4 implied): E2M1 codes of gamma(Q) [N][d], gamma(K) [M][d], V' [M][d];
  * E8M0 exponents (unbiased) [N][d/32], [M][d/32] per 32 channels and [ceil(M/32)][d] per 32
  * tokens of each V channel.  flags: ORC_SMOOTH_V / ORC_NO_SMOOTH_K / ORC_NO_SMOOTH_Q. */
@@ -93,6 +89,12 @@ int orc_preprocess_mx_head(const uint16_t* q, const uint16_t* k, const uint16_t*
                            int N, int M, int d, unsigned flags,
                            uint8_t* qcode, int* qexp, uint8_t* kcode, int* kexp,
                            uint8_t* vcode, int* vexp);
+/* ---- forward of one head: the quantized method, FP64 everywhere it is not quantized ----
+ * rows: the query rows to produce (NULL with nrows = N means all rows in order);
+ * out: [nrows][d] in FP64.  causal: 0 none; 1 key t visible to row r iff t <= r (first
+ * query aligned with the first key); 2 iff t <= r + M - N (last query aligned with the last
+ * key; needs N <= M).
+ * Returns 0, or -1 on a bad argument. */
 int orc_forward_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, int in_fp16,
                      int N, int M, int d, int causal, double sm_scale, unsigned flags,
                      const int* rows, int nrows, double* out);

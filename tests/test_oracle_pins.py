@@ -124,6 +124,58 @@ def test_identity_quantizers_equal_textbook_attention(fp16, d, N, M, causal, fla
     assert np.array_equal(sub, idm[rows])
 
 
+# ---------------------------------------------------------------- causal alignments, N != M
+@pytest.mark.parametrize("N,M", [(37, 37), (20, 53), (53, 20), (1, 9)])
+def test_causal_alignments_match_torch_masks(N, M):
+    """causal = 1: key t visible to row r iff t <= r (the upper triangle of the N x M score
+    matrix masked, as the pages' reference code does); causal = 2: iff t <= r + M - N (the
+    last query aligned with the last key).  Masks built independently with torch.tril."""
+    rng = np.random.default_rng(N * 100 + M)
+    d = 16
+    q, k, v = rng.standard_normal((N, d)), rng.standard_normal((M, d)), rng.standard_normal((M, d))
+    S = torch.from_numpy(q) @ torch.from_numpy(k).T * 0.41
+    for causal, diag in [(1, 0), (2, M - N)]:
+        if causal == 2 and N > M:
+            with pytest.raises(ValueError):
+                oracle.exact_f64(q, k, v, causal, 0.41)
+            continue
+        keep = torch.ones(N, M, dtype=torch.bool).tril(diag)
+        ref = (torch.softmax(S.masked_fill(~keep, float("-inf")), dim=-1) @ torch.from_numpy(v)).numpy()
+        got = oracle.exact_f64(q, k, v, causal, 0.41)
+        assert np.abs(got - ref).max() < 1e-13
+
+
+def test_bottom_right_equals_suffix_of_full_causal():
+    """The last N queries of a causal sequence of M tokens, attending under causal = 2, give the
+    last N rows of causal attention over all M queries."""
+    cfg = sy.CONFIGS["tiny"].with_shape(N=150, M=150)
+    q, k, v = [x[0, 0] for x in sy.make_qkv(cfg)]
+    s = 1 / 8
+    full = oracle.exact_head(q, k, v, True, 1, s)
+    tail = oracle.exact_head(q[100:], k, v, True, 2, s)
+    assert np.abs(tail - full[100:]).max() < 1e-13
+
+
+@pytest.mark.parametrize("N,M,causal,flags", [(90, 300, 2, 0), (90, 300, 1, oracle.SMOOTH_V),
+                                              (300, 90, 1, 0), (200, 200, 2, oracle.SMOOTH_V)])
+def test_identity_quantizers_causal_alignments(N, M, causal, flags):
+    cfg = sy.CONFIGS["video17k"].with_shape(N=N, M=M, d=64, H=1, B=1)
+    q, k, v = [x[0, 0] for x in sy.make_qkv(cfg)]
+    s = 1 / 8
+    ex = oracle.exact_head(q, k, v, False, causal, s)
+    idm = oracle.forward_head(q, k, v, False, causal, s, flags | oracle.QK_IDENTITY | oracle.PV_IDENTITY)
+    assert np.abs(idm - ex).max() < 1e-10
+
+
+def test_causal_argument_rejected():
+    q = np.zeros((5, 64), np.uint16)
+    k = np.zeros((3, 64), np.uint16)
+    with pytest.raises(ValueError):
+        oracle.forward_head(q, k, k, False, 2, 0.1)  # bottom-right needs N <= M
+    with pytest.raises(ValueError):
+        oracle.forward_head(q, q, q, False, 3, 0.1)
+
+
 # ---------------------------------------------------------------- QK-lossless construction
 def qk_lossless_case(seed, N, M, d):
     """fp16 inputs whose smoothed Q, K are exactly on the per-token / per-group INT8 grids."""
