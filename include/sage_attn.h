@@ -19,8 +19,12 @@
  *   - Q is [B][H][N][d], K and V are [B][H][M][d], out is [B][H][N][d]; all contiguous,
  *     row-major, 16-byte aligned device pointers on the current HIP device.  Inputs are bf16
  *     or fp16 (SAGE_IN_*); out is the input type, or FP32 with SAGE_OUT_FP32.
- *   - d is 64 or 128; B, H, N, M >= 1; B*H*max(N,M)*d < 2^40.  causal masks key t > query r
- *     (top-left alignment) and needs N == M.
+ *   - d is 64 or 128; B, H, N, M >= 1; B*H*max(N,M)*d < 2^40.
+ *   - causal: 0 no mask; 1 key t visible to query r iff t <= r (the first query aligned with
+ *     the first key: the upper triangle of the N x M score matrix is masked, as the pages'
+ *     reference code does; any N, M); 2 iff t <= r + M - N (the last query aligned with the
+ *     last key: the N queries follow the M - N earlier tokens of a key/value cache; needs
+ *     N <= M, else SAGE_ERR_UNSUPPORTED).  Other values are SAGE_ERR_INVALID_ARG.
  *   - sm_scale <= 0 or not finite selects 1/sqrt(d).
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue work on it and
  *     never synchronize the host; the caller keeps every buffer alive until the stream has
@@ -43,8 +47,8 @@ extern "C" {
 typedef enum {
   SAGE_OK = 0,
   SAGE_ERR_INVALID_ARG = -1, /* null/misaligned pointer, bad size, bad variant bits      */
-  SAGE_ERR_UNSUPPORTED = -2, /* valid request this build does not serve (d, causal N!=M,
-                                non-gfx950 device)                                         */
+  SAGE_ERR_UNSUPPORTED = -2, /* valid request this build does not serve (d, causal = 2 with
+                                N > M, non-gfx950 device)                                  */
   SAGE_ERR_NO_MEMORY = -3,   /* workspace allocation failed, or a given workspace is small */
   SAGE_ERR_LAUNCH = -4,      /* a kernel launch or stream call failed                      */
   SAGE_ERR_DEVICE = -5       /* no usable HIP device                                       */
@@ -110,7 +114,8 @@ int sage_attn_fwd_ws(const void* q, const void* k, const void* v, void* out,
  *   v_mean  float [BH][d]       token mean of V (0 unless SAGE_SMOOTH_V)
  *   q_mean  float [BH][nqb][d]  per-block mean of Q
  *   delta_s float [BH][nqb][Mp] Delta S_i[t] = q_i . gamma(K)[t] (FP32); with causal only
- *           t < 128*(i+1) is written
+ *           the 64-key tiles that block i attends to (t < 128*(i+1) + (M - N for causal = 2))
+ *           are written
  * With SAGE_PATH_MXFP4 the quantized tensors are E2M1 codes (sign << 3 | magnitude index
  * into {0, 0.5, 1, 1.5, 2, 3, 4, 6}), two per byte, the lower-indexed element in the low
  * nibble, and the scales are E8M0 bytes (2^(byte - 127)):

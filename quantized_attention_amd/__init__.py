@@ -155,7 +155,9 @@ def sage_attn(q, k, v, causal: bool = False, sm_scale: float | None = None, smoo
     """softmax(Q K^T * sm_scale) V with the quantized method, for [B, H, N, d] tensors.
 
     q: [B, H, N, d], k/v: [B, H, M, d], all the same dtype (bf16/fp16), contiguous, on the
-    current device.  Returns out [B, H, N, d] in the input dtype (FP32 with out_fp32).
+    current device.  causal: False/0 none, True/1 key t visible to query r iff t <= r, 2 iff
+    t <= r + M - N (queries are the last N of M tokens).  Returns out [B, H, N, d] in the
+    input dtype (FP32 with out_fp32).
     mxfp4 selects the MXFP4 variant (E2M1 operands with E8M0 block scales).
     """
     import torch

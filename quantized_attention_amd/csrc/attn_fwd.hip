@@ -73,6 +73,7 @@ struct AttnArgs {
   const float* ds;  // Delta S * sm_scale * log2(e)
   void* out;
   int N, M, BH, nqb, nkt, Np, Mp;
+  int coff;         // causal: key t visible to query r iff t <= r + coff
   float qk_scale;   // sm_scale * log2(e)
   int xcd_map;      // 1: heads grouped per XCD
 };
@@ -237,7 +238,7 @@ __global__ __launch_bounds__(256, OCC) void attn_fwd_kernel(AttnArgs a) {
     for (int r = 0; r < 16; r++) O[c][r] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  const int jend = CAUSAL ? min(a.nkt, (q0 + kBQ + kBK - 1) / kBK) : a.nkt;
+  const int jend = CAUSAL ? min(a.nkt, (q0 + kBQ + a.coff + kBK - 1) / kBK) : a.nkt;
   const int8_t* kbase = a.khat + (size_t)bh * a.Mp * D;
   const uint8_t* vbase = a.vhat + (size_t)bh * a.nkt * D * kBK;
   const float* dsbase = a.ds + ((size_t)bh * a.nqb + qb) * a.Mp;
@@ -281,7 +282,7 @@ __global__ __launch_bounds__(256, OCC) void attn_fwd_kernel(AttnArgs a) {
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kPerTile) : "memory");
   };
 
-  auto skip_t = [&](int j) { return CAUSAL && j * kBK > wq0 + 31; };  // fully masked for this wave
+  auto skip_t = [&](int j) { return CAUSAL && j * kBK > wq0 + 31 + a.coff; };  // fully masked for this wave
   if constexpr (PIPE) {
     // Software pipeline per wave: the QK MFMAs of tile j+1 are issued before the softmax of
     // tile j, so the matrix core works on j+1 while the VALU works on j.  Tile j+3 streams into
@@ -292,9 +293,9 @@ __global__ __launch_bounds__(256, OCC) void attn_fwd_kernel(AttnArgs a) {
       if (j + 1 < jend && !skip_t(j + 1)) qk_tile<D>(sK[(j + 1) % NB], qf, h, col, nxt);
       if (!skip_t(j)) {
         const int key0 = j * kBK;
-        const bool masked = (CAUSAL && key0 + kBK - 1 > wq0) || (key0 + kBK > a.M);
+        const bool masked = (CAUSAL && key0 + kBK - 1 > wq0 + a.coff) || (key0 + kBK > a.M);
         const int b = j % NB;
-        softmax_pv<D, CAUSAL, ACC_VALU>(cur, sV[b], sDS[b], sDK[b], dql, h, col, key0, qrow, a.M, masked, O,
+        softmax_pv<D, CAUSAL, ACC_VALU>(cur, sV[b], sDS[b], sDK[b], dql, h, col, key0, qrow + a.coff, a.M, masked, O,
                                         m_run, l_run);
       }
       publish(j + 3 < jend);  // tile j+2 must be complete; j+3 may still be arriving
@@ -333,10 +334,10 @@ __global__ __launch_bounds__(256, OCC) void attn_fwd_kernel(AttnArgs a) {
       if (j + NB - 1 < jend) dma(j + NB - 1, (b + NB - 1) % NB);  // the slot tile j-1 left
       if (!skip_t(j)) {
         const int key0 = j * kBK;
-        const bool masked = (CAUSAL && key0 + kBK - 1 > wq0) || (key0 + kBK > a.M);
+        const bool masked = (CAUSAL && key0 + kBK - 1 > wq0 + a.coff) || (key0 + kBK > a.M);
         v16i acc[2];
         qk_tile<D>(sK[b], qf, h, col, acc);
-        softmax_pv<D, CAUSAL, ACC_VALU>(acc, sV[b], sDS[b], sDK[b], dql, h, col, key0, qrow, a.M, masked, O,
+        softmax_pv<D, CAUSAL, ACC_VALU>(acc, sV[b], sDS[b], sDK[b], dql, h, col, key0, qrow + a.coff, a.M, masked, O,
                                         m_run, l_run);
       }
       publish_n(min(NB - 2, jend - j - 2));
@@ -414,6 +415,7 @@ hipError_t launch_attn_fwd(const Problem& p, const Workspace& w, void* out, hipS
   a.qhat = w.qhat; a.khat = w.khat; a.vhat = w.vhat; a.dq = w.dq; a.dk = w.dk; a.dv = w.dv;
   a.vmean = w.vmean; a.ds = w.ds; a.out = out;
   a.N = p.N; a.M = p.M; a.BH = p.BH; a.nqb = p.nqb; a.nkt = p.nkt; a.Np = p.Np; a.Mp = p.Mp;
+  a.coff = p.coff;
   a.qk_scale = p.sm_scale * kLog2e;
   a.xcd_map = (p.BH % kXCD == 0) ? 1 : 0;
   const bool valu = (p.variant & SAGE_ACC_VALU) != 0;

@@ -63,6 +63,7 @@ struct MxArgs {
   const float* ds;      // Delta S * sm_scale * log2(e)
   void* out;
   int N, M, BH, nqb, nkt, Np, Mp;
+  int coff;         // causal: key t visible to query r iff t <= r + coff
   float qk_scale;       // sm_scale * log2(e)
   int xcd_map;
 };
@@ -244,7 +245,7 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 3) void attn_fwd_mx_kernel(MxArg
     for (int r = 0; r < 16; r++) O[c][r] = 0.0f;
   float m_run = -INFINITY, l_run = 0.0f;
 
-  const int jend = CAUSAL ? min(a.nkt, (q0 + kBQ + kBK - 1) / kBK) : a.nkt;
+  const int jend = CAUSAL ? min(a.nkt, (q0 + kBQ + a.coff + kBK - 1) / kBK) : a.nkt;
   const uint8_t* kbase = a.khat + (size_t)bh * a.Mp * (D / 2);
   const uint8_t* vbase = a.vhat + (size_t)bh * a.nkt * TL::VBYTES;
   const float* dsbase = a.ds + ((size_t)bh * a.nqb + qb) * a.Mp;
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 3) void attn_fwd_mx_kernel(MxArg
   // that closed it; at the end of iteration j, tile j+1 must have landed for all waves.
   auto publish = [&]() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
-  auto skip_t = [&](int j) { return CAUSAL && j * kBK > wq0 + 31; };  // fully masked for this wave
+  auto skip_t = [&](int j) { return CAUSAL && j * kBK > wq0 + 31 + a.coff; };  // fully masked for this wave
   dma(0, 0);
   publish();
   // One iteration; the slot is a compile-time constant so LDS addresses are immediates.
@@ -285,10 +286,10 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 3) void attn_fwd_mx_kernel(MxArg
     if (j + 1 < jend) dma(j + 1, 1 - b);
     if (!skip_t(j)) {
       const int key0 = j * kBK;
-      const bool masked = (CAUSAL && key0 + kBK - 1 > wq0) || (key0 + kBK > a.M);
+      const bool masked = (CAUSAL && key0 + kBK - 1 > wq0 + a.coff) || (key0 + kBK > a.M);
       v16f acc[2];
       qk_tile_mx<D>(sK[b], qf, sKS[b][lane], qs, h, col, acc);
-      softmax_pv_mx<D, CAUSAL, ACC_VALU>(acc, sV[b], sDS[b], sVS[b][lane], a.qk_scale, h, col, key0, qrow, a.M,
+      softmax_pv_mx<D, CAUSAL, ACC_VALU>(acc, sV[b], sDS[b], sVS[b][lane], a.qk_scale, h, col, key0, qrow + a.coff, a.M,
                                          masked, O, m_run, l_run);
     }
     publish();
@@ -347,6 +348,7 @@ hipError_t launch_attn_fwd_mx(const Problem& p, const Workspace& w, void* out, h
   a.qsc = w.qsc; a.ksc = w.ksc; a.vsc = w.vsc;
   a.vmean = w.vmean; a.ds = w.ds; a.out = out;
   a.N = p.N; a.M = p.M; a.BH = p.BH; a.nqb = p.nqb; a.nkt = p.nkt; a.Np = p.Np; a.Mp = p.Mp;
+  a.coff = p.coff;
   a.qk_scale = p.sm_scale * kLog2e;
   a.xcd_map = (p.BH % kXCD == 0) ? 1 : 0;
   const bool valu = (p.variant & SAGE_ACC_VALU) != 0;

@@ -306,7 +306,7 @@ struct KVArgs {
   uint8_t* ksc;  // MX: E8M0 of gamma(K) blocks, [BH][nkt][64][4]
   uint8_t* vsc;  // MX: E8M0 of V' blocks, [BH][nkt][64][4]
   float ds_scale;
-  int M, Mp, nkt, nqb, causal;
+  int M, Mp, nkt, nqb, causal, coff;
   bool fp16;
 };
 
@@ -456,7 +456,8 @@ __global__ __launch_bounds__(256, 4) void kv_quant_kernel(KVArgs a) {
   // head/tail once and computes both 32-key halves of the tile against them.
   if (a.ds) {
     const int h = lane >> 5, col = lane & 31;
-    const int ilo = a.causal ? u / 2 : 0;  // block i needs keys < 128 (i + 1)
+    // under the causal mask, block i needs keys t <= 128 (i + 1) - 1 + coff
+    const int ilo = (a.causal && t0 > a.coff) ? (t0 - a.coff) / kBQ : 0;
     for (int gidx = wave; 32 * gidx < a.nqb; gidx += 4) {
       if (32 * gidx + 31 < ilo) continue;
       const int blk = 32 * gidx + col;
@@ -618,6 +619,7 @@ hipError_t launch_kv_quant(const Problem& p, const void* k, const void* v, const
   a.nkt = p.nkt;
   a.nqb = p.nqb;
   a.causal = p.causal;
+  a.coff = p.coff;
   a.fp16 = p.fp16;
   const dim3 grid(p.nkt, p.BH);
   if (p.d == 128) {

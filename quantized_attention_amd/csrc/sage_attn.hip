@@ -108,12 +108,14 @@ int make_problem(int B, int H, int N, int M, int d, int causal, float sm_scale, 
   if (B < 1 || H < 1 || N < 1 || M < 1) return SAGE_ERR_INVALID_ARG;
   if (variant & ~kKnownBits) return SAGE_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return SAGE_ERR_UNSUPPORTED;
-  if (causal && N != M) return SAGE_ERR_UNSUPPORTED;
+  if (causal < 0 || causal > 2) return SAGE_ERR_INVALID_ARG;
+  if (causal == 2 && N > M) return SAGE_ERR_UNSUPPORTED;  // some rows would see no key
   const double big = (double)B * H * (double)(N > M ? N : M) * d;
   if (big >= 1099511627776.0) return SAGE_ERR_INVALID_ARG;  // 2^40 elements
   if ((long long)B * H > (1LL << 30)) return SAGE_ERR_INVALID_ARG;
   p->B = B; p->H = H; p->N = N; p->M = M; p->d = d;
-  p->causal = causal ? 1 : 0;
+  p->causal = causal;
+  p->coff = causal == 2 ? M - N : 0;
   p->sm_scale = (sm_scale > 0.0f && std::isfinite(sm_scale)) ? sm_scale : 1.0f / std::sqrt((float)d);
   p->variant = variant;
   p->BH = B * H;
@@ -255,7 +257,7 @@ const char* sage_attn_status_string(int status) {
   switch (status) {
     case SAGE_OK: return "ok";
     case SAGE_ERR_INVALID_ARG: return "invalid argument";
-    case SAGE_ERR_UNSUPPORTED: return "unsupported (head dim, causal with N != M, or non-gfx950 device)";
+    case SAGE_ERR_UNSUPPORTED: return "unsupported (head dim, bottom-right causal with N > M, or non-gfx950 device)";
     case SAGE_ERR_NO_MEMORY: return "workspace allocation failed or workspace too small";
     case SAGE_ERR_LAUNCH: return "kernel launch failed";
     case SAGE_ERR_DEVICE: return "no usable HIP device";

@@ -24,7 +24,8 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // Resolved problem: sizes, padded sizes and the variant bits.
 struct Problem {
   int B, H, N, M, d;
-  int causal;
+  int causal;  // 0 none, 1 first query aligned with the first key, 2 last with the last
+  int coff;    // causal: key t is visible to query r iff t <= r + coff (0, or M - N)
   float sm_scale;
   unsigned variant;
   int BH, nqb, nkt, Np, Mp;

@@ -44,7 +44,7 @@ class Config:
     M: int
     d: int
     dtype: str          # "bf16" or "fp16"
-    causal: bool
+    causal: int  # 0 none; 1 first query aligned with the first key; 2 last with the last
     dist: Dist
     seed: int
     smooth_v: bool = False
@@ -78,6 +78,9 @@ CONFIGS = {
     "video17k": Config("video17k", 2, 48, 17550, 17550, 64, "bf16", False,
                        Dist(q_off_std=3.0, k_off_std=3.0, v_bias_std=1.0), 1004, smooth_v=True,
                        note="video diffusion shape, ragged last tile, V smoothing"),
+    "chunk4k_32k": Config("chunk4k_32k", 1, 32, 4096, 32768, 128, "bf16", 2,
+                          Dist(k_off_std=4.0, k_spike=8.0, k_spike_channels=spike_channels(128)), 1006,
+                          note="chunked prefill: the last 4096 queries over a 32768-token cache, causal"),
     "mxfp4_32k": Config("mxfp4_32k", 1, 24, 32768, 32768, 128, "bf16", False,
                         Dist(k_off_std=2.0, v_bias_std=0.5), 1005, mxfp4=True,
                         note="MXFP4 variant"),

@@ -46,7 +46,9 @@ def test_argument_errors_are_reported_before_any_device_work():
     assert f(A, A, A, A, 0, 1, 64, 64, 64, 0, 0.0, 0, 0) == qa.SAGE_ERR_INVALID_ARG   # B = 0
     assert f(A, A, A, A, 1, 1, 0, 64, 64, 0, 0.0, 0, 0) == qa.SAGE_ERR_INVALID_ARG   # N = 0
     assert f(A, A, A, A, 1, 1, 64, 64, 96, 0, 0.0, 0, 0) == qa.SAGE_ERR_UNSUPPORTED  # d = 96
-    assert f(A, A, A, A, 1, 1, 64, 65, 64, 1, 0.0, 0, 0) == qa.SAGE_ERR_UNSUPPORTED  # causal N != M
+    assert f(A, A, A, A, 1, 1, 65, 64, 64, 2, 0.0, 0, 0) == qa.SAGE_ERR_UNSUPPORTED  # bottom-right, N > M
+    assert f(A, A, A, A, 1, 1, 64, 64, 64, 3, 0.0, 0, 0) == qa.SAGE_ERR_INVALID_ARG  # causal mode 3
+    assert f(A, A, A, A, 1, 1, 64, 64, 64, -1, 0.0, 0, 0) == qa.SAGE_ERR_INVALID_ARG
     assert f(A, A, A, A, 1, 1, 64, 64, 64, 0, 0.0, 0x8, 0) == qa.SAGE_ERR_INVALID_ARG  # unknown bit
     ws = qa.sage_attn_workspace_bytes(1, 1, 64, 64, 64, 0, 0)
     assert ws > 0
@@ -54,6 +56,14 @@ def test_argument_errors_are_reported_before_any_device_work():
     assert qa.sage_attn_fwd_ws(A, A, A, A, 1, 1, 64, 64, 64, 0, 0.0, 0, A + 16, ws, 0) == qa.SAGE_ERR_INVALID_ARG
     assert qa.sage_attn_workspace_bytes(1, 1, 64, 64, 80, 0, 0) == 0
     assert qa.sage_attn_quantize(0, A, A, 1, 1, 64, 64, 64, 0, 0, qa.QuantViews(), 0) == qa.SAGE_ERR_INVALID_ARG
+
+
+def test_causal_modes_accept_uneven_lengths():
+    # causal = 1 (first query aligned with the first key) takes any N, M; causal = 2 (last with
+    # last) takes N <= M: both size a workspace, N != M included
+    for causal, N, M in [(1, 64, 200), (1, 200, 64), (2, 64, 200), (2, 200, 200)]:
+        assert qa.sage_attn_workspace_bytes(1, 1, N, M, 64, causal, 0) > 0
+    assert qa.sage_attn_workspace_bytes(1, 1, 200, 64, 64, 2, 0) == 0
 
 
 def test_workspace_grows_with_problem():

@@ -49,6 +49,7 @@ MX_CASES = [
                                  sy.Dist(q_off_std=1.0, k_off_std=2.0, v_bias_std=0.5), 77)),
     ("one-token", sy.Config("one", 1, 1, 1, 1, 64, "bf16", False, sy.Dist(), 79)),
     ("few-tokens", sy.Config("few", 1, 3, 5, 3, 128, "fp16", False, sy.Dist(k_off_std=1.0), 80)),
+    ("causal-br-N<M", sy.CONFIGS["mxfp4_32k"].with_shape(H=2, N=300, M=1000, causal=2)),
 ]
 
 

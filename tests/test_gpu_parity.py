@@ -56,6 +56,10 @@ SMALL_CASES = [
                                   sy.Dist(k_off_std=3.0, k_spike=8.0, k_spike_channels=sy.spike_channels(64)), 78)),
     ("one-token", sy.Config("one", 1, 1, 1, 1, 64, "bf16", False, sy.Dist(), 79)),
     ("few-tokens", sy.Config("few", 1, 3, 5, 3, 128, "fp16", False, sy.Dist(k_off_std=1.0), 80)),
+    ("causal-br-N<M", small("prefill32k", H=2, N=300, M=1000, causal=2)),
+    ("causal-tl-N<M", small("prefill32k", H=2, N=300, M=700, causal=1)),
+    ("causal-tl-N>M", small("prefill32k", H=1, N=700, M=300, causal=1)),
+    ("causal-br-d64-smoothv", small("video17k", B=1, H=2, N=200, M=900, causal=2)),
 ]
 
 
@@ -89,7 +93,10 @@ def test_preprocess_bit_exact(name, cfg):
         assert not g["v_nat"][bh, M:].any()
         ds, ref = g["delta_s"][bh][:, :M].astype(np.float64), o["ds"]
         if cfg.causal:
-            mask = np.arange(M)[None, :] < 128 * (np.arange(ds.shape[0])[:, None] + 1)
+            # written: the 64-key tiles whose first key is < 128 (i + 1) + coff
+            coff = cfg.M - cfg.N if cfg.causal == 2 else 0
+            tile0 = 64 * (np.arange(M) // 64)
+            mask = tile0[None, :] - coff < 128 * (np.arange(ds.shape[0])[:, None] + 1)
             ds, ref = ds[mask], ref[mask]
         assert np.abs(ds - ref).max() <= 1e-5 * max(1.0, np.abs(ref).max())
 
@@ -178,7 +185,7 @@ def test_sm_scale_argument():
 
 
 # ---------------------------------------------------------------- full workload shapes
-FULL = ["n4k", "prefill32k", "video17k"]
+FULL = ["n4k", "prefill32k", "video17k", "chunk4k_32k"]
 
 
 def sample_rows(N, seed):
