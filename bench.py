@@ -3,7 +3,7 @@
 
 One step = one whole forward pass (preprocessing: means, INT8/FP8 quantization, Delta S;
 then the fused attention kernel) over one batch of seeded synthetic input already
-resident in HBM, through the C ABI (sage_attn_fwd_ws with a preallocated workspace).
+resident in HBM, through the C ABI (sage_attn_fwd_ex with a preallocated workspace).
 
 Metric: attention TOPS = 4 N^2 d H B / time, causal counted as half (the pages'
 convention: "Quantization for Attention, in depth", "When attention compute is worth
@@ -73,7 +73,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill32k",
-                    help="one of: n4k, prefill32k, video17k, chunk4k_32k, mxfp4_32k (default prefill32k)")
+                    help="one of: n4k, prefill32k, video17k, chunk4k_32k, prefill32k_gqa, mxfp4_32k (default prefill32k)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -174,7 +174,8 @@ def main():
     if cfg.mxfp4:
         var |= qa.SAGE_PATH_MXFP4
     peak = PEAK_TOPS_FP4 if cfg.mxfp4 else PEAK_TOPS
-    ws_bytes = qa.sage_attn_workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.M, cfg.d, cfg.causal, var)
+    shape = qa.SageAttnShape(cfg.B, cfg.H, cfg.hkv, cfg.N, cfg.M, cfg.d, int(cfg.causal), 1.0 / math.sqrt(cfg.d), var)
+    ws_bytes = qa.sage_attn_workspace_bytes_ex(shape)
     ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
     ws_ptr = (ws.data_ptr() + 255) // 256 * 256
     stream = torch.cuda.current_stream(dev).cuda_stream
@@ -184,10 +185,10 @@ def main():
     def step(evs=None):
         if evs is not None:
             qa.sage_attn_set_profile_events(evs[0], evs[1])
-        rc = qa.sage_attn_fwd_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), cfg.B, cfg.H,
-                                 cfg.N, cfg.M, cfg.d, cfg.causal, scale, var, ws_ptr, ws_bytes, stream)
+        rc = qa.sage_attn_fwd_ex(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), ws_ptr, ws_bytes,
+                                 stream)
         if rc != qa.SAGE_OK:
-            raise qa.SageError(rc, "sage_attn_fwd_ws")
+            raise qa.SageError(rc, "sage_attn_fwd_ex")
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
@@ -234,7 +235,7 @@ def main():
         "vs_baseline": None,
         "dtype": dtype,
         "data": "synthetic (seeded Gaussian + per-channel offsets)",
-        "config": {"workload": f"{cfg.name}: B={cfg.B} H={cfg.H} "
+        "config": {"workload": f"{cfg.name}: B={cfg.B} H={cfg.H} " + (f"Hkv={cfg.hkv} " if cfg.hkv != cfg.H else "")
                                + (f"N=M={cfg.N}" if cfg.N == cfg.M else f"N={cfg.N} M={cfg.M}")
                                + f" d={cfg.d} {cfg.dtype} "
                                f"{('causal' if cfg.causal == 1 or cfg.N == cfg.M else 'causal (last query on last key)') if cfg.causal else 'non-causal'}"

@@ -158,6 +158,46 @@ int sage_attn_quantize(const void* q, const void* k, const void* v,
                        const sage_quant_views* dst, void* stream);
 
 /*
+ * Extended entry points: the same forward pass, preprocessing and workspace query for a
+ * shape given as a struct, which also carries grouped key/value heads.
+ *
+ * Grouped heads (Hkv < Hq, Hq % Hkv == 0): query head h attends with key/value head
+ * h / (Hq / Hkv) (consecutive query heads share one key/value head).  The method is applied
+ * per (query head, key/value head) pair exactly as for Hkv == Hq: the K mean, V_m, the K and
+ * V quantization and their scales belong to the key/value head; the Q block means, Q^, its
+ * scales and Delta S_i[t] = q_i . gamma(K)[t] belong to the query head.  (The pages' example
+ * 8B layer leaves grouped-query attention aside; this is the plain extension.)
+ * Layouts: q and out [B][Hq][N][d]; k and v [B][Hkv][M][d].  In the quantize views the
+ * K/V-side tensors (k_hat, v_hat, dk, dv, k_mean, v_mean, mx_scales_k, mx_scales_v) have
+ * B*Hkv heads, the Q-side ones (q_hat, dq, q_mean, delta_s, mx_scales_q) B*Hq heads.
+ * Argument errors as for the plain entry points; Hkv < 1 or Hq % Hkv != 0 is
+ * SAGE_ERR_INVALID_ARG; a NULL shape is SAGE_ERR_INVALID_ARG (0 bytes from the size query).
+ */
+typedef struct {
+  int B;            /* batch                                                   */
+  int Hq;           /* query heads                                             */
+  int Hkv;          /* key/value heads (Hq % Hkv == 0; Hkv == Hq: no grouping) */
+  int N, M, d;      /* query tokens, key tokens, head dimension                */
+  int causal;       /* 0, 1 or 2, as above                                     */
+  float sm_scale;   /* <= 0 or not finite: 1/sqrt(d)                           */
+  unsigned variant; /* SAGE_* bits                                             */
+} sage_attn_shape;
+
+/* Workspace bytes sage_attn_fwd_ex needs for this shape (0 on bad arguments). */
+size_t sage_attn_workspace_bytes_ex(const sage_attn_shape* shape);
+
+/* The forward pass.  workspace: a caller-owned device buffer of ws_bytes bytes (256-byte
+ * aligned; SAGE_ERR_NO_MEMORY if smaller than sage_attn_workspace_bytes_ex), or NULL to
+ * allocate and release it on the stream (stream-ordered). */
+int sage_attn_fwd_ex(const sage_attn_shape* shape, const void* q, const void* k, const void* v, void* out,
+                     void* workspace, size_t ws_bytes, void* stream);
+
+/* The preprocessing step alone, into caller buffers (layouts as for sage_attn_quantize, with
+ * the per-head counts above). */
+int sage_attn_quantize_ex(const sage_attn_shape* shape, const void* q, const void* k, const void* v,
+                          const sage_quant_views* dst, void* stream);
+
+/*
  * sage_attn_set_profile_events -- measurement hook.  With both arguments non-NULL (two
  * hipEvent_t handles), the next sage_attn_fwd / sage_attn_fwd_ws call on this thread
  * records `start` on its stream just before the fused attention kernel and `stop` just

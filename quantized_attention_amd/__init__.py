@@ -21,6 +21,7 @@ __all__ = [
     "library_path", "load_library", "sage_attn_fwd", "sage_attn_fwd_ws",
     "sage_attn_workspace_bytes", "sage_attn_quantize", "sage_attn_status_string",
     "sage_attn_version", "sage_attn_set_profile_events", "sage_attn", "QuantViews",
+    "SageAttnShape", "sage_attn_fwd_ex", "sage_attn_workspace_bytes_ex", "sage_attn_quantize_ex",
 ]
 
 SAGE_OK = 0
@@ -62,6 +63,13 @@ class QuantViews(ctypes.Structure):
                  "mx_scales_q", "mx_scales_k", "mx_scales_v")]
 
 
+class SageAttnShape(ctypes.Structure):
+    """Mirror of ``sage_attn_shape`` (the extended entry points' shape, grouped heads included)."""
+    _fields_ = [("B", ctypes.c_int), ("Hq", ctypes.c_int), ("Hkv", ctypes.c_int), ("N", ctypes.c_int),
+                ("M", ctypes.c_int), ("d", ctypes.c_int), ("causal", ctypes.c_int),
+                ("sm_scale", ctypes.c_float), ("variant", ctypes.c_uint)]
+
+
 def library_path() -> str:
     return _LIB_PATH
 
@@ -90,6 +98,13 @@ def load_library():
     L.sage_attn_set_profile_events.restype = None
     L.sage_attn_version.argtypes = []
     L.sage_attn_version.restype = i
+    SP = ctypes.POINTER(SageAttnShape)
+    L.sage_attn_workspace_bytes_ex.argtypes = [SP]
+    L.sage_attn_workspace_bytes_ex.restype = sz
+    L.sage_attn_fwd_ex.argtypes = [SP, P, P, P, P, P, sz, P]
+    L.sage_attn_fwd_ex.restype = i
+    L.sage_attn_quantize_ex.argtypes = [SP, P, P, P, ctypes.POINTER(QuantViews), P]
+    L.sage_attn_quantize_ex.restype = i
     _lib = L
     return L
 
@@ -113,6 +128,22 @@ def sage_attn_workspace_bytes(B, H, N, M, d, causal, variant) -> int:
 def sage_attn_quantize(q, k, v, B, H, N, M, d, causal, variant, views: QuantViews, stream) -> int:
     return load_library().sage_attn_quantize(q, k, v, B, H, N, M, d, int(causal), variant,
                                              ctypes.byref(views), stream)
+
+
+def _shape_ptr(shape):
+    return ctypes.byref(shape) if shape is not None else None
+
+
+def sage_attn_workspace_bytes_ex(shape) -> int:
+    return load_library().sage_attn_workspace_bytes_ex(_shape_ptr(shape))
+
+
+def sage_attn_fwd_ex(shape, q, k, v, out, workspace, ws_bytes, stream) -> int:
+    return load_library().sage_attn_fwd_ex(_shape_ptr(shape), q, k, v, out, workspace, ws_bytes, stream)
+
+
+def sage_attn_quantize_ex(shape, q, k, v, views: QuantViews, stream) -> int:
+    return load_library().sage_attn_quantize_ex(_shape_ptr(shape), q, k, v, ctypes.byref(views), stream)
 
 
 def sage_attn_set_profile_events(start, stop) -> None:
@@ -154,8 +185,8 @@ def sage_attn(q, k, v, causal: bool = False, sm_scale: float | None = None, smoo
               out_fp32: bool = False, out=None, acc_valu: bool = False, mxfp4: bool = False):
     """softmax(Q K^T * sm_scale) V with the quantized method, for [B, H, N, d] tensors.
 
-    q: [B, H, N, d], k/v: [B, H, M, d], all the same dtype (bf16/fp16), contiguous, on the
-    current device.  causal: False/0 none, True/1 key t visible to query r iff t <= r, 2 iff
+    q: [B, H, N, d], k/v: [B, Hkv, M, d] (Hkv divides H: query head h reads key/value head
+    h // (H // Hkv)), all the same dtype (bf16/fp16), contiguous, on the current device.  causal: False/0 none, True/1 key t visible to query r iff t <= r, 2 iff
     t <= r + M - N (queries are the last N of M tokens).  Returns out [B, H, N, d] in the
     input dtype (FP32 with out_fp32).
     mxfp4 selects the MXFP4 variant (E2M1 operands with E8M0 block scales).
@@ -164,9 +195,11 @@ def sage_attn(q, k, v, causal: bool = False, sm_scale: float | None = None, smoo
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [B, H, T, d]")
     B, H, N, d = q.shape
-    M = k.shape[2]
-    if tuple(k.shape) != (B, H, M, d) or tuple(v.shape) != (B, H, M, d):
-        raise ValueError("k and v must be [B, H, M, d] matching q")
+    Hkv, M = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, M, d) or tuple(v.shape) != (B, Hkv, M, d):
+        raise ValueError("k and v must be [B, Hkv, M, d] matching q")
+    if Hkv < 1 or H % Hkv:
+        raise ValueError("the query heads must be a multiple of the key/value heads")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share a dtype")
     for t in (q, k, v):
@@ -177,8 +210,8 @@ def sage_attn(q, k, v, causal: bool = False, sm_scale: float | None = None, smoo
         out = torch.empty((B, H, N, d), dtype=torch.float32 if out_fp32 else q.dtype, device=q.device)
     scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(d)
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    rc = sage_attn_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, N, M, d,
-                       causal, scale, var, stream)
+    shape = SageAttnShape(B, H, Hkv, N, M, d, int(causal), scale, var)
+    rc = sage_attn_fwd_ex(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), None, 0, stream)
     if rc != SAGE_OK:
-        raise SageError(rc, "sage_attn_fwd")
+        raise SageError(rc, "sage_attn_fwd_ex")
     return out

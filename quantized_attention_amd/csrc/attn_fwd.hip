@@ -74,6 +74,7 @@ struct AttnArgs {
   void* out;
   int N, M, BH, nqb, nkt, Np, Mp;
   int coff;         // causal: key t visible to query r iff t <= r + coff
+  int H, Hkv, G;    // query heads, key/value heads, query heads per key/value head
   float qk_scale;   // sm_scale * log2(e)
   int xcd_map;      // 1: heads grouped per XCD
 };
@@ -208,15 +209,19 @@ __global__ __launch_bounds__(256, OCC) void attn_fwd_kernel(AttnArgs a) {
   int bh, qi;
   {
     const int L = blockIdx.x;
-    if (a.xcd_map) {  // XCD x gets heads x, x+8, ...; a head's blocks stay together
-      const int x = L % kXCD, r = L / kXCD;
-      bh = x + kXCD * (r / a.nqb);
+    if (a.xcd_map) {
+      // XCD x (work-groups are dealt to the XCDs round-robin) takes whole groups of query heads
+      // that share a key/value head: groups x, x+8, ...; a head's blocks stay together, so a
+      // key/value head's tiles are read through one XCD's L2.
+      const int x = L % kXCD, r = L / kXCD, k = r / a.nqb;
+      bh = (x + kXCD * (k / a.G)) * a.G + k % a.G;
       qi = r % a.nqb;
     } else {
       bh = L / a.nqb;
       qi = L % a.nqb;
     }
   }
+  const int kvh = kv_head(bh, a.H, a.Hkv, a.G);  // the key/value head this query head reads
   const int qb = CAUSAL ? (a.nqb - 1 - qi) : qi;  // heavy blocks first
   const int q0 = qb * kBQ;
   const int wq0 = q0 + 32 * w;       // first query of this wave
@@ -239,10 +244,10 @@ __global__ __launch_bounds__(256, OCC) void attn_fwd_kernel(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.0f;
 
   const int jend = CAUSAL ? min(a.nkt, (q0 + kBQ + a.coff + kBK - 1) / kBK) : a.nkt;
-  const int8_t* kbase = a.khat + (size_t)bh * a.Mp * D;
-  const uint8_t* vbase = a.vhat + (size_t)bh * a.nkt * D * kBK;
+  const int8_t* kbase = a.khat + (size_t)kvh * a.Mp * D;
+  const uint8_t* vbase = a.vhat + (size_t)kvh * a.nkt * D * kBK;
   const float* dsbase = a.ds + ((size_t)bh * a.nqb + qb) * a.Mp;
-  const float* dkbase = a.dk + (size_t)bh * a.nkt * 4;
+  const float* dkbase = a.dk + (size_t)kvh * a.nkt * 4;
 
   // ---- staging: global -> LDS by DMA (global_load_lds), no registers, no LDS stores ----
   // Per-lane source offsets inside a tile (the swizzle is the same for every tile).
@@ -354,8 +359,8 @@ __global__ __launch_bounds__(256, OCC) void attn_fwd_kernel(AttnArgs a) {
   const float l_tot = pair_sum(l_run);
   if (qrow >= a.N) return;
   const float inv = 1.0f / l_tot;
-  const float* dvp = a.dv + (size_t)bh * D;
-  const float* vmp = a.vmean + (size_t)bh * D;
+  const float* dvp = a.dv + (size_t)kvh * D;
+  const float* vmp = a.vmean + (size_t)kvh * D;
   const size_t orow = ((size_t)bh * a.N + qrow) * D;
 #pragma unroll
   for (int c = 0; c < NKS; c++) {
@@ -417,7 +422,8 @@ hipError_t launch_attn_fwd(const Problem& p, const Workspace& w, void* out, hipS
   a.N = p.N; a.M = p.M; a.BH = p.BH; a.nqb = p.nqb; a.nkt = p.nkt; a.Np = p.Np; a.Mp = p.Mp;
   a.coff = p.coff;
   a.qk_scale = p.sm_scale * kLog2e;
-  a.xcd_map = (p.BH % kXCD == 0) ? 1 : 0;
+  a.H = p.H; a.Hkv = p.Hkv; a.G = p.G;
+  a.xcd_map = (p.BH % (kXCD * p.G) == 0) ? 1 : 0;
   const bool valu = (p.variant & SAGE_ACC_VALU) != 0;
   if (p.d == 128) return valu ? launch_c<128, true>(p, a, s) : launch_c<128, false>(p, a, s);
   return valu ? launch_c<64, true>(p, a, s) : launch_c<64, false>(p, a, s);

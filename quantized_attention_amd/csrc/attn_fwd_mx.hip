@@ -64,6 +64,7 @@ struct MxArgs {
   void* out;
   int N, M, BH, nqb, nkt, Np, Mp;
   int coff;         // causal: key t visible to query r iff t <= r + coff
+  int H, Hkv, G;    // query heads, key/value heads, query heads per key/value head
   float qk_scale;       // sm_scale * log2(e)
   int xcd_map;
 };
@@ -211,15 +212,19 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 3) void attn_fwd_mx_kernel(MxArg
   int bh, qi;
   {
     const int L = blockIdx.x;
-    if (a.xcd_map) {  // XCD x gets heads x, x+8, ...; a head's blocks stay together
-      const int x = L % kXCD, r = L / kXCD;
-      bh = x + kXCD * (r / a.nqb);
+    if (a.xcd_map) {
+      // XCD x (work-groups are dealt to the XCDs round-robin) takes whole groups of query heads
+      // that share a key/value head: groups x, x+8, ...; a head's blocks stay together, so a
+      // key/value head's tiles are read through one XCD's L2.
+      const int x = L % kXCD, r = L / kXCD, k = r / a.nqb;
+      bh = (x + kXCD * (k / a.G)) * a.G + k % a.G;
       qi = r % a.nqb;
     } else {
       bh = L / a.nqb;
       qi = L % a.nqb;
     }
   }
+  const int kvh = kv_head(bh, a.H, a.Hkv, a.G);  // the key/value head this query head reads
   const int qb = CAUSAL ? (a.nqb - 1 - qi) : qi;  // heavy blocks first
   const int q0 = qb * kBQ;
   const int wq0 = q0 + 32 * w;
@@ -246,11 +251,11 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 3) void attn_fwd_mx_kernel(MxArg
   float m_run = -INFINITY, l_run = 0.0f;
 
   const int jend = CAUSAL ? min(a.nkt, (q0 + kBQ + a.coff + kBK - 1) / kBK) : a.nkt;
-  const uint8_t* kbase = a.khat + (size_t)bh * a.Mp * (D / 2);
-  const uint8_t* vbase = a.vhat + (size_t)bh * a.nkt * TL::VBYTES;
+  const uint8_t* kbase = a.khat + (size_t)kvh * a.Mp * (D / 2);
+  const uint8_t* vbase = a.vhat + (size_t)kvh * a.nkt * TL::VBYTES;
   const float* dsbase = a.ds + ((size_t)bh * a.nqb + qb) * a.Mp;
-  const uint8_t* ksbase = a.ksc + (size_t)bh * a.nkt * 256;
-  const uint8_t* vsbase = a.vsc + (size_t)bh * a.nkt * 256;
+  const uint8_t* ksbase = a.ksc + (size_t)kvh * a.nkt * 256;
+  const uint8_t* vsbase = a.vsc + (size_t)kvh * a.nkt * 256;
 
   // ---- staging by LDS DMA.  D = 128: wave w moves K^ KiB w and V^ KiB w; D = 64: waves 0-1
   // move K^, waves 2-3 move V^.  Waves 0, 1, 2 also move Delta S, the K scales, the V scales.
@@ -305,7 +310,7 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 3) void attn_fwd_mx_kernel(MxArg
   const float l_tot = pair_sum(l_run);
   if (qrow >= a.N) return;
   const float inv = 1.0f / l_tot;
-  const float* vmp = a.vmean + (size_t)bh * D;
+  const float* vmp = a.vmean + (size_t)kvh * D;
   const size_t orow = ((size_t)bh * a.N + qrow) * D;
 #pragma unroll
   for (int c = 0; c < NG; c++) {
@@ -350,7 +355,8 @@ hipError_t launch_attn_fwd_mx(const Problem& p, const Workspace& w, void* out, h
   a.N = p.N; a.M = p.M; a.BH = p.BH; a.nqb = p.nqb; a.nkt = p.nkt; a.Np = p.Np; a.Mp = p.Mp;
   a.coff = p.coff;
   a.qk_scale = p.sm_scale * kLog2e;
-  a.xcd_map = (p.BH % kXCD == 0) ? 1 : 0;
+  a.H = p.H; a.Hkv = p.Hkv; a.G = p.G;
+  a.xcd_map = (p.BH % (kXCD * p.G) == 0) ? 1 : 0;
   const bool valu = (p.variant & SAGE_ACC_VALU) != 0;
   if (p.d == 128) return valu ? launch_c<128, true>(p, a, s) : launch_c<128, false>(p, a, s);
   return valu ? launch_c<64, true>(p, a, s) : launch_c<64, false>(p, a, s);

@@ -307,14 +307,16 @@ struct KVArgs {
   uint8_t* vsc;  // MX: E8M0 of V' blocks, [BH][nkt][64][4]
   float ds_scale;
   int M, Mp, nkt, nqb, causal, coff;
+  int H, Hkv, G;  // query heads, key/value heads, query heads per key/value head
   bool fp16;
 };
 
-// ---- one 64-key tile: gamma(K), group scales, K^; Delta S against every query block;
+// ---- one 64-key tile of one key/value head (blockIdx.y): gamma(K), group scales, K^;
+// Delta S against every query block of every query head that reads this key/value head;
 // V' / dV -> E4M3, transposed in the P-fragment key order.  MX: gamma(K) and V' in E2M1
 // with an E8M0 scale per 32 channels of a key / per 32 tokens of a channel ----
 template <int D, bool MX>
-__global__ __launch_bounds__(256, 4) void kv_quant_kernel(KVArgs a) {
+__global__ __launch_bounds__(256, MX ? 3 : 4) void kv_quant_kernel(KVArgs a) {
   constexpr int RS = D + 8;                 // bf16 split of gamma(K), 16-byte aligned rows
   constexpr int CH = kBK * D / 8 / 256;     // 8-element chunks per thread
   // The bf16 split of gamma(K) (read by the Delta S MFMAs) and the staged V' (read by the
@@ -452,17 +454,21 @@ __global__ __launch_bounds__(256, 4) void kv_quant_kernel(KVArgs a) {
   __syncthreads();  // sAh / sAl complete before the Delta S MFMAs read them
 
   // ---- Delta S^T[key][block] = gamma(K) q^T on the bf16 MFMA, split operands ----
-  // A wave takes groups of 32 query blocks (gidx = wave, wave + 4, ...), loads their q-mean
-  // head/tail once and computes both 32-key halves of the tile against them.
+  // Work units are (query head of this key/value head, group of 32 query blocks); a wave
+  // takes units wave, wave + 4, ..., loads the group's q-mean head/tail once and computes
+  // both 32-key halves of the tile against them.
   if (a.ds) {
     const int h = lane >> 5, col = lane & 31;
     // under the causal mask, block i needs keys t <= 128 (i + 1) - 1 + coff
     const int ilo = (a.causal && t0 > a.coff) ? (t0 - a.coff) / kBQ : 0;
-    for (int gidx = wave; 32 * gidx < a.nqb; gidx += 4) {
+    const int ngrp = (a.nqb + 31) / 32;
+    for (int unit = wave; unit < a.G * ngrp; unit += 4) {
+      const int g = unit / ngrp, gidx = unit % ngrp;
       if (32 * gidx + 31 < ilo) continue;
+      const int bhq = (bh / a.Hkv) * a.H + (bh % a.Hkv) * a.G + g;  // query head
       const int blk = 32 * gidx + col;
       const bool bv = blk < a.nqb;
-      const size_t qo = ((size_t)bh * a.nqb + (bv ? blk : 0)) * D;
+      const size_t qo = ((size_t)bhq * a.nqb + (bv ? blk : 0)) * D;
       v8bf bq[D / 16], bl[D / 16];  // the block's q-mean head/tail, all loads in flight
 #pragma unroll
       for (int s = 0; s < D / 16; s++) {
@@ -483,7 +489,7 @@ __global__ __launch_bounds__(256, 4) void kv_quant_kernel(KVArgs a) {
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bq[s], acc, 0, 0, 0);
         }
         if (bv && blk >= ilo) {
-          float* dst = a.ds + ((size_t)bh * a.nqb + blk) * a.Mp + t0 + 32 * T + 4 * h;
+          float* dst = a.ds + ((size_t)bhq * a.nqb + blk) * a.Mp + t0 + 32 * T + 4 * h;
 #pragma unroll
           for (int b = 0; b < 4; b++)
             *reinterpret_cast<float4*>(dst + 8 * b) =
@@ -568,7 +574,7 @@ __global__ __launch_bounds__(256, 4) void kv_quant_kernel(KVArgs a) {
 }  // namespace
 
 hipError_t launch_kv_stats(const Problem& p, const void* k, const void* v, const Workspace& w, hipStream_t s) {
-  const dim3 grid(p.nkt, p.BH);
+  const dim3 grid(p.nkt, p.BHkv);
   if (p.d == 128)
     hipLaunchKernelGGL(kv_stats_kernel<128>, grid, dim3(256), 0, s, (const uint16_t*)k, (const uint16_t*)v,
                        w.kpart, w.vpart, w.vmaxp, w.vminp, p.M, p.nkt, p.fp16, p.smooth_v);
@@ -579,7 +585,7 @@ hipError_t launch_kv_stats(const Problem& p, const void* k, const void* v, const
 }
 
 hipError_t launch_kv_finalize(const Problem& p, const Workspace& w, hipStream_t s) {
-  hipLaunchKernelGGL(kv_finalize_kernel, dim3(p.BH, p.d / kFinCh), dim3(256), 0, s, w.kpart, w.vpart, w.vmaxp,
+  hipLaunchKernelGGL(kv_finalize_kernel, dim3(p.BHkv, p.d / kFinCh), dim3(256), 0, s, w.kpart, w.vpart, w.vmaxp,
                      w.vminp, w.kmean, w.vmean, w.dv, p.M, p.d, p.nkt, p.smooth_v);
   return hipGetLastError();
 }
@@ -620,8 +626,11 @@ hipError_t launch_kv_quant(const Problem& p, const void* k, const void* v, const
   a.nqb = p.nqb;
   a.causal = p.causal;
   a.coff = p.coff;
+  a.H = p.H;
+  a.Hkv = p.Hkv;
+  a.G = p.G;
   a.fp16 = p.fp16;
-  const dim3 grid(p.nkt, p.BH);
+  const dim3 grid(p.nkt, p.BHkv);
   if (p.d == 128) {
     if (p.mx) hipLaunchKernelGGL((kv_quant_kernel<128, true>), grid, dim3(256), 0, s, a);
     else hipLaunchKernelGGL((kv_quant_kernel<128, false>), grid, dim3(256), 0, s, a);

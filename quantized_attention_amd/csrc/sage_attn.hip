@@ -18,28 +18,28 @@ namespace sage {
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t workspace_layout(const Problem& p, size_t* sizes) {
-  const size_t BH = (size_t)p.BH, d = (size_t)p.d;
+  const size_t BH = (size_t)p.BH, BK = (size_t)p.BHkv, d = (size_t)p.d;
   const size_t qd = p.mx ? d / 2 : d;                // bytes per quantized row
   size_t s[kWsSlices];
   s[0] = BH * p.Np * qd;                             // qhat
-  s[1] = BH * p.Mp * qd;                             // khat
-  s[2] = BH * p.nkt * d * (p.mx ? kBK / 2 : kBK);    // vhat
+  s[1] = BK * p.Mp * qd;                             // khat
+  s[2] = BK * p.nkt * d * (p.mx ? kBK / 2 : kBK);    // vhat
   s[3] = p.mx ? 0 : BH * p.Np * sizeof(float);       // dq
-  s[4] = p.mx ? 0 : BH * p.nkt * 4 * sizeof(float);  // dk
-  s[5] = BH * d * sizeof(float);                     // dv
-  s[6] = BH * d * sizeof(float);                     // kmean
-  s[7] = BH * d * sizeof(float);                     // vmean
+  s[4] = p.mx ? 0 : BK * p.nkt * 4 * sizeof(float);  // dk
+  s[5] = BK * d * sizeof(float);                     // dv
+  s[6] = BK * d * sizeof(float);                     // kmean
+  s[7] = BK * d * sizeof(float);                     // vmean
   s[8] = BH * p.nqb * d * sizeof(float);             // qmean
   s[9] = BH * p.nqb * (size_t)p.Mp * sizeof(float);  // ds
-  s[10] = BH * p.nkt * d * sizeof(double);           // kpart
-  s[11] = BH * p.nkt * d * sizeof(double);           // vpart
-  s[12] = BH * p.nkt * d * sizeof(float);            // vmaxp
-  s[13] = BH * p.nkt * d * sizeof(float);            // vminp
+  s[10] = BK * p.nkt * d * sizeof(double);           // kpart
+  s[11] = BK * p.nkt * d * sizeof(double);           // vpart
+  s[12] = BK * p.nkt * d * sizeof(float);            // vmaxp
+  s[13] = BK * p.nkt * d * sizeof(float);            // vminp
   s[14] = BH * p.nqb * d * sizeof(uint16_t);         // qm_hi
   s[15] = BH * p.nqb * d * sizeof(uint16_t);         // qm_lo
   s[16] = p.mx ? BH * p.Np * (d / 32) : 0;           // qsc
-  s[17] = p.mx ? BH * p.nkt * 256 : 0;               // ksc
-  s[18] = p.mx ? BH * p.nkt * 256 : 0;               // vsc
+  s[17] = p.mx ? BK * p.nkt * 256 : 0;               // ksc
+  s[18] = p.mx ? BK * p.nkt * 256 : 0;               // vsc
   size_t tot = 0;
   for (int i = 0; i < kWsSlices; i++) {
     if (sizes) sizes[i] = s[i];
@@ -103,22 +103,24 @@ int device_check() {
   return ok[dev] ? SAGE_OK : SAGE_ERR_UNSUPPORTED;
 }
 
-int make_problem(int B, int H, int N, int M, int d, int causal, float sm_scale, unsigned variant,
+int make_problem(int B, int H, int Hkv, int N, int M, int d, int causal, float sm_scale, unsigned variant,
                  Problem* p) {
-  if (B < 1 || H < 1 || N < 1 || M < 1) return SAGE_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || Hkv < 1 || N < 1 || M < 1) return SAGE_ERR_INVALID_ARG;
+  if (H % Hkv) return SAGE_ERR_INVALID_ARG;
   if (variant & ~kKnownBits) return SAGE_ERR_INVALID_ARG;
-  if (d != 64 && d != 128) return SAGE_ERR_UNSUPPORTED;
   if (causal < 0 || causal > 2) return SAGE_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return SAGE_ERR_UNSUPPORTED;
   if (causal == 2 && N > M) return SAGE_ERR_UNSUPPORTED;  // some rows would see no key
   const double big = (double)B * H * (double)(N > M ? N : M) * d;
   if (big >= 1099511627776.0) return SAGE_ERR_INVALID_ARG;  // 2^40 elements
   if ((long long)B * H > (1LL << 30)) return SAGE_ERR_INVALID_ARG;
-  p->B = B; p->H = H; p->N = N; p->M = M; p->d = d;
+  p->B = B; p->H = H; p->Hkv = Hkv; p->G = H / Hkv; p->N = N; p->M = M; p->d = d;
   p->causal = causal;
   p->coff = causal == 2 ? M - N : 0;
   p->sm_scale = (sm_scale > 0.0f && std::isfinite(sm_scale)) ? sm_scale : 1.0f / std::sqrt((float)d);
   p->variant = variant;
   p->BH = B * H;
+  p->BHkv = B * Hkv;
   p->nqb = (N + kBQ - 1) / kBQ;
   p->nkt = (M + kBK - 1) / kBK;
   p->Np = p->nqb * kBQ;
@@ -127,9 +129,14 @@ int make_problem(int B, int H, int N, int M, int d, int causal, float sm_scale, 
   p->out_fp32 = (variant & SAGE_OUT_FP32) != 0;
   p->smooth_v = (variant & SAGE_SMOOTH_V) != 0;
   p->mx = (variant & SAGE_PATH_MXFP4) != 0;
-  // grid limits: y = B*H for every kernel, x = blocks/tiles
+  // grid limits: y = B*H (or B*Hkv) for the preprocessing kernels, x = blocks/tiles
   if (p->BH > 65535 || p->nkt > (1 << 30)) return SAGE_ERR_INVALID_ARG;
   return SAGE_OK;
+}
+
+int make_problem(const sage_attn_shape* sh, Problem* p) {
+  if (!sh) return SAGE_ERR_INVALID_ARG;
+  return make_problem(sh->B, sh->Hq, sh->Hkv, sh->N, sh->M, sh->d, sh->causal, sh->sm_scale, sh->variant, p);
 }
 
 bool aligned16(const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) == 0; }
@@ -175,33 +182,30 @@ using namespace sage;
 
 extern "C" {
 
-size_t sage_attn_workspace_bytes(int B, int H, int N, int M, int d, int causal, unsigned variant) {
+size_t sage_attn_workspace_bytes_ex(const sage_attn_shape* shape) {
   Problem p;
-  if (make_problem(B, H, N, M, d, causal, 0.0f, variant, &p) != SAGE_OK) return 0;
+  if (make_problem(shape, &p) != SAGE_OK) return 0;
   return workspace_layout(p, nullptr);
 }
 
-int sage_attn_fwd_ws(const void* q, const void* k, const void* v, void* out, int B, int H, int N,
-                     int M, int d, int causal, float sm_scale, unsigned variant, void* workspace,
-                     size_t ws_bytes, void* stream) {
-  Problem p;
-  int rc = make_problem(B, H, N, M, d, causal, sm_scale, variant, &p);
-  if (rc != SAGE_OK) return rc;
-  if ((rc = check_io(q, k, v, out)) != SAGE_OK) return rc;
-  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)) return SAGE_ERR_INVALID_ARG;
-  if (ws_bytes < workspace_layout(p, nullptr)) return SAGE_ERR_NO_MEMORY;
-  if ((rc = device_check()) != SAGE_OK) return rc;
-  return fwd_impl(q, k, v, out, p, workspace, (hipStream_t)stream);
+size_t sage_attn_workspace_bytes(int B, int H, int N, int M, int d, int causal, unsigned variant) {
+  const sage_attn_shape sh = {B, H, H, N, M, d, causal, 0.0f, variant};
+  return sage_attn_workspace_bytes_ex(&sh);
 }
 
-int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int M,
-                  int d, int causal, float sm_scale, unsigned variant, void* stream) {
+int sage_attn_fwd_ex(const sage_attn_shape* shape, const void* q, const void* k, const void* v, void* out,
+                     void* workspace, size_t ws_bytes, void* stream) {
   Problem p;
-  int rc = make_problem(B, H, N, M, d, causal, sm_scale, variant, &p);
+  int rc = make_problem(shape, &p);
   if (rc != SAGE_OK) return rc;
   if ((rc = check_io(q, k, v, out)) != SAGE_OK) return rc;
+  if (workspace) {
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return SAGE_ERR_INVALID_ARG;
+    if (ws_bytes < workspace_layout(p, nullptr)) return SAGE_ERR_NO_MEMORY;
+  }
   if ((rc = device_check()) != SAGE_OK) return rc;
   hipStream_t s = (hipStream_t)stream;
+  if (workspace) return fwd_impl(q, k, v, out, p, workspace, s);
   void* ws = nullptr;
   if (hipMallocAsync(&ws, workspace_layout(p, nullptr), s) != hipSuccess || !ws) {
     (void)hipGetLastError();
@@ -212,10 +216,24 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B,
   return rc;
 }
 
-int sage_attn_quantize(const void* q, const void* k, const void* v, int B, int H, int N, int M, int d,
-                       int causal, unsigned variant, const sage_quant_views* dst, void* stream) {
+int sage_attn_fwd_ws(const void* q, const void* k, const void* v, void* out, int B, int H, int N,
+                     int M, int d, int causal, float sm_scale, unsigned variant, void* workspace,
+                     size_t ws_bytes, void* stream) {
+  if (!workspace) return SAGE_ERR_INVALID_ARG;
+  const sage_attn_shape sh = {B, H, H, N, M, d, causal, sm_scale, variant};
+  return sage_attn_fwd_ex(&sh, q, k, v, out, workspace, ws_bytes, stream);
+}
+
+int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int H, int N, int M,
+                  int d, int causal, float sm_scale, unsigned variant, void* stream) {
+  const sage_attn_shape sh = {B, H, H, N, M, d, causal, sm_scale, variant};
+  return sage_attn_fwd_ex(&sh, q, k, v, out, nullptr, 0, stream);
+}
+
+int sage_attn_quantize_ex(const sage_attn_shape* shape, const void* q, const void* k, const void* v,
+                          const sage_quant_views* dst, void* stream) {
   Problem p;
-  int rc = make_problem(B, H, N, M, d, causal, 0.0f, variant, &p);
+  int rc = make_problem(shape, &p);
   if (rc != SAGE_OK) return rc;
   if (!dst || !q || !k || !v) return SAGE_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return SAGE_ERR_INVALID_ARG;
@@ -242,6 +260,12 @@ int sage_attn_quantize(const void* q, const void* k, const void* v, int B, int H
   }
   if (hipFreeAsync(ws, s) != hipSuccess && rc == SAGE_OK) rc = SAGE_ERR_LAUNCH;
   return rc;
+}
+
+int sage_attn_quantize(const void* q, const void* k, const void* v, int B, int H, int N, int M, int d,
+                       int causal, unsigned variant, const sage_quant_views* dst, void* stream) {
+  const sage_attn_shape sh = {B, H, H, N, M, d, causal, 0.0f, variant};
+  return sage_attn_quantize_ex(&sh, q, k, v, dst, stream);
 }
 
 void sage_attn_set_profile_events(void* start, void* stop) {

@@ -24,18 +24,20 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // Resolved problem: sizes, padded sizes and the variant bits.
 struct Problem {
   int B, H, N, M, d;
+  int Hkv, G;  // key/value heads; query head h reads key/value head h / G (G = H / Hkv)
   int causal;  // 0 none, 1 first query aligned with the first key, 2 last with the last
   int coff;    // causal: key t is visible to query r iff t <= r + coff (0, or M - N)
   float sm_scale;
   unsigned variant;
-  int BH, nqb, nkt, Np, Mp;
+  int BH, BHkv, nqb, nkt, Np, Mp;  // BH = B*H query heads, BHkv = B*Hkv key/value heads
   bool fp16, out_fp32, smooth_v;
   bool mx;  // SAGE_PATH_MXFP4
 };
 
 // Device workspace (all 256-byte aligned slices of one allocation).  Layouts of the
 // quantized tensors and scales are those sage_attn.h documents for the quantize views
-// (INT8/FP8, or E2M1 codes with E8M0 scales for the MX variant).
+// (INT8/FP8, or E2M1 codes with E8M0 scales for the MX variant).  The Q side (qhat, dq,
+// qmean, ds, qm_hi/lo, qsc) has one head per query head; the K/V side one per key/value head.
 struct Workspace {
   int8_t* qhat;     // [BH][Np][d]            (MX: [BH][Np][d/2] E2M1 pairs)
   int8_t* khat;     // [BH][Mp][d]            (MX: [BH][Mp][d/2])
@@ -72,6 +74,9 @@ __host__ __device__ inline int kperm(int h, int b) {
 
 // Scale group (0..3) of key t inside its 64-key tile: the lane half of the S^T accumulator
 // that holds it, within its 32-key half.
+// The key/value head (in [0, B*Hkv)) that query head bh (in [0, B*H)) reads.
+__host__ __device__ inline int kv_head(int bh, int H, int Hkv, int G) { return (bh / H) * Hkv + (bh % H) / G; }
+
 __host__ __device__ inline int kgroup(int t) {
   int u = t & 63;
   return 2 * (u >> 5) + ((u >> 2) & 1);

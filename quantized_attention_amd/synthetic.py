@@ -50,10 +50,15 @@ class Config:
     smooth_v: bool = False
     mxfp4: bool = False
     note: str = ""
+    Hkv: int = 0        # key/value heads (0: H); query head h reads key/value head h // (H // Hkv)
 
     @property
     def fp16(self) -> bool:
         return self.dtype == "fp16"
+
+    @property
+    def hkv(self) -> int:
+        return self.Hkv or self.H
 
     def with_shape(self, **kw) -> "Config":
         return replace(self, **kw)
@@ -81,6 +86,9 @@ CONFIGS = {
     "chunk4k_32k": Config("chunk4k_32k", 1, 32, 4096, 32768, 128, "bf16", 2,
                           Dist(k_off_std=4.0, k_spike=8.0, k_spike_channels=spike_channels(128)), 1006,
                           note="chunked prefill: the last 4096 queries over a 32768-token cache, causal"),
+    "prefill32k_gqa": Config("prefill32k_gqa", 1, 32, 32768, 32768, 128, "bf16", 1,
+                             Dist(k_off_std=4.0, k_spike=8.0, k_spike_channels=spike_channels(128)), 1007,
+                             Hkv=8, note="LLM prefill with grouped key/value heads (32 query heads, 8 key/value)"),
     "mxfp4_32k": Config("mxfp4_32k", 1, 24, 32768, 32768, 128, "bf16", False,
                         Dist(k_off_std=2.0, v_bias_std=0.5), 1005, mxfp4=True,
                         note="MXFP4 variant"),
@@ -137,20 +145,21 @@ def _head(cfg: Config, tensor: int, b: int, h: int, T: int) -> np.ndarray:
 
 
 def make_tensor(cfg: Config, tensor: int, heads=None) -> np.ndarray:
-    """One of Q, K, V as uint16 bits [B, H, T, d] (or [len(heads), T, d] for a subset of
-    flattened (b*H + h) head indices)."""
+    """One of Q, K, V as uint16 bits [B, H, T, d] (K and V: [B, Hkv, T, d]), or
+    [len(heads), T, d] for a subset of flattened (b*heads + h) head indices."""
     T = cfg.N if tensor == TENSOR_Q else cfg.M
-    idx = list(range(cfg.B * cfg.H)) if heads is None else list(heads)
+    H = cfg.H if tensor == TENSOR_Q else cfg.hkv
+    idx = list(range(cfg.B * H)) if heads is None else list(heads)
     out = np.empty((len(idx), T, cfg.d), np.uint16)
 
     def fill(i):  # each head has its own generator, so threads do not change the values
         bh = idx[i]
-        out[i] = _head(cfg, tensor, bh // cfg.H, bh % cfg.H, T)
+        out[i] = _head(cfg, tensor, bh // H, bh % H, T)
 
     with ThreadPoolExecutor(max_workers=min(8, len(idx))) as ex:
         list(ex.map(fill, range(len(idx))))
     if heads is None:
-        return out.reshape(cfg.B, cfg.H, T, cfg.d)
+        return out.reshape(cfg.B, H, T, cfg.d)
     return out
 
 

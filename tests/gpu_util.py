@@ -9,7 +9,7 @@ import torch
 
 import quantized_attention_amd as qa
 
-BQ, BK = qa.SAGE_BQ, qa.SAGE_BK
+BQ, BK_ = qa.SAGE_BQ, qa.SAGE_BK
 
 
 def to_dev(bits: np.ndarray, fp16: bool) -> torch.Tensor:
@@ -45,36 +45,38 @@ def fwd(q, k, v, fp16, causal, sm_scale, smooth_v=False, out_fp32=True, acc_valu
 
 
 def quantize(q, k, v, fp16, causal, smooth_v=False):
-    """Preprocessing through sage_attn_quantize, returned per head in natural layouts."""
+    """Preprocessing through sage_attn_quantize_ex, returned per head in natural layouts
+    (K/V-side tensors for the key/value heads, Q-side ones for the query heads)."""
     B, H, N, d = q.shape
-    M = k.shape[2]
-    BH = B * H
-    nqb, nkt = -(-N // BQ), -(-M // BK)
-    Np, Mp = nqb * BQ, nkt * BK
+    Hkv, M = k.shape[1], k.shape[2]
+    BH, BK = B * H, B * Hkv
+    nqb, nkt = -(-N // BQ), -(-M // BK_)
+    Np, Mp = nqb * BQ, nkt * BK_
     dev = torch.device("cuda")
     bufs = dict(
         q_hat=torch.empty((BH, Np, d), dtype=torch.int8, device=dev),
-        k_hat=torch.empty((BH, Mp, d), dtype=torch.int8, device=dev),
-        v_hat=torch.empty((BH, nkt, d, 64), dtype=torch.uint8, device=dev),
+        k_hat=torch.empty((BK, Mp, d), dtype=torch.int8, device=dev),
+        v_hat=torch.empty((BK, nkt, d, 64), dtype=torch.uint8, device=dev),
         dq=torch.empty((BH, Np), dtype=torch.float32, device=dev),
-        dk=torch.empty((BH, nkt, 4), dtype=torch.float32, device=dev),
-        dv=torch.empty((BH, d), dtype=torch.float32, device=dev),
-        k_mean=torch.empty((BH, d), dtype=torch.float32, device=dev),
-        v_mean=torch.empty((BH, d), dtype=torch.float32, device=dev),
+        dk=torch.empty((BK, nkt, 4), dtype=torch.float32, device=dev),
+        dv=torch.empty((BK, d), dtype=torch.float32, device=dev),
+        k_mean=torch.empty((BK, d), dtype=torch.float32, device=dev),
+        v_mean=torch.empty((BK, d), dtype=torch.float32, device=dev),
         q_mean=torch.empty((BH, nqb, d), dtype=torch.float32, device=dev),
         delta_s=torch.full((BH, nqb, Mp), float("nan"), dtype=torch.float32, device=dev),
     )
     views = qa.QuantViews(**{n: t.data_ptr() for n, t in bufs.items()})
     tq, tk, tv = to_dev(q, fp16), to_dev(k, fp16), to_dev(v, fp16)
     var = (qa.SAGE_IN_FP16 if fp16 else qa.SAGE_IN_BF16) | (qa.SAGE_SMOOTH_V if smooth_v else 0)
-    rc = qa.sage_attn_quantize(tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), B, H, N, M, d, causal, var,
-                               views, torch.cuda.current_stream().cuda_stream)
+    shape = qa.SageAttnShape(B, H, Hkv, N, M, d, int(causal), 0.0, var)
+    rc = qa.sage_attn_quantize_ex(shape, tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), views,
+                                  torch.cuda.current_stream().cuda_stream)
     assert rc == qa.SAGE_OK, qa.sage_attn_status_string(rc)
     torch.cuda.synchronize()
     h = {n: t.cpu().numpy() for n, t in bufs.items()}
-    # V^: [BH][nkt][d][64] (permuted keys) -> [BH][Mp][d]
+    # V^: [BK][nkt][d][64] (permuted keys) -> [BK][Mp][d]
     vt = h["v_hat"]
-    vnat = np.zeros((BH, Mp, d), np.uint8)
+    vnat = np.zeros((BK, Mp, d), np.uint8)
     for u in range(nkt):
         vnat[:, u * 64 + INV_PERM, :] = vt[:, u].transpose(0, 2, 1)
     h["v_nat"] = vnat
@@ -95,8 +97,8 @@ def quantize_mx(q, k, v, fp16, causal, smooth_v=False):
     B, H, N, d = q.shape
     M = k.shape[2]
     BH = B * H
-    nqb, nkt = -(-N // BQ), -(-M // BK)
-    Np, Mp = nqb * BQ, nkt * BK
+    nqb, nkt = -(-N // BQ), -(-M // BK_)
+    Np, Mp = nqb * BQ, nkt * BK_
     dev = torch.device("cuda")
     fill = dict(dtype=torch.uint8, device=dev)
     bufs = dict(

@@ -20,7 +20,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted(["sage_attn_fwd", "sage_attn_fwd_ws", "sage_attn_workspace_bytes",
                             "sage_attn_quantize", "sage_attn_set_profile_events",
-                            "sage_attn_status_string", "sage_attn_version"])
+                            "sage_attn_status_string", "sage_attn_version", "sage_attn_fwd_ex",
+                            "sage_attn_workspace_bytes_ex", "sage_attn_quantize_ex"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -64,6 +65,24 @@ def test_causal_modes_accept_uneven_lengths():
     for causal, N, M in [(1, 64, 200), (1, 200, 64), (2, 64, 200), (2, 200, 200)]:
         assert qa.sage_attn_workspace_bytes(1, 1, N, M, 64, causal, 0) > 0
     assert qa.sage_attn_workspace_bytes(1, 1, 200, 64, 64, 2, 0) == 0
+
+
+def test_extended_shape_checks():
+    S = qa.SageAttnShape
+    A = 256
+    assert qa.sage_attn_workspace_bytes_ex(None) == 0
+    assert qa.sage_attn_fwd_ex(None, A, A, A, A, None, 0, None) == qa.SAGE_ERR_INVALID_ARG
+    assert qa.sage_attn_fwd_ex(S(1, 8, 3, 64, 64, 64, 0, 0.0, 0), A, A, A, A, None, 0, None) == qa.SAGE_ERR_INVALID_ARG
+    assert qa.sage_attn_fwd_ex(S(1, 8, 0, 64, 64, 64, 0, 0.0, 0), A, A, A, A, None, 0, None) == qa.SAGE_ERR_INVALID_ARG
+    assert qa.sage_attn_workspace_bytes_ex(S(1, 8, 3, 64, 64, 64, 0, 0.0, 0)) == 0
+    # same shape, Hkv = Hq: the plain entry point's size; grouped heads shrink the K/V side only
+    full = qa.sage_attn_workspace_bytes_ex(S(1, 8, 8, 4096, 4096, 128, 0, 0.0, 0))
+    assert full == qa.sage_attn_workspace_bytes(1, 8, 4096, 4096, 128, 0, 0)
+    grouped = qa.sage_attn_workspace_bytes_ex(S(1, 8, 2, 4096, 4096, 128, 0, 0.0, 0))
+    assert 0 < grouped < full
+    ws = qa.sage_attn_workspace_bytes_ex(S(1, 8, 2, 64, 64, 64, 0, 0.0, 0))
+    assert qa.sage_attn_fwd_ex(S(1, 8, 2, 64, 64, 64, 0, 0.0, 0), A, A, A, A, A, ws - 1, None) == qa.SAGE_ERR_NO_MEMORY
+    assert qa.sage_attn_fwd_ex(S(1, 8, 2, 64, 64, 64, 0, 0.0, 0), A, A, A, A, A + 16, ws, None) == qa.SAGE_ERR_INVALID_ARG
 
 
 def test_workspace_grows_with_problem():
