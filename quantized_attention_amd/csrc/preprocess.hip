@@ -278,15 +278,8 @@ __global__ __launch_bounds__(256) void q_prep_kernel(const uint16_t* __restrict_
       }
       const float sc = (r < n) ? int8_scale(am) : 1.0f;
       if (cl == 0) dq[row] = sc;
-      uint32_t w0 = 0, w1 = 0;
-      if (r < n) {
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          w0 |= (uint32_t)(uint8_t)int8_code(g[e], sc) << (8 * e);
-          w1 |= (uint32_t)(uint8_t)int8_code(g[4 + e], sc) << (8 * e);
-        }
-      }
-      *reinterpret_cast<uint2*>(qhat + row * D + c0) = make_uint2(w0, w1);
+      const uint2 w = (r < n) ? int8_pack8_rcp(g, sc, __fdiv_rn(1.0f, sc)) : make_uint2(0u, 0u);
+      *reinterpret_cast<uint2*>(qhat + row * D + c0) = w;
     }
   }
 }
@@ -328,12 +321,15 @@ __global__ __launch_bounds__(256, MX ? 3 : 4) void kv_quant_kernel(KVArgs a) {
   uint16_t* sAl = sAh + kBK * RS;
   float (*sv)[D + 1] = reinterpret_cast<float (*)[D + 1]>(smem);
   __shared__ float gmax[4][4];
-  __shared__ float sdk[4];
+  __shared__ float sdk[4], srk[4];  // K group scales and their reciprocals
+  __shared__ float ssv[MX ? 1 : D], srv[MX ? 1 : D];  // dV and 1 / dV per channel (srv: d = 64)
   const int u = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int t0 = u * kBK, n = min(kBK, a.M - t0);
   const size_t in_base = ((size_t)bh * a.M + t0) * D;
   const float* km = a.kmean + (size_t)bh * D;
+  // dV of channel tid: loaded with the K/V chunks, inverted into srv once Delta S is done
+  const float dv_t = (!MX && tid < D) ? a.dv[(size_t)bh * D + tid] : 1.0f;
 
   // ---- all of this thread's K and V chunks in flight at once ----
   v4i kraw[CH], vraw[CH];
@@ -428,6 +424,7 @@ __global__ __launch_bounds__(256, MX ? 3 : 4) void kv_quant_kernel(KVArgs a) {
     for (int w = 1; w < 4; w++) m = gmax[tid][w] > m ? gmax[tid][w] : m;
     const float s = int8_scale(m);
     sdk[tid] = s;
+    srk[tid] = __fdiv_rn(1.0f, s);
     a.dk[((size_t)bh * a.nkt + u) * 4 + tid] = s;
   }
   __syncthreads();
@@ -438,16 +435,8 @@ __global__ __launch_bounds__(256, MX ? 3 : 4) void kv_quant_kernel(KVArgs a) {
 #pragma unroll
     for (int i = 0; i < CH; i++) {
       const int x = tid + 256 * i, row = x / (D / 8), c0 = (x % (D / 8)) * 8;
-      const float s = sdk[kgroup(row)];
-      uint32_t w0 = 0, w1 = 0;
-      if (row < n) {
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-          w0 |= (uint32_t)(uint8_t)int8_code(g[i][e], s) << (8 * e);
-          w1 |= (uint32_t)(uint8_t)int8_code(g[i][4 + e], s) << (8 * e);
-        }
-      }
-      *reinterpret_cast<uint2*>(kout + (size_t)row * D + c0) = make_uint2(w0, w1);
+      const uint2 w = (row < n) ? int8_pack8_rcp(g[i], sdk[kgroup(row)], srk[kgroup(row)]) : make_uint2(0u, 0u);
+      *reinterpret_cast<uint2*>(kout + (size_t)row * D + c0) = w;
     }
   }
   }
@@ -499,13 +488,17 @@ __global__ __launch_bounds__(256, MX ? 3 : 4) void kv_quant_kernel(KVArgs a) {
       }
     }
   }
-  __syncthreads();  // the split of gamma(K) is dead: its LDS now stages V'
+  if constexpr (!MX)
+    if (tid < D) {
+      ssv[tid] = dv_t;
+      if constexpr (D == 64) srv[tid] = __fdiv_rn(1.0f, dv_t);
+    }
+  __syncthreads();  // the split of gamma(K) is dead: its LDS now stages V'; ssv, srv are complete
 
-  // ---- V: V' / dV (IEEE division), saturated to the E4M3 range, staged in LDS ----
+  // ---- V: V' / dV (the IEEE quotient's E4M3 value), saturated to the E4M3 range, staged in LDS ----
   // (MX: V' itself; the block scale comes from the staged values)
   {
     const float* vm = a.vmean + (size_t)bh * D;
-    const float* sc = a.dv + (size_t)bh * D;
 #pragma unroll
     for (int i = 0; i < CH; i++) {
       const int x = tid + 256 * i, row = x / (D / 8), c0 = (x % (D / 8)) * 8;
@@ -513,13 +506,17 @@ __global__ __launch_bounds__(256, MX ? 3 : 4) void kv_quant_kernel(KVArgs a) {
       if (row < n) {
         widen8(vraw[i], a.fp16, w);
 #pragma unroll
-        for (int e = 0; e < 8; e++) {
-          if constexpr (MX) {
-            w[e] = w[e] - vm[c0 + e];
-          } else {
-            float y = __fdiv_rn(w[e] - vm[c0 + e], sc[c0 + e]);
-            y = y > 448.0f ? 448.0f : (y < -448.0f ? -448.0f : y);  // NaN stays NaN
-            w[e] = y;
+        for (int e = 0; e < 8; e++) w[e] = w[e] - vm[c0 + e];
+        if constexpr (!MX) {
+          if constexpr (D == 64) {
+            e4m3_in8_rcp(w, ssv + c0, srv + c0);
+          } else {  // d = 128: the product shortcut measured no faster here than the division
+#pragma unroll
+            for (int e = 0; e < 8; e++) {
+              const float y = __fdiv_rn(w[e], ssv[c0 + e]);
+              const float c = fminf(fmaxf(y, -448.0f), 448.0f);
+              w[e] = (y == y) ? c : y;  // NaN stays NaN
+            }
           }
         }
       } else {

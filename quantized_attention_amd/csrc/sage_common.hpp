@@ -134,6 +134,58 @@ __device__ inline int8_t int8_code(float x, float scale) {
   return static_cast<int8_t>(static_cast<int>(y));
 }
 
+// Eight INT8 codes int8_code(x[e], scale), packed little-endian into two words, from the
+// products with rcp = __fdiv_rn(1, scale).  |x / scale| <= 127.0001, and x * rcp is within
+// |x / scale| * 2^-23 < 1.6e-5 of it; the IEEE quotient is within half an ulp (< 4e-6) of it
+// too.  So the two round to the same integer unless a half-integer lies within 2e-5 of
+// x * rcp.  A chunk holding such an element (about 1 element in 5000), or a NaN, is coded
+// again with the division: one branch per chunk, not per element.
+__device__ inline uint2 int8_pack8_rcp(const float (&x)[8], float scale, float rcp) {
+  uint32_t w[2] = {0u, 0u};
+  uint32_t near = 0u;
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    const float q = x[e] * rcp, n = rintf(q);
+    near |= static_cast<uint32_t>(!(fabsf(q - n) < 0.4999f));
+    const float y = n > 127.0f ? 127.0f : (n < -127.0f ? -127.0f : n);
+    w[e >> 2] |= (uint32_t)(uint8_t)static_cast<int8_t>(static_cast<int>(y)) << (8 * (e & 3));
+  }
+  if (near) {
+    w[0] = w[1] = 0u;
+#pragma unroll
+    for (int e = 0; e < 8; e++) w[e >> 2] |= (uint32_t)(uint8_t)int8_code(x[e], scale) << (8 * (e & 3));
+  }
+  return make_uint2(w[0], w[1]);
+}
+
+// The E4M3 inputs x[e] / scale[e] (IEEE division) saturated to +-448, in place, from the
+// products with rcp[e] = __fdiv_rn(1, scale[e]).  A product is within 3 ulps of the quotient,
+// so the two round to the same E4M3 value unless the 20 low mantissa bits (the ones E4M3
+// drops from a normal value) lie within 16 ulps of the rounding midpoint 2^19, or the value
+// is below the E4M3 normal range (2^-6), or NaN.  A chunk holding such an element is divided
+// instead.
+__device__ inline void e4m3_in8_rcp(float (&x)[8], const float* scale, const float* rcp) {
+  float y[8];
+  uint32_t near = 0u;
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    y[e] = x[e] * rcp[e];
+    const uint32_t mag = __float_as_uint(y[e]) & 0x7FFFFFFFu;
+    // below 2^-6 (wraps) or NaN / Inf, as one unsigned range test; then the midpoint window
+    near |= static_cast<uint32_t>(mag - 0x3C800000u >= 0x7F800000u - 0x3C800000u);
+    near |= static_cast<uint32_t>((mag & 0xFFFFFu) - (0x80000u - 15u) < 31u);
+  }
+  if (near) {
+#pragma unroll
+    for (int e = 0; e < 8; e++) y[e] = __fdiv_rn(x[e], scale[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    const float c = fminf(fmaxf(y[e], -448.0f), 448.0f);
+    x[e] = (y[e] == y[e]) ? c : y[e];  // NaN stays NaN
+  }
+}
+
 __device__ inline float int8_scale(float amax) {
   float a = amax > 1e-8f ? amax : 1e-8f;
   return __fdiv_rn(a, 127.0f);
