@@ -32,6 +32,7 @@ PV_IDENTITY = 0x0100
 PV_E5M2 = 0x0200
 PV_INT8 = 0x0400
 MXFP4 = 0x1000
+QK_E4M3 = 0x2000  # Q^, K^ in E4M3 (scale amax / 448, same groups); khat, qhat then hold E4M3 codes
 
 
 def build(force: bool = True) -> str:
@@ -118,6 +119,8 @@ def preprocess_head(q, k, v, fp16: bool, flags: int = 0) -> dict:
                                                           "dv", "qhat", "dq", "qmean", "ds")])
     if rc != 0:
         raise ValueError("orc_preprocess_head rejected its arguments")
+    if flags & QK_E4M3:
+        o["qhat"], o["khat"] = o["qhat"].view(np.uint8), o["khat"].view(np.uint8)
     return o
 
 

@@ -260,6 +260,28 @@ static int8_t int8_code(float x, float scale) {
   return (int8_t)y;
 }
 
+/* The E4M3 knob for Q and K ([SA2] the missing FP8-QK ablation the review section names;
+ * "FP8 Quantization" fixes the E4M3 range the same way for V): scale = amax / 448 with the
+ * same groups as INT8, code = E4M3 of the FP32 quotient (round to nearest even, saturated).
+ * Readings: the amax floor 1e-8 and the FP32 division as for INT8. */
+static float e4m3_scale(float amax) {
+  float a = amax > 1e-8f ? amax : 1e-8f;
+  return a / 448.0f;
+}
+static float qk_scale(const head_t* h, float amax) {
+  return (h->flags & ORC_QK_E4M3) ? e4m3_scale(amax) : int8_scale(amax);
+}
+/* The stored code byte: INT8 two's complement, or the E4M3 code. */
+static int8_t qk_code(const head_t* h, float x, float scale) {
+  if (h->flags & ORC_QK_E4M3) return (int8_t)orc_e4m3_encode((double)(x / scale));
+  return int8_code(x, scale);
+}
+/* The value a stored code stands for, before its scale. */
+static double qk_value(const head_t* h, int8_t c) {
+  if (h->flags & ORC_QK_E4M3) return orc_e4m3_decode((uint8_t)c);
+  return (double)c;
+}
+
 /* Max of |x| that ignores NaN (a NaN element does not set the scale). */
 static float amax_upd(float m, float x) {
   float a = fabsf(x);
@@ -285,41 +307,41 @@ static int setup_k(head_t* h) {
     h->gkd[i] = (double)h->Kf[i] - (double)h->kmean[c];
   }
   if (h->flags & (ORC_QK_IDENTITY | ORC_MXFP4)) return 0;
-  /* Step 3: scale groups per the selected granularity, then the INT8 codes. */
+  /* Step 3: scale groups per the selected granularity, then the INT8 (or E4M3) codes. */
   unsigned g = h->flags;
   if (g & ORC_QK_PER_TENSOR) {
     float am = 0.0f;
     for (size_t i = 0; i < Md; i++) am = amax_upd(am, h->gk[i]);
-    float s = int8_scale(am);
+    float s = qk_scale(h, am);
     for (int t = 0; t < M; t++) h->dk_key[t] = s;
   } else if (g & ORC_QK_PER_TOKEN) {
     for (int t = 0; t < M; t++) {
       float am = 0.0f;
       for (int c = 0; c < d; c++) am = amax_upd(am, h->gk[(size_t)t * d + c]);
-      h->dk_key[t] = int8_scale(am);
+      h->dk_key[t] = qk_scale(h, am);
     }
   } else if (g & ORC_QK_PER_BLOCK) {
     for (int u = 0; u < h->nkt; u++) {
       float am = 0.0f;
       for (int t = u * ORC_BK; t < M && t < (u + 1) * ORC_BK; t++)
         for (int c = 0; c < d; c++) am = amax_upd(am, h->gk[(size_t)t * d + c]);
-      float s = int8_scale(am);
+      float s = qk_scale(h, am);
       for (int t = u * ORC_BK; t < M && t < (u + 1) * ORC_BK; t++) h->dk_key[t] = s;
     }
   } else { /* per-thread groups (default); a group with no valid key (ragged last tile)
-            * has amax 0 and so the floor scale 1e-8/127 */
+            * has amax 0 and so the floor scale 1e-8/127 (1e-8/448) */
     for (int u = 0; u < h->nkt; u++) {
       float am[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       for (int t = u * ORC_BK; t < M && t < (u + 1) * ORC_BK; t++) {
         int gr = orc_k_group(t);
         for (int c = 0; c < d; c++) am[gr] = amax_upd(am[gr], h->gk[(size_t)t * d + c]);
       }
-      for (int gr = 0; gr < 4; gr++) h->dk_grp[(size_t)u * 4 + gr] = int8_scale(am[gr]);
+      for (int gr = 0; gr < 4; gr++) h->dk_grp[(size_t)u * 4 + gr] = qk_scale(h, am[gr]);
       for (int t = u * ORC_BK; t < M && t < (u + 1) * ORC_BK; t++)
         h->dk_key[t] = h->dk_grp[(size_t)u * 4 + orc_k_group(t)];
     }
   }
-  for (size_t i = 0; i < Md; i++) h->khat[i] = int8_code(h->gk[i], h->dk_key[i / d]);
+  for (size_t i = 0; i < Md; i++) h->khat[i] = qk_code(h, h->gk[i], h->dk_key[i / d]);
   return 0;
 }
 
@@ -422,22 +444,22 @@ static int setup_q(head_t* h) {
   if (g & ORC_QK_PER_TENSOR) {
     float am = 0.0f;
     for (size_t x = 0; x < Nd; x++) am = amax_upd(am, h->gq[x]);
-    for (int r = 0; r < N; r++) h->dq[r] = int8_scale(am);
+    for (int r = 0; r < N; r++) h->dq[r] = qk_scale(h, am);
   } else if (g & ORC_QK_PER_BLOCK) {
     for (int i = 0; i < h->nqb; i++) {
       int r0 = i * ORC_BQ, r1 = r0 + ORC_BQ < N ? r0 + ORC_BQ : N;
       float am = 0.0f;
       for (size_t x = (size_t)r0 * d; x < (size_t)r1 * d; x++) am = amax_upd(am, h->gq[x]);
-      for (int r = r0; r < r1; r++) h->dq[r] = int8_scale(am);
+      for (int r = r0; r < r1; r++) h->dq[r] = qk_scale(h, am);
     }
   } else { /* per token: the default per-thread map and the per-token ablation agree */
     for (int r = 0; r < N; r++) {
       float am = 0.0f;
       for (int c = 0; c < d; c++) am = amax_upd(am, h->gq[(size_t)r * d + c]);
-      h->dq[r] = int8_scale(am);
+      h->dq[r] = qk_scale(h, am);
     }
   }
-  for (size_t x = 0; x < Nd; x++) h->qhat[x] = int8_code(h->gq[x], h->dq[x / d]);
+  for (size_t x = 0; x < Nd; x++) h->qhat[x] = qk_code(h, h->gq[x], h->dq[x / d]);
   return 0;
 }
 
@@ -519,6 +541,13 @@ static double qk_term(const head_t* h, int r, int t) {
       s += ldexp(p, h->qe[(size_t)r * nb + b] + h->ke[(size_t)t * nb + b]);
     }
     return s;
+  }
+  if (h->flags & ORC_QK_E4M3) {
+    /* exact in FP64: each product has at most 8 significant bits between 2^-18 and 2^18 */
+    double acc = 0.0;
+    for (int c = 0; c < d; c++)
+      acc += qk_value(h, h->qhat[(size_t)r * d + c]) * qk_value(h, h->khat[(size_t)t * d + c]);
+    return acc * (double)h->dq[r] * (double)h->dk_key[t];
   }
   long acc = 0; /* exact integer dot product (|acc| <= 127*127*128 < 2^31) */
   for (int c = 0; c < d; c++) acc += (long)h->qhat[(size_t)r * d + c] * (long)h->khat[(size_t)t * d + c];
@@ -625,6 +654,7 @@ int orc_forward_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, in
   if (!q || !k || !v || !out || nrows < 0) return -1;
   if (causal_offset(causal, N, M, &off)) return -1;
   if ((flags & ORC_MXFP4) && (flags & (ORC_QK_IDENTITY | ORC_PV_IDENTITY | ORC_PV_E5M2 | ORC_PV_INT8))) return -1;
+  if ((flags & ORC_QK_E4M3) && (flags & (ORC_QK_IDENTITY | ORC_MXFP4))) return -1;
   if (!rows && nrows != N) return -1;
   head_t h;
   if (head_setup(&h, q, k, v, in_fp16, N, M, d, flags)) { head_free(&h); return -1; }
@@ -673,7 +703,7 @@ int orc_preprocess_head(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                         uint8_t* vhat, float* dv, int8_t* qhat, float* dq,
                         float* qmean, double* ds) {
   if (!q || !k || !v) return -1;
-  if (flags & ~(ORC_SMOOTH_V | ORC_NO_SMOOTH_K | ORC_NO_SMOOTH_Q | ORC_QK_PER_BLOCK)) return -1;
+  if (flags & ~(ORC_SMOOTH_V | ORC_NO_SMOOTH_K | ORC_NO_SMOOTH_Q | ORC_QK_PER_BLOCK | ORC_QK_E4M3)) return -1;
   head_t h;
   if (head_setup(&h, q, k, v, in_fp16, N, M, d, flags)) { head_free(&h); return -1; }
   if (kmean) memcpy(kmean, h.kmean, sizeof(float) * d);

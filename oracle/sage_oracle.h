@@ -51,6 +51,7 @@ extern "C" {
 #define ORC_PV_E5M2       0x0200u /* ablation: P~ and V in E5M2 (static scale 1/57344, per-channel V)    */
 #define ORC_PV_INT8       0x0400u /* ablation: naive INT8 P~ (static 1/127) and per-channel INT8 V       */
 #define ORC_MXFP4         0x1000u /* MX variant: E2M1 values, E8M0 scale per 32 along the reduction dim  */
+#define ORC_QK_E4M3       0x2000u /* knob: Q^, K^ in E4M3 (scale amax/448, same groups) instead of INT8  */
 
 /* ---- scalar formats ---- */
 float   orc_bf16_to_f32(uint16_t h);
@@ -73,9 +74,9 @@ int orc_k_group(int t);
  *   vhat[M][d] (E4M3 codes), dv[d], qhat[N][d], dq[N], qmean[ceil(N/128)][d],
  *   ds[ceil(N/128)][M] (FP64 Delta S).
  * Only the default quantizers (per-thread INT8 QK, E4M3 PV) are written by this call;
- * flags may hold ORC_SMOOTH_V, ORC_NO_SMOOTH_K, ORC_NO_SMOOTH_Q and ORC_QK_PER_BLOCK (the
- * per-block ablation; dk then repeats the tile scale).  Returns 0, or -1 on a
- * bad argument. */
+ * flags may hold ORC_SMOOTH_V, ORC_NO_SMOOTH_K, ORC_NO_SMOOTH_Q, ORC_QK_PER_BLOCK (the
+ * per-block ablation; dk then repeats the tile scale) and ORC_QK_E4M3 (khat and qhat then
+ * hold E4M3 codes, dk and dq the E4M3 scales).  Returns 0, or -1 on a bad argument. */
 int orc_preprocess_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, int in_fp16,
                         int N, int M, int d, unsigned flags,
                         float* kmean, float* vmean, int8_t* khat, float* dk,
