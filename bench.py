@@ -73,7 +73,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill32k",
-                    help="one of: n4k, prefill32k, video17k, chunk4k_32k, prefill32k_gqa, mxfp4_32k (default prefill32k)")
+                    help="one of: n4k, prefill32k, video17k, chunk4k_32k, prefill32k_gqa, prefill32k_qkfp8, mxfp4_32k "
+                         "(default prefill32k)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -131,6 +132,7 @@ def cpu_baseline(cfg, budget_s: float) -> dict:
     rng = np.random.default_rng(7)
     s = 1.0 / math.sqrt(cfg.d)
     flags = (oracle.SMOOTH_V if cfg.smooth_v else 0) | (oracle.MXFP4 if cfg.mxfp4 else 0)
+    flags |= oracle.QK_E4M3 if cfg.qk_fp8 else 0
     ops, t_used, nrows, batch = 0.0, 0.0, 0, 8
     while t_used < budget_s:
         rows = np.sort(rng.integers(0, cfg.N, batch))
@@ -173,6 +175,8 @@ def main():
     var = (qa.SAGE_IN_FP16 if cfg.fp16 else qa.SAGE_IN_BF16) | (qa.SAGE_SMOOTH_V if cfg.smooth_v else 0)
     if cfg.mxfp4:
         var |= qa.SAGE_PATH_MXFP4
+    if cfg.qk_fp8:
+        var |= qa.SAGE_QK_FP8
     peak = PEAK_TOPS_FP4 if cfg.mxfp4 else PEAK_TOPS
     shape = qa.SageAttnShape(cfg.B, cfg.H, cfg.hkv, cfg.N, cfg.M, cfg.d, int(cfg.causal), 1.0 / math.sqrt(cfg.d), var)
     ws_bytes = qa.sage_attn_workspace_bytes_ex(shape)
@@ -215,11 +219,12 @@ def main():
     achieved = ops / (kms * 1e-3) / 1e12
     traffic = measured_traffic(cfg.name, cfg.mxfp4)
     dtype = ("e2m1 + e8m0 1x32 blocks (QK, PV), fp32 softmax/accumulate" if cfg.mxfp4
-             else "int8(QK)+fp8e4m3(PV), fp32 softmax/accumulate")
+             else ("fp8e4m3(QK)+fp8e4m3(PV)" if cfg.qk_fp8 else "int8(QK)+fp8e4m3(PV)")
+             + ", fp32 softmax/accumulate")
     shape = (f"N={cfg.N}" if cfg.N == cfg.M else f"N={cfg.N} M={cfg.M}") + f" d={cfg.d}" + (" causal" if cfg.causal else "")
     counting = ("4*N^2*d*H*B/time, causal counted as half" if cfg.N == cfg.M
                 else "4*d*(visible query-key pairs)*H*B/time")
-    metric = (f"attention TOPS ({counting}) at {shape}, % of INT8/FP8 MFMA peak"
+    metric = (f"attention TOPS ({counting}) at {shape}{', E4M3 QK' if cfg.qk_fp8 else ''}, % of INT8/FP8 MFMA peak"
               if not cfg.mxfp4 else
               f"attention TOPS ({counting}) at {shape}, MXFP4 variant, % of FP4 MFMA peak")
     line = {

@@ -63,6 +63,12 @@ typedef enum {
                                    of a token; P~: 32 keys of a query row; V': 32 tokens of a
                                    channel), on the block-scaled FP4 MFMA.  No 448 and no dV:
                                    the epilogue is O / l (+ V_m).  Means and Delta S as above. */
+#define SAGE_QK_FP8     0x0002u /* Q^ and K^ in FP8 E4M3 instead of INT8, with the same groups
+                                   (per-token Q, 4 groups / 64 keys K) and the scale
+                                   max(amax, 1e-8) / 448; Q K^T on the FP8 MFMA ("SageAttention2
+                                   Technical Report" summary, "Critical Assessment": the FP8-QK
+                                   form of SageAttention2-8b the pages do not evaluate).  Not
+                                   combinable with SAGE_PATH_MXFP4 (SAGE_ERR_INVALID_ARG). */
 #define SAGE_SMOOTH_V   0x0010u /* V' = V - mean_t(V) before quantization, O += V_m           */
 #define SAGE_IN_BF16    0x0000u
 #define SAGE_IN_FP16    0x0100u
@@ -116,6 +122,8 @@ int sage_attn_fwd_ws(const void* q, const void* k, const void* v, void* out,
  *   delta_s float [BH][nqb][Mp] Delta S_i[t] = q_i . gamma(K)[t] (FP32); with causal only
  *           the 64-key tiles that block i attends to (t < 128*(i+1) + (M - N for causal = 2))
  *           are written
+ * With SAGE_QK_FP8, q_hat and k_hat hold OCP E4M3 codes (round to nearest even of the FP32
+ * quotient, saturated to +-448) in the same layouts, and dq, dk the scales amax / 448.
  * With SAGE_PATH_MXFP4 the quantized tensors are E2M1 codes (sign << 3 | magnitude index
  * into {0, 0.5, 1, 1.5, 2, 3, 4, 6}), two per byte, the lower-indexed element in the low
  * nibble, and the scales are E8M0 bytes (2^(byte - 127)):

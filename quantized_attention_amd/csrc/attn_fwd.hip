@@ -79,28 +79,46 @@ struct AttnArgs {
   int xcd_map;      // 1: heads grouped per XCD
 };
 
-// S^T = K^ Q^T of one 64-key tile on the INT8 MFMA (exact INT32): two 32-key halves.
-template <int D>
+// Score accumulator of one 32-key half: exact INT32 (INT8 Q^, K^) or FP32 (E4M3 Q^, K^).
+template <bool QF8>
+using acc_t = std::conditional_t<QF8, v16f, v16i>;
+
+// S^T = K^ Q^T of one 64-key tile: two 32-key halves.  INT8: four 32-channel MFMAs
+// (v_mfma_i32_32x32x32_i8).  E4M3 (QF8): two 64-channel MFMAs (v_mfma_f32_32x32x64_f8f6f4)
+// over the same register bytes -- the A and B operands share one lane/byte -> k mapping, so
+// pairing the K^ and Q^ chunks of two INT8 steps sums the same 64 channels.
+template <int D, bool QF8>
 __device__ __forceinline__ void qk_tile(const int8_t* __restrict__ sK, const v4i (&qf)[D / 32], int h, int col,
-                                        v16i (&acc)[2]) {
+                                        acc_t<QF8> (&acc)[2]) {
   constexpr int NKS = D / 32;
 #pragma unroll
   for (int T = 0; T < 2; T++) {
 #pragma unroll
     for (int r = 0; r < 16; r++) acc[T][r] = 0;
+    if constexpr (QF8) {
 #pragma unroll
-    for (int s = 0; s < NKS; s++) {
-      const v4i kf = *reinterpret_cast<const v4i*>(&sK[Tiles<D>::koff(32 * T + col, 2 * s + h)]);
-      acc[T] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[s], acc[T], 0, 0, 0);
+      for (int s = 0; s < NKS; s += 2) {
+        const v4i k0 = *reinterpret_cast<const v4i*>(&sK[Tiles<D>::koff(32 * T + col, 2 * s + h)]);
+        const v4i k1 = *reinterpret_cast<const v4i*>(&sK[Tiles<D>::koff(32 * T + col, 2 * s + 2 + h)]);
+        const v8i kf = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
+        const v8i qq = {qf[s][0], qf[s][1], qf[s][2], qf[s][3], qf[s + 1][0], qf[s + 1][1], qf[s + 1][2], qf[s + 1][3]};
+        acc[T] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qq, acc[T], 0, 0, 0, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < NKS; s++) {
+        const v4i kf = *reinterpret_cast<const v4i*>(&sK[Tiles<D>::koff(32 * T + col, 2 * s + h)]);
+        acc[T] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[s], acc[T], 0, 0, 0);
+      }
     }
   }
 }
 
-// The rest of one tile for one wave, from its INT32 scores: dequantize, online softmax,
-// P^ V^ into O.  `masked` (wave-uniform) selects the causal / ragged-tail mask; interior
-// tiles skip it.
-template <int D, bool CAUSAL, bool ACC_VALU>
-__device__ __forceinline__ void softmax_pv(const v16i (&acc)[2], const uint8_t* __restrict__ sV,
+// The rest of one tile for one wave, from its INT32 (or FP32) scores: dequantize, online
+// softmax, P^ V^ into O.  `masked` (wave-uniform) selects the causal / ragged-tail mask;
+// interior tiles skip it.
+template <int D, bool CAUSAL, bool ACC_VALU, typename ACC>
+__device__ __forceinline__ void softmax_pv(const ACC (&acc)[2], const uint8_t* __restrict__ sV,
                                            const float* __restrict__ sDS, const float* __restrict__ sDK,
                                            float dql, int h, int col, int key0, int qrow, int M, bool masked,
                                            v16f (&O)[D / 32], float& m_run, float& l_run) {
@@ -190,7 +208,7 @@ __device__ __forceinline__ void softmax_pv(const v16i (&acc)[2], const uint8_t* 
 // PIPE: the QK MFMAs of tile j+1 are issued before the softmax of tile j (one wave overlaps
 // its own matrix and vector work); otherwise the waves of other work-groups provide the
 // overlap.  NB: LDS ring slots.  OCC: work-groups per CU the register budget is sized for.
-template <int D, bool CAUSAL, int OUT, bool ACC_VALU, bool PIPE, int NB, int OCC>  // OUT: 0 bf16, 1 fp16, 2 fp32
+template <int D, bool CAUSAL, int OUT, bool ACC_VALU, bool QF8, bool PIPE, int NB, int OCC>  // OUT: 0 bf16, 1 fp16, 2 fp32
 __global__ __launch_bounds__(256, OCC) void attn_fwd_kernel(AttnArgs a) {
   using TL = Tiles<D>;
   constexpr int NKS = D / 32;
@@ -293,14 +311,14 @@ __global__ __launch_bounds__(256, OCC) void attn_fwd_kernel(AttnArgs a) {
     // tile j, so the matrix core works on j+1 while the VALU works on j.  Tile j+3 streams into
     // the ring slot last read in the previous iteration; two tiles are always in flight, and one
     // barrier per tile publishes the next.
-    auto body = [&](int j, v16i (&cur)[2], v16i (&nxt)[2]) {
+    auto body = [&](int j, acc_t<QF8> (&cur)[2], acc_t<QF8> (&nxt)[2]) {
       if (j + 3 < jend) dma(j + 3, (j + 3) % NB);
-      if (j + 1 < jend && !skip_t(j + 1)) qk_tile<D>(sK[(j + 1) % NB], qf, h, col, nxt);
+      if (j + 1 < jend && !skip_t(j + 1)) qk_tile<D, QF8>(sK[(j + 1) % NB], qf, h, col, nxt);
       if (!skip_t(j)) {
         const int key0 = j * kBK;
         const bool masked = (CAUSAL && key0 + kBK - 1 > wq0 + a.coff) || (key0 + kBK > a.M);
         const int b = j % NB;
-        softmax_pv<D, CAUSAL, ACC_VALU>(cur, sV[b], sDS[b], sDK[b], dql, h, col, key0, qrow + a.coff, a.M, masked, O,
+        softmax_pv<D, CAUSAL, ACC_VALU, acc_t<QF8>>(cur, sV[b], sDS[b], sDK[b], dql, h, col, key0, qrow + a.coff, a.M, masked, O,
                                         m_run, l_run);
       }
       publish(j + 3 < jend);  // tile j+2 must be complete; j+3 may still be arriving
@@ -310,8 +328,8 @@ __global__ __launch_bounds__(256, OCC) void attn_fwd_kernel(AttnArgs a) {
     if (jend > 1) dma(1, 1);
     if (jend > 2) dma(2, 2);
     publish(jend > 2);  // tiles 0 and 1 landed; tile 2 may be arriving
-    v16i accA[2], accB[2];
-    qk_tile<D>(sK[0], qf, h, col, accA);  // tile 0 is never masked away
+    acc_t<QF8> accA[2], accB[2];
+    qk_tile<D, QF8>(sK[0], qf, h, col, accA);  // tile 0 is never masked away
     for (int j = 0; j < jend; j += 2) {
       body(j, accA, accB);
       if (j + 1 < jend) body(j + 1, accB, accA);
@@ -340,9 +358,9 @@ __global__ __launch_bounds__(256, OCC) void attn_fwd_kernel(AttnArgs a) {
       if (!skip_t(j)) {
         const int key0 = j * kBK;
         const bool masked = (CAUSAL && key0 + kBK - 1 > wq0 + a.coff) || (key0 + kBK > a.M);
-        v16i acc[2];
-        qk_tile<D>(sK[b], qf, h, col, acc);
-        softmax_pv<D, CAUSAL, ACC_VALU>(acc, sV[b], sDS[b], sDK[b], dql, h, col, key0, qrow + a.coff, a.M, masked, O,
+        acc_t<QF8> acc[2];
+        qk_tile<D, QF8>(sK[b], qf, h, col, acc);
+        softmax_pv<D, CAUSAL, ACC_VALU, acc_t<QF8>>(acc, sV[b], sDS[b], sDK[b], dql, h, col, key0, qrow + a.coff, a.M, masked, O,
                                         m_run, l_run);
       }
       publish_n(min(NB - 2, jend - j - 2));
@@ -395,22 +413,30 @@ constexpr int occ_for() {
   return kPipe ? 2 : (SAGE_ATTN_OCC ? SAGE_ATTN_OCC : (D == 64 ? 4 : 3));
 }
 
-template <int D, bool CAUSAL, bool ACC_VALU>
+template <int D, bool CAUSAL, bool ACC_VALU, bool QF8>
 hipError_t launch_d(const Problem& p, const AttnArgs& a, hipStream_t s) {
   dim3 grid(p.nqb * p.BH);
   const int out = p.out_fp32 ? 2 : (p.fp16 ? 1 : 0);
   if (out == 2)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, 2, ACC_VALU, kPipe, kRing, occ_for<D>()>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, 2, ACC_VALU, QF8, kPipe, kRing, occ_for<D>()>), grid, dim3(256), 0, s,
+                       a);
   else if (out == 1)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, 1, ACC_VALU, kPipe, kRing, occ_for<D>()>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, 1, ACC_VALU, QF8, kPipe, kRing, occ_for<D>()>), grid, dim3(256), 0, s,
+                       a);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, 0, ACC_VALU, kPipe, kRing, occ_for<D>()>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, 0, ACC_VALU, QF8, kPipe, kRing, occ_for<D>()>), grid, dim3(256), 0, s,
+                       a);
   return hipGetLastError();
 }
 
-template <int D, bool ACC_VALU>
+template <int D, bool ACC_VALU, bool QF8>
 hipError_t launch_c(const Problem& p, const AttnArgs& a, hipStream_t s) {
-  return p.causal ? launch_d<D, true, ACC_VALU>(p, a, s) : launch_d<D, false, ACC_VALU>(p, a, s);
+  return p.causal ? launch_d<D, true, ACC_VALU, QF8>(p, a, s) : launch_d<D, false, ACC_VALU, QF8>(p, a, s);
+}
+
+template <int D, bool ACC_VALU>
+hipError_t launch_q(const Problem& p, const AttnArgs& a, hipStream_t s) {
+  return p.qf8 ? launch_c<D, ACC_VALU, true>(p, a, s) : launch_c<D, ACC_VALU, false>(p, a, s);
 }
 
 }  // namespace
@@ -425,8 +451,8 @@ hipError_t launch_attn_fwd(const Problem& p, const Workspace& w, void* out, hipS
   a.H = p.H; a.Hkv = p.Hkv; a.G = p.G;
   a.xcd_map = (p.BH % (kXCD * p.G) == 0) ? 1 : 0;
   const bool valu = (p.variant & SAGE_ACC_VALU) != 0;
-  if (p.d == 128) return valu ? launch_c<128, true>(p, a, s) : launch_c<128, false>(p, a, s);
-  return valu ? launch_c<64, true>(p, a, s) : launch_c<64, false>(p, a, s);
+  if (p.d == 128) return valu ? launch_q<128, true>(p, a, s) : launch_q<128, false>(p, a, s);
+  return valu ? launch_q<64, true>(p, a, s) : launch_q<64, false>(p, a, s);
 }
 
 }  // namespace sage

@@ -188,8 +188,8 @@ __global__ __launch_bounds__(256) void kv_finalize_kernel(const double* __restri
   }
 }
 
-// ---- Q: block mean (and its bf16 head/tail), gamma(Q), per-token scale, INT8 codes ----
-template <int D, bool MX>
+// ---- Q: block mean (and its bf16 head/tail), gamma(Q), per-token scale, INT8 (F8: E4M3) codes ----
+template <int D, bool MX, bool F8>
 __global__ __launch_bounds__(256) void q_prep_kernel(const uint16_t* __restrict__ Q,
                                                      int8_t* __restrict__ qhat, float* __restrict__ dq,
                                                      uint8_t* __restrict__ qsc,
@@ -276,9 +276,10 @@ __global__ __launch_bounds__(256) void q_prep_kernel(const uint16_t* __restrict_
         const float o = __shfl_xor(am, off);
         am = o > am ? o : am;
       }
-      const float sc = (r < n) ? int8_scale(am) : 1.0f;
+      const float sc = (r < n) ? (F8 ? e4m3_scale(am) : int8_scale(am)) : 1.0f;
       if (cl == 0) dq[row] = sc;
-      const uint2 w = (r < n) ? int8_pack8_rcp(g, sc, __fdiv_rn(1.0f, sc)) : make_uint2(0u, 0u);
+      uint2 w = make_uint2(0u, 0u);
+      if (r < n) w = F8 ? e4m3_pack8_rcp(g, sc, __fdiv_rn(1.0f, sc)) : int8_pack8_rcp(g, sc, __fdiv_rn(1.0f, sc));
       *reinterpret_cast<uint2*>(qhat + row * D + c0) = w;
     }
   }
@@ -308,7 +309,7 @@ struct KVArgs {
 // Delta S against every query block of every query head that reads this key/value head;
 // V' / dV -> E4M3, transposed in the P-fragment key order.  MX: gamma(K) and V' in E2M1
 // with an E8M0 scale per 32 channels of a key / per 32 tokens of a channel ----
-template <int D, bool MX>
+template <int D, bool MX, bool F8>
 __global__ __launch_bounds__(256, MX ? 3 : 4) void kv_quant_kernel(KVArgs a) {
   constexpr int RS = D + 8;                 // bf16 split of gamma(K), 16-byte aligned rows
   constexpr int CH = kBK * D / 8 / 256;     // 8-element chunks per thread
@@ -422,7 +423,7 @@ __global__ __launch_bounds__(256, MX ? 3 : 4) void kv_quant_kernel(KVArgs a) {
   if (tid < 4) {
     float m = gmax[tid][0];
     for (int w = 1; w < 4; w++) m = gmax[tid][w] > m ? gmax[tid][w] : m;
-    const float s = int8_scale(m);
+    const float s = F8 ? e4m3_scale(m) : int8_scale(m);
     sdk[tid] = s;
     srk[tid] = __fdiv_rn(1.0f, s);
     a.dk[((size_t)bh * a.nkt + u) * 4 + tid] = s;
@@ -435,7 +436,10 @@ __global__ __launch_bounds__(256, MX ? 3 : 4) void kv_quant_kernel(KVArgs a) {
 #pragma unroll
     for (int i = 0; i < CH; i++) {
       const int x = tid + 256 * i, row = x / (D / 8), c0 = (x % (D / 8)) * 8;
-      const uint2 w = (row < n) ? int8_pack8_rcp(g[i], sdk[kgroup(row)], srk[kgroup(row)]) : make_uint2(0u, 0u);
+      uint2 w = make_uint2(0u, 0u);
+      if (row < n)
+        w = F8 ? e4m3_pack8_rcp(g[i], sdk[kgroup(row)], srk[kgroup(row)])
+               : int8_pack8_rcp(g[i], sdk[kgroup(row)], srk[kgroup(row)]);
       *reinterpret_cast<uint2*>(kout + (size_t)row * D + c0) = w;
     }
   }
@@ -594,9 +598,11 @@ hipError_t launch_q_prep(const Problem& p, const void* q, const Workspace& w, hi
                        w.qm_lo, p.N, p.Np, p.nqb, p.fp16);
   };
   if (p.d == 128)
-    p.mx ? go(q_prep_kernel<128, true>) : go(q_prep_kernel<128, false>);
+    p.mx ? go(q_prep_kernel<128, true, false>)
+         : (p.qf8 ? go(q_prep_kernel<128, false, true>) : go(q_prep_kernel<128, false, false>));
   else
-    p.mx ? go(q_prep_kernel<64, true>) : go(q_prep_kernel<64, false>);
+    p.mx ? go(q_prep_kernel<64, true, false>)
+         : (p.qf8 ? go(q_prep_kernel<64, false, true>) : go(q_prep_kernel<64, false, false>));
   return hipGetLastError();
 }
 
@@ -629,11 +635,13 @@ hipError_t launch_kv_quant(const Problem& p, const void* k, const void* v, const
   a.fp16 = p.fp16;
   const dim3 grid(p.nkt, p.BHkv);
   if (p.d == 128) {
-    if (p.mx) hipLaunchKernelGGL((kv_quant_kernel<128, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((kv_quant_kernel<128, false>), grid, dim3(256), 0, s, a);
+    if (p.mx) hipLaunchKernelGGL((kv_quant_kernel<128, true, false>), grid, dim3(256), 0, s, a);
+    else if (p.qf8) hipLaunchKernelGGL((kv_quant_kernel<128, false, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((kv_quant_kernel<128, false, false>), grid, dim3(256), 0, s, a);
   } else {
-    if (p.mx) hipLaunchKernelGGL((kv_quant_kernel<64, true>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((kv_quant_kernel<64, false>), grid, dim3(256), 0, s, a);
+    if (p.mx) hipLaunchKernelGGL((kv_quant_kernel<64, true, false>), grid, dim3(256), 0, s, a);
+    else if (p.qf8) hipLaunchKernelGGL((kv_quant_kernel<64, false, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((kv_quant_kernel<64, false, false>), grid, dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

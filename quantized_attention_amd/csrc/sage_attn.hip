@@ -80,7 +80,8 @@ void carve_workspace(const Problem& p, void* base, Workspace* w) {
 
 namespace {
 
-constexpr unsigned kKnownBits = SAGE_PATH_MXFP4 | SAGE_SMOOTH_V | SAGE_IN_FP16 | SAGE_OUT_FP32 | SAGE_ACC_VALU;
+constexpr unsigned kKnownBits =
+    SAGE_PATH_MXFP4 | SAGE_QK_FP8 | SAGE_SMOOTH_V | SAGE_IN_FP16 | SAGE_OUT_FP32 | SAGE_ACC_VALU;
 
 // Per-device "is gfx950" cache, filled once per device under a mutex.
 int device_check() {
@@ -108,6 +109,7 @@ int make_problem(int B, int H, int Hkv, int N, int M, int d, int causal, float s
   if (B < 1 || H < 1 || Hkv < 1 || N < 1 || M < 1) return SAGE_ERR_INVALID_ARG;
   if (H % Hkv) return SAGE_ERR_INVALID_ARG;
   if (variant & ~kKnownBits) return SAGE_ERR_INVALID_ARG;
+  if ((variant & SAGE_PATH_MXFP4) && (variant & SAGE_QK_FP8)) return SAGE_ERR_INVALID_ARG;
   if (causal < 0 || causal > 2) return SAGE_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return SAGE_ERR_UNSUPPORTED;
   if (causal == 2 && N > M) return SAGE_ERR_UNSUPPORTED;  // some rows would see no key
@@ -129,6 +131,7 @@ int make_problem(int B, int H, int Hkv, int N, int M, int d, int causal, float s
   p->out_fp32 = (variant & SAGE_OUT_FP32) != 0;
   p->smooth_v = (variant & SAGE_SMOOTH_V) != 0;
   p->mx = (variant & SAGE_PATH_MXFP4) != 0;
+  p->qf8 = (variant & SAGE_QK_FP8) != 0;
   // grid limits: y = B*H (or B*Hkv) for the preprocessing kernels, x = blocks/tiles
   if (p->BH > 65535 || p->nkt > (1 << 30)) return SAGE_ERR_INVALID_ARG;
   return SAGE_OK;

@@ -32,6 +32,7 @@ struct Problem {
   int BH, BHkv, nqb, nkt, Np, Mp;  // BH = B*H query heads, BHkv = B*Hkv key/value heads
   bool fp16, out_fp32, smooth_v;
   bool mx;  // SAGE_PATH_MXFP4
+  bool qf8;  // SAGE_QK_FP8
 };
 
 // Device workspace (all 256-byte aligned slices of one allocation).  Layouts of the
@@ -189,6 +190,31 @@ __device__ inline void e4m3_in8_rcp(float (&x)[8], const float* scale, const flo
 __device__ inline float int8_scale(float amax) {
   float a = amax > 1e-8f ? amax : 1e-8f;
   return __fdiv_rn(a, 127.0f);
+}
+
+// Scale of the E4M3 form of Q^ / K^ (SAGE_QK_FP8): amax / 448 with the INT8 path's floor.
+__device__ inline float e4m3_scale(float amax) {
+  float a = amax > 1e-8f ? amax : 1e-8f;
+  return __fdiv_rn(a, 448.0f);
+}
+
+// Eight E4M3 codes of x[e] / scale (the IEEE quotient, saturated to +-448), packed
+// little-endian into two words, through the reciprocal product with its exact fallback.
+__device__ inline uint2 e4m3_pack8_rcp(const float (&x)[8], float scale, float rcp) {
+  float y[8];
+  float sc[8], rc[8];
+#pragma unroll
+  for (int e = 0; e < 8; e++) {
+    y[e] = x[e];
+    sc[e] = scale;
+    rc[e] = rcp;
+  }
+  e4m3_in8_rcp(y, sc, rc);
+  uint32_t w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+  w0 = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], w0, true);
+  uint32_t w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[4], y[5], 0, false);
+  w1 = __builtin_amdgcn_cvt_pk_fp8_f32(y[6], y[7], w1, true);
+  return make_uint2(w0, w1);
 }
 
 // bf16 bits of an FP32 value, round to nearest even (hardware conversion).

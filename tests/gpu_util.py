@@ -33,18 +33,19 @@ def doc_vperm_mx(h: int, j: int) -> int:
 INV_PERM_MX = np.array([doc_vperm_mx(p // 32, p % 32) for p in range(64)])
 
 
-def fwd(q, k, v, fp16, causal, sm_scale, smooth_v=False, out_fp32=True, acc_valu=False, mxfp4=False):
+def fwd(q, k, v, fp16, causal, sm_scale, smooth_v=False, out_fp32=True, acc_valu=False, mxfp4=False,
+        qk_fp8=False):
     """q, k, v: uint16 bits [B, H, T, d] on the host; returns the output as a device tensor."""
     B, H, N, d = q.shape
     M = k.shape[2]
     tq, tk, tv = to_dev(q, fp16), to_dev(k, fp16), to_dev(v, fp16)
     out = qa.sage_attn(tq, tk, tv, causal=causal, sm_scale=sm_scale, smooth_v=smooth_v, out_fp32=out_fp32,
-                       acc_valu=acc_valu, mxfp4=mxfp4)
+                       acc_valu=acc_valu, mxfp4=mxfp4, qk_fp8=qk_fp8)
     torch.cuda.synchronize()
     return out
 
 
-def quantize(q, k, v, fp16, causal, smooth_v=False):
+def quantize(q, k, v, fp16, causal, smooth_v=False, qk_fp8=False):
     """Preprocessing through sage_attn_quantize_ex, returned per head in natural layouts
     (K/V-side tensors for the key/value heads, Q-side ones for the query heads)."""
     B, H, N, d = q.shape
@@ -68,6 +69,7 @@ def quantize(q, k, v, fp16, causal, smooth_v=False):
     views = qa.QuantViews(**{n: t.data_ptr() for n, t in bufs.items()})
     tq, tk, tv = to_dev(q, fp16), to_dev(k, fp16), to_dev(v, fp16)
     var = (qa.SAGE_IN_FP16 if fp16 else qa.SAGE_IN_BF16) | (qa.SAGE_SMOOTH_V if smooth_v else 0)
+    var |= qa.SAGE_QK_FP8 if qk_fp8 else 0
     shape = qa.SageAttnShape(B, H, Hkv, N, M, d, int(causal), 0.0, var)
     rc = qa.sage_attn_quantize_ex(shape, tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), views,
                                   torch.cuda.current_stream().cuda_stream)

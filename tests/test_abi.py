@@ -51,6 +51,12 @@ def test_argument_errors_are_reported_before_any_device_work():
     assert f(A, A, A, A, 1, 1, 64, 64, 64, 3, 0.0, 0, 0) == qa.SAGE_ERR_INVALID_ARG  # causal mode 3
     assert f(A, A, A, A, 1, 1, 64, 64, 64, -1, 0.0, 0, 0) == qa.SAGE_ERR_INVALID_ARG
     assert f(A, A, A, A, 1, 1, 64, 64, 64, 0, 0.0, 0x8, 0) == qa.SAGE_ERR_INVALID_ARG  # unknown bit
+    both = qa.SAGE_PATH_MXFP4 | qa.SAGE_QK_FP8  # two Q K^T formats at once
+    assert f(A, A, A, A, 1, 1, 64, 64, 64, 0, 0.0, both, 0) == qa.SAGE_ERR_INVALID_ARG
+    assert qa.sage_attn_workspace_bytes(1, 1, 64, 64, 64, 0, both) == 0
+    # E4M3 Q^ / K^ take the INT8 layouts: the same workspace
+    assert qa.sage_attn_workspace_bytes(1, 4, 300, 500, 128, 1, qa.SAGE_QK_FP8) == \
+        qa.sage_attn_workspace_bytes(1, 4, 300, 500, 128, 1, 0)
     ws = qa.sage_attn_workspace_bytes(1, 1, 64, 64, 64, 0, 0)
     assert ws > 0
     assert qa.sage_attn_fwd_ws(A, A, A, A, 1, 1, 64, 64, 64, 0, 0.0, 0, A, ws - 1, 0) == qa.SAGE_ERR_NO_MEMORY
