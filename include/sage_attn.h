@@ -206,6 +206,49 @@ int sage_attn_quantize_ex(const sage_attn_shape* shape, const void* q, const voi
                           const sage_quant_views* dst, void* stream);
 
 /*
+ * Variable-length batches ("Handling Varying Sequence Lengths with VarLen Kernels": a ragged
+ * batch of `batch` sequences concatenated along the token axis, no padding, described by
+ * cumulative offsets and the bounds on the lengths).
+ *
+ * Layouts: q and out [total_q][Hq][d], k and v [total_k][Hkv][d] (token-major, heads
+ * interleaved), contiguous, 16-byte aligned, the same dtypes as sage_attn_fwd.  Sequence b owns
+ * query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key/value rows cu_seqlens_k[b] ..
+ * cu_seqlens_k[b+1]-1.  Every sequence is computed exactly as sage_attn_fwd_ex computes it on
+ * its own (B = 1, N and M its lengths): its own K mean, V_m, scales, 128-query blocks from its
+ * first query, Delta S and causal alignment (causal = 2 aligns its last query with its last
+ * key).  Rows of a sequence that see no key (a sequence without keys, or causal = 2 with more
+ * queries than keys) are written as 0.  Rows of `out` outside every sequence are not written.
+ *
+ * The offsets stay on the device (the call does not synchronize): cu_seqlens_q[0] = 0,
+ * non-decreasing, cu_seqlens_q[batch] = total_q; likewise for k.  The library clamps every
+ * offset to [0, total] and every length to its max_seqlen bound, so a malformed array cannot
+ * make it read or write outside q, k, v, out or the workspace; the values it then writes are
+ * unspecified.  The workspace is laid out for `batch` sequences of the bound lengths
+ * (sage_attn_varlen_workspace_bytes), so tight bounds keep it small.
+ */
+typedef struct {
+  int batch;                       /* sequences, >= 1                                     */
+  int Hq, Hkv, d;                  /* as in sage_attn_shape                               */
+  int total_q, total_k;            /* rows of q (and out) and of k, v, >= 1               */
+  int max_seqlen_q, max_seqlen_k;  /* bounds on the query / key length of a sequence, >= 1 */
+  const int* cu_seqlens_q;         /* device, batch + 1 offsets into q and out, 4-aligned */
+  const int* cu_seqlens_k;         /* device, batch + 1 offsets into k and v              */
+  int causal;                      /* 0, 1, 2 per sequence, as in sage_attn_shape         */
+  float sm_scale;                  /* <= 0 or non-finite: 1/sqrt(d)                       */
+  unsigned variant;                /* as in sage_attn_shape                               */
+} sage_attn_varlen_shape;
+
+/* Workspace bytes of sage_attn_varlen_fwd (0 on bad arguments). */
+size_t sage_attn_varlen_workspace_bytes(const sage_attn_varlen_shape* shape);
+
+/* The forward of a variable-length batch on `stream`.  workspace: NULL for a stream-ordered
+ * allocation, else a 256-byte aligned device buffer of ws_bytes bytes.  Returns SAGE_OK or a
+ * negative sage_status (SAGE_ERR_INVALID_ARG for a NULL shape or offset array, a misaligned
+ * pointer, a size below 1 or bad variant bits; SAGE_ERR_NO_MEMORY for a short workspace). */
+int sage_attn_varlen_fwd(const sage_attn_varlen_shape* shape, const void* q, const void* k, const void* v,
+                         void* out, void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * sage_attn_set_profile_events -- measurement hook.  With both arguments non-NULL (two
  * hipEvent_t handles), the next sage_attn_fwd / sage_attn_fwd_ws call on this thread
  * records `start` on its stream just before the fused attention kernel and `stop` just

@@ -22,6 +22,7 @@ __all__ = [
     "sage_attn_workspace_bytes", "sage_attn_quantize", "sage_attn_status_string",
     "sage_attn_version", "sage_attn_set_profile_events", "sage_attn", "QuantViews",
     "SageAttnShape", "sage_attn_fwd_ex", "sage_attn_workspace_bytes_ex", "sage_attn_quantize_ex",
+    "SageAttnVarlenShape", "sage_attn_varlen_workspace_bytes", "sage_attn_varlen_fwd", "sage_attn_varlen",
 ]
 
 SAGE_OK = 0
@@ -71,6 +72,14 @@ class SageAttnShape(ctypes.Structure):
                 ("sm_scale", ctypes.c_float), ("variant", ctypes.c_uint)]
 
 
+class SageAttnVarlenShape(ctypes.Structure):
+    """Mirror of ``sage_attn_varlen_shape`` (a packed batch of variable-length sequences)."""
+    _fields_ = [("batch", ctypes.c_int), ("Hq", ctypes.c_int), ("Hkv", ctypes.c_int), ("d", ctypes.c_int),
+                ("total_q", ctypes.c_int), ("total_k", ctypes.c_int), ("max_seqlen_q", ctypes.c_int),
+                ("max_seqlen_k", ctypes.c_int), ("cu_seqlens_q", ctypes.c_void_p), ("cu_seqlens_k", ctypes.c_void_p),
+                ("causal", ctypes.c_int), ("sm_scale", ctypes.c_float), ("variant", ctypes.c_uint)]
+
+
 def library_path() -> str:
     return _LIB_PATH
 
@@ -106,6 +115,11 @@ def load_library():
     L.sage_attn_fwd_ex.restype = i
     L.sage_attn_quantize_ex.argtypes = [SP, P, P, P, ctypes.POINTER(QuantViews), P]
     L.sage_attn_quantize_ex.restype = i
+    VP = ctypes.POINTER(SageAttnVarlenShape)
+    L.sage_attn_varlen_workspace_bytes.argtypes = [VP]
+    L.sage_attn_varlen_workspace_bytes.restype = sz
+    L.sage_attn_varlen_fwd.argtypes = [VP, P, P, P, P, P, sz, P]
+    L.sage_attn_varlen_fwd.restype = i
     _lib = L
     return L
 
@@ -145,6 +159,14 @@ def sage_attn_fwd_ex(shape, q, k, v, out, workspace, ws_bytes, stream) -> int:
 
 def sage_attn_quantize_ex(shape, q, k, v, views: QuantViews, stream) -> int:
     return load_library().sage_attn_quantize_ex(_shape_ptr(shape), q, k, v, ctypes.byref(views), stream)
+
+
+def sage_attn_varlen_workspace_bytes(shape) -> int:
+    return load_library().sage_attn_varlen_workspace_bytes(_shape_ptr(shape))
+
+
+def sage_attn_varlen_fwd(shape, q, k, v, out, workspace, ws_bytes, stream) -> int:
+    return load_library().sage_attn_varlen_fwd(_shape_ptr(shape), q, k, v, out, workspace, ws_bytes, stream)
 
 
 def sage_attn_set_profile_events(start, stop) -> None:
@@ -220,4 +242,47 @@ def sage_attn(q, k, v, causal: bool = False, sm_scale: float | None = None, smoo
     rc = sage_attn_fwd_ex(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), None, 0, stream)
     if rc != SAGE_OK:
         raise SageError(rc, "sage_attn_fwd_ex")
+    return out
+
+
+def sage_attn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, causal: int = 0,
+                     sm_scale: float | None = None, smooth_v: bool = False, out_fp32: bool = False, out=None,
+                     mxfp4: bool = False, qk_fp8: bool = False):
+    """The forward of a packed batch of variable-length sequences.
+
+    q: [total_q, Hq, d], k/v: [total_k, Hkv, d] (same bf16/fp16 dtype, contiguous, on the
+    device); cu_seqlens_q / cu_seqlens_k: int32 device tensors of batch + 1 offsets;
+    max_seqlen_*: bounds on the sequence lengths.  Each sequence is computed as ``sage_attn``
+    computes it alone; rows that see no key are 0.  Returns out [total_q, Hq, d].
+    """
+    import torch
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be 3-D [total, H, d]")
+    total_q, H, d = q.shape
+    total_k, Hkv = k.shape[0], k.shape[1]
+    if tuple(k.shape) != (total_k, Hkv, d) or tuple(v.shape) != (total_k, Hkv, d):
+        raise ValueError("k and v must be [total_k, Hkv, d] matching q")
+    if Hkv < 1 or H % Hkv:
+        raise ValueError("the query heads must be a multiple of the key/value heads")
+    if not (q.dtype == k.dtype == v.dtype):
+        raise TypeError("q, k, v must share a dtype")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("q, k, v must be contiguous device tensors")
+    for c in (cu_seqlens_q, cu_seqlens_k):
+        if c.dtype != torch.int32 or not c.is_cuda or not c.is_contiguous() or c.dim() != 1:
+            raise ValueError("cu_seqlens must be contiguous int32 device vectors")
+    batch = cu_seqlens_q.numel() - 1
+    if batch < 1 or cu_seqlens_k.numel() != batch + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must hold batch + 1 offsets")
+    var = _variant_for(q, smooth_v, out_fp32, False, mxfp4, qk_fp8)
+    if out is None:
+        out = torch.empty((total_q, H, d), dtype=torch.float32 if out_fp32 else q.dtype, device=q.device)
+    scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(d)
+    shape = SageAttnVarlenShape(batch, H, Hkv, d, total_q, total_k, int(max_seqlen_q), int(max_seqlen_k),
+                                cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), int(causal), scale, var)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = sage_attn_varlen_fwd(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), None, 0, stream)
+    if rc != SAGE_OK:
+        raise SageError(rc, "sage_attn_varlen_fwd")
     return out

@@ -5,6 +5,7 @@
 // store of four output channels.
 #pragma once
 
+#include <cfloat>
 #include <type_traits>
 
 #include "sage_common.hpp"

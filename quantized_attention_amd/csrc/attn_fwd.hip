@@ -72,8 +72,9 @@ struct AttnArgs {
   const float* vmean;
   const float* ds;  // Delta S * sm_scale * log2(e)
   void* out;
-  int N, M, BH, nqb, nkt, Np, Mp;
-  int coff;         // causal: key t visible to query r iff t <= r + coff
+  int BH, nqb, nkt, Np, Mp;  // bounds: padded workspace strides
+  int causal2;      // causal = 2: key t visible to query r iff t <= r + M - N (else t <= r)
+  SeqLayout ql, kl; // rows of q / out and of k, v per sequence (dense or packed)
   int H, Hkv, G;    // query heads, key/value heads, query heads per key/value head
   float qk_scale;   // sm_scale * log2(e)
   int xcd_map;      // 1: heads grouped per XCD
@@ -151,8 +152,8 @@ __device__ __forceinline__ void softmax_pv(const ACC (&acc)[2], const uint8_t* _
 #pragma unroll
     for (int r = 0; r < 16; r++) mt = fmaxf(mt, sc[T][r]);
   mt = pair_max(mt);
-  const float m_new = fmaxf(m_run, mt);
-  const float base = (m_new == -INFINITY) ? 0.0f : m_new - kLog2_448;
+  const float m_new = fmaxf(m_run, mt);  // finite: m_run starts at -FLT_MAX
+  const float base = m_new - kLog2_448;
   const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile, exactly 1 if m is unchanged
   m_run = m_new;
   // ---- P = 448 P~ (FP32), row sum, E4M3 pack in the PV B-operand order ----
@@ -240,7 +241,13 @@ __global__ __launch_bounds__(256, OCC) void attn_fwd_kernel(AttnArgs a) {
     }
   }
   const int kvh = kv_head(bh, a.H, a.Hkv, a.G);  // the key/value head this query head reads
-  const int qb = CAUSAL ? (a.nqb - 1 - qi) : qi;  // heavy blocks first
+  // this sequence's queries and keys (every sequence of a dense batch has N and M)
+  const int bseq = bh / a.H;
+  const int nseq = seq_rows(a.ql, bseq, 0, a.H, D).len, mseq = seq_rows(a.kl, bseq, 0, a.Hkv, D).len;
+  const int coff = a.causal2 ? mseq - nseq : 0;  // key t visible to query r iff t <= r + coff
+  const int nqbs = (nseq + kBQ - 1) / kBQ, nkts = (mseq + kBK - 1) / kBK;
+  if (qi >= nqbs) return;  // a block past this sequence's queries (variable-length batches)
+  const int qb = CAUSAL ? (nqbs - 1 - qi) : qi;  // heavy blocks first
   const int q0 = qb * kBQ;
   const int wq0 = q0 + 32 * w;       // first query of this wave
   const int qrow = wq0 + col;        // this lane's query
@@ -259,9 +266,13 @@ __global__ __launch_bounds__(256, OCC) void attn_fwd_kernel(AttnArgs a) {
   for (int c = 0; c < NKS; c++)
 #pragma unroll
     for (int r = 0; r < 16; r++) O[c][r] = 0.0f;
-  float m_run = -INFINITY, l_run = 0.0f;
+  // The running max starts at -FLT_MAX, not -inf: a row that sees no key in a tile (only
+  // possible in a variable-length batch) then keeps alpha = 1, l = 0 and O = 0 instead of NaN,
+  // and the epilogue writes it as 0.  Any visible score exceeds -FLT_MAX, so alpha on a row's
+  // first visible tile is exactly 0, as with -inf.
+  float m_run = -FLT_MAX, l_run = 0.0f;
 
-  const int jend = CAUSAL ? min(a.nkt, (q0 + kBQ + a.coff + kBK - 1) / kBK) : a.nkt;
+  const int jend = CAUSAL ? max(0, min(nkts, (q0 + kBQ + coff + kBK - 1) / kBK)) : nkts;
   const int8_t* kbase = a.khat + (size_t)kvh * a.Mp * D;
   const uint8_t* vbase = a.vhat + (size_t)kvh * a.nkt * D * kBK;
   const float* dsbase = a.ds + ((size_t)bh * a.nqb + qb) * a.Mp;
@@ -305,7 +316,7 @@ __global__ __launch_bounds__(256, OCC) void attn_fwd_kernel(AttnArgs a) {
       asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kPerTile) : "memory");
   };
 
-  auto skip_t = [&](int j) { return CAUSAL && j * kBK > wq0 + 31 + a.coff; };  // fully masked for this wave
+  auto skip_t = [&](int j) { return CAUSAL && j * kBK > wq0 + 31 + coff; };  // fully masked for this wave
   if constexpr (PIPE) {
     // Software pipeline per wave: the QK MFMAs of tile j+1 are issued before the softmax of
     // tile j, so the matrix core works on j+1 while the VALU works on j.  Tile j+3 streams into
@@ -316,20 +327,20 @@ __global__ __launch_bounds__(256, OCC) void attn_fwd_kernel(AttnArgs a) {
       if (j + 1 < jend && !skip_t(j + 1)) qk_tile<D, QF8>(sK[(j + 1) % NB], qf, h, col, nxt);
       if (!skip_t(j)) {
         const int key0 = j * kBK;
-        const bool masked = (CAUSAL && key0 + kBK - 1 > wq0 + a.coff) || (key0 + kBK > a.M);
+        const bool masked = (CAUSAL && key0 + kBK - 1 > wq0 + coff) || (key0 + kBK > mseq);
         const int b = j % NB;
-        softmax_pv<D, CAUSAL, ACC_VALU, acc_t<QF8>>(cur, sV[b], sDS[b], sDK[b], dql, h, col, key0, qrow + a.coff, a.M, masked, O,
+        softmax_pv<D, CAUSAL, ACC_VALU, acc_t<QF8>>(cur, sV[b], sDS[b], sDK[b], dql, h, col, key0, qrow + coff, mseq, masked, O,
                                         m_run, l_run);
       }
       publish(j + 3 < jend);  // tile j+2 must be complete; j+3 may still be arriving
     };
 
-    dma(0, 0);
+    if (jend > 0) dma(0, 0);
     if (jend > 1) dma(1, 1);
     if (jend > 2) dma(2, 2);
     publish(jend > 2);  // tiles 0 and 1 landed; tile 2 may be arriving
     acc_t<QF8> accA[2], accB[2];
-    qk_tile<D, QF8>(sK[0], qf, h, col, accA);  // tile 0 is never masked away
+    if (jend > 0) qk_tile<D, QF8>(sK[0], qf, h, col, accA);  // tile 0 is never masked away
     for (int j = 0; j < jend; j += 2) {
       body(j, accA, accB);
       if (j + 1 < jend) body(j + 1, accB, accA);
@@ -357,10 +368,10 @@ __global__ __launch_bounds__(256, OCC) void attn_fwd_kernel(AttnArgs a) {
       if (j + NB - 1 < jend) dma(j + NB - 1, (b + NB - 1) % NB);  // the slot tile j-1 left
       if (!skip_t(j)) {
         const int key0 = j * kBK;
-        const bool masked = (CAUSAL && key0 + kBK - 1 > wq0 + a.coff) || (key0 + kBK > a.M);
+        const bool masked = (CAUSAL && key0 + kBK - 1 > wq0 + coff) || (key0 + kBK > mseq);
         acc_t<QF8> acc[2];
         qk_tile<D, QF8>(sK[b], qf, h, col, acc);
-        softmax_pv<D, CAUSAL, ACC_VALU, acc_t<QF8>>(acc, sV[b], sDS[b], sDK[b], dql, h, col, key0, qrow + a.coff, a.M, masked, O,
+        softmax_pv<D, CAUSAL, ACC_VALU, acc_t<QF8>>(acc, sV[b], sDS[b], sDK[b], dql, h, col, key0, qrow + coff, mseq, masked, O,
                                         m_run, l_run);
       }
       publish_n(min(NB - 2, jend - j - 2));
@@ -373,13 +384,15 @@ __global__ __launch_bounds__(256, OCC) void attn_fwd_kernel(AttnArgs a) {
     }
   }
 
-  // ---- epilogue: O / l (l holds 448 * sum P~) * dV (+ V_m) ----
+  // ---- epilogue: O / l (l holds 448 * sum P~) * dV (+ V_m); 0 for a row that saw no key ----
   const float l_tot = pair_sum(l_run);
-  if (qrow >= a.N) return;
+  if (qrow >= nseq) return;
   const float inv = 1.0f / l_tot;
+  const bool none = l_tot == 0.0f;
   const float* dvp = a.dv + (size_t)kvh * D;
   const float* vmp = a.vmean + (size_t)kvh * D;
-  const size_t orow = ((size_t)bh * a.N + qrow) * D;
+  const SeqRows ro = seq_rows(a.ql, bseq, bh % a.H, a.H, D);
+  const size_t orow = ro.base + (size_t)qrow * ro.stride;
 #pragma unroll
   for (int c = 0; c < NKS; c++) {
 #pragma unroll
@@ -387,7 +400,7 @@ __global__ __launch_bounds__(256, OCC) void attn_fwd_kernel(AttnArgs a) {
       const int ch = 32 * c + 8 * b + 4 * h;
       float o[4];
 #pragma unroll
-      for (int k = 0; k < 4; k++) o[k] = fmaf(O[c][4 * b + k] * inv, dvp[ch + k], vmp[ch + k]);
+      for (int k = 0; k < 4; k++) o[k] = none ? 0.0f : fmaf(O[c][4 * b + k] * inv, dvp[ch + k], vmp[ch + k]);
       store_out4<OUT>(a.out, orow + ch, o);
     }
   }
@@ -445,8 +458,9 @@ hipError_t launch_attn_fwd(const Problem& p, const Workspace& w, void* out, hipS
   AttnArgs a;
   a.qhat = w.qhat; a.khat = w.khat; a.vhat = w.vhat; a.dq = w.dq; a.dk = w.dk; a.dv = w.dv;
   a.vmean = w.vmean; a.ds = w.ds; a.out = out;
-  a.N = p.N; a.M = p.M; a.BH = p.BH; a.nqb = p.nqb; a.nkt = p.nkt; a.Np = p.Np; a.Mp = p.Mp;
-  a.coff = p.coff;
+  a.BH = p.BH; a.nqb = p.nqb; a.nkt = p.nkt; a.Np = p.Np; a.Mp = p.Mp;
+  a.causal2 = p.causal == 2 ? 1 : 0;
+  a.ql = p.ql; a.kl = p.kl;
   a.qk_scale = p.sm_scale * kLog2e;
   a.H = p.H; a.Hkv = p.Hkv; a.G = p.G;
   a.xcd_map = (p.BH % (kXCD * p.G) == 0) ? 1 : 0;

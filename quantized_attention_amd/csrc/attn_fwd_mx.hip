@@ -62,8 +62,9 @@ struct MxArgs {
   const float* vmean;
   const float* ds;      // Delta S * sm_scale * log2(e)
   void* out;
-  int N, M, BH, nqb, nkt, Np, Mp;
-  int coff;         // causal: key t visible to query r iff t <= r + coff
+  int BH, nqb, nkt, Np, Mp;  // bounds: padded workspace strides
+  int causal2;      // causal = 2: key t visible to query r iff t <= r + M - N (else t <= r)
+  SeqLayout ql, kl; // rows of q / out and of k, v per sequence (dense or packed)
   int H, Hkv, G;    // query heads, key/value heads, query heads per key/value head
   float qk_scale;       // sm_scale * log2(e)
   int xcd_map;
@@ -129,8 +130,8 @@ __device__ __forceinline__ void softmax_pv_mx(const v16f (&acc)[2], const uint8_
     for (int r = 0; r < 16; r++) m = fmaxf(m, sc[T][r]);
     mb[T] = pair_max(m);
   }
-  const float m_new = fmaxf(m_run, fmaxf(mb[0], mb[1]));
-  const float base = (m_new == -INFINITY) ? 0.0f : m_new;
+  const float m_new = fmaxf(m_run, fmaxf(mb[0], mb[1]));  // finite: m_run starts at -FLT_MAX
+  const float base = m_new;
   const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile, exactly 1 if m is unchanged
   m_run = m_new;
   // E8M0 of each P block: from its largest P~ (0 for a fully masked block: code 0)
@@ -225,7 +226,13 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 3) void attn_fwd_mx_kernel(MxArg
     }
   }
   const int kvh = kv_head(bh, a.H, a.Hkv, a.G);  // the key/value head this query head reads
-  const int qb = CAUSAL ? (a.nqb - 1 - qi) : qi;  // heavy blocks first
+  // this sequence's queries and keys (every sequence of a dense batch has N and M)
+  const int bseq = bh / a.H;
+  const int nseq = seq_rows(a.ql, bseq, 0, a.H, D).len, mseq = seq_rows(a.kl, bseq, 0, a.Hkv, D).len;
+  const int coff = a.causal2 ? mseq - nseq : 0;  // key t visible to query r iff t <= r + coff
+  const int nqbs = (nseq + kBQ - 1) / kBQ, nkts = (mseq + kBK - 1) / kBK;
+  if (qi >= nqbs) return;  // a block past this sequence's queries (variable-length batches)
+  const int qb = CAUSAL ? (nqbs - 1 - qi) : qi;  // heavy blocks first
   const int q0 = qb * kBQ;
   const int wq0 = q0 + 32 * w;
   const int qrow = wq0 + col;
@@ -248,9 +255,11 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 3) void attn_fwd_mx_kernel(MxArg
   for (int c = 0; c < NG; c++)
 #pragma unroll
     for (int r = 0; r < 16; r++) O[c][r] = 0.0f;
-  float m_run = -INFINITY, l_run = 0.0f;
+  // -FLT_MAX, not -inf: a row that sees no key (variable-length batches) keeps l = 0 and O = 0
+  // instead of NaN; a row's first visible tile still gets alpha = 0 exactly.
+  float m_run = -FLT_MAX, l_run = 0.0f;
 
-  const int jend = CAUSAL ? min(a.nkt, (q0 + kBQ + a.coff + kBK - 1) / kBK) : a.nkt;
+  const int jend = CAUSAL ? max(0, min(nkts, (q0 + kBQ + coff + kBK - 1) / kBK)) : nkts;
   const uint8_t* kbase = a.khat + (size_t)kvh * a.Mp * (D / 2);
   const uint8_t* vbase = a.vhat + (size_t)kvh * a.nkt * TL::VBYTES;
   const float* dsbase = a.ds + ((size_t)bh * a.nqb + qb) * a.Mp;
@@ -282,8 +291,8 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 3) void attn_fwd_mx_kernel(MxArg
   // that closed it; at the end of iteration j, tile j+1 must have landed for all waves.
   auto publish = [&]() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
 
-  auto skip_t = [&](int j) { return CAUSAL && j * kBK > wq0 + 31 + a.coff; };  // fully masked for this wave
-  dma(0, 0);
+  auto skip_t = [&](int j) { return CAUSAL && j * kBK > wq0 + 31 + coff; };  // fully masked for this wave
+  if (jend > 0) dma(0, 0);
   publish();
   // One iteration; the slot is a compile-time constant so LDS addresses are immediates.
   auto iter = [&](int j, auto slotc) {
@@ -291,10 +300,10 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 3) void attn_fwd_mx_kernel(MxArg
     if (j + 1 < jend) dma(j + 1, 1 - b);
     if (!skip_t(j)) {
       const int key0 = j * kBK;
-      const bool masked = (CAUSAL && key0 + kBK - 1 > wq0 + a.coff) || (key0 + kBK > a.M);
+      const bool masked = (CAUSAL && key0 + kBK - 1 > wq0 + coff) || (key0 + kBK > mseq);
       v16f acc[2];
       qk_tile_mx<D>(sK[b], qf, sKS[b][lane], qs, h, col, acc);
-      softmax_pv_mx<D, CAUSAL, ACC_VALU>(acc, sV[b], sDS[b], sVS[b][lane], a.qk_scale, h, col, key0, qrow + a.coff, a.M,
+      softmax_pv_mx<D, CAUSAL, ACC_VALU>(acc, sV[b], sDS[b], sVS[b][lane], a.qk_scale, h, col, key0, qrow + coff, mseq,
                                          masked, O, m_run, l_run);
     }
     publish();
@@ -306,12 +315,14 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 3) void attn_fwd_mx_kernel(MxArg
     });
   }
 
-  // ---- epilogue: O / l (+ V_m) ----
+  // ---- epilogue: O / l (+ V_m); 0 for a row that saw no key ----
   const float l_tot = pair_sum(l_run);
-  if (qrow >= a.N) return;
+  if (qrow >= nseq) return;
   const float inv = 1.0f / l_tot;
+  const bool none = l_tot == 0.0f;
   const float* vmp = a.vmean + (size_t)kvh * D;
-  const size_t orow = ((size_t)bh * a.N + qrow) * D;
+  const SeqRows ro = seq_rows(a.ql, bseq, bh % a.H, a.H, D);
+  const size_t orow = ro.base + (size_t)qrow * ro.stride;
 #pragma unroll
   for (int c = 0; c < NG; c++) {
 #pragma unroll
@@ -319,7 +330,7 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 3) void attn_fwd_mx_kernel(MxArg
       const int ch = 32 * c + 8 * b + 4 * h;
       float o[4];
 #pragma unroll
-      for (int k = 0; k < 4; k++) o[k] = fmaf(O[c][4 * b + k], inv, vmp[ch + k]);
+      for (int k = 0; k < 4; k++) o[k] = none ? 0.0f : fmaf(O[c][4 * b + k], inv, vmp[ch + k]);
       store_out4<OUT>(a.out, orow + ch, o);
     }
   }
@@ -352,8 +363,9 @@ hipError_t launch_attn_fwd_mx(const Problem& p, const Workspace& w, void* out, h
   a.vhat = w.vhat;
   a.qsc = w.qsc; a.ksc = w.ksc; a.vsc = w.vsc;
   a.vmean = w.vmean; a.ds = w.ds; a.out = out;
-  a.N = p.N; a.M = p.M; a.BH = p.BH; a.nqb = p.nqb; a.nkt = p.nkt; a.Np = p.Np; a.Mp = p.Mp;
-  a.coff = p.coff;
+  a.BH = p.BH; a.nqb = p.nqb; a.nkt = p.nkt; a.Np = p.Np; a.Mp = p.Mp;
+  a.causal2 = p.causal == 2 ? 1 : 0;
+  a.ql = p.ql; a.kl = p.kl;
   a.qk_scale = p.sm_scale * kLog2e;
   a.H = p.H; a.Hkv = p.Hkv; a.G = p.G;
   a.xcd_map = (p.BH % (kXCD * p.G) == 0) ? 1 : 0;

@@ -54,19 +54,23 @@ __global__ __launch_bounds__(256) void kv_stats_kernel(const uint16_t* __restric
                                                        const uint16_t* __restrict__ V,
                                                        double* __restrict__ kpart, double* __restrict__ vpart,
                                                        float* __restrict__ vmaxp, float* __restrict__ vminp,
-                                                       int M, int nkt, bool fp16, bool smooth_v) {
+                                                       SeqLayout kl, int Hkv, int nkt, bool fp16, bool smooth_v) {
   constexpr int RS = D + 8;  // LDS row stride (16-bit elements), 16-byte aligned rows
   __shared__ __attribute__((aligned(16))) uint16_t sk[kBK * RS];
   __shared__ __attribute__((aligned(16))) uint16_t sv[kBK * RS];
   const int u = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
-  const int t0 = u * kBK, n = min(kBK, M - t0);
-  const size_t base = ((size_t)bh * M + t0) * D;
+  const SeqRows R = seq_rows(kl, bh / Hkv, bh % Hkv, Hkv, D);
+  const int t0 = u * kBK;
+  if (t0 >= R.len) return;  // past this sequence's keys: no chunk
+  const int n = min(kBK, R.len - t0);
+  const size_t base = R.base + (size_t)t0 * R.stride;
 #pragma unroll
   for (int i = 0; i < kBK * D / 8 / 256; i++) {
     const int x = tid + 256 * i, row = x / (D / 8), c0 = (x % (D / 8)) * 8;
     if (row < n) {
-      *reinterpret_cast<v4i*>(&sk[row * RS + c0]) = *reinterpret_cast<const v4i*>(K + base + (size_t)row * D + c0);
-      *reinterpret_cast<v4i*>(&sv[row * RS + c0]) = *reinterpret_cast<const v4i*>(V + base + (size_t)row * D + c0);
+      const size_t off = base + (size_t)row * R.stride + c0;
+      *reinterpret_cast<v4i*>(&sk[row * RS + c0]) = *reinterpret_cast<const v4i*>(K + off);
+      *reinterpret_cast<v4i*>(&sv[row * RS + c0]) = *reinterpret_cast<const v4i*>(V + off);
     }
   }
   __syncthreads();
@@ -116,17 +120,19 @@ __global__ __launch_bounds__(256) void kv_finalize_kernel(const double* __restri
                                                           const float* __restrict__ vmaxp,
                                                           const float* __restrict__ vminp,
                                                           float* __restrict__ kmean, float* __restrict__ vmean,
-                                                          float* __restrict__ dv, int M, int d, int nkt,
-                                                          bool smooth_v) {
+                                                          float* __restrict__ dv, SeqLayout kl, int Hkv, int d,
+                                                          int nkt, bool smooth_v) {
   __shared__ double sk[kFinStage][kFinCh];
   __shared__ double svs[kFinStage][kFinCh];
   __shared__ float smx[kFinStage][kFinCh];
   __shared__ float smn[kFinStage][kFinCh];
   const int bh = blockIdx.x, c0 = blockIdx.y * kFinCh, tid = threadIdx.x;
+  const int M = seq_rows(kl, bh / Hkv, bh % Hkv, Hkv, d).len;  // this sequence's keys
+  const int nk = (M + kBK - 1) / kBK;                           // its chunks
   double ks = 0.0, vs = 0.0;
   float mx = -INFINITY, mn = INFINITY;
-  for (int u0 = 0; u0 < nkt; u0 += kFinStage) {
-    const int ns = min(kFinStage, nkt - u0);
+  for (int u0 = 0; u0 < nk; u0 += kFinStage) {
+    const int ns = min(kFinStage, nk - u0);
 #pragma unroll
     for (int i = 0; i < kFinStage * kFinCh / 256; i++) {
       const int x = tid + 256 * i, uu = x / kFinCh, cc = x % kFinCh;
@@ -173,13 +179,14 @@ __global__ __launch_bounds__(256) void kv_finalize_kernel(const double* __restri
     __syncthreads();
   }
   // the K sum lives in threads 0..7, the V statistics in threads 64..71
+  // a sequence without keys (variable-length batches only) gets zero means and the floor scale
   if (tid < kFinCh) {
-    const float km = (float)(ks / (double)M);
+    const float km = M > 0 ? (float)(ks / (double)M) : 0.0f;
     kmean[(size_t)bh * d + c0 + tid] = km;
   }
   if (tid >= 64 && tid < 64 + kFinCh) {
     const int c = c0 + tid - 64;
-    const float vm = smooth_v ? (float)(vs / (double)M) : 0.0f;
+    const float vm = (smooth_v && M > 0) ? (float)(vs / (double)M) : 0.0f;
     vmean[(size_t)bh * d + c] = vm;
     const float a1 = mx - vm, a2 = vm - mn;  // max |fp32(V - V_m)| over the tokens
     const float am = a1 > a2 ? a1 : a2;
@@ -194,20 +201,23 @@ __global__ __launch_bounds__(256) void q_prep_kernel(const uint16_t* __restrict_
                                                      int8_t* __restrict__ qhat, float* __restrict__ dq,
                                                      uint8_t* __restrict__ qsc,
                                                      float* __restrict__ qmean, uint16_t* __restrict__ qm_hi,
-                                                     uint16_t* __restrict__ qm_lo, int N, int Np, int nqb,
-                                                     bool fp16) {
+                                                     uint16_t* __restrict__ qm_lo, SeqLayout ql, int H, int Np,
+                                                     int nqb, bool fp16) {
   constexpr int RS = D + 8;
   __shared__ __attribute__((aligned(16))) uint16_t sq[kBQ * RS];
   __shared__ float sm[D];
   const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int r0 = i * kBQ, n = min(kBQ, N - r0);
-  const size_t in_base = ((size_t)bh * N + r0) * D;
+  const SeqRows R = seq_rows(ql, bh / H, bh % H, H, D);
+  const int r0 = i * kBQ;
+  if (r0 >= R.len) return;  // past this sequence's queries: the block is never read
+  const int n = min(kBQ, R.len - r0);
+  const size_t in_base = R.base + (size_t)r0 * R.stride;
 #pragma unroll
   for (int k = 0; k < kBQ * D / 8 / 256; k++) {
     const int x = tid + 256 * k, r = x / (D / 8), c0 = (x % (D / 8)) * 8;
     if (r < n)
-      *reinterpret_cast<v4i*>(&sq[r * RS + c0]) = *reinterpret_cast<const v4i*>(Q + in_base + (size_t)r * D + c0);
+      *reinterpret_cast<v4i*>(&sq[r * RS + c0]) = *reinterpret_cast<const v4i*>(Q + in_base + (size_t)r * R.stride + c0);
   }
   __syncthreads();
   if (tid < D) {
@@ -300,8 +310,9 @@ struct KVArgs {
   uint8_t* ksc;  // MX: E8M0 of gamma(K) blocks, [BH][nkt][64][4]
   uint8_t* vsc;  // MX: E8M0 of V' blocks, [BH][nkt][64][4]
   float ds_scale;
-  int M, Mp, nkt, nqb, causal, coff;
+  int Mp, nkt, nqb, causal;  // nkt, nqb, Mp: the bounds (padded workspace strides)
   int H, Hkv, G;  // query heads, key/value heads, query heads per key/value head
+  SeqLayout ql, kl;  // rows of q and of k, v
   bool fp16;
 };
 
@@ -326,8 +337,12 @@ __global__ __launch_bounds__(256, MX ? 3 : 4) void kv_quant_kernel(KVArgs a) {
   __shared__ float ssv[MX ? 1 : D], srv[MX ? 1 : D];  // dV and 1 / dV per channel (srv: d = 64)
   const int u = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int t0 = u * kBK, n = min(kBK, a.M - t0);
-  const size_t in_base = ((size_t)bh * a.M + t0) * D;
+  const int b = bh / a.Hkv;
+  const SeqRows R = seq_rows(a.kl, b, bh % a.Hkv, a.Hkv, D);
+  const int t0 = u * kBK;
+  if (t0 >= R.len) return;  // past this sequence's keys: the tile is never read
+  const int n = min(kBK, R.len - t0);
+  const size_t in_base = R.base + (size_t)t0 * R.stride;
   const float* km = a.kmean + (size_t)bh * D;
   // dV of channel tid: loaded with the K/V chunks, inverted into srv once Delta S is done
   const float dv_t = (!MX && tid < D) ? a.dv[(size_t)bh * D + tid] : 1.0f;
@@ -337,7 +352,7 @@ __global__ __launch_bounds__(256, MX ? 3 : 4) void kv_quant_kernel(KVArgs a) {
 #pragma unroll
   for (int i = 0; i < CH; i++) {
     const int x = tid + 256 * i, row = x / (D / 8), c0 = (x % (D / 8)) * 8;
-    const size_t off = in_base + (size_t)min(row, n - 1) * D + c0;  // rows >= n are not used
+    const size_t off = in_base + (size_t)min(row, n - 1) * R.stride + c0;  // rows >= n are not used
     kraw[i] = *reinterpret_cast<const v4i*>(a.K + off);
     vraw[i] = *reinterpret_cast<const v4i*>(a.V + off);
   }
@@ -452,15 +467,19 @@ __global__ __launch_bounds__(256, MX ? 3 : 4) void kv_quant_kernel(KVArgs a) {
   // both 32-key halves of the tile against them.
   if (a.ds) {
     const int h = lane >> 5, col = lane & 31;
+    // this sequence's query blocks and causal offset (key t visible to query r iff t <= r + coff);
     // under the causal mask, block i needs keys t <= 128 (i + 1) - 1 + coff
-    const int ilo = (a.causal && t0 > a.coff) ? (t0 - a.coff) / kBQ : 0;
-    const int ngrp = (a.nqb + 31) / 32;
+    const int nq = seq_rows(a.ql, b, 0, a.H, D).len;
+    const int nqb = (nq + kBQ - 1) / kBQ;
+    const int coff = a.causal == 2 ? R.len - nq : 0;
+    const int ilo = (a.causal && t0 > coff) ? (t0 - coff) / kBQ : 0;
+    const int ngrp = (nqb + 31) / 32;
     for (int unit = wave; unit < a.G * ngrp; unit += 4) {
       const int g = unit / ngrp, gidx = unit % ngrp;
       if (32 * gidx + 31 < ilo) continue;
       const int bhq = (bh / a.Hkv) * a.H + (bh % a.Hkv) * a.G + g;  // query head
       const int blk = 32 * gidx + col;
-      const bool bv = blk < a.nqb;
+      const bool bv = blk < nqb;
       const size_t qo = ((size_t)bhq * a.nqb + (bv ? blk : 0)) * D;
       v8bf bq[D / 16], bl[D / 16];  // the block's q-mean head/tail, all loads in flight
 #pragma unroll
@@ -578,16 +597,16 @@ hipError_t launch_kv_stats(const Problem& p, const void* k, const void* v, const
   const dim3 grid(p.nkt, p.BHkv);
   if (p.d == 128)
     hipLaunchKernelGGL(kv_stats_kernel<128>, grid, dim3(256), 0, s, (const uint16_t*)k, (const uint16_t*)v,
-                       w.kpart, w.vpart, w.vmaxp, w.vminp, p.M, p.nkt, p.fp16, p.smooth_v);
+                       w.kpart, w.vpart, w.vmaxp, w.vminp, p.kl, p.Hkv, p.nkt, p.fp16, p.smooth_v);
   else
     hipLaunchKernelGGL(kv_stats_kernel<64>, grid, dim3(256), 0, s, (const uint16_t*)k, (const uint16_t*)v,
-                       w.kpart, w.vpart, w.vmaxp, w.vminp, p.M, p.nkt, p.fp16, p.smooth_v);
+                       w.kpart, w.vpart, w.vmaxp, w.vminp, p.kl, p.Hkv, p.nkt, p.fp16, p.smooth_v);
   return hipGetLastError();
 }
 
 hipError_t launch_kv_finalize(const Problem& p, const Workspace& w, hipStream_t s) {
   hipLaunchKernelGGL(kv_finalize_kernel, dim3(p.BHkv, p.d / kFinCh), dim3(256), 0, s, w.kpart, w.vpart, w.vmaxp,
-                     w.vminp, w.kmean, w.vmean, w.dv, p.M, p.d, p.nkt, p.smooth_v);
+                     w.vminp, w.kmean, w.vmean, w.dv, p.kl, p.Hkv, p.d, p.nkt, p.smooth_v);
   return hipGetLastError();
 }
 
@@ -595,7 +614,7 @@ hipError_t launch_q_prep(const Problem& p, const void* q, const Workspace& w, hi
   const dim3 grid(p.nqb, p.BH);
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, (const uint16_t*)q, w.qhat, w.dq, w.qsc, w.qmean, w.qm_hi,
-                       w.qm_lo, p.N, p.Np, p.nqb, p.fp16);
+                       w.qm_lo, p.ql, p.H, p.Np, p.nqb, p.fp16);
   };
   if (p.d == 128)
     p.mx ? go(q_prep_kernel<128, true, false>)
@@ -623,12 +642,12 @@ hipError_t launch_kv_quant(const Problem& p, const void* k, const void* v, const
   a.ksc = w.ksc;
   a.vsc = w.vsc;
   a.ds_scale = ds_scale;
-  a.M = p.M;
   a.Mp = p.Mp;
   a.nkt = p.nkt;
   a.nqb = p.nqb;
   a.causal = p.causal;
-  a.coff = p.coff;
+  a.ql = p.ql;
+  a.kl = p.kl;
   a.H = p.H;
   a.Hkv = p.Hkv;
   a.G = p.G;

@@ -118,7 +118,6 @@ int make_problem(int B, int H, int Hkv, int N, int M, int d, int causal, float s
   if ((long long)B * H > (1LL << 30)) return SAGE_ERR_INVALID_ARG;
   p->B = B; p->H = H; p->Hkv = Hkv; p->G = H / Hkv; p->N = N; p->M = M; p->d = d;
   p->causal = causal;
-  p->coff = causal == 2 ? M - N : 0;
   p->sm_scale = (sm_scale > 0.0f && std::isfinite(sm_scale)) ? sm_scale : 1.0f / std::sqrt((float)d);
   p->variant = variant;
   p->BH = B * H;
@@ -132,6 +131,8 @@ int make_problem(int B, int H, int Hkv, int N, int M, int d, int causal, float s
   p->smooth_v = (variant & SAGE_SMOOTH_V) != 0;
   p->mx = (variant & SAGE_PATH_MXFP4) != 0;
   p->qf8 = (variant & SAGE_QK_FP8) != 0;
+  p->ql = {nullptr, N, 0};
+  p->kl = {nullptr, M, 0};
   // grid limits: y = B*H (or B*Hkv) for the preprocessing kernels, x = blocks/tiles
   if (p->BH > 65535 || p->nkt > (1 << 30)) return SAGE_ERR_INVALID_ARG;
   return SAGE_OK;
@@ -140,6 +141,27 @@ int make_problem(int B, int H, int Hkv, int N, int M, int d, int causal, float s
 int make_problem(const sage_attn_shape* sh, Problem* p) {
   if (!sh) return SAGE_ERR_INVALID_ARG;
   return make_problem(sh->B, sh->Hq, sh->Hkv, sh->N, sh->M, sh->d, sh->causal, sh->sm_scale, sh->variant, p);
+}
+
+// A variable-length batch is the dense problem with B = batch and N, M = the length bounds
+// (the workspace is laid out for them); the kernels read each sequence's rows and lengths
+// through the offsets.  causal = 2 with N > M is allowed here: the rows of a sequence that see
+// no key are written as 0.
+int make_problem(const sage_attn_varlen_shape* sh, Problem* p) {
+  if (!sh || !sh->cu_seqlens_q || !sh->cu_seqlens_k) return SAGE_ERR_INVALID_ARG;
+  if (sh->total_q < 1 || sh->total_k < 1) return SAGE_ERR_INVALID_ARG;
+  if ((reinterpret_cast<uintptr_t>(sh->cu_seqlens_q) | reinterpret_cast<uintptr_t>(sh->cu_seqlens_k)) & 3u)
+    return SAGE_ERR_INVALID_ARG;
+  const int causal_check = sh->causal == 2 ? 1 : sh->causal;  // N > M is not an error here
+  int rc = make_problem(sh->batch, sh->Hq, sh->Hkv, sh->max_seqlen_q, sh->max_seqlen_k, sh->d, causal_check,
+                        sh->sm_scale, sh->variant, p);
+  if (rc != SAGE_OK) return rc;
+  if ((double)sh->total_q * sh->Hq * sh->d >= 1099511627776.0 || (double)sh->total_k * sh->Hkv * sh->d >= 1099511627776.0)
+    return SAGE_ERR_INVALID_ARG;
+  p->causal = sh->causal;
+  p->ql = {sh->cu_seqlens_q, sh->max_seqlen_q, sh->total_q};
+  p->kl = {sh->cu_seqlens_k, sh->max_seqlen_k, sh->total_k};
+  return SAGE_OK;
 }
 
 bool aligned16(const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) == 0; }
@@ -178,6 +200,29 @@ int check_io(const void* q, const void* k, const void* v, const void* out) {
   return SAGE_OK;
 }
 
+// The forward of a resolved problem: argument checks, then the caller's workspace or a
+// stream-ordered one.
+int fwd_checked(const Problem& p, const void* q, const void* k, const void* v, void* out, void* workspace,
+                size_t ws_bytes, void* stream) {
+  int rc = check_io(q, k, v, out);
+  if (rc != SAGE_OK) return rc;
+  if (workspace) {
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return SAGE_ERR_INVALID_ARG;
+    if (ws_bytes < workspace_layout(p, nullptr)) return SAGE_ERR_NO_MEMORY;
+  }
+  if ((rc = device_check()) != SAGE_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  if (workspace) return fwd_impl(q, k, v, out, p, workspace, s);
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, workspace_layout(p, nullptr), s) != hipSuccess || !ws) {
+    (void)hipGetLastError();
+    return SAGE_ERR_NO_MEMORY;
+  }
+  rc = fwd_impl(q, k, v, out, p, ws, s);
+  if (hipFreeAsync(ws, s) != hipSuccess && rc == SAGE_OK) rc = SAGE_ERR_LAUNCH;
+  return rc;
+}
+
 }  // namespace
 }  // namespace sage
 
@@ -199,24 +244,8 @@ size_t sage_attn_workspace_bytes(int B, int H, int N, int M, int d, int causal, 
 int sage_attn_fwd_ex(const sage_attn_shape* shape, const void* q, const void* k, const void* v, void* out,
                      void* workspace, size_t ws_bytes, void* stream) {
   Problem p;
-  int rc = make_problem(shape, &p);
-  if (rc != SAGE_OK) return rc;
-  if ((rc = check_io(q, k, v, out)) != SAGE_OK) return rc;
-  if (workspace) {
-    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return SAGE_ERR_INVALID_ARG;
-    if (ws_bytes < workspace_layout(p, nullptr)) return SAGE_ERR_NO_MEMORY;
-  }
-  if ((rc = device_check()) != SAGE_OK) return rc;
-  hipStream_t s = (hipStream_t)stream;
-  if (workspace) return fwd_impl(q, k, v, out, p, workspace, s);
-  void* ws = nullptr;
-  if (hipMallocAsync(&ws, workspace_layout(p, nullptr), s) != hipSuccess || !ws) {
-    (void)hipGetLastError();
-    return SAGE_ERR_NO_MEMORY;
-  }
-  rc = fwd_impl(q, k, v, out, p, ws, s);
-  if (hipFreeAsync(ws, s) != hipSuccess && rc == SAGE_OK) rc = SAGE_ERR_LAUNCH;
-  return rc;
+  const int rc = make_problem(shape, &p);
+  return rc != SAGE_OK ? rc : fwd_checked(p, q, k, v, out, workspace, ws_bytes, stream);
 }
 
 int sage_attn_fwd_ws(const void* q, const void* k, const void* v, void* out, int B, int H, int N,
@@ -231,6 +260,19 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B,
                   int d, int causal, float sm_scale, unsigned variant, void* stream) {
   const sage_attn_shape sh = {B, H, H, N, M, d, causal, sm_scale, variant};
   return sage_attn_fwd_ex(&sh, q, k, v, out, nullptr, 0, stream);
+}
+
+size_t sage_attn_varlen_workspace_bytes(const sage_attn_varlen_shape* shape) {
+  Problem p;
+  if (make_problem(shape, &p) != SAGE_OK) return 0;
+  return workspace_layout(p, nullptr);
+}
+
+int sage_attn_varlen_fwd(const sage_attn_varlen_shape* shape, const void* q, const void* k, const void* v, void* out,
+                         void* workspace, size_t ws_bytes, void* stream) {
+  Problem p;
+  const int rc = make_problem(shape, &p);
+  return rc != SAGE_OK ? rc : fwd_checked(p, q, k, v, out, workspace, ws_bytes, stream);
 }
 
 int sage_attn_quantize_ex(const sage_attn_shape* shape, const void* q, const void* k, const void* v,

@@ -21,18 +21,43 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
+// Where the rows of one (sequence, head) of a q / k / v / out tensor live.  Dense tensors are
+// [B][H][T][d]; packed ones (variable-length batches) are [total][H][d], sequence b in rows
+// cu[b] .. cu[b+1]-1.
+struct SeqLayout {
+  const int* cu;  // device offsets of the B + 1 sequence starts; null: dense
+  int T;          // dense: tokens per sequence; packed: the bound on a sequence's length
+  int total;      // packed: rows of the tensor
+};
+struct SeqRows {
+  size_t base;    // element offset of (token 0, channel 0)
+  size_t stride;  // elements from one token to the next
+  int len;        // tokens of this sequence
+};
+// A packed sequence's offsets are clamped to [0, total] and its length to T, so that no
+// offset array, however malformed, moves an access outside the tensor or the workspace.
+__device__ inline SeqRows seq_rows(const SeqLayout& L, int b, int h, int H, int d) {
+  if (L.cu == nullptr) return {((size_t)b * H + h) * (size_t)L.T * d, (size_t)d, L.T};
+  int s = L.cu[b], e = L.cu[b + 1];
+  s = s < 0 ? 0 : (s > L.total ? L.total : s);
+  e = e < s ? s : (e > L.total ? L.total : e);
+  return {((size_t)s * H + h) * d, (size_t)H * d, e - s < L.T ? e - s : L.T};
+}
+
 // Resolved problem: sizes, padded sizes and the variant bits.
 struct Problem {
   int B, H, N, M, d;
   int Hkv, G;  // key/value heads; query head h reads key/value head h / G (G = H / Hkv)
   int causal;  // 0 none, 1 first query aligned with the first key, 2 last with the last
-  int coff;    // causal: key t is visible to query r iff t <= r + coff (0, or M - N)
   float sm_scale;
   unsigned variant;
   int BH, BHkv, nqb, nkt, Np, Mp;  // BH = B*H query heads, BHkv = B*Hkv key/value heads
   bool fp16, out_fp32, smooth_v;
   bool mx;  // SAGE_PATH_MXFP4
   bool qf8;  // SAGE_QK_FP8
+  // Rows of q / out (ql) and of k, v (kl): dense [B][H][T][d], or packed [total][H][d] for a
+  // variable-length batch (then N and M are the bounds on the sequence lengths)
+  SeqLayout ql, kl;
 };
 
 // Device workspace (all 256-byte aligned slices of one allocation).  Layouts of the

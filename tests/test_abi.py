@@ -21,7 +21,8 @@ def test_header_declares_the_boundary():
     assert names == sorted(["sage_attn_fwd", "sage_attn_fwd_ws", "sage_attn_workspace_bytes",
                             "sage_attn_quantize", "sage_attn_set_profile_events",
                             "sage_attn_status_string", "sage_attn_version", "sage_attn_fwd_ex",
-                            "sage_attn_workspace_bytes_ex", "sage_attn_quantize_ex"])
+                            "sage_attn_workspace_bytes_ex", "sage_attn_quantize_ex",
+                            "sage_attn_varlen_workspace_bytes", "sage_attn_varlen_fwd"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -97,3 +98,33 @@ def test_workspace_grows_with_problem():
     assert 0 < a < b
     # dominated by Delta S (nqb * Mp floats per head) and the three quantized tensors
     assert b < 2 * 1024 ** 3
+
+
+def test_varlen_shape_checks():
+    V = qa.SageAttnVarlenShape
+    A = 256  # stand-in device addresses, never dereferenced on these paths
+
+    def shape(**kw):
+        f = dict(batch=3, Hq=4, Hkv=2, d=64, total_q=500, total_k=700, max_seqlen_q=300, max_seqlen_k=400,
+                 cu_seqlens_q=A, cu_seqlens_k=A + 64, causal=1, sm_scale=0.0, variant=0)
+        f.update(kw)
+        return V(**f)
+
+    # the workspace is the dense layout of `batch` sequences of the bound lengths
+    assert qa.sage_attn_varlen_workspace_bytes(shape()) == qa.sage_attn_workspace_bytes_ex(
+        qa.SageAttnShape(3, 4, 2, 300, 400, 64, 1, 0.0, 0))
+    # causal = 2 with a longer query bound is allowed (rows without keys are written as 0)
+    assert qa.sage_attn_varlen_workspace_bytes(shape(causal=2, max_seqlen_q=500, max_seqlen_k=100)) > 0
+    bad = [shape(batch=0), shape(total_q=0), shape(total_k=0), shape(max_seqlen_q=0), shape(Hkv=3),
+           shape(cu_seqlens_q=None), shape(cu_seqlens_k=None), shape(cu_seqlens_q=A + 2), shape(causal=3),
+           shape(variant=qa.SAGE_PATH_MXFP4 | qa.SAGE_QK_FP8)]
+    for s in bad:
+        assert qa.sage_attn_varlen_workspace_bytes(s) == 0
+        assert qa.sage_attn_varlen_fwd(s, A, A, A, A, None, 0, None) == qa.SAGE_ERR_INVALID_ARG
+    assert qa.sage_attn_varlen_workspace_bytes(shape(d=96)) == 0
+    assert qa.sage_attn_varlen_fwd(shape(d=96), A, A, A, A, None, 0, None) == qa.SAGE_ERR_UNSUPPORTED
+    assert qa.sage_attn_varlen_workspace_bytes(None) == 0
+    ws = qa.sage_attn_varlen_workspace_bytes(shape())
+    assert qa.sage_attn_varlen_fwd(shape(), A, A, A, A, A, ws - 1, None) == qa.SAGE_ERR_NO_MEMORY
+    assert qa.sage_attn_varlen_fwd(shape(), A + 8, A, A, A, None, 0, None) == qa.SAGE_ERR_INVALID_ARG
+
