@@ -17,6 +17,7 @@ import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "sage_oracle.c")
+SOURCES = [SRC, os.path.join(HERE, "sagebwd_oracle.c"), os.path.join(HERE, "sage_oracle.h")]
 LIB = os.path.join(HERE, "liboracle.so")
 
 BQ, BK = 128, 64
@@ -35,12 +36,16 @@ MXFP4 = 0x1000
 QK_E4M3 = 0x2000  # Q^, K^ in E4M3 (scale amax / 448, same groups); khat, qhat then hold E4M3 codes
 
 
+def _stale() -> bool:
+    return not os.path.exists(LIB) or any(os.path.getmtime(LIB) < os.path.getmtime(f) for f in SOURCES)
+
+
 def build(force: bool = True) -> str:
     """Compile the oracle with gcc (plain C11, no fast-math, no FP contraction)."""
-    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+    if force or _stale():
         tmp = LIB + ".tmp"
         cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
-               "-fno-fast-math", SRC, "-o", tmp, "-lm"]
+               "-fno-fast-math", *[f for f in SOURCES if f.endswith(".c")], "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, LIB)
     return LIB
@@ -52,7 +57,7 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        if _stale():
             build(force=True)
         L = ctypes.CDLL(LIB)
         P = ctypes.c_void_p
@@ -87,6 +92,12 @@ def lib():
         L.orc_fp16_to_f32.restype = ctypes.c_float
         L.orc_k_group.argtypes = [i]
         L.orc_k_group.restype = i
+        L.orc_sagebwd_forward.argtypes = [P, P, P, i, i, i, i, i, dbl, u, P, P]
+        L.orc_sagebwd_forward.restype = i
+        L.orc_sagebwd_backward.argtypes = [P, P, P, P, i, i, i, i, i, dbl, u, P, P, P, P, P]
+        L.orc_sagebwd_backward.restype = i
+        L.orc_sagebwd_quantize.argtypes = [P, P, P, P, i, i, i, i, u] + [P] * 9
+        L.orc_sagebwd_quantize.restype = i
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = i
         _lib = L
@@ -188,6 +199,57 @@ def exact_f64(q, k, v, causal: int, sm_scale: float):
     if rc != 0:
         raise ValueError("orc_exact_f64 rejected its arguments")
     return out
+
+
+SB_IDENTITY = 0x1     # SageBwd: no quantizer anywhere
+SB_NO_SMOOTH_K = 0x2  # SageBwd ablation: skip K - mean(K)
+SB_DP_INT8 = 0x4      # SageBwd ablation: dP = dO V^T from per-block INT8 dO and V
+
+
+def sagebwd_forward(q, k, v, fp16: bool, causal: int, sm_scale: float, flags: int = 0):
+    """SageBwd forward of one head: (out [N][d], lse [N]) in FP64."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    N, d = q.shape
+    M = k.shape[0]
+    out, lse = np.zeros((N, d)), np.zeros(N)
+    rc = lib().orc_sagebwd_forward(_ptr(q), _ptr(k), _ptr(v), int(fp16), N, M, d, int(causal), float(sm_scale),
+                                   flags, _ptr(out), _ptr(lse))
+    if rc != 0:
+        raise ValueError("orc_sagebwd_forward rejected its arguments")
+    return out, lse
+
+
+def sagebwd_backward(q, k, v, dout, fp16: bool, causal: int, sm_scale: float, flags: int = 0) -> dict:
+    """SageBwd forward and backward of one head: out, lse, dq, dk, dv in FP64."""
+    q, k, v, dout = _u16(q), _u16(k), _u16(v), _u16(dout)
+    N, d = q.shape
+    M = k.shape[0]
+    o = dict(out=np.zeros((N, d)), lse=np.zeros(N), dq=np.zeros((N, d)), dk=np.zeros((M, d)), dv=np.zeros((M, d)))
+    rc = lib().orc_sagebwd_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), int(fp16), N, M, d, int(causal),
+                                    float(sm_scale), flags, *[_ptr(o[n]) for n in ("out", "lse", "dq", "dk", "dv")])
+    if rc != 0:
+        raise ValueError("orc_sagebwd_backward rejected its arguments")
+    return o
+
+
+def sagebwd_quantize(q, k, v, dout, fp16: bool, flags: int = 0) -> dict:
+    """SageBwd's INT8 codes and block scales of one head (dout may be None)."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    dout = _u16(dout) if dout is not None else None
+    N, d = q.shape
+    M = k.shape[0]
+    nqb, nkt = -(-N // BQ), -(-M // BK)
+    o = dict(qcode=np.zeros((N, d), np.int8), sq=np.zeros(nqb, np.float32), kcode=np.zeros((M, d), np.int8),
+             sk=np.zeros(nkt, np.float32), vcode=np.zeros((M, d), np.int8), sv=np.zeros(nkt, np.float32),
+             docode=np.zeros((N, d), np.int8), sdo=np.zeros(nqb, np.float32), kmean=np.zeros(d, np.float32))
+    rc = lib().orc_sagebwd_quantize(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), int(fp16), N, M, d, flags,
+                                    *[_ptr(o[n]) for n in ("qcode", "sq", "kcode", "sk", "vcode", "sv", "docode",
+                                                           "sdo", "kmean")])
+    if rc != 0:
+        raise ValueError("orc_sagebwd_quantize rejected its arguments")
+    if dout is None:
+        del o["docode"], o["sdo"]
+    return o
 
 
 def e4m3_decode_table() -> np.ndarray:

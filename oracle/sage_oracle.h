@@ -90,6 +90,26 @@ int orc_preprocess_mx_head(const uint16_t* q, const uint16_t* k, const uint16_t*
                            int N, int M, int d, unsigned flags,
                            uint8_t* qcode, int* qexp, uint8_t* kcode, int* kexp,
                            uint8_t* vcode, int* vexp);
+/* ---- SageBwd (trainable INT8 attention; sagebwd_oracle.c): forward with the row
+ * log-sum-exp, and the backward, for one head.  q, dout: [N][d], k, v: [M][d] raw 16-bit
+ * codes; causal as orc_forward_head.  Outputs in FP64: out [N][d], lse [N] (natural log, of
+ * the scores after K smoothing), dq [N][d], dk, dv [M][d].  The backward runs the forward
+ * itself (out and lse are written by both calls).  Returns 0, or -1 on a bad argument. */
+#define ORC_SB_IDENTITY    0x0001u /* no quantizer anywhere: exact attention and its gradients    */
+#define ORC_SB_NO_SMOOTH_K 0x0002u /* ablation: skip K - mean(K)                                   */
+#define ORC_SB_DP_INT8     0x0004u /* ablation: dP = dO V^T from per-block INT8 dO and V           */
+int orc_sagebwd_forward(const uint16_t* q, const uint16_t* k, const uint16_t* v, int in_fp16, int N, int M, int d,
+                        int causal, double sm_scale, unsigned flags, double* out, double* lse);
+int orc_sagebwd_backward(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
+                         int in_fp16, int N, int M, int d, int causal, double sm_scale, unsigned flags,
+                         double* out, double* lse, double* dq, double* dk, double* dv);
+/* SageBwd's quantized tensors: INT8 codes of Q, dO per 128 rows and of smoothed K, V per 64
+ * keys, the FP32 block scales, and the K mean.  Any output may be NULL (dout too). */
+int orc_sagebwd_quantize(const uint16_t* q, const uint16_t* k, const uint16_t* v, const uint16_t* dout,
+                         int in_fp16, int N, int M, int d, unsigned flags, int8_t* qcode, float* sq,
+                         int8_t* kcode, float* sk, int8_t* vcode, float* sv, int8_t* docode, float* sdo,
+                         float* kmean);
+
 /* ---- forward of one head: the quantized method, FP64 everywhere it is not quantized ----
  * rows: the query rows to produce (NULL with nrows = N means all rows in order);
  * out: [nrows][d] in FP64.  causal: 0 none; 1 key t visible to row r iff t <= r (first
