@@ -249,6 +249,37 @@ int sage_attn_varlen_fwd(const sage_attn_varlen_shape* shape, const void* q, con
                          void* out, void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * SageBwd, the trainable 8-bit attention ("SageAttention3: Microscaling FP4 Attention for
+ * Inference and An Exploration of 8-Bit Training" summary, "SageBwd Forward Pass: INT8
+ * Quantization for Training" and "SageBwd Backward Pass and the Critical dOV^T Decision").
+ * A method of its own, beside the inference path above:
+ *   forward  K smoothed (K - mean(K)); Q per 128 rows, K and V per 64 keys quantized to INT8
+ *            (scale max|X| / 127); S = Q^ K^T s_Q s_K sm_scale; P per (row, 64-key block) to
+ *            INT8 against the row's block max of P; O = sum P^ V^ s_P s_V / l, and the row's
+ *            log-sum-exp L = m + ln l (natural log, of the scores after K smoothing: it differs
+ *            from that of Q K^T by sm_scale q . mean(K));
+ *   backward D = rowsum(dO o O); per (128-query, 64-key) block S again and P = exp(S - L), P
+ *            and dS = P o (dP - D) quantized per block to INT8; dV = P^^T dO^ (dO per 128
+ *            rows), dP = dO V^T from the 16-bit inputs (not quantized), dQ = dS^ K^ sm_scale
+ *            + sm_scale rowsum(dS) mean(K), dK = dS^^T Q^ sm_scale.
+ * Shapes as sage_attn_shape with Hkv = Hq (grouped heads: SAGE_ERR_UNSUPPORTED), d 64 or 128,
+ * causal 0, 1 or 2 (2 needs N <= M).  variant: SAGE_IN_BF16 / SAGE_IN_FP16, SAGE_OUT_FP32 (the
+ * dtype of out, which the backward reads back in the same dtype), SAGE_TRAIN_NO_SMOOTH_K;
+ * other bits are SAGE_ERR_INVALID_ARG.  q, dout [B][H][N][d], k, v [B][H][M][d] (16-bit);
+ * lse [B][H][N] FP32; dq [B][H][N][d], dk, dv [B][H][M][d] FP32.  workspace: NULL for a
+ * stream-ordered allocation, else a 256-byte aligned buffer of
+ * sage_attn_train_workspace_bytes() bytes (enough for either call).  All pointers are device
+ * pointers, 16-byte aligned (lse 4-byte); outputs must not overlap inputs.
+ */
+#define SAGE_TRAIN_NO_SMOOTH_K 0x4000u /* ablation: K is not smoothed (training entry points) */
+size_t sage_attn_train_workspace_bytes(const sage_attn_shape* shape);
+int sage_attn_train_fwd(const sage_attn_shape* shape, const void* q, const void* k, const void* v, void* out,
+                        float* lse, void* workspace, size_t ws_bytes, void* stream);
+int sage_attn_train_bwd(const sage_attn_shape* shape, const void* q, const void* k, const void* v,
+                        const void* out, const void* dout, const float* lse, float* dq, float* dk, float* dv,
+                        void* workspace, size_t ws_bytes, void* stream);
+
+/*
  * sage_attn_set_profile_events -- measurement hook.  With both arguments non-NULL (two
  * hipEvent_t handles), the next sage_attn_fwd / sage_attn_fwd_ws call on this thread
  * records `start` on its stream just before the fused attention kernel and `stop` just

@@ -23,6 +23,8 @@ __all__ = [
     "sage_attn_version", "sage_attn_set_profile_events", "sage_attn", "QuantViews",
     "SageAttnShape", "sage_attn_fwd_ex", "sage_attn_workspace_bytes_ex", "sage_attn_quantize_ex",
     "SageAttnVarlenShape", "sage_attn_varlen_workspace_bytes", "sage_attn_varlen_fwd", "sage_attn_varlen",
+    "SAGE_TRAIN_NO_SMOOTH_K", "sage_attn_train_workspace_bytes", "sage_attn_train_fwd", "sage_attn_train_bwd",
+    "sage_attn_train_forward", "sage_attn_train_backward", "SageBwdAttention",
 ]
 
 SAGE_OK = 0
@@ -41,6 +43,7 @@ SAGE_IN_FP16 = 0x0100
 SAGE_OUT_SAME = 0x0000
 SAGE_OUT_FP32 = 0x1000
 SAGE_ACC_VALU = 0x2000
+SAGE_TRAIN_NO_SMOOTH_K = 0x4000
 
 SAGE_BQ = 128
 SAGE_BK = 64
@@ -120,6 +123,12 @@ def load_library():
     L.sage_attn_varlen_workspace_bytes.restype = sz
     L.sage_attn_varlen_fwd.argtypes = [VP, P, P, P, P, P, sz, P]
     L.sage_attn_varlen_fwd.restype = i
+    L.sage_attn_train_workspace_bytes.argtypes = [SP]
+    L.sage_attn_train_workspace_bytes.restype = sz
+    L.sage_attn_train_fwd.argtypes = [SP, P, P, P, P, P, P, sz, P]
+    L.sage_attn_train_fwd.restype = i
+    L.sage_attn_train_bwd.argtypes = [SP, P, P, P, P, P, P, P, P, P, P, sz, P]
+    L.sage_attn_train_bwd.restype = i
     _lib = L
     return L
 
@@ -167,6 +176,19 @@ def sage_attn_varlen_workspace_bytes(shape) -> int:
 
 def sage_attn_varlen_fwd(shape, q, k, v, out, workspace, ws_bytes, stream) -> int:
     return load_library().sage_attn_varlen_fwd(_shape_ptr(shape), q, k, v, out, workspace, ws_bytes, stream)
+
+
+def sage_attn_train_workspace_bytes(shape) -> int:
+    return load_library().sage_attn_train_workspace_bytes(_shape_ptr(shape))
+
+
+def sage_attn_train_fwd(shape, q, k, v, out, lse, workspace, ws_bytes, stream) -> int:
+    return load_library().sage_attn_train_fwd(_shape_ptr(shape), q, k, v, out, lse, workspace, ws_bytes, stream)
+
+
+def sage_attn_train_bwd(shape, q, k, v, out, dout, lse, dq, dk, dv, workspace, ws_bytes, stream) -> int:
+    return load_library().sage_attn_train_bwd(_shape_ptr(shape), q, k, v, out, dout, lse, dq, dk, dv, workspace,
+                                              ws_bytes, stream)
 
 
 def sage_attn_set_profile_events(start, stop) -> None:
@@ -286,3 +308,94 @@ def sage_attn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max
     if rc != SAGE_OK:
         raise SageError(rc, "sage_attn_varlen_fwd")
     return out
+
+
+# ---------------------------------------------------------------- SageBwd (training)
+def _train_shape(q, k, causal, sm_scale, out_fp32, smooth_k):
+    import torch
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, T, d]")
+    B, H, N, d = q.shape
+    M = k.shape[2]
+    var = (SAGE_IN_FP16 if q.dtype == torch.float16 else SAGE_IN_BF16) | (SAGE_OUT_FP32 if out_fp32 else 0)
+    if not smooth_k:
+        var |= SAGE_TRAIN_NO_SMOOTH_K
+    scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(d)
+    return SageAttnShape(B, H, H, N, M, d, int(causal), scale, var)
+
+
+def _check_train_inputs(*ts):
+    import torch
+    for t in ts:
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous device tensors")
+        if t.dtype not in (torch.bfloat16, torch.float16):
+            raise TypeError("q, k, v, dout must be bf16 or fp16")
+    if len({t.dtype for t in ts}) != 1:
+        raise TypeError("q, k, v, dout must share a dtype")
+
+
+def sage_attn_train_forward(q, k, v, causal: int = 0, sm_scale: float | None = None, out_fp32: bool = False,
+                            smooth_k: bool = True):
+    """SageBwd forward: (out [B, H, N, d], lse [B, H, N] FP32) for q [B, H, N, d], k/v [B, H, M, d]."""
+    import torch
+    _check_train_inputs(q, k, v)
+    shape = _train_shape(q, k, causal, sm_scale, out_fp32, smooth_k)
+    B, H, N, d = q.shape
+    out = torch.empty((B, H, N, d), dtype=torch.float32 if out_fp32 else q.dtype, device=q.device)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = sage_attn_train_fwd(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), None,
+                             0, stream)
+    if rc != SAGE_OK:
+        raise SageError(rc, "sage_attn_train_fwd")
+    return out, lse
+
+
+def sage_attn_train_backward(q, k, v, out, dout, lse, causal: int = 0, sm_scale: float | None = None,
+                             smooth_k: bool = True):
+    """SageBwd backward: (dq, dk, dv) in FP32, from the forward's out (its dtype) and lse."""
+    import torch
+    _check_train_inputs(q, k, v, dout)
+    shape = _train_shape(q, k, causal, sm_scale, out.dtype == torch.float32, smooth_k)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    rc = sage_attn_train_bwd(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), None, 0, stream)
+    if rc != SAGE_OK:
+        raise SageError(rc, "sage_attn_train_bwd")
+    return dq, dk, dv
+
+
+def _sagebwd_function():
+    import torch
+
+    class SageBwdAttention(torch.autograd.Function):
+        """softmax(Q K^T sm_scale) V with SageBwd's INT8 forward and backward, as a torch op.
+
+        apply(q, k, v, causal=0, sm_scale=None); gradients come back in the input dtype."""
+
+        @staticmethod
+        def forward(ctx, q, k, v, causal=0, sm_scale=None):
+            q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+            out, lse = sage_attn_train_forward(q, k, v, causal, sm_scale)
+            ctx.save_for_backward(q, k, v, out, lse)
+            ctx.causal, ctx.sm_scale = causal, sm_scale
+            return out
+
+        @staticmethod
+        def backward(ctx, dout):
+            q, k, v, out, lse = ctx.saved_tensors
+            dq, dk, dv = sage_attn_train_backward(q, k, v, out, dout.contiguous().to(q.dtype), lse, ctx.causal,
+                                                  ctx.sm_scale)
+            return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None
+
+    return SageBwdAttention
+
+
+def __getattr__(name):
+    if name == "SageBwdAttention":
+        return _sagebwd_function()
+    raise AttributeError(name)

@@ -223,6 +223,37 @@ int fwd_checked(const Problem& p, const void* q, const void* k, const void* v, v
   return rc;
 }
 
+// SageBwd problems: the dense shape with Hkv = Hq; the variant carries the input and output
+// dtypes and the K-smoothing ablation.
+int make_train_problem(const sage_attn_shape* sh, Problem* p, bool* smooth_k) {
+  if (!sh) return SAGE_ERR_INVALID_ARG;
+  if (sh->variant & ~(SAGE_IN_FP16 | SAGE_OUT_FP32 | SAGE_TRAIN_NO_SMOOTH_K)) return SAGE_ERR_INVALID_ARG;
+  const int rc = make_problem(sh->B, sh->Hq, sh->Hkv, sh->N, sh->M, sh->d, sh->causal, sh->sm_scale,
+                              sh->variant & ~SAGE_TRAIN_NO_SMOOTH_K, p);
+  if (rc != SAGE_OK) return rc;
+  if (sh->Hkv != sh->Hq) return SAGE_ERR_UNSUPPORTED;
+  *smooth_k = (sh->variant & SAGE_TRAIN_NO_SMOOTH_K) == 0;
+  return SAGE_OK;
+}
+
+// A caller's workspace, or a stream-ordered one for the duration of `body`.
+template <typename F>
+int with_workspace(size_t need, void* workspace, size_t ws_bytes, hipStream_t s, F&& body) {
+  if (workspace) {
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return SAGE_ERR_INVALID_ARG;
+    if (ws_bytes < need) return SAGE_ERR_NO_MEMORY;
+    return body(static_cast<char*>(workspace));
+  }
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, need, s) != hipSuccess || !ws) {
+    (void)hipGetLastError();
+    return SAGE_ERR_NO_MEMORY;
+  }
+  int rc = body(static_cast<char*>(ws));
+  if (hipFreeAsync(ws, s) != hipSuccess && rc == SAGE_OK) rc = SAGE_ERR_LAUNCH;
+  return rc;
+}
+
 }  // namespace
 }  // namespace sage
 
@@ -311,6 +342,52 @@ int sage_attn_quantize(const void* q, const void* k, const void* v, int B, int H
                        int causal, unsigned variant, const sage_quant_views* dst, void* stream) {
   const sage_attn_shape sh = {B, H, H, N, M, d, causal, 0.0f, variant};
   return sage_attn_quantize_ex(&sh, q, k, v, dst, stream);
+}
+
+size_t sage_attn_train_workspace_bytes(const sage_attn_shape* shape) {
+  Problem p;
+  bool smooth_k;
+  if (make_train_problem(shape, &p, &smooth_k) != SAGE_OK) return 0;
+  return sb_layout(p, true, nullptr);
+}
+
+int sage_attn_train_fwd(const sage_attn_shape* shape, const void* q, const void* k, const void* v, void* out,
+                        float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  Problem p;
+  bool smooth_k;
+  int rc = make_train_problem(shape, &p, &smooth_k);
+  if (rc != SAGE_OK) return rc;
+  if ((rc = check_io(q, k, v, out)) != SAGE_OK) return rc;
+  if (!lse || (reinterpret_cast<uintptr_t>(lse) & 3u)) return SAGE_ERR_INVALID_ARG;
+  if (workspace && ws_bytes < sb_layout(p, true, nullptr)) return SAGE_ERR_NO_MEMORY;
+  if ((rc = device_check()) != SAGE_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  return with_workspace(sb_layout(p, false, nullptr), workspace, ws_bytes, s, [&](char* ws) {
+    if (sb_prep_fwd(p, q, k, v, ws, false, smooth_k, s) != hipSuccess) return (int)SAGE_ERR_LAUNCH;
+    if (sb_forward(p, ws, false, out, lse, s) != hipSuccess) return (int)SAGE_ERR_LAUNCH;
+    return (int)SAGE_OK;
+  });
+}
+
+int sage_attn_train_bwd(const sage_attn_shape* shape, const void* q, const void* k, const void* v, const void* out,
+                        const void* dout, const float* lse, float* dq, float* dk, float* dv, void* workspace,
+                        size_t ws_bytes, void* stream) {
+  Problem p;
+  bool smooth_k;
+  int rc = make_train_problem(shape, &p, &smooth_k);
+  if (rc != SAGE_OK) return rc;
+  if ((rc = check_io(q, k, v, out)) != SAGE_OK) return rc;
+  if (!dout || !dq || !dk || !dv || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return SAGE_ERR_INVALID_ARG;
+  if (!lse || (reinterpret_cast<uintptr_t>(lse) & 3u)) return SAGE_ERR_INVALID_ARG;
+  if ((rc = device_check()) != SAGE_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  return with_workspace(sb_layout(p, true, nullptr), workspace, ws_bytes, s, [&](char* ws) {
+    if (sb_prep_fwd(p, q, k, v, ws, true, smooth_k, s) != hipSuccess) return (int)SAGE_ERR_LAUNCH;
+    if (sb_prep_bwd(p, out, dout, lse, ws, s) != hipSuccess) return (int)SAGE_ERR_LAUNCH;
+    if (sb_backward(p, ws, smooth_k, v, dout, dq, dk, dv, s) != hipSuccess) return (int)SAGE_ERR_LAUNCH;
+    return (int)SAGE_OK;
+  });
 }
 
 void sage_attn_set_profile_events(void* start, void* stop) {

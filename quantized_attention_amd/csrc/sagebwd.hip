@@ -1,0 +1,803 @@
+// sagebwd.hip -- SageBwd, the trainable 8-bit attention (gfx950): preprocessing, the forward
+// with the row log-sum-exp, and the backward.
+//
+// "SageAttention3: Microscaling FP4 Attention for Inference and An Exploration of 8-Bit
+// Training" summary, "SageBwd Forward Pass: INT8 Quantization for Training" and "SageBwd
+// Backward Pass and the Critical dOV^T Decision":
+//   forward   K <- K - mean(K); Q (128 rows), K, V (64 keys) quantized per block to INT8;
+//             S = Q^ K^T s_Q s_K sm; online softmax; P per (row, key block) to INT8 with
+//             s_P = (the row's block max of P) / 127; O += P^ V^ s_P s_V;  L = m + ln l
+//   backward  D = rowsum(dO o O); per (query block i, key block j): S again, P = exp(S - L),
+//             P^ per block; dV_j += P^^T dO^_i;  dP = dO_i V_j^T on 16-bit inputs;
+//             dS = P o (dP - D), dS^ per block;  dQ_i += dS^ K^_j;  dK_j += dS^^T Q^_i;
+//             dQ += rowsum(dS) k (the smoothing term)
+//
+// Mapping.  Every score tile is computed transposed (S^T = K^ Q^T on v_mfma_i32_32x32x32_i8:
+// a lane owns one query, 16 keys of each 32-key half), so row quantities (L, D, the running
+// max) are per lane.  The P^ (forward) and dS^ (dQ kernel) bytes of a lane are then the B
+// operand of an INT8 MFMA whose A operand (V^T, K^T) is stored with its keys permuted to the
+// lane order (i8perm), as the FP8 P^ V^ product of the inference kernel.  The dK/dV kernel
+// writes P^ and dS^ key-major to LDS and contracts over the queries against transposed Q^ and
+// dO^ (one 32-query step per MFMA).  dP^T = V dO^T runs on the bf16 MFMA from the 16-bit
+// inputs.
+#include "attn_device.hpp"
+
+namespace sage {
+namespace {
+
+using namespace attn;
+
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLog2_127 = 6.988684686772166f;
+
+// Position p of a key-permuted 64-key row (i8perm) holds key 32T + 8(b/4) + 4h + b%4,
+// T = p / 32, h = p / 16 % 2, b = p % 16: the key that byte b of lane half h feeds into the
+// INT8 MFMA of key half T, when the B operand is a lane's 16 score-accumulator values.
+__host__ __device__ inline int i8perm(int p) {
+  const int T = p >> 5, h = (p >> 4) & 1, b = p & 15;
+  return 32 * T + 8 * (b >> 2) + 4 * h + (b & 3);
+}
+
+// ---- per-block INT8 quantization of a [T][D] tensor of one head (Q, dO: 128 rows; K, V: 64):
+// scale = max(amax, 1e-8) / 127 over the block's valid rows (K: after subtracting the mean),
+// codes into the row layout [Tp][D] (rows >= T are 0) and / or the transposed layout
+// [blocks][D][RB] (positions natural, or i8perm for 64-row blocks) ----
+template <int D, int RB, bool PERM>
+__global__ __launch_bounds__(256) void sb_quant_kernel(const uint16_t* __restrict__ src, const float* __restrict__ mean,
+                                                       int8_t* __restrict__ rows, int8_t* __restrict__ trans,
+                                                       float* __restrict__ scale, int T, int Tp, int nb, bool fp16) {
+  constexpr int CH = RB * D / 8 / 256;  // 8-element chunks per thread
+  constexpr int LS = D + 16;            // LDS code row stride (bytes)
+  __shared__ __attribute__((aligned(16))) int8_t sc[RB * LS];
+  __shared__ float wmax[4];
+  const int blk = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r0 = blk * RB, n = min(RB, T - r0);
+  const size_t base = ((size_t)bh * T + r0) * D;
+  float x[CH][8];
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < CH; i++) {
+    const int e = tid + 256 * i, r = e / (D / 8), c0 = (e % (D / 8)) * 8;
+    if (r < n) {
+      const v4i raw = *reinterpret_cast<const v4i*>(src + base + (size_t)r * D + c0);
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        const uint32_t u = static_cast<uint32_t>(raw[k]);
+        const uint16_t lo = static_cast<uint16_t>(u & 0xffffu), hi = static_cast<uint16_t>(u >> 16);
+        x[i][2 * k] = fp16 ? static_cast<float>(__builtin_bit_cast(_Float16, lo)) : __uint_as_float(u << 16);
+        x[i][2 * k + 1] = fp16 ? static_cast<float>(__builtin_bit_cast(_Float16, hi)) : __uint_as_float(u & 0xffff0000u);
+      }
+      if (mean) {
+#pragma unroll
+        for (int k = 0; k < 8; k++) x[i][k] = x[i][k] - mean[(size_t)bh * D + c0 + k];
+      }
+#pragma unroll
+      for (int k = 0; k < 8; k++) am = amax_upd(am, x[i][k]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; k++) x[i][k] = 0.0f;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float o = __shfl_xor(am, off);
+    am = o > am ? o : am;
+  }
+  if (lane == 0) wmax[wave] = am;
+  __syncthreads();
+  am = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float s = int8_scale(am);
+  if (tid == 0) scale[(size_t)bh * nb + blk] = s;
+  const float rcp = __fdiv_rn(1.0f, s);
+#pragma unroll
+  for (int i = 0; i < CH; i++) {
+    const int e = tid + 256 * i, r = e / (D / 8), c0 = (e % (D / 8)) * 8;
+    const uint2 w = (r < n) ? int8_pack8_rcp(x[i], s, rcp) : make_uint2(0u, 0u);
+    if (rows) *reinterpret_cast<uint2*>(rows + ((size_t)bh * Tp + r0 + r) * D + c0) = w;
+    *reinterpret_cast<uint2*>(&sc[r * LS + c0]) = w;
+  }
+  if (!trans) return;
+  __syncthreads();
+  // transposed: 16 positions of one channel per thread step
+  int8_t* tb = trans + ((size_t)bh * nb + blk) * (size_t)D * RB;
+  for (int e = tid; e < D * (RB / 16); e += 256) {
+    const int c = e / (RB / 16), p0 = (e % (RB / 16)) * 16;
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int k = 0; k < 4; k++) {
+        const int p = p0 + 4 * q + k;
+        const int r = PERM ? i8perm(p) : p;
+        v |= (uint32_t)(uint8_t)sc[r * LS + c] << (8 * k);
+      }
+      w[q] = v;
+    }
+    *reinterpret_cast<uint4*>(tb + (size_t)c * RB + p0) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+struct FwdArgs {
+  const int8_t* qh;  // [BH][Np][D]
+  const float* sq;   // [BH][nqb]
+  const int8_t* kh;  // [BH][Mp][D]
+  const float* sk;   // [BH][nkt]
+  const int8_t* vt;  // [BH][nkt][D][64], keys in i8perm order
+  const float* sv;   // [BH][nkt]
+  void* out;         // [BH][N][D]
+  float* lse;        // [BH][N]
+  int N, M, nqb, nkt, Np, Mp, coff;
+  float qk_scale;    // sm_scale * log2(e)
+};
+
+// ---- forward: one work-group per (head, 128-query block), wave w owns queries 32w.. ----
+template <int D, bool CAUSAL, int OUT>
+__global__ __launch_bounds__(256, 2) void sb_fwd_kernel(FwdArgs a) {
+  constexpr int NKS = D / 32;
+  constexpr int KS = D + 16, VS = kBK + 16;  // padded LDS row strides (bytes)
+  __shared__ __attribute__((aligned(16))) int8_t sK[kBK * KS];
+  __shared__ __attribute__((aligned(16))) int8_t sV[D * VS];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
+  const int bh = blockIdx.x / a.nqb, qi = blockIdx.x % a.nqb;
+  const int qb = CAUSAL ? (a.nqb - 1 - qi) : qi;
+  const int q0 = qb * kBQ, wq0 = q0 + 32 * w, qrow = wq0 + col;
+  v4i qf[NKS];
+  {
+    const int8_t* qp = a.qh + ((size_t)bh * a.Np + qrow) * D + 16 * h;
+#pragma unroll
+    for (int s = 0; s < NKS; s++) qf[s] = *reinterpret_cast<const v4i*>(qp + 32 * s);
+  }
+  const float sqk = a.sq[(size_t)bh * a.nqb + qb] * a.qk_scale;
+  v16f O[NKS];
+#pragma unroll
+  for (int c = 0; c < NKS; c++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) O[c][r] = 0.0f;
+  float m_run = -FLT_MAX, l_run = 0.0f;
+  const int jend = CAUSAL ? max(0, min(a.nkt, (q0 + kBQ + a.coff + kBK - 1) / kBK)) : a.nkt;
+  for (int j = 0; j < jend; j++) {
+    __syncthreads();  // the previous tile's LDS reads are done
+    {
+      const int8_t* kt = a.kh + ((size_t)bh * a.Mp + (size_t)j * kBK) * D;
+      const int8_t* vt = a.vt + ((size_t)bh * a.nkt + j) * (size_t)D * kBK;
+      for (int e = tid; e < kBK * D / 16; e += 256) {
+        const int r = e / (D / 16), c = (e % (D / 16)) * 16;
+        *reinterpret_cast<v4i*>(&sK[r * KS + c]) = *reinterpret_cast<const v4i*>(kt + (size_t)r * D + c);
+      }
+      for (int e = tid; e < D * kBK / 16; e += 256) {
+        const int r = e / (kBK / 16), c = (e % (kBK / 16)) * 16;
+        *reinterpret_cast<v4i*>(&sV[r * VS + c]) = *reinterpret_cast<const v4i*>(vt + (size_t)r * kBK + c);
+      }
+    }
+    __syncthreads();
+    const int key0 = j * kBK;
+    if (CAUSAL && key0 > wq0 + 31 + a.coff) continue;  // every key of the tile is masked for this wave
+    v16i acc[2];
+#pragma unroll
+    for (int T = 0; T < 2; T++) {
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[T][r] = 0;
+#pragma unroll
+      for (int s = 0; s < NKS; s++) {
+        const v4i kf = *reinterpret_cast<const v4i*>(&sK[(32 * T + col) * KS + 32 * s + 16 * h]);
+        acc[T] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[s], acc[T], 0, 0, 0);
+      }
+    }
+    const float mul = sqk * a.sk[(size_t)bh * a.nkt + j];
+    float sc[2][16];
+    int lim = a.M - 1 - key0;
+    if (CAUSAL) lim = min(lim, qrow + a.coff - key0);
+    lim -= 4 * h;
+    float rm = -INFINITY;
+#pragma unroll
+    for (int T = 0; T < 2; T++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const float x = (float)acc[T][r] * mul;
+        sc[T][r] = (32 * T + 8 * (r >> 2) + (r & 3) <= lim) ? x : -INFINITY;
+        rm = fmaxf(rm, sc[T][r]);
+      }
+    rm = pair_max(rm);  // the row's max over this tile
+    const float m_new = fmaxf(m_run, rm);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    // e = 127 P / (the row's block max of P) = 127 exp2(S - rm); P^ = rne(e)
+    const float base = (rm == -INFINITY) ? 0.0f : rm - kLog2_127;
+    float esum = 0.0f;
+    v4i pb[2];
+#pragma unroll
+    for (int T = 0; T < 2; T++)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; q4++) {
+        uint32_t wd = 0;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          const float e = fast_exp2(sc[T][4 * q4 + k] - base);
+          esum += e;
+          wd |= (uint32_t)(int)rintf(e) << (8 * k);
+        }
+        pb[T][q4] = (int)wd;
+      }
+    esum = pair_sum(esum);
+    const float sp = (rm == -INFINITY) ? 0.0f : fast_exp2(rm - m_new) * (1.0f / 127.0f);  // s_P
+    l_run = fmaf(l_run, alpha, esum * sp);
+    const float osc = sp * a.sv[(size_t)bh * a.nkt + j];
+#pragma unroll
+    for (int c = 0; c < NKS; c++) {
+      v16i R;
+#pragma unroll
+      for (int r = 0; r < 16; r++) R[r] = 0;
+#pragma unroll
+      for (int T = 0; T < 2; T++) {
+        const v4i vf = *reinterpret_cast<const v4i*>(&sV[(32 * c + col) * VS + 32 * T + 16 * h]);
+        R = __builtin_amdgcn_mfma_i32_32x32x32_i8(vf, pb[T], R, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; r++) O[c][r] = fmaf((float)R[r], osc, O[c][r] * alpha);
+    }
+  }
+  if (qrow >= a.N) return;
+  const float inv = 1.0f / l_run;
+  if (h == 0) a.lse[(size_t)bh * a.N + qrow] = (m_run + __log2f(l_run)) * kLn2;
+  const size_t orow = ((size_t)bh * a.N + qrow) * D;
+#pragma unroll
+  for (int c = 0; c < NKS; c++)
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      const int ch = 32 * c + 8 * b + 4 * h;
+      float o[4];
+#pragma unroll
+      for (int k = 0; k < 4; k++) o[k] = O[c][4 * b + k] * inv;
+      store_out4<OUT>(a.out, orow + ch, o);
+    }
+}
+
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+
+// One 32x32x16 step of dP^T = V dO^T on the MFMA of the input type (bf16 or fp16).
+template <bool FP16>
+__device__ __forceinline__ v16f mfma16(const v4i& a, const v4i& b, const v16f& c) {
+  if constexpr (FP16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0,
+                                                   0);
+}
+
+// ---- backward preprocessing: D = rowsum(dO o O) (FP64 sum), L2 = L log2(e); padded rows
+// get D = 0 and L2 = +inf (their P is 0) ----
+template <int D, int OUT>
+__global__ __launch_bounds__(256) void sb_dprep_kernel(const void* __restrict__ out, const uint16_t* __restrict__ dout,
+                                                       const float* __restrict__ lse, float* __restrict__ Dr,
+                                                       float* __restrict__ L2, int N, int Np, bool fp16) {
+  const int tid = threadIdx.x, bh = blockIdx.y;
+  const int row = blockIdx.x * kBQ + (tid >> 1), half = tid & 1;
+  double s = 0.0;
+  if (row < N) {
+    const size_t base = ((size_t)bh * N + row) * D + half * (D / 2);
+    for (int c = 0; c < D / 2; c++) {
+      const float o = OUT == 2 ? reinterpret_cast<const float*>(out)[base + c]
+                               : load_in(reinterpret_cast<const uint16_t*>(out), base + c, OUT == 1);
+      s += (double)load_in(dout, base + c, fp16) * (double)o;
+    }
+  }
+  s += __shfl_xor(s, 1);
+  if (half == 0) {
+    const size_t o = (size_t)bh * Np + row;
+    Dr[o] = row < N ? (float)s : 0.0f;
+    L2[o] = row < N ? lse[(size_t)bh * N + row] * kLog2e : INFINITY;
+  }
+}
+
+struct BwdArgs {
+  const int8_t* qh;    // [BH][Np][D] Q^ rows
+  const int8_t* qt;    // [BH][nqb][D][128] Q^ transposed
+  const float* sq;     // [BH][nqb]
+  const int8_t* kh;    // [BH][Mp][D] K^ rows
+  const int8_t* kt;    // [BH][nkt][D][64] K^ transposed, keys in i8perm order
+  const float* sk;     // [BH][nkt]
+  const int8_t* dot;   // [BH][nqb][D][128] dO^ transposed
+  const float* sdo;    // [BH][nqb]
+  const float* Dr;     // [BH][Np]
+  const float* L2;     // [BH][Np]
+  const float* kmean;  // [BH][D] (null: K not smoothed)
+  const uint16_t* V;   // [BH][M][D] 16-bit
+  const uint16_t* dO;  // [BH][N][D] 16-bit
+  float* dq;           // [BH][N][D]
+  float* dk;           // [BH][M][D]
+  float* dv;           // [BH][M][D]
+  int N, M, nqb, nkt, Np, Mp, coff;
+  float qk_scale;      // sm_scale * log2(e)
+  float sm;            // sm_scale
+};
+
+// The elementwise part shared by both backward kernels, for one wave's 32 queries (lane = query,
+// 16 keys per 32-key half): S^T from K^ / Q^ fragments, P = exp2(S - L2), dP^T = V dO^T on the
+// bf16 MFMA from the 16-bit V tile in LDS, dS = P (dP - D).  Masked pairs give P = dS = 0.
+template <int D, bool FP16>
+__device__ __forceinline__ void sb_pair(const v4i (&kf)[2][D / 32], const v4i (&qf)[D / 32], const v4i (&of)[D / 16],
+                                        const uint16_t* __restrict__ sVb, int vs, float mul, float l2, float dr,
+                                        int lim, int h, int col, float (&P)[2][16], float (&dS)[2][16]) {
+#pragma unroll
+  for (int T = 0; T < 2; T++) {
+    v16i acc;
+#pragma unroll
+    for (int r = 0; r < 16; r++) acc[r] = 0;
+#pragma unroll
+    for (int s = 0; s < D / 32; s++) acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[T][s], qf[s], acc, 0, 0, 0);
+    v16f dp;
+#pragma unroll
+    for (int r = 0; r < 16; r++) dp[r] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < D / 16; s++) {
+      const v4i vf = *reinterpret_cast<const v4i*>(sVb + (32 * T + col) * vs + 16 * s + 8 * h);
+      dp = mfma16<FP16>(vf, of[s], dp);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const bool vis = 32 * T + 8 * (r >> 2) + (r & 3) <= lim;
+      const float p = vis ? fast_exp2((float)acc[r] * mul - l2) : 0.0f;
+      P[T][r] = p;
+      dS[T][r] = p * (dp[r] - dr);
+    }
+  }
+}
+
+// Block maxima of P and |dS| over the work-group's 128 x 64 block (4 waves; two barriers).
+__device__ __forceinline__ void sb_block_max(float pm, float dm, float* xs, int lane, int w, float& pmax, float& dmax) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    pm = fmaxf(pm, __shfl_xor(pm, off));
+    dm = fmaxf(dm, __shfl_xor(dm, off));
+  }
+  if (lane == 0) {
+    xs[w] = pm;
+    xs[4 + w] = dm;
+  }
+  __syncthreads();
+  pmax = fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3]));
+  dmax = fmaxf(fmaxf(xs[4], xs[5]), fmaxf(xs[6], xs[7]));
+}
+
+// INT8 code of x against 127 / amax (inv = 0: the block is all zero).
+__device__ __forceinline__ uint32_t sb_code8(float x, float inv) {
+  float y = rintf(x * inv);
+  y = fminf(fmaxf(y, -127.0f), 127.0f);
+  return (uint32_t)(uint8_t)(int8_t)(int)y;
+}
+
+// The 16-bit rows of one 64-key V tile into LDS (rows >= M are 0).
+template <int D>
+__device__ __forceinline__ void sb_load_v(const uint16_t* __restrict__ V, int M, int t0, uint16_t* sVb, int vs, int tid) {
+  for (int e = tid; e < kBK * D / 8; e += 256) {
+    const int r = e / (D / 8), c = (e % (D / 8)) * 8;
+    v4i x = {0, 0, 0, 0};
+    if (t0 + r < M) x = *reinterpret_cast<const v4i*>(V + (size_t)(t0 + r) * D + c);
+    *reinterpret_cast<v4i*>(sVb + r * vs + c) = x;
+  }
+}
+
+// The fragments of one query row: Q^ (INT8 MFMA B operand) and dO (bf16 MFMA B operand).
+template <int D>
+__device__ __forceinline__ void sb_q_frags(const BwdArgs& a, int bh, int qrow, int h, v4i (&qf)[D / 32],
+                                           v4i (&of)[D / 16]) {
+  const int8_t* qp = a.qh + ((size_t)bh * a.Np + qrow) * D + 16 * h;
+#pragma unroll
+  for (int s = 0; s < D / 32; s++) qf[s] = *reinterpret_cast<const v4i*>(qp + 32 * s);
+  const bool ok = qrow < a.N;
+  const uint16_t* op = a.dO + ((size_t)bh * a.N + (ok ? qrow : 0)) * D + 8 * h;
+#pragma unroll
+  for (int s = 0; s < D / 16; s++) {
+    of[s] = ok ? *reinterpret_cast<const v4i*>(op + 16 * s) : v4i{0, 0, 0, 0};
+  }
+}
+
+// ---- dQ: one work-group per (head, 128-query block); loops over the key blocks ----
+template <int D, bool CAUSAL, bool FP16>
+__global__ __launch_bounds__(256, 2) void sb_dq_kernel(BwdArgs a) {
+  constexpr int NKS = D / 32, KS = D + 16, TS = kBK + 16, VS = D + 8;
+  __shared__ __attribute__((aligned(16))) int8_t sK[kBK * KS];
+  __shared__ __attribute__((aligned(16))) int8_t sKt[D * TS];
+  __shared__ __attribute__((aligned(16))) uint16_t sVb[kBK * VS];
+  __shared__ float xs[8];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
+  const int bh = blockIdx.x / a.nqb, qi = blockIdx.x % a.nqb;
+  const int qb = CAUSAL ? (a.nqb - 1 - qi) : qi;
+  const int q0 = qb * kBQ, qrow = q0 + 32 * w + col;
+  v4i qf[NKS];
+  v4i of[D / 16];
+  sb_q_frags<D>(a, bh, qrow, h, qf, of);
+  const float l2 = a.L2[(size_t)bh * a.Np + qrow], dr = a.Dr[(size_t)bh * a.Np + qrow];
+  const float sq = a.sq[(size_t)bh * a.nqb + qb];
+  v16f dq[NKS];
+#pragma unroll
+  for (int c = 0; c < NKS; c++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) dq[c][r] = 0.0f;
+  float rs = 0.0f;
+  const int jend = CAUSAL ? max(0, min(a.nkt, (q0 + kBQ + a.coff + kBK - 1) / kBK)) : a.nkt;
+  for (int j = 0; j < jend; j++) {
+    __syncthreads();
+    {
+      const int8_t* kr = a.kh + ((size_t)bh * a.Mp + (size_t)j * kBK) * D;
+      const int8_t* kt = a.kt + ((size_t)bh * a.nkt + j) * (size_t)D * kBK;
+      for (int e = tid; e < kBK * D / 16; e += 256) {
+        const int r = e / (D / 16), c = (e % (D / 16)) * 16;
+        *reinterpret_cast<v4i*>(&sK[r * KS + c]) = *reinterpret_cast<const v4i*>(kr + (size_t)r * D + c);
+      }
+      for (int e = tid; e < D * kBK / 16; e += 256) {
+        const int r = e / (kBK / 16), c = (e % (kBK / 16)) * 16;
+        *reinterpret_cast<v4i*>(&sKt[r * TS + c]) = *reinterpret_cast<const v4i*>(kt + (size_t)r * kBK + c);
+      }
+      sb_load_v<D>(a.V + (size_t)bh * a.M * D, a.M, j * kBK, sVb, VS, tid);
+    }
+    __syncthreads();
+    v4i kf[2][NKS];
+#pragma unroll
+    for (int T = 0; T < 2; T++)
+#pragma unroll
+      for (int s = 0; s < NKS; s++) kf[T][s] = *reinterpret_cast<const v4i*>(&sK[(32 * T + col) * KS + 32 * s + 16 * h]);
+    const int key0 = j * kBK;
+    int lim = a.M - 1 - key0;
+    if (CAUSAL) lim = min(lim, qrow + a.coff - key0);
+    lim -= 4 * h;
+    float P[2][16], dS[2][16];
+    sb_pair<D, FP16>(kf, qf, of, sVb, VS, sq * a.sk[(size_t)bh * a.nkt + j] * a.qk_scale, l2, dr, lim, h, col, P, dS);
+    float pm = 0.0f, dm = 0.0f;
+#pragma unroll
+    for (int T = 0; T < 2; T++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        pm = fmaxf(pm, P[T][r]);
+        dm = fmaxf(dm, fabsf(dS[T][r]));
+        rs += dS[T][r];
+      }
+    float pmax, dmax;
+    sb_block_max(pm, dm, xs, lane, w, pmax, dmax);
+    const float inv = dmax > 0.0f ? __fdiv_rn(127.0f, dmax) : 0.0f;
+    const float sds = __fdiv_rn(dmax, 127.0f);
+    v4i db[2];
+#pragma unroll
+    for (int T = 0; T < 2; T++)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; q4++) {
+        uint32_t wd = 0;
+#pragma unroll
+        for (int k = 0; k < 4; k++) wd |= sb_code8(dS[T][4 * q4 + k], inv) << (8 * k);
+        db[T][q4] = (int)wd;
+      }
+    const float osc = sds * a.sk[(size_t)bh * a.nkt + j] * a.sm;
+#pragma unroll
+    for (int c = 0; c < NKS; c++) {
+      v16i R;
+#pragma unroll
+      for (int r = 0; r < 16; r++) R[r] = 0;
+#pragma unroll
+      for (int T = 0; T < 2; T++) {
+        const v4i kt = *reinterpret_cast<const v4i*>(&sKt[(32 * c + col) * TS + 32 * T + 16 * h]);
+        R = __builtin_amdgcn_mfma_i32_32x32x32_i8(kt, db[T], R, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; r++) dq[c][r] = fmaf((float)R[r], osc, dq[c][r]);
+    }
+  }
+  rs = pair_sum(rs);
+  if (qrow >= a.N) return;
+  const size_t orow = ((size_t)bh * a.N + qrow) * D;
+#pragma unroll
+  for (int c = 0; c < NKS; c++)
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      const int ch = 32 * c + 8 * b + 4 * h;
+      float o[4];
+#pragma unroll
+      for (int k = 0; k < 4; k++)
+        o[k] = a.kmean ? fmaf(a.sm * rs, a.kmean[(size_t)bh * D + ch + k], dq[c][4 * b + k]) : dq[c][4 * b + k];
+      store_out4<2>(a.dq, orow + ch, o);
+    }
+}
+
+// ---- dK, dV: one work-group per (head, 64-key block); loops over the query blocks.  P^ and
+// dS^ of a pair go to LDS key-major; wave w then owns key half w % 2 and half of the channel
+// groups of both outputs, and contracts over the block's 128 queries ----
+template <int D, bool CAUSAL, bool FP16>
+__global__ __launch_bounds__(256, 1) void sb_dkv_kernel(BwdArgs a) {
+  constexpr int NKS = D / 32, NG = NKS / 2, VS = D + 8, PS = kBQ + 16;
+  __shared__ __attribute__((aligned(16))) uint16_t sVb[kBK * VS];
+  __shared__ __attribute__((aligned(16))) int8_t sP[kBK * PS];
+  __shared__ __attribute__((aligned(16))) int8_t sD[kBK * PS];
+  __shared__ float xs[8];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
+  const int bh = blockIdx.x / a.nkt, j = blockIdx.x % a.nkt;
+  const int key0 = j * kBK;
+  sb_load_v<D>(a.V + (size_t)bh * a.M * D, a.M, key0, sVb, VS, tid);
+  v4i kf[2][NKS];
+  {
+    const int8_t* kr = a.kh + ((size_t)bh * a.Mp + key0) * D;
+#pragma unroll
+    for (int T = 0; T < 2; T++)
+#pragma unroll
+      for (int s = 0; s < NKS; s++)
+        kf[T][s] = *reinterpret_cast<const v4i*>(kr + (size_t)(32 * T + col) * D + 32 * s + 16 * h);
+  }
+  const float skj = a.sk[(size_t)bh * a.nkt + j];
+  // this wave's output tiles, of both dV and dK: key half Tw, channel groups c0 .. c0 + NG - 1
+  const int Tw = w & 1, c0 = (w >> 1) * NG;
+  v16f accV[NG], accK[NG];
+#pragma unroll
+  for (int g = 0; g < NG; g++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) accV[g][r] = accK[g][r] = 0.0f;
+  const int ilo = CAUSAL ? max(0, (key0 - a.coff) / kBQ) : 0;
+  for (int i = ilo; i < a.nqb; i++) {
+    __syncthreads();  // the previous pair's LDS reads are done (and V is staged, i = ilo)
+    const int q0 = i * kBQ, qrow = q0 + 32 * w + col;
+    v4i qf[NKS];
+    v4i of[D / 16];
+    sb_q_frags<D>(a, bh, qrow, h, qf, of);
+    const float l2 = a.L2[(size_t)bh * a.Np + qrow], dr = a.Dr[(size_t)bh * a.Np + qrow];
+    int lim = a.M - 1 - key0;
+    if (CAUSAL) lim = min(lim, qrow + a.coff - key0);
+    lim -= 4 * h;
+    float P[2][16], dS[2][16];
+    // the score multiplier in the dQ kernel's order, so that both kernels see the same P and dS
+    sb_pair<D, FP16>(kf, qf, of, sVb, VS, a.sq[(size_t)bh * a.nqb + i] * skj * a.qk_scale, l2, dr, lim, h, col, P, dS);
+    float pm = 0.0f, dm = 0.0f;
+#pragma unroll
+    for (int T = 0; T < 2; T++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        pm = fmaxf(pm, P[T][r]);
+        dm = fmaxf(dm, fabsf(dS[T][r]));
+      }
+    float pmax, dmax;
+    sb_block_max(pm, dm, xs, lane, w, pmax, dmax);
+    const float pinv = pmax > 0.0f ? __fdiv_rn(127.0f, pmax) : 0.0f;
+    const float dinv = dmax > 0.0f ? __fdiv_rn(127.0f, dmax) : 0.0f;
+    // P^, dS^ key-major: byte [key][query]
+    const int qc = 32 * w + col;
+#pragma unroll
+    for (int T = 0; T < 2; T++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int key = 32 * T + 8 * (r >> 2) + 4 * h + (r & 3);
+        sP[key * PS + qc] = (int8_t)sb_code8(P[T][r], pinv);
+        sD[key * PS + qc] = (int8_t)sb_code8(dS[T][r], dinv);
+      }
+    __syncthreads();
+    const float vsc = __fdiv_rn(pmax, 127.0f) * a.sdo[(size_t)bh * a.nqb + i];
+    const float ksc = __fdiv_rn(dmax, 127.0f) * a.sq[(size_t)bh * a.nqb + i] * a.sm;
+    const int8_t* dob = a.dot + ((size_t)bh * a.nqb + i) * (size_t)D * kBQ;
+    const int8_t* qtb = a.qt + ((size_t)bh * a.nqb + i) * (size_t)D * kBQ;
+#pragma unroll
+    for (int g = 0; g < NG; g++) {
+      const int c = c0 + g;
+      {
+        v16i R;
+#pragma unroll
+        for (int r = 0; r < 16; r++) R[r] = 0;
+#pragma unroll
+        for (int qs = 0; qs < kBQ / 32; qs++) {
+          const v4i pa = *reinterpret_cast<const v4i*>(&sP[(32 * Tw + col) * PS + 32 * qs + 16 * h]);
+          const v4i ob = *reinterpret_cast<const v4i*>(dob + (size_t)(32 * c + col) * kBQ + 32 * qs + 16 * h);
+          R = __builtin_amdgcn_mfma_i32_32x32x32_i8(pa, ob, R, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; r++) accV[g][r] = fmaf((float)R[r], vsc, accV[g][r]);
+      }
+      {
+        v16i R;
+#pragma unroll
+        for (int r = 0; r < 16; r++) R[r] = 0;
+#pragma unroll
+        for (int qs = 0; qs < kBQ / 32; qs++) {
+          const v4i da = *reinterpret_cast<const v4i*>(&sD[(32 * Tw + col) * PS + 32 * qs + 16 * h]);
+          const v4i qb = *reinterpret_cast<const v4i*>(qtb + (size_t)(32 * c + col) * kBQ + 32 * qs + 16 * h);
+          R = __builtin_amdgcn_mfma_i32_32x32x32_i8(da, qb, R, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; r++) accK[g][r] = fmaf((float)R[r], ksc, accK[g][r]);
+      }
+    }
+  }
+  // C[i = key][j = channel]: lane = channel 32 c + col, rows = keys 32 Tw + 8 (r / 4) + 4 h + r % 4
+#pragma unroll
+  for (int g = 0; g < NG; g++) {
+    const int c = c0 + g;
+#pragma unroll
+    for (int r = 0; r < 16; r++) {
+      const int key = key0 + 32 * Tw + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (key >= a.M) continue;
+      const size_t o = ((size_t)bh * a.M + key) * D + 32 * c + col;
+      a.dv[o] = accV[g][r];
+      a.dk[o] = accK[g][r];
+    }
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- host side
+
+// Workspace slices of SageBwd (256-byte aligned).
+enum SbSlice { kSbQh, kSbQt, kSbSq, kSbKh, kSbKt, kSbSk, kSbVt, kSbSv, kSbDot, kSbSdo, kSbD, kSbL2,
+               kSbKpart, kSbVpart, kSbVmax, kSbVmin, kSbKmean, kSbVmean, kSbDv, kSbSlices };
+
+size_t sb_layout(const Problem& p, bool bwd, size_t* s) {
+  const size_t BH = (size_t)p.BH, d = (size_t)p.d;
+  size_t z[kSbSlices];
+  z[kSbQh] = BH * p.Np * d;
+  z[kSbQt] = bwd ? BH * p.Np * d : 0;
+  z[kSbSq] = BH * p.nqb * 4;
+  z[kSbKh] = BH * p.Mp * d;
+  z[kSbKt] = bwd ? BH * p.Mp * d : 0;
+  z[kSbSk] = BH * p.nkt * 4;
+  z[kSbVt] = BH * p.Mp * d;
+  z[kSbSv] = BH * p.nkt * 4;
+  z[kSbDot] = bwd ? BH * p.Np * d : 0;
+  z[kSbSdo] = bwd ? BH * p.nqb * 4 : 0;
+  z[kSbD] = bwd ? BH * p.Np * 4 : 0;
+  z[kSbL2] = bwd ? BH * p.Np * 4 : 0;
+  z[kSbKpart] = BH * p.nkt * d * 8;
+  z[kSbVpart] = BH * p.nkt * d * 8;
+  z[kSbVmax] = BH * p.nkt * d * 4;
+  z[kSbVmin] = BH * p.nkt * d * 4;
+  z[kSbKmean] = BH * d * 4;
+  z[kSbVmean] = BH * d * 4;
+  z[kSbDv] = BH * d * 4;
+  size_t tot = 0;
+  for (int i = 0; i < kSbSlices; i++) {
+    if (s) s[i] = tot;
+    tot += (z[i] + 255) & ~(size_t)255;
+  }
+  return tot;
+}
+
+// K mean (the inference path's kernels, pinned order) and the per-block codes of Q, K, V.
+hipError_t sb_prep_fwd(const Problem& p, const void* q, const void* k, const void* v, char* ws, bool bwd,
+                       bool smooth_k, hipStream_t st) {
+  size_t o[kSbSlices];
+  sb_layout(p, bwd, o);
+  Workspace w{};
+  w.kpart = (double*)(ws + o[kSbKpart]);
+  w.vpart = (double*)(ws + o[kSbVpart]);
+  w.vmaxp = (float*)(ws + o[kSbVmax]);
+  w.vminp = (float*)(ws + o[kSbVmin]);
+  w.kmean = (float*)(ws + o[kSbKmean]);
+  w.vmean = (float*)(ws + o[kSbVmean]);
+  w.dv = (float*)(ws + o[kSbDv]);
+  hipError_t e;
+  if (smooth_k) {
+    if ((e = launch_kv_stats(p, k, v, w, st)) != hipSuccess) return e;
+    if ((e = launch_kv_finalize(p, w, st)) != hipSuccess) return e;
+  }
+  const float* km = smooth_k ? w.kmean : nullptr;
+  const dim3 gq(p.nqb, p.BH), gk(p.nkt, p.BH);
+  auto Q = (const uint16_t*)q;
+  auto K = (const uint16_t*)k;
+  auto V = (const uint16_t*)v;
+  int8_t* qh = (int8_t*)(ws + o[kSbQh]);
+  int8_t* qt = bwd ? (int8_t*)(ws + o[kSbQt]) : nullptr;
+  int8_t* kh = (int8_t*)(ws + o[kSbKh]);
+  int8_t* kt = bwd ? (int8_t*)(ws + o[kSbKt]) : nullptr;
+  int8_t* vt = (int8_t*)(ws + o[kSbVt]);
+  float* sq = (float*)(ws + o[kSbSq]);
+  float* sk = (float*)(ws + o[kSbSk]);
+  float* sv = (float*)(ws + o[kSbSv]);
+  if (p.d == 128) {
+    hipLaunchKernelGGL((sb_quant_kernel<128, 128, false>), gq, dim3(256), 0, st, Q, nullptr, qh, qt, sq, p.N, p.Np,
+                       p.nqb, p.fp16);
+    hipLaunchKernelGGL((sb_quant_kernel<128, 64, true>), gk, dim3(256), 0, st, K, km, kh, kt, sk, p.M, p.Mp, p.nkt,
+                       p.fp16);
+    hipLaunchKernelGGL((sb_quant_kernel<128, 64, true>), gk, dim3(256), 0, st, V, nullptr, nullptr, vt, sv, p.M,
+                       p.Mp, p.nkt, p.fp16);
+  } else {
+    hipLaunchKernelGGL((sb_quant_kernel<64, 128, false>), gq, dim3(256), 0, st, Q, nullptr, qh, qt, sq, p.N, p.Np,
+                       p.nqb, p.fp16);
+    hipLaunchKernelGGL((sb_quant_kernel<64, 64, true>), gk, dim3(256), 0, st, K, km, kh, kt, sk, p.M, p.Mp, p.nkt,
+                       p.fp16);
+    hipLaunchKernelGGL((sb_quant_kernel<64, 64, true>), gk, dim3(256), 0, st, V, nullptr, nullptr, vt, sv, p.M,
+                       p.Mp, p.nkt, p.fp16);
+  }
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+void sb_fwd_launch(const Problem& p, const FwdArgs& a, hipStream_t st) {
+  const dim3 grid(p.nqb * p.BH);
+  if (p.out_fp32) hipLaunchKernelGGL((sb_fwd_kernel<D, CAUSAL, 2>), grid, dim3(256), 0, st, a);
+  else if (p.fp16) hipLaunchKernelGGL((sb_fwd_kernel<D, CAUSAL, 1>), grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((sb_fwd_kernel<D, CAUSAL, 0>), grid, dim3(256), 0, st, a);
+}
+
+hipError_t sb_forward(const Problem& p, char* ws, bool bwd, void* out, float* lse, hipStream_t st) {
+  size_t o[kSbSlices];
+  sb_layout(p, bwd, o);
+  FwdArgs a;
+  a.qh = (const int8_t*)(ws + o[kSbQh]);
+  a.sq = (const float*)(ws + o[kSbSq]);
+  a.kh = (const int8_t*)(ws + o[kSbKh]);
+  a.sk = (const float*)(ws + o[kSbSk]);
+  a.vt = (const int8_t*)(ws + o[kSbVt]);
+  a.sv = (const float*)(ws + o[kSbSv]);
+  a.out = out;
+  a.lse = lse;
+  a.N = p.N; a.M = p.M; a.nqb = p.nqb; a.nkt = p.nkt; a.Np = p.Np; a.Mp = p.Mp;
+  a.coff = p.causal == 2 ? p.M - p.N : 0;
+  a.qk_scale = p.sm_scale * kLog2e;
+  if (p.d == 128) p.causal ? sb_fwd_launch<128, true>(p, a, st) : sb_fwd_launch<128, false>(p, a, st);
+  else p.causal ? sb_fwd_launch<64, true>(p, a, st) : sb_fwd_launch<64, false>(p, a, st);
+  return hipGetLastError();
+}
+
+// The backward's own preprocessing: dO^ transposed per 128 rows, D, L2.
+hipError_t sb_prep_bwd(const Problem& p, const void* out, const void* dout, const float* lse, char* ws,
+                       hipStream_t st) {
+  size_t o[kSbSlices];
+  sb_layout(p, true, o);
+  int8_t* dot = (int8_t*)(ws + o[kSbDot]);
+  float* sdo = (float*)(ws + o[kSbSdo]);
+  float* Dr = (float*)(ws + o[kSbD]);
+  float* L2 = (float*)(ws + o[kSbL2]);
+  const dim3 gq(p.nqb, p.BH);
+  auto dO = (const uint16_t*)dout;
+  const int outk = p.out_fp32 ? 2 : (p.fp16 ? 1 : 0);
+  if (p.d == 128) {
+    hipLaunchKernelGGL((sb_quant_kernel<128, 128, false>), gq, dim3(256), 0, st, dO, nullptr, nullptr, dot, sdo, p.N,
+                       p.Np, p.nqb, p.fp16);
+    if (outk == 2) hipLaunchKernelGGL((sb_dprep_kernel<128, 2>), gq, dim3(256), 0, st, out, dO, lse, Dr, L2, p.N, p.Np, p.fp16);
+    else if (outk == 1) hipLaunchKernelGGL((sb_dprep_kernel<128, 1>), gq, dim3(256), 0, st, out, dO, lse, Dr, L2, p.N, p.Np, p.fp16);
+    else hipLaunchKernelGGL((sb_dprep_kernel<128, 0>), gq, dim3(256), 0, st, out, dO, lse, Dr, L2, p.N, p.Np, p.fp16);
+  } else {
+    hipLaunchKernelGGL((sb_quant_kernel<64, 128, false>), gq, dim3(256), 0, st, dO, nullptr, nullptr, dot, sdo, p.N,
+                       p.Np, p.nqb, p.fp16);
+    if (outk == 2) hipLaunchKernelGGL((sb_dprep_kernel<64, 2>), gq, dim3(256), 0, st, out, dO, lse, Dr, L2, p.N, p.Np, p.fp16);
+    else if (outk == 1) hipLaunchKernelGGL((sb_dprep_kernel<64, 1>), gq, dim3(256), 0, st, out, dO, lse, Dr, L2, p.N, p.Np, p.fp16);
+    else hipLaunchKernelGGL((sb_dprep_kernel<64, 0>), gq, dim3(256), 0, st, out, dO, lse, Dr, L2, p.N, p.Np, p.fp16);
+  }
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, bool FP16>
+void sb_bwd_launch(const Problem& p, const BwdArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((sb_dq_kernel<D, CAUSAL, FP16>), dim3(p.nqb * p.BH), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((sb_dkv_kernel<D, CAUSAL, FP16>), dim3(p.nkt * p.BH), dim3(256), 0, st, a);
+}
+
+template <int D>
+void sb_bwd_d(const Problem& p, const BwdArgs& a, hipStream_t st) {
+  if (p.causal) p.fp16 ? sb_bwd_launch<D, true, true>(p, a, st) : sb_bwd_launch<D, true, false>(p, a, st);
+  else p.fp16 ? sb_bwd_launch<D, false, true>(p, a, st) : sb_bwd_launch<D, false, false>(p, a, st);
+}
+
+hipError_t sb_backward(const Problem& p, char* ws, bool smooth_k, const void* v, const void* dout, float* dq,
+                       float* dk, float* dv, hipStream_t st) {
+  size_t o[kSbSlices];
+  sb_layout(p, true, o);
+  BwdArgs a;
+  a.qh = (const int8_t*)(ws + o[kSbQh]);
+  a.qt = (const int8_t*)(ws + o[kSbQt]);
+  a.sq = (const float*)(ws + o[kSbSq]);
+  a.kh = (const int8_t*)(ws + o[kSbKh]);
+  a.kt = (const int8_t*)(ws + o[kSbKt]);
+  a.sk = (const float*)(ws + o[kSbSk]);
+  a.dot = (const int8_t*)(ws + o[kSbDot]);
+  a.sdo = (const float*)(ws + o[kSbSdo]);
+  a.Dr = (const float*)(ws + o[kSbD]);
+  a.L2 = (const float*)(ws + o[kSbL2]);
+  a.kmean = smooth_k ? (const float*)(ws + o[kSbKmean]) : nullptr;
+  a.V = (const uint16_t*)v;
+  a.dO = (const uint16_t*)dout;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.N = p.N; a.M = p.M; a.nqb = p.nqb; a.nkt = p.nkt; a.Np = p.Np; a.Mp = p.Mp;
+  a.coff = p.causal == 2 ? p.M - p.N : 0;
+  a.qk_scale = p.sm_scale * kLog2e;
+  a.sm = p.sm_scale;
+  if (p.d == 128) sb_bwd_d<128>(p, a, st);
+  else sb_bwd_d<64>(p, a, st);
+  return hipGetLastError();
+}
+
+}  // namespace sage

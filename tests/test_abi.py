@@ -22,7 +22,8 @@ def test_header_declares_the_boundary():
                             "sage_attn_quantize", "sage_attn_set_profile_events",
                             "sage_attn_status_string", "sage_attn_version", "sage_attn_fwd_ex",
                             "sage_attn_workspace_bytes_ex", "sage_attn_quantize_ex",
-                            "sage_attn_varlen_workspace_bytes", "sage_attn_varlen_fwd"])
+                            "sage_attn_varlen_workspace_bytes", "sage_attn_varlen_fwd",
+                            "sage_attn_train_workspace_bytes", "sage_attn_train_fwd", "sage_attn_train_bwd"])
 
 
 def test_library_exports_every_declared_symbol():
