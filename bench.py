@@ -73,8 +73,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill32k",
-                    help="one of: n4k, prefill32k, video17k, chunk4k_32k, prefill32k_gqa, prefill32k_qkfp8, mxfp4_32k "
-                         "(default prefill32k)")
+                    help="one of: n4k, prefill32k, video17k, chunk4k_32k, prefill32k_gqa, prefill32k_qkfp8, mxfp4_32k, "
+                         "train8k (default prefill32k)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -150,6 +150,118 @@ def cpu_baseline(cfg, budget_s: float) -> dict:
                       f"(per-head preprocessing and Delta S rows included), {t_used:.1f} s"}
 
 
+def train_cpu_baseline(cfg, n=1024):
+    """The SageBwd oracle (forward + backward) on head 0, cut to n queries and keys."""
+    import oracle
+    from quantized_attention_amd import synthetic as sy
+    sub = cfg.with_shape(B=1, H=1, N=min(n, cfg.N), M=min(n, cfg.M))
+    q, k, v = [x[0, 0] for x in sy.make_qkv(sub)]
+    do = sy.f32_to_bf16_bits(np.random.default_rng(5).standard_normal(q.shape).astype(np.float32))
+    t0 = time.perf_counter()
+    oracle.sagebwd_backward(q, k, v, do, sub.fp16, sub.causal, 1.0 / math.sqrt(sub.d))
+    dt = time.perf_counter() - t0
+    ops = counted_ops(sub) * 14 / 4
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"head 0, first {sub.N} queries and keys (forward + backward, per-head preprocessing "
+                      f"included), {dt:.1f} s"}
+
+
+def main_train(args, cfg):
+    """A SageBwd training step of the attention: forward (out, lse) then backward (dq, dk, dv)."""
+    import torch
+
+    import quantized_attention_amd as qa
+    from quantized_attention_amd import synthetic as sy
+    qa.load_library()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating {cfg.name} B={cfg.B} H={cfg.H} N={cfg.N} d={cfg.d}", file=sys.stderr, flush=True)
+    qb, kb, vb = sy.make_qkv(cfg)
+    dob = sy.f32_to_bf16_bits(np.random.default_rng(5).standard_normal(qb.shape).astype(np.float32))
+    dt = torch.bfloat16
+    q, k, v, do = (torch.from_numpy(x.view(np.int16)).view(dt).to(dev) for x in (qb, kb, vb, dob))
+    del qb, kb, vb, dob
+    out = torch.empty_like(q)
+    lse = torch.empty((cfg.B, cfg.H, cfg.N), dtype=torch.float32, device=dev)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
+    shape = qa.SageAttnShape(cfg.B, cfg.H, cfg.H, cfg.N, cfg.M, cfg.d, int(cfg.causal), 1.0 / math.sqrt(cfg.d),
+                             qa.SAGE_IN_BF16)
+    ws_bytes = qa.sage_attn_train_workspace_bytes(shape)
+    ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
+    ws_ptr = (ws.data_ptr() + 255) // 256 * 256
+    stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def fwd():
+        rc = qa.sage_attn_train_fwd(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                    ws_ptr, ws_bytes, stream)
+        if rc != qa.SAGE_OK:
+            raise qa.SageError(rc, "sage_attn_train_fwd")
+
+    def bwd():
+        rc = qa.sage_attn_train_bwd(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), do.data_ptr(),
+                                    lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_bytes,
+                                    stream)
+        if rc != qa.SAGE_OK:
+            raise qa.SageError(rc, "sage_attn_train_bwd")
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        fwd()
+        bwd()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for a, b, c in ev:
+        a.record()
+        fwd()
+        b.record()
+        bwd()
+        c.record()
+    t_stop.record()
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_stop) / args.steps
+    f_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
+    b_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    ops = counted_ops(cfg) * 14 / 4
+    value = ops / (ms * 1e-3) / 1e12
+    shape_s = f"N={cfg.N} d={cfg.d}" + (" causal" if cfg.causal else "")
+    line = {
+        "metric": f"training attention TOPS (SageBwd forward + backward, 14*N^2*d*H*B/time, causal counted as half) "
+                  f"at {shape_s}, % of INT8 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 (QK^T, P^T dO, dS K, dS^T Q, P V) + bf16 (dO V^T), fp32 softmax/accumulate",
+        "data": "synthetic (seeded Gaussian + per-channel offsets; dO standard normal)",
+        "config": {"workload": f"{cfg.name}: B={cfg.B} H={cfg.H} N=M={cfg.N} d={cfg.d} {cfg.dtype} "
+                               f"{'causal' if cfg.causal else 'non-causal'}, forward + backward",
+                   "global_batch": cfg.B, "seq_len": cfg.N, "heads": cfg.H, "head_dim": cfg.d,
+                   "parallelism": "single GPU"},
+        "frac_of_peak": round(value / PEAK_TOPS, 4),
+        "forward_ms": round(f_ms, 4),
+        "backward_ms": round(b_ms, 4),
+        "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_TOPS, "unit": "TOPS",
+                     "frac": round(value / PEAK_TOPS, 4), "traffic": None,
+                     "note": "whole step (preprocessing included) against the INT8 peak; dO V^T runs at the bf16 rate"},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = train_cpu_baseline(cfg)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -163,6 +275,8 @@ def main():
     from quantized_attention_amd import synthetic as sy
 
     cfg = sy.CONFIGS[args.workload]
+    if cfg.train:
+        return main_train(args, cfg)
     qa.load_library()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)

@@ -52,6 +52,7 @@ class Config:
     note: str = ""
     Hkv: int = 0        # key/value heads (0: H); query head h reads key/value head h // (H // Hkv)
     qk_fp8: bool = False  # Q^, K^ in E4M3 instead of INT8
+    train: bool = False   # SageBwd forward + backward (a training step of the attention)
 
     @property
     def fp16(self) -> bool:
@@ -93,6 +94,9 @@ CONFIGS = {
     "prefill32k_qkfp8": Config("prefill32k_qkfp8", 1, 32, 32768, 32768, 128, "bf16", True,
                                Dist(k_off_std=4.0, k_spike=8.0, k_spike_channels=spike_channels(128)), 1003,
                                qk_fp8=True, note="the prefill layer with Q^, K^ in E4M3 (same inputs)"),
+    "train8k": Config("train8k", 1, 32, 8192, 8192, 128, "bf16", True,
+                      Dist(k_off_std=4.0, k_spike=8.0, k_spike_channels=spike_channels(128)), 1008, train=True,
+                      note="SageBwd training step (forward + backward) of an 8k-token causal layer"),
     "mxfp4_32k": Config("mxfp4_32k", 1, 24, 32768, 32768, 128, "bf16", False,
                         Dist(k_off_std=2.0, v_bias_std=0.5), 1005, mxfp4=True,
                         note="MXFP4 variant"),
