@@ -12,6 +12,7 @@
 #include <mutex>
 
 #include "sage_common.hpp"
+#include "sagebwd.hpp"
 
 namespace sage {
 

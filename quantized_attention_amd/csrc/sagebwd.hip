@@ -21,6 +21,7 @@
 // dO^ (one 32-query step per MFMA).  dP^T = V dO^T runs on the bf16 MFMA from the 16-bit
 // inputs.
 #include "attn_device.hpp"
+#include "sagebwd.hpp"
 
 namespace sage {
 namespace {

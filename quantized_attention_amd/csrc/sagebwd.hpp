@@ -1,0 +1,20 @@
+// sagebwd.hpp -- host entry points of SageBwd, the trainable INT8 attention (sagebwd.hip).
+#pragma once
+
+#include "sage_common.hpp"
+
+namespace sage {
+
+// Workspace bytes (offsets of its slices into `offsets` when given), the preprocessing of Q,
+// K, V (K smoothed when smooth_k), the forward (out, lse), the backward's preprocessing (dO^,
+// D, L) and the backward (dq, dk, dv in FP32).
+size_t sb_layout(const Problem& p, bool bwd, size_t* offsets);
+hipError_t sb_prep_fwd(const Problem& p, const void* q, const void* k, const void* v, char* ws, bool bwd,
+                       bool smooth_k, hipStream_t st);
+hipError_t sb_forward(const Problem& p, char* ws, bool bwd, void* out, float* lse, hipStream_t st);
+hipError_t sb_prep_bwd(const Problem& p, const void* out, const void* dout, const float* lse, char* ws,
+                       hipStream_t st);
+hipError_t sb_backward(const Problem& p, char* ws, bool smooth_k, const void* v, const void* dout, float* dq,
+                       float* dk, float* dv, hipStream_t st);
+
+}  // namespace sage
