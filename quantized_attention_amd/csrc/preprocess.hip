@@ -235,8 +235,12 @@ __global__ __launch_bounds__(256) void q_prep_kernel(const uint16_t* __restrict_
     const size_t o = ((size_t)bh * nqb + i) * D + tid;
     qmean[o] = m;
     const uint16_t hb = bf16_rn(m);
-    qm_hi[o] = hb;
-    qm_lo[o] = bf16_rn(m - bf16_val(hb));
+    // head / tail in the Delta S MFMA's B-operand order: per group of 32 blocks, channel step
+    // s = c / 16, lane 32 ((c % 16) / 8) + block % 32, 8 bf16 per lane
+    const size_t sw = ((((size_t)bh * ((nqb + 31) / 32) + i / 32) * (D / 16) + tid / 16) * 64 +
+                       32 * ((tid % 16) / 8) + i % 32) * 8 + tid % 8;
+    qm_hi[sw] = hb;
+    qm_lo[sw] = bf16_rn(m - bf16_val(hb));
   }
   __syncthreads();
   // Each wave takes 32 rows.  A row is spread over LPR = D/8 lanes holding 8 consecutive
@@ -473,19 +477,21 @@ __global__ __launch_bounds__(256, MX ? 3 : 4) void kv_quant_kernel(KVArgs a) {
     const int nqb = (nq + kBQ - 1) / kBQ;
     const int coff = a.causal == 2 ? R.len - nq : 0;
     const int ilo = (a.causal && t0 > coff) ? (t0 - coff) / kBQ : 0;
-    const int ngrp = (nqb + 31) / 32;
+    const int ngrp = (nqb + 31) / 32, ngrp_all = (a.nqb + 31) / 32;  // this sequence's / the bound's
     for (int unit = wave; unit < a.G * ngrp; unit += 4) {
       const int g = unit / ngrp, gidx = unit % ngrp;
       if (32 * gidx + 31 < ilo) continue;
       const int bhq = (bh / a.Hkv) * a.H + (bh % a.Hkv) * a.G + g;  // query head
       const int blk = 32 * gidx + col;
       const bool bv = blk < nqb;
-      const size_t qo = ((size_t)bhq * a.nqb + (bv ? blk : 0)) * D;
-      v8bf bq[D / 16], bl[D / 16];  // the block's q-mean head/tail, all loads in flight
+      // the block's q-mean head/tail, stored in this operand order: each load reads 1 KiB
+      // contiguously (64 lanes x 16 bytes); all loads in flight
+      const size_t qo = ((size_t)bhq * ngrp_all + gidx) * (D / 16) * 512 + (size_t)lane * 8;
+      v8bf bq[D / 16], bl[D / 16];
 #pragma unroll
       for (int s = 0; s < D / 16; s++) {
-        bq[s] = bv ? *reinterpret_cast<const v8bf*>(a.qm_hi + qo + 16 * s + 8 * h) : v8bf{};
-        bl[s] = bv ? *reinterpret_cast<const v8bf*>(a.qm_lo + qo + 16 * s + 8 * h) : v8bf{};
+        bq[s] = bv ? *reinterpret_cast<const v8bf*>(a.qm_hi + qo + 512 * s) : v8bf{};
+        bl[s] = bv ? *reinterpret_cast<const v8bf*>(a.qm_lo + qo + 512 * s) : v8bf{};
       }
 #pragma unroll
       for (int T = 0; T < 2; T++) {

@@ -36,8 +36,9 @@ size_t workspace_layout(const Problem& p, size_t* sizes) {
   s[11] = BK * p.nkt * d * sizeof(double);           // vpart
   s[12] = BK * p.nkt * d * sizeof(float);            // vmaxp
   s[13] = BK * p.nkt * d * sizeof(float);            // vminp
-  s[14] = BH * p.nqb * d * sizeof(uint16_t);         // qm_hi
-  s[15] = BH * p.nqb * d * sizeof(uint16_t);         // qm_lo
+  const size_t nqb32 = (size_t)(p.nqb + 31) / 32 * 32;  // q-mean head/tail: groups of 32 blocks
+  s[14] = BH * nqb32 * d * sizeof(uint16_t);         // qm_hi
+  s[15] = BH * nqb32 * d * sizeof(uint16_t);         // qm_lo
   s[16] = p.mx ? BH * p.Np * (d / 32) : 0;           // qsc
   s[17] = p.mx ? BK * p.nkt * 256 : 0;               // ksc
   s[18] = p.mx ? BK * p.nkt * 256 : 0;               // vsc

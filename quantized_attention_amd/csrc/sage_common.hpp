@@ -79,8 +79,10 @@ struct Workspace {
   double* vpart;    // [BH][nkt][d] FP64 chunk sums of V (V smoothing)
   float* vmaxp;     // [BH][nkt][d] chunk max of V
   float* vminp;     // [BH][nkt][d] chunk min of V
-  uint16_t* qm_hi;  // [BH][nqb][d] bf16 head of the block mean (Delta S operand)
-  uint16_t* qm_lo;  // [BH][nqb][d] bf16 tail: q_mean - hi, rounded to bf16
+  uint16_t* qm_hi;  // bf16 head of the block mean, in the Delta S MFMA operand order:
+                    // [BH][ceil(nqb/32)][d/16][64 lanes][8] (lane 32 h + block % 32 holds
+                    // channels 16 s + 8 h .. +7)
+  uint16_t* qm_lo;  // the bf16 tail, q_mean - hi rounded to bf16, in the same order
   uint8_t* qsc;     // MX: [BH][Np][d/32] E8M0 of gamma(Q) blocks
   uint8_t* ksc;     // MX: [BH][nkt][64][4] E8M0 of gamma(K) blocks, MFMA A-operand lane order
   uint8_t* vsc;     // MX: [BH][nkt][64][4] E8M0 of V' blocks, MFMA A-operand lane order
