@@ -47,101 +47,116 @@ __device__ __forceinline__ void widen8(const v4i& raw, bool fp16, float (&x)[8])
   }
 }
 
-// ---- K and V chunk statistics: tile staged in LDS with 16-byte loads; one thread per
-// channel adds the chunk's tokens in order (FP64); V max / min (and sum when smoothing) ----
+// ---- K and V chunk statistics.  A wave takes one 64-token chunk of K or of V; lane l owns
+// channels D/64 l .. +D/64-1 and loads the chunk's rows straight into registers, all 64
+// loads in flight (one wave load reads a row's 128 or 256 contiguous bytes), then adds them in
+// token order (FP64); for V also the max / min, and the sum when smoothing ----
 template <int D>
 __global__ __launch_bounds__(256) void kv_stats_kernel(const uint16_t* __restrict__ K,
                                                        const uint16_t* __restrict__ V,
                                                        double* __restrict__ kpart, double* __restrict__ vpart,
                                                        float* __restrict__ vmaxp, float* __restrict__ vminp,
                                                        SeqLayout kl, int Hkv, int nkt, bool fp16, bool smooth_v) {
-  constexpr int RS = D + 8;  // LDS row stride (16-bit elements), 16-byte aligned rows
-  __shared__ __attribute__((aligned(16))) uint16_t sk[kBK * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t sv[kBK * RS];
-  const int u = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  constexpr int CPL = D / 64;  // channels per lane
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int u = 2 * blockIdx.x + (w >> 1), bh = blockIdx.y;  // waves 0, 1: chunk 2x; 2, 3: 2x + 1
+  const bool isv = (w & 1) != 0;
+  if (u >= nkt) return;
   const SeqRows R = seq_rows(kl, bh / Hkv, bh % Hkv, Hkv, D);
   const int t0 = u * kBK;
   if (t0 >= R.len) return;  // past this sequence's keys: no chunk
   const int n = min(kBK, R.len - t0);
-  const size_t base = R.base + (size_t)t0 * R.stride;
+  const uint16_t* src = (isv ? V : K) + R.base + (size_t)t0 * R.stride + CPL * lane;
+  uint32_t raw[kBK];  // row t (clamped to the chunk's last valid row), this lane's channels
 #pragma unroll
-  for (int i = 0; i < kBK * D / 8 / 256; i++) {
-    const int x = tid + 256 * i, row = x / (D / 8), c0 = (x % (D / 8)) * 8;
-    if (row < n) {
-      const size_t off = base + (size_t)row * R.stride + c0;
-      *reinterpret_cast<v4i*>(&sk[row * RS + c0]) = *reinterpret_cast<const v4i*>(K + off);
-      *reinterpret_cast<v4i*>(&sv[row * RS + c0]) = *reinterpret_cast<const v4i*>(V + off);
-    }
+  for (int t = 0; t < kBK; t++) {
+    const size_t off = (size_t)min(t, n - 1) * R.stride;
+    raw[t] = CPL == 2 ? *reinterpret_cast<const uint32_t*>(src + off) : (uint32_t)src[off];
   }
-  __syncthreads();
-  const size_t o = ((size_t)bh * nkt + u) * D;
-  if (tid < D) {
-    double s = 0.0;
-    for (int t0b = 0; t0b < n; t0b += 8) {  // 8 LDS reads in flight; the adds stay in token order
-      float x[8];
+  auto val = [&](int t, int j) {
+    const uint32_t hbits = CPL == 2 ? (j ? raw[t] >> 16 : raw[t] & 0xffffu) : raw[t];
+    return fp16 ? static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(hbits)))
+                : __uint_as_float(hbits << 16);
+  };
+  const size_t o = ((size_t)bh * nkt + u) * D + CPL * lane;
+  double s[CPL];
+  float mx[CPL], mn[CPL];
 #pragma unroll
-      for (int e = 0; e < 8; e++) x[e] = load_in(sk, (size_t)min(t0b + e, kBK - 1) * RS + tid, fp16);
+  for (int j = 0; j < CPL; j++) {
+    s[j] = 0.0;
+    mx[j] = -INFINITY;
+    mn[j] = INFINITY;
+  }
+  if (!isv) {
 #pragma unroll
-      for (int e = 0; e < 8; e++)
-        if (t0b + e < n) s += (double)x[e];
-    }
-    kpart[o + tid] = s;
-  } else if (tid >= 128 && tid - 128 < D) {
-    const int c = tid - 128;
-    double s = 0.0;
-    float mx = -INFINITY, mn = INFINITY;
-    for (int t0b = 0; t0b < n; t0b += 8) {
-      float x[8];
+    for (int t = 0; t < kBK; t++)
+      if (t < n)
 #pragma unroll
-      for (int e = 0; e < 8; e++) x[e] = load_in(sv, (size_t)min(t0b + e, kBK - 1) * RS + c, fp16);
+        for (int j = 0; j < CPL; j++) s[j] += (double)val(t, j);
 #pragma unroll
-      for (int e = 0; e < 8; e++) {
-        if (t0b + e < n) {
-          if (smooth_v) s += (double)x[e];
-          mx = x[e] > mx ? x[e] : mx;  // NaN ignored
-          mn = x[e] < mn ? x[e] : mn;
+    for (int j = 0; j < CPL; j++) kpart[o + j] = s[j];
+  } else {
+#pragma unroll
+    for (int t = 0; t < kBK; t++)
+      if (t < n)
+#pragma unroll
+        for (int j = 0; j < CPL; j++) {
+          const float x = val(t, j);
+          if (smooth_v) s[j] += (double)x;
+          mx[j] = x > mx[j] ? x : mx[j];  // NaN ignored
+          mn[j] = x < mn[j] ? x : mn[j];
         }
-      }
+#pragma unroll
+    for (int j = 0; j < CPL; j++) {
+      if (smooth_v) vpart[o + j] = s[j];
+      vmaxp[o + j] = mx[j];
+      vminp[o + j] = mn[j];
     }
-    if (smooth_v) vpart[o + c] = s;
-    vmaxp[o + c] = mx;
-    vminp[o + c] = mn;
   }
 }
 
 // ---- chunk statistics -> k mean, V_m (when smoothing) and the V scale ----
-// One work-group per (head, 8 channels).  The partials of a stage of 256 chunks are staged in
+// One work-group per (head, 8 channels).  The partials of 64 chunks at a time are staged in
 // LDS by all 256 threads at once (the loads overlap instead of forming a chain of round
-// trips); then one thread per channel adds them in chunk order, as the pinned order requires.
-constexpr int kFinCh = 8;       // channels per work-group
-constexpr int kFinStage = 256;  // chunks staged per round
-__global__ __launch_bounds__(256) void kv_finalize_kernel(const double* __restrict__ kpart,
-                                                          const double* __restrict__ vpart,
-                                                          const float* __restrict__ vmaxp,
-                                                          const float* __restrict__ vminp,
-                                                          float* __restrict__ kmean, float* __restrict__ vmean,
-                                                          float* __restrict__ dv, SeqLayout kl, int Hkv, int d,
-                                                          int nkt, bool smooth_v) {
-  __shared__ double sk[kFinStage][kFinCh];
-  __shared__ double svs[kFinStage][kFinCh];
-  __shared__ float smx[kFinStage][kFinCh];
-  __shared__ float smn[kFinStage][kFinCh];
-  const int bh = blockIdx.x, c0 = blockIdx.y * kFinCh, tid = threadIdx.x;
-  const int M = seq_rows(kl, bh / Hkv, bh % Hkv, Hkv, d).len;  // this sequence's keys
-  const int nk = (M + kBK - 1) / kBK;                           // its chunks
+// trips); then one thread per channel adds them in chunk order, as the pinned order requires:
+// thread c < 8 the K sums, thread 64 + c the V max / min (and sums).
+struct FinArgs {
+  const double* kpart;
+  const double* vpart;
+  const float* vmaxp;
+  const float* vminp;
+  float* kmean;
+  float* vmean;
+  float* dv;
+  SeqLayout kl;
+  int Hkv, d, nkt;
+  bool smooth_v;
+};
+constexpr int kFinCh = 8;                                       // channels per work-group
+constexpr int kFinStage = 64;                                   // chunks staged per round
+constexpr int kFinLds = kFinStage * kFinCh * (8 + 8 + 4 + 4);   // LDS bytes (12 KiB)
+__device__ __forceinline__ void kv_finalize_part(const FinArgs& f, int bh, int c0, int tid,
+                                                 unsigned char* __restrict__ lds) {
+  double* sk = reinterpret_cast<double*>(lds);  // [kFinStage][kFinCh] each
+  double* svs = sk + kFinStage * kFinCh;
+  float* smx = reinterpret_cast<float*>(svs + kFinStage * kFinCh);
+  float* smn = smx + kFinStage * kFinCh;
+  const int M = seq_rows(f.kl, bh / f.Hkv, bh % f.Hkv, f.Hkv, f.d).len;  // this sequence's keys
+  const int nk = (M + kBK - 1) / kBK;                                    // its chunks
   double ks = 0.0, vs = 0.0;
   float mx = -INFINITY, mn = INFINITY;
   for (int u0 = 0; u0 < nk; u0 += kFinStage) {
     const int ns = min(kFinStage, nk - u0);
-#pragma unroll
-    for (int i = 0; i < kFinStage * kFinCh / 256; i++) {
-      const int x = tid + 256 * i, uu = x / kFinCh, cc = x % kFinCh;
+    __syncthreads();  // the previous round's LDS reads are done
+    for (int x = tid; x < kFinStage * kFinCh; x += 256) {
+      const int uu = x / kFinCh, cc = x % kFinCh;
       if (uu < ns) {
-        const size_t o = ((size_t)bh * nkt + u0 + uu) * d + c0 + cc;
-        sk[uu][cc] = kpart[o];
-        if (smooth_v) svs[uu][cc] = vpart[o];
-        smx[uu][cc] = vmaxp[o];
-        smn[uu][cc] = vminp[o];
+        const size_t o = ((size_t)bh * f.nkt + u0 + uu) * f.d + c0 + cc;
+        sk[x] = f.kpart[o];
+        if (f.smooth_v) svs[x] = f.vpart[o];
+        smx[x] = f.vmaxp[o];
+        smn[x] = f.vminp[o];
       }
     }
     __syncthreads();
@@ -149,7 +164,7 @@ __global__ __launch_bounds__(256) void kv_finalize_kernel(const double* __restri
       for (int ub = 0; ub < ns; ub += 8) {  // 8 LDS reads in flight, adds in chunk order
         double x[8];
 #pragma unroll
-        for (int e = 0; e < 8; e++) x[e] = sk[min(ub + e, kFinStage - 1)][tid];
+        for (int e = 0; e < 8; e++) x[e] = sk[min(ub + e, kFinStage - 1) * kFinCh + tid];
 #pragma unroll
         for (int e = 0; e < 8; e++)
           if (ub + e < ns) ks += x[e];
@@ -161,38 +176,41 @@ __global__ __launch_bounds__(256) void kv_finalize_kernel(const double* __restri
         float hx[8], lx[8];
 #pragma unroll
         for (int e = 0; e < 8; e++) {
-          const int uu = min(ub + e, kFinStage - 1);
-          x[e] = smooth_v ? svs[uu][cc] : 0.0;
-          hx[e] = smx[uu][cc];
-          lx[e] = smn[uu][cc];
+          const int uu = min(ub + e, kFinStage - 1) * kFinCh + cc;
+          x[e] = f.smooth_v ? svs[uu] : 0.0;
+          hx[e] = smx[uu];
+          lx[e] = smn[uu];
         }
 #pragma unroll
         for (int e = 0; e < 8; e++) {
           if (ub + e < ns) {
-            if (smooth_v) vs += x[e];
+            if (f.smooth_v) vs += x[e];
             mx = hx[e] > mx ? hx[e] : mx;  // NaN ignored
             mn = lx[e] < mn ? lx[e] : mn;
           }
         }
       }
     }
-    __syncthreads();
   }
-  // the K sum lives in threads 0..7, the V statistics in threads 64..71
   // a sequence without keys (variable-length batches only) gets zero means and the floor scale
   if (tid < kFinCh) {
-    const float km = M > 0 ? (float)(ks / (double)M) : 0.0f;
-    kmean[(size_t)bh * d + c0 + tid] = km;
-  }
-  if (tid >= 64 && tid < 64 + kFinCh) {
+    f.kmean[(size_t)bh * f.d + c0 + tid] = M > 0 ? (float)(ks / (double)M) : 0.0f;
+  } else if (tid >= 64 && tid < 64 + kFinCh) {
     const int c = c0 + tid - 64;
-    const float vm = (smooth_v && M > 0) ? (float)(vs / (double)M) : 0.0f;
-    vmean[(size_t)bh * d + c] = vm;
+    const float vm = (f.smooth_v && M > 0) ? (float)(vs / (double)M) : 0.0f;
+    f.vmean[(size_t)bh * f.d + c] = vm;
     const float a1 = mx - vm, a2 = vm - mn;  // max |fp32(V - V_m)| over the tokens
     const float am = a1 > a2 ? a1 : a2;
     const float a = am > 1e-8f ? am : 1e-8f;
-    dv[(size_t)bh * d + c] = __fdiv_rn(a, 448.0f);
+    f.dv[(size_t)bh * f.d + c] = __fdiv_rn(a, 448.0f);
   }
+}
+
+// work-group x: head x / (d / 8), channels 8 (x % (d / 8)) ..
+__global__ __launch_bounds__(256) void kv_finalize_kernel(FinArgs f) {
+  __shared__ __attribute__((aligned(16))) unsigned char lds[kFinLds];
+  const int per = f.d / kFinCh;
+  kv_finalize_part(f, blockIdx.x / per, kFinCh * (blockIdx.x % per), threadIdx.x, lds);
 }
 
 // ---- Q: block mean (and its bf16 head/tail), gamma(Q), per-token scale, INT8 (F8: E4M3) codes ----
@@ -206,7 +224,8 @@ __global__ __launch_bounds__(256) void q_prep_kernel(const uint16_t* __restrict_
   constexpr int RS = D + 8;
   __shared__ __attribute__((aligned(16))) uint16_t sq[kBQ * RS];
   __shared__ float sm[D];
-  const int i = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int i = blockIdx.x, bh = blockIdx.y;
   const int lane = tid & 63, wave = tid >> 6;
   const SeqRows R = seq_rows(ql, bh / H, bh % H, H, D);
   const int r0 = i * kBQ;
@@ -269,12 +288,7 @@ __global__ __launch_bounds__(256) void q_prep_kernel(const uint16_t* __restrict_
 #pragma unroll
     for (int e = 0; e < 8; e++) am = amax_upd(am, g[e]);
     if constexpr (MX) {
-      // one E8M0 scale per 32 channels: 4 lanes
-#pragma unroll
-      for (int off = 2; off >= 1; off >>= 1) {
-        const float o = __shfl_xor(am, off);
-        am = o > am ? o : am;
-      }
+      am = group_max<4>(am);  // one E8M0 scale per 32 channels: 4 lanes
       const uint32_t code = e8m0_code(am);  // padded rows: amax 0 -> code 0, values 0
       const float sc = __uint_as_float(code << 23);
       uint32_t wd = 0;
@@ -285,11 +299,7 @@ __global__ __launch_bounds__(256) void q_prep_kernel(const uint16_t* __restrict_
       *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(qhat) + row * (D / 2) + c0 / 2) = wd;
       if ((cl & 3) == 0) qsc[row * (D / 32) + cl / 4] = (uint8_t)code;
     } else {
-#pragma unroll
-      for (int off = LPR / 2; off >= 1; off >>= 1) {
-        const float o = __shfl_xor(am, off);
-        am = o > am ? o : am;
-      }
+      am = group_max<LPR>(am);
       const float sc = (r < n) ? (F8 ? e4m3_scale(am) : int8_scale(am)) : 1.0f;
       if (cl == 0) dq[row] = sc;
       uint2 w = make_uint2(0u, 0u);
@@ -406,10 +416,7 @@ __global__ __launch_bounds__(256, MX ? 3 : 4) void kv_quant_kernel(KVArgs a) {
       float m = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; e++) m = amax_upd(m, g[i][e]);
-      float o = __shfl_xor(m, 1);
-      m = o > m ? o : m;
-      o = __shfl_xor(m, 2);
-      m = o > m ? o : m;
+      m = group_max<4>(m);
       const uint32_t code = e8m0_code(m);  // keys >= M: all zero -> code 0, codes 0
       const float sc = __uint_as_float(code << 23);
       uint32_t wd = 0;
@@ -430,12 +437,7 @@ __global__ __launch_bounds__(256, MX ? 3 : 4) void kv_quant_kernel(KVArgs a) {
   } else {
 #pragma unroll
   for (int q = 0; q < 4; q++) {
-    float m = am[q];
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float o = __shfl_xor(m, off);
-      m = o > m ? o : m;
-    }
+    const float m = wave_max(am[q]);
     if (lane == 0) gmax[q][wave] = m;
   }
   __syncthreads();
@@ -600,7 +602,7 @@ __global__ __launch_bounds__(256, MX ? 3 : 4) void kv_quant_kernel(KVArgs a) {
 }  // namespace
 
 hipError_t launch_kv_stats(const Problem& p, const void* k, const void* v, const Workspace& w, hipStream_t s) {
-  const dim3 grid(p.nkt, p.BHkv);
+  const dim3 grid((p.nkt + 1) / 2, p.BHkv);
   if (p.d == 128)
     hipLaunchKernelGGL(kv_stats_kernel<128>, grid, dim3(256), 0, s, (const uint16_t*)k, (const uint16_t*)v,
                        w.kpart, w.vpart, w.vmaxp, w.vminp, p.kl, p.Hkv, p.nkt, p.fp16, p.smooth_v);
@@ -610,9 +612,16 @@ hipError_t launch_kv_stats(const Problem& p, const void* k, const void* v, const
   return hipGetLastError();
 }
 
+FinArgs fin_args(const Problem& p, const Workspace& w) {
+  FinArgs f;
+  f.kpart = w.kpart; f.vpart = w.vpart; f.vmaxp = w.vmaxp; f.vminp = w.vminp;
+  f.kmean = w.kmean; f.vmean = w.vmean; f.dv = w.dv;
+  f.kl = p.kl; f.Hkv = p.Hkv; f.d = p.d; f.nkt = p.nkt; f.smooth_v = p.smooth_v;
+  return f;
+}
+
 hipError_t launch_kv_finalize(const Problem& p, const Workspace& w, hipStream_t s) {
-  hipLaunchKernelGGL(kv_finalize_kernel, dim3(p.BHkv, p.d / kFinCh), dim3(256), 0, s, w.kpart, w.vpart, w.vmaxp,
-                     w.vminp, w.kmean, w.vmean, w.dv, p.kl, p.Hkv, p.d, p.nkt, p.smooth_v);
+  hipLaunchKernelGGL(kv_finalize_kernel, dim3(p.BHkv * (p.d / kFinCh)), dim3(256), 0, s, fin_args(p, w));
   return hipGetLastError();
 }
 

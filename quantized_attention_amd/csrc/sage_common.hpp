@@ -148,10 +148,26 @@ __device__ inline uint32_t f32_to_fp16_bits(float x) {
   return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<_Float16>(x)));
 }
 
-// |x| max that ignores NaN (a NaN element does not set a scale).
-__device__ inline float amax_upd(float m, float x) {
-  float a = fabsf(x);
-  return (a > m) ? a : m;
+// |x| max that ignores NaN (a NaN element does not set a scale): IEEE maxNum of the magnitudes.
+__device__ inline float amax_upd(float m, float x) { return fmaxf(m, fabsf(x)); }
+
+// Lane value from a DPP pattern of the lane's row (16 lanes).
+template <int CTRL>
+__device__ inline float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+// Max over aligned groups of G lanes (G = 2, 4, 8 or 16), every lane of a group receiving it,
+// for values that are not NaN: lane swaps inside quads, then the half-row and row mirrors
+// (each exchanges the two halves of the group reduced so far).  No LDS round trips.
+template <int G>
+__device__ inline float group_max(float v) {
+  static_assert(G == 2 || G == 4 || G == 8 || G == 16, "group of 2, 4, 8 or 16 lanes");
+  v = fmaxf(v, dpp_f32<0xB1>(v));                     // quad_perm [1, 0, 3, 2]
+  if constexpr (G >= 4) v = fmaxf(v, dpp_f32<0x4E>(v));   // quad_perm [2, 3, 0, 1]
+  if constexpr (G >= 8) v = fmaxf(v, dpp_f32<0x141>(v));  // row_half_mirror
+  if constexpr (G >= 16) v = fmaxf(v, dpp_f32<0x140>(v)); // row_mirror
+  return v;
 }
 
 // Symmetric INT8 code: RNE of x / scale (IEEE FP32 division), clamped to +-127; NaN -> 0.
@@ -162,23 +178,48 @@ __device__ inline int8_t int8_code(float x, float scale) {
   return static_cast<int8_t>(static_cast<int>(y));
 }
 
+// Max over the 64 lanes of a wave (values that are not NaN), every lane receiving it: the
+// row maxima, then rows l and l ^ 16, then the wave halves (gfx950 lane-swap instructions).
+__device__ inline float wave_max(float v) {
+  v = group_max<16>(v);
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // Eight INT8 codes int8_code(x[e], scale), packed little-endian into two words, from the
-// products with rcp = __fdiv_rn(1, scale).  |x / scale| <= 127.0001, and x * rcp is within
-// |x / scale| * 2^-23 < 1.6e-5 of it; the IEEE quotient is within half an ulp (< 4e-6) of it
-// too.  So the two round to the same integer unless a half-integer lies within 2e-5 of
-// x * rcp.  A chunk holding such an element (about 1 element in 5000), or a NaN, is coded
-// again with the division: one branch per chunk, not per element.
+// products with rcp = __fdiv_rn(1, scale).  |x / scale| <= 127.0001, and the exact product
+// u = x * rcp is within |x / scale| * 2^-23 < 1.6e-5 of it; the IEEE quotient is within half
+// an ulp (< 4e-6) of it too.  So the two round to the same integer unless a half-integer lies
+// within 2e-5 of u.  t = fma(x, rcp, 1.5 * 2^23) rounds u to the nearest integer n (half to
+// even) and holds n + 1.5 * 2^23 exactly, so n's two's-complement low byte is t's low byte;
+// |x| <= amax keeps |n| <= 127.  A chunk with some |u - n| >= 0.4999 (about 1 in 5000), or a
+// NaN (whose t lies above the integers' bit range), is coded again with the division: one
+// branch per chunk, not per element.
 __device__ inline uint2 int8_pack8_rcp(const float (&x)[8], float scale, float rcp) {
-  uint32_t w[2] = {0u, 0u};
-  uint32_t near = 0u;
+  constexpr float kMagic = 12582912.0f;  // 1.5 * 2^23: floats in [2^23, 2^24) step by 1
+  uint32_t t[8];
+  float rmax = 0.0f;
+  uint32_t tmax = 0u;
 #pragma unroll
   for (int e = 0; e < 8; e++) {
-    const float q = x[e] * rcp, n = rintf(q);
-    near |= static_cast<uint32_t>(!(fabsf(q - n) < 0.4999f));
-    const float y = n > 127.0f ? 127.0f : (n < -127.0f ? -127.0f : n);
-    w[e >> 2] |= (uint32_t)(uint8_t)static_cast<int8_t>(static_cast<int>(y)) << (8 * (e & 3));
+    const float tf = fmaf(x[e], rcp, kMagic);
+    const float n = tf - kMagic;
+    rmax = fmaxf(rmax, fabsf(fmaf(x[e], rcp, -n)));  // a NaN residual is caught by tmax
+    t[e] = __float_as_uint(tf);
+    tmax = max(tmax, t[e]);
   }
-  if (near) {
+  uint32_t w[2];
+#pragma unroll
+  for (int k = 0; k < 2; k++) {
+    // low bytes of t[4k .. 4k + 3] -> bytes 0 .. 3 (v_perm_b32: selector byte i picks byte i
+    // of {S0, S1} as bytes 7..4, 3..0; 0x0c gives zero)
+    const uint32_t lo = __builtin_amdgcn_perm(t[4 * k + 1], t[4 * k], 0x0c0c0400u);
+    const uint32_t hi = __builtin_amdgcn_perm(t[4 * k + 3], t[4 * k + 2], 0x04000c0cu);
+    w[k] = lo | hi;
+  }
+  if (!(rmax < 0.4999f) || tmax > 0x4B40007Fu) {  // 0x4B40007F: the bits of 1.5 * 2^23 + 127
     w[0] = w[1] = 0u;
 #pragma unroll
     for (int e = 0; e < 8; e++) w[e >> 2] |= (uint32_t)(uint8_t)int8_code(x[e], scale) << (8 * (e & 3));

@@ -79,11 +79,7 @@ __global__ __launch_bounds__(256) void sb_quant_kernel(const uint16_t* __restric
       for (int k = 0; k < 8; k++) x[i][k] = 0.0f;
     }
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float o = __shfl_xor(am, off);
-    am = o > am ? o : am;
-  }
+  am = wave_max(am);
   if (lane == 0) wmax[wave] = am;
   __syncthreads();
   am = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
@@ -348,11 +344,8 @@ __device__ __forceinline__ void sb_pair(const v4i (&kf)[2][D / 32], const v4i (&
 
 // Block maxima of P and |dS| over the work-group's 128 x 64 block (4 waves; two barriers).
 __device__ __forceinline__ void sb_block_max(float pm, float dm, float* xs, int lane, int w, float& pmax, float& dmax) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    pm = fmaxf(pm, __shfl_xor(pm, off));
-    dm = fmaxf(dm, __shfl_xor(dm, off));
-  }
+  pm = wave_max(pm);
+  dm = wave_max(dm);
   if (lane == 0) {
     xs[w] = pm;
     xs[4 + w] = dm;
