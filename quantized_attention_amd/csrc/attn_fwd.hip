@@ -118,11 +118,13 @@ __device__ __forceinline__ void qk_tile(const int8_t* __restrict__ sK, const v4i
 // The rest of one tile for one wave, from its INT32 (or FP32) scores: dequantize, online
 // softmax, P^ V^ into O.  `masked` (wave-uniform) selects the causal / ragged-tail mask;
 // interior tiles skip it.
+// vlo / vhi: this lane's byte offsets of its two 16-byte V^ chunks in a slot's first 32-channel
+// sub-tile (the sub-tiles follow at 32 * kBK bytes).
 template <int D, bool CAUSAL, bool ACC_VALU, typename ACC>
 __device__ __forceinline__ void softmax_pv(const ACC (&acc)[2], const uint8_t* __restrict__ sV,
                                            const float* __restrict__ sDS, const float* __restrict__ sDK,
-                                           float dql, int h, int col, int key0, int qrow, int M, bool masked,
-                                           v16f (&O)[D / 32], float& m_run, float& l_run) {
+                                           float dql, int h, int col, int vlo, int vhi, int key0, int qrow, int M,
+                                           bool masked, v16f (&O)[D / 32], float& m_run, float& l_run) {
   constexpr int NKS = D / 32;
   // ---- dequantize (dQ dK sm_scale log2e) and add Delta S ----
   float sc[2][16];
@@ -157,7 +159,8 @@ __device__ __forceinline__ void softmax_pv(const ACC (&acc)[2], const uint8_t* _
   const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile, exactly 1 if m is unchanged
   m_run = m_new;
   // ---- P = 448 P~ (FP32), row sum, E4M3 pack in the PV B-operand order ----
-  float psum = 0.0f;
+  // l = alpha l + rowsum P, as one chain that starts from alpha l
+  float lsum;
   v8i pf;
 #pragma unroll
   for (int T = 0; T < 2; T++) {
@@ -167,7 +170,8 @@ __device__ __forceinline__ void softmax_pv(const ACC (&acc)[2], const uint8_t* _
       const float p1 = fast_exp2(sc[T][4 * q4 + 1] - base);
       const float p2 = fast_exp2(sc[T][4 * q4 + 2] - base);
       const float p3 = fast_exp2(sc[T][4 * q4 + 3] - base);
-      psum += (p0 + p1) + (p2 + p3);
+      const float g = (p0 + p1) + (p2 + p3);
+      lsum = (T == 0 && q4 == 0) ? fmaf(l_run, alpha, g) : lsum + g;
       // the instruction keeps the other half-word of its destination: seed it with a dead
       // register (the score p0 came from) so that no copy is needed
       int wd = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, __float_as_int(sc[T][4 * q4 + 0]), false);
@@ -175,7 +179,7 @@ __device__ __forceinline__ void softmax_pv(const ACC (&acc)[2], const uint8_t* _
       pf[4 * T + q4] = wd;
     }
   }
-  l_run = fmaf(l_run, alpha, psum);
+  l_run = lsum;
   // The packed P^ must exist before the rescale branch below: otherwise the exp work is sunk
   // past it and a rescale waits on the previous tile's PV MFMAs instead of overlapping them.
   asm volatile("" : "+v"(pf));
@@ -190,8 +194,8 @@ __device__ __forceinline__ void softmax_pv(const ACC (&acc)[2], const uint8_t* _
   }
 #pragma unroll
   for (int c = 0; c < NKS; c++) {
-    const v4i lo = *reinterpret_cast<const v4i*>(&sV[Tiles<D>::voff(32 * c + col, 2 * h)]);
-    const v4i hi = *reinterpret_cast<const v4i*>(&sV[Tiles<D>::voff(32 * c + col, 2 * h + 1)]);
+    const v4i lo = *reinterpret_cast<const v4i*>(&sV[vlo + 32 * kBK * c]);
+    const v4i hi = *reinterpret_cast<const v4i*>(&sV[vhi + 32 * kBK * c]);
     const v8i vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     if (ACC_VALU) {
       v16f R;
@@ -260,6 +264,10 @@ __global__ __launch_bounds__(256, OCC) void attn_fwd_kernel(AttnArgs a) {
     for (int s = 0; s < NKS; s++) qf[s] = *reinterpret_cast<const v4i*>(qp + 32 * s);
   }
   const float dql = a.dq[(size_t)bh * a.Np + qrow] * a.qk_scale;
+  // V^ fragment offsets (the swizzle of rows 32 c + col does not depend on c); kept in two
+  // registers rather than recomputed per tile
+  int vlo = TL::voff(col, 2 * h), vhi = TL::voff(col, 2 * h + 1);
+  asm volatile("" : "+v"(vlo), "+v"(vhi));
 
   v16f O[NKS];
 #pragma unroll
@@ -329,7 +337,7 @@ __global__ __launch_bounds__(256, OCC) void attn_fwd_kernel(AttnArgs a) {
         const int key0 = j * kBK;
         const bool masked = (CAUSAL && key0 + kBK - 1 > wq0 + coff) || (key0 + kBK > mseq);
         const int b = j % NB;
-        softmax_pv<D, CAUSAL, ACC_VALU, acc_t<QF8>>(cur, sV[b], sDS[b], sDK[b], dql, h, col, key0, qrow + coff, mseq, masked, O,
+        softmax_pv<D, CAUSAL, ACC_VALU, acc_t<QF8>>(cur, sV[b], sDS[b], sDK[b], dql, h, col, vlo, vhi, key0, qrow + coff, mseq, masked, O,
                                         m_run, l_run);
       }
       publish(j + 3 < jend);  // tile j+2 must be complete; j+3 may still be arriving
@@ -371,7 +379,7 @@ __global__ __launch_bounds__(256, OCC) void attn_fwd_kernel(AttnArgs a) {
         const bool masked = (CAUSAL && key0 + kBK - 1 > wq0 + coff) || (key0 + kBK > mseq);
         acc_t<QF8> acc[2];
         qk_tile<D, QF8>(sK[b], qf, h, col, acc);
-        softmax_pv<D, CAUSAL, ACC_VALU, acc_t<QF8>>(acc, sV[b], sDS[b], sDK[b], dql, h, col, key0, qrow + coff, mseq, masked, O,
+        softmax_pv<D, CAUSAL, ACC_VALU, acc_t<QF8>>(acc, sV[b], sDS[b], sDK[b], dql, h, col, vlo, vhi, key0, qrow + coff, mseq, masked, O,
                                         m_run, l_run);
       }
       publish_n(min(NB - 2, jend - j - 2));
