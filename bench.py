@@ -39,10 +39,10 @@ PEAK_TOPS_FP4 = 10100.0  # MI355X dense MXFP4 MFMA peak, 10.1 PFLOP/s (the MX va
 # the kernel source it was taken on: the hash of that fused kernel's sources is checked,
 # and a changed kernel reports traffic null until the counters are taken again.
 TRAFFIC_BYTES = {
-    "prefill32k": {"source_sha256_16": "225170728a154336",
-                   "fetch_bytes": 1783144647, "write_bytes": 271008800},
-    "mxfp4_32k": {"source_sha256_16": "bae1660b00b68f1c",
-                  "fetch_bytes": 1694341138, "write_bytes": 201326624},
+    "prefill32k": {"source_sha256_16": "a75e0fb6e5de2ed2",
+                   "fetch_bytes": 1803111707, "write_bytes": 271033888},
+    "mxfp4_32k": {"source_sha256_16": "d063131a3c4d42dc",
+                  "fetch_bytes": 1694310863, "write_bytes": 201326976},
 }
 _COMMON_SOURCES = ("quantized_attention_amd/csrc/attn_device.hpp", "quantized_attention_amd/csrc/sage_common.hpp")
 KERNEL_SOURCES = {
