@@ -115,6 +115,24 @@ __global__ __launch_bounds__(256) void sb_quant_kernel(const uint16_t* __restric
   }
 }
 
+// An LDS tile of R rows of RB bytes, unpadded; the 16-byte chunks of a row are XOR-swizzled so
+// that the 16 lanes one ds_read_b128 serves at once (16 consecutive rows, one chunk column)
+// hit 16 distinct 16-byte bank groups.  Filled by LDS DMA: instruction i of wave w writes the
+// tile's bytes [1024 (NPW w + i), +1024), lane l the 16-byte chunk 64 (NPW w + i) + l.
+template <int R, int RB>
+struct SbTile {
+  static constexpr int BYTES = R * RB, CH = RB / 16, RPL = RB >= 256 ? 1 : 256 / RB, NPW = BYTES / 4096;
+  static_assert(BYTES % 4096 == 0 && CH >= 4 && CH <= 16, "tile shape");
+  __device__ static int swz(int r) { return (r / RPL) & (CH - 1); }
+  __device__ static int off(int r, int c) { return r * RB + 16 * (c ^ swz(r)); }
+  // the row and logical chunk that lane `lane` of wave w's instruction i fills
+  __device__ static void src(int w, int i, int lane, int& r, int& c) {
+    const int q = (NPW * w + i) * 64 + lane;
+    r = q / CH;
+    c = (q % CH) ^ swz(r);
+  }
+};
+
 struct FwdArgs {
   const int8_t* qh;  // [BH][Np][D]
   const float* sq;   // [BH][nqb]
@@ -128,14 +146,17 @@ struct FwdArgs {
   float qk_scale;    // sm_scale * log2(e)
 };
 
-// ---- forward: one work-group per (head, 128-query block), wave w owns queries 32w.. ----
+// ---- forward: one work-group per (head, 128-query block), wave w owns queries 32w..; the key
+// block's K^ rows and V^ transposed stream into a 2-slot LDS ring by DMA ----
 template <int D, bool CAUSAL, int OUT>
 __global__ __launch_bounds__(256, 2) void sb_fwd_kernel(FwdArgs a) {
   constexpr int NKS = D / 32;
-  constexpr int KS = D + 16, VS = kBK + 16;  // padded LDS row strides (bytes)
-  __shared__ __attribute__((aligned(16))) int8_t sK[kBK * KS];
-  __shared__ __attribute__((aligned(16))) int8_t sV[D * VS];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
+  using TK = SbTile<kBK, D>;  // K^ rows
+  using TV = SbTile<D, kBK>;  // V^ transposed, keys in i8perm order
+  __shared__ __attribute__((aligned(1024))) int8_t sK[2][TK::BYTES];
+  __shared__ __attribute__((aligned(1024))) int8_t sV[2][TV::BYTES];
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bh = blockIdx.x / a.nqb, qi = blockIdx.x % a.nqb;
   const int qb = CAUSAL ? (a.nqb - 1 - qi) : qi;
   const int q0 = qb * kBQ, wq0 = q0 + 32 * w, qrow = wq0 + col;
@@ -153,86 +174,102 @@ __global__ __launch_bounds__(256, 2) void sb_fwd_kernel(FwdArgs a) {
     for (int r = 0; r < 16; r++) O[c][r] = 0.0f;
   float m_run = -FLT_MAX, l_run = 0.0f;
   const int jend = CAUSAL ? max(0, min(a.nkt, (q0 + kBQ + a.coff + kBK - 1) / kBK)) : a.nkt;
+  int ko[TK::NPW], vo[TV::NPW];  // per-lane DMA source offsets inside a block
+#pragma unroll
+  for (int i = 0; i < TK::NPW; i++) {
+    int r, c;
+    TK::src(w, i, lane, r, c);
+    ko[i] = r * D + 16 * c;
+  }
+#pragma unroll
+  for (int i = 0; i < TV::NPW; i++) {
+    int r, c;
+    TV::src(w, i, lane, r, c);
+    vo[i] = r * kBK + 16 * c;
+  }
+  auto dma = [&](int j, int b) {
+    const int8_t* kt = a.kh + ((size_t)bh * a.Mp + (size_t)j * kBK) * D;
+    const int8_t* vt = a.vt + ((size_t)bh * a.nkt + j) * (size_t)D * kBK;
+#pragma unroll
+    for (int i = 0; i < TK::NPW; i++) dma16(lds_addr(&sK[b][(TK::NPW * w + i) * 1024]), kt, ko[i]);
+#pragma unroll
+    for (int i = 0; i < TV::NPW; i++) dma16(lds_addr(&sV[b][(TV::NPW * w + i) * 1024]), vt, vo[i]);
+  };
+  if (jend > 0) dma(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // block 0 landed
   for (int j = 0; j < jend; j++) {
-    __syncthreads();  // the previous tile's LDS reads are done
-    {
-      const int8_t* kt = a.kh + ((size_t)bh * a.Mp + (size_t)j * kBK) * D;
-      const int8_t* vt = a.vt + ((size_t)bh * a.nkt + j) * (size_t)D * kBK;
-      for (int e = tid; e < kBK * D / 16; e += 256) {
-        const int r = e / (D / 16), c = (e % (D / 16)) * 16;
-        *reinterpret_cast<v4i*>(&sK[r * KS + c]) = *reinterpret_cast<const v4i*>(kt + (size_t)r * D + c);
-      }
-      for (int e = tid; e < D * kBK / 16; e += 256) {
-        const int r = e / (kBK / 16), c = (e % (kBK / 16)) * 16;
-        *reinterpret_cast<v4i*>(&sV[r * VS + c]) = *reinterpret_cast<const v4i*>(vt + (size_t)r * kBK + c);
-      }
-    }
-    __syncthreads();
+    const int b = j & 1;
+    if (j + 1 < jend) dma(j + 1, b ^ 1);  // the slot block j-1 left (freed by the last barrier)
     const int key0 = j * kBK;
-    if (CAUSAL && key0 > wq0 + 31 + a.coff) continue;  // every key of the tile is masked for this wave
-    v16i acc[2];
-#pragma unroll
-    for (int T = 0; T < 2; T++) {
-#pragma unroll
-      for (int r = 0; r < 16; r++) acc[T][r] = 0;
-#pragma unroll
-      for (int s = 0; s < NKS; s++) {
-        const v4i kf = *reinterpret_cast<const v4i*>(&sK[(32 * T + col) * KS + 32 * s + 16 * h]);
-        acc[T] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[s], acc[T], 0, 0, 0);
-      }
-    }
-    const float mul = sqk * a.sk[(size_t)bh * a.nkt + j];
-    float sc[2][16];
-    int lim = a.M - 1 - key0;
-    if (CAUSAL) lim = min(lim, qrow + a.coff - key0);
-    lim -= 4 * h;
-    float rm = -INFINITY;
-#pragma unroll
-    for (int T = 0; T < 2; T++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const float x = (float)acc[T][r] * mul;
-        sc[T][r] = (32 * T + 8 * (r >> 2) + (r & 3) <= lim) ? x : -INFINITY;
-        rm = fmaxf(rm, sc[T][r]);
-      }
-    rm = pair_max(rm);  // the row's max over this tile
-    const float m_new = fmaxf(m_run, rm);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-    // e = 127 P / (the row's block max of P) = 127 exp2(S - rm); P^ = rne(e)
-    const float base = (rm == -INFINITY) ? 0.0f : rm - kLog2_127;
-    float esum = 0.0f;
-    v4i pb[2];
-#pragma unroll
-    for (int T = 0; T < 2; T++)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; q4++) {
-        uint32_t wd = 0;
-#pragma unroll
-        for (int k = 0; k < 4; k++) {
-          const float e = fast_exp2(sc[T][4 * q4 + k] - base);
-          esum += e;
-          wd |= (uint32_t)(int)rintf(e) << (8 * k);
-        }
-        pb[T][q4] = (int)wd;
-      }
-    esum = pair_sum(esum);
-    const float sp = (rm == -INFINITY) ? 0.0f : fast_exp2(rm - m_new) * (1.0f / 127.0f);  // s_P
-    l_run = fmaf(l_run, alpha, esum * sp);
-    const float osc = sp * a.sv[(size_t)bh * a.nkt + j];
-#pragma unroll
-    for (int c = 0; c < NKS; c++) {
-      v16i R;
-#pragma unroll
-      for (int r = 0; r < 16; r++) R[r] = 0;
+    if (!(CAUSAL && key0 > wq0 + 31 + a.coff)) {  // else every key of the block is masked for this wave
+      const int8_t* cK = sK[b];
+      const int8_t* cV = sV[b];
+      v16i acc[2];
 #pragma unroll
       for (int T = 0; T < 2; T++) {
-        const v4i vf = *reinterpret_cast<const v4i*>(&sV[(32 * c + col) * VS + 32 * T + 16 * h]);
-        R = __builtin_amdgcn_mfma_i32_32x32x32_i8(vf, pb[T], R, 0, 0, 0);
-      }
 #pragma unroll
-      for (int r = 0; r < 16; r++) O[c][r] = fmaf((float)R[r], osc, O[c][r] * alpha);
+        for (int r = 0; r < 16; r++) acc[T][r] = 0;
+#pragma unroll
+        for (int s = 0; s < NKS; s++) {
+          const v4i kf = *reinterpret_cast<const v4i*>(&cK[TK::off(32 * T + col, 2 * s + h)]);
+          acc[T] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[s], acc[T], 0, 0, 0);
+        }
+      }
+      const float mul = sqk * a.sk[(size_t)bh * a.nkt + j];
+      float sc[2][16];
+      int lim = a.M - 1 - key0;
+      if (CAUSAL) lim = min(lim, qrow + a.coff - key0);
+      lim -= 4 * h;
+      float rm = -INFINITY;
+#pragma unroll
+      for (int T = 0; T < 2; T++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+          const float x = (float)acc[T][r] * mul;
+          sc[T][r] = (32 * T + 8 * (r >> 2) + (r & 3) <= lim) ? x : -INFINITY;
+          rm = fmaxf(rm, sc[T][r]);
+        }
+      rm = pair_max(rm);  // the row's max over this tile
+      const float m_new = fmaxf(m_run, rm);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      // e = 127 P / (the row's block max of P) = 127 exp2(S - rm); P^ = rne(e)
+      const float base = (rm == -INFINITY) ? 0.0f : rm - kLog2_127;
+      float esum = 0.0f;
+      v4i pb[2];
+#pragma unroll
+      for (int T = 0; T < 2; T++)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; q4++) {
+          uint32_t wd = 0;
+#pragma unroll
+          for (int k = 0; k < 4; k++) {
+            const float e = fast_exp2(sc[T][4 * q4 + k] - base);
+            esum += e;
+            wd |= (uint32_t)(int)rintf(e) << (8 * k);
+          }
+          pb[T][q4] = (int)wd;
+        }
+      esum = pair_sum(esum);
+      const float sp = (rm == -INFINITY) ? 0.0f : fast_exp2(rm - m_new) * (1.0f / 127.0f);  // s_P
+      l_run = fmaf(l_run, alpha, esum * sp);
+      const float osc = sp * a.sv[(size_t)bh * a.nkt + j];
+#pragma unroll
+      for (int c = 0; c < NKS; c++) {
+        v16i R;
+#pragma unroll
+        for (int r = 0; r < 16; r++) R[r] = 0;
+#pragma unroll
+        for (int T = 0; T < 2; T++) {
+          const v4i vf = *reinterpret_cast<const v4i*>(&cV[TV::off(32 * c + col, 2 * T + h)]);
+          R = __builtin_amdgcn_mfma_i32_32x32x32_i8(vf, pb[T], R, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; r++) O[c][r] = fmaf((float)R[r], osc, O[c][r] * alpha);
+      }
     }
+    // block j+1 landed (this wave's DMAs, then everyone's); slot b may be refilled
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
   if (qrow >= a.N) return;
   const float inv = 1.0f / l_run;
@@ -313,9 +350,10 @@ struct BwdArgs {
 // The elementwise part shared by both backward kernels, for one wave's 32 queries (lane = query,
 // 16 keys per 32-key half): S^T from K^ / Q^ fragments, P = exp2(S - L2), dP^T = V dO^T on the
 // bf16 MFMA from the 16-bit V tile in LDS, dS = P (dP - D).  Masked pairs give P = dS = 0.
-template <int D, bool FP16>
+// vfrag(T, s): the lane's 16 bytes (8 values, channels 16 s + 8 h ..) of V row 32 T + col.
+template <int D, bool FP16, typename VF>
 __device__ __forceinline__ void sb_pair(const v4i (&kf)[2][D / 32], const v4i (&qf)[D / 32], const v4i (&of)[D / 16],
-                                        const uint16_t* __restrict__ sVb, int vs, float mul, float l2, float dr,
+                                        VF&& vfrag, float mul, float l2, float dr,
                                         int lim, int h, int col, float (&P)[2][16], float (&dS)[2][16]) {
 #pragma unroll
   for (int T = 0; T < 2; T++) {
@@ -329,20 +367,20 @@ __device__ __forceinline__ void sb_pair(const v4i (&kf)[2][D / 32], const v4i (&
     for (int r = 0; r < 16; r++) dp[r] = 0.0f;
 #pragma unroll
     for (int s = 0; s < D / 16; s++) {
-      const v4i vf = *reinterpret_cast<const v4i*>(sVb + (32 * T + col) * vs + 16 * s + 8 * h);
-      dp = mfma16<FP16>(vf, of[s], dp);
+      dp = mfma16<FP16>(vfrag(T, s), of[s], dp);
     }
 #pragma unroll
     for (int r = 0; r < 16; r++) {
       const bool vis = 32 * T + 8 * (r >> 2) + (r & 3) <= lim;
       const float p = vis ? fast_exp2((float)acc[r] * mul - l2) : 0.0f;
       P[T][r] = p;
-      dS[T][r] = p * (dp[r] - dr);
+      dS[T][r] = vis ? p * (dp[r] - dr) : 0.0f;  // a masked key's V row may be a stand-in
     }
   }
 }
 
-// Block maxima of P and |dS| over the work-group's 128 x 64 block (4 waves; two barriers).
+// Block maxima of P and |dS| over the work-group's 128 x 64 block (4 waves; one barrier; xs is
+// rewritten only after the caller's next barrier).
 __device__ __forceinline__ void sb_block_max(float pm, float dm, float* xs, int lane, int w, float& pmax, float& dmax) {
   pm = wave_max(pm);
   dm = wave_max(dm);
@@ -350,7 +388,7 @@ __device__ __forceinline__ void sb_block_max(float pm, float dm, float* xs, int 
     xs[w] = pm;
     xs[4 + w] = dm;
   }
-  __syncthreads();
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // LDS only: tile DMAs stay in flight
   pmax = fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3]));
   dmax = fmaxf(fmaxf(xs[4], xs[5]), fmaxf(xs[6], xs[7]));
 }
@@ -388,15 +426,21 @@ __device__ __forceinline__ void sb_q_frags(const BwdArgs& a, int bh, int qrow, i
   }
 }
 
-// ---- dQ: one work-group per (head, 128-query block); loops over the key blocks ----
+// ---- dQ: one work-group per (head, 128-query block); loops over the key blocks.  The key
+// block's K^ rows, K^ transposed and 16-bit V rows stream into a 2-slot LDS ring by DMA: block
+// j+1 is in flight while block j is computed, one barrier per block publishes the next ----
 template <int D, bool CAUSAL, bool FP16>
 __global__ __launch_bounds__(256, 2) void sb_dq_kernel(BwdArgs a) {
-  constexpr int NKS = D / 32, KS = D + 16, TS = kBK + 16, VS = D + 8;
-  __shared__ __attribute__((aligned(16))) int8_t sK[kBK * KS];
-  __shared__ __attribute__((aligned(16))) int8_t sKt[D * TS];
-  __shared__ __attribute__((aligned(16))) uint16_t sVb[kBK * VS];
+  constexpr int NKS = D / 32;
+  using TK = SbTile<kBK, D>;      // K^ rows
+  using TT = SbTile<D, kBK>;      // K^ transposed, keys in i8perm order
+  using TV = SbTile<kBK, 2 * D>;  // V rows, 16-bit
+  __shared__ __attribute__((aligned(1024))) int8_t sK[2][TK::BYTES];
+  __shared__ __attribute__((aligned(1024))) int8_t sKt[2][TT::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sVb[2][TV::BYTES];
   __shared__ float xs[8];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bh = blockIdx.x / a.nqb, qi = blockIdx.x % a.nqb;
   const int qb = CAUSAL ? (a.nqb - 1 - qi) : qi;
   const int q0 = qb * kBQ, qrow = q0 + 32 * w + col;
@@ -412,33 +456,64 @@ __global__ __launch_bounds__(256, 2) void sb_dq_kernel(BwdArgs a) {
     for (int r = 0; r < 16; r++) dq[c][r] = 0.0f;
   float rs = 0.0f;
   const int jend = CAUSAL ? max(0, min(a.nkt, (q0 + kBQ + a.coff + kBK - 1) / kBK)) : a.nkt;
+
+  // per-lane DMA source offsets inside a block (V: row and byte column; its rows are clamped to
+  // the last key, a stand-in for keys >= M, whose P and dS are 0)
+  int ko[TK::NPW], to[TT::NPW], vr[TV::NPW], vc[TV::NPW];
+#pragma unroll
+  for (int i = 0; i < TK::NPW; i++) {
+    int r, c;
+    TK::src(w, i, lane, r, c);
+    ko[i] = r * D + 16 * c;
+  }
+#pragma unroll
+  for (int i = 0; i < TT::NPW; i++) {
+    int r, c;
+    TT::src(w, i, lane, r, c);
+    to[i] = r * kBK + 16 * c;
+  }
+#pragma unroll
+  for (int i = 0; i < TV::NPW; i++) {
+    int r, c;
+    TV::src(w, i, lane, r, c);
+    vr[i] = r;
+    vc[i] = 16 * c;
+  }
+  auto dma = [&](int j, int b) {
+    const int8_t* kr = a.kh + ((size_t)bh * a.Mp + (size_t)j * kBK) * D;
+    const int8_t* kt = a.kt + ((size_t)bh * a.nkt + j) * (size_t)D * kBK;
+    const uint16_t* vb = a.V + ((size_t)bh * a.M + (size_t)j * kBK) * D;
+    const int vlast = a.M - 1 - j * kBK;  // >= 0: block j holds a key
+#pragma unroll
+    for (int i = 0; i < TK::NPW; i++) dma16(lds_addr(&sK[b][(TK::NPW * w + i) * 1024]), kr, ko[i]);
+#pragma unroll
+    for (int i = 0; i < TT::NPW; i++) dma16(lds_addr(&sKt[b][(TT::NPW * w + i) * 1024]), kt, to[i]);
+#pragma unroll
+    for (int i = 0; i < TV::NPW; i++)
+      dma16(lds_addr(&sVb[b][(TV::NPW * w + i) * 1024]), vb, min(vr[i], vlast) * (2 * D) + vc[i]);
+  };
+  if (jend > 0) dma(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // block 0 landed
   for (int j = 0; j < jend; j++) {
-    __syncthreads();
-    {
-      const int8_t* kr = a.kh + ((size_t)bh * a.Mp + (size_t)j * kBK) * D;
-      const int8_t* kt = a.kt + ((size_t)bh * a.nkt + j) * (size_t)D * kBK;
-      for (int e = tid; e < kBK * D / 16; e += 256) {
-        const int r = e / (D / 16), c = (e % (D / 16)) * 16;
-        *reinterpret_cast<v4i*>(&sK[r * KS + c]) = *reinterpret_cast<const v4i*>(kr + (size_t)r * D + c);
-      }
-      for (int e = tid; e < D * kBK / 16; e += 256) {
-        const int r = e / (kBK / 16), c = (e % (kBK / 16)) * 16;
-        *reinterpret_cast<v4i*>(&sKt[r * TS + c]) = *reinterpret_cast<const v4i*>(kt + (size_t)r * kBK + c);
-      }
-      sb_load_v<D>(a.V + (size_t)bh * a.M * D, a.M, j * kBK, sVb, VS, tid);
-    }
-    __syncthreads();
+    const int b = j & 1;
+    if (j + 1 < jend) dma(j + 1, b ^ 1);  // the slot block j-1 left (freed by the last barrier)
+    const int8_t* cK = sK[b];
+    const int8_t* cKt = sKt[b];
+    const uint8_t* cV = sVb[b];
     v4i kf[2][NKS];
 #pragma unroll
     for (int T = 0; T < 2; T++)
 #pragma unroll
-      for (int s = 0; s < NKS; s++) kf[T][s] = *reinterpret_cast<const v4i*>(&sK[(32 * T + col) * KS + 32 * s + 16 * h]);
+      for (int s = 0; s < NKS; s++) kf[T][s] = *reinterpret_cast<const v4i*>(&cK[TK::off(32 * T + col, 2 * s + h)]);
     const int key0 = j * kBK;
     int lim = a.M - 1 - key0;
     if (CAUSAL) lim = min(lim, qrow + a.coff - key0);
     lim -= 4 * h;
     float P[2][16], dS[2][16];
-    sb_pair<D, FP16>(kf, qf, of, sVb, VS, sq * a.sk[(size_t)bh * a.nkt + j] * a.qk_scale, l2, dr, lim, h, col, P, dS);
+    auto vfrag = [&](int T, int s) {
+      return *reinterpret_cast<const v4i*>(&cV[TV::off(32 * T + col, 2 * s + h)]);
+    };
+    sb_pair<D, FP16>(kf, qf, of, vfrag, sq * a.sk[(size_t)bh * a.nkt + j] * a.qk_scale, l2, dr, lim, h, col, P, dS);
     float pm = 0.0f, dm = 0.0f;
 #pragma unroll
     for (int T = 0; T < 2; T++)
@@ -470,12 +545,14 @@ __global__ __launch_bounds__(256, 2) void sb_dq_kernel(BwdArgs a) {
       for (int r = 0; r < 16; r++) R[r] = 0;
 #pragma unroll
       for (int T = 0; T < 2; T++) {
-        const v4i kt = *reinterpret_cast<const v4i*>(&sKt[(32 * c + col) * TS + 32 * T + 16 * h]);
+        const v4i kt = *reinterpret_cast<const v4i*>(&cKt[TT::off(32 * c + col, 2 * T + h)]);
         R = __builtin_amdgcn_mfma_i32_32x32x32_i8(kt, db[T], R, 0, 0, 0);
       }
 #pragma unroll
       for (int r = 0; r < 16; r++) dq[c][r] = fmaf((float)R[r], osc, dq[c][r]);
     }
+    // block j+1 landed (this wave's DMAs, then everyone's); slot b may be refilled
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
   rs = pair_sum(rs);
   if (qrow >= a.N) return;
@@ -537,7 +614,10 @@ __global__ __launch_bounds__(256, 1) void sb_dkv_kernel(BwdArgs a) {
     lim -= 4 * h;
     float P[2][16], dS[2][16];
     // the score multiplier in the dQ kernel's order, so that both kernels see the same P and dS
-    sb_pair<D, FP16>(kf, qf, of, sVb, VS, a.sq[(size_t)bh * a.nqb + i] * skj * a.qk_scale, l2, dr, lim, h, col, P, dS);
+    auto vfrag = [&](int T, int s) {
+      return *reinterpret_cast<const v4i*>(sVb + (32 * T + col) * VS + 16 * s + 8 * h);
+    };
+    sb_pair<D, FP16>(kf, qf, of, vfrag, a.sq[(size_t)bh * a.nqb + i] * skj * a.qk_scale, l2, dr, lim, h, col, P, dS);
     float pm = 0.0f, dm = 0.0f;
 #pragma unroll
     for (int T = 0; T < 2; T++)
