@@ -133,6 +133,11 @@ struct SbTile {
   }
 };
 
+// The low bytes of four words, packed little-endian (v_perm_b32 byte selects).
+__device__ __forceinline__ uint32_t sb_pack4(uint32_t t0, uint32_t t1, uint32_t t2, uint32_t t3) {
+  return __builtin_amdgcn_perm(t1, t0, 0x0c0c0400u) | __builtin_amdgcn_perm(t3, t2, 0x04000c0cu);
+}
+
 struct FwdArgs {
   const int8_t* qh;  // [BH][Np][D]
   const float* sq;   // [BH][nqb]
@@ -221,12 +226,14 @@ __global__ __launch_bounds__(256, 2) void sb_fwd_kernel(FwdArgs a) {
       if (CAUSAL) lim = min(lim, qrow + a.coff - key0);
       lim -= 4 * h;
       float rm = -INFINITY;
+      // boundary blocks only (keys past M, or after a query of the wave): the per-score test
+      const bool masked = key0 + kBK > a.M || (CAUSAL && key0 + kBK - 1 > wq0 + a.coff);
 #pragma unroll
       for (int T = 0; T < 2; T++)
 #pragma unroll
         for (int r = 0; r < 16; r++) {
           const float x = (float)acc[T][r] * mul;
-          sc[T][r] = (32 * T + 8 * (r >> 2) + (r & 3) <= lim) ? x : -INFINITY;
+          sc[T][r] = (!masked || 32 * T + 8 * (r >> 2) + (r & 3) <= lim) ? x : -INFINITY;
           rm = fmaxf(rm, sc[T][r]);
         }
       rm = pair_max(rm);  // the row's max over this tile
@@ -241,19 +248,25 @@ __global__ __launch_bounds__(256, 2) void sb_fwd_kernel(FwdArgs a) {
       for (int T = 0; T < 2; T++)
 #pragma unroll
         for (int q4 = 0; q4 < 4; q4++) {
-          uint32_t wd = 0;
+          uint32_t t[4];
 #pragma unroll
           for (int k = 0; k < 4; k++) {
             const float e = fast_exp2(sc[T][4 * q4 + k] - base);
             esum += e;
-            wd |= (uint32_t)(int)rintf(e) << (8 * k);
+            t[k] = __float_as_uint(e + 12582912.0f);  // e in [0, 127]: round half to even in the low byte
           }
-          pb[T][q4] = (int)wd;
+          pb[T][q4] = (int)sb_pack4(t[0], t[1], t[2], t[3]);
         }
       esum = pair_sum(esum);
       const float sp = (rm == -INFINITY) ? 0.0f : fast_exp2(rm - m_new) * (1.0f / 127.0f);  // s_P
       l_run = fmaf(l_run, alpha, esum * sp);
       const float osc = sp * a.sv[(size_t)bh * a.nkt + j];
+      if (__any(alpha != 1.0f)) {  // some row of the wave raised its max: rescale O first
+#pragma unroll
+        for (int c = 0; c < NKS; c++)
+#pragma unroll
+          for (int r = 0; r < 16; r++) O[c][r] *= alpha;
+      }
 #pragma unroll
       for (int c = 0; c < NKS; c++) {
         v16i R;
@@ -265,7 +278,7 @@ __global__ __launch_bounds__(256, 2) void sb_fwd_kernel(FwdArgs a) {
           R = __builtin_amdgcn_mfma_i32_32x32x32_i8(vf, pb[T], R, 0, 0, 0);
         }
 #pragma unroll
-        for (int r = 0; r < 16; r++) O[c][r] = fmaf((float)R[r], osc, O[c][r] * alpha);
+        for (int r = 0; r < 16; r++) O[c][r] = fmaf((float)R[r], osc, O[c][r]);
       }
     }
     // block j+1 landed (this wave's DMAs, then everyone's); slot b may be refilled
@@ -351,9 +364,11 @@ struct BwdArgs {
 // 16 keys per 32-key half): S^T from K^ / Q^ fragments, P = exp2(S - L2), dP^T = V dO^T on the
 // bf16 MFMA from the 16-bit V tile in LDS, dS = P (dP - D).  Masked pairs give P = dS = 0.
 // vfrag(T, s): the lane's 16 bytes (8 values, channels 16 s + 8 h ..) of V row 32 T + col.
+// masked (wave-uniform): some key of the block is past M or after a query of the wave (causal);
+// otherwise every pair is visible and the per-pair test is skipped.
 template <int D, bool FP16, typename VF>
 __device__ __forceinline__ void sb_pair(const v4i (&kf)[2][D / 32], const v4i (&qf)[D / 32], const v4i (&of)[D / 16],
-                                        VF&& vfrag, float mul, float l2, float dr,
+                                        VF&& vfrag, float mul, float l2, float dr, bool masked,
                                         int lim, int h, int col, float (&P)[2][16], float (&dS)[2][16]) {
 #pragma unroll
   for (int T = 0; T < 2; T++) {
@@ -369,12 +384,21 @@ __device__ __forceinline__ void sb_pair(const v4i (&kf)[2][D / 32], const v4i (&
     for (int s = 0; s < D / 16; s++) {
       dp = mfma16<FP16>(vfrag(T, s), of[s], dp);
     }
+    if (masked) {
 #pragma unroll
-    for (int r = 0; r < 16; r++) {
-      const bool vis = 32 * T + 8 * (r >> 2) + (r & 3) <= lim;
-      const float p = vis ? fast_exp2((float)acc[r] * mul - l2) : 0.0f;
-      P[T][r] = p;
-      dS[T][r] = vis ? p * (dp[r] - dr) : 0.0f;  // a masked key's V row may be a stand-in
+      for (int r = 0; r < 16; r++) {
+        const bool vis = 32 * T + 8 * (r >> 2) + (r & 3) <= lim;
+        const float p = vis ? fast_exp2((float)acc[r] * mul - l2) : 0.0f;
+        P[T][r] = p;
+        dS[T][r] = vis ? p * (dp[r] - dr) : 0.0f;  // a masked key's V row may be a stand-in
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const float p = fast_exp2((float)acc[r] * mul - l2);
+        P[T][r] = p;
+        dS[T][r] = p * (dp[r] - dr);
+      }
     }
   }
 }
@@ -393,11 +417,12 @@ __device__ __forceinline__ void sb_block_max(float pm, float dm, float* xs, int 
   dmax = fmaxf(fmaxf(xs[4], xs[5]), fmaxf(xs[6], xs[7]));
 }
 
-// INT8 code of x against 127 / amax (inv = 0: the block is all zero).
+// INT8 code of x against 127 / amax (inv = 0: the block is all zero), in the low byte of the
+// result: the clamped product plus 1.5 * 2^23 holds its round-half-even integer in the low
+// mantissa bits (no convert; a NaN product clamps to -127, as clamping after rounding does).
 __device__ __forceinline__ uint32_t sb_code8(float x, float inv) {
-  float y = rintf(x * inv);
-  y = fminf(fmaxf(y, -127.0f), 127.0f);
-  return (uint32_t)(uint8_t)(int8_t)(int)y;
+  const float y = fminf(fmaxf(x * inv, -127.0f), 127.0f);
+  return __float_as_uint(y + 12582912.0f);
 }
 
 // The 16-bit rows of one 64-key V tile into LDS (rows >= M are 0).
@@ -513,7 +538,9 @@ __global__ __launch_bounds__(256, 2) void sb_dq_kernel(BwdArgs a) {
     auto vfrag = [&](int T, int s) {
       return *reinterpret_cast<const v4i*>(&cV[TV::off(32 * T + col, 2 * s + h)]);
     };
-    sb_pair<D, FP16>(kf, qf, of, vfrag, sq * a.sk[(size_t)bh * a.nkt + j] * a.qk_scale, l2, dr, lim, h, col, P, dS);
+    const bool masked = key0 + kBK > a.M || (CAUSAL && key0 + kBK - 1 > q0 + 32 * w + a.coff);
+    sb_pair<D, FP16>(kf, qf, of, vfrag, sq * a.sk[(size_t)bh * a.nkt + j] * a.qk_scale, l2, dr, masked, lim, h, col, P,
+                     dS);
     float pm = 0.0f, dm = 0.0f;
 #pragma unroll
     for (int T = 0; T < 2; T++)
@@ -532,10 +559,8 @@ __global__ __launch_bounds__(256, 2) void sb_dq_kernel(BwdArgs a) {
     for (int T = 0; T < 2; T++)
 #pragma unroll
       for (int q4 = 0; q4 < 4; q4++) {
-        uint32_t wd = 0;
-#pragma unroll
-        for (int k = 0; k < 4; k++) wd |= sb_code8(dS[T][4 * q4 + k], inv) << (8 * k);
-        db[T][q4] = (int)wd;
+        db[T][q4] = (int)sb_pack4(sb_code8(dS[T][4 * q4 + 0], inv), sb_code8(dS[T][4 * q4 + 1], inv),
+                                  sb_code8(dS[T][4 * q4 + 2], inv), sb_code8(dS[T][4 * q4 + 3], inv));
       }
     const float osc = sds * a.sk[(size_t)bh * a.nkt + j] * a.sm;
 #pragma unroll
@@ -574,7 +599,7 @@ __global__ __launch_bounds__(256, 2) void sb_dq_kernel(BwdArgs a) {
 // dS^ of a pair go to LDS key-major; wave w then owns key half w % 2 and half of the channel
 // groups of both outputs, and contracts over the block's 128 queries ----
 template <int D, bool CAUSAL, bool FP16>
-__global__ __launch_bounds__(256, 1) void sb_dkv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void sb_dkv_kernel(BwdArgs a) {
   constexpr int NKS = D / 32, NG = NKS / 2, VS = D + 8, PS = kBQ + 16;
   __shared__ __attribute__((aligned(16))) uint16_t sVb[kBK * VS];
   __shared__ __attribute__((aligned(16))) int8_t sP[kBK * PS];
@@ -617,7 +642,9 @@ __global__ __launch_bounds__(256, 1) void sb_dkv_kernel(BwdArgs a) {
     auto vfrag = [&](int T, int s) {
       return *reinterpret_cast<const v4i*>(sVb + (32 * T + col) * VS + 16 * s + 8 * h);
     };
-    sb_pair<D, FP16>(kf, qf, of, vfrag, a.sq[(size_t)bh * a.nqb + i] * skj * a.qk_scale, l2, dr, lim, h, col, P, dS);
+    const bool masked = key0 + kBK > a.M || (CAUSAL && key0 + kBK - 1 > q0 + 32 * w + a.coff);
+    sb_pair<D, FP16>(kf, qf, of, vfrag, a.sq[(size_t)bh * a.nqb + i] * skj * a.qk_scale, l2, dr, masked, lim, h, col, P,
+                     dS);
     float pm = 0.0f, dm = 0.0f;
 #pragma unroll
     for (int T = 0; T < 2; T++)
