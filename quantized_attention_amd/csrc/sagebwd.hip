@@ -601,11 +601,15 @@ __global__ __launch_bounds__(256, 2) void sb_dq_kernel(BwdArgs a) {
 template <int D, bool CAUSAL, bool FP16>
 __global__ __launch_bounds__(256, 2) void sb_dkv_kernel(BwdArgs a) {
   constexpr int NKS = D / 32, NG = NKS / 2, VS = D + 8, PS = kBQ + 16;
+  using TQ = SbTile<D, kBQ>;  // dO^ and Q^ transposed: [channel][query] of one query block
   __shared__ __attribute__((aligned(16))) uint16_t sVb[kBK * VS];
   __shared__ __attribute__((aligned(16))) int8_t sP[kBK * PS];
   __shared__ __attribute__((aligned(16))) int8_t sD[kBK * PS];
+  __shared__ __attribute__((aligned(1024))) int8_t sOt[TQ::BYTES];
+  __shared__ __attribute__((aligned(1024))) int8_t sQt[TQ::BYTES];
   __shared__ float xs[8];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, col = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int bh = blockIdx.x / a.nkt, j = blockIdx.x % a.nkt;
   const int key0 = j * kBK;
   sb_load_v<D>(a.V + (size_t)bh * a.M * D, a.M, key0, sVb, VS, tid);
@@ -626,6 +630,13 @@ __global__ __launch_bounds__(256, 2) void sb_dkv_kernel(BwdArgs a) {
   for (int g = 0; g < NG; g++)
 #pragma unroll
     for (int r = 0; r < 16; r++) accV[g][r] = accK[g][r] = 0.0f;
+  int to[TQ::NPW];  // per-lane DMA source offsets inside a transposed block
+#pragma unroll
+  for (int x = 0; x < TQ::NPW; x++) {
+    int r, c;
+    TQ::src(w, x, lane, r, c);
+    to[x] = r * kBQ + 16 * c;
+  }
   const int ilo = CAUSAL ? max(0, (key0 - a.coff) / kBQ) : 0;
   for (int i = ilo; i < a.nqb; i++) {
     __syncthreads();  // the previous pair's LDS reads are done (and V is staged, i = ilo)
@@ -634,6 +645,16 @@ __global__ __launch_bounds__(256, 2) void sb_dkv_kernel(BwdArgs a) {
     v4i of[D / 16];
     sb_q_frags<D>(a, bh, qrow, h, qf, of);
     const float l2 = a.L2[(size_t)bh * a.Np + qrow], dr = a.Dr[(size_t)bh * a.Np + qrow];
+    {
+      // the block's dO^ and Q^ transposed for the dV / dK products, by DMA: they land while the
+      // scores and gradients of the block are computed (issued after this wave's row loads)
+      const int8_t* dob = a.dot + ((size_t)bh * a.nqb + i) * (size_t)D * kBQ;
+      const int8_t* qtb = a.qt + ((size_t)bh * a.nqb + i) * (size_t)D * kBQ;
+#pragma unroll
+      for (int x = 0; x < TQ::NPW; x++) dma16(lds_addr(&sOt[(TQ::NPW * w + x) * 1024]), dob, to[x]);
+#pragma unroll
+      for (int x = 0; x < TQ::NPW; x++) dma16(lds_addr(&sQt[(TQ::NPW * w + x) * 1024]), qtb, to[x]);
+    }
     int lim = a.M - 1 - key0;
     if (CAUSAL) lim = min(lim, qrow + a.coff - key0);
     lim -= 4 * h;
@@ -667,11 +688,10 @@ __global__ __launch_bounds__(256, 2) void sb_dkv_kernel(BwdArgs a) {
         sP[key * PS + qc] = (int8_t)sb_code8(P[T][r], pinv);
         sD[key * PS + qc] = (int8_t)sb_code8(dS[T][r], dinv);
       }
-    __syncthreads();
+    // P^ / dS^ visible, and this block's dO^ / Q^ transposed landed (every wave's DMAs)
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const float vsc = __fdiv_rn(pmax, 127.0f) * a.sdo[(size_t)bh * a.nqb + i];
     const float ksc = __fdiv_rn(dmax, 127.0f) * a.sq[(size_t)bh * a.nqb + i] * a.sm;
-    const int8_t* dob = a.dot + ((size_t)bh * a.nqb + i) * (size_t)D * kBQ;
-    const int8_t* qtb = a.qt + ((size_t)bh * a.nqb + i) * (size_t)D * kBQ;
 #pragma unroll
     for (int g = 0; g < NG; g++) {
       const int c = c0 + g;
@@ -682,7 +702,7 @@ __global__ __launch_bounds__(256, 2) void sb_dkv_kernel(BwdArgs a) {
 #pragma unroll
         for (int qs = 0; qs < kBQ / 32; qs++) {
           const v4i pa = *reinterpret_cast<const v4i*>(&sP[(32 * Tw + col) * PS + 32 * qs + 16 * h]);
-          const v4i ob = *reinterpret_cast<const v4i*>(dob + (size_t)(32 * c + col) * kBQ + 32 * qs + 16 * h);
+          const v4i ob = *reinterpret_cast<const v4i*>(&sOt[TQ::off(32 * c + col, 2 * qs + h)]);
           R = __builtin_amdgcn_mfma_i32_32x32x32_i8(pa, ob, R, 0, 0, 0);
         }
 #pragma unroll
@@ -695,7 +715,7 @@ __global__ __launch_bounds__(256, 2) void sb_dkv_kernel(BwdArgs a) {
 #pragma unroll
         for (int qs = 0; qs < kBQ / 32; qs++) {
           const v4i da = *reinterpret_cast<const v4i*>(&sD[(32 * Tw + col) * PS + 32 * qs + 16 * h]);
-          const v4i qb = *reinterpret_cast<const v4i*>(qtb + (size_t)(32 * c + col) * kBQ + 32 * qs + 16 * h);
+          const v4i qb = *reinterpret_cast<const v4i*>(&sQt[TQ::off(32 * c + col, 2 * qs + h)]);
           R = __builtin_amdgcn_mfma_i32_32x32x32_i8(da, qb, R, 0, 0, 0);
         }
 #pragma unroll
