@@ -33,6 +33,7 @@ PV_IDENTITY = 0x0100
 PV_E5M2 = 0x0200
 PV_INT8 = 0x0400
 MXFP4 = 0x1000
+MX_P_TWO_LEVEL = 0x4000  # MX knob: P~ row-scaled by rowmax / 6 before the E2M1 quantizer
 QK_E4M3 = 0x2000  # Q^, K^ in E4M3 (scale amax / 448, same groups); khat, qhat then hold E4M3 codes
 
 

@@ -610,6 +610,23 @@ static void forward_row(const head_t* h, int r, int causal, int off, double sm_s
     if (h->flags & ORC_MXFP4) {
       /* P~ in E2M1 with one E8M0 scale per 32 keys of the row (2 blocks per 64-key tile);
        * R = sum_blk X_P X_V (P^ . V^)_blk. */
+      /* Two-level knob ([SA3] "Two-Level Quantization for the Attention Map P"): level one
+       * divides the row's P~ of this tile by an FP32 factor s1 taken from the row maximum
+       * (which is exp(rowmax S - m), the softmax's own maximum), level two is the block
+       * quantizer above, and the tile's product is multiplied back by s1.  Reading: the pages
+       * send the row maximum to 448 * 6 because their block scales are E4M3; with E8M0 block
+       * scales any power of two in s1 is absorbed by the block scale, so only the mantissa of
+       * the target matters, and 448 * 6 = 1.3125 * 2^11 would put the maximum at 5.25 times
+       * its block scale, off the E2M1 grid.  The target kept is 6, the largest E2M1 value,
+       * which is what the pages' choice achieves for their format: s1 = rowmax / 6. */
+      /* P2 = P~ / s1 is formed as 6 (P~ / rowmax), so that the row maximum is 6 exactly. */
+      const int two = (h->flags & ORC_MX_P_TWO_LEVEL) != 0;
+      double pm = 0.0;
+      if (two)
+        for (int x = 0; x < n; x++) if (Pt[x] > pm) pm = Pt[x];
+      /* pm > 0: a visited tile holds at least one visible key of the row */
+      const double s1 = two ? pm / 6.0 : 1.0;
+      for (int x = 0; x < n; x++) Pt[x] = two ? 6.0 * (Pt[x] / pm) : Pt[x]; /* l already summed */
       for (int c = 0; c < d; c++) R[c] = 0.0;
       for (int b0 = 0; b0 < n; b0 += 32) {
         int b1 = b0 + 32 < n ? b0 + 32 : n;
@@ -624,6 +641,7 @@ static void forward_row(const head_t* h, int r, int causal, int off, double sm_s
           R[c] += ldexp(p, ep + h->ve[(size_t)vb * d + c]);
         }
       }
+      for (int c = 0; c < d; c++) R[c] *= s1;
     } else {
       for (int x = 0; x < n; x++) Ph[x] = quant_p(h, Pt[x]);
       /* R = P^ V^ over this tile only (the per-tile inner accumulator). */
@@ -655,6 +673,7 @@ int orc_forward_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, in
   if (causal_offset(causal, N, M, &off)) return -1;
   if ((flags & ORC_MXFP4) && (flags & (ORC_QK_IDENTITY | ORC_PV_IDENTITY | ORC_PV_E5M2 | ORC_PV_INT8))) return -1;
   if ((flags & ORC_QK_E4M3) && (flags & (ORC_QK_IDENTITY | ORC_MXFP4))) return -1;
+  if ((flags & ORC_MX_P_TWO_LEVEL) && !(flags & ORC_MXFP4)) return -1;
   if (!rows && nrows != N) return -1;
   head_t h;
   if (head_setup(&h, q, k, v, in_fp16, N, M, d, flags)) { head_free(&h); return -1; }

@@ -52,6 +52,8 @@ extern "C" {
 #define ORC_PV_INT8       0x0400u /* ablation: naive INT8 P~ (static 1/127) and per-channel INT8 V       */
 #define ORC_MXFP4         0x1000u /* MX variant: E2M1 values, E8M0 scale per 32 along the reduction dim  */
 #define ORC_QK_E4M3       0x2000u /* knob: Q^, K^ in E4M3 (scale amax/448, same groups) instead of INT8  */
+#define ORC_MX_P_TWO_LEVEL 0x4000u /* MX knob: P~ of each tile row divided by rowmax/6 before the E2M1  */
+                                   /* quantizer, the tile's P^V product multiplied back by it [SA3]      */
 
 /* ---- scalar formats ---- */
 float   orc_bf16_to_f32(uint16_t h);

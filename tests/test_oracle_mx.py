@@ -158,3 +158,74 @@ def test_mx_p_block_exponent_follows_block_max_not_row_max():
     l0 = 31 * 2.0 ** -2 + 2.0 ** -4 + 32
     assert abs(ex[0, 0] - 4 * 2.0 ** -4 / l0) < 1e-15
     assert np.abs(got - ex).max() < 1e-12
+
+
+# ---- two-level quantization of P~ (knob MX_P_TWO_LEVEL) ----
+# "SageAttention3" summary, 3.4 "Two-Level Quantization for the Attention Map P": each row of
+# a tile's P~ is first divided by an FP32 factor s1 from the row maximum (the maximum of P~ is
+# exp(rowmax S - m), the softmax's own maximum), then block-quantized; the tile's product is
+# multiplied back by s1.  With E8M0 block scales the reading is s1 = rowmax / 6, so that the
+# row maximum is exactly the largest E2M1 value.
+
+def two_level_case(seed, N, M, d):
+    """All query rows equal (so Q^ = 0 and S = Delta S * sm_scale exactly), K channel 0 in {0, 1}
+    (so gamma K takes two values one apart), every other channel zero, and V on the E2M1 grid of
+    every 32-token block (M a power of two keeps mean(K) exact).  With sm_scale = ln(3/2) a row's visible scores sit on two levels whose
+    P~ ratio is exactly 2/3; the first two tiles hold low keys only, so the running maximum
+    rises later.  Level one maps a tile's larger level to 6 and the smaller to 4, both on the
+    grid, so every quantizer is exact; quantizing P~ directly puts 2/3 of the block maximum
+    (16/3 or 8/3 times the block scale) off the grid."""
+    rng = np.random.default_rng(seed)
+    Q = np.zeros((N, d)); Q[:, 0] = 1.0
+    K = np.zeros((M, d))
+    hi = rng.random(M) < 0.4
+    hi[:128] = False
+    hi[min(M - 1, 130)] = True
+    K[hi, 0] = 1.0
+    V = rng.choice([0.0, 0.5, 1.0, 1.5, 2.0, 3.0], (M, d)) * rng.choice([-1.0, 1.0], (M, d))
+    return Q, K, V
+
+
+def textbook(Q, K, V, sm, causal):
+    """softmax(Q K^T sm) V in FP64 with numpy (top-left causal mask)."""
+    s = (Q @ K.T) * sm
+    if causal:
+        s = np.where(np.arange(K.shape[0])[None, :] <= np.arange(Q.shape[0])[:, None], s, -np.inf)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    return (p / p.sum(axis=1, keepdims=True)) @ V
+
+
+@pytest.mark.parametrize("N,M,d,causal", [(256, 256, 64, False), (256, 256, 64, True), (192, 512, 128, False)])
+def test_mx_two_level_p_lossless_on_two_levels(N, M, d, causal):
+    Q, K, V = two_level_case(50 + N + d, N, M, d)
+    q, k, v = f16(Q), f16(K), f16(V)
+    sm = math.log(1.5)
+    ex = textbook(Q, K, V, sm, causal)
+    two = oracle.forward_head(q, k, v, True, causal, sm, oracle.MXFP4 | oracle.MX_P_TWO_LEVEL)
+    direct = oracle.forward_head(q, k, v, True, causal, sm, oracle.MXFP4)
+    assert np.abs(two - ex).max() < 1e-12
+    assert np.abs(direct - ex).max() > 1e-3  # the construction tells the two apart
+
+
+def test_mx_two_level_p_is_mx_only():
+    q = k = v = np.zeros((64, 64), np.uint16)
+    with pytest.raises(ValueError):
+        oracle.forward_head(q, k, v, True, 0, 0.125, oracle.MX_P_TWO_LEVEL)
+
+
+@pytest.mark.parametrize("name", ["mxfp4_32k", "prefill32k", "video17k"])
+def test_mx_two_level_p_lowers_error(name):
+    """Direction of the pages' Table 1(b): against exact attention, two-level P has a lower
+    mean error than direct P quantization (here with E8M0 block scales, on the synthetic
+    stand-ins for the pages' workloads, 2 heads of 2048 tokens, every 7th row)."""
+    from quantized_attention_amd import synthetic as sy
+    cfg = sy.CONFIGS[name].with_shape(B=1, H=2, N=2048, M=2048)
+    qb, kb, vb = sy.make_qkv(cfg)
+    sm = 1 / math.sqrt(cfg.d)
+    rows = np.arange(0, 2048, 7)
+    for h in range(2):
+        args = (qb[0, h], kb[0, h], vb[0, h], cfg.fp16, 1 if cfg.causal else 0, sm)
+        ex = oracle.exact_head(*args, rows=rows)
+        e_two = np.abs(oracle.forward_head(*args, oracle.MXFP4 | oracle.MX_P_TWO_LEVEL, rows=rows) - ex).mean()
+        e_dir = np.abs(oracle.forward_head(*args, oracle.MXFP4, rows=rows) - ex).mean()
+        assert e_two < e_dir
