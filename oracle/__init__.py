@@ -69,6 +69,8 @@ def lib():
         L.orc_preprocess_mx_head.restype = i
         L.orc_forward_head.argtypes = [P, P, P, i, i, i, i, i, dbl, u, P, i, P]
         L.orc_forward_head.restype = i
+        L.orc_forward_head_ties.argtypes = [P, P, P, i, i, i, i, i, dbl, u, P, i, P, dbl, P]
+        L.orc_forward_head_ties.restype = i
         L.orc_exact_head.argtypes = [P, P, P, i, i, i, i, i, dbl, P, i, P]
         L.orc_exact_head.restype = i
         L.orc_exact_f64.argtypes = [P, P, P, i, i, i, i, dbl, P]
@@ -168,6 +170,28 @@ def forward_head(q, k, v, fp16: bool, causal: int, sm_scale: float, flags: int =
     if rc != 0:
         raise ValueError("orc_forward_head rejected its arguments")
     return out
+
+
+def forward_head_ties(q, k, v, fp16: bool, causal: int, sm_scale: float, flags: int = 0, rows=None,
+                      tie_eps: float = 2.0 ** -16):
+    """forward_head, and per row the count of its P rounding decisions whose input lies within
+    relative distance tie_eps of a rounding boundary (where an FP32 kernel may round the other
+    way): (out, ties)."""
+    q, k, v = _u16(q), _u16(k), _u16(v)
+    N, d = q.shape
+    M = k.shape[0]
+    if rows is None:
+        nrows, rp = N, None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int32)
+        nrows, rp = len(rows), rows
+    out = np.zeros((nrows, d), np.float64)
+    ties = np.zeros(nrows, np.int32)
+    rc = lib().orc_forward_head_ties(_ptr(q), _ptr(k), _ptr(v), int(fp16), N, M, d, int(causal),
+                                     float(sm_scale), flags, _ptr(rp), nrows, _ptr(out), float(tie_eps), _ptr(ties))
+    if rc != 0:
+        raise ValueError("orc_forward_head_ties rejected its arguments")
+    return out, ties
 
 
 def exact_head(q, k, v, fp16: bool, causal: int, sm_scale: float, rows=None):

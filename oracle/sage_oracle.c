@@ -577,9 +577,36 @@ static int causal_offset(int causal, int N, int M, int* off) {
   return -1;
 }
 
-/* Steps 7-8 for one row: the tile loop and the epilogue. */
+/* ---- rounding-decision margins (a diagnostic, not part of the method) ----
+ * A quantizer's output code is decided by comparing its input with the midpoints between
+ * adjacent representable values (and, for an E8M0 block scale, the block maximum with
+ * 6 * 2^e).  The oracle decides in FP64 from exact exponentials; a kernel decides in FP32
+ * from its own exp2, so an input within a few FP32 ulps of such a boundary may land on the
+ * other side there, and both codes are correct roundings of the method's value.  These
+ * helpers say whether x lies within relative distance eps of a boundary. */
+static int near_rel(double x, double b, double eps) { return fabs(x - b) <= eps * fabs(b); }
+
+static int e4m3_near_tie(double y, double eps) {
+  if (!(y > 0.0) || y >= 448.0) return 0;
+  uint8_t c = orc_e4m3_encode(y);
+  double v = orc_e4m3_decode(c);
+  double w = v <= y ? orc_e4m3_decode((uint8_t)(c + 1)) : orc_e4m3_decode((uint8_t)(c - 1));
+  return near_rel(y, 0.5 * (v + w), eps);
+}
+
+static int e2m1_near_tie(double y, double eps) {
+  static const double mid[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+  for (int i = 0; i < 7; i++)
+    if (near_rel(fabs(y), mid[i], eps)) return 1;
+  return 0;
+}
+
+/* Steps 7-8 for one row: the tile loop and the epilogue.  With ties != NULL, *ties counts the
+ * P quantization decisions of the row whose inputs lie within relative tie_eps of a rounding
+ * boundary. */
 static void forward_row(const head_t* h, int r, int causal, int off, double sm_scale, const double* ds,
-                        double* S, double* Pt, double* Ph, double* R, double* out) {
+                        double* S, double* Pt, double* Ph, double* R, double* out, double tie_eps, int* ties) {
+  if (ties) *ties = 0;
   int d = h->d, M = h->M;
   double m = -INFINITY, l = 0.0;
   for (int c = 0; c < d; c++) out[c] = 0.0;
@@ -634,6 +661,12 @@ static void forward_row(const head_t* h, int r, int causal, int off, double sm_s
         for (int x = b0; x < b1; x++) if (Pt[x] > am) am = Pt[x];
         int ep = orc_e8m0_exponent(am);
         for (int x = b0; x < b1; x++) Ph[x] = orc_e2m1_decode(orc_e2m1_encode(ldexp(Pt[x], -ep)));
+        /* the two-level row maximum is exactly 6 by construction, not a rounded input */
+        if (ties && am > 0.0 && !(two && am == 6.0)) {
+          *ties += near_rel(am, 6.0 * ldexp(1.0, ep), tie_eps) + near_rel(am, 6.0 * ldexp(1.0, ep - 1), tie_eps);
+        }
+        if (ties)
+          for (int x = b0; x < b1; x++) *ties += e2m1_near_tie(ldexp(Pt[x], -ep), tie_eps);
         int vb = (t0 + b0) / 32;
         for (int c = 0; c < d; c++) {
           double p = 0.0;
@@ -644,6 +677,8 @@ static void forward_row(const head_t* h, int r, int causal, int off, double sm_s
       for (int c = 0; c < d; c++) R[c] *= s1;
     } else {
       for (int x = 0; x < n; x++) Ph[x] = quant_p(h, Pt[x]);
+      if (ties && !(h->flags & (ORC_PV_IDENTITY | ORC_PV_E5M2 | ORC_PV_INT8)))
+        for (int x = 0; x < n; x++) *ties += e4m3_near_tie(h->pscale * Pt[x], tie_eps);
       /* R = P^ V^ over this tile only (the per-tile inner accumulator). */
       for (int c = 0; c < d; c++) {
         double acc = 0.0;
@@ -668,6 +703,12 @@ static void forward_row(const head_t* h, int r, int causal, int off, double sm_s
 int orc_forward_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, int in_fp16,
                      int N, int M, int d, int causal, double sm_scale, unsigned flags,
                      const int* rows, int nrows, double* out) {
+  return orc_forward_head_ties(q, k, v, in_fp16, N, M, d, causal, sm_scale, flags, rows, nrows, out, 0.0, NULL);
+}
+
+int orc_forward_head_ties(const uint16_t* q, const uint16_t* k, const uint16_t* v, int in_fp16,
+                          int N, int M, int d, int causal, double sm_scale, unsigned flags,
+                          const int* rows, int nrows, double* out, double tie_eps, int* ties) {
   int off;
   if (!q || !k || !v || !out || nrows < 0) return -1;
   if (causal_offset(causal, N, M, &off)) return -1;
@@ -704,7 +745,8 @@ int orc_forward_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, in
 #pragma omp for schedule(dynamic, 4)
       for (int x = 0; x < nrows; x++) {
         int r = rows ? rows[x] : x;
-        forward_row(&h, r, causal, off, sm_scale, dsr[r / ORC_BQ], S, Pt, Ph, R, out + (size_t)x * d);
+        forward_row(&h, r, causal, off, sm_scale, dsr[r / ORC_BQ], S, Pt, Ph, R, out + (size_t)x * d, tie_eps,
+                    ties ? ties + x : NULL);
       }
       free(S); free(Pt); free(Ph); free(R);
     }

@@ -229,3 +229,21 @@ def test_mx_two_level_p_lowers_error(name):
         e_two = np.abs(oracle.forward_head(*args, oracle.MXFP4 | oracle.MX_P_TWO_LEVEL, rows=rows) - ex).mean()
         e_dir = np.abs(oracle.forward_head(*args, oracle.MXFP4, rows=rows) - ex).mean()
         assert e_two < e_dir
+
+
+def test_tie_diagnostic_counts_exact_midpoints():
+    """The rounding-boundary diagnostic: with the two-level construction's scores (two levels one
+    unit apart, all rows equal) and sm_scale = ln(448 / 17), every low key has 448 P~ = 17, the
+    midpoint between the E4M3 values 16 and 18, and every high key 448; so a row's count is the
+    number of low keys it sees (non-causal: all of them, once per row)."""
+    N = M = 256
+    Q, K, V = two_level_case(7, N, M, 64)
+    q, k, v = f16(Q), f16(K), f16(V)
+    out, ties = oracle.forward_head_ties(q, k, v, True, False, math.log(448 / 17), 0)
+    n_low = int((K[:, 0] == 0).sum())
+    # low keys before the first high one were quantized relative to their own (lower) maximum:
+    # there 448 P~ = 448 exactly, not a tie
+    first_hi = int(np.flatnonzero(K[:, 0] == 1)[0])
+    lead = (first_hi // 64) * 64
+    assert (ties == n_low - lead).all()
+    assert np.array_equal(out, oracle.forward_head(q, k, v, True, False, math.log(448 / 17), 0))
