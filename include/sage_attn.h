@@ -69,6 +69,16 @@ typedef enum {
                                    Technical Report" summary, "Critical Assessment": the FP8-QK
                                    form of SageAttention2-8b the pages do not evaluate).  Not
                                    combinable with SAGE_PATH_MXFP4 (SAGE_ERR_INVALID_ARG). */
+#define SAGE_MX_P_TWO_LEVEL 0x0004u /* MXFP4 only: two-level quantization of P~ ("SageAttention3"
+                                   summary, 3.4 "Two-Level Quantization for the Attention Map
+                                   P").  Each row of a tile's P~ is divided by the FP32 factor
+                                   s1 = rowmax(P~) / 6 before the E2M1 block quantizer, so that
+                                   the row's largest value is exactly 6 (the pages' 448 * 6
+                                   targets E4M3 block scales; with E8M0 scales only the
+                                   factor's mantissa matters), and the tile's product is
+                                   multiplied back by s1.  Costs one rescale of O per tile.
+                                   SAGE_ERR_INVALID_ARG without SAGE_PATH_MXFP4 or together
+                                   with SAGE_ACC_VALU. */
 #define SAGE_SMOOTH_V   0x0010u /* V' = V - mean_t(V) before quantization, O += V_m           */
 #define SAGE_IN_BF16    0x0000u
 #define SAGE_IN_FP16    0x0100u

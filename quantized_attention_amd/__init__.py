@@ -16,7 +16,7 @@ import os
 
 __all__ = [
     "SAGE_OK", "SAGE_ERR_INVALID_ARG", "SAGE_ERR_UNSUPPORTED", "SAGE_ERR_NO_MEMORY",
-    "SAGE_ERR_LAUNCH", "SAGE_ERR_DEVICE", "SAGE_PATH_I8F8", "SAGE_PATH_MXFP4", "SAGE_QK_FP8", "SAGE_SMOOTH_V", "SAGE_IN_BF16",
+    "SAGE_ERR_LAUNCH", "SAGE_ERR_DEVICE", "SAGE_PATH_I8F8", "SAGE_PATH_MXFP4", "SAGE_QK_FP8", "SAGE_MX_P_TWO_LEVEL", "SAGE_SMOOTH_V", "SAGE_IN_BF16",
     "SAGE_IN_FP16", "SAGE_OUT_SAME", "SAGE_OUT_FP32", "SAGE_ACC_VALU", "SAGE_BQ", "SAGE_BK", "SageError",
     "library_path", "load_library", "sage_attn_fwd", "sage_attn_fwd_ws",
     "sage_attn_workspace_bytes", "sage_attn_quantize", "sage_attn_status_string",
@@ -37,6 +37,7 @@ SAGE_ERR_DEVICE = -5
 SAGE_PATH_I8F8 = 0x0000
 SAGE_PATH_MXFP4 = 0x0001
 SAGE_QK_FP8 = 0x0002
+SAGE_MX_P_TWO_LEVEL = 0x0004
 SAGE_SMOOTH_V = 0x0010
 SAGE_IN_BF16 = 0x0000
 SAGE_IN_FP16 = 0x0100
@@ -208,7 +209,7 @@ def sage_attn_version() -> int:
 
 # ---------------------------------------------------------------- torch convenience
 def _variant_for(q, smooth_v: bool, out_fp32: bool, acc_valu: bool = False, mxfp4: bool = False,
-                 qk_fp8: bool = False) -> int:
+                 qk_fp8: bool = False, mx_p_two_level: bool = False) -> int:
     import torch
     if q.dtype == torch.bfloat16:
         var = SAGE_IN_BF16
@@ -226,12 +227,14 @@ def _variant_for(q, smooth_v: bool, out_fp32: bool, acc_valu: bool = False, mxfp
         var |= SAGE_PATH_MXFP4
     if qk_fp8:
         var |= SAGE_QK_FP8
+    if mx_p_two_level:
+        var |= SAGE_MX_P_TWO_LEVEL
     return var
 
 
 def sage_attn(q, k, v, causal: bool = False, sm_scale: float | None = None, smooth_v: bool = False,
               out_fp32: bool = False, out=None, acc_valu: bool = False, mxfp4: bool = False,
-              qk_fp8: bool = False):
+              qk_fp8: bool = False, mx_p_two_level: bool = False):
     """softmax(Q K^T * sm_scale) V with the quantized method, for [B, H, N, d] tensors.
 
     q: [B, H, N, d], k/v: [B, Hkv, M, d] (Hkv divides H: query head h reads key/value head
@@ -239,7 +242,8 @@ def sage_attn(q, k, v, causal: bool = False, sm_scale: float | None = None, smoo
     t <= r + M - N (queries are the last N of M tokens).  Returns out [B, H, N, d] in the
     input dtype (FP32 with out_fp32).
     mxfp4 selects the MXFP4 variant (E2M1 operands with E8M0 block scales); qk_fp8 quantizes
-    Q and K to E4M3 instead of INT8 (same groups, scale amax / 448).
+    Q and K to E4M3 instead of INT8 (same groups, scale amax / 448); mx_p_two_level (with
+    mxfp4) divides each row of a tile's P~ by rowmax / 6 before its E2M1 quantization.
     """
     import torch
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
@@ -255,7 +259,7 @@ def sage_attn(q, k, v, causal: bool = False, sm_scale: float | None = None, smoo
     for t in (q, k, v):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("q, k, v must be contiguous device tensors")
-    var = _variant_for(q, smooth_v, out_fp32, acc_valu, mxfp4, qk_fp8)
+    var = _variant_for(q, smooth_v, out_fp32, acc_valu, mxfp4, qk_fp8, mx_p_two_level)
     if out is None:
         out = torch.empty((B, H, N, d), dtype=torch.float32 if out_fp32 else q.dtype, device=q.device)
     scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(d)

@@ -26,6 +26,17 @@
 // scale, and V^ was stored with its keys in that order (vperm_mx).  O^T = V^T P^T then
 // accumulates through the MFMA's FP32 C operand (lazy rescale when a row's maximum rises),
 // or, as a variant, from a zero accumulator with one VALU FMA into O.
+//
+// Two-level P (knob; "SageAttention3" summary, 3.4 "Two-Level Quantization for the Attention
+// Map P"): level one divides each row of the tile's P~ by s1 = rowmax(P~) / 6, so the row's
+// largest value is exactly 6; level two is the block quantizer above; the tile's product is
+// multiplied back by s1.  The row maximum of P~ comes from the softmax's maximum of S (the
+// pages' reuse): P2 = P~ / s1 = exp2(S - (rowmax S - log2 6)), one exp2 per element as before,
+// with the block scales from 6 exp2(block max S - rowmax S).  The factor s1 is not applied to
+// the product: O is kept divided by the current s1 (O_true = s1 O), so a tile multiplies O by
+// s1_old alpha / s1_new = exp2(b_old - b_new) (b = rowmax S - log2 6, the level-one base)
+// before its product accumulates through the C operand, and the epilogue multiplies by
+// s1 = exp2(b - m).
 #include "attn_device.hpp"
 
 namespace sage {
@@ -98,11 +109,14 @@ __device__ __forceinline__ void qk_tile_mx(const uint8_t* __restrict__ sK, const
   });
 }
 
-template <int D, bool CAUSAL, bool ACC_VALU>
+constexpr float kLog2_6 = 2.5849625007211562f;  // log2(6)
+
+template <int D, bool CAUSAL, bool ACC_VALU, bool P2L>
 __device__ __forceinline__ void softmax_pv_mx(const v16f (&acc)[2], const uint8_t* __restrict__ sV,
                                               const float* __restrict__ sDS, uint32_t vs, float qk_scale, int h,
                                               int col, int key0, int qrow, int M, bool masked, v16f (&O)[D / 32],
-                                              float& m_run, float& l_run) {
+                                              float& m_run, float& l_run, float& b_run) {
+  static_assert(!(P2L && ACC_VALU), "two-level P accumulates through the C operand");
   // ---- scores: sm_scale log2(e) and Delta S (the block scales were applied by the MFMA) ----
   float sc[2][16];
 #pragma unroll
@@ -130,13 +144,29 @@ __device__ __forceinline__ void softmax_pv_mx(const v16f (&acc)[2], const uint8_
     for (int r = 0; r < 16; r++) m = fmaxf(m, sc[T][r]);
     mb[T] = pair_max(m);
   }
-  const float m_new = fmaxf(m_run, fmaxf(mb[0], mb[1]));  // finite: m_run starts at -FLT_MAX
-  const float base = m_new;
+  const float m_tile = fmaxf(mb[0], mb[1]);
+  const float m_new = fmaxf(m_run, m_tile);  // finite: m_run starts at -FLT_MAX
   const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile, exactly 1 if m is unchanged
   m_run = m_new;
-  // E8M0 of each P block: from its largest P~ (0 for a fully masked block: code 0)
-  const uint32_t pc0 = e8m0_code(fast_exp2(mb[0] - base));
-  const uint32_t pc1 = e8m0_code(fast_exp2(mb[1] - base));
+  float base, resc = alpha;  // exponent base of the quantized values; factor on O before the MFMA
+  uint32_t pc0, pc1;
+  if constexpr (P2L) {
+    // Level one: the row's largest P~ of this tile maps to 6.  A row with no visible key in the
+    // tile keeps its base (its P2 are 0 and O stays as it is).
+    const bool vis = m_tile > -INFINITY;
+    base = vis ? m_tile - kLog2_6 : b_run;
+    resc = fast_exp2(b_run - base);
+    b_run = base;
+    // E8M0 of each P2 block: from its largest value 6 exp2(block max - row max), which is
+    // exactly 6 for the block holding the row maximum
+    pc0 = vis ? e8m0_code(6.0f * fast_exp2(mb[0] - m_tile)) : 0u;
+    pc1 = vis ? e8m0_code(6.0f * fast_exp2(mb[1] - m_tile)) : 0u;
+  } else {
+    base = m_new;
+    // E8M0 of each P block: from its largest P~ (0 for a fully masked block: code 0)
+    pc0 = e8m0_code(fast_exp2(mb[0] - base));
+    pc1 = e8m0_code(fast_exp2(mb[1] - base));
+  }
   // ---- P~ (FP32), row sum of the unquantized values, E2M1 pack ----
   float psum = 0.0f;
   uint32_t pk[2][2];
@@ -157,7 +187,8 @@ __device__ __forceinline__ void softmax_pv_mx(const v16f (&acc)[2], const uint8_
       pk[T][q] = wd;
     }
   }
-  l_run = fmaf(l_run, alpha, psum);
+  // l sums the unquantized P~ = s1 P2 in the two-level form, s1 = exp2(base - m_new)
+  l_run = fmaf(l_run, alpha, P2L ? psum * fast_exp2(base - m_new) : psum);
   // ---- regroup: lane half h takes the whole 32-key half T = h (half 0's keys first) ----
 #pragma unroll
   for (int q = 0; q < 2; q++) {
@@ -169,11 +200,11 @@ __device__ __forceinline__ void softmax_pv_mx(const v16f (&acc)[2], const uint8_
   const uint32_t pcode = h ? pc1 : pc0;
   // ---- O^T += sum_blk X_V X_P (V^T P^T)_blk per 32-channel sub-tile ----
   if (!ACC_VALU) {
-    if (__any(alpha != 1.0f)) {
+    if (__any(resc != 1.0f)) {
 #pragma unroll
       for (int c = 0; c < D / 32; c++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) O[c][r] *= alpha;
+        for (int r = 0; r < 16; r++) O[c][r] *= resc;
     }
   }
   static_for<0, D / 32>([&](auto gc) {
@@ -195,7 +226,7 @@ __device__ __forceinline__ void softmax_pv_mx(const v16f (&acc)[2], const uint8_
 // Registers are budgeted for OCC work-groups per CU (three waves per SIMD at d = 128, four at
 // d = 64), which overlap one another's matrix and vector work; the K/V tiles use a 2-slot
 // ring: tile j+1 streams in while tile j is computed.
-template <int D, bool CAUSAL, int OUT, bool ACC_VALU>  // OUT: 0 bf16, 1 fp16, 2 fp32
+template <int D, bool CAUSAL, int OUT, bool ACC_VALU, bool P2L>  // OUT: 0 bf16, 1 fp16, 2 fp32
 __global__ __launch_bounds__(256, D == 64 ? 4 : 3) void attn_fwd_mx_kernel(MxArgs a) {
   using TL = MxTiles<D>;
   constexpr int NG = D / 32;  // 32-channel sub-tiles of O
@@ -258,6 +289,7 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 3) void attn_fwd_mx_kernel(MxArg
   // -FLT_MAX, not -inf: a row that sees no key (variable-length batches) keeps l = 0 and O = 0
   // instead of NaN; a row's first visible tile still gets alpha = 0 exactly.
   float m_run = -FLT_MAX, l_run = 0.0f;
+  float b_run = -FLT_MAX;  // two-level P: the level-one base of O (O_true = exp2(b_run - m_run) O)
 
   const int jend = CAUSAL ? max(0, min(nkts, (q0 + kBQ + coff + kBK - 1) / kBK)) : nkts;
   const uint8_t* kbase = a.khat + (size_t)kvh * a.Mp * (D / 2);
@@ -303,8 +335,8 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 3) void attn_fwd_mx_kernel(MxArg
       const bool masked = (CAUSAL && key0 + kBK - 1 > wq0 + coff) || (key0 + kBK > mseq);
       v16f acc[2];
       qk_tile_mx<D>(sK[b], qf, sKS[b][lane], qs, h, col, acc);
-      softmax_pv_mx<D, CAUSAL, ACC_VALU>(acc, sV[b], sDS[b], sVS[b][lane], a.qk_scale, h, col, key0, qrow + coff, mseq,
-                                         masked, O, m_run, l_run);
+      softmax_pv_mx<D, CAUSAL, ACC_VALU, P2L>(acc, sV[b], sDS[b], sVS[b][lane], a.qk_scale, h, col, key0,
+                                              qrow + coff, mseq, masked, O, m_run, l_run, b_run);
     }
     publish();
   };
@@ -318,7 +350,7 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 3) void attn_fwd_mx_kernel(MxArg
   // ---- epilogue: O / l (+ V_m); 0 for a row that saw no key ----
   const float l_tot = pair_sum(l_run);
   if (qrow >= nseq) return;
-  const float inv = 1.0f / l_tot;
+  const float inv = (P2L ? fast_exp2(b_run - m_run) : 1.0f) / l_tot;
   const bool none = l_tot == 0.0f;
   const float* vmp = a.vmean + (size_t)kvh * D;
   const SeqRows ro = seq_rows(a.ql, bseq, bh % a.H, a.H, D);
@@ -336,22 +368,22 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 3) void attn_fwd_mx_kernel(MxArg
   }
 }
 
-template <int D, bool CAUSAL, bool ACC_VALU>
+template <int D, bool CAUSAL, bool ACC_VALU, bool P2L>
 hipError_t launch_d(const Problem& p, const MxArgs& a, hipStream_t s) {
   dim3 grid(p.nqb * p.BH);
   const int out = p.out_fp32 ? 2 : (p.fp16 ? 1 : 0);
   if (out == 2)
-    hipLaunchKernelGGL((attn_fwd_mx_kernel<D, CAUSAL, 2, ACC_VALU>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_fwd_mx_kernel<D, CAUSAL, 2, ACC_VALU, P2L>), grid, dim3(256), 0, s, a);
   else if (out == 1)
-    hipLaunchKernelGGL((attn_fwd_mx_kernel<D, CAUSAL, 1, ACC_VALU>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_fwd_mx_kernel<D, CAUSAL, 1, ACC_VALU, P2L>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((attn_fwd_mx_kernel<D, CAUSAL, 0, ACC_VALU>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_fwd_mx_kernel<D, CAUSAL, 0, ACC_VALU, P2L>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-template <int D, bool ACC_VALU>
+template <int D, bool ACC_VALU, bool P2L = false>
 hipError_t launch_c(const Problem& p, const MxArgs& a, hipStream_t s) {
-  return p.causal ? launch_d<D, true, ACC_VALU>(p, a, s) : launch_d<D, false, ACC_VALU>(p, a, s);
+  return p.causal ? launch_d<D, true, ACC_VALU, P2L>(p, a, s) : launch_d<D, false, ACC_VALU, P2L>(p, a, s);
 }
 
 }  // namespace
@@ -370,6 +402,8 @@ hipError_t launch_attn_fwd_mx(const Problem& p, const Workspace& w, void* out, h
   a.H = p.H; a.Hkv = p.Hkv; a.G = p.G;
   a.xcd_map = (p.BH % (kXCD * p.G) == 0) ? 1 : 0;
   const bool valu = (p.variant & SAGE_ACC_VALU) != 0;
+  if (p.variant & SAGE_MX_P_TWO_LEVEL)  // the host check keeps SAGE_ACC_VALU out of this form
+    return p.d == 128 ? launch_c<128, false, true>(p, a, s) : launch_c<64, false, true>(p, a, s);
   if (p.d == 128) return valu ? launch_c<128, true>(p, a, s) : launch_c<128, false>(p, a, s);
   return valu ? launch_c<64, true>(p, a, s) : launch_c<64, false>(p, a, s);
 }

@@ -83,7 +83,8 @@ void carve_workspace(const Problem& p, void* base, Workspace* w) {
 namespace {
 
 constexpr unsigned kKnownBits =
-    SAGE_PATH_MXFP4 | SAGE_QK_FP8 | SAGE_SMOOTH_V | SAGE_IN_FP16 | SAGE_OUT_FP32 | SAGE_ACC_VALU;
+    SAGE_PATH_MXFP4 | SAGE_QK_FP8 | SAGE_MX_P_TWO_LEVEL | SAGE_SMOOTH_V | SAGE_IN_FP16 | SAGE_OUT_FP32 |
+    SAGE_ACC_VALU;
 
 // Per-device "is gfx950" cache, filled once per device under a mutex.
 int device_check() {
@@ -112,6 +113,8 @@ int make_problem(int B, int H, int Hkv, int N, int M, int d, int causal, float s
   if (H % Hkv) return SAGE_ERR_INVALID_ARG;
   if (variant & ~kKnownBits) return SAGE_ERR_INVALID_ARG;
   if ((variant & SAGE_PATH_MXFP4) && (variant & SAGE_QK_FP8)) return SAGE_ERR_INVALID_ARG;
+  if ((variant & SAGE_MX_P_TWO_LEVEL) && (!(variant & SAGE_PATH_MXFP4) || (variant & SAGE_ACC_VALU)))
+    return SAGE_ERR_INVALID_ARG;
   if (causal < 0 || causal > 2) return SAGE_ERR_INVALID_ARG;
   if (d != 64 && d != 128) return SAGE_ERR_UNSUPPORTED;
   if (causal == 2 && N > M) return SAGE_ERR_UNSUPPORTED;  // some rows would see no key

@@ -34,13 +34,13 @@ INV_PERM_MX = np.array([doc_vperm_mx(p // 32, p % 32) for p in range(64)])
 
 
 def fwd(q, k, v, fp16, causal, sm_scale, smooth_v=False, out_fp32=True, acc_valu=False, mxfp4=False,
-        qk_fp8=False):
+        qk_fp8=False, mx_p_two_level=False):
     """q, k, v: uint16 bits [B, H, T, d] on the host; returns the output as a device tensor."""
     B, H, N, d = q.shape
     M = k.shape[2]
     tq, tk, tv = to_dev(q, fp16), to_dev(k, fp16), to_dev(v, fp16)
     out = qa.sage_attn(tq, tk, tv, causal=causal, sm_scale=sm_scale, smooth_v=smooth_v, out_fp32=out_fp32,
-                       acc_valu=acc_valu, mxfp4=mxfp4, qk_fp8=qk_fp8)
+                       acc_valu=acc_valu, mxfp4=mxfp4, qk_fp8=qk_fp8, mx_p_two_level=mx_p_two_level)
     torch.cuda.synchronize()
     return out
 

@@ -56,6 +56,11 @@ def test_argument_errors_are_reported_before_any_device_work():
     both = qa.SAGE_PATH_MXFP4 | qa.SAGE_QK_FP8  # two Q K^T formats at once
     assert f(A, A, A, A, 1, 1, 64, 64, 64, 0, 0.0, both, 0) == qa.SAGE_ERR_INVALID_ARG
     assert qa.sage_attn_workspace_bytes(1, 1, 64, 64, 64, 0, both) == 0
+    # two-level P needs the MX path and accumulates through the MFMA C operand
+    for bad in (qa.SAGE_MX_P_TWO_LEVEL, qa.SAGE_MX_P_TWO_LEVEL | qa.SAGE_PATH_MXFP4 | qa.SAGE_ACC_VALU):
+        assert f(A, A, A, A, 1, 1, 64, 64, 64, 0, 0.0, bad, 0) == qa.SAGE_ERR_INVALID_ARG
+    assert qa.sage_attn_workspace_bytes(1, 1, 64, 64, 64, 0, qa.SAGE_MX_P_TWO_LEVEL | qa.SAGE_PATH_MXFP4) == \
+        qa.sage_attn_workspace_bytes(1, 1, 64, 64, 64, 0, qa.SAGE_PATH_MXFP4)
     # E4M3 Q^ / K^ take the INT8 layouts: the same workspace
     assert qa.sage_attn_workspace_bytes(1, 4, 300, 500, 128, 1, qa.SAGE_QK_FP8) == \
         qa.sage_attn_workspace_bytes(1, 4, 300, 500, 128, 1, 0)
