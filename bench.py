@@ -74,7 +74,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill32k",
                     help="one of: n4k, prefill32k, video17k, chunk4k_32k, prefill32k_gqa, prefill32k_qkfp8, mxfp4_32k, "
-                         "train8k (default prefill32k)")
+                         "mxfp4_32k_p2l, train8k (default prefill32k)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -133,6 +133,7 @@ def cpu_baseline(cfg, budget_s: float) -> dict:
     s = 1.0 / math.sqrt(cfg.d)
     flags = (oracle.SMOOTH_V if cfg.smooth_v else 0) | (oracle.MXFP4 if cfg.mxfp4 else 0)
     flags |= oracle.QK_E4M3 if cfg.qk_fp8 else 0
+    flags |= oracle.MX_P_TWO_LEVEL if cfg.mx_p_two_level else 0
     ops, t_used, nrows, batch = 0.0, 0.0, 0, 8
     while t_used < budget_s:
         rows = np.sort(rng.integers(0, cfg.N, batch))
@@ -291,6 +292,8 @@ def main():
         var |= qa.SAGE_PATH_MXFP4
     if cfg.qk_fp8:
         var |= qa.SAGE_QK_FP8
+    if cfg.mx_p_two_level:
+        var |= qa.SAGE_MX_P_TWO_LEVEL
     peak = PEAK_TOPS_FP4 if cfg.mxfp4 else PEAK_TOPS
     shape = qa.SageAttnShape(cfg.B, cfg.H, cfg.hkv, cfg.N, cfg.M, cfg.d, int(cfg.causal), 1.0 / math.sqrt(cfg.d), var)
     ws_bytes = qa.sage_attn_workspace_bytes_ex(shape)
@@ -340,7 +343,8 @@ def main():
                 else "4*d*(visible query-key pairs)*H*B/time")
     metric = (f"attention TOPS ({counting}) at {shape}{', E4M3 QK' if cfg.qk_fp8 else ''}, % of INT8/FP8 MFMA peak"
               if not cfg.mxfp4 else
-              f"attention TOPS ({counting}) at {shape}, MXFP4 variant, % of FP4 MFMA peak")
+              f"attention TOPS ({counting}) at {shape}, MXFP4 variant"
+              f"{' with two-level P' if cfg.mx_p_two_level else ''}, % of FP4 MFMA peak")
     line = {
         "metric": metric,
         "value": round(value, 2),
@@ -363,6 +367,8 @@ def main():
                    "parallelism": "single GPU"},
         "frac_of_peak": round(value / peak, 4),
         "attn_kernel_ms": round(kms, 4),
+        "attn_kernel_ms_median": round(float(np.median(kern_ms)), 4),
+        "attn_kernel_ms_min": round(float(np.min(kern_ms)), 4),
         "preprocess_ms": round(ms - kms, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TOPS",
                      "frac": round(achieved / peak, 4), "traffic": traffic},

@@ -53,6 +53,7 @@ class Config:
     Hkv: int = 0        # key/value heads (0: H); query head h reads key/value head h // (H // Hkv)
     qk_fp8: bool = False  # Q^, K^ in E4M3 instead of INT8
     train: bool = False   # SageBwd forward + backward (a training step of the attention)
+    mx_p_two_level: bool = False  # MX variant with two-level P quantization (row-scaled by rowmax / 6)
 
     @property
     def fp16(self) -> bool:
@@ -100,6 +101,9 @@ CONFIGS = {
     "mxfp4_32k": Config("mxfp4_32k", 1, 24, 32768, 32768, 128, "bf16", False,
                         Dist(k_off_std=2.0, v_bias_std=0.5), 1005, mxfp4=True,
                         note="MXFP4 variant"),
+    "mxfp4_32k_p2l": Config("mxfp4_32k_p2l", 1, 24, 32768, 32768, 128, "bf16", False,
+                            Dist(k_off_std=2.0, v_bias_std=0.5), 1005, mxfp4=True, mx_p_two_level=True,
+                            note="MXFP4 variant with two-level P quantization (same inputs)"),
 }
 
 
