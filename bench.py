@@ -41,8 +41,8 @@ PEAK_TOPS_FP4 = 10100.0  # MI355X dense MXFP4 MFMA peak, 10.1 PFLOP/s (the MX va
 TRAFFIC_BYTES = {
     "prefill32k": {"source_sha256_16": "a75e0fb6e5de2ed2",
                    "fetch_bytes": 1803111707, "write_bytes": 271033888},
-    "mxfp4_32k": {"source_sha256_16": "d063131a3c4d42dc",
-                  "fetch_bytes": 1694310863, "write_bytes": 201326976},
+    "mxfp4_32k": {"source_sha256_16": "003f5491510e3934",
+                  "fetch_bytes": 1694316556, "write_bytes": 201326899},
 }
 _COMMON_SOURCES = ("quantized_attention_amd/csrc/attn_device.hpp", "quantized_attention_amd/csrc/sage_common.hpp")
 KERNEL_SOURCES = {
