@@ -69,7 +69,7 @@ def lib():
         L.orc_preprocess_mx_head.restype = i
         L.orc_forward_head.argtypes = [P, P, P, i, i, i, i, i, dbl, u, P, i, P]
         L.orc_forward_head.restype = i
-        L.orc_forward_head_ties.argtypes = [P, P, P, i, i, i, i, i, dbl, u, P, i, P, dbl, P]
+        L.orc_forward_head_ties.argtypes = [P, P, P, i, i, i, i, i, dbl, u, P, i, P, dbl, P, P]
         L.orc_forward_head_ties.restype = i
         L.orc_exact_head.argtypes = [P, P, P, i, i, i, i, i, dbl, P, i, P]
         L.orc_exact_head.restype = i
@@ -176,7 +176,7 @@ def forward_head_ties(q, k, v, fp16: bool, causal: int, sm_scale: float, flags: 
                       tie_eps: float = 2.0 ** -16):
     """forward_head, and per row the count of its P rounding decisions whose input lies within
     relative distance tie_eps of a rounding boundary (where an FP32 kernel may round the other
-    way): (out, ties)."""
+    way) and a bound on the output change if all of them do: (out, ties, bound)."""
     q, k, v = _u16(q), _u16(k), _u16(v)
     N, d = q.shape
     M = k.shape[0]
@@ -187,11 +187,13 @@ def forward_head_ties(q, k, v, fp16: bool, causal: int, sm_scale: float, flags: 
         nrows, rp = len(rows), rows
     out = np.zeros((nrows, d), np.float64)
     ties = np.zeros(nrows, np.int32)
+    bound = np.zeros(nrows, np.float64)
     rc = lib().orc_forward_head_ties(_ptr(q), _ptr(k), _ptr(v), int(fp16), N, M, d, int(causal),
-                                     float(sm_scale), flags, _ptr(rp), nrows, _ptr(out), float(tie_eps), _ptr(ties))
+                                     float(sm_scale), flags, _ptr(rp), nrows, _ptr(out), float(tie_eps), _ptr(ties),
+                                     _ptr(bound))
     if rc != 0:
         raise ValueError("orc_forward_head_ties rejected its arguments")
-    return out, ties
+    return out, ties, bound
 
 
 def exact_head(q, k, v, fp16: bool, causal: int, sm_scale: float, rows=None):

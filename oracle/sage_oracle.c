@@ -586,27 +586,39 @@ static int causal_offset(int causal, int N, int M, int* off) {
  * helpers say whether x lies within relative distance eps of a boundary. */
 static int near_rel(double x, double b, double eps) { return fabs(x - b) <= eps * fabs(b); }
 
-static int e4m3_near_tie(double y, double eps) {
-  if (!(y > 0.0) || y >= 448.0) return 0;
+/* The gap between the two E4M3 values around y when y lies within relative eps of their
+ * midpoint (the change of the code's value should it round the other way), else 0. */
+static double e4m3_tie_step(double y, double eps) {
+  if (!(y > 0.0) || y >= 448.0) return 0.0;
   uint8_t c = orc_e4m3_encode(y);
   double v = orc_e4m3_decode(c);
   double w = v <= y ? orc_e4m3_decode((uint8_t)(c + 1)) : orc_e4m3_decode((uint8_t)(c - 1));
-  return near_rel(y, 0.5 * (v + w), eps);
+  return near_rel(y, 0.5 * (v + w), eps) ? fabs(w - v) : 0.0;
 }
 
-static int e2m1_near_tie(double y, double eps) {
+/* The same for E2M1 (midpoints of the value set and the gaps around them). */
+static double e2m1_tie_step(double y, double eps) {
   static const double mid[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+  static const double gap[7] = {0.5, 0.5, 0.5, 0.5, 1.0, 1.0, 2.0};
   for (int i = 0; i < 7; i++)
-    if (near_rel(fabs(y), mid[i], eps)) return 1;
-  return 0;
+    if (near_rel(fabs(y), mid[i], eps)) return gap[i];
+  return 0.0;
 }
 
-/* Steps 7-8 for one row: the tile loop and the epilogue.  With ties != NULL, *ties counts the
- * P quantization decisions of the row whose inputs lie within relative tie_eps of a rounding
- * boundary. */
+/* Per-row margin bookkeeping: the count of near-boundary decisions, and a bound on how far
+ * the row's output moves if every one of them rounds the other way -- the change of each
+ * affected P^ value times the largest dequantized V value of its key, carried through the
+ * tile loop like O (scaled by alpha, divided by l at the end). */
+typedef struct { int count; double mass; } margin_t;
+
+/* Steps 7-8 for one row: the tile loop and the epilogue.  With mg != NULL, *ties and *bound
+ * receive the row's near-boundary decisions (inputs within relative tie_eps of a rounding
+ * boundary) and the bound on the output change they can cause. */
 static void forward_row(const head_t* h, int r, int causal, int off, double sm_scale, const double* ds,
-                        double* S, double* Pt, double* Ph, double* R, double* out, double tie_eps, int* ties) {
-  if (ties) *ties = 0;
+                        double* S, double* Pt, double* Ph, double* R, double* out, double tie_eps, int* ties,
+                        double* bound) {
+  margin_t mg = {0, 0.0};
+  const int track = ties != NULL || bound != NULL;
   int d = h->d, M = h->M;
   double m = -INFINITY, l = 0.0;
   for (int c = 0; c < d; c++) out[c] = 0.0;
@@ -634,6 +646,7 @@ static void forward_row(const head_t* h, int r, int causal, int off, double sm_s
     }
     /* Reading: l accumulates the unquantized P~ (the online softmax precedes the cast). */
     l = alpha * l + sum;
+    mg.mass *= alpha;
     if (h->flags & ORC_MXFP4) {
       /* P~ in E2M1 with one E8M0 scale per 32 keys of the row (2 blocks per 64-key tile);
        * R = sum_blk X_P X_V (P^ . V^)_blk. */
@@ -661,13 +674,31 @@ static void forward_row(const head_t* h, int r, int causal, int off, double sm_s
         for (int x = b0; x < b1; x++) if (Pt[x] > am) am = Pt[x];
         int ep = orc_e8m0_exponent(am);
         for (int x = b0; x < b1; x++) Ph[x] = orc_e2m1_decode(orc_e2m1_encode(ldexp(Pt[x], -ep)));
-        /* the two-level row maximum is exactly 6 by construction, not a rounded input */
-        if (ties && am > 0.0 && !(two && am == 6.0)) {
-          *ties += near_rel(am, 6.0 * ldexp(1.0, ep), tie_eps) + near_rel(am, 6.0 * ldexp(1.0, ep - 1), tie_eps);
-        }
-        if (ties)
-          for (int x = b0; x < b1; x++) *ties += e2m1_near_tie(ldexp(Pt[x], -ep), tie_eps);
         int vb = (t0 + b0) / 32;
+        if (track) {
+          /* the largest dequantized V' value of key x, over channels */
+          double blk = 0.0;
+          for (int x = b0; x < b1; x++) {
+            double vm = 0.0;
+            for (int c = 0; c < d; c++) {
+              double a = fabs(ldexp(h->vx[(size_t)(t0 + x) * d + c], h->ve[(size_t)vb * d + c]));
+              if (a > vm) vm = a;
+            }
+            double st = e2m1_tie_step(ldexp(Pt[x], -ep), tie_eps);
+            mg.count += st > 0.0;
+            blk += st * vm;
+            S[x] = vm; /* kept for the exponent decision below (S is not read again) */
+          }
+          /* the block exponent: a near-boundary maximum may move the whole block one octave,
+           * each value by at most one top step (2) of the coarser grid (the two-level row
+           * maximum is exactly 6 by construction, not a rounded input) */
+          if (am > 0.0 && !(two && am == 6.0) &&
+              (near_rel(am, 6.0 * ldexp(1.0, ep), tie_eps) || near_rel(am, 6.0 * ldexp(1.0, ep - 1), tie_eps))) {
+            mg.count++;
+            for (int x = b0; x < b1; x++) blk += 4.0 * S[x];
+          }
+          mg.mass += s1 * ldexp(blk, ep);
+        }
         for (int c = 0; c < d; c++) {
           double p = 0.0;
           for (int x = b0; x < b1; x++) p += Ph[x] * h->vx[(size_t)(t0 + x) * d + c];
@@ -677,8 +708,18 @@ static void forward_row(const head_t* h, int r, int causal, int off, double sm_s
       for (int c = 0; c < d; c++) R[c] *= s1;
     } else {
       for (int x = 0; x < n; x++) Ph[x] = quant_p(h, Pt[x]);
-      if (ties && !(h->flags & (ORC_PV_IDENTITY | ORC_PV_E5M2 | ORC_PV_INT8)))
-        for (int x = 0; x < n; x++) *ties += e4m3_near_tie(h->pscale * Pt[x], tie_eps);
+      if (track && !(h->flags & (ORC_PV_IDENTITY | ORC_PV_E5M2 | ORC_PV_INT8)))
+        for (int x = 0; x < n; x++) {
+          double st = e4m3_tie_step(h->pscale * Pt[x], tie_eps);
+          if (st == 0.0) continue;
+          double vm = 0.0; /* the largest dequantized V value of the key (V^ times dV) */
+          for (int c = 0; c < d; c++) {
+            double a = fabs(h->vq[(size_t)(t0 + x) * d + c] * (double)h->dv[c]);
+            if (a > vm) vm = a;
+          }
+          mg.count++;
+          mg.mass += st * vm / h->pscale;
+        }
       /* R = P^ V^ over this tile only (the per-tile inner accumulator). */
       for (int c = 0; c < d; c++) {
         double acc = 0.0;
@@ -698,17 +739,20 @@ static void forward_row(const head_t* h, int r, int causal, int off, double sm_s
     if (!(h->flags & ORC_MXFP4)) o = o / h->pscale * (double)h->dv[c];
     out[c] = o + (double)h->vmean[c];
   }
+  if (ties) *ties = mg.count;
+  if (bound) *bound = mg.mass / l;
 }
 
 int orc_forward_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, int in_fp16,
                      int N, int M, int d, int causal, double sm_scale, unsigned flags,
                      const int* rows, int nrows, double* out) {
-  return orc_forward_head_ties(q, k, v, in_fp16, N, M, d, causal, sm_scale, flags, rows, nrows, out, 0.0, NULL);
+  return orc_forward_head_ties(q, k, v, in_fp16, N, M, d, causal, sm_scale, flags, rows, nrows, out, 0.0, NULL,
+                               NULL);
 }
 
 int orc_forward_head_ties(const uint16_t* q, const uint16_t* k, const uint16_t* v, int in_fp16,
                           int N, int M, int d, int causal, double sm_scale, unsigned flags,
-                          const int* rows, int nrows, double* out, double tie_eps, int* ties) {
+                          const int* rows, int nrows, double* out, double tie_eps, int* ties, double* bound) {
   int off;
   if (!q || !k || !v || !out || nrows < 0) return -1;
   if (causal_offset(causal, N, M, &off)) return -1;
@@ -746,7 +790,7 @@ int orc_forward_head_ties(const uint16_t* q, const uint16_t* k, const uint16_t* 
       for (int x = 0; x < nrows; x++) {
         int r = rows ? rows[x] : x;
         forward_row(&h, r, causal, off, sm_scale, dsr[r / ORC_BQ], S, Pt, Ph, R, out + (size_t)x * d, tie_eps,
-                    ties ? ties + x : NULL);
+                    ties ? ties + x : NULL, bound ? bound + x : NULL);
       }
       free(S); free(Pt); free(Ph); free(R);
     }

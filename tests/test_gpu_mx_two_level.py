@@ -7,13 +7,14 @@ E2M1 block quantizer; the tile's product multiplied back by the factor), with th
 s1 = rowmax / 6 for E8M0 block scales.
 
 Bars: the output within mean |err| <= 1e-3 of the oracle run with the same knob (FP32
-output), and within max |err| <= 1e-2 on every row none of whose P rounding decisions has its
-input within 2^-16 (relative) of a rounding boundary.  On the rows the oracle flags, the
-kernel's FP32 exponentials may round a code the other way -- either code is a correct rounding
-of the method's value -- and one step at the top of the E2M1 grid (4 <-> 6, a third of the row
-maximum) can move a short row by about 1e-2; their error is reported.  On the lossless
-two-level construction (every quantizer exact), the output equals textbook attention up to
-FP32 arithmetic, while the direct P quantizer does not.
+output), and every row within max |err| <= 1e-2 plus the oracle's bound for that row's
+near-boundary decisions: P rounding decisions whose input lies within 2^-16 (relative) of a
+rounding boundary, where the kernel's FP32 exponentials may round the other way (either code
+is a correct rounding of the method's value; one step at the top of the E2M1 grid, 4 <-> 6, is
+a third of the row maximum).  The bound is the change of each such P^ value times its key's
+largest V value, carried through the tile loop like O; it is 0 on rows without such a
+decision.  On the lossless two-level construction (every quantizer exact), the output equals
+textbook attention up to FP32 arithmetic, while the direct P quantizer does not.
 """
 import math
 import sys
@@ -69,19 +70,19 @@ def test_two_level_parity_small(name, cfg):
     out = run(cfg, q, k, v)
     s = 1 / math.sqrt(cfg.d)
     fl = FLAGS | (oracle.SMOOTH_V if cfg.smooth_v else 0)
-    err, tie = [], []
+    err, bnd = [], []
     for bh in range(cfg.B * cfg.H):
         b, h = bh // cfg.H, bh % cfg.H
-        ref, t = oracle.forward_head_ties(q[b, h], k[b, h], v[b, h], cfg.fp16, cfg.causal, s, fl)
+        ref, _, bd = oracle.forward_head_ties(q[b, h], k[b, h], v[b, h], cfg.fp16, cfg.causal, s, fl)
         err.append(np.abs(out[b, h].astype(np.float64) - ref))
-        tie.append(t > 0)
-    err, tie = np.stack(err), np.stack(tie)
-    clean = err[~tie]
-    say(f"  max abs {clean.max() if clean.size else 0:.3g} mean abs {err.mean():.3g}; "
-        f"{tie.sum()} rows near a rounding boundary, max abs there {err[tie].max() if tie.any() else 0:.3g}")
+        bnd.append(bd)
+    err, bnd = np.stack(err), np.stack(bnd)
+    rmax = err.max(axis=-1)
+    say(f"  max abs {err.max():.3g} mean abs {err.mean():.3g}; {(bnd > 0).sum()} rows with near-boundary "
+        f"decisions (bound up to {bnd.max():.3g}); max abs beyond the bound {(rmax - bnd).max():.3g}")
     assert np.isfinite(out).all()
     assert err.mean() <= MEAN_ABS
-    assert clean.size == 0 or clean.max() <= MAX_ABS
+    assert (rmax <= MAX_ABS + bnd).all()
 
 
 @pytest.mark.parametrize("N,M,d,causal", [(256, 256, 64, False), (256, 256, 64, True), (192, 512, 128, False)])
@@ -110,8 +111,9 @@ def test_two_level_full_size_sampled():
         b, h = bh // cfg.H, bh % cfg.H
         rows = np.array(sorted(set([0, 1, 127, 128, cfg.N // 2, cfg.N - 1] + list(rng.integers(0, cfg.N, 12)))))
         got = out[b, h, torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
-        ref, t = oracle.forward_head_ties(q[b, h], k[b, h], v[b, h], cfg.fp16, cfg.causal, s, FLAGS, rows=rows)
+        ref, _, bd = oracle.forward_head_ties(q[b, h], k[b, h], v[b, h], cfg.fp16, cfg.causal, s, FLAGS, rows=rows)
         err = np.abs(got - ref)
-        say(f"  head {bh}: max abs {err.max():.3g}, {(t > 0).sum()} rows near a rounding boundary")
+        say(f"  head {bh}: max abs {err.max():.3g}, {(bd > 0).sum()} rows with near-boundary decisions "
+            f"(bound up to {bd.max():.3g})")
         assert err.mean() <= MEAN_ABS
-        assert err[t == 0].max() <= MAX_ABS
+        assert (err.max(axis=-1) <= MAX_ABS + bd).all()

@@ -235,15 +235,22 @@ def test_tie_diagnostic_counts_exact_midpoints():
     """The rounding-boundary diagnostic: with the two-level construction's scores (two levels one
     unit apart, all rows equal) and sm_scale = ln(448 / 17), every low key has 448 P~ = 17, the
     midpoint between the E4M3 values 16 and 18, and every high key 448; so a row's count is the
-    number of low keys it sees (non-causal: all of them, once per row)."""
+    number of low keys it sees after the first high one (non-causal: the same for every row),
+    and its bound is those keys' P^ gap (2, of 448) times their largest dequantized V value,
+    over l = (high keys) + (low keys) 17 / 448."""
     N = M = 256
     Q, K, V = two_level_case(7, N, M, 64)
     q, k, v = f16(Q), f16(K), f16(V)
-    out, ties = oracle.forward_head_ties(q, k, v, True, False, math.log(448 / 17), 0)
-    n_low = int((K[:, 0] == 0).sum())
+    out, ties, bound = oracle.forward_head_ties(q, k, v, True, False, math.log(448 / 17), 0)
+    hi = K[:, 0] == 1
     # low keys before the first high one were quantized relative to their own (lower) maximum:
     # there 448 P~ = 448 exactly, not a tie
-    first_hi = int(np.flatnonzero(K[:, 0] == 1)[0])
-    lead = (first_hi // 64) * 64
-    assert (ties == n_low - lead).all()
+    lead = (int(np.flatnonzero(hi)[0]) // 64) * 64
+    late_low = ~hi & (np.arange(M) >= lead)
+    assert (ties == late_low.sum()).all()
+    p = oracle.preprocess_head(q, k, v, True)
+    vdq = oracle.e4m3_decode_table()[p["vhat"]] * p["dv"].astype(np.float64)[None, :]
+    vm = np.abs(vdq).max(axis=1)
+    l = hi.sum() + (~hi).sum() * 17 / 448
+    assert np.allclose(bound, (2 / 448) * vm[late_low].sum() / l, rtol=1e-12, atol=0)
     assert np.array_equal(out, oracle.forward_head(q, k, v, True, False, math.log(448 / 17), 0))
