@@ -232,11 +232,21 @@ __global__ __launch_bounds__(256) void q_prep_kernel(const uint16_t* __restrict_
   if (r0 >= R.len) return;  // past this sequence's queries: the block is never read
   const int n = min(kBQ, R.len - r0);
   const size_t in_base = R.base + (size_t)r0 * R.stride;
+  {
+    // all of this thread's row chunks in flight at once (rows past the block's last valid row
+    // re-read that row and are not stored; nothing reads them), then into LDS
+    constexpr int NCH = kBQ * D / 8 / 256;
+    v4i raw[NCH];
 #pragma unroll
-  for (int k = 0; k < kBQ * D / 8 / 256; k++) {
-    const int x = tid + 256 * k, r = x / (D / 8), c0 = (x % (D / 8)) * 8;
-    if (r < n)
-      *reinterpret_cast<v4i*>(&sq[r * RS + c0]) = *reinterpret_cast<const v4i*>(Q + in_base + (size_t)r * R.stride + c0);
+    for (int k = 0; k < NCH; k++) {
+      const int x = tid + 256 * k, r = x / (D / 8), c0 = (x % (D / 8)) * 8;
+      raw[k] = *reinterpret_cast<const v4i*>(Q + in_base + (size_t)min(r, n - 1) * R.stride + c0);
+    }
+#pragma unroll
+    for (int k = 0; k < NCH; k++) {
+      const int x = tid + 256 * k, r = x / (D / 8), c0 = (x % (D / 8)) * 8;
+      if (r < n) *reinterpret_cast<v4i*>(&sq[r * RS + c0]) = raw[k];
+    }
   }
   __syncthreads();
   if (tid < D) {

@@ -56,11 +56,17 @@ __global__ __launch_bounds__(256) void sb_quant_kernel(const uint16_t* __restric
   const size_t base = ((size_t)bh * T + r0) * D;
   float x[CH][8];
   float am = 0.0f;
+  v4i raws[CH];  // every chunk of the thread in flight at once (rows >= n re-read row n - 1, unused)
+#pragma unroll
+  for (int i = 0; i < CH; i++) {
+    const int e = tid + 256 * i, r = e / (D / 8), c0 = (e % (D / 8)) * 8;
+    raws[i] = *reinterpret_cast<const v4i*>(src + base + (size_t)min(r, n - 1) * D + c0);
+  }
 #pragma unroll
   for (int i = 0; i < CH; i++) {
     const int e = tid + 256 * i, r = e / (D / 8), c0 = (e % (D / 8)) * 8;
     if (r < n) {
-      const v4i raw = *reinterpret_cast<const v4i*>(src + base + (size_t)r * D + c0);
+      const v4i raw = raws[i];
 #pragma unroll
       for (int k = 0; k < 4; k++) {
         const uint32_t u = static_cast<uint32_t>(raw[k]);
@@ -313,28 +319,70 @@ __device__ __forceinline__ v16f mfma16(const v4i& a, const v4i& b, const v16f& c
                                                    0);
 }
 
+// 8 consecutive 16-bit inputs (bf16 or fp16) widened to FP32.
+__device__ __forceinline__ void sb_widen8(const v4i& raw, bool fp16, float (&x)[8]) {
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    const uint32_t u = static_cast<uint32_t>(raw[e]);
+    if (fp16) {
+      x[2 * e] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(u & 0xffffu)));
+      x[2 * e + 1] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(u >> 16)));
+    } else {
+      x[2 * e] = __uint_as_float(u << 16);
+      x[2 * e + 1] = __uint_as_float(u & 0xffff0000u);
+    }
+  }
+}
+
 // ---- backward preprocessing: D = rowsum(dO o O) (FP64 sum), L2 = L log2(e); padded rows
-// get D = 0 and L2 = +inf (their P is 0) ----
+// get D = 0 and L2 = +inf (their P is 0).  A row is spread over D/8 lanes holding 8
+// consecutive channels each (16- or 32-byte loads); every load of the thread's rows is issued
+// before any is used, and the lanes' FP64 partial sums meet in a butterfly. ----
 template <int D, int OUT>
 __global__ __launch_bounds__(256) void sb_dprep_kernel(const void* __restrict__ out, const uint16_t* __restrict__ dout,
                                                        const float* __restrict__ lse, float* __restrict__ Dr,
                                                        float* __restrict__ L2, int N, int Np, bool fp16) {
-  const int tid = threadIdx.x, bh = blockIdx.y;
-  const int row = blockIdx.x * kBQ + (tid >> 1), half = tid & 1;
-  double s = 0.0;
-  if (row < N) {
-    const size_t base = ((size_t)bh * N + row) * D + half * (D / 2);
-    for (int c = 0; c < D / 2; c++) {
-      const float o = OUT == 2 ? reinterpret_cast<const float*>(out)[base + c]
-                               : load_in(reinterpret_cast<const uint16_t*>(out), base + c, OUT == 1);
-      s += (double)load_in(dout, base + c, fp16) * (double)o;
+  constexpr int LPR = D / 8;          // lanes per row
+  constexpr int RPP = 256 / LPR;      // rows per pass
+  constexpr int NP = kBQ / RPP;       // passes per 128-row block
+  const int tid = threadIdx.x, bh = blockIdx.y, sub = tid / LPR, cl = tid % LPR;
+  v4i rd[NP], ro[NP], ro2[NP];
+#pragma unroll
+  for (int p = 0; p < NP; p++) {
+    const int row = min(blockIdx.x * kBQ + p * RPP + sub, N - 1);  // rows >= N: a valid row, not used
+    const size_t base = ((size_t)bh * N + row) * D + 8 * cl;
+    rd[p] = *reinterpret_cast<const v4i*>(dout + base);
+    if constexpr (OUT == 2) {
+      ro[p] = *reinterpret_cast<const v4i*>(reinterpret_cast<const float*>(out) + base);
+      ro2[p] = *reinterpret_cast<const v4i*>(reinterpret_cast<const float*>(out) + base + 4);
+    } else {
+      ro[p] = *reinterpret_cast<const v4i*>(reinterpret_cast<const uint16_t*>(out) + base);
     }
   }
-  s += __shfl_xor(s, 1);
-  if (half == 0) {
-    const size_t o = (size_t)bh * Np + row;
-    Dr[o] = row < N ? (float)s : 0.0f;
-    L2[o] = row < N ? lse[(size_t)bh * N + row] * kLog2e : INFINITY;
+#pragma unroll
+  for (int p = 0; p < NP; p++) {
+    const int row = blockIdx.x * kBQ + p * RPP + sub;
+    float dv[8], ov[8];
+    sb_widen8(rd[p], fp16, dv);
+    if constexpr (OUT == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        ov[e] = __int_as_float(ro[p][e]);
+        ov[4 + e] = __int_as_float(ro2[p][e]);
+      }
+    } else {
+      sb_widen8(ro[p], OUT == 1, ov);
+    }
+    double s = 0.0;
+#pragma unroll
+    for (int e = 0; e < 8; e++) s += (double)dv[e] * (double)ov[e];
+#pragma unroll
+    for (int x = 1; x < LPR; x <<= 1) s += __shfl_xor(s, x);
+    if (cl == 0) {
+      const size_t o = (size_t)bh * Np + row;
+      Dr[o] = row < N ? (float)s : 0.0f;
+      L2[o] = row < N ? lse[(size_t)bh * N + row] * kLog2e : INFINITY;
+    }
   }
 }
 
