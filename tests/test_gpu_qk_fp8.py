@@ -10,15 +10,17 @@ Bars:
   * the output within mean |err| <= 1e-3 of the oracle (FP32 output), and its cosine
     against FP64 attention within 1e-4 of the oracle's own (0.9985 - 0.9999 on these
     inputs), with a floor of 0.998;
-  * at least 99% of the rows within max |err| <= 1e-2 (the INT8 path's bar, which holds
-    there for every row), and every row within one P^ step: max |err| <= max|V| / 8.
-    Why not every row: the oracle sums Q^ K^ exactly, while the FP8 MFMA sums each
-    64-channel step in an internal accumulator below FP32 (about 2^-15 of the step's largest
-    code product).  A score can then differ from the oracle's by ~1e-4 - 1e-3 (log2 units),
-    and where 448 P~ lies that close to an E4M3 rounding midpoint the two sides store
+  * every row within max |err| <= 1e-2 plus the oracle's margin bound for that row, taken
+    with a relative margin of 2^-12 around the E4M3 rounding midpoints of 448 P~ (0 on rows
+    with no P~ that close to a midpoint), and within one P^ step: max |err| <= max|V| / 8.
+    Why a margin: the oracle sums Q^ K^ exactly, while the FP8 MFMA sums each 64-channel
+    step in an internal accumulator below FP32 (about 2^-15 of the step's largest code
+    product).  A score can then differ from the oracle's by ~1e-5 - 1e-4 (log2 units), and
+    where 448 P~ lies that close to an E4M3 rounding midpoint the two sides store
     neighbouring P^ codes.  One E4M3 step (at most 1/8 of the value) of one key moves its
     row by up to (1/8) (P~_t / l) |v_t - o|: invisible in a long row, up to a few 1e-2 in a
-    short causal one.  The INT8 MFMA sums exactly, so the INT8 path has no such rows.
+    short causal one.  The bound is that move for every flagged key of the row.  The INT8
+    MFMA sums exactly, so the INT8 path needs no such margin.
 """
 import math
 import sys
@@ -32,18 +34,21 @@ from quantized_attention_amd import synthetic as sy
 
 pytestmark = pytest.mark.gpu
 
-ROW_ABS, ROW_SHARE, MEAN_ABS, MIN_COS, COS_MATCH = 1e-2, 0.01, 1e-3, 0.998, 1e-4
+ROW_ABS, MEAN_ABS, MIN_COS, COS_MATCH = 1e-2, 1e-3, 0.998, 1e-4
+TIE_EPS = 2.0 ** -12  # relative margin around the E4M3 midpoints (the FP8 MFMA's score error, x4)
 
 
-def check_rows(got, ref, vmax, min_rows_over=1):
-    """got, ref: [..., rows, d].  Mean bar on all elements; per-row max bar on all but a
-    small share of rows; the one-step bound on every row."""
+def check_rows(got, ref, bound, vmax):
+    """got, ref: [..., rows, d]; bound: [..., rows].  Mean bar on all elements; every row within
+    the max bar plus its margin bound, and within the one-step bound."""
     err = np.abs(got - ref)
     row = err.reshape(-1, err.shape[-1]).max(axis=1)
+    bd = np.asarray(bound, np.float64).reshape(-1)
     over = int((row > ROW_ABS).sum())
-    say(f"  rows over {ROW_ABS}: {over} of {row.size}; worst {row.max():.3g} (one-step bound {vmax / 8:.3g})")
+    say(f"  rows over {ROW_ABS}: {over} of {row.size}; worst {row.max():.3g}; rows with a margin: {(bd > 0).sum()}; "
+        f"worst beyond 1e-2 + margin {(row - ROW_ABS - bd).max():.3g} (one-step bound {vmax / 8:.3g})")
     assert err.mean() <= MEAN_ABS
-    assert over <= max(min_rows_over, ROW_SHARE * row.size)
+    assert (row <= ROW_ABS + bd).all()
     assert row.max() <= vmax / 8
 
 
@@ -112,11 +117,13 @@ def test_qk_fp8_forward_parity_small(name, cfg):
     say(f"qk-fp8 forward {name} B={cfg.B} H={cfg.H} N={cfg.N} M={cfg.M} d={cfg.d} causal={cfg.causal}")
     out = gu.fwd(q, k, v, cfg.fp16, cfg.causal, None, cfg.smooth_v, qk_fp8=True).cpu().numpy()
     s = 1 / math.sqrt(cfg.d)
-    got, ref, ex = [], [], []
+    got, ref, ex, bnd = [], [], [], []
     for b, h, gh in heads(cfg):
         got.append(out[b, h].astype(np.float64))
-        ref.append(oracle.forward_head(q[b, h], k[b, gh], v[b, gh], cfg.fp16, cfg.causal, s,
-                                       vflags(cfg) | oracle.QK_E4M3))
+        o, _, bd = oracle.forward_head_ties(q[b, h], k[b, gh], v[b, gh], cfg.fp16, cfg.causal, s,
+                                            vflags(cfg) | oracle.QK_E4M3, tie_eps=TIE_EPS)
+        ref.append(o)
+        bnd.append(bd)
         ex.append(oracle.exact_head(q[b, h], k[b, gh], v[b, gh], cfg.fp16, cfg.causal, s))
     g, r, e = np.stack(got), np.stack(ref), np.stack(ex)
     err = np.abs(g - r)
@@ -124,7 +131,7 @@ def test_qk_fp8_forward_parity_small(name, cfg):
         f"cos(oracle, fp64) {cosine(r, e):.6f}")
     assert np.isfinite(g).all()
     vmax = max(np.abs(sy.bits_to_f32(v, cfg.fp16)).max(), 1.0)
-    check_rows(g, r, vmax)
+    check_rows(g, r, np.stack(bnd), vmax)
     if cfg.N > 8:
         assert cosine(g, e) >= MIN_COS
         assert abs(cosine(g, e) - cosine(r, e)) <= COS_MATCH
@@ -153,7 +160,7 @@ def test_qk_fp8_full_size_sampled(name):
         b, h = bh // cfg.H, bh % cfg.H
         rows = np.array(sorted(set([0, 1, 127, 128, cfg.N // 2, cfg.N - 1] + list(rng.integers(0, cfg.N, 16)))))
         got = out[b, h, torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
-        ref = oracle.forward_head(q[b, h], k[b, h], v[b, h], cfg.fp16, cfg.causal, s,
-                                  vflags(cfg) | oracle.QK_E4M3, rows=rows)
+        ref, _, bd = oracle.forward_head_ties(q[b, h], k[b, h], v[b, h], cfg.fp16, cfg.causal, s,
+                                              vflags(cfg) | oracle.QK_E4M3, rows=rows, tie_eps=TIE_EPS)
         say(f"  head {bh}:")
-        check_rows(got, ref, max(np.abs(sy.bits_to_f32(v[b, h], cfg.fp16)).max(), 1.0))
+        check_rows(got, ref, bd, max(np.abs(sy.bits_to_f32(v[b, h], cfg.fp16)).max(), 1.0))
