@@ -119,6 +119,33 @@ def test_two_equal_score_keys_closed_form():
     assert np.abs(o["dk"][1] + sm * a * qv).max() <= 1e-12 * max(1, abs(a) * 16)
 
 
+def test_smoothing_k_term_of_dq_closed_form():
+    """The smoothing-K term of dQ, sm rowsum(dS) k, in isolation.  N = 1, two keys
+    kbar +- w with w along channel 0 only and kbar = 8 on channel 1 (so gamma K and K^ are 0
+    there): the main term sm dS^ K^ contributes nothing to dQ[1], and
+    dQ[1] = sm * 8 * rowsum(dS).  The backward's P = exp(S - L) sums to 1 and dP = dO V^T is
+    exact on 16-bit inputs, so rowsum(dS) = dO . O_exact - D with D = dO . O from the forward,
+    whose INT8 P^ is lossy here (127 e^-delta is not an integer).  O_exact is numpy's softmax
+    of the scores times V.  Dropping the term, its sign or its sm_scale fails this."""
+    rng = np.random.default_rng(3)
+    d, sm = 64, 0.2
+    qv = np.zeros(d); qv[0] = 127 * 2.0 ** -7
+    w = np.zeros(d); w[0] = 127 * 2.0 ** -6  # scales 2^-7, 2^-6: exact; P~ ratio e^-(2 sm q0 w0), lossy in INT8
+    kbar = np.zeros(d); kbar[1] = 8.0
+    K = np.stack([kbar + w, kbar - w])
+    V = grid_rows(rng, 2, d, -5)
+    dO = grid_rows(rng, 1, d, -2)
+    q, k, v, do = f16(qv[None]), f16(K), f16(V), f16(dO)
+    o = oracle.sagebwd_backward(q, k, v, do, True, 0, sm)
+    s = sm * (K @ qv)
+    p = np.exp(s - s.max())
+    o_exact = (p / p.sum()) @ V
+    rs = dO[0] @ o_exact - dO[0] @ o["out"][0]
+    assert abs(rs) > 1e-4  # the forward's P^ is lossy: the term does not vanish
+    # rowsum(dS) is a difference of terms near D (~3e2 here), so FP64 rounding leaves ~1e-13 on it
+    assert abs(o["dq"][0, 1] - sm * 8.0 * rs) <= 1e-9 * abs(sm * 8.0 * rs)
+
+
 def test_backward_p_scale_is_per_block():
     """Rows 0 (peaked, P ~ [1, 0]) and 1 (split, P = [1/2, 1/2]) share one block: the split row's
     P^ is coded against the block max P_00, so 0.5 becomes rne(63.5 / P_00) * P_00 / 127."""
