@@ -123,6 +123,32 @@ def test_train_backward_parity(name, cfg, smooth_k):
         assert np.isfinite(mx) and mx <= 1e-2 and mn <= 1e-3, nm
 
 
+def test_train_full_size():
+    """The train8k workload (B=1 H=32 N=M=8192 d=128 bf16 causal) in the launch configuration the
+    benchmark times, FP32 outputs: the forward (out, lse) and all three gradients of the first
+    and the last head against the oracle, whole heads, to the bars above."""
+    cfg = sy.CONFIGS["train8k"]
+    q, k, v = sy.make_qkv(cfg)
+    do = rand_bits(q.shape, cfg.fp16, 45)
+    say(f"train full size B={cfg.B} H={cfg.H} N={cfg.N} d={cfg.d} causal={cfg.causal}")
+    tq, tk, tv, tdo = (gu.to_dev(x, cfg.fp16) for x in (q, k, v, do))
+    out, lse = qa.sage_attn_train_forward(tq, tk, tv, cfg.causal, None, out_fp32=True)
+    dq, dk, dv = qa.sage_attn_train_backward(tq, tk, tv, out, tdo, lse, cfg.causal, None)
+    torch.cuda.synchronize()
+    s = 1 / math.sqrt(cfg.d)
+    for h in (0, cfg.H - 1):
+        ref = oracle.sagebwd_backward(q[0, h], k[0, h], v[0, h], do[0, h], cfg.fp16, cfg.causal, s)
+        o = out[0, h].cpu().numpy().astype(np.float64)
+        err = np.abs(o - ref["out"])
+        lerr = np.abs(lse[0, h].cpu().numpy().astype(np.float64) - ref["lse"]).max()
+        say(f"  head {h}: out max {err.max():.3g} mean {err.mean():.3g}; lse {lerr:.3g}")
+        assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS and lerr <= LSE_ABS
+        for nm, got in (("dq", dq[0, h]), ("dk", dk[0, h]), ("dv", dv[0, h])):
+            mx, mn = rel_err(got.cpu().numpy(), ref[nm])
+            say(f"  head {h} {nm}: max rel {mx:.3g} mean rel {mn:.3g}")
+            assert np.isfinite(mx) and mx <= 1e-2 and mn <= 1e-3, nm
+
+
 def test_train_autograd_function():
     cfg = sy.CONFIGS["prefill32k"].with_shape(H=2, N=200, M=200)
     q, k, v = sy.make_qkv(cfg)
