@@ -73,8 +73,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill32k",
-                    help="one of: n4k, prefill32k, video17k, chunk4k_32k, prefill32k_gqa, prefill32k_qkfp8, mxfp4_32k, "
-                         "mxfp4_32k_p2l, train8k (default prefill32k)")
+                    help="one of: n4k, prefill32k, full32k, video17k, chunk4k_32k, prefill32k_gqa, prefill32k_qkfp8, "
+                         "mxfp4_32k, mxfp4_32k_p2l, train8k (default prefill32k)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -366,6 +366,8 @@ def main():
                    "global_batch": cfg.B, "seq_len": cfg.N, "heads": cfg.H, "head_dim": cfg.d,
                    "parallelism": "single GPU"},
         "frac_of_peak": round(value / peak, 4),
+        # the raw formula 4 N^2 d H B / time, without the causal halving (causal N = M only)
+        "tops_raw_formula": round(2 * value, 2) if (cfg.causal and cfg.N == cfg.M) else round(value, 2),
         "attn_kernel_ms": round(kms, 4),
         "attn_kernel_ms_median": round(float(np.median(kern_ms)), 4),
         "attn_kernel_ms_min": round(float(np.min(kern_ms)), 4),

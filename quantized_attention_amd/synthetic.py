@@ -92,6 +92,9 @@ CONFIGS = {
     "prefill32k_gqa": Config("prefill32k_gqa", 1, 32, 32768, 32768, 128, "bf16", 1,
                              Dist(k_off_std=4.0, k_spike=8.0, k_spike_channels=spike_channels(128)), 1007,
                              Hkv=8, note="LLM prefill with grouped key/value heads (32 query heads, 8 key/value)"),
+    "full32k": Config("full32k", 1, 32, 32768, 32768, 128, "bf16", False,
+                      Dist(k_off_std=4.0, k_spike=8.0, k_spike_channels=spike_channels(128)), 1003,
+                      note="the prefill layer's shape and inputs without the causal mask (no counting convention)"),
     "prefill32k_qkfp8": Config("prefill32k_qkfp8", 1, 32, 32768, 32768, 128, "bf16", True,
                                Dist(k_off_std=4.0, k_spike=8.0, k_spike_channels=spike_channels(128)), 1003,
                                qk_fp8=True, note="the prefill layer with Q^, K^ in E4M3 (same inputs)"),
