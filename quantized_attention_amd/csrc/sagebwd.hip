@@ -157,6 +157,22 @@ struct FwdArgs {
   float qk_scale;    // sm_scale * log2(e)
 };
 
+// Work-group L of a grid of nblk blocks per head -> (head, block).  Work-groups are dealt to the
+// 8 XCDs round-robin; XCD x takes whole heads x, x + 8, ... (in block order), so the operands a
+// head's blocks share (its K/V tiles, or its query-side tiles) are read through one XCD's L2.
+// Plain head-major order when the head count is not a multiple of 8.
+__device__ __forceinline__ void sb_map(int nblk, int& bh, int& blk) {
+  const int L = blockIdx.x, BH = gridDim.x / nblk;
+  if (BH % kXCD == 0) {
+    const int x = L % kXCD, r = L / kXCD;
+    bh = x + kXCD * (r / nblk);
+    blk = r % nblk;
+  } else {
+    bh = L / nblk;
+    blk = L % nblk;
+  }
+}
+
 // ---- forward: one work-group per (head, 128-query block), wave w owns queries 32w..; the key
 // block's K^ rows and V^ transposed stream into a 2-slot LDS ring by DMA ----
 template <int D, bool CAUSAL, int OUT>
@@ -168,7 +184,8 @@ __global__ __launch_bounds__(256, 2) void sb_fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) int8_t sV[2][TV::BYTES];
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int bh = blockIdx.x / a.nqb, qi = blockIdx.x % a.nqb;
+  int bh, qi;
+  sb_map(a.nqb, bh, qi);
   const int qb = CAUSAL ? (a.nqb - 1 - qi) : qi;
   const int q0 = qb * kBQ, wq0 = q0 + 32 * w, qrow = wq0 + col;
   v4i qf[NKS];
@@ -514,7 +531,8 @@ __global__ __launch_bounds__(256, 2) void sb_dq_kernel(BwdArgs a) {
   __shared__ float xs[8];
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int bh = blockIdx.x / a.nqb, qi = blockIdx.x % a.nqb;
+  int bh, qi;
+  sb_map(a.nqb, bh, qi);
   const int qb = CAUSAL ? (a.nqb - 1 - qi) : qi;
   const int q0 = qb * kBQ, qrow = q0 + 32 * w + col;
   v4i qf[NKS];
@@ -658,7 +676,8 @@ __global__ __launch_bounds__(256, 2) void sb_dkv_kernel(BwdArgs a) {
   __shared__ float xs[8];
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int bh = blockIdx.x / a.nkt, j = blockIdx.x % a.nkt;
+  int bh, j;
+  sb_map(a.nkt, bh, j);
   const int key0 = j * kBK;
   sb_load_v<D>(a.V + (size_t)bh * a.M * D, a.M, key0, sVb, VS, tid);
   v4i kf[2][NKS];
