@@ -19,7 +19,8 @@
  *   - Q is [B][H][N][d], K and V are [B][H][M][d], out is [B][H][N][d]; all contiguous,
  *     row-major, 16-byte aligned device pointers on the current HIP device.  Inputs are bf16
  *     or fp16 (SAGE_IN_*); out is the input type, or FP32 with SAGE_OUT_FP32.
- *   - d is 64 or 128; B, H, N, M >= 1; B*H*max(N,M)*d < 2^40.
+ *   - d is 64 or 128; B, H, N, M >= 1; B*H*max(N,M)*d < 2^40; B*H <= 65535 and
+ *     B*H*ceil(max(N/128, M/64)) < 2^24 (the kernels' grid sizes); SAGE_ERR_INVALID_ARG otherwise.
  *   - causal: 0 no mask; 1 key t visible to query r iff t <= r (the first query aligned with
  *     the first key: the upper triangle of the N x M score matrix is masked, as the pages'
  *     reference code does; any N, M); 2 iff t <= r + M - N (the last query aligned with the

@@ -138,8 +138,11 @@ int make_problem(int B, int H, int Hkv, int N, int M, int d, int causal, float s
   p->qf8 = (variant & SAGE_QK_FP8) != 0;
   p->ql = {nullptr, N, 0};
   p->kl = {nullptr, M, 0};
-  // grid limits: y = B*H (or B*Hkv) for the preprocessing kernels, x = blocks/tiles
+  // grid limits: y = B*H (or B*Hkv) for the preprocessing kernels, x = blocks/tiles; the
+  // one-dimensional grids of the fused and SageBwd kernels (B*H times the query blocks or the
+  // key tiles, 256 work-items each) must count fewer than 2^32 work-items
   if (p->BH > 65535 || p->nkt > (1 << 30)) return SAGE_ERR_INVALID_ARG;
+  if ((long long)p->BH * (p->nqb > p->nkt ? p->nqb : p->nkt) >= (1LL << 24)) return SAGE_ERR_INVALID_ARG;
   return SAGE_OK;
 }
 

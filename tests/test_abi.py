@@ -78,6 +78,12 @@ def test_causal_modes_accept_uneven_lengths():
     for causal, N, M in [(1, 64, 200), (1, 200, 64), (2, 64, 200), (2, 200, 200)]:
         assert qa.sage_attn_workspace_bytes(1, 1, N, M, 64, causal, 0) > 0
     assert qa.sage_attn_workspace_bytes(1, 1, 200, 64, 64, 2, 0) == 0
+    # grid bounds: B*H <= 65535, and B*H times the query blocks / key tiles below 2^24
+    assert qa.sage_attn_workspace_bytes(1, 65536, 64, 64, 64, 0, 0) == 0
+    assert qa.sage_attn_workspace_bytes(1, 65535, 128, 64, 64, 0, 0) > 0
+    assert qa.sage_attn_workspace_bytes(1, 65535, 256 * 128, 256 * 64, 64, 0, 0) > 0
+    assert qa.sage_attn_workspace_bytes(1, 65535, 128, 257 * 64, 64, 0, 0) == 0
+    assert qa.sage_attn_workspace_bytes(1, 65535, 257 * 128, 64, 64, 0, 0) == 0
 
 
 def test_extended_shape_checks():
