@@ -254,11 +254,19 @@ __global__ __launch_bounds__(256, 2) void sb_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int T = 0; T < 2; T++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) {
-          const float x = (float)acc[T][r] * mul;
-          sc[T][r] = (!masked || 32 * T + 8 * (r >> 2) + (r & 3) <= lim) ? x : -INFINITY;
-          rm = fmaxf(rm, sc[T][r]);
-        }
+        for (int r = 0; r < 16; r++) sc[T][r] = (float)acc[T][r] * mul;
+      if (masked) {
+        asm volatile("" ::: "memory");  // keep this a real branch: interior blocks skip the test
+#pragma unroll
+        for (int T = 0; T < 2; T++)
+#pragma unroll
+          for (int r = 0; r < 16; r++)
+            sc[T][r] = (32 * T + 8 * (r >> 2) + (r & 3) <= lim) ? sc[T][r] : -INFINITY;
+      }
+#pragma unroll
+      for (int T = 0; T < 2; T++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) rm = fmaxf(rm, sc[T][r]);
       rm = pair_max(rm);  // the row's max over this tile
       const float m_new = fmaxf(m_run, rm);
       const float alpha = fast_exp2(m_run - m_new);
