@@ -490,6 +490,14 @@ __device__ __forceinline__ void sb_block_max(float pm, float dm, float* xs, int 
   dmax = fmaxf(fmaxf(xs[4], xs[5]), fmaxf(xs[6], xs[7]));
 }
 
+// The block maximum of |dS| alone (the dQ kernel quantizes only dS); same barrier and slots.
+__device__ __forceinline__ float sb_block_max_ds(float dm, float* xs, int lane, int w) {
+  dm = wave_max(dm);
+  if (lane == 0) xs[4 + w] = dm;
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // LDS only: tile DMAs stay in flight
+  return fmaxf(fmaxf(xs[4], xs[5]), fmaxf(xs[6], xs[7]));
+}
+
 // INT8 code of x against 127 / amax (inv = 0: the block is all zero), in the low byte of the
 // result: the clamped product plus 1.5 * 2^23 holds its round-half-even integer in the low
 // mantissa bits (no convert; a NaN product clamps to -127, as clamping after rounding does).
@@ -615,17 +623,15 @@ __global__ __launch_bounds__(256, 2) void sb_dq_kernel(BwdArgs a) {
     const bool masked = key0 + kBK > a.M || (CAUSAL && key0 + kBK - 1 > q0 + 32 * w + a.coff);
     sb_pair<D, FP16>(kf, qf, of, vfrag, sq * a.sk[(size_t)bh * a.nkt + j] * a.qk_scale, l2, dr, masked, lim, h, col, P,
                      dS);
-    float pm = 0.0f, dm = 0.0f;
+    float dm = 0.0f;
 #pragma unroll
     for (int T = 0; T < 2; T++)
 #pragma unroll
       for (int r = 0; r < 16; r++) {
-        pm = fmaxf(pm, P[T][r]);
         dm = fmaxf(dm, fabsf(dS[T][r]));
         rs += dS[T][r];
       }
-    float pmax, dmax;
-    sb_block_max(pm, dm, xs, lane, w, pmax, dmax);
+    const float dmax = sb_block_max_ds(dm, xs, lane, w);
     const float inv = dmax > 0.0f ? __fdiv_rn(127.0f, dmax) : 0.0f;
     const float sds = __fdiv_rn(dmax, 127.0f);
     v4i db[2];
