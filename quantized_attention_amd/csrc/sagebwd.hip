@@ -499,11 +499,12 @@ __device__ __forceinline__ float sb_block_max_ds(float dm, float* xs, int lane, 
 }
 
 // INT8 code of x against 127 / amax (inv = 0: the block is all zero), in the low byte of the
-// result: the clamped product plus 1.5 * 2^23 holds its round-half-even integer in the low
-// mantissa bits (no convert; a NaN product clamps to -127, as clamping after rounding does).
+// result: the product plus 1.5 * 2^23 holds its round-half-even integer in the low mantissa bits
+// (no convert).  Every caller quantizes a block against its own maximum, |x| <= amax, and
+// inv = rn(127 / amax), so |x * inv| <= 127 (1 + 2^-24)^2, which rounds to 127: the clamp to
+// [-127, 127] the codes are defined with never acts on finite values and is left out.
 __device__ __forceinline__ uint32_t sb_code8(float x, float inv) {
-  const float y = fminf(fmaxf(x * inv, -127.0f), 127.0f);
-  return __float_as_uint(y + 12582912.0f);
+  return __float_as_uint(fmaf(x, inv, 12582912.0f));
 }
 
 // The 16-bit rows of one 64-key V tile into LDS (rows >= M are 0).
