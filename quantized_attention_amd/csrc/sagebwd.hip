@@ -251,10 +251,13 @@ __global__ __launch_bounds__(256, 2) void sb_fwd_kernel(FwdArgs a) {
       float rm = -INFINITY;
       // boundary blocks only (keys past M, or after a query of the wave): the per-score test
       const bool masked = key0 + kBK > a.M || (CAUSAL && key0 + kBK - 1 > wq0 + a.coff);
+      // sc holds the exact integer scores (|acc| < 2^24); S = sc * mul.  As mul > 0 and rounding
+      // is monotonic, the row's max of the rounded products is the rounded product of its max,
+      // and the exponent takes S - base in one FMA.
 #pragma unroll
       for (int T = 0; T < 2; T++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) sc[T][r] = (float)acc[T][r] * mul;
+        for (int r = 0; r < 16; r++) sc[T][r] = (float)acc[T][r];
       if (masked) {
         asm volatile("" ::: "memory");  // keep this a real branch: interior blocks skip the test
 #pragma unroll
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(256, 2) void sb_fwd_kernel(FwdArgs a) {
       for (int T = 0; T < 2; T++)
 #pragma unroll
         for (int r = 0; r < 16; r++) rm = fmaxf(rm, sc[T][r]);
-      rm = pair_max(rm);  // the row's max over this tile
+      rm = pair_max(rm) * mul;  // the row's max of S over this tile
       const float m_new = fmaxf(m_run, rm);
       const float alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
@@ -282,7 +285,7 @@ __global__ __launch_bounds__(256, 2) void sb_fwd_kernel(FwdArgs a) {
           uint32_t t[4];
 #pragma unroll
           for (int k = 0; k < 4; k++) {
-            const float e = fast_exp2(sc[T][4 * q4 + k] - base);
+            const float e = fast_exp2(fmaf(sc[T][4 * q4 + k], mul, -base));
             esum += e;
             t[k] = __float_as_uint(e + 12582912.0f);  // e in [0, 127]: round half to even in the low byte
           }
