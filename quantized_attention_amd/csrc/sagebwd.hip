@@ -200,7 +200,13 @@ __global__ __launch_bounds__(256, 2) void sb_fwd_kernel(FwdArgs a) {
   for (int c = 0; c < NKS; c++)
 #pragma unroll
     for (int r = 0; r < 16; r++) O[c][r] = 0.0f;
-  float m_run = -FLT_MAX, l_run = 0.0f;
+  // O and l are held relative to exp2(m_ref), a reference for the row's running max: a block's
+  // contribution is scaled by exp2(rm - m_ref) / 127 instead of rescaling O whenever the max
+  // rises.  m_ref moves (and O, l are rescaled) only when a block's max exceeds it by more than
+  // kRefSlack, which keeps every scale below 2^kRefSlack / 127; a row's first visible block
+  // always moves it.  The quotient O / l and the log-sum-exp m_ref + log2 l do not depend on it.
+  constexpr float kRefSlack = 16.0f;
+  float m_ref = -FLT_MAX, l_run = 0.0f;
   const int jend = CAUSAL ? max(0, min(a.nkt, (q0 + kBQ + a.coff + kBK - 1) / kBK)) : a.nkt;
   int ko[TK::NPW], vo[TV::NPW];  // per-lane DMA source offsets inside a block
 #pragma unroll
@@ -271,9 +277,16 @@ __global__ __launch_bounds__(256, 2) void sb_fwd_kernel(FwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; r++) rm = fmaxf(rm, sc[T][r]);
       rm = pair_max(rm) * mul;  // the row's max of S over this tile
-      const float m_new = fmaxf(m_run, rm);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
+      if (__any(rm > m_ref + kRefSlack)) {  // some row of the wave moves its reference
+        const float m_new = rm > m_ref + kRefSlack ? rm : m_ref;
+        const float alpha = fast_exp2(m_ref - m_new);  // 1 for the rows that keep theirs
+        m_ref = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int c = 0; c < NKS; c++)
+#pragma unroll
+          for (int r = 0; r < 16; r++) O[c][r] *= alpha;
+      }
       // e = 127 P / (the row's block max of P) = 127 exp2(S - rm); P^ = rne(e)
       const float base = (rm == -INFINITY) ? 0.0f : rm - kLog2_127;
       float esum = 0.0f;
@@ -292,15 +305,10 @@ __global__ __launch_bounds__(256, 2) void sb_fwd_kernel(FwdArgs a) {
           pb[T][q4] = (int)sb_pack4(t[0], t[1], t[2], t[3]);
         }
       esum = pair_sum(esum);
-      const float sp = (rm == -INFINITY) ? 0.0f : fast_exp2(rm - m_new) * (1.0f / 127.0f);  // s_P
-      l_run = fmaf(l_run, alpha, esum * sp);
+      // s_P = exp2(rm - m) / 127 against the running max m, here against m_ref
+      const float sp = (rm == -INFINITY) ? 0.0f : fast_exp2(rm - m_ref) * (1.0f / 127.0f);
+      l_run = fmaf(esum, sp, l_run);
       const float osc = sp * a.sv[(size_t)bh * a.nkt + j];
-      if (__any(alpha != 1.0f)) {  // some row of the wave raised its max: rescale O first
-#pragma unroll
-        for (int c = 0; c < NKS; c++)
-#pragma unroll
-          for (int r = 0; r < 16; r++) O[c][r] *= alpha;
-      }
 #pragma unroll
       for (int c = 0; c < NKS; c++) {
         v16i R;
@@ -320,7 +328,7 @@ __global__ __launch_bounds__(256, 2) void sb_fwd_kernel(FwdArgs a) {
   }
   if (qrow >= a.N) return;
   const float inv = 1.0f / l_run;
-  if (h == 0) a.lse[(size_t)bh * a.N + qrow] = (m_run + __log2f(l_run)) * kLn2;
+  if (h == 0) a.lse[(size_t)bh * a.N + qrow] = (m_ref + __log2f(l_run)) * kLn2;
   const size_t orow = ((size_t)bh * a.N + qrow) * D;
 #pragma unroll
   for (int c = 0; c < NKS; c++)
