@@ -9,9 +9,11 @@ patterns (``uint16``) with a flag that says whether they are fp16 or bf16.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import subprocess
+import tempfile
 
 import numpy as np
 
@@ -21,6 +23,7 @@ SOURCES = [SRC, os.path.join(HERE, "sagebwd_oracle.c"), os.path.join(HERE, "sage
 LIB = os.path.join(HERE, "liboracle.so")
 
 BQ, BK = 128, 64
+_CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-fno-fast-math"]
 
 SMOOTH_V = 0x0001
 NO_SMOOTH_K = 0x0002
@@ -45,8 +48,7 @@ def build(force: bool = True) -> str:
     """Compile the oracle with gcc (plain C11, no fast-math, no FP contraction)."""
     if force or _stale():
         tmp = LIB + ".tmp"
-        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
-               "-fno-fast-math", *[f for f in SOURCES if f.endswith(".c")], "-o", tmp, "-lm"]
+        cmd = ["gcc", *_CFLAGS, *[f for f in SOURCES if f.endswith(".c")], "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, LIB)
     return LIB
@@ -55,56 +57,91 @@ def build(force: bool = True) -> str:
 _lib = None
 
 
+def _configure(L):
+    """Declare the argument and result types of the library's entry points."""
+    P = ctypes.c_void_p
+    i, u, dbl = ctypes.c_int, ctypes.c_uint, ctypes.c_double
+    L.orc_preprocess_head.argtypes = [P, P, P, i, i, i, i, u] + [P] * 10
+    L.orc_preprocess_head.restype = i
+    L.orc_preprocess_mx_head.argtypes = [P, P, P, i, i, i, i, u, P, P, P, P, P, P]
+    L.orc_preprocess_mx_head.restype = i
+    L.orc_forward_head.argtypes = [P, P, P, i, i, i, i, i, dbl, u, P, i, P]
+    L.orc_forward_head.restype = i
+    L.orc_forward_head_ties.argtypes = [P, P, P, i, i, i, i, i, dbl, u, P, i, P, dbl, P, P]
+    L.orc_forward_head_ties.restype = i
+    L.orc_exact_head.argtypes = [P, P, P, i, i, i, i, i, dbl, P, i, P]
+    L.orc_exact_head.restype = i
+    L.orc_exact_f64.argtypes = [P, P, P, i, i, i, i, dbl, P]
+    L.orc_exact_f64.restype = i
+    L.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+    L.orc_e4m3_decode.restype = dbl
+    L.orc_e4m3_encode.argtypes = [dbl]
+    L.orc_e4m3_encode.restype = ctypes.c_uint8
+    L.orc_e5m2_decode.argtypes = [ctypes.c_uint8]
+    L.orc_e5m2_decode.restype = dbl
+    L.orc_e5m2_encode.argtypes = [dbl]
+    L.orc_e5m2_encode.restype = ctypes.c_uint8
+    L.orc_e2m1_decode.argtypes = [ctypes.c_uint8]
+    L.orc_e2m1_decode.restype = dbl
+    L.orc_e2m1_encode.argtypes = [dbl]
+    L.orc_e2m1_encode.restype = ctypes.c_uint8
+    L.orc_e8m0_exponent.argtypes = [dbl]
+    L.orc_e8m0_exponent.restype = i
+    L.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
+    L.orc_bf16_to_f32.restype = ctypes.c_float
+    L.orc_fp16_to_f32.argtypes = [ctypes.c_uint16]
+    L.orc_fp16_to_f32.restype = ctypes.c_float
+    L.orc_k_group.argtypes = [i]
+    L.orc_k_group.restype = i
+    L.orc_sagebwd_forward.argtypes = [P, P, P, i, i, i, i, i, dbl, u, P, P]
+    L.orc_sagebwd_forward.restype = i
+    L.orc_sagebwd_backward.argtypes = [P, P, P, P, i, i, i, i, i, dbl, u, P, P, P, P, P]
+    L.orc_sagebwd_backward.restype = i
+    L.orc_sagebwd_quantize.argtypes = [P, P, P, P, i, i, i, i, u] + [P] * 9
+    L.orc_sagebwd_quantize.restype = i
+    L.orc_num_threads.argtypes = []
+    L.orc_num_threads.restype = i
+    return L
+
+
 def lib():
     global _lib
     if _lib is None:
         if _stale():
             build(force=True)
-        L = ctypes.CDLL(LIB)
-        P = ctypes.c_void_p
-        i, u, dbl = ctypes.c_int, ctypes.c_uint, ctypes.c_double
-        L.orc_preprocess_head.argtypes = [P, P, P, i, i, i, i, u] + [P] * 10
-        L.orc_preprocess_head.restype = i
-        L.orc_preprocess_mx_head.argtypes = [P, P, P, i, i, i, i, u, P, P, P, P, P, P]
-        L.orc_preprocess_mx_head.restype = i
-        L.orc_forward_head.argtypes = [P, P, P, i, i, i, i, i, dbl, u, P, i, P]
-        L.orc_forward_head.restype = i
-        L.orc_forward_head_ties.argtypes = [P, P, P, i, i, i, i, i, dbl, u, P, i, P, dbl, P, P]
-        L.orc_forward_head_ties.restype = i
-        L.orc_exact_head.argtypes = [P, P, P, i, i, i, i, i, dbl, P, i, P]
-        L.orc_exact_head.restype = i
-        L.orc_exact_f64.argtypes = [P, P, P, i, i, i, i, dbl, P]
-        L.orc_exact_f64.restype = i
-        L.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
-        L.orc_e4m3_decode.restype = dbl
-        L.orc_e4m3_encode.argtypes = [dbl]
-        L.orc_e4m3_encode.restype = ctypes.c_uint8
-        L.orc_e5m2_decode.argtypes = [ctypes.c_uint8]
-        L.orc_e5m2_decode.restype = dbl
-        L.orc_e5m2_encode.argtypes = [dbl]
-        L.orc_e5m2_encode.restype = ctypes.c_uint8
-        L.orc_e2m1_decode.argtypes = [ctypes.c_uint8]
-        L.orc_e2m1_decode.restype = dbl
-        L.orc_e2m1_encode.argtypes = [dbl]
-        L.orc_e2m1_encode.restype = ctypes.c_uint8
-        L.orc_e8m0_exponent.argtypes = [dbl]
-        L.orc_e8m0_exponent.restype = i
-        L.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
-        L.orc_bf16_to_f32.restype = ctypes.c_float
-        L.orc_fp16_to_f32.argtypes = [ctypes.c_uint16]
-        L.orc_fp16_to_f32.restype = ctypes.c_float
-        L.orc_k_group.argtypes = [i]
-        L.orc_k_group.restype = i
-        L.orc_sagebwd_forward.argtypes = [P, P, P, i, i, i, i, i, dbl, u, P, P]
-        L.orc_sagebwd_forward.restype = i
-        L.orc_sagebwd_backward.argtypes = [P, P, P, P, i, i, i, i, i, dbl, u, P, P, P, P, P]
-        L.orc_sagebwd_backward.restype = i
-        L.orc_sagebwd_quantize.argtypes = [P, P, P, P, i, i, i, i, u] + [P] * 9
-        L.orc_sagebwd_quantize.restype = i
-        L.orc_num_threads.argtypes = []
-        L.orc_num_threads.restype = i
-        _lib = L
+        _lib = _configure(ctypes.CDLL(LIB))
     return _lib
+
+
+@contextlib.contextmanager
+def planted_mistake(*edits):
+    """Temporarily replace the oracle by a copy compiled with deliberate mistakes, for tests
+    that show a pin catches them.  edits: (file name, text, replacement) triples; each text
+    must occur exactly once in that source file.  The mutant is built in a temporary
+    directory with the same compiler flags; the real library is restored on exit."""
+    global _lib
+    with tempfile.TemporaryDirectory() as tmp:
+        srcs = []
+        for f in SOURCES:
+            with open(f) as fh:
+                text = fh.read()
+            for name, old, new in edits:
+                if name == os.path.basename(f):
+                    if text.count(old) != 1:
+                        raise ValueError(f"planted_mistake: {old!r} occurs {text.count(old)} times in {name}")
+                    text = text.replace(old, new)
+            dst = os.path.join(tmp, os.path.basename(f))
+            with open(dst, "w") as fh:
+                fh.write(text)
+            srcs.append(dst)
+        so = os.path.join(tmp, "liboracle_mutant.so")
+        subprocess.run(["gcc", *_CFLAGS, *[f for f in srcs if f.endswith(".c")], "-o", so, "-lm"], check=True)
+        saved = lib()
+        _lib = _configure(ctypes.CDLL(so))
+        try:
+            yield
+        finally:
+            _lib = saved
 
 
 def _ptr(a):

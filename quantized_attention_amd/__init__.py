@@ -315,36 +315,43 @@ def sage_attn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max
 
 
 # ---------------------------------------------------------------- SageBwd (training)
-def _train_shape(q, k, causal, sm_scale, out_fp32, smooth_k):
+def _train_shape(q, k, v, causal, sm_scale, out_fp32, smooth_k):
+    """The SageBwd shape of q [B, H, N, d] and k, v [B, Hkv, M, d]; shapes are checked here so
+    that no mismatched buffer reaches the kernels (the library itself rejects Hkv != H)."""
     import torch
-    if q.dim() != 4 or k.dim() != 4:
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [B, H, T, d]")
     B, H, N, d = q.shape
-    M = k.shape[2]
+    Hkv, M = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, M, d) or tuple(v.shape) != (B, Hkv, M, d):
+        raise ValueError("k and v must be [B, H, M, d] matching q")
+    if Hkv != H:
+        raise ValueError("SageBwd needs as many key/value heads as query heads (grouped heads are not served)")
     var = (SAGE_IN_FP16 if q.dtype == torch.float16 else SAGE_IN_BF16) | (SAGE_OUT_FP32 if out_fp32 else 0)
     if not smooth_k:
         var |= SAGE_TRAIN_NO_SMOOTH_K
     scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(d)
-    return SageAttnShape(B, H, H, N, M, d, int(causal), scale, var)
+    return SageAttnShape(B, H, Hkv, N, M, d, int(causal), scale, var)
 
 
 def _check_train_inputs(*ts):
     import torch
     for t in ts:
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("tensors must be contiguous device tensors")
         if t.dtype not in (torch.bfloat16, torch.float16):
             raise TypeError("q, k, v, dout must be bf16 or fp16")
     if len({t.dtype for t in ts}) != 1:
         raise TypeError("q, k, v, dout must share a dtype")
+    for t in ts:
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous device tensors")
 
 
 def sage_attn_train_forward(q, k, v, causal: int = 0, sm_scale: float | None = None, out_fp32: bool = False,
                             smooth_k: bool = True):
     """SageBwd forward: (out [B, H, N, d], lse [B, H, N] FP32) for q [B, H, N, d], k/v [B, H, M, d]."""
     import torch
+    shape = _train_shape(q, k, v, causal, sm_scale, out_fp32, smooth_k)
     _check_train_inputs(q, k, v)
-    shape = _train_shape(q, k, causal, sm_scale, out_fp32, smooth_k)
     B, H, N, d = q.shape
     out = torch.empty((B, H, N, d), dtype=torch.float32 if out_fp32 else q.dtype, device=q.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
@@ -360,8 +367,18 @@ def sage_attn_train_backward(q, k, v, out, dout, lse, causal: int = 0, sm_scale:
                              smooth_k: bool = True):
     """SageBwd backward: (dq, dk, dv) in FP32, from the forward's out (its dtype) and lse."""
     import torch
+    shape = _train_shape(q, k, v, causal, sm_scale, out.dtype == torch.float32, smooth_k)
+    B, H, N, d = q.shape
+    if tuple(dout.shape) != (B, H, N, d) or tuple(out.shape) != (B, H, N, d):
+        raise ValueError("out and dout must be [B, H, N, d] like q")
+    if out.dtype not in (q.dtype, torch.float32):
+        raise TypeError("out must have q's dtype or float32 (the forward's output)")
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N):
+        raise ValueError("lse must be float32 [B, H, N]")
     _check_train_inputs(q, k, v, dout)
-    shape = _train_shape(q, k, causal, sm_scale, out.dtype == torch.float32, smooth_k)
+    for t in (out, lse):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous device tensors")
     dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
     dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)

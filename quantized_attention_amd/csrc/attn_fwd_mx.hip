@@ -110,6 +110,7 @@ __device__ __forceinline__ void qk_tile_mx(const uint8_t* __restrict__ sK, const
 }
 
 constexpr float kLog2_6 = 2.5849625007211562f;  // log2(6)
+constexpr float kP2Span = 64.0f;  // two-level P: level-one reference at most this far (log2) below the max
 
 template <int D, bool CAUSAL, bool ACC_VALU, bool P2L>
 __device__ __forceinline__ void softmax_pv_mx(const v16f (&acc)[2], const uint8_t* __restrict__ sV,
@@ -152,15 +153,19 @@ __device__ __forceinline__ void softmax_pv_mx(const v16f (&acc)[2], const uint8_
   uint32_t pc0, pc1;
   if constexpr (P2L) {
     // Level one: the row's largest P~ of this tile maps to 6.  A row with no visible key in the
-    // tile keeps its base (its P2 are 0 and O stays as it is).
+    // tile keeps its base (its P2 are 0 and O stays as it is).  The reference of level one is
+    // kept within kP2Span octaves of the running maximum: a tile whose maximum lies further
+    // below contributes less than 2^-kP2Span of the row's sum (invisible in FP32), and the
+    // rescale exp2(b_old - b_new) of O stays below 2^kP2Span, so O never leaves the FP32 range.
     const bool vis = m_tile > -INFINITY;
-    base = vis ? m_tile - kLog2_6 : b_run;
+    const float bref = fmaxf(m_tile, m_new - kP2Span);
+    base = vis ? bref - kLog2_6 : b_run;
     resc = fast_exp2(b_run - base);
     b_run = base;
-    // E8M0 of each P2 block: from its largest value 6 exp2(block max - row max), which is
-    // exactly 6 for the block holding the row maximum
-    pc0 = vis ? e8m0_code(6.0f * fast_exp2(mb[0] - m_tile)) : 0u;
-    pc1 = vis ? e8m0_code(6.0f * fast_exp2(mb[1] - m_tile)) : 0u;
+    // E8M0 of each P2 block: from its largest value 6 exp2(block max - bref), which is exactly 6
+    // for the block holding the row maximum of the tile (bref = m_tile unless clamped)
+    pc0 = vis ? e8m0_code(6.0f * fast_exp2(mb[0] - bref)) : 0u;
+    pc1 = vis ? e8m0_code(6.0f * fast_exp2(mb[1] - bref)) : 0u;
   } else {
     base = m_new;
     // E8M0 of each P block: from its largest P~ (0 for a fully masked block: code 0)

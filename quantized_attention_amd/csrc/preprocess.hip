@@ -50,24 +50,44 @@ __device__ __forceinline__ void widen8(const v4i& raw, bool fp16, float (&x)[8])
 // ---- K and V chunk statistics.  A wave takes one 64-token chunk of K or of V; lane l owns
 // channels D/64 l .. +D/64-1 and loads the chunk's rows straight into registers, all 64
 // loads in flight (one wave load reads a row's 128 or 256 contiguous bytes), then adds them in
-// token order (FP64); for V also the max / min, and the sum when smoothing ----
+// token order (FP64); for V also the max / min (one float2 per channel), and the sum when
+// smoothing.  Work-group u2 of key/value head bh: waves 0, 1 take chunk 2 u2 (K, V), waves
+// 2, 3 chunk 2 u2 + 1 ----
+struct StatsArgs {
+  const uint16_t* Q;
+  const uint16_t* K;
+  const uint16_t* V;
+  // Q side (q_prep)
+  int8_t* qhat;
+  float* dq;
+  uint8_t* qsc;
+  float* qmean;
+  uint16_t* qm_hi;
+  uint16_t* qm_lo;
+  // K / V side
+  double* kpart;
+  double* vpart;
+  float2* vmm;
+  SeqLayout ql, kl;
+  int H, Hkv, Np, nqb, nkt;
+  int nq_blocks;  // work-groups of the Q side (0: statistics only), placed first in the grid
+  int nkv_x;      // work-groups of the K / V side per key/value head
+  bool fp16, smooth_v;
+};
+
 template <int D>
-__global__ __launch_bounds__(256) void kv_stats_kernel(const uint16_t* __restrict__ K,
-                                                       const uint16_t* __restrict__ V,
-                                                       double* __restrict__ kpart, double* __restrict__ vpart,
-                                                       float* __restrict__ vmaxp, float* __restrict__ vminp,
-                                                       SeqLayout kl, int Hkv, int nkt, bool fp16, bool smooth_v) {
+__device__ __forceinline__ void kv_stats_block(const StatsArgs& a, int u2, int bh) {
   constexpr int CPL = D / 64;  // channels per lane
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int u = 2 * blockIdx.x + (w >> 1), bh = blockIdx.y;  // waves 0, 1: chunk 2x; 2, 3: 2x + 1
+  const int u = 2 * u2 + (w >> 1);
   const bool isv = (w & 1) != 0;
-  if (u >= nkt) return;
-  const SeqRows R = seq_rows(kl, bh / Hkv, bh % Hkv, Hkv, D);
+  if (u >= a.nkt) return;
+  const SeqRows R = seq_rows(a.kl, bh / a.Hkv, bh % a.Hkv, a.Hkv, D);
   const int t0 = u * kBK;
   if (t0 >= R.len) return;  // past this sequence's keys: no chunk
   const int n = min(kBK, R.len - t0);
-  const uint16_t* src = (isv ? V : K) + R.base + (size_t)t0 * R.stride + CPL * lane;
+  const uint16_t* src = (isv ? a.V : a.K) + R.base + (size_t)t0 * R.stride + CPL * lane;
   uint32_t raw[kBK];  // row t (clamped to the chunk's last valid row), this lane's channels
 #pragma unroll
   for (int t = 0; t < kBK; t++) {
@@ -76,15 +96,15 @@ __global__ __launch_bounds__(256) void kv_stats_kernel(const uint16_t* __restric
   }
   auto val = [&](int t, int j) {
     const uint32_t hbits = CPL == 2 ? (j ? raw[t] >> 16 : raw[t] & 0xffffu) : raw[t];
-    return fp16 ? static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(hbits)))
-                : __uint_as_float(hbits << 16);
+    return a.fp16 ? static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(hbits)))
+                  : __uint_as_float(hbits << 16);
   };
-  const size_t o = ((size_t)bh * nkt + u) * D + CPL * lane;
-  double s[CPL];
+  const size_t o = ((size_t)bh * a.nkt + u) * D + CPL * lane;
+  double sm[CPL];
   float mx[CPL], mn[CPL];
 #pragma unroll
   for (int j = 0; j < CPL; j++) {
-    s[j] = 0.0;
+    sm[j] = 0.0;
     mx[j] = -INFINITY;
     mn[j] = INFINITY;
   }
@@ -93,9 +113,9 @@ __global__ __launch_bounds__(256) void kv_stats_kernel(const uint16_t* __restric
     for (int t = 0; t < kBK; t++)
       if (t < n)
 #pragma unroll
-        for (int j = 0; j < CPL; j++) s[j] += (double)val(t, j);
+        for (int j = 0; j < CPL; j++) sm[j] += (double)val(t, j);
 #pragma unroll
-    for (int j = 0; j < CPL; j++) kpart[o + j] = s[j];
+    for (int j = 0; j < CPL; j++) a.kpart[o + j] = sm[j];
   } else {
 #pragma unroll
     for (int t = 0; t < kBK; t++)
@@ -103,29 +123,28 @@ __global__ __launch_bounds__(256) void kv_stats_kernel(const uint16_t* __restric
 #pragma unroll
         for (int j = 0; j < CPL; j++) {
           const float x = val(t, j);
-          if (smooth_v) s[j] += (double)x;
+          if (a.smooth_v) sm[j] += (double)x;
           mx[j] = x > mx[j] ? x : mx[j];  // NaN ignored
           mn[j] = x < mn[j] ? x : mn[j];
         }
 #pragma unroll
     for (int j = 0; j < CPL; j++) {
-      if (smooth_v) vpart[o + j] = s[j];
-      vmaxp[o + j] = mx[j];
-      vminp[o + j] = mn[j];
+      if (a.smooth_v) a.vpart[o + j] = sm[j];
+      a.vmm[o + j] = make_float2(mx[j], mn[j]);
     }
   }
 }
 
-// ---- chunk statistics -> k mean, V_m (when smoothing) and the V scale ----
-// One work-group per (head, 8 channels).  The partials of 64 chunks at a time are staged in
-// LDS by all 256 threads at once (the loads overlap instead of forming a chain of round
-// trips); then one thread per channel adds them in chunk order, as the pinned order requires:
-// thread c < 8 the K sums, thread 64 + c the V max / min (and sums).
+// ---- chunk statistics -> K mean, V_m (when smoothing) and the V scale ----
+// One work-group per (key/value head, 16 channels).  The partials of kFinStage chunks at a time
+// are staged in LDS by all 256 threads at once, double-buffered: the loads of the next round are
+// in flight while one thread per channel adds the current round in chunk order, as the pinned
+// order requires (threads c < 16 the K sums, threads 64 + c the V max / min and sums).  Each
+// chunk row of 16 channels is one 128-byte line of every partial array.
 struct FinArgs {
   const double* kpart;
   const double* vpart;
-  const float* vmaxp;
-  const float* vminp;
+  const float2* vmm;
   float* kmean;
   float* vmean;
   float* dv;
@@ -133,38 +152,60 @@ struct FinArgs {
   int Hkv, d, nkt;
   bool smooth_v;
 };
-constexpr int kFinCh = 8;                                       // channels per work-group
-constexpr int kFinStage = 64;                                   // chunks staged per round
-constexpr int kFinLds = kFinStage * kFinCh * (8 + 8 + 4 + 4);   // LDS bytes (12 KiB)
-__device__ __forceinline__ void kv_finalize_part(const FinArgs& f, int bh, int c0, int tid,
-                                                 unsigned char* __restrict__ lds) {
-  double* sk = reinterpret_cast<double*>(lds);  // [kFinStage][kFinCh] each
-  double* svs = sk + kFinStage * kFinCh;
-  float* smx = reinterpret_cast<float*>(svs + kFinStage * kFinCh);
-  float* smn = smx + kFinStage * kFinCh;
+constexpr int kFinCh = 16;     // channels per work-group
+constexpr int kFinStage = 128;  // chunks staged per round
+constexpr int kFinRound = kFinStage * kFinCh;  // elements of one array per round
+constexpr int kFinPieces = kFinRound / 512;    // 16-byte pieces of one array per thread and round
+
+__global__ __launch_bounds__(256) void kv_finalize_kernel(FinArgs f) {
+  __shared__ __attribute__((aligned(16))) double sk[2][kFinRound];
+  __shared__ __attribute__((aligned(16))) double svs[2][kFinRound];
+  __shared__ __attribute__((aligned(16))) float2 smm[2][kFinRound];
+  const int tid = threadIdx.x;
+  const int per = f.d / kFinCh;
+  const int bh = blockIdx.x / per, c0 = kFinCh * (blockIdx.x % per);
   const int M = seq_rows(f.kl, bh / f.Hkv, bh % f.Hkv, f.Hkv, f.d).len;  // this sequence's keys
   const int nk = (M + kBK - 1) / kBK;                                    // its chunks
+  const int nr = (nk + kFinStage - 1) / kFinStage;                       // rounds
+  // each thread moves kFinPieces 16-byte pieces (2 doubles or 2 float2) of every array per round;
+  // piece e of thread tid is element x = 2 (tid + 256 e) of the round: chunk x / 16, channel x % 16
+  typedef double d2 __attribute__((ext_vector_type(2)));
+  d2 rk[kFinPieces], rv[kFinPieces];
+  v4i rm[kFinPieces];
+#define SAGE_FIN_LOAD(r)                                                                      \
+  _Pragma("unroll") for (int e = 0; e < kFinPieces; e++) {                                   \
+    const int x = 2 * (tid + 256 * e);                                                        \
+    const int uu = min((r) * kFinStage + x / kFinCh, nk - 1);                                 \
+    const size_t o = ((size_t)bh * f.nkt + uu) * f.d + c0 + x % kFinCh;                       \
+    rk[e] = *reinterpret_cast<const d2*>(f.kpart + o);                                        \
+    if (f.smooth_v) rv[e] = *reinterpret_cast<const d2*>(f.vpart + o);                        \
+    rm[e] = *reinterpret_cast<const v4i*>(f.vmm + o);                                         \
+  }
+#define SAGE_FIN_STORE(buf)                                                                   \
+  _Pragma("unroll") for (int e = 0; e < kFinPieces; e++) {                                   \
+    const int x = 2 * (tid + 256 * e);                                                        \
+    *reinterpret_cast<d2*>(&sk[buf][x]) = rk[e];                                              \
+    if (f.smooth_v) *reinterpret_cast<d2*>(&svs[buf][x]) = rv[e];                             \
+    *reinterpret_cast<v4i*>(&smm[buf][x]) = rm[e];                                            \
+  }
   double ks = 0.0, vs = 0.0;
   float mx = -INFINITY, mn = INFINITY;
-  for (int u0 = 0; u0 < nk; u0 += kFinStage) {
-    const int ns = min(kFinStage, nk - u0);
-    __syncthreads();  // the previous round's LDS reads are done
-    for (int x = tid; x < kFinStage * kFinCh; x += 256) {
-      const int uu = x / kFinCh, cc = x % kFinCh;
-      if (uu < ns) {
-        const size_t o = ((size_t)bh * f.nkt + u0 + uu) * f.d + c0 + cc;
-        sk[x] = f.kpart[o];
-        if (f.smooth_v) svs[x] = f.vpart[o];
-        smx[x] = f.vmaxp[o];
-        smn[x] = f.vminp[o];
-      }
+  if (nk > 0) {
+    SAGE_FIN_LOAD(0)
+    SAGE_FIN_STORE(0)
+  }
+  __syncthreads();
+  for (int r = 0; r < nr; r++) {
+    const int buf = r & 1;
+    if (r + 1 < nr) {  // in flight during this round's sums
+      SAGE_FIN_LOAD(r + 1)
     }
-    __syncthreads();
+    const int ns = min(kFinStage, nk - r * kFinStage);
     if (tid < kFinCh) {
       for (int ub = 0; ub < ns; ub += 8) {  // 8 LDS reads in flight, adds in chunk order
         double x[8];
 #pragma unroll
-        for (int e = 0; e < 8; e++) x[e] = sk[min(ub + e, kFinStage - 1) * kFinCh + tid];
+        for (int e = 0; e < 8; e++) x[e] = sk[buf][min(ub + e, kFinStage - 1) * kFinCh + tid];
 #pragma unroll
         for (int e = 0; e < 8; e++)
           if (ub + e < ns) ks += x[e];
@@ -173,25 +214,30 @@ __device__ __forceinline__ void kv_finalize_part(const FinArgs& f, int bh, int c
       const int cc = tid - 64;
       for (int ub = 0; ub < ns; ub += 8) {
         double x[8];
-        float hx[8], lx[8];
+        float2 m[8];
 #pragma unroll
         for (int e = 0; e < 8; e++) {
           const int uu = min(ub + e, kFinStage - 1) * kFinCh + cc;
-          x[e] = f.smooth_v ? svs[uu] : 0.0;
-          hx[e] = smx[uu];
-          lx[e] = smn[uu];
+          x[e] = f.smooth_v ? svs[buf][uu] : 0.0;
+          m[e] = smm[buf][uu];
         }
 #pragma unroll
         for (int e = 0; e < 8; e++) {
           if (ub + e < ns) {
             if (f.smooth_v) vs += x[e];
-            mx = hx[e] > mx ? hx[e] : mx;  // NaN ignored
-            mn = lx[e] < mn ? lx[e] : mn;
+            mx = m[e].x > mx ? m[e].x : mx;  // NaN ignored
+            mn = m[e].y < mn ? m[e].y : mn;
           }
         }
       }
     }
+    if (r + 1 < nr) {  // the other buffer was last read in round r - 1
+      SAGE_FIN_STORE(buf ^ 1)
+    }
+    __syncthreads();
   }
+#undef SAGE_FIN_LOAD
+#undef SAGE_FIN_STORE
   // a sequence without keys (variable-length batches only) gets zero means and the floor scale
   if (tid < kFinCh) {
     f.kmean[(size_t)bh * f.d + c0 + tid] = M > 0 ? (float)(ks / (double)M) : 0.0f;
@@ -206,28 +252,22 @@ __device__ __forceinline__ void kv_finalize_part(const FinArgs& f, int bh, int c
   }
 }
 
-// work-group x: head x / (d / 8), channels 8 (x % (d / 8)) ..
-__global__ __launch_bounds__(256) void kv_finalize_kernel(FinArgs f) {
-  __shared__ __attribute__((aligned(16))) unsigned char lds[kFinLds];
-  const int per = f.d / kFinCh;
-  kv_finalize_part(f, blockIdx.x / per, kFinCh * (blockIdx.x % per), threadIdx.x, lds);
-}
-
-// ---- Q: block mean (and its bf16 head/tail), gamma(Q), per-token scale, INT8 (F8: E4M3) codes ----
+// ---- Q: block mean (and its bf16 head/tail), gamma(Q), per-token scale, INT8 (F8: E4M3) codes;
+// query block i of query head bh ----
 template <int D, bool MX, bool F8>
-__global__ __launch_bounds__(256) void q_prep_kernel(const uint16_t* __restrict__ Q,
-                                                     int8_t* __restrict__ qhat, float* __restrict__ dq,
-                                                     uint8_t* __restrict__ qsc,
-                                                     float* __restrict__ qmean, uint16_t* __restrict__ qm_hi,
-                                                     uint16_t* __restrict__ qm_lo, SeqLayout ql, int H, int Np,
-                                                     int nqb, bool fp16) {
+__device__ __forceinline__ void q_prep_block(const StatsArgs& a, int i, int bh) {
+  const uint16_t* __restrict__ Q = a.Q;
+  int8_t* __restrict__ qhat = a.qhat;
+  float* __restrict__ dq = a.dq;
+  uint8_t* __restrict__ qsc = a.qsc;
+  const int H = a.H, Np = a.Np, nqb = a.nqb;
+  const bool fp16 = a.fp16;
   constexpr int RS = D + 8;
   __shared__ __attribute__((aligned(16))) uint16_t sq[kBQ * RS];
   __shared__ float sm[D];
   const int tid = threadIdx.x;
-  const int i = blockIdx.x, bh = blockIdx.y;
   const int lane = tid & 63, wave = tid >> 6;
-  const SeqRows R = seq_rows(ql, bh / H, bh % H, H, D);
+  const SeqRows R = seq_rows(a.ql, bh / H, bh % H, H, D);
   const int r0 = i * kBQ;
   if (r0 >= R.len) return;  // past this sequence's queries: the block is never read
   const int n = min(kBQ, R.len - r0);
@@ -262,14 +302,14 @@ __global__ __launch_bounds__(256) void q_prep_kernel(const uint16_t* __restrict_
     const float m = (float)(s / (double)n);
     sm[tid] = m;
     const size_t o = ((size_t)bh * nqb + i) * D + tid;
-    qmean[o] = m;
+    a.qmean[o] = m;
     const uint16_t hb = bf16_rn(m);
     // head / tail in the Delta S MFMA's B-operand order: per group of 32 blocks, channel step
     // s = c / 16, lane 32 ((c % 16) / 8) + block % 32, 8 bf16 per lane
     const size_t sw = ((((size_t)bh * ((nqb + 31) / 32) + i / 32) * (D / 16) + tid / 16) * 64 +
                        32 * ((tid % 16) / 8) + i % 32) * 8 + tid % 8;
-    qm_hi[sw] = hb;
-    qm_lo[sw] = bf16_rn(m - bf16_val(hb));
+    a.qm_hi[sw] = hb;
+    a.qm_lo[sw] = bf16_rn(m - bf16_val(hb));
   }
   __syncthreads();
   // Each wave takes 32 rows.  A row is spread over LPR = D/8 lanes holding 8 consecutive
@@ -316,6 +356,20 @@ __global__ __launch_bounds__(256) void q_prep_kernel(const uint16_t* __restrict_
       if (r < n) w = F8 ? e4m3_pack8_rcp(g, sc, __fdiv_rn(1.0f, sc)) : int8_pack8_rcp(g, sc, __fdiv_rn(1.0f, sc));
       *reinterpret_cast<uint2*>(qhat + row * D + c0) = w;
     }
+  }
+}
+
+// ---- the first preprocessing launch: the Q blocks (work-groups [0, nq_blocks)) and the K / V
+// chunk statistics (the rest) side by side.  Neither needs the other, and both are bound by
+// HBM reads, so one grid keeps the memory system busy with both ----
+template <int D, bool MX, bool F8>
+__global__ __launch_bounds__(256) void stats_kernel(StatsArgs a) {
+  const int x = blockIdx.x;
+  if (x < a.nq_blocks) {
+    q_prep_block<D, MX, F8>(a, x % a.nqb, x / a.nqb);
+  } else {
+    const int y = x - a.nq_blocks;
+    kv_stats_block<D>(a, y % a.nkv_x, y / a.nkv_x);
   }
 }
 
@@ -611,42 +665,39 @@ __global__ __launch_bounds__(256, MX ? 3 : 4) void kv_quant_kernel(KVArgs a) {
 
 }  // namespace
 
-hipError_t launch_kv_stats(const Problem& p, const void* k, const void* v, const Workspace& w, hipStream_t s) {
-  const dim3 grid((p.nkt + 1) / 2, p.BHkv);
+hipError_t launch_stats(const Problem& p, const void* q, const void* k, const void* v, const Workspace& w,
+                        hipStream_t s) {
+  StatsArgs a;
+  a.Q = (const uint16_t*)q;
+  a.K = (const uint16_t*)k;
+  a.V = (const uint16_t*)v;
+  a.qhat = w.qhat; a.dq = w.dq; a.qsc = w.qsc; a.qmean = w.qmean; a.qm_hi = w.qm_hi; a.qm_lo = w.qm_lo;
+  a.kpart = w.kpart; a.vpart = w.vpart; a.vmm = w.vmm;
+  a.ql = p.ql; a.kl = p.kl;
+  a.H = p.H; a.Hkv = p.Hkv; a.Np = p.Np; a.nqb = p.nqb; a.nkt = p.nkt;
+  a.nq_blocks = q ? p.nqb * p.BH : 0;
+  a.nkv_x = (p.nkt + 1) / 2;
+  a.fp16 = p.fp16;
+  a.smooth_v = p.smooth_v;
+  const long long blocks = (long long)a.nq_blocks + (long long)a.nkv_x * p.BHkv;
+  if (blocks >= (1LL << 31)) return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)blocks);
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, a); };
   if (p.d == 128)
-    hipLaunchKernelGGL(kv_stats_kernel<128>, grid, dim3(256), 0, s, (const uint16_t*)k, (const uint16_t*)v,
-                       w.kpart, w.vpart, w.vmaxp, w.vminp, p.kl, p.Hkv, p.nkt, p.fp16, p.smooth_v);
+    p.mx ? go(stats_kernel<128, true, false>)
+         : (p.qf8 ? go(stats_kernel<128, false, true>) : go(stats_kernel<128, false, false>));
   else
-    hipLaunchKernelGGL(kv_stats_kernel<64>, grid, dim3(256), 0, s, (const uint16_t*)k, (const uint16_t*)v,
-                       w.kpart, w.vpart, w.vmaxp, w.vminp, p.kl, p.Hkv, p.nkt, p.fp16, p.smooth_v);
+    p.mx ? go(stats_kernel<64, true, false>)
+         : (p.qf8 ? go(stats_kernel<64, false, true>) : go(stats_kernel<64, false, false>));
   return hipGetLastError();
-}
-
-FinArgs fin_args(const Problem& p, const Workspace& w) {
-  FinArgs f;
-  f.kpart = w.kpart; f.vpart = w.vpart; f.vmaxp = w.vmaxp; f.vminp = w.vminp;
-  f.kmean = w.kmean; f.vmean = w.vmean; f.dv = w.dv;
-  f.kl = p.kl; f.Hkv = p.Hkv; f.d = p.d; f.nkt = p.nkt; f.smooth_v = p.smooth_v;
-  return f;
 }
 
 hipError_t launch_kv_finalize(const Problem& p, const Workspace& w, hipStream_t s) {
-  hipLaunchKernelGGL(kv_finalize_kernel, dim3(p.BHkv * (p.d / kFinCh)), dim3(256), 0, s, fin_args(p, w));
-  return hipGetLastError();
-}
-
-hipError_t launch_q_prep(const Problem& p, const void* q, const Workspace& w, hipStream_t s) {
-  const dim3 grid(p.nqb, p.BH);
-  auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, (const uint16_t*)q, w.qhat, w.dq, w.qsc, w.qmean, w.qm_hi,
-                       w.qm_lo, p.ql, p.H, p.Np, p.nqb, p.fp16);
-  };
-  if (p.d == 128)
-    p.mx ? go(q_prep_kernel<128, true, false>)
-         : (p.qf8 ? go(q_prep_kernel<128, false, true>) : go(q_prep_kernel<128, false, false>));
-  else
-    p.mx ? go(q_prep_kernel<64, true, false>)
-         : (p.qf8 ? go(q_prep_kernel<64, false, true>) : go(q_prep_kernel<64, false, false>));
+  FinArgs f;
+  f.kpart = w.kpart; f.vpart = w.vpart; f.vmm = w.vmm;
+  f.kmean = w.kmean; f.vmean = w.vmean; f.dv = w.dv;
+  f.kl = p.kl; f.Hkv = p.Hkv; f.d = p.d; f.nkt = p.nkt; f.smooth_v = p.smooth_v;
+  hipLaunchKernelGGL(kv_finalize_kernel, dim3(p.BHkv * (p.d / kFinCh)), dim3(256), 0, s, f);
   return hipGetLastError();
 }
 

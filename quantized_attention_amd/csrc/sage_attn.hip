@@ -34,8 +34,8 @@ size_t workspace_layout(const Problem& p, size_t* sizes) {
   s[9] = BH * p.nqb * (size_t)p.Mp * sizeof(float);  // ds
   s[10] = BK * p.nkt * d * sizeof(double);           // kpart
   s[11] = BK * p.nkt * d * sizeof(double);           // vpart
-  s[12] = BK * p.nkt * d * sizeof(float);            // vmaxp
-  s[13] = BK * p.nkt * d * sizeof(float);            // vminp
+  s[12] = BK * p.nkt * d * sizeof(float2);           // vmm
+  s[13] = 0;                                         // (unused)
   const size_t nqb32 = (size_t)(p.nqb + 31) / 32 * 32;  // q-mean head/tail: groups of 32 blocks
   s[14] = BH * nqb32 * d * sizeof(uint16_t);         // qm_hi
   s[15] = BH * nqb32 * d * sizeof(uint16_t);         // qm_lo
@@ -71,8 +71,7 @@ void carve_workspace(const Problem& p, void* base, Workspace* w) {
   w->ds = (float*)ptr[9];
   w->kpart = (double*)ptr[10];
   w->vpart = (double*)ptr[11];
-  w->vmaxp = (float*)ptr[12];
-  w->vminp = (float*)ptr[13];
+  w->vmm = (float2*)ptr[12];
   w->qm_hi = (uint16_t*)ptr[14];
   w->qm_lo = (uint16_t*)ptr[15];
   w->qsc = (uint8_t*)ptr[16];
@@ -174,48 +173,14 @@ int make_problem(const sage_attn_varlen_shape* sh, Problem* p) {
 
 bool aligned16(const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) == 0; }
 
-// A second stream with its fork / join events, per host thread and device, for work that does
-// not depend on the caller's K / V work (the Q blocks beside the K / V statistics).  Created on
-// first use with the device current, default priority, held until the process ends; per thread,
-// so that calls from several host threads never share one.
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool failed = false;
-};
-thread_local SideStream t_side[64];
-
-SideStream* side_stream() {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-  SideStream& x = t_side[dev];
-  if (x.failed) return nullptr;
-  if (!x.s) {
-    if (hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&x.join, hipEventDisableTiming) != hipSuccess) {
-      (void)hipGetLastError();
-      x.failed = true;  // the preprocessing then runs in order on the caller's stream
-      return nullptr;
-    }
-  }
-  return &x;
-}
-
-// The preprocessing launches; ds goes to ds_out scaled by ds_scale.  The Q blocks (q_prep) run
-// on the side stream, forked from and joined back into s, while s computes the K / V statistics:
-// the two HBM-bound passes and the statistics' reduction chains overlap.  kv_quant needs both.
+// The preprocessing launches, in order on s; ds goes to ds_out scaled by ds_scale.  The first
+// launch covers the Q blocks and the K / V chunk statistics together (both HBM-bound, neither
+// needs the other); the chunk statistics are then reduced to the K mean, V_m and the V scale,
+// which kv_quant needs.
 int run_preprocess(const Problem& p, const void* q, const void* k, const void* v, const Workspace& w,
                    float ds_scale, float* ds_out, hipStream_t s) {
-  SideStream* side = side_stream();
-  hipStream_t sq = side ? side->s : s;
-  if (side && (hipEventRecord(side->fork, s) != hipSuccess || hipStreamWaitEvent(sq, side->fork, 0) != hipSuccess))
-    return SAGE_ERR_LAUNCH;
-  if (launch_q_prep(p, q, w, sq) != hipSuccess) return SAGE_ERR_LAUNCH;
-  if (side && hipEventRecord(side->join, sq) != hipSuccess) return SAGE_ERR_LAUNCH;
-  if (launch_kv_stats(p, k, v, w, s) != hipSuccess) return SAGE_ERR_LAUNCH;
+  if (launch_stats(p, q, k, v, w, s) != hipSuccess) return SAGE_ERR_LAUNCH;
   if (launch_kv_finalize(p, w, s) != hipSuccess) return SAGE_ERR_LAUNCH;
-  if (side && hipStreamWaitEvent(s, side->join, 0) != hipSuccess) return SAGE_ERR_LAUNCH;
   if (launch_kv_quant(p, k, v, w, ds_scale, ds_out, s) != hipSuccess) return SAGE_ERR_LAUNCH;
   return SAGE_OK;
 }

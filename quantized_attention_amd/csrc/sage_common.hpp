@@ -77,8 +77,7 @@ struct Workspace {
   float* ds;        // [BH][nqb][Mp], Delta S (pre-multiplied by ds_scale)
   double* kpart;    // [BH][nkt][d] FP64 chunk sums of K
   double* vpart;    // [BH][nkt][d] FP64 chunk sums of V (V smoothing)
-  float* vmaxp;     // [BH][nkt][d] chunk max of V
-  float* vminp;     // [BH][nkt][d] chunk min of V
+  float2* vmm;      // [BH][nkt][d] chunk (max, min) of V
   uint16_t* qm_hi;  // bf16 head of the block mean, in the Delta S MFMA operand order:
                     // [BH][ceil(nqb/32)][d/16][64 lanes][8] (lane 32 h + block % 32 holds
                     // channels 16 s + 8 h .. +7)
@@ -292,9 +291,12 @@ __device__ inline uint16_t bf16_rn(float x) {
 __device__ inline float bf16_val(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
 // Launchers; each returns hipSuccess or the launch error.
-hipError_t launch_kv_stats(const Problem& p, const void* k, const void* v, const Workspace& w, hipStream_t s);
+// The Q blocks (q_hat, dq or the MX scales, q_mean and its bf16 head/tail; skipped when q is null)
+// and the K / V chunk statistics, in one launch.
+hipError_t launch_stats(const Problem& p, const void* q, const void* k, const void* v, const Workspace& w,
+                        hipStream_t s);
+// Chunk statistics -> K mean, V_m and the V scale.
 hipError_t launch_kv_finalize(const Problem& p, const Workspace& w, hipStream_t s);
-hipError_t launch_q_prep(const Problem& p, const void* q, const Workspace& w, hipStream_t s);
 // K^, Delta S (into ds_out scaled by ds_scale; skipped when ds_out is null) and V^.
 hipError_t launch_kv_quant(const Problem& p, const void* k, const void* v, const Workspace& w,
                            float ds_scale, float* ds_out, hipStream_t s);

@@ -856,8 +856,8 @@ size_t sb_layout(const Problem& p, bool bwd, size_t* s) {
   z[kSbL2] = bwd ? BH * p.Np * 4 : 0;
   z[kSbKpart] = BH * p.nkt * d * 8;
   z[kSbVpart] = BH * p.nkt * d * 8;
-  z[kSbVmax] = BH * p.nkt * d * 4;
-  z[kSbVmin] = BH * p.nkt * d * 4;
+  z[kSbVmax] = BH * p.nkt * d * 8;  // (max, min) pairs
+  z[kSbVmin] = 0;
   z[kSbKmean] = BH * d * 4;
   z[kSbVmean] = BH * d * 4;
   z[kSbDv] = BH * d * 4;
@@ -877,14 +877,13 @@ hipError_t sb_prep_fwd(const Problem& p, const void* q, const void* k, const voi
   Workspace w{};
   w.kpart = (double*)(ws + o[kSbKpart]);
   w.vpart = (double*)(ws + o[kSbVpart]);
-  w.vmaxp = (float*)(ws + o[kSbVmax]);
-  w.vminp = (float*)(ws + o[kSbVmin]);
+  w.vmm = (float2*)(ws + o[kSbVmax]);
   w.kmean = (float*)(ws + o[kSbKmean]);
   w.vmean = (float*)(ws + o[kSbVmean]);
   w.dv = (float*)(ws + o[kSbDv]);
   hipError_t e;
   if (smooth_k) {
-    if ((e = launch_kv_stats(p, k, v, w, st)) != hipSuccess) return e;
+    if ((e = launch_stats(p, nullptr, k, v, w, st)) != hipSuccess) return e;
     if ((e = launch_kv_finalize(p, w, st)) != hipSuccess) return e;
   }
   const float* km = smooth_k ? w.kmean : nullptr;

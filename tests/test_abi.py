@@ -140,3 +140,36 @@ def test_varlen_shape_checks():
     assert qa.sage_attn_varlen_fwd(shape(), A, A, A, A, A, ws - 1, None) == qa.SAGE_ERR_NO_MEMORY
     assert qa.sage_attn_varlen_fwd(shape(), A + 8, A, A, A, None, 0, None) == qa.SAGE_ERR_INVALID_ARG
 
+
+
+def test_train_binding_rejects_mismatched_tensors():
+    """The SageBwd wrappers check every tensor's shape and dtype against q before the library
+    sees a pointer (CPU tensors: the shape checks come before the device check)."""
+    import torch
+    bf = torch.bfloat16
+    q = torch.zeros(1, 4, 64, 64, dtype=bf)
+    k = torch.zeros(1, 4, 96, 64, dtype=bf)
+    grouped = torch.zeros(1, 2, 96, 64, dtype=bf)
+    bad_forward = [(q, grouped, grouped), (q, k, torch.zeros(1, 4, 80, 64, dtype=bf)),
+                   (q, torch.zeros(1, 4, 96, 128, dtype=bf), torch.zeros(1, 4, 96, 128, dtype=bf))]
+    for a, b, c in bad_forward:
+        with pytest.raises(ValueError):
+            qa.sage_attn_train_forward(a, b, c)
+    with pytest.raises(ValueError):  # right shapes, host tensors
+        qa.sage_attn_train_forward(q, k, k)
+    out = torch.zeros_like(q)
+    lse = torch.zeros(1, 4, 64, dtype=torch.float32)
+    bad_backward = [
+        dict(k=grouped, v=grouped),
+        dict(dout=torch.zeros(1, 4, 63, 64, dtype=bf)),
+        dict(out=torch.zeros(1, 4, 64, 128, dtype=bf)),
+        dict(lse=torch.zeros(1, 4, 65, dtype=torch.float32)),
+        dict(lse=torch.zeros(1, 4, 64, dtype=torch.float64)),
+        dict(out=torch.zeros(1, 4, 64, 64, dtype=torch.float16)),
+    ]
+    for change in bad_backward:
+        args = dict(q=q, k=k, v=k, out=out, dout=q, lse=lse)
+        args.update(change)
+        with pytest.raises((ValueError, TypeError)):
+            qa.sage_attn_train_backward(**args)
+

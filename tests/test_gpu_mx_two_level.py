@@ -117,3 +117,29 @@ def test_two_level_full_size_sampled():
             f"(bound up to {bd.max():.3g})")
         assert err.mean() <= MEAN_ABS
         assert (err.max(axis=-1) <= MAX_ABS + bd).all()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_two_level_large_score_gaps(causal):
+    """Tiles whose row maximum lies far below the running maximum (76 and 185 octaves here, and a
+    later tile 4 octaves below): the level-one rescale of O must stay finite.  All query rows equal
+    (Q^ = 0, S = Delta S sm_scale); K channel 0 = 1024 on key 0, 600 on every key of tile 1, 0 on
+    tile 2, 1000 on one key of tile 3.  The oracle (FP64) gives the reference; every path of the MX
+    variant, and the INT8/FP8 path, must stay within the usual bars."""
+    N = M = 256
+    d = 64
+    rng = np.random.default_rng(31)
+    Q = np.zeros((N, d)); Q[:, 0] = 1.0
+    K = np.zeros((M, d)); K[0, 0] = 1024.0; K[64:128, 0] = 600.0; K[200, 0] = 1000.0
+    V = rng.choice([0.0, 0.5, 1.0, 1.5, 2.0, 3.0], (M, d)) * rng.choice([-1.0, 1.0], (M, d))
+    q, k, v = (f16(x) for x in (Q, K, V))
+    sm = 0.125
+    for flags, kw in ((FLAGS, dict(mxfp4=True, mx_p_two_level=True)), (oracle.MXFP4, dict(mxfp4=True)), (0, {})):
+        say(f"large score gaps, causal={causal}, {kw or 'int8/fp8'}")
+        got = gu.fwd(q[None, None], k[None, None], v[None, None], True, causal, sm, **kw).cpu().numpy()[0, 0]
+        ref, _, bd = oracle.forward_head_ties(q, k, v, True, causal, sm, flags)
+        err = np.abs(got.astype(np.float64) - ref)
+        say(f"  max abs {err.max():.3g} mean abs {err.mean():.3g}")
+        assert np.isfinite(got).all()
+        assert err.mean() <= MEAN_ABS
+        assert (err.max(axis=-1) <= MAX_ABS + bd).all()

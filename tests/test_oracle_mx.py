@@ -254,3 +254,105 @@ def test_tie_diagnostic_counts_exact_midpoints():
     l = hi.sum() + (~hi).sum() * 17 / 448
     assert np.allclose(bound, (2 / 448) * vm[late_low].sum() / l, rtol=1e-12, atol=0)
     assert np.array_equal(out, oracle.forward_head(q, k, v, True, False, math.log(448 / 17), 0))
+
+
+# ---- the MX branch of the rounding-decision margin (orc_forward_head_ties) ----
+# The diagnostic counts, per output row, the P quantization decisions whose input lies within a
+# relative tie_eps of a rounding boundary, and bounds the output change should every one of
+# them round the other way.  In the MX form there are two kinds of decision ("SageAttention3"
+# summary, 3.4 "The NVFP4 Microscaling Format and Quantization Operator"): an element's E2M1
+# code (boundaries at the midpoints 0.25, 0.75, ..., 5 of the value set, times the block
+# scale 2^e; the code then moves by the gap between its neighbours) and a 32-key block's E8M0
+# exponent (the block maximum against 6 2^e from below or 6 2^(e-1) from above; the whole
+# block is then quantized one octave coarser or finer, each value moving by less than 4 2^e).
+# The construction below puts every late P~ on one of these boundaries, up to a relative
+# offset of 1e-9 chosen so that the FP64 side of each decision is fixed, and states the count
+# and the bound in closed form.
+
+TIE_EPS = 2.0 ** -16
+HI_KEYS = (70, 130, 200)  # one high key in 32-key blocks 2, 4 and 6; blocks 0, 1 lie before the first
+
+
+def mx_tie_case():
+    """All query rows equal (Q^ = 0, so S = Delta S * sm_scale), K channel 0 equal to 1 on the
+    high keys and 0 elsewhere (M = 256, so mean(K) = 3/256 and gamma K are exact), V on the
+    E2M1 grid of every 32-token block.  A low key's P~ relative to a high maximum is then
+    r = exp(-sm_scale); the tile of the first high key and every later tile hold a high key,
+    so every low key from key 64 on is quantized against the high maximum."""
+    rng = np.random.default_rng(11)
+    N = M = 256
+    d = 64
+    Q = np.zeros((N, d)); Q[:, 0] = 1.0
+    K = np.zeros((M, d)); K[list(HI_KEYS), 0] = 1.0
+    V = rng.choice([0.0, 0.5, 1.0, 1.5, 2.0, 3.0], (M, d)) * rng.choice([-1.0, 1.0], (M, d))
+    return f16(Q), f16(K), f16(V), V
+
+
+def check_mx_ties(two_level=False):
+    """Counts and bounds of the MX margin diagnostic in closed form (raises AssertionError)."""
+    q, k, v, V = mx_tie_case()
+    M = 256
+    vmax = np.abs(V).max(axis=1)                       # the largest dequantized V' value of each key
+    hi = np.zeros(M, bool); hi[list(HI_KEYS)] = True
+    late_low = ~hi & (np.arange(M) >= 64)
+    low_blocks = [3, 5, 7]                             # late 32-key blocks without a high key
+    flags = oracle.MXFP4 | (oracle.MX_P_TWO_LEVEL if two_level else 0)
+
+    def run(r):
+        out, ties, bound = oracle.forward_head_ties(q, k, v, True, 0, -math.log(r), flags, tie_eps=TIE_EPS)
+        l = hi.sum() + (~hi).sum() * r                 # l in the final frame (high maximum)
+        return out, ties, bound, l
+
+    if not two_level:
+        # (a) element midpoints: block scale 2^-2 (block maximum 1 or 7/8), every late low value
+        # at 3.5 (1 + 1e-9) times it, gap 1; no exponent decision near a boundary
+        out, ties, bound, l = run(0.875 * (1 + 1e-9))
+        assert (ties == late_low.sum()).all(), ties
+        assert np.allclose(bound, 0.25 * vmax[late_low].sum() / l, rtol=1e-7, atol=0)
+        # (b) a low-only block's maximum r just below 6 2^-3 = 0.75: exponent -3, its values
+        # at 6 (1 - 1e-9) 2^-3 (on the grid); the exponent decision is near 6 2^e
+        out, ties, bound, l = run(0.75 * (1 - 1e-9))
+        blk = sum(vmax[32 * b:32 * b + 32].sum() for b in low_blocks)
+        assert (ties == len(low_blocks)).all(), ties
+        assert np.allclose(bound, 4 * 2.0 ** -3 * blk / l, rtol=1e-7, atol=0)
+        # (c) the maximum just above 0.75 = 6 2^(e-1): exponent -2, values at 3 (1 + 1e-9) 2^-2
+        out, ties, bound, l = run(0.75 * (1 + 1e-9))
+        assert (ties == len(low_blocks)).all(), ties
+        assert np.allclose(bound, 4 * 2.0 ** -2 * blk / l, rtol=1e-7, atol=0)
+        assert np.array_equal(out, oracle.forward_head(q, k, v, True, 0, -math.log(0.75 * (1 + 1e-9)), flags))
+    else:
+        # two-level P: every late tile holds a high key, so s1 = 1/6 and the high keys map to 6
+        # exactly (not a rounded input: no exponent decision); low keys at 6 r = 3.5 (1 + 1e-9)
+        # with block scale 2^0, gap 1, weighted by s1
+        out, ties, bound, l = run((7.0 / 12.0) * (1 + 1e-9))
+        assert (ties == late_low.sum()).all(), ties
+        assert np.allclose(bound, (1.0 / 6.0) * vmax[late_low].sum() / l, rtol=1e-7, atol=0)
+
+
+@pytest.mark.parametrize("two_level", [False, True])
+def test_mx_tie_diagnostic_closed_form(two_level):
+    check_mx_ties(two_level)
+
+
+# Plausible mistakes in the MX branch of the margin bound, each planted in a copy of the oracle:
+# the octave move of an exponent decision bounded by 2 instead of 4 steps; the exponent decision
+# dropped; only one side of it checked; the element gap table off; the block scale 2^e left out;
+# the two-level factor s1 left out.
+MX_TIE_MISTAKES = {
+    "octave_x2": ("blk += 4.0 * S[x];", "blk += 2.0 * S[x];"),
+    "no_exponent_decision": ("if (am > 0.0 && !(two && am == 6.0) &&", "if (0 && am > 0.0 && !(two && am == 6.0) &&"),
+    "exponent_one_side": ("|| near_rel(am, 6.0 * ldexp(1.0, ep - 1), tie_eps))", ")"),
+    "gap_table": ("static const double gap[7] = {0.5, 0.5, 0.5, 0.5, 1.0, 1.0, 2.0};",
+                  "static const double gap[7] = {0.5, 0.5, 0.5, 0.5, 1.0, 0.5, 2.0};"),
+    "no_block_scale": ("mg.mass += s1 * ldexp(blk, ep);", "mg.mass += s1 * blk;"),
+    "no_s1": ("mg.mass += s1 * ldexp(blk, ep);", "mg.mass += ldexp(blk, ep);"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MX_TIE_MISTAKES))
+def test_mx_tie_diagnostic_catches_planted_mistake(name):
+    old, new = MX_TIE_MISTAKES[name]
+    with oracle.planted_mistake(("sage_oracle.c", old, new)):
+        with pytest.raises(AssertionError):
+            check_mx_ties(False)
+            check_mx_ties(True)

@@ -245,7 +245,9 @@ def pv_lossless_case(seed, N, M, d, smooth_v):
     grid = np.array([dec[c] for c in range(0x30, 0x7F)])  # magnitudes 0.5 .. 448
     Q = np.zeros((N, d))
     Q[np.arange(N), rng.integers(0, d, N)] = 8.0
-    K = rng.integers(0, 13, (M, d)).astype(np.float64)
+    # one more per 64-key tile: every tile raises the running maximum by exactly one octave, so
+    # each one rescales O and l by alpha = 1/2 (P~ stays within 2^-15 of its tile's maximum)
+    K = (rng.integers(0, 13, (M, d)) + (np.arange(M) // 64)[:, None]).astype(np.float64)
     ev = rng.integers(-6, -1, d)
     Z = np.zeros((M, d))
     for c in range(d):
