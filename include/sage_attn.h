@@ -291,6 +291,23 @@ int sage_attn_train_bwd(const sage_attn_shape* shape, const void* q, const void*
                         void* workspace, size_t ws_bytes, void* stream);
 
 /*
+ * sage_attn_fwd_noalloc -- the forward pass of sage_attn_fwd_ex for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  It calls no allocating routine.  Its workspace is a scratch array of
+ * SAGE_NOALLOC_MAX_BYTES bytes that the library holds in device memory, one per GPU it runs on,
+ * from the first call on that GPU until the process ends.
+ * Arguments and layouts as for sage_attn_fwd_ex (no workspace arguments).  A problem whose
+ * workspace (sage_attn_workspace_bytes_ex) exceeds SAGE_NOALLOC_MAX_BYTES returns
+ * SAGE_ERR_NO_MEMORY before anything is enqueued.
+ * Every call on one GPU uses that GPU's single scratch array: calls whose work overlaps on one
+ * GPU (two streams, two host threads) race on it and must be ordered by the caller.  The array
+ * keeps the last call's contents; nothing in it needs to start at zero.
+ */
+#define SAGE_NOALLOC_MAX_BYTES ((size_t)128 << 20)
+int sage_attn_fwd_noalloc(const sage_attn_shape* shape, const void* q, const void* k, const void* v, void* out,
+                          void* stream);
+
+/*
  * sage_attn_set_profile_events -- measurement hook.  With both arguments non-NULL (two
  * hipEvent_t handles), the next sage_attn_fwd / sage_attn_fwd_ws call on this thread
  * records `start` on its stream just before the fused attention kernel and `stop` just

@@ -25,6 +25,7 @@ __all__ = [
     "SageAttnVarlenShape", "sage_attn_varlen_workspace_bytes", "sage_attn_varlen_fwd", "sage_attn_varlen",
     "SAGE_TRAIN_NO_SMOOTH_K", "sage_attn_train_workspace_bytes", "sage_attn_train_fwd", "sage_attn_train_bwd",
     "sage_attn_train_forward", "sage_attn_train_backward", "SageBwdAttention",
+    "SAGE_NOALLOC_MAX_BYTES", "sage_attn_fwd_noalloc",
 ]
 
 SAGE_OK = 0
@@ -48,6 +49,7 @@ SAGE_TRAIN_NO_SMOOTH_K = 0x4000
 
 SAGE_BQ = 128
 SAGE_BK = 64
+SAGE_NOALLOC_MAX_BYTES = 128 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "lib", "libsage_attn.so")
@@ -124,6 +126,8 @@ def load_library():
     L.sage_attn_varlen_workspace_bytes.restype = sz
     L.sage_attn_varlen_fwd.argtypes = [VP, P, P, P, P, P, sz, P]
     L.sage_attn_varlen_fwd.restype = i
+    L.sage_attn_fwd_noalloc.argtypes = [SP, P, P, P, P, P]
+    L.sage_attn_fwd_noalloc.restype = i
     L.sage_attn_train_workspace_bytes.argtypes = [SP]
     L.sage_attn_train_workspace_bytes.restype = sz
     L.sage_attn_train_fwd.argtypes = [SP, P, P, P, P, P, P, sz, P]
@@ -177,6 +181,10 @@ def sage_attn_varlen_workspace_bytes(shape) -> int:
 
 def sage_attn_varlen_fwd(shape, q, k, v, out, workspace, ws_bytes, stream) -> int:
     return load_library().sage_attn_varlen_fwd(_shape_ptr(shape), q, k, v, out, workspace, ws_bytes, stream)
+
+
+def sage_attn_fwd_noalloc(shape, q, k, v, out, stream) -> int:
+    return load_library().sage_attn_fwd_noalloc(_shape_ptr(shape), q, k, v, out, stream)
 
 
 def sage_attn_train_workspace_bytes(shape) -> int:

@@ -232,6 +232,32 @@ int fwd_checked(const Problem& p, const void* q, const void* k, const void* v, v
   return rc;
 }
 
+// Workspace of the no-allocation entry point: one array per device, held while the library is
+// loaded.  In host code `scratch` is a stand-in symbol, not a device address; the device address
+// of each GPU's copy comes from hipGetSymbolAddress on that GPU (scratch_on_current_device).
+static __device__ __align__(256) unsigned char scratch[SAGE_NOALLOC_MAX_BYTES];
+
+// The device address of this device's scratch array, looked up once per device (with that
+// device current) and kept; null if the lookup fails.
+void* scratch_on_current_device() {
+  static std::mutex mu;
+  static void* ptr[64];
+  static bool looked[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> g(mu);
+  if (!looked[dev]) {
+    void* a = nullptr;
+    if (hipGetSymbolAddress(&a, HIP_SYMBOL(scratch)) != hipSuccess) {
+      (void)hipGetLastError();
+      return nullptr;  // not cached: a later call may succeed
+    }
+    ptr[dev] = a;
+    looked[dev] = true;
+  }
+  return ptr[dev];
+}
+
 // SageBwd problems: the dense shape with Hkv = Hq; the variant carries the input and output
 // dtypes and the K-smoothing ablation.
 int make_train_problem(const sage_attn_shape* sh, Problem* p, bool* smooth_k) {
@@ -300,6 +326,19 @@ int sage_attn_fwd(const void* q, const void* k, const void* v, void* out, int B,
                   int d, int causal, float sm_scale, unsigned variant, void* stream) {
   const sage_attn_shape sh = {B, H, H, N, M, d, causal, sm_scale, variant};
   return sage_attn_fwd_ex(&sh, q, k, v, out, nullptr, 0, stream);
+}
+
+int sage_attn_fwd_noalloc(const sage_attn_shape* shape, const void* q, const void* k, const void* v, void* out,
+                          void* stream) {
+  Problem p;
+  int rc = make_problem(shape, &p);
+  if (rc != SAGE_OK) return rc;
+  if ((rc = check_io(q, k, v, out)) != SAGE_OK) return rc;
+  if (workspace_layout(p, nullptr) > SAGE_NOALLOC_MAX_BYTES) return SAGE_ERR_NO_MEMORY;
+  if ((rc = device_check()) != SAGE_OK) return rc;
+  void* ws = scratch_on_current_device();
+  if (!ws) return SAGE_ERR_DEVICE;
+  return fwd_impl(q, k, v, out, p, ws, (hipStream_t)stream);
 }
 
 size_t sage_attn_varlen_workspace_bytes(const sage_attn_varlen_shape* shape) {

@@ -23,7 +23,8 @@ def test_header_declares_the_boundary():
                             "sage_attn_status_string", "sage_attn_version", "sage_attn_fwd_ex",
                             "sage_attn_workspace_bytes_ex", "sage_attn_quantize_ex",
                             "sage_attn_varlen_workspace_bytes", "sage_attn_varlen_fwd",
-                            "sage_attn_train_workspace_bytes", "sage_attn_train_fwd", "sage_attn_train_bwd"])
+                            "sage_attn_train_workspace_bytes", "sage_attn_train_fwd", "sage_attn_train_bwd",
+                            "sage_attn_fwd_noalloc"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -173,3 +174,15 @@ def test_train_binding_rejects_mismatched_tensors():
         with pytest.raises((ValueError, TypeError)):
             qa.sage_attn_train_backward(**args)
 
+
+def test_noalloc_rejects_problems_beyond_its_scratch():
+    """The no-allocation entry point checks the problem's workspace against its fixed scratch
+    before touching a device."""
+    S = qa.SageAttnShape
+    A = 256
+    big = S(1, 32, 32, 32768, 32768, 128, 1, 0.0, 0)
+    assert qa.sage_attn_workspace_bytes_ex(big) > qa.SAGE_NOALLOC_MAX_BYTES
+    assert qa.sage_attn_fwd_noalloc(big, A, A, A, A, None) == qa.SAGE_ERR_NO_MEMORY
+    assert qa.sage_attn_fwd_noalloc(None, A, A, A, A, None) == qa.SAGE_ERR_INVALID_ARG
+    small = S(1, 2, 2, 256, 256, 64, 0, 0.0, 0)
+    assert qa.sage_attn_fwd_noalloc(small, 0, A, A, A, None) == qa.SAGE_ERR_INVALID_ARG
