@@ -32,6 +32,18 @@ sys.path.insert(0, ROOT)
 
 PEAK_TOPS = 5000.0     # MI355X dense INT8 / OCP-FP8 MFMA peak, 5.0 POPS
 PEAK_TOPS_FP4 = 10100.0  # MI355X dense MXFP4 MFMA peak, 10.1 PFLOP/s (the MX variant's contractions)
+# VALU issue peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-slots per second (the published
+# FP32 vector 157.3 TFLOP/s counts 2 flops per FMA and 2 lanes per packed FP32 instruction,
+# and the kernels use no packed FP32).  A half-rate instruction (v_exp_f32, the FP8 and FP4
+# packs) takes two slots.
+PEAK_VALU_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
+
+# The softmax's VALU work per score element, in lane-slots: the method's steps as the fewest
+# gfx950 instructions that carry them out (INT8 path: convert the INT32 score, one FMA for
+# dequantization and Delta S, half a v_max3 for the row max, the subtraction of the running
+# max, exp2 (2 slots), the row sum, half of a two-value FP8 pack (2 slots); E4M3 QK: no
+# convert; MX: no convert, the FP4 pack of two values per instruction).
+VALU_SLOTS_PER_SCORE = {"i8f8": 7.5, "qkfp8": 6.5, "mx": 6.5}
 
 # Kernel-level HBM traffic of the fused attention kernel, one launch on the named workload:
 # rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (KiB per dispatch) scaled by what the same
@@ -44,6 +56,11 @@ TRAFFIC_BYTES = {
     "mxfp4_32k": {"source_sha256_16": "003f5491510e3934",
                   "fetch_bytes": 1694316556, "write_bytes": 201326899},
 }
+# SQ counters of the fused attention kernel on the named workload (rocprofv3 --pmc, the summary
+# under profiles/): VALU and matrix-core busy fractions of the SIMD cycles, VALU instructions per
+# (wave, 64-key tile), and the engine clock under that load (GRBM_GUI_ACTIVE cycles over the
+# dispatch's own duration).  Keyed by the same source hash as the traffic; null once stale.
+COUNTERS = {}
 _COMMON_SOURCES = ("quantized_attention_amd/csrc/attn_device.hpp", "quantized_attention_amd/csrc/sage_common.hpp")
 KERNEL_SOURCES = {
     False: ("quantized_attention_amd/csrc/attn_fwd.hip",) + _COMMON_SOURCES,    # INT8/FP8 path
@@ -67,16 +84,46 @@ def measured_traffic(name: str, mx: bool = False):
     return t["fetch_bytes"] + t["write_bytes"]
 
 
+def measured_counters(name: str, mx: bool = False):
+    c = COUNTERS.get(name)
+    if c is None or c["source_sha256_16"] != kernel_source_hash(mx):
+        return None
+    return {k: v for k, v in c.items() if k != "source_sha256_16"}
+
+
+def scores_of(cfg) -> float:
+    """(query, key) score elements the fused kernel evaluates, with the metric's causal counting
+    (half of N^2 for causal N = M; the visible pairs otherwise)."""
+    return counted_ops(cfg) / (4.0 * cfg.d)
+
+
+def host_info() -> dict:
+    """The host the CPU baseline ran on: logical CPUs and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model}
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill32k",
-                    help="one of: n4k, prefill32k, full32k, video17k, chunk4k_32k, prefill32k_gqa, prefill32k_qkfp8, "
+                    help="one of: n4k, prefill32k, prefill32k_b, full32k, video17k, chunk4k_32k, prefill32k_gqa, "
+                         "prefill32k_qkfp8, "
                          "mxfp4_32k, mxfp4_32k_p2l, train8k (default prefill32k)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-measured-peak", action="store_true",
+                    help="skip the matrix-core rate probe (libsage_probe.so) after the timed steps")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="after the steps, copy a MIB-MiB device buffer twice (a plain copy kernel of "
                          "known size, the reference point for HBM byte counters)")
@@ -148,7 +195,8 @@ def cpu_baseline(cfg, budget_s: float) -> dict:
             batch *= 2
     return {"value": ops / t_used / 1e12, "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"head 0 of {cfg.B * cfg.H}, {nrows} seeded random query rows of N={cfg.N} "
-                      f"(per-head preprocessing and Delta S rows included), {t_used:.1f} s"}
+                      f"(per-head preprocessing and Delta S rows included), {t_used:.1f} s",
+            "omp_threads": oracle.num_threads(), **host_info()}
 
 
 def train_cpu_baseline(cfg, n=1024):
@@ -164,7 +212,7 @@ def train_cpu_baseline(cfg, n=1024):
     ops = counted_ops(sub) * 14 / 4
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"head 0, first {sub.N} queries and keys (forward + backward, per-head preprocessing "
-                      f"included), {dt:.1f} s"}
+                      f"included), {dt:.1f} s", "omp_threads": oracle.num_threads(), **host_info()}
 
 
 def main_train(args, cfg):
@@ -335,6 +383,26 @@ def main():
     value = ops / (ms * 1e-3) / 1e12
     achieved = ops / (kms * 1e-3) / 1e12
     traffic = measured_traffic(cfg.name, cfg.mxfp4)
+    path = "mx" if cfg.mxfp4 else ("qkfp8" if cfg.qk_fp8 else "i8f8")
+    slots = VALU_SLOTS_PER_SCORE[path] * scores_of(cfg) / (kms * 1e-3) / 1e12
+    measured_peak = None
+    if not args.no_measured_peak:
+        from quantized_attention_amd import probe
+        measured_peak = round(probe.mfma_rate(2 if cfg.mxfp4 else (1 if cfg.qk_fp8 else 0)), 1)
+    # The fused kernel's binding resource is its vector work: per (wave, 64-key tile) the softmax
+    # needs VALU_SLOTS_PER_SCORE x 32 x 4 cycles against 512 (INT8/FP8, d = 128) or 256 (FP4)
+    # cycles of matrix-core work, so the roofline is the VALU issue rate; the metric's matrix-core
+    # fraction is reported beside it.
+    roofline = {
+        "bound": "alu", "achieved": round(slots, 3), "peak": round(PEAK_VALU_TSLOTS, 3),
+        "unit": "T VALU lane-slots/s", "frac": round(slots / PEAK_VALU_TSLOTS, 4), "traffic": traffic,
+        "work": f"{VALU_SLOTS_PER_SCORE[path]} VALU lane-slots per score element x {scores_of(cfg):.4g} scores "
+                f"per launch",
+        "mfma": {"achieved": round(achieved, 2), "peak": peak, "unit": "TOPS", "frac": round(achieved / peak, 4),
+                 "peak_measured": measured_peak,
+                 "frac_of_measured": round(achieved / measured_peak, 4) if measured_peak else None},
+        "counters": measured_counters(cfg.name, cfg.mxfp4),
+    }
     dtype = ("e2m1 + e8m0 1x32 blocks (QK, PV), fp32 softmax/accumulate" if cfg.mxfp4
              else ("fp8e4m3(QK)+fp8e4m3(PV)" if cfg.qk_fp8 else "int8(QK)+fp8e4m3(PV)")
              + ", fp32 softmax/accumulate")
@@ -372,13 +440,7 @@ def main():
         "attn_kernel_ms_median": round(float(np.median(kern_ms)), 4),
         "attn_kernel_ms_min": round(float(np.min(kern_ms)), 4),
         "preprocess_ms": round(ms - kms, 4),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TOPS",
-                     "frac": round(achieved / peak, 4), "traffic": traffic,
-                     "note": "the fused kernel's ceiling is its vector (VALU) work, not the matrix cores: the "
-                             "softmax needs about 7.5 VALU issue slots per score element (exp2 and the "
-                             "low-precision pack at half rate) against about 4 that would keep the MFMA at "
-                             "peak; rocprofv3 SQ counters show the VALU busy about 91% of the kernel's cycles "
-                             "at prefill32k"},
+        "roofline": roofline,
     }
     if args.copy_calibration > 0:
         n = args.copy_calibration << 20

@@ -67,7 +67,7 @@ def _configure(L):
     L.orc_preprocess_mx_head.restype = i
     L.orc_forward_head.argtypes = [P, P, P, i, i, i, i, i, dbl, u, P, i, P]
     L.orc_forward_head.restype = i
-    L.orc_forward_head_ties.argtypes = [P, P, P, i, i, i, i, i, dbl, u, P, i, P, dbl, P, P]
+    L.orc_forward_head_ties.argtypes = [P, P, P, i, i, i, i, i, dbl, u, P, i, P, dbl, dbl, P, P]
     L.orc_forward_head_ties.restype = i
     L.orc_exact_head.argtypes = [P, P, P, i, i, i, i, i, dbl, P, i, P]
     L.orc_exact_head.restype = i
@@ -77,6 +77,8 @@ def _configure(L):
     L.orc_e4m3_decode.restype = dbl
     L.orc_e4m3_encode.argtypes = [dbl]
     L.orc_e4m3_encode.restype = ctypes.c_uint8
+    L.orc_e4m3_encode_f32_array.argtypes = [P, P, ctypes.c_size_t]
+    L.orc_e4m3_encode_f32_array.restype = None
     L.orc_e5m2_decode.argtypes = [ctypes.c_uint8]
     L.orc_e5m2_decode.restype = dbl
     L.orc_e5m2_encode.argtypes = [dbl]
@@ -210,10 +212,12 @@ def forward_head(q, k, v, fp16: bool, causal: int, sm_scale: float, flags: int =
 
 
 def forward_head_ties(q, k, v, fp16: bool, causal: int, sm_scale: float, flags: int = 0, rows=None,
-                      tie_eps: float = 2.0 ** -16):
+                      tie_eps: float = 2.0 ** -16, qk_step_err: float = 0.0):
     """forward_head, and per row the count of its P rounding decisions whose input lies within
     relative distance tie_eps of a rounding boundary (where an FP32 kernel may round the other
-    way) and a bound on the output change if all of them do: (out, ties, bound)."""
+    way) and a bound on the output change if all of them do: (out, ties, bound).  qk_step_err
+    (with QK_E4M3): widen each decision's margin by the score error of a matrix core that sums
+    every 64-channel step of Q^ K^ to within qk_step_err of the step's largest code product."""
     q, k, v = _u16(q), _u16(k), _u16(v)
     N, d = q.shape
     M = k.shape[0]
@@ -226,8 +230,8 @@ def forward_head_ties(q, k, v, fp16: bool, causal: int, sm_scale: float, flags: 
     ties = np.zeros(nrows, np.int32)
     bound = np.zeros(nrows, np.float64)
     rc = lib().orc_forward_head_ties(_ptr(q), _ptr(k), _ptr(v), int(fp16), N, M, d, int(causal),
-                                     float(sm_scale), flags, _ptr(rp), nrows, _ptr(out), float(tie_eps), _ptr(ties),
-                                     _ptr(bound))
+                                     float(sm_scale), flags, _ptr(rp), nrows, _ptr(out), float(tie_eps),
+                                     float(qk_step_err), _ptr(ties), _ptr(bound))
     if rc != 0:
         raise ValueError("orc_forward_head_ties rejected its arguments")
     return out, ties, bound
@@ -314,6 +318,14 @@ def sagebwd_quantize(q, k, v, dout, fp16: bool, flags: int = 0) -> dict:
     if dout is None:
         del o["docode"], o["sdo"]
     return o
+
+
+def e4m3_encode_f32(x) -> np.ndarray:
+    """E4M3 codes (round to nearest even, saturated) of an FP32 array, elementwise."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, np.uint8)
+    lib().orc_e4m3_encode_f32_array(_ptr(x), _ptr(out), x.size)
+    return out
 
 
 def e4m3_decode_table() -> np.ndarray:

@@ -122,6 +122,13 @@ uint8_t orc_e4m3_encode(double x) {
   return (uint8_t)(s | nearest_even_index(e4m3_mag, 127, fabs(x)));
 }
 
+/* The same cast over an array of FP32 values (for exhaustive checks of a device conversion). */
+void orc_e4m3_encode_f32_array(const float* x, uint8_t* out, size_t n) {
+  init_tables();
+#pragma omp parallel for schedule(static)
+  for (long long i = 0; i < (long long)n; i++) out[i] = orc_e4m3_encode((double)x[i]);
+}
+
 /* OCP E5M2: 1 sign, 5 exponent (bias 15), 2 mantissa bits, IEEE-like Inf/NaN. */
 double orc_e5m2_decode(uint8_t c) {
   int s = c >> 7, e = (c >> 2) & 31, m = c & 3;
@@ -611,14 +618,36 @@ static double e2m1_tie_step(double y, double eps) {
  * tile loop like O (scaled by alpha, divided by l at the end). */
 typedef struct { int count; double mass; } margin_t;
 
+/* The score error a kernel may make under the E4M3 QK knob when its matrix core sums each
+ * 64-channel step of Q^ K^ with an error of at most qk_step_err times the step's largest product
+ * of code values: sum over the steps of that, times dQ dK sm_scale (natural-log units, so that
+ * exp turns it into the same relative error of P~). */
+static double qk_score_err(const head_t* h, int r, int t, double sm_scale, double qk_step_err) {
+  int d = h->d;
+  double e = 0.0;
+  for (int c0 = 0; c0 < d; c0 += 64) {
+    double mx = 0.0;
+    for (int c = c0; c < c0 + 64; c++) {
+      double p = fabs(qk_value(h, h->qhat[(size_t)r * d + c]) * qk_value(h, h->khat[(size_t)t * d + c]));
+      if (p > mx) mx = p;
+    }
+    e += mx;
+  }
+  return qk_step_err * e * (double)h->dq[r] * (double)h->dk_key[t] * sm_scale;
+}
+
 /* Steps 7-8 for one row: the tile loop and the epilogue.  With mg != NULL, *ties and *bound
  * receive the row's near-boundary decisions (inputs within relative tie_eps of a rounding
  * boundary) and the bound on the output change they can cause. */
 static void forward_row(const head_t* h, int r, int causal, int off, double sm_scale, const double* ds,
-                        double* S, double* Pt, double* Ph, double* R, double* out, double tie_eps, int* ties,
-                        double* bound) {
+                        double* S, double* Pt, double* Ph, double* R, double* out, double tie_eps,
+                        double qk_step_err, int* ties, double* bound) {
   margin_t mg = {0, 0.0};
   const int track = ties != NULL || bound != NULL;
+  /* score errors of the keys of this tile and the largest of the keys seen so far (the running
+   * maximum carries at most that), when the E4M3 QK kernel model is asked for */
+  const int qk_err = track && (h->flags & ORC_QK_E4M3) && qk_step_err > 0.0;
+  double E[ORC_BK], emax = 0.0;
   int d = h->d, M = h->M;
   double m = -INFINITY, l = 0.0;
   for (int c = 0; c < d; c++) out[c] = 0.0;
@@ -635,6 +664,10 @@ static void forward_row(const head_t* h, int r, int causal, int off, double sm_s
       if (causal && t > r + off) { S[x] = -INFINITY; continue; }
       S[x] = (qk_term(h, r, t) + ds[t]) * sm_scale; /* [SA2 Alg. 1] S = deq(QK) + Delta S */
       if (S[x] > mt) mt = S[x];
+      if (qk_err) {
+        E[x] = qk_score_err(h, r, t, sm_scale, qk_step_err);
+        if (E[x] > emax) emax = E[x];
+      }
     }
     /* Online softmax ([SA2 Alg. 1] step 3; [QA] datapath): running max, then exp. */
     double mnew = mt > m ? mt : m;
@@ -710,7 +743,7 @@ static void forward_row(const head_t* h, int r, int causal, int off, double sm_s
       for (int x = 0; x < n; x++) Ph[x] = quant_p(h, Pt[x]);
       if (track && !(h->flags & (ORC_PV_IDENTITY | ORC_PV_E5M2 | ORC_PV_INT8)))
         for (int x = 0; x < n; x++) {
-          double st = e4m3_tie_step(h->pscale * Pt[x], tie_eps);
+          double st = e4m3_tie_step(h->pscale * Pt[x], tie_eps + (qk_err ? E[x] + emax : 0.0));
           if (st == 0.0) continue;
           double vm = 0.0; /* the largest dequantized V value of the key (V^ times dV) */
           for (int c = 0; c < d; c++) {
@@ -746,13 +779,14 @@ static void forward_row(const head_t* h, int r, int causal, int off, double sm_s
 int orc_forward_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, int in_fp16,
                      int N, int M, int d, int causal, double sm_scale, unsigned flags,
                      const int* rows, int nrows, double* out) {
-  return orc_forward_head_ties(q, k, v, in_fp16, N, M, d, causal, sm_scale, flags, rows, nrows, out, 0.0, NULL,
-                               NULL);
+  return orc_forward_head_ties(q, k, v, in_fp16, N, M, d, causal, sm_scale, flags, rows, nrows, out, 0.0, 0.0,
+                               NULL, NULL);
 }
 
 int orc_forward_head_ties(const uint16_t* q, const uint16_t* k, const uint16_t* v, int in_fp16,
                           int N, int M, int d, int causal, double sm_scale, unsigned flags,
-                          const int* rows, int nrows, double* out, double tie_eps, int* ties, double* bound) {
+                          const int* rows, int nrows, double* out, double tie_eps, double qk_step_err,
+                          int* ties, double* bound) {
   int off;
   if (!q || !k || !v || !out || nrows < 0) return -1;
   if (causal_offset(causal, N, M, &off)) return -1;
@@ -790,7 +824,7 @@ int orc_forward_head_ties(const uint16_t* q, const uint16_t* k, const uint16_t* 
       for (int x = 0; x < nrows; x++) {
         int r = rows ? rows[x] : x;
         forward_row(&h, r, causal, off, sm_scale, dsr[r / ORC_BQ], S, Pt, Ph, R, out + (size_t)x * d, tie_eps,
-                    ties ? ties + x : NULL, bound ? bound + x : NULL);
+                    qk_step_err, ties ? ties + x : NULL, bound ? bound + x : NULL);
       }
       free(S); free(Pt); free(Ph); free(R);
     }

@@ -60,6 +60,7 @@ float   orc_bf16_to_f32(uint16_t h);
 float   orc_fp16_to_f32(uint16_t h);
 double  orc_e4m3_decode(uint8_t code);  /* OCP E4M3FN: bias 7, max 448, no Inf, S.1111.111 = NaN */
 uint8_t orc_e4m3_encode(double x);      /* round-to-nearest-even, saturate to +-448, NaN -> 0x7F */
+void    orc_e4m3_encode_f32_array(const float* x, uint8_t* out, size_t n); /* the cast above, per element */
 double  orc_e5m2_decode(uint8_t code);  /* OCP E5M2: bias 15, max 57344                           */
 uint8_t orc_e5m2_encode(double x);      /* RNE, saturate to +-57344                               */
 double  orc_e2m1_decode(uint8_t code);  /* 4-bit E2M1: {0, .5, 1, 1.5, 2, 3, 4, 6} and negatives   */
@@ -125,10 +126,15 @@ int orc_forward_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, in
  * quantization decisions (E4M3 codes of 448 P~; MX: E2M1 codes and E8M0 block exponents) whose
  * input lies within relative distance tie_eps of a rounding boundary -- a kernel working in
  * FP32 may round those the other way, and either result is a correct rounding -- and a bound
- * on how far the row's output can move if all of them do (a diagnostic for parity tests). */
+ * on how far the row's output can move if all of them do (a diagnostic for parity tests).
+ * qk_step_err (ORC_QK_E4M3 only; 0 otherwise): a kernel whose matrix core sums each 64-channel
+ * step of Q^ K^ with an error of at most qk_step_err times the step's largest code product; the
+ * margin of each E4M3 decision of P^ then widens by the score errors this allows (that of the
+ * key and that of the row maximum). */
 int orc_forward_head_ties(const uint16_t* q, const uint16_t* k, const uint16_t* v, int in_fp16,
                           int N, int M, int d, int causal, double sm_scale, unsigned flags,
-                          const int* rows, int nrows, double* out, double tie_eps, int* ties, double* bound);
+                          const int* rows, int nrows, double* out, double tie_eps, double qk_step_err,
+                          int* ties, double* bound);
 
 /* ---- textbook attention softmax(Q K^T * sm_scale) V in FP64 on the widened inputs ---- */
 int orc_exact_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, int in_fp16,

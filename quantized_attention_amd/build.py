@@ -2,7 +2,9 @@
 
 Every .hip file under csrc/ is compiled to an object in parallel, then linked into
 quantized_attention_amd/lib/libsage_attn.so.  The library exports the C ABI declared in
-include/sage_attn.h.
+include/sage_attn.h.  The instruction probes under probe/ (matrix-core precision and rates,
+the E4M3 conversion) are built into their own library, lib/libsage_probe.so, which the GPU
+unit tests and bench.py's measured peak load; the attention library does not depend on it.
 """
 from __future__ import annotations
 
@@ -18,6 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libsage_attn.so")
+PROBE_SRC = os.path.join(PKG, "probe", "sage_probe.hip")
+PROBE_LIB = os.path.join(LIBDIR, "libsage_probe.so")
 OBJDIR = os.path.join(ROOT, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -49,8 +53,10 @@ def build(verbose: bool = False) -> str:
             print(r.stderr, file=sys.stderr)
         return obj
 
-    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+    with ThreadPoolExecutor(max_workers=min(8, len(srcs) + 1)) as ex:
+        probe = ex.submit(build_probe)
         objs = list(ex.map(compile_one, srcs))
+        probe.result()
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -58,6 +64,17 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
     return LIB
+
+
+def build_probe() -> str:
+    """The probe library (one source, compiled and linked in one step)."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC, *FLAGS, "-shared", PROBE_SRC, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {PROBE_SRC}:\n{r.stderr}")
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
 
 
 if __name__ == "__main__":

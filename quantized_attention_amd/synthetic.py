@@ -83,6 +83,9 @@ CONFIGS = {
     "prefill32k": Config("prefill32k", 1, 32, 32768, 32768, 128, "bf16", True,
                          Dist(k_off_std=4.0, k_spike=8.0, k_spike_channels=spike_channels(128)), 1003,
                          note="LLM prefill layer (8B-style), causal"),
+    "prefill32k_b": Config("prefill32k_b", 1, 32, 32768, 32768, 128, "bf16", True,
+                           Dist(k_off_std=4.0, v_bias_std=0.5), 1009,
+                           note="the prefill layer with the N = 4096 workload's distribution and K offset std 4"),
     "video17k": Config("video17k", 2, 48, 17550, 17550, 64, "bf16", False,
                        Dist(q_off_std=3.0, k_off_std=3.0, v_bias_std=1.0), 1004, smooth_v=True,
                        note="video diffusion shape, ragged last tile, V smoothing"),

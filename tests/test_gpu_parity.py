@@ -69,36 +69,55 @@ def oracle_head(cfg, q, k, v, bh, flags=0, rows=None):
                                flags | (oracle.SMOOTH_V if cfg.smooth_v else 0), rows=rows)
 
 
+def check_preprocess_head(cfg, g, q, k, v, bh):
+    """Every quantize view of head bh against the oracle's preprocessing: means, scales and codes
+    bit for bit; Delta S (FP32 against FP64) within 1e-5 relative, on the tiles that are written."""
+    N, M = cfg.N, cfg.M
+    b, h = bh // cfg.H, bh % cfg.H
+    o = oracle.preprocess_head(q[b, h], k[b, h], v[b, h], cfg.fp16, oracle.SMOOTH_V if cfg.smooth_v else 0)
+    assert np.array_equal(g["k_mean"][bh].view(np.uint32), o["kmean"].view(np.uint32))
+    assert np.array_equal(g["v_mean"][bh].view(np.uint32), o["vmean"].view(np.uint32))
+    assert np.array_equal(g["q_mean"][bh].view(np.uint32), o["qmean"].view(np.uint32))
+    assert np.array_equal(g["dq"][bh, :N].view(np.uint32), o["dq"].view(np.uint32))
+    assert np.array_equal(g["dk"][bh].view(np.uint32), o["dk"].view(np.uint32))
+    assert np.array_equal(g["dv"][bh].view(np.uint32), o["dv"].view(np.uint32))
+    assert np.array_equal(g["q_hat"][bh, :N], o["qhat"])
+    assert not g["q_hat"][bh, N:].any()
+    assert np.array_equal(g["k_hat"][bh, :M], o["khat"])
+    assert not g["k_hat"][bh, M:].any()
+    assert np.array_equal(g["v_nat"][bh, :M], o["vhat"])
+    assert not g["v_nat"][bh, M:].any()
+    ds, ref = g["delta_s"][bh][:, :M].astype(np.float64), o["ds"]
+    if cfg.causal:
+        # written: the 64-key tiles whose first key is < 128 (i + 1) + coff
+        coff = cfg.M - cfg.N if cfg.causal == 2 else 0
+        tile0 = 64 * (np.arange(M) // 64)
+        mask = tile0[None, :] - coff < 128 * (np.arange(ds.shape[0])[:, None] + 1)
+        ds, ref = ds[mask], ref[mask]
+    assert np.abs(ds - ref).max() <= 1e-5 * max(1.0, np.abs(ref).max())
+
+
 @pytest.mark.parametrize("name,cfg", SMALL_CASES, ids=[c[0] for c in SMALL_CASES])
 def test_preprocess_bit_exact(name, cfg):
     q, k, v = sy.make_qkv(cfg)
     say(f"quantize {name} B={cfg.B} H={cfg.H} N={cfg.N} M={cfg.M} d={cfg.d}")
     g = gu.quantize(q, k, v, cfg.fp16, cfg.causal, cfg.smooth_v)
-    N, M = cfg.N, cfg.M
     for bh in range(cfg.B * cfg.H):
-        b, h = bh // cfg.H, bh % cfg.H
-        o = oracle.preprocess_head(q[b, h], k[b, h], v[b, h], cfg.fp16,
-                                   oracle.SMOOTH_V if cfg.smooth_v else 0)
-        assert np.array_equal(g["k_mean"][bh].view(np.uint32), o["kmean"].view(np.uint32))
-        assert np.array_equal(g["v_mean"][bh].view(np.uint32), o["vmean"].view(np.uint32))
-        assert np.array_equal(g["q_mean"][bh].view(np.uint32), o["qmean"].view(np.uint32))
-        assert np.array_equal(g["dq"][bh, :N].view(np.uint32), o["dq"].view(np.uint32))
-        assert np.array_equal(g["dk"][bh].view(np.uint32), o["dk"].view(np.uint32))
-        assert np.array_equal(g["dv"][bh].view(np.uint32), o["dv"].view(np.uint32))
-        assert np.array_equal(g["q_hat"][bh, :N], o["qhat"])
-        assert not g["q_hat"][bh, N:].any()
-        assert np.array_equal(g["k_hat"][bh, :M], o["khat"])
-        assert not g["k_hat"][bh, M:].any()
-        assert np.array_equal(g["v_nat"][bh, :M], o["vhat"])
-        assert not g["v_nat"][bh, M:].any()
-        ds, ref = g["delta_s"][bh][:, :M].astype(np.float64), o["ds"]
-        if cfg.causal:
-            # written: the 64-key tiles whose first key is < 128 (i + 1) + coff
-            coff = cfg.M - cfg.N if cfg.causal == 2 else 0
-            tile0 = 64 * (np.arange(M) // 64)
-            mask = tile0[None, :] - coff < 128 * (np.arange(ds.shape[0])[:, None] + 1)
-            ds, ref = ds[mask], ref[mask]
-        assert np.abs(ds - ref).max() <= 1e-5 * max(1.0, np.abs(ref).max())
+        check_preprocess_head(cfg, g, q, k, v, bh)
+
+
+@pytest.mark.parametrize("name,heads", [("n4k", None), ("prefill32k", (0, 31)), ("video17k", (0, 95))])
+def test_preprocess_bit_exact_full_size(name, heads):
+    """The full workload through the same launches as the benchmark's forward (all heads on the
+    GPU): every head of the 4096-token workload, and the first and last heads of the 32768-token
+    prefill (512 K-mean chunks, 256 query blocks, 8 groups of 32 query blocks in the Delta S
+    operand, the causal Delta S of the whole triangle) and of the ragged 17550-token video shape."""
+    cfg = sy.CONFIGS[name]
+    q, k, v = sy.make_qkv(cfg)
+    say(f"quantize full {name} B={cfg.B} H={cfg.H} N={cfg.N} M={cfg.M} d={cfg.d}")
+    g = gu.quantize(q, k, v, cfg.fp16, cfg.causal, cfg.smooth_v)
+    for bh in (range(cfg.B * cfg.H) if heads is None else heads):
+        check_preprocess_head(cfg, g, q, k, v, bh)
 
 
 def check_output(got, ref, exact=None):

@@ -146,3 +146,41 @@ def test_qk_e4m3_rejected_with_mx_and_identity():
     for f in (oracle.MXFP4, oracle.QK_IDENTITY):
         with pytest.raises(ValueError):
             oracle.forward_head(q, q, q, False, 0, 0.1, oracle.QK_E4M3 | f)
+
+
+def qk_margin_case(delta, qk_step_err):
+    """Two rows Q = +-e0 and two keys K = +-e0 (d = 64): the smoothing means are 0, every code is
+    +-448 with the scales 1/448, so each score is +-sm_scale and one step's largest code product
+    is 448^2 for every (row, key).  A score's error bound is then e = qk_step_err x 448^2 x dQ dK x
+    sm_scale (= qk_step_err sm_scale up to the FP32 rounding of 1/448), and the low key of each row
+    has 448 P~ = 448 exp(-2 sm_scale); sm_scale is set so that this is 17 (1 + delta), delta above
+    the E4M3 midpoint between 16 and 18.  That decision's margin is e (the key) + e (the row
+    maximum)."""
+    Q = np.zeros((2, 64)); Q[0, 0], Q[1, 0] = 1.0, -1.0
+    K = Q.copy()
+    V = np.zeros((2, 64)); V[:, 0] = [1.0, 2.0]
+    sm = -math.log(17 * (1 + delta) / 448) / 2
+    out, ties, bound = oracle.forward_head_ties(f16(Q), f16(K), f16(V), True, 0, sm, oracle.QK_E4M3,
+                                                tie_eps=1e-12, qk_step_err=qk_step_err)
+    return ties, 2 * qk_step_err * sm
+
+
+def test_qk_margin_widens_by_the_score_errors():
+    eps = 2.0 ** -10
+    _, e2 = qk_margin_case(0.0, eps)  # twice the per-score bound, for this sm_scale
+    for frac, flagged in ((0.9, 1), (1.1, 0)):
+        ties, e2 = qk_margin_case(frac * e2, eps)
+        assert (ties == flagged).all(), (frac, ties)
+    ties, _ = qk_margin_case(0.5 * e2, 0.0)  # no kernel error model: no margin beyond tie_eps
+    assert (ties == 0).all()
+
+
+@pytest.mark.parametrize("old,new", [
+    ("  return qk_step_err * e * (double)h->dq[r] * (double)h->dk_key[t] * sm_scale;",
+     "  return qk_step_err * e * (double)h->dk_key[t] * sm_scale;"),
+    ("tie_eps + (qk_err ? E[x] + emax : 0.0)", "tie_eps + (qk_err ? E[x] : 0.0)"),
+])
+def test_qk_margin_catches_planted_mistake(old, new):
+    with oracle.planted_mistake(("sage_oracle.c", old, new)):
+        with pytest.raises(AssertionError):
+            test_qk_margin_widens_by_the_score_errors()
