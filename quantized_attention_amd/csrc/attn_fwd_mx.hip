@@ -112,6 +112,25 @@ __device__ __forceinline__ void qk_tile_mx(const uint8_t* __restrict__ sK, const
 constexpr float kLog2_6 = 2.5849625007211562f;  // log2(6)
 constexpr float kP2Span = 64.0f;  // two-level P: level-one reference at most this far (log2) below the max
 
+// max of two values that are not signalling NaNs (scores and their maxima), without the quieting
+// step fmaxf asks the compiler for when an input comes out of a lane exchange
+__device__ __forceinline__ float max2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// E8M0 code (biased exponent) of an MX block whose largest magnitude is 6 * 2^y, from yb = y + 127:
+// the smallest e with 6 * 2^y <= 6 * 2^e is ceil(y), clamped to [-127, 127] and biased by 127, so
+// the code is ceil(yb) clamped to [0, 254]; y = -inf (a fully masked block) gives code 0.
+// Computed on the score arithmetic itself, so the block maximum needs no exp2 of its own; yb
+// carries the FP32 rounding of the score arithmetic and of the bias, a relative 2^-16 at most in
+// 6 * 2^y, the margin within which either exponent is a correct rounding of the method's value.
+__device__ __forceinline__ uint32_t e8m0_code_log2(float yb) {
+  return (uint32_t)__builtin_amdgcn_fmed3f(ceilf(yb), 0.0f, 254.0f);
+}
+constexpr float kBias6 = 127.0f - kLog2_6;  // the bias of e8m0_code_log2 less log2(6)
+
 template <int D, bool CAUSAL, bool ACC_VALU, bool P2L>
 __device__ __forceinline__ void softmax_pv_mx(const v16f (&acc)[2], const uint8_t* __restrict__ sV,
                                               const float* __restrict__ sDS, uint32_t vs, float qk_scale, int h,
@@ -137,20 +156,27 @@ __device__ __forceinline__ void softmax_pv_mx(const v16f (&acc)[2], const uint8_
         sc[T][r] = (32 * T + 8 * (r >> 2) + (r & 3) <= lim) ? sc[T][r] : -INFINITY;
   }
   // ---- running max; each 32-key half's maximum is also its P block's ----
-  float mb[2];
+  // One lane swap of the two halves' partial maxima leaves lane half h with block h's maximum
+  // (its lane pair's), a second one hands it the other block's; no NaN canonicalization is
+  // needed on these values (max3 / med3 below).
+  float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
-  for (int T = 0; T < 2; T++) {
-    float m = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; r++) m = fmaxf(m, sc[T][r]);
-    mb[T] = pair_max(m);
+  for (int r = 0; r < 16; r++) {
+    m0 = fmaxf(m0, sc[0][r]);
+    m1 = fmaxf(m1, sc[1][r]);
   }
-  const float m_tile = fmaxf(mb[0], mb[1]);
+  const auto x1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m0), __float_as_uint(m1), false, false);
+  const float mown = max2(__uint_as_float(x1[0]), __uint_as_float(x1[1]));  // block h
+  const auto x2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mown), __float_as_uint(mown), false, false);
+  const float moth = h ? __uint_as_float(x2[0]) : __uint_as_float(x2[1]);   // block 1 - h
+  const float m_tile = max2(mown, moth);
   const float m_new = fmaxf(m_run, m_tile);  // finite: m_run starts at -FLT_MAX
   const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile, exactly 1 if m is unchanged
   m_run = m_new;
   float base, resc = alpha;  // exponent base of the quantized values; factor on O before the MFMA
-  uint32_t pc0, pc1;
+  // E8M0 codes of the P blocks from the log2 of their largest values, this lane's own block and
+  // the other one (code 0 for a fully masked block)
+  uint32_t pc_own, pc_oth;
   if constexpr (P2L) {
     // Level one: the row's largest P~ of this tile maps to 6.  A row with no visible key in the
     // tile keeps its base (its P2 are 0 and O stays as it is).  The reference of level one is
@@ -158,22 +184,23 @@ __device__ __forceinline__ void softmax_pv_mx(const v16f (&acc)[2], const uint8_
     // below contributes less than 2^-kP2Span of the row's sum (invisible in FP32), and the
     // rescale exp2(b_old - b_new) of O stays below 2^kP2Span, so O never leaves the FP32 range.
     const bool vis = m_tile > -INFINITY;
-    const float bref = fmaxf(m_tile, m_new - kP2Span);
+    const float bref = max2(m_tile, m_new - kP2Span);
     base = vis ? bref - kLog2_6 : b_run;
     resc = fast_exp2(b_run - base);
     b_run = base;
-    // E8M0 of each P2 block: from its largest value 6 exp2(block max - bref), which is exactly 6
-    // for the block holding the row maximum of the tile (bref = m_tile unless clamped)
-    pc0 = vis ? e8m0_code(6.0f * fast_exp2(mb[0] - bref)) : 0u;
-    pc1 = vis ? e8m0_code(6.0f * fast_exp2(mb[1] - bref)) : 0u;
+    // a block's largest P2 is 6 exp2(block max - bref): exactly 6 (code 127) for the block that
+    // holds the tile's row maximum (bref = m_tile unless clamped)
+    pc_own = vis ? e8m0_code_log2((mown - bref) + 127.0f) : 0u;
+    pc_oth = vis ? e8m0_code_log2((moth - bref) + 127.0f) : 0u;
   } else {
     base = m_new;
-    // E8M0 of each P block: from its largest P~ (0 for a fully masked block: code 0)
-    pc0 = e8m0_code(fast_exp2(mb[0] - base));
-    pc1 = e8m0_code(fast_exp2(mb[1] - base));
+    // a block's largest P~ is exp2(block max - base)
+    pc_own = e8m0_code_log2((mown - base) + kBias6);
+    pc_oth = e8m0_code_log2((moth - base) + kBias6);
   }
+  const uint32_t pc0 = h ? pc_oth : pc_own, pc1 = h ? pc_own : pc_oth;
   // ---- P~ (FP32), row sum of the unquantized values, E2M1 pack ----
-  float psum = 0.0f;
+  float psum;
   uint32_t pk[2][2];
 #pragma unroll
   for (int T = 0; T < 2; T++) {
@@ -183,8 +210,11 @@ __device__ __forceinline__ void softmax_pv_mx(const v16f (&acc)[2], const uint8_
       float p[8];
 #pragma unroll
       for (int e = 0; e < 8; e++) p[e] = fast_exp2(sc[T][8 * q + e] - base);
-      psum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-      uint32_t wd = 0;
+      const float g = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+      psum = (T == 0 && q == 0) ? g : psum + g;
+      // each conversion writes one byte of its destination: seed it with a dead register (the
+      // score the first value came from) so that no zeroing move is needed
+      uint32_t wd = __float_as_uint(sc[T][8 * q]);
       wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, p[0], p[1], scl, 0);
       wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, p[2], p[3], scl, 1);
       wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, p[4], p[5], scl, 2);
@@ -202,7 +232,7 @@ __device__ __forceinline__ void softmax_pv_mx(const v16f (&acc)[2], const uint8_
     pk[1][q] = r[1];
   }
   const v4i pf = {(int)pk[0][0], (int)pk[0][1], (int)pk[1][0], (int)pk[1][1]};
-  const uint32_t pcode = h ? pc1 : pc0;
+  const uint32_t pcode = pc_own;
   // ---- O^T += sum_blk X_V X_P (V^T P^T)_blk per 32-channel sub-tile ----
   if (!ACC_VALU) {
     if (__any(resc != 1.0f)) {
