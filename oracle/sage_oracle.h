@@ -122,7 +122,7 @@ int orc_sagebwd_quantize(const uint16_t* q, const uint16_t* k, const uint16_t* v
 int orc_forward_head(const uint16_t* q, const uint16_t* k, const uint16_t* v, int in_fp16,
                      int N, int M, int d, int causal, double sm_scale, unsigned flags,
                      const int* rows, int nrows, double* out);
-/* orc_forward_head, and per output row (each output may be NULL) the number of its P
+/* orc_forward_head, and per output row (ties and bound may each be NULL) the number of its P
  * quantization decisions (E4M3 codes of 448 P~; MX: E2M1 codes and E8M0 block exponents) whose
  * input lies within relative distance tie_eps of a rounding boundary -- a kernel working in
  * FP32 may round those the other way, and either result is a correct rounding -- and a bound
