@@ -51,16 +51,30 @@ VALU_SLOTS_PER_SCORE = {"i8f8": 7.5, "qkfp8": 6.5, "mx": 6.5}
 # the kernel source it was taken on: the hash of that fused kernel's sources is checked,
 # and a changed kernel reports traffic null until the counters are taken again.
 TRAFFIC_BYTES = {
-    "prefill32k": {"source_sha256_16": "a75e0fb6e5de2ed2",
-                   "fetch_bytes": 1803111707, "write_bytes": 271033888},
-    "mxfp4_32k": {"source_sha256_16": "003f5491510e3934",
-                  "fetch_bytes": 1694316556, "write_bytes": 201326899},
+    "prefill32k": {"source_sha256_16": "7046a1c764f322e1",
+                   "fetch_bytes": 1795686080, "write_bytes": 271541312},
+    "mxfp4_32k": {"source_sha256_16": "860c9f1396cf36e7",
+                  "fetch_bytes": 1690066202, "write_bytes": 201326688},
 }
 # SQ counters of the fused attention kernel on the named workload (rocprofv3 --pmc, the summary
-# under profiles/): VALU and matrix-core busy fractions of the SIMD cycles, VALU instructions per
-# (wave, 64-key tile), and the engine clock under that load (GRBM_GUI_ACTIVE cycles over the
-# dispatch's own duration).  Keyed by the same source hash as the traffic; null once stale.
-COUNTERS = {}
+# under profiles/): VALU and matrix-core busy fractions of the SIMD cycles, instructions per
+# (wave, 64-key tile) as SQ_INSTS_VALU (which counts the MFMA instructions too) and
+# SQ_INSTS_MFMA report them, and the engine clock of the profiled dispatch (GRBM_GUI_ACTIVE
+# cycles per XCD over its duration).  Keyed by the same source hash as the traffic; null once stale.
+COUNTERS = {
+    "prefill32k": {"source_sha256_16": "7046a1c764f322e1", "valu_busy": 0.900, "mfma_busy": 0.404,
+                   "valu_insts_per_wave_tile": 235.5, "mfma_insts_per_wave_tile": 12.0,
+                   "clock_ghz_profiled": 1.759, "wave_tiles": 8404992,
+                   "summary": "profiles/attn_fwd_prefill32k_counters.md"},
+    "mxfp4_32k": {"source_sha256_16": "860c9f1396cf36e7", "valu_busy": 0.993, "mfma_busy": 0.231,
+                  "valu_insts_per_wave_tile": 214.0, "mfma_insts_per_wave_tile": 8.0,
+                  "clock_ghz_profiled": 1.934, "wave_tiles": 12582912,
+                  "summary": "profiles/attn_fwd_mx_mxfp4_32k_counters.md"},
+    "video17k": {"source_sha256_16": "7046a1c764f322e1", "valu_busy": 1.047, "mfma_busy": 0.255,
+                 "valu_insts_per_wave_tile": 214.3, "mfma_insts_per_wave_tile": 6.03,
+                 "clock_ghz_profiled": 1.910, "wave_tiles": 14493600,
+                 "summary": "profiles/attn_fwd_video17k_counters.md"},
+}
 _COMMON_SOURCES = ("quantized_attention_amd/csrc/attn_device.hpp", "quantized_attention_amd/csrc/sage_common.hpp")
 KERNEL_SOURCES = {
     False: ("quantized_attention_amd/csrc/attn_fwd.hip",) + _COMMON_SOURCES,    # INT8/FP8 path
