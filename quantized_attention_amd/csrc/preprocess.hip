@@ -18,9 +18,9 @@
 // subtraction of a fixed V_m is monotone, so max |fp32(V - V_m)| = max(fp32(max V - V_m),
 // fp32(V_m - min V)) exactly, and V is read twice, not three times.
 //
-// Launches (all HBM-bound): kv_stats (K, V chunk statistics) and q_prep (Q blocks) read the
-// inputs once; kv_finalize turns chunk statistics into means and the V scale; kv_quant reads
-// K and V once more and writes K^, V^ and Delta S.  Delta S_i[t] = q_i . gamma(K)[t] for one
+// Launches, in order on the caller's stream: stats (one grid: the Q blocks first, then the
+// K / V chunk statistics) reads the inputs once; kv_finalize turns chunk statistics into means
+// and the V scale; kv_quant reads K and V once more and writes K^, V^ and Delta S.  Delta S_i[t] = q_i . gamma(K)[t] for one
 // 64-key tile against every query block is a small GEMM done on the bf16 MFMA with both
 // operands split into a bf16 head and tail (x = hi + lo, exact to 2^-16 relative), three
 // products accumulated in FP32 -- FP32-class accuracy at matrix-core speed.

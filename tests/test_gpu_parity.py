@@ -204,7 +204,7 @@ def test_sm_scale_argument():
 
 
 # ---------------------------------------------------------------- full workload shapes
-FULL = ["n4k", "prefill32k", "full32k", "video17k", "chunk4k_32k"]
+FULL = ["n4k", "prefill32k", "prefill32k_b", "full32k", "video17k", "chunk4k_32k"]
 
 
 def sample_rows(N, seed):
