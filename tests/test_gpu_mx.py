@@ -144,3 +144,21 @@ def test_mx_full_size_sampled():
         err = np.abs(got - ref)
         say(f"  head {bh}: max abs {err.max():.3g}")
         assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS
+
+
+def test_mx_long_sequence_sampled():
+    """One head of 262144 tokens on the MX path (causal, prefill-shaped): Delta S is 2 GiB, so the
+    workspace and tile offsets pass 2^31 bytes; rows at both ends and around the middle."""
+    cfg = sy.CONFIGS["mxfp4_32k"].with_shape(H=1, N=262144, M=262144, causal=1)
+    q, k, v = sy.make_qkv(cfg)
+    say(f"mx long forward N={cfg.N} d={cfg.d} causal={cfg.causal}")
+    out = gu.fwd(q, k, v, cfg.fp16, cfg.causal, None, cfg.smooth_v, mxfp4=True)
+    N = cfg.N
+    rows = np.array(sorted(set([0, 1, 127, 128, N // 2 - 1, N // 2, N - 2, N - 1]
+                               + list(np.random.default_rng(9).integers(0, N, 6)))))
+    got = out[0, 0, torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    ref = oracle.forward_head(q[0, 0], k[0, 0], v[0, 0], cfg.fp16, cfg.causal, 1 / math.sqrt(cfg.d), flags(cfg),
+                              rows=rows)
+    err = np.abs(got - ref)
+    say(f"  max abs {err.max():.3g}")
+    assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS

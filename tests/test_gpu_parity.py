@@ -231,3 +231,28 @@ def test_full_size_sampled(name):
         ex = oracle.exact_head(q[b, h], k[b, h], v[b, h], cfg.fp16, cfg.causal, s, rows=rows)
         say(f"  head {bh}: max abs {np.abs(got - ref).max():.3g}")
         check_output(got, ref, ex)
+
+
+# ---------------------------------------------------------------- the longest sequences
+# One head of 262144 tokens: Delta S alone is 2 GiB (2048 query blocks x 262144 keys x 4 bytes),
+# so every byte offset of the workspace and of the tiles passes 2^31; the rows sampled include
+# both ends of the sequence and of the blocks around its middle.
+LONG = [
+    ("long256k-causal", sy.CONFIGS["prefill32k"].with_shape(H=1, N=262144, M=262144)),
+    ("long256k-d64-smoothv", sy.CONFIGS["video17k"].with_shape(B=1, H=1, N=262144, M=262144)),
+]
+
+
+@pytest.mark.parametrize("name,cfg", LONG, ids=[n for n, _ in LONG])
+def test_long_sequence_sampled(name, cfg):
+    q, k, v = sy.make_qkv(cfg)
+    say(f"long forward {name} N={cfg.N} d={cfg.d} causal={cfg.causal}")
+    out = gu.fwd(q, k, v, cfg.fp16, cfg.causal, None, cfg.smooth_v)
+    N = cfg.N
+    rows = np.array(sorted(set([0, 1, 127, 128, N // 2 - 1, N // 2, N - 129, N - 128, N - 2, N - 1]
+                               + list(np.random.default_rng(7).integers(0, N, 6)))))
+    got = out[0, 0, torch.from_numpy(rows).cuda()].cpu().numpy().astype(np.float64)
+    ref = oracle_head(cfg, q, k, v, 0, rows=rows)
+    ex = oracle.exact_head(q[0, 0], k[0, 0], v[0, 0], cfg.fp16, cfg.causal, 1 / math.sqrt(cfg.d), rows=rows)
+    say(f"  max abs {np.abs(got - ref).max():.3g}")
+    check_output(got, ref, ex)
