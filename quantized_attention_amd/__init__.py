@@ -216,6 +216,19 @@ def sage_attn_version() -> int:
 
 
 # ---------------------------------------------------------------- torch convenience
+def _check_out(out, shape, dtype):
+    """A caller's output buffer must be exactly what the library writes (shape and dtype)."""
+    if tuple(out.shape) != tuple(shape) or out.dtype != dtype:
+        raise ValueError(f"out must be {tuple(shape)} of {dtype}, got {tuple(out.shape)} of {out.dtype}")
+
+
+def _check_device(ts, device):
+    """Every tensor the library reads or writes: contiguous, on the GPU, on q's device."""
+    for t in ts:
+        if not t.is_cuda or not t.is_contiguous() or t.device != device:
+            raise ValueError("tensors must be contiguous device tensors on q's device")
+
+
 def _variant_for(q, smooth_v: bool, out_fp32: bool, acc_valu: bool = False, mxfp4: bool = False,
                  qk_fp8: bool = False, mx_p_two_level: bool = False) -> int:
     import torch
@@ -264,16 +277,18 @@ def sage_attn(q, k, v, causal: bool = False, sm_scale: float | None = None, smoo
         raise ValueError("the query heads must be a multiple of the key/value heads")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share a dtype")
-    for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous device tensors")
+    out_dtype = torch.float32 if out_fp32 else q.dtype
+    if out is not None:
+        _check_out(out, (B, H, N, d), out_dtype)
+    _check_device((q, k, v) if out is None else (q, k, v, out), q.device)
     var = _variant_for(q, smooth_v, out_fp32, acc_valu, mxfp4, qk_fp8, mx_p_two_level)
     if out is None:
-        out = torch.empty((B, H, N, d), dtype=torch.float32 if out_fp32 else q.dtype, device=q.device)
+        out = torch.empty((B, H, N, d), dtype=out_dtype, device=q.device)
     scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(d)
-    stream = torch.cuda.current_stream(q.device).cuda_stream
     shape = SageAttnShape(B, H, Hkv, N, M, d, int(causal), scale, var)
-    rc = sage_attn_fwd_ex(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), None, 0, stream)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = sage_attn_fwd_ex(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), None, 0, stream)
     if rc != SAGE_OK:
         raise SageError(rc, "sage_attn_fwd_ex")
     return out
@@ -300,23 +315,26 @@ def sage_attn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max
         raise ValueError("the query heads must be a multiple of the key/value heads")
     if not (q.dtype == k.dtype == v.dtype):
         raise TypeError("q, k, v must share a dtype")
-    for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("q, k, v must be contiguous device tensors")
     for c in (cu_seqlens_q, cu_seqlens_k):
-        if c.dtype != torch.int32 or not c.is_cuda or not c.is_contiguous() or c.dim() != 1:
-            raise ValueError("cu_seqlens must be contiguous int32 device vectors")
+        if c.dtype != torch.int32 or c.dim() != 1:
+            raise ValueError("cu_seqlens must be int32 vectors")
     batch = cu_seqlens_q.numel() - 1
     if batch < 1 or cu_seqlens_k.numel() != batch + 1:
         raise ValueError("cu_seqlens_q and cu_seqlens_k must hold batch + 1 offsets")
+    out_dtype = torch.float32 if out_fp32 else q.dtype
+    if out is not None:
+        _check_out(out, (total_q, H, d), out_dtype)
+    _check_device((q, k, v, cu_seqlens_q, cu_seqlens_k) + (() if out is None else (out,)), q.device)
     var = _variant_for(q, smooth_v, out_fp32, False, mxfp4, qk_fp8)
     if out is None:
-        out = torch.empty((total_q, H, d), dtype=torch.float32 if out_fp32 else q.dtype, device=q.device)
+        out = torch.empty((total_q, H, d), dtype=out_dtype, device=q.device)
     scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(d)
     shape = SageAttnVarlenShape(batch, H, Hkv, d, total_q, total_k, int(max_seqlen_q), int(max_seqlen_k),
                                 cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), int(causal), scale, var)
-    stream = torch.cuda.current_stream(q.device).cuda_stream
-    rc = sage_attn_varlen_fwd(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), None, 0, stream)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = sage_attn_varlen_fwd(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), None, 0,
+                                  stream)
     if rc != SAGE_OK:
         raise SageError(rc, "sage_attn_varlen_fwd")
     return out
@@ -349,9 +367,7 @@ def _check_train_inputs(*ts):
             raise TypeError("q, k, v, dout must be bf16 or fp16")
     if len({t.dtype for t in ts}) != 1:
         raise TypeError("q, k, v, dout must share a dtype")
-    for t in ts:
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("tensors must be contiguous device tensors")
+    _check_device(ts, ts[0].device)
 
 
 def sage_attn_train_forward(q, k, v, causal: int = 0, sm_scale: float | None = None, out_fp32: bool = False,
@@ -363,9 +379,10 @@ def sage_attn_train_forward(q, k, v, causal: int = 0, sm_scale: float | None = N
     B, H, N, d = q.shape
     out = torch.empty((B, H, N, d), dtype=torch.float32 if out_fp32 else q.dtype, device=q.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    stream = torch.cuda.current_stream(q.device).cuda_stream
-    rc = sage_attn_train_fwd(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), None,
-                             0, stream)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = sage_attn_train_fwd(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                 None, 0, stream)
     if rc != SAGE_OK:
         raise SageError(rc, "sage_attn_train_fwd")
     return out, lse
@@ -384,15 +401,14 @@ def sage_attn_train_backward(q, k, v, out, dout, lse, causal: int = 0, sm_scale:
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N):
         raise ValueError("lse must be float32 [B, H, N]")
     _check_train_inputs(q, k, v, dout)
-    for t in (out, lse):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("tensors must be contiguous device tensors")
+    _check_device((out, lse), q.device)
     dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
     dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
-    stream = torch.cuda.current_stream(q.device).cuda_stream
-    rc = sage_attn_train_bwd(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
-                             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), None, 0, stream)
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        rc = sage_attn_train_bwd(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
+                                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), None, 0, stream)
     if rc != SAGE_OK:
         raise SageError(rc, "sage_attn_train_bwd")
     return dq, dk, dv

@@ -186,3 +186,28 @@ def test_noalloc_rejects_problems_beyond_its_scratch():
     assert qa.sage_attn_fwd_noalloc(None, A, A, A, A, None) == qa.SAGE_ERR_INVALID_ARG
     small = S(1, 2, 2, 256, 256, 64, 0, 0.0, 0)
     assert qa.sage_attn_fwd_noalloc(small, 0, A, A, A, None) == qa.SAGE_ERR_INVALID_ARG
+
+
+def test_forward_bindings_check_a_caller_output_buffer():
+    """A caller's out must have the shape and dtype the library writes; the check comes before
+    the device checks, so host tensors show it."""
+    import torch
+    bf = torch.bfloat16
+    q = torch.zeros(1, 4, 64, 64, dtype=bf)
+    kv = torch.zeros(1, 2, 96, 64, dtype=bf)
+    for bad in (torch.zeros(1, 4, 64, 32, dtype=bf), torch.zeros(1, 4, 65, 64, dtype=bf),
+                torch.zeros(1, 4, 64, 64, dtype=torch.float16), torch.zeros(1, 4, 64, 64, dtype=torch.float32)):
+        with pytest.raises(ValueError):
+            qa.sage_attn(q, kv, kv, out=bad)
+    with pytest.raises(ValueError):  # fp32 requested, bf16 given
+        qa.sage_attn(q, kv, kv, out_fp32=True, out=torch.zeros(1, 4, 64, 64, dtype=bf))
+    qv = torch.zeros(100, 4, 64, dtype=bf)
+    kvv = torch.zeros(120, 2, 64, dtype=bf)
+    cu = torch.tensor([0, 40, 100], dtype=torch.int32)
+    cuk = torch.tensor([0, 50, 120], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        qa.sage_attn_varlen(qv, kvv, kvv, cu, cuk, 60, 70, out=torch.zeros(99, 4, 64, dtype=bf))
+    with pytest.raises(ValueError):  # right shapes, host tensors
+        qa.sage_attn_varlen(qv, kvv, kvv, cu, cuk, 60, 70)
+    with pytest.raises(ValueError):
+        qa.sage_attn(q, kv, kv)
