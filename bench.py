@@ -195,7 +195,7 @@ def cpu_baseline(cfg, budget_s: float) -> dict:
     flags = (oracle.SMOOTH_V if cfg.smooth_v else 0) | (oracle.MXFP4 if cfg.mxfp4 else 0)
     flags |= oracle.QK_E4M3 if cfg.qk_fp8 else 0
     flags |= oracle.MX_P_TWO_LEVEL if cfg.mx_p_two_level else 0
-    ops, t_used, nrows, batch = 0.0, 0.0, 0, 8
+    ops, t_used, nrows, batch, ncalls = 0.0, 0.0, 0, 8, 0
     while t_used < budget_s:
         rows = np.sort(rng.integers(0, cfg.N, batch))
         t0 = time.perf_counter()
@@ -203,13 +203,15 @@ def cpu_baseline(cfg, budget_s: float) -> dict:
         dt = time.perf_counter() - t0
         t_used += dt
         nrows += batch
+        ncalls += 1
         coff = cfg.M - cfg.N if cfg.causal == 2 else 0
         ops += sum(4.0 * cfg.d * (min(cfg.M, int(r) + coff + 1) if cfg.causal else cfg.M) for r in rows)
         if dt < budget_s / 8:
-            batch *= 2
+            batch = min(2 * batch, cfg.N)
     return {"value": ops / t_used / 1e12, "unit": "TOPS", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"head 0 of {cfg.B * cfg.H}, {nrows} seeded random query rows of N={cfg.N} "
-                      f"(per-head preprocessing and Delta S rows included), {t_used:.1f} s",
+            "sample": f"head 0 of {cfg.B * cfg.H}: {ncalls} oracle calls on seeded random query rows of "
+                      f"N={cfg.N} ({nrows} rows in all, drawn with replacement; every call includes the head's "
+                      f"preprocessing and its Delta S rows), {t_used:.1f} s",
             "omp_threads": oracle.num_threads(), **host_info()}
 
 
