@@ -256,3 +256,62 @@ def test_long_sequence_sampled(name, cfg):
     ex = oracle.exact_head(q[0, 0], k[0, 0], v[0, 0], cfg.fp16, cfg.causal, 1 / math.sqrt(cfg.d), rows=rows)
     say(f"  max abs {np.abs(got - ref).max():.3g}")
     check_output(got, ref, ex)
+
+
+# ---------------------------------------------------------------- degenerate inputs
+# Inputs where the quantizers meet their edge cases: every scale at its floor (all zeros), gamma(K)
+# exactly 0 (all keys equal: K^ = 0, Delta S = 0, every visible score equal), gamma(Q) and the
+# block means 0 (Q = 0: the same uniform rows), and V' exactly 0 (every value row equal, with V
+# smoothing: the output is V_m itself).  Each path is compared with the oracle; the zeros case
+# must give exact zeros and the constant-value case with smoothing exactly the value row.
+DEGENERATE = ["zeros", "equal_keys", "zero_queries", "constant_values"]
+PATHS = {"int8": {}, "mxfp4": {"mxfp4": True}, "qk_fp8": {"qk_fp8": True}}
+
+
+def degenerate_inputs(kind, N, M, d, seed):
+    rng = np.random.default_rng(seed)
+    Q = rng.standard_normal((N, d)) + rng.standard_normal(d)
+    K = rng.standard_normal((M, d)) + 3.0 * rng.standard_normal(d)
+    V = rng.standard_normal((M, d)) + 0.5 * rng.standard_normal(d)
+    if kind == "zeros":
+        Q[:], K[:], V[:] = 0.0, 0.0, 0.0
+    elif kind == "equal_keys":
+        K[:] = K[0]
+    elif kind == "zero_queries":
+        Q[:] = 0.0
+    elif kind == "constant_values":
+        V[:] = V[0]
+    bits = [sy.f32_to_bf16_bits(x.astype(np.float32))[None, None] for x in (Q, K, V)]
+    return bits
+
+
+@pytest.mark.parametrize("path", sorted(PATHS))
+@pytest.mark.parametrize("kind", DEGENERATE)
+def test_degenerate_inputs(kind, path):
+    """Against the oracle with the bars of each path: mean <= 1e-3 and every row within 1e-2 plus
+    the oracle's bound for its P rounding decisions near a boundary (with the FP8 matrix core's
+    score error on the E4M3-QK path)."""
+    from tests.test_gpu_probes import FP8_MFMA_STEP_ERR
+    N, M, d = 300, 333, 128
+    q, k, v = degenerate_inputs(kind, N, M, d, 91)
+    s = 1 / math.sqrt(d)
+    flags_of = {"int8": 0, "mxfp4": oracle.MXFP4, "qk_fp8": oracle.QK_E4M3}
+    for causal in (0, 1):
+        for smooth_v in (False, True):
+            say(f"degenerate {kind} path={path} causal={causal} smooth_v={smooth_v}")
+            got = gu.fwd(q, k, v, False, causal, None, smooth_v, **PATHS[path])[0, 0].cpu().numpy().astype(np.float64)
+            ref, _, bound = oracle.forward_head_ties(
+                q[0, 0], k[0, 0], v[0, 0], False, causal, s, flags_of[path] | (oracle.SMOOTH_V if smooth_v else 0),
+                qk_step_err=FP8_MFMA_STEP_ERR if path == "qk_fp8" else 0.0)
+            err = np.abs(got - ref)
+            row = err.max(axis=1)
+            say(f"  max abs {err.max():.3g}; rows with a margin {(bound > 0).sum()}; "
+                f"worst beyond 1e-2 + margin {(row - MAX_ABS - bound).max():.3g}")
+            assert np.isfinite(got).all()
+            assert err.mean() <= MEAN_ABS
+            assert (row <= MAX_ABS + bound).all()
+            if kind == "zeros":
+                assert (got == 0.0).all()
+            if kind == "constant_values" and smooth_v:
+                row_v = sy.bits_to_f32(v[0, 0, 0], False).astype(np.float64)
+                assert (got == row_v[None, :]).all()
