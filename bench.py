@@ -42,8 +42,10 @@ PEAK_VALU_TSLOTS = 256 * 4 * 16 * 2.4e9 / 1e12
 # gfx950 instructions that carry them out (INT8 path: convert the INT32 score, one FMA for
 # dequantization and Delta S, half a v_max3 for the row max, the subtraction of the running
 # max, exp2 (2 slots), the row sum, half of a two-value FP8 pack (2 slots); E4M3 QK: no
-# convert; MX: no convert, the FP4 pack of two values per instruction).
-VALU_SLOTS_PER_SCORE = {"i8f8": 7.5, "qkfp8": 6.5, "mx": 6.5}
+# convert; MX: no convert and no dequantization (the block scales and Delta S are summed by
+# the matrix core), one FMA for sm_scale log2(e) and the running max, the FP4 pack of two
+# values per instruction).
+VALU_SLOTS_PER_SCORE = {"i8f8": 7.5, "qkfp8": 6.5, "mx": 5.5}
 
 # Kernel-level HBM traffic of the fused attention kernel, one launch on the named workload:
 # rocprofv3 --pmc FETCH_SIZE and --pmc WRITE_SIZE (KiB per dispatch) scaled by what the same

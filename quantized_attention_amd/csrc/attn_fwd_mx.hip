@@ -16,7 +16,9 @@
 // v_mfma_scale_f32_32x32x64_f8f6f4 with both operands E2M1 (64 channels per instruction,
 // each lane half a 32-channel block whose E8M0 scale the lane supplies: byte-selected from
 // one scale word per tile for K, per kernel for Q).  The block scales are applied inside
-// the MFMA, so the FP32 scores need one FMA (sm_scale log2 e, Delta S) and no dequant.
+// the MFMA, and so is Delta S: the QK accumulator starts from the tile's (unscaled) Delta S,
+// which the matrix core adds at FP32.  The FP32 score then needs no dequant, and the factor
+// sm_scale log2 e and the running max meet in the exponent's one FMA: exp2(s c - base).
 // The P~ block of a row is 32 contiguous keys: its maximum is exp2 of the block's largest
 // score (the same exp2 the element gets), which sets the E8M0 scale; the hardware
 // conversion takes that scale directly (v_cvt_scalef32_pk_fp4_f32 divides by the power of
@@ -71,7 +73,7 @@ struct MxArgs {
   const uint8_t* ksc;   // [BH][nkt][64][4]
   const uint8_t* vsc;   // [BH][nkt][64][4]
   const float* vmean;
-  const float* ds;      // Delta S * sm_scale * log2(e)
+  const float* ds;      // Delta S (unscaled)
   void* out;
   int BH, nqb, nkt, Np, Mp;  // bounds: padded workspace strides
   int causal2;      // causal = 2: key t visible to query r iff t <= r + M - N (else t <= r)
@@ -91,16 +93,18 @@ __device__ __forceinline__ v16f mfma_fp4(const v4i& a, const v4i& b, const v16f&
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, b8, c, 4, 4, OA, (int)sa, OB, (int)sb);
 }
 
-// S^T = sum_blk X_K X_Q (K^ Q^T)_blk of one 64-key tile: two 32-key halves, D/64 MFMAs each.
-// The K scale word of lane l holds byte 2T + c for key 32T + l%32, channel block 2c + l/32;
-// the Q scale word byte c for channel block 2c + l/32.
+// S^T = Delta S + sum_blk X_K X_Q (K^ Q^T)_blk of one 64-key tile (before sm_scale): two 32-key
+// halves, D/64 MFMAs each; the accumulator starts from the tile's Delta S (unscaled), which the
+// matrix core adds at FP32.  The K scale word of lane l holds byte 2T + c for key 32T + l%32,
+// channel block 2c + l/32; the Q scale word byte c for channel block 2c + l/32.
 template <int D>
-__device__ __forceinline__ void qk_tile_mx(const uint8_t* __restrict__ sK, const v4i (&qf)[D / 64], uint32_t ks,
-                                           uint32_t qs, int h, int col, v16f (&acc)[2]) {
+__device__ __forceinline__ void qk_tile_mx(const uint8_t* __restrict__ sK, const float* __restrict__ sDS,
+                                           const v4i (&qf)[D / 64], uint32_t ks, uint32_t qs, int h, int col,
+                                           v16f (&acc)[2]) {
   static_for<0, 2>([&](auto Tc) {
     constexpr int T = decltype(Tc)::value;
 #pragma unroll
-    for (int r = 0; r < 16; r++) acc[T][r] = 0.0f;
+    for (int r = 0; r < 16; r++) acc[T][r] = sDS[32 * T + 8 * (r >> 2) + 4 * h + (r & 3)];
     static_for<0, D / 64>([&](auto Cc) {
       constexpr int C = decltype(Cc)::value;
       const v4i kf = *reinterpret_cast<const v4i*>(&sK[MxTiles<D>::koff(32 * T + col, 2 * C + h)]);
@@ -133,17 +137,17 @@ constexpr float kBias6 = 127.0f - kLog2_6;  // the bias of e8m0_code_log2 less l
 
 template <int D, bool CAUSAL, bool ACC_VALU, bool P2L>
 __device__ __forceinline__ void softmax_pv_mx(const v16f (&acc)[2], const uint8_t* __restrict__ sV,
-                                              const float* __restrict__ sDS, uint32_t vs, float qk_scale, int h,
+                                              uint32_t vs, float qk_scale, int h,
                                               int col, int key0, int qrow, int M, bool masked, v16f (&O)[D / 32],
                                               float& m_run, float& l_run, float& b_run) {
   static_assert(!(P2L && ACC_VALU), "two-level P accumulates through the C operand");
-  // ---- scores: sm_scale log2(e) and Delta S (the block scales were applied by the MFMA) ----
+  // ---- scores before sm_scale log2(e): the block scales and Delta S are in the MFMA's sums;
+  // the factor joins the base in one FMA per score (exp2 argument = sc * qk_scale - base) ----
   float sc[2][16];
 #pragma unroll
   for (int T = 0; T < 2; T++)
 #pragma unroll
-    for (int r = 0; r < 16; r++)
-      sc[T][r] = fmaf(acc[T][r], qk_scale, sDS[32 * T + 8 * (r >> 2) + 4 * h + (r & 3)]);
+    for (int r = 0; r < 16; r++) sc[T][r] = acc[T][r];
   if (masked) {
     asm volatile("" ::: "memory");  // keep this a real branch (interior tiles skip it)
     int lim = M - 1 - key0;
@@ -166,9 +170,12 @@ __device__ __forceinline__ void softmax_pv_mx(const v16f (&acc)[2], const uint8_
     m1 = fmaxf(m1, sc[1][r]);
   }
   const auto x1 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m0), __float_as_uint(m1), false, false);
-  const float mown = max2(__uint_as_float(x1[0]), __uint_as_float(x1[1]));  // block h
-  const auto x2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mown), __float_as_uint(mown), false, false);
-  const float moth = h ? __uint_as_float(x2[0]) : __uint_as_float(x2[1]);   // block 1 - h
+  const float mraw = max2(__uint_as_float(x1[0]), __uint_as_float(x1[1]));  // block h
+  const auto x2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mraw), __float_as_uint(mraw), false, false);
+  // the two blocks' maxima in log2 units (rounded products, so that the tile maximum equals
+  // its block's maximum exactly)
+  const float mown = mraw * qk_scale;                                                  // block h
+  const float moth = (h ? __uint_as_float(x2[0]) : __uint_as_float(x2[1])) * qk_scale;  // block 1 - h
   const float m_tile = max2(mown, moth);
   const float m_new = fmaxf(m_run, m_tile);  // finite: m_run starts at -FLT_MAX
   const float alpha = fast_exp2(m_run - m_new);  // 0 on the first tile, exactly 1 if m is unchanged
@@ -209,7 +216,7 @@ __device__ __forceinline__ void softmax_pv_mx(const v16f (&acc)[2], const uint8_
     for (int q = 0; q < 2; q++) {
       float p[8];
 #pragma unroll
-      for (int e = 0; e < 8; e++) p[e] = fast_exp2(sc[T][8 * q + e] - base);
+      for (int e = 0; e < 8; e++) p[e] = fast_exp2(fmaf(sc[T][8 * q + e], qk_scale, -base));
       const float g = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
       psum = (T == 0 && q == 0) ? g : psum + g;
       // each conversion writes one byte of its destination: seed it with a dead register (the
@@ -369,8 +376,8 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 3) void attn_fwd_mx_kernel(MxArg
       const int key0 = j * kBK;
       const bool masked = (CAUSAL && key0 + kBK - 1 > wq0 + coff) || (key0 + kBK > mseq);
       v16f acc[2];
-      qk_tile_mx<D>(sK[b], qf, sKS[b][lane], qs, h, col, acc);
-      softmax_pv_mx<D, CAUSAL, ACC_VALU, P2L>(acc, sV[b], sDS[b], sVS[b][lane], a.qk_scale, h, col, key0,
+      qk_tile_mx<D>(sK[b], sDS[b], qf, sKS[b][lane], qs, h, col, acc);
+      softmax_pv_mx<D, CAUSAL, ACC_VALU, P2L>(acc, sV[b], sVS[b][lane], a.qk_scale, h, col, key0,
                                               qrow + coff, mseq, masked, O, m_run, l_run, b_run);
     }
     publish();

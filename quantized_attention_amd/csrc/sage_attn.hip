@@ -194,7 +194,9 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, const Probl
   carve_workspace(p, ws, &w);
   hipEvent_t e0 = t_prof_start, e1 = t_prof_stop;
   t_prof_start = t_prof_stop = nullptr;
-  int rc = run_preprocess(p, q, k, v, w, p.sm_scale * 1.4426950408889634f, w.ds, s);
+  // the MX kernel adds Delta S through its matrix core's accumulator, before sm_scale log2(e);
+  // the INT8/FP8 kernel adds it in its dequantizing FMA, scaled
+  int rc = run_preprocess(p, q, k, v, w, p.mx ? 1.0f : p.sm_scale * 1.4426950408889634f, w.ds, s);
   if (rc != SAGE_OK) return rc;
   if (e0 && hipEventRecord(e0, s) != hipSuccess) return SAGE_ERR_LAUNCH;
   if ((p.mx ? launch_attn_fwd_mx(p, w, out, s) : launch_attn_fwd(p, w, out, s)) != hipSuccess)
