@@ -55,8 +55,8 @@ VALU_SLOTS_PER_SCORE = {"i8f8": 7.5, "qkfp8": 6.5, "mx": 5.5}
 TRAFFIC_BYTES = {
     "prefill32k": {"source_sha256_16": "7046a1c764f322e1",
                    "fetch_bytes": 1795686080, "write_bytes": 271541312},
-    "mxfp4_32k": {"source_sha256_16": "860c9f1396cf36e7",
-                  "fetch_bytes": 1690066202, "write_bytes": 201326688},
+    "mxfp4_32k": {"source_sha256_16": "665e9983665ee70d",
+                  "fetch_bytes": 1689161493, "write_bytes": 201327072},
 }
 # SQ counters of the fused attention kernel on the named workload (rocprofv3 --pmc, the summary
 # under profiles/): VALU and matrix-core busy fractions of the SIMD cycles, instructions per
@@ -68,9 +68,9 @@ COUNTERS = {
                    "valu_insts_per_wave_tile": 235.5, "mfma_insts_per_wave_tile": 12.0,
                    "clock_ghz_profiled": 1.759, "wave_tiles": 8404992,
                    "summary": "profiles/attn_fwd_prefill32k_counters.md"},
-    "mxfp4_32k": {"source_sha256_16": "860c9f1396cf36e7", "valu_busy": 0.993, "mfma_busy": 0.231,
-                  "valu_insts_per_wave_tile": 214.0, "mfma_insts_per_wave_tile": 8.0,
-                  "clock_ghz_profiled": 1.934, "wave_tiles": 12582912,
+    "mxfp4_32k": {"source_sha256_16": "665e9983665ee70d", "valu_busy": 0.931, "mfma_busy": 0.242,
+                  "valu_insts_per_wave_tile": 185.0, "mfma_insts_per_wave_tile": 8.0,
+                  "clock_ghz_profiled": 1.965, "wave_tiles": 12582912,
                   "summary": "profiles/attn_fwd_mx_mxfp4_32k_counters.md"},
     "video17k": {"source_sha256_16": "7046a1c764f322e1", "valu_busy": 1.047, "mfma_busy": 0.255,
                  "valu_insts_per_wave_tile": 214.3, "mfma_insts_per_wave_tile": 6.03,
