@@ -70,8 +70,9 @@ struct StatsArgs {
   float2* vmm;
   SeqLayout ql, kl;
   int H, Hkv, Np, nqb, nkt;
-  int nq_blocks;  // work-groups of the Q side (0: statistics only), placed first in the grid
+  int nq_blocks;  // work-groups of the Q side (0: statistics only), interleaved with the K / V side
   int nkv_x;      // work-groups of the K / V side per key/value head
+  int nkv_total;  // work-groups of the K / V side
   bool fp16, smooth_v;
 };
 
@@ -359,18 +360,26 @@ __device__ __forceinline__ void q_prep_block(const StatsArgs& a, int i, int bh) 
   }
 }
 
-// ---- the first preprocessing launch: the Q blocks (work-groups [0, nq_blocks)) and the K / V
-// chunk statistics (the rest) side by side.  Neither needs the other, and both are bound by
-// HBM reads, so one grid keeps the memory system busy with both ----
+// ---- the first preprocessing launch: the Q blocks and the K / V chunk statistics side by side.
+// Neither needs the other; the two kinds are interleaved in the grid (alternately, while both
+// last) so that the CUs run both at once: the Q blocks wait on their serial block-mean chains,
+// the K / V blocks stream ----
 template <int D, bool MX, bool F8>
 __global__ __launch_bounds__(256) void stats_kernel(StatsArgs a) {
   const int x = blockIdx.x;
-  if (x < a.nq_blocks) {
-    q_prep_block<D, MX, F8>(a, x % a.nqb, x / a.nqb);
+  const int nkv = a.nkv_total;
+  const int both = 2 * min(a.nq_blocks, nkv);  // [0, both): even x a Q block, odd x a K / V block
+  int qi = -1, kvi = -1;
+  if (x < both) {
+    if (x & 1) kvi = x >> 1;
+    else qi = x >> 1;
+  } else if (a.nq_blocks > nkv) {
+    qi = x - nkv;
   } else {
-    const int y = x - a.nq_blocks;
-    kv_stats_block<D>(a, y % a.nkv_x, y / a.nkv_x);
+    kvi = x - a.nq_blocks;
   }
+  if (qi >= 0) q_prep_block<D, MX, F8>(a, qi % a.nqb, qi / a.nqb);
+  else kv_stats_block<D>(a, kvi % a.nkv_x, kvi / a.nkv_x);
 }
 
 struct KVArgs {
@@ -681,6 +690,7 @@ hipError_t launch_stats(const Problem& p, const void* q, const void* k, const vo
   a.smooth_v = p.smooth_v;
   const long long blocks = (long long)a.nq_blocks + (long long)a.nkv_x * p.BHkv;
   if (blocks >= (1LL << 31)) return hipErrorInvalidConfiguration;
+  a.nkv_total = a.nkv_x * p.BHkv;
   const dim3 grid((unsigned)blocks);
   auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, a); };
   if (p.d == 128)
