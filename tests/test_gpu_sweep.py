@@ -111,3 +111,63 @@ def test_sweep(i):
     say(f"  max abs {err.max():.3g}, mean abs {err.mean():.3g}, worst row beyond 1e-2 + margin {worst:.3g}")
     assert err.mean() <= MEAN_ABS
     assert worst <= 0.0
+
+
+# ---- SageBwd (sage_attn_train_forward / _backward): the same kind of draws, ungrouped heads ----
+N_TRAIN = 16
+
+
+def draw_train_case(i):
+    rng = np.random.default_rng(20261203 + i)
+    d = int(rng.choice([64, 128]))
+    B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+    causal = int(rng.integers(0, 3))
+    M = _length(rng, 64)
+    N = _length(rng, 128)
+    if causal == 2 and N > M:
+        N = max(1, M - int(rng.integers(0, min(M, 200))))
+    dist = sy.Dist(q_off_std=float(rng.uniform(0, 2)), k_off_std=float(rng.uniform(0, 6)),
+                   k_spike=float(rng.choice([0.0, 8.0])), k_spike_channels=sy.spike_channels(d),
+                   v_bias_std=float(rng.uniform(0, 1)))
+    cfg = sy.Config(f"train_sweep{i}", B, H, N, M, d, str(rng.choice(["bf16", "fp16"])), causal, dist, 2000 + i)
+    return cfg, bool(rng.integers(4) > 0)
+
+
+TRAIN_CASES = [draw_train_case(i) for i in range(N_TRAIN)]
+
+
+@pytest.mark.parametrize("i", range(N_TRAIN), ids=[f"train{i}" for i in range(N_TRAIN)])
+def test_train_sweep(i):
+    """Forward: out within 1e-2 max / 1e-3 mean of the oracle, lse within 1e-4.  Backward: dQ, dK,
+    dV within 1e-2 max(1, max |ref|) and 1e-3 max(1, mean |ref|) (the SageBwd bars)."""
+    import quantized_attention_amd as qa
+    cfg, smooth_k = TRAIN_CASES[i]
+    say(f"train sweep case {i}: B={cfg.B} H={cfg.H} N={cfg.N} M={cfg.M} d={cfg.d} causal={cfg.causal} "
+        f"{cfg.dtype} smooth_k={smooth_k}")
+    q, k, v = sy.make_qkv(cfg)
+    rng = np.random.default_rng(3000 + i)
+    x = rng.standard_normal(q.shape).astype(np.float32)
+    do = x.astype(np.float16).view(np.uint16) if cfg.fp16 else sy.f32_to_bf16_bits(x)
+    tq, tk, tv, tdo = (gu.to_dev(a, cfg.fp16) for a in (q, k, v, do))
+    out, lse = qa.sage_attn_train_forward(tq, tk, tv, cfg.causal, None, out_fp32=True, smooth_k=smooth_k)
+    dq, dk, dv = qa.sage_attn_train_backward(tq, tk, tv, out, tdo, lse, cfg.causal, None, smooth_k=smooth_k)
+    torch.cuda.synchronize()
+    got = {"out": out.cpu().numpy(), "lse": lse.cpu().numpy(), "dq": dq.cpu().numpy(),
+           "dk": dk.cpu().numpy(), "dv": dv.cpu().numpy()}
+    s = 1 / math.sqrt(cfg.d)
+    flags = 0 if smooth_k else oracle.SB_NO_SMOOTH_K
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            ro, rl = oracle.sagebwd_forward(q[b, h], k[b, h], v[b, h], cfg.fp16, cfg.causal, s, flags)
+            eo = np.abs(got["out"][b, h].astype(np.float64) - ro)
+            el = np.abs(got["lse"][b, h].astype(np.float64) - rl)
+            assert np.isfinite(got["out"][b, h]).all() and np.isfinite(got["lse"][b, h]).all()
+            assert eo.max() <= MAX_ABS and eo.mean() <= MEAN_ABS, (b, h, eo.max(), eo.mean())
+            assert el.max() <= 1e-4, (b, h, el.max())
+            ref = oracle.sagebwd_backward(q[b, h], k[b, h], v[b, h], do[b, h], cfg.fp16, cfg.causal, s, flags)
+            for nm in ("dq", "dk", "dv"):
+                g = got[nm][b, h].astype(np.float64)
+                e = np.abs(g - ref[nm])
+                assert np.isfinite(g).all(), nm
+                assert e.max() <= 1e-2 * max(1.0, np.abs(ref[nm]).max()), (nm, b, h, e.max())
+                assert e.mean() <= 1e-3 * max(1.0, np.abs(ref[nm]).mean()), (nm, b, h, e.mean())
