@@ -66,15 +66,18 @@ TRAFFIC_BYTES = {
 COUNTERS = {
     "prefill32k": {"source_sha256_16": "7046a1c764f322e1", "valu_busy": 0.900, "mfma_busy": 0.404,
                    "valu_insts_per_wave_tile": 235.5, "mfma_insts_per_wave_tile": 12.0,
-                   "clock_ghz_profiled": 1.759, "wave_tiles": 8404992,
+                   "clock_ghz_profiled": 1.759, "wave_tiles": 8404992, "waves_per_simd": 2.85,
+                   "waves_per_simd_max": 3,
                    "summary": "profiles/attn_fwd_prefill32k_counters.md"},
     "mxfp4_32k": {"source_sha256_16": "665e9983665ee70d", "valu_busy": 0.931, "mfma_busy": 0.242,
                   "valu_insts_per_wave_tile": 185.0, "mfma_insts_per_wave_tile": 8.0,
-                  "clock_ghz_profiled": 1.965, "wave_tiles": 12582912,
+                  "clock_ghz_profiled": 1.965, "wave_tiles": 12582912, "waves_per_simd": 2.80,
+                  "waves_per_simd_max": 3,
                   "summary": "profiles/attn_fwd_mx_mxfp4_32k_counters.md"},
     "video17k": {"source_sha256_16": "7046a1c764f322e1", "valu_busy": 1.047, "mfma_busy": 0.255,
                  "valu_insts_per_wave_tile": 214.3, "mfma_insts_per_wave_tile": 6.03,
-                 "clock_ghz_profiled": 1.910, "wave_tiles": 14493600,
+                 "clock_ghz_profiled": 1.910, "wave_tiles": 14493600, "waves_per_simd": 3.78,
+                 "waves_per_simd_max": 4,
                  "summary": "profiles/attn_fwd_video17k_counters.md"},
 }
 _COMMON_SOURCES = ("quantized_attention_amd/csrc/attn_device.hpp", "quantized_attention_amd/csrc/sage_common.hpp")
