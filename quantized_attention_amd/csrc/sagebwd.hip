@@ -730,23 +730,32 @@ __global__ __launch_bounds__(256, 2) void sb_dkv_kernel(BwdArgs a) {
     TQ::src(w, x, lane, r, c);
     to[x] = r * kBQ + 16 * c;
   }
+  // LDS addresses of this wave's DMA destinations (scalars)
+  const uint32_t ot_lds = lds_addr(&sOt[TQ::NPW * w * 1024]), qt_lds = lds_addr(&sQt[TQ::NPW * w * 1024]);
   const int ilo = CAUSAL ? max(0, (key0 - a.coff) / kBQ) : 0;
+  // this wave's query rows of the first block; each later block's rows are loaded while the
+  // block before it is contracted into dV and dK
+  v4i qf[NKS];
+  v4i of[D / 16];
+  float l2 = 0.0f, dr = 0.0f;
+  if (ilo < a.nqb) {
+    const int qr = ilo * kBQ + 32 * w + col;
+    sb_q_frags<D>(a, bh, qr, h, qf, of);
+    l2 = a.L2[(size_t)bh * a.Np + qr];
+    dr = a.Dr[(size_t)bh * a.Np + qr];
+  }
   for (int i = ilo; i < a.nqb; i++) {
     __syncthreads();  // the previous pair's LDS reads are done (and V is staged, i = ilo)
     const int q0 = i * kBQ, qrow = q0 + 32 * w + col;
-    v4i qf[NKS];
-    v4i of[D / 16];
-    sb_q_frags<D>(a, bh, qrow, h, qf, of);
-    const float l2 = a.L2[(size_t)bh * a.Np + qrow], dr = a.Dr[(size_t)bh * a.Np + qrow];
     {
       // the block's dO^ and Q^ transposed for the dV / dK products, by DMA: they land while the
       // scores and gradients of the block are computed (issued after this wave's row loads)
       const int8_t* dob = a.dot + ((size_t)bh * a.nqb + i) * (size_t)D * kBQ;
       const int8_t* qtb = a.qt + ((size_t)bh * a.nqb + i) * (size_t)D * kBQ;
 #pragma unroll
-      for (int x = 0; x < TQ::NPW; x++) dma16(lds_addr(&sOt[(TQ::NPW * w + x) * 1024]), dob, to[x]);
+      for (int x = 0; x < TQ::NPW; x++) dma16(ot_lds + 1024 * x, dob, to[x]);
 #pragma unroll
-      for (int x = 0; x < TQ::NPW; x++) dma16(lds_addr(&sQt[(TQ::NPW * w + x) * 1024]), qtb, to[x]);
+      for (int x = 0; x < TQ::NPW; x++) dma16(qt_lds + 1024 * x, qtb, to[x]);
     }
     int lim = a.M - 1 - key0;
     if (CAUSAL) lim = min(lim, qrow + a.coff - key0);
@@ -785,6 +794,12 @@ __global__ __launch_bounds__(256, 2) void sb_dkv_kernel(BwdArgs a) {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const float vsc = __fdiv_rn(pmax, 127.0f) * a.sdo[(size_t)bh * a.nqb + i];
     const float ksc = __fdiv_rn(dmax, 127.0f) * a.sq[(size_t)bh * a.nqb + i] * a.sm;
+    {  // the next block's rows (the last block reloads its own), in flight during the products
+      const int qn = i + 1 < a.nqb ? qrow + kBQ : qrow;
+      sb_q_frags<D>(a, bh, qn, h, qf, of);
+      l2 = a.L2[(size_t)bh * a.Np + qn];
+      dr = a.Dr[(size_t)bh * a.Np + qn];
+    }
 #pragma unroll
     for (int g = 0; g < NG; g++) {
       const int c = c0 + g;
