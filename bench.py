@@ -11,8 +11,8 @@ quantizing"; "SageAttention2 Technical Report", kernel speed figures).  The defa
 workload is the LLM-prefill shape B=1, H=32, N=M=32768, d=128, bf16, causal.
 
 Printed: ONE JSON line with the metric, a roofline object for the dominant kernel (the
-fused attention kernel, timed with HIP events recorded on its stream around every launch
-in the timed region) and a cpu_baseline object (the CPU oracle on a bounded sample of the
+fused attention kernel, timed with HIP events attached to every one of its launches in the
+timed region: the launch itself sets them to the kernel's start and end times) and a cpu_baseline object (the CPU oracle on a bounded sample of the
 same workload, rank 0, N=1 only).
 """
 from __future__ import annotations
@@ -281,21 +281,27 @@ def main_train(args, cfg):
         fwd()
         bwd()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
+    for _ in range(args.steps):
+        fwd()
+        bwd()
+    t_stop.record()
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_stop) / args.steps
+    # the forward / backward split, from as many further steps with an event at each boundary
+    # (outside the timed region: each event record adds a few microseconds to the stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for a, b, c in ev:
         a.record()
         fwd()
         b.record()
         bwd()
         c.record()
-    t_stop.record()
     torch.cuda.synchronize()
-    ms = t_start.elapsed_time(t_stop) / args.steps
     f_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in ev]))
     b_ms = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
     ops = counted_ops(cfg) * 14 / 4

@@ -309,10 +309,12 @@ int sage_attn_fwd_noalloc(const sage_attn_shape* shape, const void* q, const voi
 
 /*
  * sage_attn_set_profile_events -- measurement hook.  With both arguments non-NULL (two
- * hipEvent_t handles), the next sage_attn_fwd / sage_attn_fwd_ws call on this thread
- * records `start` on its stream just before the fused attention kernel and `stop` just
- * after it, then forgets both (one call, one pair).  NULL, NULL clears a pending pair.
- * Only the caller's events are touched; no state is shared between threads.
+ * hipEvent_t handles, created by the caller), the next forward call on this thread (any
+ * sage_attn_fwd* entry point) launches its fused attention kernel with them as the launch's
+ * start and stop events (hipExtLaunchKernel): they take the kernel's own start and end
+ * times, and no separate event record enters the stream.  The pair is then forgotten (one
+ * call, one pair).  NULL, NULL clears a pending pair.  Only the caller's events are touched;
+ * no state is shared between threads.
  */
 void sage_attn_set_profile_events(void* start, void* stop);
 

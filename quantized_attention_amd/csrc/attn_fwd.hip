@@ -34,6 +34,8 @@
 // kept on one XCD (work-groups are dealt to the 8 XCDs round-robin), so a head's K^/V^
 // tiles are shared through that XCD's L2.  K^/V^ tiles are double-buffered in LDS; the
 // next tile's global loads are in flight while the current one is computed.
+#include <hip/hip_ext.h>
+
 #include "attn_device.hpp"
 
 namespace sage {
@@ -434,35 +436,40 @@ constexpr int occ_for() {
   return kPipe ? 2 : (SAGE_ATTN_OCC ? SAGE_ATTN_OCC : (D == 64 ? 4 : 3));
 }
 
+struct LaunchEv {
+  hipEvent_t e0, e1;
+};
+
 template <int D, bool CAUSAL, bool ACC_VALU, bool QF8>
-hipError_t launch_d(const Problem& p, const AttnArgs& a, hipStream_t s) {
+hipError_t launch_d(const Problem& p, const AttnArgs& a, hipStream_t s, LaunchEv ev) {
   dim3 grid(p.nqb * p.BH);
   const int out = p.out_fp32 ? 2 : (p.fp16 ? 1 : 0);
   if (out == 2)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, 2, ACC_VALU, QF8, kPipe, kRing, occ_for<D>()>), grid, dim3(256), 0, s,
-                       a);
+    hipExtLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, 2, ACC_VALU, QF8, kPipe, kRing, occ_for<D>()>), grid, dim3(256), 0,
+                          s, ev.e0, ev.e1, 0, a);
   else if (out == 1)
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, 1, ACC_VALU, QF8, kPipe, kRing, occ_for<D>()>), grid, dim3(256), 0, s,
-                       a);
+    hipExtLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, 1, ACC_VALU, QF8, kPipe, kRing, occ_for<D>()>), grid, dim3(256), 0,
+                          s, ev.e0, ev.e1, 0, a);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, 0, ACC_VALU, QF8, kPipe, kRing, occ_for<D>()>), grid, dim3(256), 0, s,
-                       a);
+    hipExtLaunchKernelGGL((attn_fwd_kernel<D, CAUSAL, 0, ACC_VALU, QF8, kPipe, kRing, occ_for<D>()>), grid, dim3(256), 0,
+                          s, ev.e0, ev.e1, 0, a);
   return hipGetLastError();
 }
 
 template <int D, bool ACC_VALU, bool QF8>
-hipError_t launch_c(const Problem& p, const AttnArgs& a, hipStream_t s) {
-  return p.causal ? launch_d<D, true, ACC_VALU, QF8>(p, a, s) : launch_d<D, false, ACC_VALU, QF8>(p, a, s);
+hipError_t launch_c(const Problem& p, const AttnArgs& a, hipStream_t s, LaunchEv ev) {
+  return p.causal ? launch_d<D, true, ACC_VALU, QF8>(p, a, s, ev) : launch_d<D, false, ACC_VALU, QF8>(p, a, s, ev);
 }
 
 template <int D, bool ACC_VALU>
-hipError_t launch_q(const Problem& p, const AttnArgs& a, hipStream_t s) {
-  return p.qf8 ? launch_c<D, ACC_VALU, true>(p, a, s) : launch_c<D, ACC_VALU, false>(p, a, s);
+hipError_t launch_q(const Problem& p, const AttnArgs& a, hipStream_t s, LaunchEv ev) {
+  return p.qf8 ? launch_c<D, ACC_VALU, true>(p, a, s, ev) : launch_c<D, ACC_VALU, false>(p, a, s, ev);
 }
 
 }  // namespace
 
-hipError_t launch_attn_fwd(const Problem& p, const Workspace& w, void* out, hipStream_t s) {
+hipError_t launch_attn_fwd(const Problem& p, const Workspace& w, void* out, hipStream_t s, hipEvent_t e0,
+                           hipEvent_t e1) {
   AttnArgs a;
   a.qhat = w.qhat; a.khat = w.khat; a.vhat = w.vhat; a.dq = w.dq; a.dk = w.dk; a.dv = w.dv;
   a.vmean = w.vmean; a.ds = w.ds; a.out = out;
@@ -473,8 +480,9 @@ hipError_t launch_attn_fwd(const Problem& p, const Workspace& w, void* out, hipS
   a.H = p.H; a.Hkv = p.Hkv; a.G = p.G;
   a.xcd_map = (p.BH % (kXCD * p.G) == 0) ? 1 : 0;
   const bool valu = (p.variant & SAGE_ACC_VALU) != 0;
-  if (p.d == 128) return valu ? launch_q<128, true>(p, a, s) : launch_q<128, false>(p, a, s);
-  return valu ? launch_q<64, true>(p, a, s) : launch_q<64, false>(p, a, s);
+  const LaunchEv ev{e0, e1};
+  if (p.d == 128) return valu ? launch_q<128, true>(p, a, s, ev) : launch_q<128, false>(p, a, s, ev);
+  return valu ? launch_q<64, true>(p, a, s, ev) : launch_q<64, false>(p, a, s, ev);
 }
 
 }  // namespace sage

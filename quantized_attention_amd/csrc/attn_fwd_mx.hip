@@ -39,6 +39,8 @@
 // s1_old alpha / s1_new = exp2(b_old - b_new) (b = rowmax S - log2 6, the level-one base)
 // before its product accumulates through the C operand, and the epilogue multiplies by
 // s1 = exp2(b - m).
+#include <hip/hip_ext.h>
+
 #include "attn_device.hpp"
 
 namespace sage {
@@ -410,27 +412,32 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 3) void attn_fwd_mx_kernel(MxArg
   }
 }
 
+struct LaunchEv {
+  hipEvent_t e0, e1;
+};
+
 template <int D, bool CAUSAL, bool ACC_VALU, bool P2L>
-hipError_t launch_d(const Problem& p, const MxArgs& a, hipStream_t s) {
+hipError_t launch_d(const Problem& p, const MxArgs& a, hipStream_t s, LaunchEv ev) {
   dim3 grid(p.nqb * p.BH);
   const int out = p.out_fp32 ? 2 : (p.fp16 ? 1 : 0);
   if (out == 2)
-    hipLaunchKernelGGL((attn_fwd_mx_kernel<D, CAUSAL, 2, ACC_VALU, P2L>), grid, dim3(256), 0, s, a);
+    hipExtLaunchKernelGGL((attn_fwd_mx_kernel<D, CAUSAL, 2, ACC_VALU, P2L>), grid, dim3(256), 0, s, ev.e0, ev.e1, 0, a);
   else if (out == 1)
-    hipLaunchKernelGGL((attn_fwd_mx_kernel<D, CAUSAL, 1, ACC_VALU, P2L>), grid, dim3(256), 0, s, a);
+    hipExtLaunchKernelGGL((attn_fwd_mx_kernel<D, CAUSAL, 1, ACC_VALU, P2L>), grid, dim3(256), 0, s, ev.e0, ev.e1, 0, a);
   else
-    hipLaunchKernelGGL((attn_fwd_mx_kernel<D, CAUSAL, 0, ACC_VALU, P2L>), grid, dim3(256), 0, s, a);
+    hipExtLaunchKernelGGL((attn_fwd_mx_kernel<D, CAUSAL, 0, ACC_VALU, P2L>), grid, dim3(256), 0, s, ev.e0, ev.e1, 0, a);
   return hipGetLastError();
 }
 
 template <int D, bool ACC_VALU, bool P2L = false>
-hipError_t launch_c(const Problem& p, const MxArgs& a, hipStream_t s) {
-  return p.causal ? launch_d<D, true, ACC_VALU, P2L>(p, a, s) : launch_d<D, false, ACC_VALU, P2L>(p, a, s);
+hipError_t launch_c(const Problem& p, const MxArgs& a, hipStream_t s, LaunchEv ev) {
+  return p.causal ? launch_d<D, true, ACC_VALU, P2L>(p, a, s, ev) : launch_d<D, false, ACC_VALU, P2L>(p, a, s, ev);
 }
 
 }  // namespace
 
-hipError_t launch_attn_fwd_mx(const Problem& p, const Workspace& w, void* out, hipStream_t s) {
+hipError_t launch_attn_fwd_mx(const Problem& p, const Workspace& w, void* out, hipStream_t s, hipEvent_t e0,
+                              hipEvent_t e1) {
   MxArgs a;
   a.qhat = reinterpret_cast<const uint8_t*>(w.qhat);
   a.khat = reinterpret_cast<const uint8_t*>(w.khat);
@@ -444,10 +451,11 @@ hipError_t launch_attn_fwd_mx(const Problem& p, const Workspace& w, void* out, h
   a.H = p.H; a.Hkv = p.Hkv; a.G = p.G;
   a.xcd_map = (p.BH % (kXCD * p.G) == 0) ? 1 : 0;
   const bool valu = (p.variant & SAGE_ACC_VALU) != 0;
+  const LaunchEv ev{e0, e1};
   if (p.variant & SAGE_MX_P_TWO_LEVEL)  // the host check keeps SAGE_ACC_VALU out of this form
-    return p.d == 128 ? launch_c<128, false, true>(p, a, s) : launch_c<64, false, true>(p, a, s);
-  if (p.d == 128) return valu ? launch_c<128, true>(p, a, s) : launch_c<128, false>(p, a, s);
-  return valu ? launch_c<64, true>(p, a, s) : launch_c<64, false>(p, a, s);
+    return p.d == 128 ? launch_c<128, false, true>(p, a, s, ev) : launch_c<64, false, true>(p, a, s, ev);
+  if (p.d == 128) return valu ? launch_c<128, true>(p, a, s, ev) : launch_c<128, false>(p, a, s, ev);
+  return valu ? launch_c<64, true>(p, a, s, ev) : launch_c<64, false>(p, a, s, ev);
 }
 
 }  // namespace sage

@@ -198,10 +198,9 @@ int fwd_impl(const void* q, const void* k, const void* v, void* out, const Probl
   // the INT8/FP8 kernel adds it in its dequantizing FMA, scaled
   int rc = run_preprocess(p, q, k, v, w, p.mx ? 1.0f : p.sm_scale * 1.4426950408889634f, w.ds, s);
   if (rc != SAGE_OK) return rc;
-  if (e0 && hipEventRecord(e0, s) != hipSuccess) return SAGE_ERR_LAUNCH;
-  if ((p.mx ? launch_attn_fwd_mx(p, w, out, s) : launch_attn_fwd(p, w, out, s)) != hipSuccess)
+  // the measurement events (if any) take the fused kernel's own start and end times
+  if ((p.mx ? launch_attn_fwd_mx(p, w, out, s, e0, e1) : launch_attn_fwd(p, w, out, s, e0, e1)) != hipSuccess)
     return SAGE_ERR_LAUNCH;
-  if (e1 && hipEventRecord(e1, s) != hipSuccess) return SAGE_ERR_LAUNCH;
   return SAGE_OK;
 }
 

@@ -300,7 +300,11 @@ hipError_t launch_kv_finalize(const Problem& p, const Workspace& w, hipStream_t 
 // K^, Delta S (into ds_out scaled by ds_scale; skipped when ds_out is null) and V^.
 hipError_t launch_kv_quant(const Problem& p, const void* k, const void* v, const Workspace& w,
                            float ds_scale, float* ds_out, hipStream_t s);
-hipError_t launch_attn_fwd(const Problem& p, const Workspace& w, void* out, hipStream_t s);
-hipError_t launch_attn_fwd_mx(const Problem& p, const Workspace& w, void* out, hipStream_t s);
+// The fused kernels.  e0 / e1 (may be null): events that take the kernel's start and end
+// times from its own dispatch (no separate event records on the stream).
+hipError_t launch_attn_fwd(const Problem& p, const Workspace& w, void* out, hipStream_t s, hipEvent_t e0,
+                           hipEvent_t e1);
+hipError_t launch_attn_fwd_mx(const Problem& p, const Workspace& w, void* out, hipStream_t s, hipEvent_t e0,
+                              hipEvent_t e1);
 
 }  // namespace sage
