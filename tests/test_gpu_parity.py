@@ -258,6 +258,49 @@ def test_long_sequence_sampled(name, cfg):
     check_output(got, ref, ex)
 
 
+# ---------------------------------------------------------------- the most heads
+# B*H at the C ABI's bound (65535; the K/V kernels take the head from the grid's second
+# dimension): 65535 heads of a short ragged causal sequence, in the plain head order (B*H not a
+# multiple of 8), and 65528 heads of one batch in the XCD-grouped order.  Heads at both ends and
+# in the middle are compared with the oracle, whole.
+MANY = [
+    ("B3-H21845", sy.CONFIGS["video17k"].with_shape(B=3, H=21845, N=130, M=130, causal=1, smooth_v=False)),
+    ("B1-H65528", sy.CONFIGS["video17k"].with_shape(B=1, H=65528, N=130, M=130, causal=1, smooth_v=True)),
+]
+
+
+@pytest.mark.parametrize("path", ["int8", "mxfp4"])
+@pytest.mark.parametrize("name,cfg", MANY, ids=[n for n, _ in MANY])
+def test_most_heads(name, cfg, path):
+    import quantized_attention_amd as qa
+    BH = cfg.B * cfg.H
+    checked = sorted({0, 1, cfg.H - 1, cfg.H, BH // 2, BH - 2, BH - 1} & set(range(BH)))
+    # the checked heads hold the workload's seeded inputs; every other head a seeded normal fill
+    # (heads are independent, so the fill only has to be valid data)
+    sub = sy.make_qkv(cfg, heads=checked)
+    gen = torch.Generator(device="cuda").manual_seed(4242)
+    dev = []
+    for t, x in enumerate(sub):
+        full = torch.randn((BH, cfg.N if t == 0 else cfg.M, cfg.d), generator=gen, device="cuda").to(torch.bfloat16)
+        full[torch.tensor(checked, device="cuda")] = gu.to_dev(x, cfg.fp16)
+        dev.append(full.view(cfg.B, cfg.H, -1, cfg.d))
+    kw = {"mxfp4": True} if path == "mxfp4" else {}
+    say(f"most heads {name} path={path} B={cfg.B} H={cfg.H} N={cfg.N} d={cfg.d}")
+    out = qa.sage_attn(*dev, causal=cfg.causal, smooth_v=cfg.smooth_v, out_fp32=True, **kw)
+    torch.cuda.synchronize()
+    flags = oracle.MXFP4 if path == "mxfp4" else 0
+    s = 1 / math.sqrt(cfg.d)
+    for j, bh in enumerate(checked):
+        b, h = bh // cfg.H, bh % cfg.H
+        got = out[b, h].cpu().numpy().astype(np.float64)
+        ref, _, bound = oracle.forward_head_ties(sub[0][j], sub[1][j], sub[2][j], cfg.fp16, cfg.causal, s,
+                                                 flags | (oracle.SMOOTH_V if cfg.smooth_v else 0))
+        err = np.abs(got - ref)
+        assert np.isfinite(got).all()
+        assert err.mean() <= MEAN_ABS, (bh, err.mean())
+        assert (err.max(axis=1) <= MAX_ABS + bound).all(), (bh, err.max())
+
+
 # ---------------------------------------------------------------- degenerate inputs
 # Inputs where the quantizers meet their edge cases: every scale at its floor (all zeros), gamma(K)
 # exactly 0 (all keys equal: K^ = 0, Delta S = 0, every visible score equal), gamma(Q) and the
