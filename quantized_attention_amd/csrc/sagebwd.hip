@@ -17,9 +17,11 @@
 // max) are per lane.  The P^ (forward) and dS^ (dQ kernel) bytes of a lane are then the B
 // operand of an INT8 MFMA whose A operand (V^T, K^T) is stored with its keys permuted to the
 // lane order (i8perm), as the FP8 P^ V^ product of the inference kernel.  The dK/dV kernel
-// writes P^ and dS^ key-major to LDS and contracts over the queries against transposed Q^ and
-// dO^ (one 32-query step per MFMA).  dP^T = V dO^T runs on the bf16 MFMA from the 16-bit
-// inputs.
+// computes every pair's dS once: it writes P^ and dS^ key-major to LDS and contracts over the
+// queries against transposed Q^ and dO^ (one 32-query step per MFMA), and leaves the pair's
+// dS^ bytes (in the B-operand order of the dQ product), scale and row sums of dS in the
+// workspace; the dQ kernel, launched after it, contracts those against K^ transposed.
+// dP^T = V dO^T runs on the bf16 MFMA from the 16-bit inputs.
 #include "attn_device.hpp"
 #include "sagebwd.hpp"
 
@@ -439,6 +441,11 @@ struct BwdArgs {
   float* dq;           // [BH][N][D]
   float* dk;           // [BH][M][D]
   float* dv;           // [BH][M][D]
+  // dS^ of each (128-query block i, 64-key block j) pair, written by the dK/dV kernel and
+  // contracted by the dQ kernel: pair (i, j) of head bh is p = (bh nqb + i) nkt + j
+  int8_t* dsh;         // [pairs][4 waves][64 lanes][32]: the lane's codes in the dQ product's B order
+  float* dss;          // [pairs] max|dS| / 127
+  float* drs;          // [pairs][128] sum over the pair's keys of dS (FP32), per query
   int N, M, nqb, nkt, Np, Mp, coff;
   float qk_scale;      // sm_scale * log2(e)
   float sm;            // sm_scale
@@ -544,117 +551,68 @@ __device__ __forceinline__ void sb_q_frags(const BwdArgs& a, int bh, int qrow, i
   }
 }
 
-// ---- dQ: one work-group per (head, 128-query block); loops over the key blocks.  The key
-// block's K^ rows, K^ transposed and 16-bit V rows stream into a 2-slot LDS ring by DMA: block
-// j+1 is in flight while block j is computed, one barrier per block publishes the next ----
-template <int D, bool CAUSAL, bool FP16>
-__global__ __launch_bounds__(256, 2) void sb_dq_kernel(BwdArgs a) {
+// ---- dQ: one work-group per (head, 128-query block); loops over the key blocks.  The dK/dV
+// kernel (launched first) leaves each pair's dS^ codes in this kernel's B-operand order, the
+// pair's scale and its per-query sums of dS; here dQ = sum_j dS^_j K^_j s_j sm_scale contracts
+// them against the key block's K^ transposed, which streams through a 2-slot LDS ring by DMA
+// (block j+1 in flight while block j is used, one barrier per block) ----
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 4) void sb_dq_kernel(BwdArgs a) {
   constexpr int NKS = D / 32;
-  using TK = SbTile<kBK, D>;      // K^ rows
-  using TT = SbTile<D, kBK>;      // K^ transposed, keys in i8perm order
-  using TV = SbTile<kBK, 2 * D>;  // V rows, 16-bit
-  __shared__ __attribute__((aligned(1024))) int8_t sK[2][TK::BYTES];
+  using TT = SbTile<D, kBK>;  // K^ transposed, keys in i8perm order
   __shared__ __attribute__((aligned(1024))) int8_t sKt[2][TT::BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t sVb[2][TV::BYTES];
-  __shared__ float xs[8];
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   int bh, qi;
   sb_map(a.nqb, bh, qi);
   const int qb = CAUSAL ? (a.nqb - 1 - qi) : qi;
   const int q0 = qb * kBQ, qrow = q0 + 32 * w + col;
-  v4i qf[NKS];
-  v4i of[D / 16];
-  sb_q_frags<D>(a, bh, qrow, h, qf, of);
-  const float l2 = a.L2[(size_t)bh * a.Np + qrow], dr = a.Dr[(size_t)bh * a.Np + qrow];
-  const float sq = a.sq[(size_t)bh * a.nqb + qb];
   v16f dq[NKS];
 #pragma unroll
   for (int c = 0; c < NKS; c++)
 #pragma unroll
     for (int r = 0; r < 16; r++) dq[c][r] = 0.0f;
   float rs = 0.0f;
+  // the key blocks this query block attends to (the pairs the dK/dV kernel wrote)
   const int jend = CAUSAL ? max(0, min(a.nkt, (q0 + kBQ + a.coff + kBK - 1) / kBK)) : a.nkt;
-
-  // per-lane DMA source offsets inside a block (V: row and byte column; its rows are clamped to
-  // the last key, a stand-in for keys >= M, whose P and dS are 0)
-  int ko[TK::NPW], to[TT::NPW], vr[TV::NPW], vc[TV::NPW];
-#pragma unroll
-  for (int i = 0; i < TK::NPW; i++) {
-    int r, c;
-    TK::src(w, i, lane, r, c);
-    ko[i] = r * D + 16 * c;
-  }
+  int to[TT::NPW];  // per-lane DMA source offsets inside a block
 #pragma unroll
   for (int i = 0; i < TT::NPW; i++) {
     int r, c;
     TT::src(w, i, lane, r, c);
     to[i] = r * kBK + 16 * c;
   }
-#pragma unroll
-  for (int i = 0; i < TV::NPW; i++) {
-    int r, c;
-    TV::src(w, i, lane, r, c);
-    vr[i] = r;
-    vc[i] = 16 * c;
-  }
+  const uint32_t lds0 = lds_addr(&sKt[0][TT::NPW * w * 1024]), lds1 = lds_addr(&sKt[1][TT::NPW * w * 1024]);
   auto dma = [&](int j, int b) {
-    const int8_t* kr = a.kh + ((size_t)bh * a.Mp + (size_t)j * kBK) * D;
     const int8_t* kt = a.kt + ((size_t)bh * a.nkt + j) * (size_t)D * kBK;
-    const uint16_t* vb = a.V + ((size_t)bh * a.M + (size_t)j * kBK) * D;
-    const int vlast = a.M - 1 - j * kBK;  // >= 0: block j holds a key
+    const uint32_t base = b ? lds1 : lds0;
 #pragma unroll
-    for (int i = 0; i < TK::NPW; i++) dma16(lds_addr(&sK[b][(TK::NPW * w + i) * 1024]), kr, ko[i]);
-#pragma unroll
-    for (int i = 0; i < TT::NPW; i++) dma16(lds_addr(&sKt[b][(TT::NPW * w + i) * 1024]), kt, to[i]);
-#pragma unroll
-    for (int i = 0; i < TV::NPW; i++)
-      dma16(lds_addr(&sVb[b][(TV::NPW * w + i) * 1024]), vb, min(vr[i], vlast) * (2 * D) + vc[i]);
+    for (int i = 0; i < TT::NPW; i++) dma16(base + 1024 * i, kt, to[i]);
   };
-  if (jend > 0) dma(0, 0);
+  const size_t p0 = ((size_t)bh * a.nqb + qb) * a.nkt;  // pair (qb, 0)
+  const int8_t* dsrc = a.dsh + p0 * 8192 + (size_t)(64 * w + lane) * 32;
+  const float* rsrc = a.drs + p0 * kBQ + 32 * w + col;
+  v4i db[2] = {}, dbn[2];
+  float rv = 0.0f, rvn;
+  if (jend > 0) {
+    dma(0, 0);
+    db[0] = *reinterpret_cast<const v4i*>(dsrc);
+    db[1] = *reinterpret_cast<const v4i*>(dsrc + 16);
+    rv = rsrc[0];
+  }
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // block 0 landed
   for (int j = 0; j < jend; j++) {
     const int b = j & 1;
     if (j + 1 < jend) dma(j + 1, b ^ 1);  // the slot block j-1 left (freed by the last barrier)
-    const int8_t* cK = sK[b];
+    {  // the next pair's codes and row sums (the last pair reloads its own), in flight meanwhile
+      const int jn = j + 1 < jend ? j + 1 : j;
+      dbn[0] = *reinterpret_cast<const v4i*>(dsrc + (size_t)jn * 8192);
+      dbn[1] = *reinterpret_cast<const v4i*>(dsrc + (size_t)jn * 8192 + 16);
+      rvn = rsrc[(size_t)jn * kBQ];
+    }
+    rs += rv;
+    const float osc = a.dss[p0 + j] * a.sk[(size_t)bh * a.nkt + j] * a.sm;
     const int8_t* cKt = sKt[b];
-    const uint8_t* cV = sVb[b];
-    v4i kf[2][NKS];
-#pragma unroll
-    for (int T = 0; T < 2; T++)
-#pragma unroll
-      for (int s = 0; s < NKS; s++) kf[T][s] = *reinterpret_cast<const v4i*>(&cK[TK::off(32 * T + col, 2 * s + h)]);
-    const int key0 = j * kBK;
-    int lim = a.M - 1 - key0;
-    if (CAUSAL) lim = min(lim, qrow + a.coff - key0);
-    lim -= 4 * h;
-    float P[2][16], dS[2][16];
-    auto vfrag = [&](int T, int s) {
-      return *reinterpret_cast<const v4i*>(&cV[TV::off(32 * T + col, 2 * s + h)]);
-    };
-    const bool masked = key0 + kBK > a.M || (CAUSAL && key0 + kBK - 1 > q0 + 32 * w + a.coff);
-    sb_pair<D, FP16>(kf, qf, of, vfrag, sq * a.sk[(size_t)bh * a.nkt + j] * a.qk_scale, l2, dr, masked, lim, h, col, P,
-                     dS);
-    float dm = 0.0f;
-#pragma unroll
-    for (int T = 0; T < 2; T++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        dm = fmaxf(dm, fabsf(dS[T][r]));
-        rs += dS[T][r];
-      }
-    const float dmax = sb_block_max_ds(dm, xs, lane, w);
-    const float inv = dmax > 0.0f ? __fdiv_rn(127.0f, dmax) : 0.0f;
-    const float sds = __fdiv_rn(dmax, 127.0f);
-    v4i db[2];
-#pragma unroll
-    for (int T = 0; T < 2; T++)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; q4++) {
-        db[T][q4] = (int)sb_pack4(sb_code8(dS[T][4 * q4 + 0], inv), sb_code8(dS[T][4 * q4 + 1], inv),
-                                  sb_code8(dS[T][4 * q4 + 2], inv), sb_code8(dS[T][4 * q4 + 3], inv));
-      }
-    const float osc = sds * a.sk[(size_t)bh * a.nkt + j] * a.sm;
 #pragma unroll
     for (int c = 0; c < NKS; c++) {
       v16i R;
@@ -668,10 +626,12 @@ __global__ __launch_bounds__(256, 2) void sb_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; r++) dq[c][r] = fmaf((float)R[r], osc, dq[c][r]);
     }
+    db[0] = dbn[0];
+    db[1] = dbn[1];
+    rv = rvn;
     // block j+1 landed (this wave's DMAs, then everyone's); slot b may be refilled
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
-  rs = pair_sum(rs);
   if (qrow >= a.N) return;
   const size_t orow = ((size_t)bh * a.N + qrow) * D;
 #pragma unroll
@@ -780,16 +740,29 @@ __global__ __launch_bounds__(256, 2) void sb_dkv_kernel(BwdArgs a) {
     sb_block_max(pm, dm, xs, lane, w, pmax, dmax);
     const float pinv = pmax > 0.0f ? __fdiv_rn(127.0f, pmax) : 0.0f;
     const float dinv = dmax > 0.0f ? __fdiv_rn(127.0f, dmax) : 0.0f;
-    // P^, dS^ key-major: byte [key][query]
+    // P^, dS^ key-major: byte [key][query]; dS^ also to the pair's buffer for the dQ kernel (the
+    // lane's 32 codes as its B operand: 16 bytes per 32-key half), with the scale and the row sum
     const int qc = 32 * w + col;
+    const size_t pr = ((size_t)bh * a.nqb + i) * a.nkt + j;
+    float rsp = 0.0f;
+    v4i db[2];
 #pragma unroll
     for (int T = 0; T < 2; T++)
 #pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int key = 32 * T + 8 * (r >> 2) + 4 * h + (r & 3);
-        sP[key * PS + qc] = (int8_t)sb_code8(P[T][r], pinv);
-        sD[key * PS + qc] = (int8_t)sb_code8(dS[T][r], dinv);
+      for (int q4 = 0; q4 < 4; q4++) {
+        uint32_t dc[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const int r = 4 * q4 + e;
+          const int key = 32 * T + 8 * (r >> 2) + 4 * h + (r & 3);
+          sP[key * PS + qc] = (int8_t)sb_code8(P[T][r], pinv);
+          dc[e] = sb_code8(dS[T][r], dinv);
+          sD[key * PS + qc] = (int8_t)dc[e];
+          rsp += dS[T][r];
+        }
+        db[T][q4] = (int)sb_pack4(dc[0], dc[1], dc[2], dc[3]);
       }
+    rsp = pair_sum(rsp);
     // P^ / dS^ visible, and this block's dO^ / Q^ transposed landed (every wave's DMAs)
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     const float vsc = __fdiv_rn(pmax, 127.0f) * a.sdo[(size_t)bh * a.nqb + i];
@@ -799,6 +772,15 @@ __global__ __launch_bounds__(256, 2) void sb_dkv_kernel(BwdArgs a) {
       sb_q_frags<D>(a, bh, qn, h, qf, of);
       l2 = a.L2[(size_t)bh * a.Np + qn];
       dr = a.Dr[(size_t)bh * a.Np + qn];
+    }
+    {  // the pair's dS^, scale and row sums for the dQ kernel: stored after the barrier, so that
+       // its wait on this block's memory operations does not wait on them as well
+      // non-temporal: read once, by another kernel; they need not displace this kernel's tiles in L2
+      int8_t* dst = a.dsh + pr * 8192 + (size_t)(64 * w + lane) * 32;
+      __builtin_nontemporal_store(db[0], reinterpret_cast<v4i*>(dst));
+      __builtin_nontemporal_store(db[1], reinterpret_cast<v4i*>(dst + 16));
+      if (lane < 32) __builtin_nontemporal_store(rsp, a.drs + pr * kBQ + qc);
+      if (tid == 0) a.dss[pr] = __fdiv_rn(dmax, 127.0f);
     }
 #pragma unroll
     for (int g = 0; g < NG; g++) {
@@ -852,7 +834,8 @@ __global__ __launch_bounds__(256, 2) void sb_dkv_kernel(BwdArgs a) {
 
 // Workspace slices of SageBwd (256-byte aligned).
 enum SbSlice { kSbQh, kSbQt, kSbSq, kSbKh, kSbKt, kSbSk, kSbVt, kSbSv, kSbDot, kSbSdo, kSbD, kSbL2,
-               kSbKpart, kSbVpart, kSbVmax, kSbVmin, kSbKmean, kSbVmean, kSbDv, kSbSlices };
+               kSbKpart, kSbVpart, kSbVmax, kSbVmin, kSbKmean, kSbVmean, kSbDv, kSbDsh, kSbDss, kSbDrs,
+               kSbSlices };
 
 size_t sb_layout(const Problem& p, bool bwd, size_t* s) {
   const size_t BH = (size_t)p.BH, d = (size_t)p.d;
@@ -876,6 +859,10 @@ size_t sb_layout(const Problem& p, bool bwd, size_t* s) {
   z[kSbKmean] = BH * d * 4;
   z[kSbVmean] = BH * d * 4;
   z[kSbDv] = BH * d * 4;
+  const size_t pairs = BH * p.nqb * p.nkt;  // (query block, key block) pairs: dS^ of the backward
+  z[kSbDsh] = bwd ? pairs * 8192 : 0;
+  z[kSbDss] = bwd ? pairs * 4 : 0;
+  z[kSbDrs] = bwd ? pairs * kBQ * 4 : 0;
   size_t tot = 0;
   for (int i = 0; i < kSbSlices; i++) {
     if (s) s[i] = tot;
@@ -990,8 +977,9 @@ hipError_t sb_prep_bwd(const Problem& p, const void* out, const void* dout, cons
 
 template <int D, bool CAUSAL, bool FP16>
 void sb_bwd_launch(const Problem& p, const BwdArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((sb_dq_kernel<D, CAUSAL, FP16>), dim3(p.nqb * p.BH), dim3(256), 0, st, a);
+  // dK/dV first: it leaves every pair's dS^ for the dQ contraction
   hipLaunchKernelGGL((sb_dkv_kernel<D, CAUSAL, FP16>), dim3(p.nkt * p.BH), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((sb_dq_kernel<D, CAUSAL>), dim3(p.nqb * p.BH), dim3(256), 0, st, a);
 }
 
 template <int D>
@@ -1019,6 +1007,9 @@ hipError_t sb_backward(const Problem& p, char* ws, bool smooth_k, const void* v,
   a.V = (const uint16_t*)v;
   a.dO = (const uint16_t*)dout;
   a.dq = dq; a.dk = dk; a.dv = dv;
+  a.dsh = (int8_t*)(ws + o[kSbDsh]);
+  a.dss = (float*)(ws + o[kSbDss]);
+  a.drs = (float*)(ws + o[kSbDrs]);
   a.N = p.N; a.M = p.M; a.nqb = p.nqb; a.nkt = p.nkt; a.Np = p.Np; a.Mp = p.Mp;
   a.coff = p.causal == 2 ? p.M - p.N : 0;
   a.qk_scale = p.sm_scale * kLog2e;
