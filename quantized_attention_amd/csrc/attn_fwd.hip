@@ -403,14 +403,25 @@ __global__ __launch_bounds__(256, OCC) void attn_fwd_kernel(AttnArgs a) {
   const float* vmp = a.vmean + (size_t)kvh * D;
   const SeqRows ro = seq_rows(a.ql, bseq, bh % a.H, a.H, D);
   const size_t orow = ro.base + (size_t)qrow * ro.stride;
+  // per 32-channel group: its dV and V_m loads all issued before its stores (the stores may
+  // alias them as far as the compiler knows, which would otherwise serialize every load)
 #pragma unroll
   for (int c = 0; c < NKS; c++) {
+    float4 dv4[4], vm4[4];
 #pragma unroll
     for (int b = 0; b < 4; b++) {
       const int ch = 32 * c + 8 * b + 4 * h;
+      dv4[b] = *reinterpret_cast<const float4*>(dvp + ch);
+      vm4[b] = *reinterpret_cast<const float4*>(vmp + ch);
+    }
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      const int ch = 32 * c + 8 * b + 4 * h;
+      const float dvv[4] = {dv4[b].x, dv4[b].y, dv4[b].z, dv4[b].w};
+      const float vmv[4] = {vm4[b].x, vm4[b].y, vm4[b].z, vm4[b].w};
       float o[4];
 #pragma unroll
-      for (int k = 0; k < 4; k++) o[k] = none ? 0.0f : fmaf(O[c][4 * b + k] * inv, dvp[ch + k], vmp[ch + k]);
+      for (int k = 0; k < 4; k++) o[k] = none ? 0.0f : fmaf(O[c][4 * b + k] * inv, dvv[k], vmv[k]);
       store_out4<OUT>(a.out, orow + ch, o);
     }
   }

@@ -399,14 +399,20 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 3) void attn_fwd_mx_kernel(MxArg
   const float* vmp = a.vmean + (size_t)kvh * D;
   const SeqRows ro = seq_rows(a.ql, bseq, bh % a.H, a.H, D);
   const size_t orow = ro.base + (size_t)qrow * ro.stride;
+  // per 32-channel group: its V_m loads all issued before its stores (the stores may alias them
+  // as far as the compiler knows, which would otherwise serialize every load)
 #pragma unroll
   for (int c = 0; c < NG; c++) {
+    float4 vm4[4];
+#pragma unroll
+    for (int b = 0; b < 4; b++) vm4[b] = *reinterpret_cast<const float4*>(vmp + 32 * c + 8 * b + 4 * h);
 #pragma unroll
     for (int b = 0; b < 4; b++) {
       const int ch = 32 * c + 8 * b + 4 * h;
+      const float vmv[4] = {vm4[b].x, vm4[b].y, vm4[b].z, vm4[b].w};
       float o[4];
 #pragma unroll
-      for (int k = 0; k < 4; k++) o[k] = none ? 0.0f : fmaf(O[c][4 * b + k], inv, vmp[ch + k]);
+      for (int k = 0; k < 4; k++) o[k] = none ? 0.0f : fmaf(O[c][4 * b + k], inv, vmv[k]);
       store_out4<OUT>(a.out, orow + ch, o);
     }
   }

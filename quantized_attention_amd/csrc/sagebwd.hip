@@ -635,16 +635,24 @@ __global__ __launch_bounds__(256, 4) void sb_dq_kernel(BwdArgs a) {
   if (qrow >= a.N) return;
   const size_t orow = ((size_t)bh * a.N + qrow) * D;
 #pragma unroll
-  for (int c = 0; c < NKS; c++)
+  for (int c = 0; c < NKS; c++) {
+    // the group's K-mean loads all issued before its stores (which the compiler must otherwise
+    // order after every possibly aliasing store)
+    float4 km4[4] = {};
+    if (a.kmean)
+#pragma unroll
+      for (int b = 0; b < 4; b++)
+        km4[b] = *reinterpret_cast<const float4*>(a.kmean + (size_t)bh * D + 32 * c + 8 * b + 4 * h);
 #pragma unroll
     for (int b = 0; b < 4; b++) {
       const int ch = 32 * c + 8 * b + 4 * h;
+      const float kmv[4] = {km4[b].x, km4[b].y, km4[b].z, km4[b].w};
       float o[4];
 #pragma unroll
-      for (int k = 0; k < 4; k++)
-        o[k] = a.kmean ? fmaf(a.sm * rs, a.kmean[(size_t)bh * D + ch + k], dq[c][4 * b + k]) : dq[c][4 * b + k];
+      for (int k = 0; k < 4; k++) o[k] = a.kmean ? fmaf(a.sm * rs, kmv[k], dq[c][4 * b + k]) : dq[c][4 * b + k];
       store_out4<2>(a.dq, orow + ch, o);
     }
+  }
 }
 
 // ---- dK, dV: one work-group per (head, 64-key block); loops over the query blocks.  P^ and
