@@ -53,12 +53,12 @@ VALU_SLOTS_PER_SCORE = {"i8f8": 7.5, "qkfp8": 6.5, "mx": 5.5}
 # the kernel source it was taken on: the hash of that fused kernel's sources is checked,
 # and a changed kernel reports traffic null until the counters are taken again.
 TRAFFIC_BYTES = {
-    "prefill32k": {"source_sha256_16": "00b6446e4819ba4a",
-                   "fetch_bytes": 1812807981, "write_bytes": 271390240},
-    "mxfp4_32k": {"source_sha256_16": "19f616d05a4a01b5",
-                  "fetch_bytes": 1689409438, "write_bytes": 201328032},
-    "video17k": {"source_sha256_16": "00b6446e4819ba4a",
-                 "fetch_bytes": 2113963831, "write_bytes": 215654400},
+    "prefill32k": {"source_sha256_16": "f4b7745f9c66d9fa",
+                   "fetch_bytes": 1841364931, "write_bytes": 268501120},
+    "mxfp4_32k": {"source_sha256_16": "d4319ec4c6fe92b7",
+                  "fetch_bytes": 1688232047, "write_bytes": 201326656},
+    "video17k": {"source_sha256_16": "f4b7745f9c66d9fa",
+                 "fetch_bytes": 2110021653, "write_bytes": 215654400},
 }
 # SQ counters of the fused attention kernel on the named workload (rocprofv3 --pmc, the summary
 # under profiles/): VALU and matrix-core busy fractions of the SIMD cycles, instructions per
@@ -66,19 +66,19 @@ TRAFFIC_BYTES = {
 # SQ_INSTS_MFMA report them, and the engine clock of the profiled dispatch (GRBM_GUI_ACTIVE
 # cycles per XCD over its duration).  Keyed by the same source hash as the traffic; null once stale.
 COUNTERS = {
-    "prefill32k": {"source_sha256_16": "00b6446e4819ba4a", "valu_busy": 0.888, "mfma_busy": 0.398,
-                   "valu_insts_per_wave_tile": 235.5, "mfma_insts_per_wave_tile": 12.0,
-                   "clock_ghz_profiled": 1.783, "wave_tiles": 8404992, "waves_per_simd": 2.81,
+    "prefill32k": {"source_sha256_16": "f4b7745f9c66d9fa", "valu_busy": 0.896, "mfma_busy": 0.402,
+                   "valu_insts_per_wave_tile": 235.2, "mfma_insts_per_wave_tile": 12.0,
+                   "clock_ghz_profiled": 1.747, "wave_tiles": 8404992, "waves_per_simd": 2.81,
                    "waves_per_simd_max": 3,
                    "summary": "profiles/attn_fwd_prefill32k_counters.md"},
-    "mxfp4_32k": {"source_sha256_16": "19f616d05a4a01b5", "valu_busy": 0.930, "mfma_busy": 0.242,
-                  "valu_insts_per_wave_tile": 185.0, "mfma_insts_per_wave_tile": 8.0,
-                  "clock_ghz_profiled": 1.951, "wave_tiles": 12582912, "waves_per_simd": 2.79,
+    "mxfp4_32k": {"source_sha256_16": "d4319ec4c6fe92b7", "valu_busy": 0.917, "mfma_busy": 0.239,
+                  "valu_insts_per_wave_tile": 184.9, "mfma_insts_per_wave_tile": 8.0,
+                  "clock_ghz_profiled": 1.942, "wave_tiles": 12582912, "waves_per_simd": 2.74,
                   "waves_per_simd_max": 3,
                   "summary": "profiles/attn_fwd_mx_mxfp4_32k_counters.md"},
-    "video17k": {"source_sha256_16": "00b6446e4819ba4a", "valu_busy": 1.037, "mfma_busy": 0.252,
-                 "valu_insts_per_wave_tile": 214.3, "mfma_insts_per_wave_tile": 6.03,
-                 "clock_ghz_profiled": 1.937, "wave_tiles": 14493600, "waves_per_simd": 3.74,
+    "video17k": {"source_sha256_16": "f4b7745f9c66d9fa", "valu_busy": 1.017, "mfma_busy": 0.247,
+                 "valu_insts_per_wave_tile": 214.2, "mfma_insts_per_wave_tile": 6.03,
+                 "clock_ghz_profiled": 1.945, "wave_tiles": 14493600, "waves_per_simd": 3.66,
                  "waves_per_simd_max": 4,
                  "summary": "profiles/attn_fwd_video17k_counters.md"},
 }
