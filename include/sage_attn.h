@@ -283,6 +283,12 @@ int sage_attn_varlen_fwd(const sage_attn_varlen_shape* shape, const void* q, con
  * pointers, 16-byte aligned (lse 4-byte); outputs must not overlap inputs.
  */
 #define SAGE_TRAIN_NO_SMOOTH_K 0x4000u /* ablation: K is not smoothed (training entry points) */
+/* sage_attn_train_bwd keeps each (128-query, 64-key) block pair's INT8 dS^ (about 8.5 KiB per
+ * pair, in the workspace) from its dK/dV kernel for its dQ kernel; with this bit, or when that
+ * buffer would exceed 16 GiB, the dQ kernel recomputes S, P, dP and dS instead (slower, with a
+ * workspace of a few bytes per token).  Both give the same dK and dV; dQ agrees to FP32
+ * rounding (the order of the K-mean term's row sums). */
+#define SAGE_TRAIN_RECOMPUTE_DS 0x8000u
 size_t sage_attn_train_workspace_bytes(const sage_attn_shape* shape);
 int sage_attn_train_fwd(const sage_attn_shape* shape, const void* q, const void* k, const void* v, void* out,
                         float* lse, void* workspace, size_t ws_bytes, void* stream);

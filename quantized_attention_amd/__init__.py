@@ -23,7 +23,7 @@ __all__ = [
     "sage_attn_version", "sage_attn_set_profile_events", "sage_attn", "QuantViews",
     "SageAttnShape", "sage_attn_fwd_ex", "sage_attn_workspace_bytes_ex", "sage_attn_quantize_ex",
     "SageAttnVarlenShape", "sage_attn_varlen_workspace_bytes", "sage_attn_varlen_fwd", "sage_attn_varlen",
-    "SAGE_TRAIN_NO_SMOOTH_K", "sage_attn_train_workspace_bytes", "sage_attn_train_fwd", "sage_attn_train_bwd",
+    "SAGE_TRAIN_NO_SMOOTH_K", "SAGE_TRAIN_RECOMPUTE_DS", "sage_attn_train_workspace_bytes", "sage_attn_train_fwd", "sage_attn_train_bwd",
     "sage_attn_train_forward", "sage_attn_train_backward", "SageBwdAttention",
     "SAGE_NOALLOC_MAX_BYTES", "sage_attn_fwd_noalloc",
 ]
@@ -46,6 +46,7 @@ SAGE_OUT_SAME = 0x0000
 SAGE_OUT_FP32 = 0x1000
 SAGE_ACC_VALU = 0x2000
 SAGE_TRAIN_NO_SMOOTH_K = 0x4000
+SAGE_TRAIN_RECOMPUTE_DS = 0x8000
 
 SAGE_BQ = 128
 SAGE_BK = 64
@@ -341,7 +342,7 @@ def sage_attn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max
 
 
 # ---------------------------------------------------------------- SageBwd (training)
-def _train_shape(q, k, v, causal, sm_scale, out_fp32, smooth_k):
+def _train_shape(q, k, v, causal, sm_scale, out_fp32, smooth_k, recompute_ds=False):
     """The SageBwd shape of q [B, H, N, d] and k, v [B, Hkv, M, d]; shapes are checked here so
     that no mismatched buffer reaches the kernels (the library itself rejects Hkv != H)."""
     import torch
@@ -356,6 +357,8 @@ def _train_shape(q, k, v, causal, sm_scale, out_fp32, smooth_k):
     var = (SAGE_IN_FP16 if q.dtype == torch.float16 else SAGE_IN_BF16) | (SAGE_OUT_FP32 if out_fp32 else 0)
     if not smooth_k:
         var |= SAGE_TRAIN_NO_SMOOTH_K
+    if recompute_ds:
+        var |= SAGE_TRAIN_RECOMPUTE_DS
     scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(d)
     return SageAttnShape(B, H, Hkv, N, M, d, int(causal), scale, var)
 
@@ -389,10 +392,12 @@ def sage_attn_train_forward(q, k, v, causal: int = 0, sm_scale: float | None = N
 
 
 def sage_attn_train_backward(q, k, v, out, dout, lse, causal: int = 0, sm_scale: float | None = None,
-                             smooth_k: bool = True):
-    """SageBwd backward: (dq, dk, dv) in FP32, from the forward's out (its dtype) and lse."""
+                             smooth_k: bool = True, recompute_ds: bool = False):
+    """SageBwd backward: (dq, dk, dv) in FP32, from the forward's out (its dtype) and lse.
+    recompute_ds: the dQ kernel recomputes dS instead of reading the dK/dV kernel's stored dS^
+    codes (SAGE_TRAIN_RECOMPUTE_DS: slower, with a small workspace)."""
     import torch
-    shape = _train_shape(q, k, v, causal, sm_scale, out.dtype == torch.float32, smooth_k)
+    shape = _train_shape(q, k, v, causal, sm_scale, out.dtype == torch.float32, smooth_k, recompute_ds)
     B, H, N, d = q.shape
     if tuple(dout.shape) != (B, H, N, d) or tuple(out.shape) != (B, H, N, d):
         raise ValueError("out and dout must be [B, H, N, d] like q")

@@ -263,10 +263,12 @@ void* scratch_on_current_device() {
 // dtypes and the K-smoothing ablation.
 int make_train_problem(const sage_attn_shape* sh, Problem* p, bool* smooth_k) {
   if (!sh) return SAGE_ERR_INVALID_ARG;
-  if (sh->variant & ~(SAGE_IN_FP16 | SAGE_OUT_FP32 | SAGE_TRAIN_NO_SMOOTH_K)) return SAGE_ERR_INVALID_ARG;
+  constexpr unsigned kTrainOnly = SAGE_TRAIN_NO_SMOOTH_K | SAGE_TRAIN_RECOMPUTE_DS;
+  if (sh->variant & ~(SAGE_IN_FP16 | SAGE_OUT_FP32 | kTrainOnly)) return SAGE_ERR_INVALID_ARG;
   const int rc = make_problem(sh->B, sh->Hq, sh->Hkv, sh->N, sh->M, sh->d, sh->causal, sh->sm_scale,
-                              sh->variant & ~SAGE_TRAIN_NO_SMOOTH_K, p);
+                              sh->variant & ~kTrainOnly, p);
   if (rc != SAGE_OK) return rc;
+  p->variant |= sh->variant & SAGE_TRAIN_RECOMPUTE_DS;  // read by the backward's layout and launch
   if (sh->Hkv != sh->Hq) return SAGE_ERR_UNSUPPORTED;
   *smooth_k = (sh->variant & SAGE_TRAIN_NO_SMOOTH_K) == 0;
   return SAGE_OK;

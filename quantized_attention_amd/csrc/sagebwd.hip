@@ -551,6 +551,166 @@ __device__ __forceinline__ void sb_q_frags(const BwdArgs& a, int bh, int qrow, i
   }
 }
 
+// dQ of one lane's query row (channels 32 c + 8 b + 4 h + k), with the K-mean term
+// sm rowsum(dS) mean(K) when K was smoothed.  Each channel group's K-mean loads are issued
+// before its stores (which the compiler must otherwise order after every possibly aliasing store).
+template <int D>
+__device__ __forceinline__ void sb_dq_store(const BwdArgs& a, int bh, int qrow, int h, float rs,
+                                            const v16f (&dq)[D / 32]) {
+  const size_t orow = ((size_t)bh * a.N + qrow) * D;
+#pragma unroll
+  for (int c = 0; c < D / 32; c++) {
+    float4 km4[4] = {};
+    if (a.kmean)
+#pragma unroll
+      for (int b = 0; b < 4; b++)
+        km4[b] = *reinterpret_cast<const float4*>(a.kmean + (size_t)bh * D + 32 * c + 8 * b + 4 * h);
+#pragma unroll
+    for (int b = 0; b < 4; b++) {
+      const int ch = 32 * c + 8 * b + 4 * h;
+      const float kmv[4] = {km4[b].x, km4[b].y, km4[b].z, km4[b].w};
+      float o[4];
+#pragma unroll
+      for (int k = 0; k < 4; k++) o[k] = a.kmean ? fmaf(a.sm * rs, kmv[k], dq[c][4 * b + k]) : dq[c][4 * b + k];
+      store_out4<2>(a.dq, orow + ch, o);
+    }
+  }
+}
+
+// ---- dQ with dS recomputed (SAGE_TRAIN_RECOMPUTE_DS, or a pair buffer beyond kSbPairLimit):
+// one work-group per (head, 128-query block); loops over the key blocks.  The key block's K^
+// rows, K^ transposed and 16-bit V rows stream into a 2-slot LDS ring by DMA: block j+1 is in
+// flight while block j is computed, one barrier per block publishes the next.  S, P, dP and dS
+// come from the same elementwise part as in the dK/dV kernel, so both see the same dS^ ----
+template <int D, bool CAUSAL, bool FP16>
+__global__ __launch_bounds__(256, 2) void sb_dq_recompute_kernel(BwdArgs a) {
+  constexpr int NKS = D / 32;
+  using TK = SbTile<kBK, D>;      // K^ rows
+  using TT = SbTile<D, kBK>;      // K^ transposed, keys in i8perm order
+  using TV = SbTile<kBK, 2 * D>;  // V rows, 16-bit
+  __shared__ __attribute__((aligned(1024))) int8_t sK[2][TK::BYTES];
+  __shared__ __attribute__((aligned(1024))) int8_t sKt[2][TT::BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t sVb[2][TV::BYTES];
+  __shared__ float xs[8];
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int bh, qi;
+  sb_map(a.nqb, bh, qi);
+  const int qb = CAUSAL ? (a.nqb - 1 - qi) : qi;
+  const int q0 = qb * kBQ, qrow = q0 + 32 * w + col;
+  v4i qf[NKS];
+  v4i of[D / 16];
+  sb_q_frags<D>(a, bh, qrow, h, qf, of);
+  const float l2 = a.L2[(size_t)bh * a.Np + qrow], dr = a.Dr[(size_t)bh * a.Np + qrow];
+  const float sq = a.sq[(size_t)bh * a.nqb + qb];
+  v16f dq[NKS];
+#pragma unroll
+  for (int c = 0; c < NKS; c++)
+#pragma unroll
+    for (int r = 0; r < 16; r++) dq[c][r] = 0.0f;
+  float rs = 0.0f;
+  const int jend = CAUSAL ? max(0, min(a.nkt, (q0 + kBQ + a.coff + kBK - 1) / kBK)) : a.nkt;
+
+  // per-lane DMA source offsets inside a block (V: row and byte column; its rows are clamped to
+  // the last key, a stand-in for keys >= M, whose P and dS are 0)
+  int ko[TK::NPW], to[TT::NPW], vr[TV::NPW], vc[TV::NPW];
+#pragma unroll
+  for (int i = 0; i < TK::NPW; i++) {
+    int r, c;
+    TK::src(w, i, lane, r, c);
+    ko[i] = r * D + 16 * c;
+  }
+#pragma unroll
+  for (int i = 0; i < TT::NPW; i++) {
+    int r, c;
+    TT::src(w, i, lane, r, c);
+    to[i] = r * kBK + 16 * c;
+  }
+#pragma unroll
+  for (int i = 0; i < TV::NPW; i++) {
+    int r, c;
+    TV::src(w, i, lane, r, c);
+    vr[i] = r;
+    vc[i] = 16 * c;
+  }
+  auto dma = [&](int j, int b) {
+    const int8_t* kr = a.kh + ((size_t)bh * a.Mp + (size_t)j * kBK) * D;
+    const int8_t* kt = a.kt + ((size_t)bh * a.nkt + j) * (size_t)D * kBK;
+    const uint16_t* vb = a.V + ((size_t)bh * a.M + (size_t)j * kBK) * D;
+    const int vlast = a.M - 1 - j * kBK;  // >= 0: block j holds a key
+#pragma unroll
+    for (int i = 0; i < TK::NPW; i++) dma16(lds_addr(&sK[b][(TK::NPW * w + i) * 1024]), kr, ko[i]);
+#pragma unroll
+    for (int i = 0; i < TT::NPW; i++) dma16(lds_addr(&sKt[b][(TT::NPW * w + i) * 1024]), kt, to[i]);
+#pragma unroll
+    for (int i = 0; i < TV::NPW; i++)
+      dma16(lds_addr(&sVb[b][(TV::NPW * w + i) * 1024]), vb, min(vr[i], vlast) * (2 * D) + vc[i]);
+  };
+  if (jend > 0) dma(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // block 0 landed
+  for (int j = 0; j < jend; j++) {
+    const int b = j & 1;
+    if (j + 1 < jend) dma(j + 1, b ^ 1);  // the slot block j-1 left (freed by the last barrier)
+    const int8_t* cK = sK[b];
+    const int8_t* cKt = sKt[b];
+    const uint8_t* cV = sVb[b];
+    v4i kf[2][NKS];
+#pragma unroll
+    for (int T = 0; T < 2; T++)
+#pragma unroll
+      for (int s = 0; s < NKS; s++) kf[T][s] = *reinterpret_cast<const v4i*>(&cK[TK::off(32 * T + col, 2 * s + h)]);
+    const int key0 = j * kBK;
+    int lim = a.M - 1 - key0;
+    if (CAUSAL) lim = min(lim, qrow + a.coff - key0);
+    lim -= 4 * h;
+    float P[2][16], dS[2][16];
+    auto vfrag = [&](int T, int s) {
+      return *reinterpret_cast<const v4i*>(&cV[TV::off(32 * T + col, 2 * s + h)]);
+    };
+    const bool masked = key0 + kBK > a.M || (CAUSAL && key0 + kBK - 1 > q0 + 32 * w + a.coff);
+    sb_pair<D, FP16>(kf, qf, of, vfrag, sq * a.sk[(size_t)bh * a.nkt + j] * a.qk_scale, l2, dr, masked, lim, h, col, P,
+                     dS);
+    float dm = 0.0f;
+#pragma unroll
+    for (int T = 0; T < 2; T++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        dm = fmaxf(dm, fabsf(dS[T][r]));
+        rs += dS[T][r];
+      }
+    const float dmax = sb_block_max_ds(dm, xs, lane, w);
+    const float inv = dmax > 0.0f ? __fdiv_rn(127.0f, dmax) : 0.0f;
+    const float sds = __fdiv_rn(dmax, 127.0f);
+    v4i db[2];
+#pragma unroll
+    for (int T = 0; T < 2; T++)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; q4++) {
+        db[T][q4] = (int)sb_pack4(sb_code8(dS[T][4 * q4 + 0], inv), sb_code8(dS[T][4 * q4 + 1], inv),
+                                  sb_code8(dS[T][4 * q4 + 2], inv), sb_code8(dS[T][4 * q4 + 3], inv));
+      }
+    const float osc = sds * a.sk[(size_t)bh * a.nkt + j] * a.sm;
+#pragma unroll
+    for (int c = 0; c < NKS; c++) {
+      v16i R;
+#pragma unroll
+      for (int r = 0; r < 16; r++) R[r] = 0;
+#pragma unroll
+      for (int T = 0; T < 2; T++) {
+        const v4i kt = *reinterpret_cast<const v4i*>(&cKt[TT::off(32 * c + col, 2 * T + h)]);
+        R = __builtin_amdgcn_mfma_i32_32x32x32_i8(kt, db[T], R, 0, 0, 0);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; r++) dq[c][r] = fmaf((float)R[r], osc, dq[c][r]);
+    }
+    // block j+1 landed (this wave's DMAs, then everyone's); slot b may be refilled
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+  rs = pair_sum(rs);
+  if (qrow >= a.N) return;
+  sb_dq_store<D>(a, bh, qrow, h, rs, dq);
+}
+
 // ---- dQ: one work-group per (head, 128-query block); loops over the key blocks.  The dK/dV
 // kernel (launched first) leaves each pair's dS^ codes in this kernel's B-operand order, the
 // pair's scale and its per-query sums of dS; here dQ = sum_j dS^_j K^_j s_j sm_scale contracts
@@ -633,32 +793,13 @@ __global__ __launch_bounds__(256, 4) void sb_dq_kernel(BwdArgs a) {
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
   if (qrow >= a.N) return;
-  const size_t orow = ((size_t)bh * a.N + qrow) * D;
-#pragma unroll
-  for (int c = 0; c < NKS; c++) {
-    // the group's K-mean loads all issued before its stores (which the compiler must otherwise
-    // order after every possibly aliasing store)
-    float4 km4[4] = {};
-    if (a.kmean)
-#pragma unroll
-      for (int b = 0; b < 4; b++)
-        km4[b] = *reinterpret_cast<const float4*>(a.kmean + (size_t)bh * D + 32 * c + 8 * b + 4 * h);
-#pragma unroll
-    for (int b = 0; b < 4; b++) {
-      const int ch = 32 * c + 8 * b + 4 * h;
-      const float kmv[4] = {km4[b].x, km4[b].y, km4[b].z, km4[b].w};
-      float o[4];
-#pragma unroll
-      for (int k = 0; k < 4; k++) o[k] = a.kmean ? fmaf(a.sm * rs, kmv[k], dq[c][4 * b + k]) : dq[c][4 * b + k];
-      store_out4<2>(a.dq, orow + ch, o);
-    }
-  }
+  sb_dq_store<D>(a, bh, qrow, h, rs, dq);
 }
 
 // ---- dK, dV: one work-group per (head, 64-key block); loops over the query blocks.  P^ and
 // dS^ of a pair go to LDS key-major; wave w then owns key half w % 2 and half of the channel
 // groups of both outputs, and contracts over the block's 128 queries ----
-template <int D, bool CAUSAL, bool FP16>
+template <int D, bool CAUSAL, bool FP16, bool STORE>
 __global__ __launch_bounds__(256, 2) void sb_dkv_kernel(BwdArgs a) {
   constexpr int NKS = D / 32, NG = NKS / 2, VS = D + 8, PS = kBQ + 16;
   using TQ = SbTile<D, kBQ>;  // dO^ and Q^ transposed: [channel][query] of one query block
@@ -781,8 +922,8 @@ __global__ __launch_bounds__(256, 2) void sb_dkv_kernel(BwdArgs a) {
       l2 = a.L2[(size_t)bh * a.Np + qn];
       dr = a.Dr[(size_t)bh * a.Np + qn];
     }
-    {  // the pair's dS^, scale and row sums for the dQ kernel: stored after the barrier, so that
-       // its wait on this block's memory operations does not wait on them as well
+    if (STORE) {  // the pair's dS^, scale and row sums for the dQ kernel: stored after the
+                  // barrier, so that its wait on this block's memory operations does not wait on them
       // non-temporal: read once, by another kernel; they need not displace this kernel's tiles in L2
       int8_t* dst = a.dsh + pr * 8192 + (size_t)(64 * w + lane) * 32;
       __builtin_nontemporal_store(db[0], reinterpret_cast<v4i*>(dst));
@@ -845,6 +986,11 @@ enum SbSlice { kSbQh, kSbQt, kSbSq, kSbKh, kSbKt, kSbSk, kSbVt, kSbSv, kSbDot, k
                kSbKpart, kSbVpart, kSbVmax, kSbVmin, kSbKmean, kSbVmean, kSbDv, kSbDsh, kSbDss, kSbDrs,
                kSbSlices };
 
+bool sb_store_ds(const Problem& p) {
+  const size_t pairs = (size_t)p.BH * p.nqb * p.nkt;
+  return !(p.variant & SAGE_TRAIN_RECOMPUTE_DS) && pairs * (8192 + 4 + kBQ * 4) <= kSbPairLimit;
+}
+
 size_t sb_layout(const Problem& p, bool bwd, size_t* s) {
   const size_t BH = (size_t)p.BH, d = (size_t)p.d;
   size_t z[kSbSlices];
@@ -867,10 +1013,11 @@ size_t sb_layout(const Problem& p, bool bwd, size_t* s) {
   z[kSbKmean] = BH * d * 4;
   z[kSbVmean] = BH * d * 4;
   z[kSbDv] = BH * d * 4;
-  const size_t pairs = BH * p.nqb * p.nkt;  // (query block, key block) pairs: dS^ of the backward
-  z[kSbDsh] = bwd ? pairs * 8192 : 0;
-  z[kSbDss] = bwd ? pairs * 4 : 0;
-  z[kSbDrs] = bwd ? pairs * kBQ * 4 : 0;
+  const bool pb = bwd && sb_store_ds(p);  // the pair buffer: dS^ of every (query, key) block pair
+  const size_t pairs = BH * p.nqb * p.nkt;
+  z[kSbDsh] = pb ? pairs * 8192 : 0;
+  z[kSbDss] = pb ? pairs * 4 : 0;
+  z[kSbDrs] = pb ? pairs * kBQ * 4 : 0;
   size_t tot = 0;
   for (int i = 0; i < kSbSlices; i++) {
     if (s) s[i] = tot;
@@ -985,9 +1132,14 @@ hipError_t sb_prep_bwd(const Problem& p, const void* out, const void* dout, cons
 
 template <int D, bool CAUSAL, bool FP16>
 void sb_bwd_launch(const Problem& p, const BwdArgs& a, hipStream_t st) {
-  // dK/dV first: it leaves every pair's dS^ for the dQ contraction
-  hipLaunchKernelGGL((sb_dkv_kernel<D, CAUSAL, FP16>), dim3(p.nkt * p.BH), dim3(256), 0, st, a);
-  hipLaunchKernelGGL((sb_dq_kernel<D, CAUSAL>), dim3(p.nqb * p.BH), dim3(256), 0, st, a);
+  if (sb_store_ds(p)) {
+    // dK/dV first: it leaves every pair's dS^ for the dQ contraction
+    hipLaunchKernelGGL((sb_dkv_kernel<D, CAUSAL, FP16, true>), dim3(p.nkt * p.BH), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((sb_dq_kernel<D, CAUSAL>), dim3(p.nqb * p.BH), dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((sb_dq_recompute_kernel<D, CAUSAL, FP16>), dim3(p.nqb * p.BH), dim3(256), 0, st, a);
+    hipLaunchKernelGGL((sb_dkv_kernel<D, CAUSAL, FP16, false>), dim3(p.nkt * p.BH), dim3(256), 0, st, a);
+  }
 }
 
 template <int D>

@@ -9,6 +9,11 @@ namespace sage {
 // K, V (K smoothed when smooth_k), the forward (out, lse), the backward's preprocessing (dO^,
 // D, L) and the backward (dq, dk, dv in FP32).
 size_t sb_layout(const Problem& p, bool bwd, size_t* offsets);
+// Whether the backward keeps every (query block, key block) pair's dS^ (the dK/dV kernel writes
+// it, the dQ kernel contracts it) or the dQ kernel recomputes dS: the latter with
+// SAGE_TRAIN_RECOMPUTE_DS, or when the pair buffer would exceed kSbPairLimit bytes.
+constexpr size_t kSbPairLimit = (size_t)16 << 30;
+bool sb_store_ds(const Problem& p);
 hipError_t sb_prep_fwd(const Problem& p, const void* q, const void* k, const void* v, char* ws, bool bwd,
                        bool smooth_k, hipStream_t st);
 hipError_t sb_forward(const Problem& p, char* ws, bool bwd, void* out, float* lse, hipStream_t st);

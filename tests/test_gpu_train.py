@@ -93,14 +93,17 @@ def rel_err(got, ref):
     return e.max() / max(1.0, np.abs(ref).max()), e.mean() / max(1.0, np.abs(ref).mean())
 
 
+@pytest.mark.parametrize("recompute", [False, True], ids=["stored_ds", "recomputed_ds"])
 @pytest.mark.parametrize("name,cfg,smooth_k", CASES, ids=[c[0] for c in CASES])
-def test_train_backward_parity(name, cfg, smooth_k):
+def test_train_backward_parity(name, cfg, smooth_k, recompute):
     q, k, v = sy.make_qkv(cfg)
     do = rand_bits(q.shape, cfg.fp16, 41)
-    say(f"train backward {name} B={cfg.B} H={cfg.H} N={cfg.N} M={cfg.M} d={cfg.d} causal={cfg.causal}")
+    say(f"train backward {name} B={cfg.B} H={cfg.H} N={cfg.N} M={cfg.M} d={cfg.d} causal={cfg.causal} "
+        f"recompute_ds={recompute}")
     tq, tk, tv, tdo = (gu.to_dev(x, cfg.fp16) for x in (q, k, v, do))
     out, lse = qa.sage_attn_train_forward(tq, tk, tv, cfg.causal, None, out_fp32=True, smooth_k=smooth_k)
-    dq, dk, dv = qa.sage_attn_train_backward(tq, tk, tv, out, tdo, lse, cfg.causal, None, smooth_k=smooth_k)
+    dq, dk, dv = qa.sage_attn_train_backward(tq, tk, tv, out, tdo, lse, cfg.causal, None, smooth_k=smooth_k,
+                                             recompute_ds=recompute)
     torch.cuda.synchronize()
     dq, dk, dv = dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()
     s = 1 / math.sqrt(cfg.d)
@@ -121,6 +124,26 @@ def test_train_backward_parity(name, cfg, smooth_k):
     for nm, (mx, mn, cos) in worst.items():
         say(f"  {nm}: max rel {mx:.3g} mean rel {mn:.3g} cos vs exact {cos:.5f}")
         assert np.isfinite(mx) and mx <= 1e-2 and mn <= 1e-3, nm
+
+
+@pytest.mark.parametrize("name,cfg,smooth_k", CASES, ids=[c[0] for c in CASES])
+def test_stored_and_recomputed_ds_agree(name, cfg, smooth_k):
+    """The two backward forms compute the same dS^ codes: dK and dV bit-identical; dQ equal up to the
+    FP32 order of the K-mean term's row sums (bit-identical without K smoothing)."""
+    q, k, v = sy.make_qkv(cfg)
+    do = rand_bits(q.shape, cfg.fp16, 43)
+    tq, tk, tv, tdo = (gu.to_dev(x, cfg.fp16) for x in (q, k, v, do))
+    out, lse = qa.sage_attn_train_forward(tq, tk, tv, cfg.causal, None, out_fp32=True, smooth_k=smooth_k)
+    a = qa.sage_attn_train_backward(tq, tk, tv, out, tdo, lse, cfg.causal, None, smooth_k=smooth_k)
+    b = qa.sage_attn_train_backward(tq, tk, tv, out, tdo, lse, cfg.causal, None, smooth_k=smooth_k,
+                                    recompute_ds=True)
+    torch.cuda.synchronize()
+    (dqa, dka, dva), (dqb, dkb, dvb) = ([t.cpu().numpy() for t in x] for x in (a, b))
+    assert np.array_equal(dka, dkb) and np.array_equal(dva, dvb)
+    if smooth_k:
+        assert np.abs(dqa.astype(np.float64) - dqb).max() <= 1e-5 * max(1.0, np.abs(dqb).max())
+    else:
+        assert np.array_equal(dqa, dqb)
 
 
 def test_train_full_size():
