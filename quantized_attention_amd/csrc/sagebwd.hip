@@ -752,26 +752,36 @@ __global__ __launch_bounds__(256, 4) void sb_dq_kernel(BwdArgs a) {
   const size_t p0 = ((size_t)bh * a.nqb + qb) * a.nkt;  // pair (qb, 0)
   const int8_t* dsrc = a.dsh + p0 * 8192 + (size_t)(64 * w + lane) * 32;
   const float* rsrc = a.drs + p0 * kBQ + 32 * w + col;
+  const float* dssp = a.dss + p0;                  // the pairs' scales max|dS| / 127
+  const float* skp = a.sk + (size_t)bh * a.nkt;    // the key blocks' K^ scales
   v4i db[2] = {}, dbn[2];
-  float rv = 0.0f, rvn;
+  float rv = 0.0f, rvn, ds = 0.0f, dsn, sk = 0.0f, skn;
   if (jend > 0) {
     dma(0, 0);
     db[0] = *reinterpret_cast<const v4i*>(dsrc);
     db[1] = *reinterpret_cast<const v4i*>(dsrc + 16);
     rv = rsrc[0];
+    ds = dssp[0];
+    sk = skp[0];
   }
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // block 0 landed
   for (int j = 0; j < jend; j++) {
     const int b = j & 1;
+    // this pair's loaded values, all landed at the last barrier: an empty use here puts the
+    // compiler's wait for them before the DMA below, so that the wait cannot also hold on it
+    asm volatile("" ::"v"(db[0]), "v"(db[1]), "v"(rv), "v"(ds), "v"(sk));
     if (j + 1 < jend) dma(j + 1, b ^ 1);  // the slot block j-1 left (freed by the last barrier)
-    {  // the next pair's codes and row sums (the last pair reloads its own), in flight meanwhile
+    {  // the next pair's codes, row sums and scales (the last pair reloads its own), in flight
+       // meanwhile: nothing loaded from memory is waited for inside the iteration
       const int jn = j + 1 < jend ? j + 1 : j;
       dbn[0] = *reinterpret_cast<const v4i*>(dsrc + (size_t)jn * 8192);
       dbn[1] = *reinterpret_cast<const v4i*>(dsrc + (size_t)jn * 8192 + 16);
       rvn = rsrc[(size_t)jn * kBQ];
+      dsn = dssp[jn];
+      skn = skp[jn];
     }
     rs += rv;
-    const float osc = a.dss[p0 + j] * a.sk[(size_t)bh * a.nkt + j] * a.sm;
+    const float osc = ds * sk * a.sm;
     const int8_t* cKt = sKt[b];
 #pragma unroll
     for (int c = 0; c < NKS; c++) {
@@ -789,6 +799,8 @@ __global__ __launch_bounds__(256, 4) void sb_dq_kernel(BwdArgs a) {
     db[0] = dbn[0];
     db[1] = dbn[1];
     rv = rvn;
+    ds = dsn;
+    sk = skn;
     // block j+1 landed (this wave's DMAs, then everyone's); slot b may be refilled
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
