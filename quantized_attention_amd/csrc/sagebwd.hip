@@ -543,13 +543,17 @@ __device__ __forceinline__ void sb_q_frags(const BwdArgs& a, int bh, int qrow, i
   const int8_t* qp = a.qh + ((size_t)bh * a.Np + qrow) * D + 16 * h;
 #pragma unroll
   for (int s = 0; s < D / 32; s++) qf[s] = *reinterpret_cast<const v4i*>(qp + 32 * s);
-  const bool ok = qrow < a.N;
-  const uint16_t* op = a.dO + ((size_t)bh * a.N + (ok ? qrow : 0)) * D + 8 * h;
+  // rows past N (the last block's padding) read row 0 instead: every lane issues the same loads,
+  // and the loaded values cannot matter, since such a row's P is exactly 0 (its log-sum-exp is
+  // stored as +inf) and its dS = P (dP - 0) with dP finite
+  const uint16_t* op = a.dO + ((size_t)bh * a.N + (qrow < a.N ? qrow : 0)) * D + 8 * h;
 #pragma unroll
-  for (int s = 0; s < D / 16; s++) {
-    of[s] = ok ? *reinterpret_cast<const v4i*>(op + 16 * s) : v4i{0, 0, 0, 0};
-  }
+  for (int s = 0; s < D / 16; s++) of[s] = *reinterpret_cast<const v4i*>(op + 16 * s);
 }
+// Vector memory loads of one query block's prefetch in the dK / dV kernel: sb_q_frags, the two
+// row scalars and the block's two scales.  Its barrier waits for everything issued before them.
+template <int D>
+constexpr int kSbRowLoads = D / 32 + D / 16 + 4;
 
 // dQ of one lane's query row (channels 32 c + 8 b + 4 h + k), with the K-mean term
 // sm rowsum(dS) mean(K) when K was smoothed.  Each channel group's K-mean loads are issued
@@ -856,17 +860,29 @@ __global__ __launch_bounds__(256, 2) void sb_dkv_kernel(BwdArgs a) {
   const int ilo = CAUSAL ? max(0, (key0 - a.coff) / kBQ) : 0;
   // this wave's query rows of the first block; each later block's rows are loaded while the
   // block before it is contracted into dV and dK
+  // (with the block's Q^ and dO^ scales: loads that the kernel's own stores might alias, so the
+  // compiler issues them as vector loads, which must not be waited for next to the DMAs)
   v4i qf[NKS];
   v4i of[D / 16];
-  float l2 = 0.0f, dr = 0.0f;
+  float l2 = 0.0f, dr = 0.0f, sqb = 0.0f, sdob = 0.0f;
   if (ilo < a.nqb) {
     const int qr = ilo * kBQ + 32 * w + col;
     sb_q_frags<D>(a, bh, qr, h, qf, of);
     l2 = a.L2[(size_t)bh * a.Np + qr];
     dr = a.Dr[(size_t)bh * a.Np + qr];
+    sqb = a.sq[(size_t)bh * a.nqb + ilo];
+    sdob = a.sdo[(size_t)bh * a.nqb + ilo];
   }
   for (int i = ilo; i < a.nqb; i++) {
     __syncthreads();  // the previous pair's LDS reads are done (and V is staged, i = ilo)
+    // the block's rows and scales, loaded during the previous block: an empty use here puts the
+    // compiler's wait for them before the DMAs below, so that the wait cannot also hold on those
+#pragma unroll
+    for (int s = 0; s < NKS; s++) asm volatile("" ::"v"(qf[s]));
+#pragma unroll
+    for (int s = 0; s < D / 16; s++) asm volatile("" ::"v"(of[s]));
+    asm volatile("" ::"v"(l2), "v"(dr), "v"(sqb), "v"(sdob));
+    const float sqi = sqb, sdoi = sdob;  // this block's Q^ and dO^ scales
     const int q0 = i * kBQ, qrow = q0 + 32 * w + col;
     {
       // the block's dO^ and Q^ transposed for the dV / dK products, by DMA: they land while the
@@ -887,8 +903,17 @@ __global__ __launch_bounds__(256, 2) void sb_dkv_kernel(BwdArgs a) {
       return *reinterpret_cast<const v4i*>(sVb + (32 * T + col) * VS + 16 * s + 8 * h);
     };
     const bool masked = key0 + kBK > a.M || (CAUSAL && key0 + kBK - 1 > q0 + 32 * w + a.coff);
-    sb_pair<D, FP16>(kf, qf, of, vfrag, a.sq[(size_t)bh * a.nqb + i] * skj * a.qk_scale, l2, dr, masked, lim, h, col, P,
-                     dS);
+    sb_pair<D, FP16>(kf, qf, of, vfrag, sqi * skj * a.qk_scale, l2, dr, masked, lim, h, col, P, dS);
+    {  // the next block's rows and scales (the last block reloads its own), issued as soon as the
+       // products above have read these: in flight through the block maxima, the codes and dV / dK
+      const int in = i + 1 < a.nqb ? i + 1 : i;
+      const int qn = in * kBQ + 32 * w + col;
+      sb_q_frags<D>(a, bh, qn, h, qf, of);
+      l2 = a.L2[(size_t)bh * a.Np + qn];
+      dr = a.Dr[(size_t)bh * a.Np + qn];
+      sqb = a.sq[(size_t)bh * a.nqb + in];
+      sdob = a.sdo[(size_t)bh * a.nqb + in];
+    }
     float pm = 0.0f, dm = 0.0f;
 #pragma unroll
     for (int T = 0; T < 2; T++)
@@ -924,16 +949,17 @@ __global__ __launch_bounds__(256, 2) void sb_dkv_kernel(BwdArgs a) {
         db[T][q4] = (int)sb_pack4(dc[0], dc[1], dc[2], dc[3]);
       }
     rsp = pair_sum(rsp);
-    // P^ / dS^ visible, and this block's dO^ / Q^ transposed landed (every wave's DMAs)
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    const float vsc = __fdiv_rn(pmax, 127.0f) * a.sdo[(size_t)bh * a.nqb + i];
-    const float ksc = __fdiv_rn(dmax, 127.0f) * a.sq[(size_t)bh * a.nqb + i] * a.sm;
-    {  // the next block's rows (the last block reloads its own), in flight during the products
-      const int qn = i + 1 < a.nqb ? qrow + kBQ : qrow;
-      sb_q_frags<D>(a, bh, qn, h, qf, of);
-      l2 = a.L2[(size_t)bh * a.Np + qn];
-      dr = a.Dr[(size_t)bh * a.Np + qn];
-    }
+    // P^ / dS^ visible, and this block's dO^ / Q^ transposed landed (every wave's DMAs): vector
+    // memory operations complete in issue order, so waiting until only the next block's row
+    // loads (the last ones issued) are outstanding covers everything before them
+    if constexpr (kSbRowLoads<D> == 16)
+      asm volatile("s_waitcnt vmcnt(16) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if constexpr (kSbRowLoads<D> == 10)
+      asm volatile("s_waitcnt vmcnt(10) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+      static_assert(kSbRowLoads<D> == 16 || kSbRowLoads<D> == 10, "row load count");
+    const float vsc = __fdiv_rn(pmax, 127.0f) * sdoi;
+    const float ksc = __fdiv_rn(dmax, 127.0f) * sqi * a.sm;
     if (STORE) {  // the pair's dS^, scale and row sums for the dQ kernel: stored after the
                   // barrier, so that its wait on this block's memory operations does not wait on them
       // non-temporal: read once, by another kernel; they need not displace this kernel's tiles in L2
