@@ -231,11 +231,30 @@ __global__ __launch_bounds__(256, 2) void sb_fwd_kernel(FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < TV::NPW; i++) dma16(lds_addr(&sV[b][(TV::NPW * w + i) * 1024]), vt, vo[i]);
   };
+  // The blocks' K^ and V^ scales: loads that the kernel's own stores might alias, so the compiler
+  // issues them as vector loads.  Each block's pair is loaded during the block before it; empty
+  // uses put the compiler's waits for these (and for the Q^ rows) before the DMAs, so that no
+  // wait of its own inside a block can also hold on the next block's DMA.
+  float skn = 0.0f, svn = 0.0f;
+  if (jend > 0) {
+    skn = a.sk[(size_t)bh * a.nkt];
+    svn = a.sv[(size_t)bh * a.nkt];
+  }
+#pragma unroll
+  for (int s = 0; s < NKS; s++) asm volatile("" ::"v"(qf[s]));
+  asm volatile("" ::"v"(sqk));
   if (jend > 0) dma(0, 0);
   asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // block 0 landed
   for (int j = 0; j < jend; j++) {
     const int b = j & 1;
+    const float skj = skn, svj = svn;  // this block's scales
+    asm volatile("" ::"v"(skj), "v"(svj));
     if (j + 1 < jend) dma(j + 1, b ^ 1);  // the slot block j-1 left (freed by the last barrier)
+    {  // the next block's scales (the last block reloads its own)
+      const int jn = j + 1 < jend ? j + 1 : j;
+      skn = a.sk[(size_t)bh * a.nkt + jn];
+      svn = a.sv[(size_t)bh * a.nkt + jn];
+    }
     const int key0 = j * kBK;
     if (!(CAUSAL && key0 > wq0 + 31 + a.coff)) {  // else every key of the block is masked for this wave
       const int8_t* cK = sK[b];
@@ -251,7 +270,7 @@ __global__ __launch_bounds__(256, 2) void sb_fwd_kernel(FwdArgs a) {
           acc[T] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[s], acc[T], 0, 0, 0);
         }
       }
-      const float mul = sqk * a.sk[(size_t)bh * a.nkt + j];
+      const float mul = sqk * skj;
       float sc[2][16];
       int lim = a.M - 1 - key0;
       if (CAUSAL) lim = min(lim, qrow + a.coff - key0);
@@ -310,7 +329,7 @@ __global__ __launch_bounds__(256, 2) void sb_fwd_kernel(FwdArgs a) {
       // s_P = exp2(rm - m) / 127 against the running max m, here against m_ref
       const float sp = (rm == -INFINITY) ? 0.0f : fast_exp2(rm - m_ref) * (1.0f / 127.0f);
       l_run = fmaf(esum, sp, l_run);
-      const float osc = sp * a.sv[(size_t)bh * a.nkt + j];
+      const float osc = sp * svj;
 #pragma unroll
       for (int c = 0; c < NKS; c++) {
         v16i R;
