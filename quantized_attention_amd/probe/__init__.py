@@ -32,8 +32,9 @@ def load():
         L.sage_probe_cvt_e4m3.argtypes = [u, u, P, P]
         L.sage_probe_mfma_rate.argtypes = [i, i, i, P, P]
         L.sage_probe_valu_rate.argtypes = [i, i, i, ctypes.c_float, P, P]
+        L.sage_probe_stream.argtypes = [i, P, ctypes.c_ulonglong, P, P]
         for f in (L.sage_probe_mfma_f8, L.sage_probe_mfma_i8, L.sage_probe_cvt_e4m3, L.sage_probe_mfma_rate,
-                  L.sage_probe_valu_rate):
+                  L.sage_probe_valu_rate, L.sage_probe_stream):
             f.restype = i
         _lib = L
     return _lib
@@ -114,3 +115,19 @@ def valu_rate(kind: int, blocks: int = 2048, iters: int = 1024, repeats: int = 3
         best = min(best, e0.elapsed_time(e1))
     waves = blocks * 4
     return waves * iters * VALU_KINDS[kind][1] / (best * 1e6)
+
+
+def stream_rate(kind: int, buf, nbytes: int) -> float:
+    """Reads (kind 0) or writes (kind 1) the first nbytes of the device tensor buf once, timed with
+    events on the current stream; returns TB/s.  Whatever ran before on the stream (a buffer read or
+    written just before) is what the caller measures against."""
+    import torch
+    if nbytes > buf.numel() * buf.element_size():
+        raise ValueError("nbytes exceeds the buffer")
+    sink = torch.zeros(1, dtype=torch.float32, device=buf.device)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    _check(load().sage_probe_stream(kind, buf.data_ptr(), nbytes, sink.data_ptr(), _stream()), "stream")
+    e1.record()
+    e1.synchronize()
+    return nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e12

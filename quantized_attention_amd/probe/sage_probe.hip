@@ -10,7 +10,9 @@
 //   * the INT8 MFMA (v_mfma_i32_32x32x32_i8) sums exactly;
 //   * the E4M3 conversion (v_cvt_pk_fp8_f32) rounds to nearest even, and the kernels' clamp to
 //     +-448 before it gives the saturating E4M3 of the pages' "FP8 Quantization for P~V";
-//   * the matrix-core rates behind the roofline (INT8, FP8, and block-scaled FP4).
+//   * the matrix-core rates behind the roofline (INT8, FP8, and block-scaled FP4);
+//   * the HBM rates behind the preprocessing's floor: streaming reads and writes, and a buffer
+//     read again after its first read (the statistics and quantization passes both read K and V).
 // Every kernel runs a bounded amount of work on buffers sized by the caller; the entry points
 // only enqueue work on `stream` and return a hipError_t value (0 = success).
 #include <hip/hip_runtime.h>
@@ -133,6 +135,25 @@ __global__ __launch_bounds__(256) void valu_rate(int iters, float seed, float* s
   sink[blockIdx.x * 256 + threadIdx.x] = s;
 }
 
+// Streams n16 16-byte pieces of buf over a grid-stride loop: kind 0 reads them (the sum reaches
+// sink only if it is NaN, so the loads stay and nothing is written for finite data), kind 1
+// writes them.
+__global__ __launch_bounds__(256) void stream_rw(int kind, float4* buf, size_t n16, float* sink) {
+  const size_t step = (size_t)gridDim.x * blockDim.x;
+  size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (kind == 0) {
+    float s = 0.0f;
+    for (; i < n16; i += step) {
+      const float4 v = buf[i];
+      s += v.x + v.y + v.z + v.w;
+    }
+    if (s != s) sink[0] = s;
+  } else {
+    const float4 z = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    for (; i < n16; i += step) buf[i] = z;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -183,6 +204,15 @@ int sage_probe_valu_rate(int kind, int blocks, int iters, float seed, float* sin
     case 4: hipLaunchKernelGGL(valu_rate<4>, dim3(blocks), dim3(256), 0, s, iters, seed, sink); break;
     default: hipLaunchKernelGGL(valu_rate<5>, dim3(blocks), dim3(256), 0, s, iters, seed, sink); break;
   }
+  return (int)hipGetLastError();
+}
+
+// Reads (kind 0) or writes zeros to (kind 1) the first `bytes` of buf (a multiple of 16) with
+// 8192 work-groups of 256 lanes.  sink: one float, written only if the data read sums to NaN.
+int sage_probe_stream(int kind, void* buf, unsigned long long bytes, float* sink, void* stream) {
+  if (kind < 0 || kind > 1 || bytes == 0 || bytes % 16) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(stream_rw, dim3(8192), dim3(256), 0, (hipStream_t)stream, kind, (float4*)buf,
+                     (size_t)(bytes / 16), sink);
   return (int)hipGetLastError();
 }
 

@@ -204,3 +204,34 @@ def test_valu_rates():
     t_sum = 0.5 / rates[1] + 0.5 / fma       # half of them exp, half fma, if they add up
     say(f"exp + fma interleaved: {t_mix / t_sum:.2f} of the sum of their separate times")
     assert t_mix >= 0.8 * t_sum
+
+
+def test_hbm_reread_rates():
+    """The preprocessing reads K and V twice (statistics, then quantization).  Running the second
+    read right after the first, one group of heads at a time, would pay only if the Infinity
+    Cache served a re-read much faster than HBM.  Measured here: cold reads of 128 and 256 MiB
+    (after 2 GiB of other reads), the same buffer read again at once, and read again after 256
+    MiB of writes in between; plus plain streaming writes.  Only plausibility is asserted; the
+    printed rates are the evidence."""
+    import torch
+    MiB = 1 << 20
+    A = torch.zeros(256 * MiB // 4, dtype=torch.float32, device="cuda")
+    F = torch.zeros(2048 * MiB // 4, dtype=torch.float32, device="cuda")
+    W = torch.zeros(256 * MiB // 4, dtype=torch.float32, device="cuda")
+    med = lambda xs: sorted(xs)[len(xs) // 2]  # noqa: E731
+    rates = []
+    for size in (128 * MiB, 256 * MiB):
+        cold, again, after = [], [], []
+        for _ in range(3):
+            probe.stream_rate(0, F, 2048 * MiB)  # evicts A from every cache
+            cold.append(probe.stream_rate(0, A, size))
+            again.append(probe.stream_rate(0, A, size))
+            probe.stream_rate(1, W, 256 * MiB)
+            after.append(probe.stream_rate(0, A, size))
+        say(f"read {size // MiB} MiB: cold {med(cold):.2f} TB/s, again at once {med(again):.2f}, "
+            f"again after 256 MiB of writes {med(after):.2f}")
+        rates += cold + again + after
+    writes = [probe.stream_rate(1, W, 256 * MiB) for _ in range(3)]
+    say(f"write 256 MiB: {med(writes):.2f} TB/s")
+    rates += writes
+    assert all(0.5 < r < 30.0 for r in rates), rates
