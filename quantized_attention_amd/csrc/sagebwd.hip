@@ -461,10 +461,9 @@ struct BwdArgs {
   float* dk;           // [BH][M][D]
   float* dv;           // [BH][M][D]
   // dS^ of each (128-query block i, 64-key block j) pair, written by the dK/dV kernel and
-  // contracted by the dQ kernel: pair (i, j) of head bh is p = (bh nqb + i) nkt + j
-  int8_t* dsh;         // [pairs][4 waves][64 lanes][32]: the lane's codes in the dQ product's B order
-  float* dss;          // [pairs] max|dS| / 127
-  float* drs;          // [pairs][128] sum over the pair's keys of dS (FP32), per query
+  // contracted by the dQ kernel: pair (i, j) of head bh is p = (bh nqb + i) nkt + j, one
+  // kSbRec-byte record per pair and wave (the wave's 32 queries)
+  int8_t* dsh;         // [pairs][4 waves][kSbRec]
   int N, M, nqb, nkt, Np, Mp, coff;
   float qk_scale;      // sm_scale * log2(e)
   float sm;            // sm_scale
@@ -735,15 +734,20 @@ __global__ __launch_bounds__(256, 2) void sb_dq_recompute_kernel(BwdArgs a) {
 }
 
 // ---- dQ: one work-group per (head, 128-query block); loops over the key blocks.  The dK/dV
-// kernel (launched first) leaves each pair's dS^ codes in this kernel's B-operand order, the
-// pair's scale and its per-query sums of dS; here dQ = sum_j dS^_j K^_j s_j sm_scale contracts
-// them against the key block's K^ transposed, which streams through a 2-slot LDS ring by DMA
-// (block j+1 in flight while block j is used, one barrier per block) ----
+// kernel (launched first) leaves, per pair and wave, a record of the dS^ codes in this kernel's
+// B-operand order, the per-query sums of dS and the pair's multiplier; here
+// dQ = sum_j dS^_j K^_j (max|dS_j| / 127) s_j sm_scale contracts them against the key block's K^
+// transposed.  Both stream in by DMA: K^ transposed through a 2-slot LDS ring (block j+1 in
+// flight while block j is used), the records through a 3-slot one (record j+2 in flight), one
+// barrier per block; no wait inside a block holds on memory ----
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 4) void sb_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 3) void sb_dq_kernel(BwdArgs a) {
   constexpr int NKS = D / 32;
   using TT = SbTile<D, kBK>;  // K^ transposed, keys in i8perm order
   __shared__ __attribute__((aligned(1024))) int8_t sKt[2][TT::BYTES];
+  // a 3-slot ring of the pairs' records, one kSbRec-byte record per wave: the record of pair j+2
+  // streams in while pair j is contracted (and pair j+1's, already landed, waits)
+  __shared__ __attribute__((aligned(1024))) int8_t sRec[3][4][kSbRec];
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   int bh, qi;
@@ -772,61 +776,57 @@ __global__ __launch_bounds__(256, 4) void sb_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < TT::NPW; i++) dma16(base + 1024 * i, kt, to[i]);
   };
-  const size_t p0 = ((size_t)bh * a.nqb + qb) * a.nkt;  // pair (qb, 0)
-  const int8_t* dsrc = a.dsh + p0 * 8192 + (size_t)(64 * w + lane) * 32;
-  const float* rsrc = a.drs + p0 * kBQ + 32 * w + col;
-  const float* dssp = a.dss + p0;                  // the pairs' scales max|dS| / 127
-  const float* skp = a.sk + (size_t)bh * a.nkt;    // the key blocks' K^ scales
-  v4i db[2] = {}, dbn[2];
-  float rv = 0.0f, rvn, ds = 0.0f, dsn, sk = 0.0f, skn;
+  // this wave's record of pair (qb, jj) into ring slot r: the codes (two 1 KiB halves), then the
+  // row sums (lanes 0-31) and the pair's multiplier (lanes 32-63 all fetch it): three DMAs
+  const int8_t* rbase = a.dsh + (((size_t)bh * a.nqb + qb) * a.nkt * 4 + w) * kSbRec;
+  const uint32_t rec0 = lds_addr(&sRec[0][w][0]);
+  const uint32_t tail_off = lane < 32 ? 2048 + 4 * lane : 2048 + 4 * 32;
+  auto fetch = [&](int jj, int r) {
+    const int8_t* g = rbase + (size_t)jj * 4 * kSbRec;
+    const uint32_t l = rec0 + (uint32_t)r * 4 * kSbRec;
+    dma16(l, g, 16 * lane);
+    dma16(l + 1024, g, 1024 + 16 * lane);
+    dma4(l + 2048, g, tail_off);
+  };
   if (jend > 0) {
     dma(0, 0);
-    db[0] = *reinterpret_cast<const v4i*>(dsrc);
-    db[1] = *reinterpret_cast<const v4i*>(dsrc + 16);
-    rv = rsrc[0];
-    ds = dssp[0];
-    sk = skp[0];
+    fetch(0, 0);
+    fetch(min(1, jend - 1), 1);
   }
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // block 0 landed
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");  // block 0 and records 0, 1 landed
+  int r = 0;  // ring slot of pair j's record
   for (int j = 0; j < jend; j++) {
     const int b = j & 1;
-    // this pair's loaded values, all landed at the last barrier: an empty use here puts the
-    // compiler's wait for them before the DMA below, so that the wait cannot also hold on it
-    asm volatile("" ::"v"(db[0]), "v"(db[1]), "v"(rv), "v"(ds), "v"(sk));
     if (j + 1 < jend) dma(j + 1, b ^ 1);  // the slot block j-1 left (freed by the last barrier)
-    {  // the next pair's codes, row sums and scales (the last pair reloads its own), in flight
-       // meanwhile: nothing loaded from memory is waited for inside the iteration
-      const int jn = j + 1 < jend ? j + 1 : j;
-      dbn[0] = *reinterpret_cast<const v4i*>(dsrc + (size_t)jn * 8192);
-      dbn[1] = *reinterpret_cast<const v4i*>(dsrc + (size_t)jn * 8192 + 16);
-      rvn = rsrc[(size_t)jn * kBQ];
-      dsn = dssp[jn];
-      skn = skp[jn];
-    }
-    rs += rv;
-    const float osc = ds * sk * a.sm;
+    // pair j+2's record (the last pairs fetch pair jend-1 again, into a slot nobody reads) into the
+    // slot pair j-1 left; always three DMAs, which the wait below leaves in flight
+    fetch(min(j + 2, jend - 1), r == 0 ? 2 : r - 1);
+    const int8_t* rec = &sRec[r][w][0];
+    const v4i db0 = *reinterpret_cast<const v4i*>(rec + 16 * lane);
+    const v4i db1 = *reinterpret_cast<const v4i*>(rec + 1024 + 16 * lane);
+    const float* tail = reinterpret_cast<const float*>(rec + 2048);
+    rs += tail[col];
+    const float osc = tail[32];  // (max|dS| / 127) s_K sm_scale
     const int8_t* cKt = sKt[b];
 #pragma unroll
     for (int c = 0; c < NKS; c++) {
       v16i R;
 #pragma unroll
-      for (int r = 0; r < 16; r++) R[r] = 0;
+      for (int rr = 0; rr < 16; rr++) R[rr] = 0;
+      const v4i kt0 = *reinterpret_cast<const v4i*>(&cKt[TT::off(32 * c + col, h)]);
+      const v4i kt1 = *reinterpret_cast<const v4i*>(&cKt[TT::off(32 * c + col, 2 + h)]);
+      R = __builtin_amdgcn_mfma_i32_32x32x32_i8(kt0, db0, R, 0, 0, 0);
+      R = __builtin_amdgcn_mfma_i32_32x32x32_i8(kt1, db1, R, 0, 0, 0);
 #pragma unroll
-      for (int T = 0; T < 2; T++) {
-        const v4i kt = *reinterpret_cast<const v4i*>(&cKt[TT::off(32 * c + col, 2 * T + h)]);
-        R = __builtin_amdgcn_mfma_i32_32x32x32_i8(kt, db[T], R, 0, 0, 0);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; r++) dq[c][r] = fmaf((float)R[r], osc, dq[c][r]);
+      for (int rr = 0; rr < 16; rr++) dq[c][rr] = fmaf((float)R[rr], osc, dq[c][rr]);
     }
-    db[0] = dbn[0];
-    db[1] = dbn[1];
-    rv = rvn;
-    ds = dsn;
-    sk = skn;
-    // block j+1 landed (this wave's DMAs, then everyone's); slot b may be refilled
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    r = r == 2 ? 0 : r + 1;
+    // block j+1 and record j+1 landed (this wave's DMAs, then everyone's; only the three of
+    // record j+2, issued last, may still be in flight); slot b and record slot r-1 may be refilled
+    asm volatile("s_waitcnt vmcnt(3) lgkmcnt(0)\n\ts_barrier" ::: "memory");
   }
+  // no DMA may still write this work-group's LDS when it ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if (qrow >= a.N) return;
   sb_dq_store<D>(a, bh, qrow, h, rs, dq);
 }
@@ -979,14 +979,16 @@ __global__ __launch_bounds__(256, 2) void sb_dkv_kernel(BwdArgs a) {
       static_assert(kSbRowLoads<D> == 16 || kSbRowLoads<D> == 10, "row load count");
     const float vsc = __fdiv_rn(pmax, 127.0f) * sdoi;
     const float ksc = __fdiv_rn(dmax, 127.0f) * sqi * a.sm;
-    if (STORE) {  // the pair's dS^, scale and row sums for the dQ kernel: stored after the
-                  // barrier, so that its wait on this block's memory operations does not wait on them
-      // non-temporal: read once, by another kernel; they need not displace this kernel's tiles in L2
-      int8_t* dst = a.dsh + pr * 8192 + (size_t)(64 * w + lane) * 32;
-      __builtin_nontemporal_store(db[0], reinterpret_cast<v4i*>(dst));
-      __builtin_nontemporal_store(db[1], reinterpret_cast<v4i*>(dst + 16));
-      if (lane < 32) __builtin_nontemporal_store(rsp, a.drs + pr * kBQ + qc);
-      if (tid == 0) a.dss[pr] = __fdiv_rn(dmax, 127.0f);
+    if (STORE) {  // the wave's record of the pair for the dQ kernel: stored after the barrier, so
+                  // that its wait on this block's memory operations does not wait on the stores;
+                  // non-temporal: read once, by another kernel, it need not displace this kernel's
+                  // tiles in L2
+      int8_t* rec = a.dsh + (pr * 4 + w) * kSbRec;
+      __builtin_nontemporal_store(db[0], reinterpret_cast<v4i*>(rec + 16 * lane));
+      __builtin_nontemporal_store(db[1], reinterpret_cast<v4i*>(rec + 1024 + 16 * lane));
+      float* tail = reinterpret_cast<float*>(rec + 2048);
+      if (lane < 32) __builtin_nontemporal_store(rsp, tail + lane);
+      else if (lane == 32) __builtin_nontemporal_store(__fdiv_rn(dmax, 127.0f) * skj * a.sm, tail + 32);
     }
 #pragma unroll
     for (int g = 0; g < NG; g++) {
@@ -1040,12 +1042,11 @@ __global__ __launch_bounds__(256, 2) void sb_dkv_kernel(BwdArgs a) {
 
 // Workspace slices of SageBwd (256-byte aligned).
 enum SbSlice { kSbQh, kSbQt, kSbSq, kSbKh, kSbKt, kSbSk, kSbVt, kSbSv, kSbDot, kSbSdo, kSbD, kSbL2,
-               kSbKpart, kSbVpart, kSbVmax, kSbVmin, kSbKmean, kSbVmean, kSbDv, kSbDsh, kSbDss, kSbDrs,
-               kSbSlices };
+               kSbKpart, kSbVpart, kSbVmax, kSbVmin, kSbKmean, kSbVmean, kSbDv, kSbDsh, kSbSlices };
 
 bool sb_store_ds(const Problem& p) {
   const size_t pairs = (size_t)p.BH * p.nqb * p.nkt;
-  return !(p.variant & SAGE_TRAIN_RECOMPUTE_DS) && pairs * (8192 + 4 + kBQ * 4) <= kSbPairLimit;
+  return !(p.variant & SAGE_TRAIN_RECOMPUTE_DS) && pairs * 4 * kSbRec <= kSbPairLimit;
 }
 
 size_t sb_layout(const Problem& p, bool bwd, size_t* s) {
@@ -1072,9 +1073,7 @@ size_t sb_layout(const Problem& p, bool bwd, size_t* s) {
   z[kSbDv] = BH * d * 4;
   const bool pb = bwd && sb_store_ds(p);  // the pair buffer: dS^ of every (query, key) block pair
   const size_t pairs = BH * p.nqb * p.nkt;
-  z[kSbDsh] = pb ? pairs * 8192 : 0;
-  z[kSbDss] = pb ? pairs * 4 : 0;
-  z[kSbDrs] = pb ? pairs * kBQ * 4 : 0;
+  z[kSbDsh] = pb ? pairs * 4 * kSbRec : 0;
   size_t tot = 0;
   for (int i = 0; i < kSbSlices; i++) {
     if (s) s[i] = tot;
@@ -1225,8 +1224,6 @@ hipError_t sb_backward(const Problem& p, char* ws, bool smooth_k, const void* v,
   a.dO = (const uint16_t*)dout;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.dsh = (int8_t*)(ws + o[kSbDsh]);
-  a.dss = (float*)(ws + o[kSbDss]);
-  a.drs = (float*)(ws + o[kSbDrs]);
   a.N = p.N; a.M = p.M; a.nqb = p.nqb; a.nkt = p.nkt; a.Np = p.Np; a.Mp = p.Mp;
   a.coff = p.causal == 2 ? p.M - p.N : 0;
   a.qk_scale = p.sm_scale * kLog2e;

@@ -13,6 +13,11 @@ size_t sb_layout(const Problem& p, bool bwd, size_t* offsets);
 // it, the dQ kernel contracts it) or the dQ kernel recomputes dS: the latter with
 // SAGE_TRAIN_RECOMPUTE_DS, or when the pair buffer would exceed kSbPairLimit bytes.
 constexpr size_t kSbPairLimit = (size_t)16 << 30;
+// The pair buffer holds one record per (pair, wave of the pair's query block): the wave's dS^
+// codes in the dQ product's B-operand order (two halves of 64 lanes x 16 bytes), the FP32 sums of
+// dS over the pair's keys for the wave's 32 queries, the pair's dQ multiplier
+// (max|dS| / 127) s_K sm_scale, and padding to 2304 bytes.
+constexpr int kSbRec = 2304;
 bool sb_store_ds(const Problem& p);
 hipError_t sb_prep_fwd(const Problem& p, const void* q, const void* k, const void* v, char* ws, bool bwd,
                        bool smooth_k, hipStream_t st);
