@@ -239,7 +239,9 @@ def train_cpu_baseline(cfg, n=1024):
 
 
 def main_train(args, cfg):
-    """A SageBwd training step of the attention: forward (out, lse) then backward (dq, dk, dv)."""
+    """A SageBwd training step of the attention: forward (out, lse) then backward (dq, dk, dv), both on
+    one workspace with SAGE_TRAIN_KEEP_QUANT: the forward quantizes Q, K and V once and leaves them
+    there for the backward, as a training framework keeps the forward's activations."""
     import torch
 
     import quantized_attention_amd as qa
@@ -259,7 +261,7 @@ def main_train(args, cfg):
     dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
     dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
     shape = qa.SageAttnShape(cfg.B, cfg.H, cfg.H, cfg.N, cfg.M, cfg.d, int(cfg.causal), 1.0 / math.sqrt(cfg.d),
-                             qa.SAGE_IN_BF16)
+                             qa.SAGE_IN_BF16 | qa.SAGE_TRAIN_KEEP_QUANT)
     ws_bytes = qa.sage_attn_train_workspace_bytes(shape)
     ws = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
     ws_ptr = (ws.data_ptr() + 255) // 256 * 256
@@ -330,6 +332,7 @@ def main_train(args, cfg):
         "frac_of_peak": round(value / PEAK_TOPS, 4),
         "forward_ms": round(f_ms, 4),
         "backward_ms": round(b_ms, 4),
+        "train_mode": "the forward quantizes Q, K, V once and the backward reuses them (SAGE_TRAIN_KEEP_QUANT)",
         "roofline": {"bound": "mfma", "achieved": round(value, 2), "peak": PEAK_TOPS, "unit": "TOPS",
                      "frac": round(value / PEAK_TOPS, 4), "traffic": None,
                      "note": "whole step (preprocessing included) against the INT8 peak; dO V^T runs at the bf16 rate"},

@@ -283,12 +283,21 @@ int sage_attn_varlen_fwd(const sage_attn_varlen_shape* shape, const void* q, con
  * pointers, 16-byte aligned (lse 4-byte); outputs must not overlap inputs.
  */
 #define SAGE_TRAIN_NO_SMOOTH_K 0x4000u /* ablation: K is not smoothed (training entry points) */
-/* sage_attn_train_bwd keeps each (128-query, 64-key) block pair's INT8 dS^ (about 8.5 KiB per
- * pair, in the workspace) from its dK/dV kernel for its dQ kernel; with this bit, or when that
+/* sage_attn_train_bwd keeps each (128-query, 64-key) block pair's INT8 dS^ (9 KiB per pair,
+ * in the workspace) from its dK/dV kernel for its dQ kernel; with this bit, or when that
  * buffer would exceed 16 GiB, the dQ kernel recomputes S, P, dP and dS instead (slower, with a
  * workspace of a few bytes per token).  Both give the same dK and dV; dQ agrees to FP32
  * rounding (the order of the K-mean term's row sums). */
 #define SAGE_TRAIN_RECOMPUTE_DS 0x8000u
+/* Both training calls of one step, with this bit and the same caller workspace: the forward
+ * leaves its INT8 Q^, K^, V^ (with their scales, the backward's transposed copies and K's mean)
+ * in the workspace, and the backward takes them from there instead of quantizing q, k, v again,
+ * as a training framework keeps the forward's activations for the backward.  The caller
+ * guarantees that between the two calls nothing writes the workspace and q, k, v keep their
+ * contents, and passes the same shape (SAGE_TRAIN_RECOMPUTE_DS may differ: the pair buffer is the
+ * workspace's last part).  Either call with this bit and a NULL workspace returns
+ * SAGE_ERR_INVALID_ARG.  Results are identical to those of the two calls without it. */
+#define SAGE_TRAIN_KEEP_QUANT 0x10000u
 size_t sage_attn_train_workspace_bytes(const sage_attn_shape* shape);
 int sage_attn_train_fwd(const sage_attn_shape* shape, const void* q, const void* k, const void* v, void* out,
                         float* lse, void* workspace, size_t ws_bytes, void* stream);

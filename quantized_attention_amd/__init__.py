@@ -23,7 +23,7 @@ __all__ = [
     "sage_attn_version", "sage_attn_set_profile_events", "sage_attn", "QuantViews",
     "SageAttnShape", "sage_attn_fwd_ex", "sage_attn_workspace_bytes_ex", "sage_attn_quantize_ex",
     "SageAttnVarlenShape", "sage_attn_varlen_workspace_bytes", "sage_attn_varlen_fwd", "sage_attn_varlen",
-    "SAGE_TRAIN_NO_SMOOTH_K", "SAGE_TRAIN_RECOMPUTE_DS", "sage_attn_train_workspace_bytes", "sage_attn_train_fwd", "sage_attn_train_bwd",
+    "SAGE_TRAIN_NO_SMOOTH_K", "SAGE_TRAIN_RECOMPUTE_DS", "SAGE_TRAIN_KEEP_QUANT", "sage_attn_train_workspace_bytes", "sage_attn_train_fwd", "sage_attn_train_bwd",
     "sage_attn_train_forward", "sage_attn_train_backward", "SageBwdAttention",
     "SAGE_NOALLOC_MAX_BYTES", "sage_attn_fwd_noalloc",
 ]
@@ -47,6 +47,7 @@ SAGE_OUT_FP32 = 0x1000
 SAGE_ACC_VALU = 0x2000
 SAGE_TRAIN_NO_SMOOTH_K = 0x4000
 SAGE_TRAIN_RECOMPUTE_DS = 0x8000
+SAGE_TRAIN_KEEP_QUANT = 0x10000
 
 SAGE_BQ = 128
 SAGE_BK = 64
@@ -342,7 +343,7 @@ def sage_attn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max
 
 
 # ---------------------------------------------------------------- SageBwd (training)
-def _train_shape(q, k, v, causal, sm_scale, out_fp32, smooth_k, recompute_ds=False):
+def _train_shape(q, k, v, causal, sm_scale, out_fp32, smooth_k, recompute_ds=False, keep=False):
     """The SageBwd shape of q [B, H, N, d] and k, v [B, Hkv, M, d]; shapes are checked here so
     that no mismatched buffer reaches the kernels (the library itself rejects Hkv != H)."""
     import torch
@@ -359,6 +360,8 @@ def _train_shape(q, k, v, causal, sm_scale, out_fp32, smooth_k, recompute_ds=Fal
         var |= SAGE_TRAIN_NO_SMOOTH_K
     if recompute_ds:
         var |= SAGE_TRAIN_RECOMPUTE_DS
+    if keep:
+        var |= SAGE_TRAIN_KEEP_QUANT
     scale = float(sm_scale) if sm_scale is not None else 1.0 / math.sqrt(d)
     return SageAttnShape(B, H, Hkv, N, M, d, int(causal), scale, var)
 
@@ -373,31 +376,49 @@ def _check_train_inputs(*ts):
     _check_device(ts, ts[0].device)
 
 
-def sage_attn_train_forward(q, k, v, causal: int = 0, sm_scale: float | None = None, out_fp32: bool = False,
-                            smooth_k: bool = True):
-    """SageBwd forward: (out [B, H, N, d], lse [B, H, N] FP32) for q [B, H, N, d], k/v [B, H, M, d]."""
+def _train_context(shape, device):
+    """A workspace for one training step's two calls (SAGE_TRAIN_KEEP_QUANT): a uint8 tensor and its
+    256-byte aligned pointer and size."""
     import torch
-    shape = _train_shape(q, k, v, causal, sm_scale, out_fp32, smooth_k)
+    n = sage_attn_train_workspace_bytes(shape)
+    if n == 0:
+        raise SageError(SAGE_ERR_INVALID_ARG, "sage_attn_train_workspace_bytes")
+    ws = torch.empty(n + 256, dtype=torch.uint8, device=device)
+    return ws, (ws.data_ptr() + 255) // 256 * 256, n
+
+
+def sage_attn_train_forward(q, k, v, causal: int = 0, sm_scale: float | None = None, out_fp32: bool = False,
+                            smooth_k: bool = True, keep: bool = False):
+    """SageBwd forward: (out [B, H, N, d], lse [B, H, N] FP32) for q [B, H, N, d], k/v [B, H, M, d].
+    keep: also return a context (a device workspace holding the INT8 Q, K, V) for
+    sage_attn_train_backward(ctx=...), which then does not quantize q, k, v again
+    (SAGE_TRAIN_KEEP_QUANT); q, k, v must not change in between."""
+    import torch
+    shape = _train_shape(q, k, v, causal, sm_scale, out_fp32, smooth_k, keep=keep)
     _check_train_inputs(q, k, v)
     B, H, N, d = q.shape
     out = torch.empty((B, H, N, d), dtype=torch.float32 if out_fp32 else q.dtype, device=q.device)
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    ctx = _train_context(shape, q.device) if keep else None
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         rc = sage_attn_train_fwd(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                                 None, 0, stream)
+                                 ctx[1] if keep else None, ctx[2] if keep else 0, stream)
     if rc != SAGE_OK:
         raise SageError(rc, "sage_attn_train_fwd")
-    return out, lse
+    return (out, lse, ctx) if keep else (out, lse)
 
 
 def sage_attn_train_backward(q, k, v, out, dout, lse, causal: int = 0, sm_scale: float | None = None,
-                             smooth_k: bool = True, recompute_ds: bool = False):
+                             smooth_k: bool = True, recompute_ds: bool = False, ctx=None):
     """SageBwd backward: (dq, dk, dv) in FP32, from the forward's out (its dtype) and lse.
     recompute_ds: the dQ kernel recomputes dS instead of reading the dK/dV kernel's stored dS^
-    codes (SAGE_TRAIN_RECOMPUTE_DS: slower, with a small workspace)."""
+    codes (SAGE_TRAIN_RECOMPUTE_DS: slower, with a small workspace).  ctx: the context of
+    sage_attn_train_forward(keep=True) on the same q, k, v (same causal, sm_scale, smooth_k and
+    recompute_ds); the quantized inputs are then taken from it."""
     import torch
-    shape = _train_shape(q, k, v, causal, sm_scale, out.dtype == torch.float32, smooth_k, recompute_ds)
+    keep = ctx is not None
+    shape = _train_shape(q, k, v, causal, sm_scale, out.dtype == torch.float32, smooth_k, recompute_ds, keep)
     B, H, N, d = q.shape
     if tuple(dout.shape) != (B, H, N, d) or tuple(out.shape) != (B, H, N, d):
         raise ValueError("out and dout must be [B, H, N, d] like q")
@@ -410,10 +431,13 @@ def sage_attn_train_backward(q, k, v, out, dout, lse, causal: int = 0, sm_scale:
     dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
     dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    if keep and (ctx[0].device != q.device or ctx[2] < sage_attn_train_workspace_bytes(shape)):
+        raise ValueError("ctx comes from a forward of another shape or device")
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream(q.device).cuda_stream
         rc = sage_attn_train_bwd(shape, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), dout.data_ptr(),
-                                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), None, 0, stream)
+                                 lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                 ctx[1] if keep else None, ctx[2] if keep else 0, stream)
     if rc != SAGE_OK:
         raise SageError(rc, "sage_attn_train_bwd")
     return dq, dk, dv
@@ -430,16 +454,18 @@ def _sagebwd_function():
         @staticmethod
         def forward(ctx, q, k, v, causal=0, sm_scale=None):
             q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-            out, lse = sage_attn_train_forward(q, k, v, causal, sm_scale)
+            # the INT8 Q, K, V stay in a workspace for the backward, as activations do
+            out, lse, ws = sage_attn_train_forward(q, k, v, causal, sm_scale, keep=True)
             ctx.save_for_backward(q, k, v, out, lse)
-            ctx.causal, ctx.sm_scale = causal, sm_scale
+            ctx.causal, ctx.sm_scale, ctx.ws = causal, sm_scale, ws
             return out
 
         @staticmethod
         def backward(ctx, dout):
             q, k, v, out, lse = ctx.saved_tensors
             dq, dk, dv = sage_attn_train_backward(q, k, v, out, dout.contiguous().to(q.dtype), lse, ctx.causal,
-                                                  ctx.sm_scale)
+                                                  ctx.sm_scale, ctx=ctx.ws)
+            ctx.ws = None
             return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None
 
     return SageBwdAttention

@@ -263,12 +263,13 @@ void* scratch_on_current_device() {
 // dtypes and the K-smoothing ablation.
 int make_train_problem(const sage_attn_shape* sh, Problem* p, bool* smooth_k) {
   if (!sh) return SAGE_ERR_INVALID_ARG;
-  constexpr unsigned kTrainOnly = SAGE_TRAIN_NO_SMOOTH_K | SAGE_TRAIN_RECOMPUTE_DS;
+  constexpr unsigned kTrainOnly = SAGE_TRAIN_NO_SMOOTH_K | SAGE_TRAIN_RECOMPUTE_DS | SAGE_TRAIN_KEEP_QUANT;
   if (sh->variant & ~(SAGE_IN_FP16 | SAGE_OUT_FP32 | kTrainOnly)) return SAGE_ERR_INVALID_ARG;
   const int rc = make_problem(sh->B, sh->Hq, sh->Hkv, sh->N, sh->M, sh->d, sh->causal, sh->sm_scale,
                               sh->variant & ~kTrainOnly, p);
   if (rc != SAGE_OK) return rc;
-  p->variant |= sh->variant & SAGE_TRAIN_RECOMPUTE_DS;  // read by the backward's layout and launch
+  // read by the backward's layout and launch, and by the keeping of the quantized inputs
+  p->variant |= sh->variant & (SAGE_TRAIN_RECOMPUTE_DS | SAGE_TRAIN_KEEP_QUANT);
   if (sh->Hkv != sh->Hq) return SAGE_ERR_UNSUPPORTED;
   *smooth_k = (sh->variant & SAGE_TRAIN_NO_SMOOTH_K) == 0;
   return SAGE_OK;
@@ -408,14 +409,18 @@ int sage_attn_train_fwd(const sage_attn_shape* shape, const void* q, const void*
   bool smooth_k;
   int rc = make_train_problem(shape, &p, &smooth_k);
   if (rc != SAGE_OK) return rc;
+  // keeping the quantized inputs for the backward: they go to the backward's layout of the
+  // caller's workspace
+  const bool keep = (p.variant & SAGE_TRAIN_KEEP_QUANT) != 0;
+  if (keep && !workspace) return SAGE_ERR_INVALID_ARG;
   if ((rc = check_io(q, k, v, out)) != SAGE_OK) return rc;
   if (!lse || (reinterpret_cast<uintptr_t>(lse) & 3u)) return SAGE_ERR_INVALID_ARG;
   if (workspace && ws_bytes < sb_layout(p, true, nullptr)) return SAGE_ERR_NO_MEMORY;
   if ((rc = device_check()) != SAGE_OK) return rc;
   hipStream_t s = (hipStream_t)stream;
-  return with_workspace(sb_layout(p, false, nullptr), workspace, ws_bytes, s, [&](char* ws) {
-    if (sb_prep_fwd(p, q, k, v, ws, false, smooth_k, s) != hipSuccess) return (int)SAGE_ERR_LAUNCH;
-    if (sb_forward(p, ws, false, out, lse, s) != hipSuccess) return (int)SAGE_ERR_LAUNCH;
+  return with_workspace(sb_layout(p, keep, nullptr), workspace, ws_bytes, s, [&](char* ws) {
+    if (sb_prep_fwd(p, q, k, v, ws, keep, smooth_k, s) != hipSuccess) return (int)SAGE_ERR_LAUNCH;
+    if (sb_forward(p, ws, keep, out, lse, s) != hipSuccess) return (int)SAGE_ERR_LAUNCH;
     return (int)SAGE_OK;
   });
 }
@@ -427,6 +432,8 @@ int sage_attn_train_bwd(const sage_attn_shape* shape, const void* q, const void*
   bool smooth_k;
   int rc = make_train_problem(shape, &p, &smooth_k);
   if (rc != SAGE_OK) return rc;
+  const bool keep = (p.variant & SAGE_TRAIN_KEEP_QUANT) != 0;  // the forward's Q^, K^, V^ are there
+  if (keep && !workspace) return SAGE_ERR_INVALID_ARG;
   if ((rc = check_io(q, k, v, out)) != SAGE_OK) return rc;
   if (!dout || !dq || !dk || !dv || !aligned16(dout) || !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
     return SAGE_ERR_INVALID_ARG;
@@ -434,7 +441,7 @@ int sage_attn_train_bwd(const sage_attn_shape* shape, const void* q, const void*
   if ((rc = device_check()) != SAGE_OK) return rc;
   hipStream_t s = (hipStream_t)stream;
   return with_workspace(sb_layout(p, true, nullptr), workspace, ws_bytes, s, [&](char* ws) {
-    if (sb_prep_fwd(p, q, k, v, ws, true, smooth_k, s) != hipSuccess) return (int)SAGE_ERR_LAUNCH;
+    if (!keep && sb_prep_fwd(p, q, k, v, ws, true, smooth_k, s) != hipSuccess) return (int)SAGE_ERR_LAUNCH;
     if (sb_prep_bwd(p, out, dout, lse, ws, s) != hipSuccess) return (int)SAGE_ERR_LAUNCH;
     if (sb_backward(p, ws, smooth_k, v, dout, dq, dk, dv, s) != hipSuccess) return (int)SAGE_ERR_LAUNCH;
     return (int)SAGE_OK;

@@ -1040,9 +1040,12 @@ __global__ __launch_bounds__(256, 2) void sb_dkv_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------- host side
 
-// Workspace slices of SageBwd (256-byte aligned).
+// Workspace slices of SageBwd (256-byte aligned).  The pair buffer comes last: the other slices
+// sit at the same offsets with or without it, which lets a backward with SAGE_TRAIN_RECOMPUTE_DS
+// take the quantized inputs a forward without it kept (SAGE_TRAIN_KEEP_QUANT).
 enum SbSlice { kSbQh, kSbQt, kSbSq, kSbKh, kSbKt, kSbSk, kSbVt, kSbSv, kSbDot, kSbSdo, kSbD, kSbL2,
                kSbKpart, kSbVpart, kSbVmax, kSbVmin, kSbKmean, kSbVmean, kSbDv, kSbDsh, kSbSlices };
+static_assert(kSbDsh == kSbSlices - 1, "the pair buffer is the last slice");
 
 bool sb_store_ds(const Problem& p) {
   const size_t pairs = (size_t)p.BH * p.nqb * p.nkt;

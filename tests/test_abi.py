@@ -191,7 +191,17 @@ def test_train_workspace_holds_the_pair_buffer_up_to_its_limit():
     # 32 heads of 32768 tokens: 4 Mi pairs, 36 GB of pair buffer -> the recomputing form
     big = (1, 32, 32768, 32768, 128, 1)
     assert ws(*big, 0) == ws(*big, qa.SAGE_TRAIN_RECOMPUTE_DS) > 0
-    assert ws(1, 2, 128, 128, 64, 0, 0x10000) == 0  # unknown bit
+    assert ws(1, 2, 128, 128, 64, 0, 0x20000) == 0  # unknown bit
+    assert ws(1, 2, 128, 128, 64, 0, qa.SAGE_TRAIN_KEEP_QUANT) == ws(1, 2, 128, 128, 64, 0, 0) > 0
+
+
+def test_kept_quantization_needs_a_caller_workspace():
+    """SAGE_TRAIN_KEEP_QUANT passes the forward's INT8 inputs to the backward through the caller's
+    workspace: either call without one is an invalid argument, rejected before any device work."""
+    A = 256
+    sh = qa.SageAttnShape(1, 2, 2, 128, 128, 64, 0, 0.0, qa.SAGE_IN_BF16 | qa.SAGE_TRAIN_KEEP_QUANT)
+    assert qa.sage_attn_train_fwd(sh, A, A, A, A, A, None, 0, None) == qa.SAGE_ERR_INVALID_ARG
+    assert qa.sage_attn_train_bwd(sh, A, A, A, A, A, A, A, A, A, None, 0, None) == qa.SAGE_ERR_INVALID_ARG
 
 
 def test_noalloc_rejects_problems_beyond_its_scratch():

@@ -146,6 +146,29 @@ def test_stored_and_recomputed_ds_agree(name, cfg, smooth_k):
         assert np.array_equal(dqa, dqb)
 
 
+@pytest.mark.parametrize("recompute", [False, True], ids=["stored_ds", "recomputed_ds"])
+@pytest.mark.parametrize("name,cfg,smooth_k", CASES, ids=[c[0] for c in CASES])
+def test_kept_quantization_gives_identical_results(name, cfg, smooth_k, recompute):
+    """SAGE_TRAIN_KEEP_QUANT: the forward leaves its INT8 Q, K, V in the step's workspace and the
+    backward takes them from there instead of quantizing again; the same codes, so out, lse, dq,
+    dk and dv are bit-identical to the two calls without it."""
+    q, k, v = sy.make_qkv(cfg)
+    do = rand_bits(q.shape, cfg.fp16, 47)
+    tq, tk, tv, tdo = (gu.to_dev(x, cfg.fp16) for x in (q, k, v, do))
+    say(f"kept quantization {name} recompute={recompute}")
+    o1, l1 = qa.sage_attn_train_forward(tq, tk, tv, cfg.causal, None, out_fp32=True, smooth_k=smooth_k)
+    g1 = qa.sage_attn_train_backward(tq, tk, tv, o1, tdo, l1, cfg.causal, None, smooth_k=smooth_k,
+                                     recompute_ds=recompute)
+    o2, l2, ctx = qa.sage_attn_train_forward(tq, tk, tv, cfg.causal, None, out_fp32=True, smooth_k=smooth_k,
+                                             keep=True)
+    g2 = qa.sage_attn_train_backward(tq, tk, tv, o2, tdo, l2, cfg.causal, None, smooth_k=smooth_k,
+                                     recompute_ds=recompute, ctx=ctx)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
 def test_train_full_size():
     """The train8k workload (B=1 H=32 N=M=8192 d=128 bf16 causal) in the launch configuration the
     benchmark times, FP32 outputs: the forward (out, lse) and all three gradients of the first
