@@ -52,7 +52,7 @@ __device__ __forceinline__ void widen8(const v4i& raw, bool fp16, float (&x)[8])
 // loads in flight (one wave load reads a row's 128 or 256 contiguous bytes), then adds them in
 // token order (FP64); for V also the max / min (one float2 per channel), and the sum when
 // smoothing.  Work-group u2 of key/value head bh: waves 0, 1 take chunk 2 u2 (K, V), waves
-// 2, 3 chunk 2 u2 + 1 ----
+// 2, 3 chunk 2 u2 + 1; with K only (SageBwd needs no V statistics), wave w takes chunk 4 u2 + w ----
 struct StatsArgs {
   const uint16_t* Q;
   const uint16_t* K;
@@ -74,6 +74,7 @@ struct StatsArgs {
   int nkv_x;      // work-groups of the K / V side per key/value head
   int nkv_total;  // work-groups of the K / V side
   bool fp16, smooth_v;
+  bool k_only;    // K's chunks only (no V statistics): every wave takes a chunk of K
 };
 
 template <int D>
@@ -81,8 +82,8 @@ __device__ __forceinline__ void kv_stats_block(const StatsArgs& a, int u2, int b
   constexpr int CPL = D / 64;  // channels per lane
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int u = 2 * u2 + (w >> 1);
-  const bool isv = (w & 1) != 0;
+  const int u = a.k_only ? 4 * u2 + w : 2 * u2 + (w >> 1);
+  const bool isv = !a.k_only && (w & 1) != 0;
   if (u >= a.nkt) return;
   const SeqRows R = seq_rows(a.kl, bh / a.Hkv, bh % a.Hkv, a.Hkv, D);
   const int t0 = u * kBK;
@@ -152,6 +153,7 @@ struct FinArgs {
   SeqLayout kl;
   int Hkv, d, nkt;
   bool smooth_v;
+  bool k_only;  // the K mean only (no V statistics were taken)
 };
 constexpr int kFinCh = 16;     // channels per work-group
 constexpr int kFinStage = 128;  // chunks staged per round
@@ -180,14 +182,14 @@ __global__ __launch_bounds__(256) void kv_finalize_kernel(FinArgs f) {
     const size_t o = ((size_t)bh * f.nkt + uu) * f.d + c0 + x % kFinCh;                       \
     rk[e] = *reinterpret_cast<const d2*>(f.kpart + o);                                        \
     if (f.smooth_v) rv[e] = *reinterpret_cast<const d2*>(f.vpart + o);                        \
-    rm[e] = *reinterpret_cast<const v4i*>(f.vmm + o);                                         \
+    if (!f.k_only) rm[e] = *reinterpret_cast<const v4i*>(f.vmm + o);                          \
   }
 #define SAGE_FIN_STORE(buf)                                                                   \
   _Pragma("unroll") for (int e = 0; e < kFinPieces; e++) {                                   \
     const int x = 2 * (tid + 256 * e);                                                        \
     *reinterpret_cast<d2*>(&sk[buf][x]) = rk[e];                                              \
     if (f.smooth_v) *reinterpret_cast<d2*>(&svs[buf][x]) = rv[e];                             \
-    *reinterpret_cast<v4i*>(&smm[buf][x]) = rm[e];                                            \
+    if (!f.k_only) *reinterpret_cast<v4i*>(&smm[buf][x]) = rm[e];                             \
   }
   double ks = 0.0, vs = 0.0;
   float mx = -INFINITY, mn = INFINITY;
@@ -211,7 +213,7 @@ __global__ __launch_bounds__(256) void kv_finalize_kernel(FinArgs f) {
         for (int e = 0; e < 8; e++)
           if (ub + e < ns) ks += x[e];
       }
-    } else if (tid >= 64 && tid < 64 + kFinCh) {
+    } else if (!f.k_only && tid >= 64 && tid < 64 + kFinCh) {
       const int cc = tid - 64;
       for (int ub = 0; ub < ns; ub += 8) {
         double x[8];
@@ -242,7 +244,7 @@ __global__ __launch_bounds__(256) void kv_finalize_kernel(FinArgs f) {
   // a sequence without keys (variable-length batches only) gets zero means and the floor scale
   if (tid < kFinCh) {
     f.kmean[(size_t)bh * f.d + c0 + tid] = M > 0 ? (float)(ks / (double)M) : 0.0f;
-  } else if (tid >= 64 && tid < 64 + kFinCh) {
+  } else if (!f.k_only && tid >= 64 && tid < 64 + kFinCh) {
     const int c = c0 + tid - 64;
     const float vm = (f.smooth_v && M > 0) ? (float)(vs / (double)M) : 0.0f;
     f.vmean[(size_t)bh * f.d + c] = vm;
@@ -685,7 +687,8 @@ hipError_t launch_stats(const Problem& p, const void* q, const void* k, const vo
   a.ql = p.ql; a.kl = p.kl;
   a.H = p.H; a.Hkv = p.Hkv; a.Np = p.Np; a.nqb = p.nqb; a.nkt = p.nkt;
   a.nq_blocks = q ? p.nqb * p.BH : 0;
-  a.nkv_x = (p.nkt + 1) / 2;
+  a.k_only = v == nullptr;  // K's mean only
+  a.nkv_x = a.k_only ? (p.nkt + 3) / 4 : (p.nkt + 1) / 2;
   a.fp16 = p.fp16;
   a.smooth_v = p.smooth_v;
   const long long blocks = (long long)a.nq_blocks + (long long)a.nkv_x * p.BHkv;
@@ -702,13 +705,24 @@ hipError_t launch_stats(const Problem& p, const void* q, const void* k, const vo
   return hipGetLastError();
 }
 
-hipError_t launch_kv_finalize(const Problem& p, const Workspace& w, hipStream_t s) {
+namespace {
+hipError_t kv_finalize(const Problem& p, const Workspace& w, hipStream_t s, bool k_only) {
   FinArgs f;
   f.kpart = w.kpart; f.vpart = w.vpart; f.vmm = w.vmm;
   f.kmean = w.kmean; f.vmean = w.vmean; f.dv = w.dv;
-  f.kl = p.kl; f.Hkv = p.Hkv; f.d = p.d; f.nkt = p.nkt; f.smooth_v = p.smooth_v;
+  f.kl = p.kl; f.Hkv = p.Hkv; f.d = p.d; f.nkt = p.nkt; f.smooth_v = p.smooth_v && !k_only;
+  f.k_only = k_only;
   hipLaunchKernelGGL(kv_finalize_kernel, dim3(p.BHkv * (p.d / kFinCh)), dim3(256), 0, s, f);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_kv_finalize(const Problem& p, const Workspace& w, hipStream_t s) {
+  return kv_finalize(p, w, s, false);
+}
+
+hipError_t launch_kv_finalize_k_only(const Problem& p, const Workspace& w, hipStream_t s) {
+  return kv_finalize(p, w, s, true);
 }
 
 hipError_t launch_kv_quant(const Problem& p, const void* k, const void* v, const Workspace& w,

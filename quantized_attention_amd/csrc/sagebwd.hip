@@ -1099,8 +1099,9 @@ hipError_t sb_prep_fwd(const Problem& p, const void* q, const void* k, const voi
   w.dv = (float*)(ws + o[kSbDv]);
   hipError_t e;
   if (smooth_k) {
-    if ((e = launch_stats(p, nullptr, k, v, w, st)) != hipSuccess) return e;
-    if ((e = launch_kv_finalize(p, w, st)) != hipSuccess) return e;
+    // K's mean only: V is quantized per block, with no statistics over all tokens
+    if ((e = launch_stats(p, nullptr, k, nullptr, w, st)) != hipSuccess) return e;
+    if ((e = launch_kv_finalize_k_only(p, w, st)) != hipSuccess) return e;
   }
   const float* km = smooth_k ? w.kmean : nullptr;
   const dim3 gq(p.nqb, p.BH), gk(p.nkt, p.BH);

@@ -19,6 +19,9 @@ constexpr size_t kSbPairLimit = (size_t)16 << 30;
 // (max|dS| / 127) s_K sm_scale, and padding to 2304 bytes.
 constexpr int kSbRec = 2304;
 bool sb_store_ds(const Problem& p);
+// The chunk reduction to K's mean alone, after launch_stats with v null (SageBwd takes no V
+// statistics); defined with the other preprocessing launchers.
+hipError_t launch_kv_finalize_k_only(const Problem& p, const Workspace& w, hipStream_t s);
 hipError_t sb_prep_fwd(const Problem& p, const void* q, const void* k, const void* v, char* ws, bool bwd,
                        bool smooth_k, hipStream_t st);
 hipError_t sb_forward(const Problem& p, char* ws, bool bwd, void* out, float* lse, hipStream_t st);
