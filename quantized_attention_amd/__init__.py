@@ -454,18 +454,19 @@ def _sagebwd_function():
         @staticmethod
         def forward(ctx, q, k, v, causal=0, sm_scale=None):
             q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
-            # the INT8 Q, K, V stay in a workspace for the backward, as activations do
-            out, lse, ws = sage_attn_train_forward(q, k, v, causal, sm_scale, keep=True)
+            # the backward quantizes q, k, v again: holding the forward's workspace (the INT8 inputs
+            # and, behind them, room for the backward's pair buffer) from each layer's forward to its
+            # backward would cost more memory than the quantization costs time
+            out, lse = sage_attn_train_forward(q, k, v, causal, sm_scale)
             ctx.save_for_backward(q, k, v, out, lse)
-            ctx.causal, ctx.sm_scale, ctx.ws = causal, sm_scale, ws
+            ctx.causal, ctx.sm_scale = causal, sm_scale
             return out
 
         @staticmethod
         def backward(ctx, dout):
             q, k, v, out, lse = ctx.saved_tensors
             dq, dk, dv = sage_attn_train_backward(q, k, v, out, dout.contiguous().to(q.dtype), lse, ctx.causal,
-                                                  ctx.sm_scale, ctx=ctx.ws)
-            ctx.ws = None
+                                                  ctx.sm_scale)
             return dq.to(q.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None
 
     return SageBwdAttention
