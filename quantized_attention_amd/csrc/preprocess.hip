@@ -138,11 +138,12 @@ __device__ __forceinline__ void kv_stats_block(const StatsArgs& a, int u2, int b
 }
 
 // ---- chunk statistics -> K mean, V_m (when smoothing) and the V scale ----
-// One work-group per (key/value head, 16 channels).  The partials of kFinStage chunks at a time
-// are staged in LDS by all 256 threads at once, double-buffered: the loads of the next round are
-// in flight while one thread per channel adds the current round in chunk order, as the pinned
-// order requires (threads c < 16 the K sums, threads 64 + c the V max / min and sums).  Each
-// chunk row of 16 channels is one 128-byte line of every partial array.
+// One work-group per key/value head, 3 d threads in three roles: thread c < d adds channel c's K
+// chunk sums, thread d + c takes channel c's V max / min, thread 2 d + c adds its V sums (when
+// smoothing); each in chunk order, as the pinned order requires.  A chunk's partials of one array
+// are d contiguous values, so the d threads of a role read each chunk row as one contiguous
+// piece (1 KiB for the FP64 sums at d = 128), a batch of rows at a time, two batches in flight
+// while a third is added.
 struct FinArgs {
   const double* kpart;
   const double* vpart;
@@ -155,98 +156,72 @@ struct FinArgs {
   bool smooth_v;
   bool k_only;  // the K mean only (no V statistics were taken)
 };
-constexpr int kFinCh = 16;     // channels per work-group
-constexpr int kFinStage = 128;  // chunks staged per round
-constexpr int kFinRound = kFinStage * kFinCh;  // elements of one array per round
-constexpr int kFinPieces = kFinRound / 512;    // 16-byte pieces of one array per thread and round
 
-__global__ __launch_bounds__(256) void kv_finalize_kernel(FinArgs f) {
-  __shared__ __attribute__((aligned(16))) double sk[2][kFinRound];
-  __shared__ __attribute__((aligned(16))) double svs[2][kFinRound];
-  __shared__ __attribute__((aligned(16))) float2 smm[2][kFinRound];
-  const int tid = threadIdx.x;
-  const int per = f.d / kFinCh;
-  const int bh = blockIdx.x / per, c0 = kFinCh * (blockIdx.x % per);
+// In-order reduction of one channel's nk chunk values (stride `stride` elements apart): the sum
+// (T = double) or the max / min pair (T = float2).  Three batches of B loads rotate, so that two
+// are in flight while the third is combined.
+template <int B, typename T, typename F>
+__device__ __forceinline__ void fin_chain(const T* __restrict__ p, size_t stride, int nk, F&& take) {
+  T a[B], b[B], c[B];
+  // rows past the last chunk re-read it (always in bounds; not combined): every batch issues the
+  // same loads, so the compiler's waits keep the other two batches in flight
+  auto load = [&](T (&x)[B], int u0) {
+#pragma unroll
+    for (int e = 0; e < B; e++) x[e] = p[(size_t)min(u0 + e, nk - 1) * stride];
+  };
+  auto use = [&](const T (&x)[B], int u0) {
+    if (u0 + B <= nk) {  // a whole batch: the plain chain
+#pragma unroll
+      for (int e = 0; e < B; e++) take(x[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < B; e++)
+        if (u0 + e < nk) take(x[e]);
+    }
+  };
+  if (nk <= 0) return;
+  load(a, 0);
+  load(b, B);
+  for (int u0 = 0; u0 < nk; u0 += 3 * B) {
+    load(c, u0 + 2 * B);
+    use(a, u0);
+    if (u0 + B >= nk) break;
+    load(a, u0 + 3 * B);
+    use(b, u0 + B);
+    if (u0 + 2 * B >= nk) break;
+    load(b, u0 + 4 * B);
+    use(c, u0 + 2 * B);
+  }
+}
+
+// B: chunk rows per batch of loads (32 for long sequences, 8 for short ones, whose last batches
+// would otherwise mostly re-read the last chunk)
+template <int B>
+__global__ __launch_bounds__(384) void kv_finalize_kernel(FinArgs f) {
+  __shared__ float svm[128];  // V_m per channel, from the V-sum role to the max / min role
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int role = tid / f.d, c = tid % f.d;
   const int M = seq_rows(f.kl, bh / f.Hkv, bh % f.Hkv, f.Hkv, f.d).len;  // this sequence's keys
   const int nk = (M + kBK - 1) / kBK;                                    // its chunks
-  const int nr = (nk + kFinStage - 1) / kFinStage;                       // rounds
-  // each thread moves kFinPieces 16-byte pieces (2 doubles or 2 float2) of every array per round;
-  // piece e of thread tid is element x = 2 (tid + 256 e) of the round: chunk x / 16, channel x % 16
-  typedef double d2 __attribute__((ext_vector_type(2)));
-  d2 rk[kFinPieces], rv[kFinPieces];
-  v4i rm[kFinPieces];
-#define SAGE_FIN_LOAD(r)                                                                      \
-  _Pragma("unroll") for (int e = 0; e < kFinPieces; e++) {                                   \
-    const int x = 2 * (tid + 256 * e);                                                        \
-    const int uu = min((r) * kFinStage + x / kFinCh, nk - 1);                                 \
-    const size_t o = ((size_t)bh * f.nkt + uu) * f.d + c0 + x % kFinCh;                       \
-    rk[e] = *reinterpret_cast<const d2*>(f.kpart + o);                                        \
-    if (f.smooth_v) rv[e] = *reinterpret_cast<const d2*>(f.vpart + o);                        \
-    if (!f.k_only) rm[e] = *reinterpret_cast<const v4i*>(f.vmm + o);                          \
-  }
-#define SAGE_FIN_STORE(buf)                                                                   \
-  _Pragma("unroll") for (int e = 0; e < kFinPieces; e++) {                                   \
-    const int x = 2 * (tid + 256 * e);                                                        \
-    *reinterpret_cast<d2*>(&sk[buf][x]) = rk[e];                                              \
-    if (f.smooth_v) *reinterpret_cast<d2*>(&svs[buf][x]) = rv[e];                             \
-    if (!f.k_only) *reinterpret_cast<v4i*>(&smm[buf][x]) = rm[e];                             \
-  }
-  double ks = 0.0, vs = 0.0;
-  float mx = -INFINITY, mn = INFINITY;
-  if (nk > 0) {
-    SAGE_FIN_LOAD(0)
-    SAGE_FIN_STORE(0)
+  const size_t o = (size_t)bh * f.nkt * f.d + c;  // channel c of chunk 0; chunk u at o + u d
+  if (role == 0) {
+    double ks = 0.0;
+    fin_chain<B>(f.kpart + o, (size_t)f.d, nk, [&](double x) { ks += x; });
+    // a sequence without keys (variable-length batches only) gets zero means and the floor scale
+    f.kmean[(size_t)bh * f.d + c] = M > 0 ? (float)(ks / (double)M) : 0.0f;
+  } else if (role == 2) {
+    double vs = 0.0;
+    if (f.smooth_v && !f.k_only) fin_chain<B>(f.vpart + o, (size_t)f.d, nk, [&](double x) { vs += x; });
+    svm[c] = (f.smooth_v && M > 0) ? (float)(vs / (double)M) : 0.0f;
   }
   __syncthreads();
-  for (int r = 0; r < nr; r++) {
-    const int buf = r & 1;
-    if (r + 1 < nr) {  // in flight during this round's sums
-      SAGE_FIN_LOAD(r + 1)
-    }
-    const int ns = min(kFinStage, nk - r * kFinStage);
-    if (tid < kFinCh) {
-      for (int ub = 0; ub < ns; ub += 8) {  // 8 LDS reads in flight, adds in chunk order
-        double x[8];
-#pragma unroll
-        for (int e = 0; e < 8; e++) x[e] = sk[buf][min(ub + e, kFinStage - 1) * kFinCh + tid];
-#pragma unroll
-        for (int e = 0; e < 8; e++)
-          if (ub + e < ns) ks += x[e];
-      }
-    } else if (!f.k_only && tid >= 64 && tid < 64 + kFinCh) {
-      const int cc = tid - 64;
-      for (int ub = 0; ub < ns; ub += 8) {
-        double x[8];
-        float2 m[8];
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-          const int uu = min(ub + e, kFinStage - 1) * kFinCh + cc;
-          x[e] = f.smooth_v ? svs[buf][uu] : 0.0;
-          m[e] = smm[buf][uu];
-        }
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-          if (ub + e < ns) {
-            if (f.smooth_v) vs += x[e];
-            mx = m[e].x > mx ? m[e].x : mx;  // NaN ignored
-            mn = m[e].y < mn ? m[e].y : mn;
-          }
-        }
-      }
-    }
-    if (r + 1 < nr) {  // the other buffer was last read in round r - 1
-      SAGE_FIN_STORE(buf ^ 1)
-    }
-    __syncthreads();
-  }
-#undef SAGE_FIN_LOAD
-#undef SAGE_FIN_STORE
-  // a sequence without keys (variable-length batches only) gets zero means and the floor scale
-  if (tid < kFinCh) {
-    f.kmean[(size_t)bh * f.d + c0 + tid] = M > 0 ? (float)(ks / (double)M) : 0.0f;
-  } else if (!f.k_only && tid >= 64 && tid < 64 + kFinCh) {
-    const int c = c0 + tid - 64;
-    const float vm = (f.smooth_v && M > 0) ? (float)(vs / (double)M) : 0.0f;
+  if (role == 1 && !f.k_only) {
+    float mx = -INFINITY, mn = INFINITY;
+    fin_chain<B>(f.vmm + o, (size_t)f.d, nk, [&](float2 m) {
+      mx = m.x > mx ? m.x : mx;  // NaN ignored
+      mn = m.y < mn ? m.y : mn;
+    });
+    const float vm = svm[c];
     f.vmean[(size_t)bh * f.d + c] = vm;
     const float a1 = mx - vm, a2 = vm - mn;  // max |fp32(V - V_m)| over the tokens
     const float am = a1 > a2 ? a1 : a2;
@@ -712,7 +687,8 @@ hipError_t kv_finalize(const Problem& p, const Workspace& w, hipStream_t s, bool
   f.kmean = w.kmean; f.vmean = w.vmean; f.dv = w.dv;
   f.kl = p.kl; f.Hkv = p.Hkv; f.d = p.d; f.nkt = p.nkt; f.smooth_v = p.smooth_v && !k_only;
   f.k_only = k_only;
-  hipLaunchKernelGGL(kv_finalize_kernel, dim3(p.BHkv * (p.d / kFinCh)), dim3(256), 0, s, f);
+  if (p.nkt >= 96) hipLaunchKernelGGL(kv_finalize_kernel<32>, dim3(p.BHkv), dim3(3 * p.d), 0, s, f);
+  else hipLaunchKernelGGL(kv_finalize_kernel<8>, dim3(p.BHkv), dim3(3 * p.d), 0, s, f);
   return hipGetLastError();
 }
 }  // namespace
