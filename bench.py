@@ -54,11 +54,11 @@ VALU_SLOTS_PER_SCORE = {"i8f8": 7.5, "qkfp8": 6.5, "mx": 5.5}
 # and a changed kernel reports traffic null until the counters are taken again.
 TRAFFIC_BYTES = {
     "prefill32k": {"source_sha256_16": "f4b7745f9c66d9fa",
-                   "fetch_bytes": 1841364931, "write_bytes": 268501120},
+                   "fetch_bytes": 1834093315, "write_bytes": 268486042},
     "mxfp4_32k": {"source_sha256_16": "d4319ec4c6fe92b7",
-                  "fetch_bytes": 1688232047, "write_bytes": 201326656},
+                  "fetch_bytes": 1688355523, "write_bytes": 201327104},
     "video17k": {"source_sha256_16": "f4b7745f9c66d9fa",
-                 "fetch_bytes": 2110021653, "write_bytes": 215654400},
+                 "fetch_bytes": 2110387978, "write_bytes": 215654400},
 }
 # SQ counters of the fused attention kernel on the named workload (rocprofv3 --pmc, the summary
 # under profiles/): VALU and matrix-core busy fractions of the SIMD cycles, instructions per
@@ -66,19 +66,19 @@ TRAFFIC_BYTES = {
 # SQ_INSTS_MFMA report them, and the engine clock of the profiled dispatch (GRBM_GUI_ACTIVE
 # cycles per XCD over its duration).  Keyed by the same source hash as the traffic; null once stale.
 COUNTERS = {
-    "prefill32k": {"source_sha256_16": "f4b7745f9c66d9fa", "valu_busy": 0.896, "mfma_busy": 0.402,
+    "prefill32k": {"source_sha256_16": "f4b7745f9c66d9fa", "valu_busy": 0.902, "mfma_busy": 0.405,
                    "valu_insts_per_wave_tile": 235.2, "mfma_insts_per_wave_tile": 12.0,
-                   "clock_ghz_profiled": 1.747, "wave_tiles": 8404992, "waves_per_simd": 2.81,
+                   "clock_ghz_profiled": 1.779, "wave_tiles": 8404992, "waves_per_simd": 2.83,
                    "waves_per_simd_max": 3,
                    "summary": "profiles/attn_fwd_prefill32k_counters.md"},
-    "mxfp4_32k": {"source_sha256_16": "d4319ec4c6fe92b7", "valu_busy": 0.917, "mfma_busy": 0.239,
+    "mxfp4_32k": {"source_sha256_16": "d4319ec4c6fe92b7", "valu_busy": 0.943, "mfma_busy": 0.245,
                   "valu_insts_per_wave_tile": 184.9, "mfma_insts_per_wave_tile": 8.0,
-                  "clock_ghz_profiled": 1.942, "wave_tiles": 12582912, "waves_per_simd": 2.74,
+                  "clock_ghz_profiled": 1.955, "wave_tiles": 12582912, "waves_per_simd": 2.82,
                   "waves_per_simd_max": 3,
                   "summary": "profiles/attn_fwd_mx_mxfp4_32k_counters.md"},
-    "video17k": {"source_sha256_16": "f4b7745f9c66d9fa", "valu_busy": 1.017, "mfma_busy": 0.247,
+    "video17k": {"source_sha256_16": "f4b7745f9c66d9fa", "valu_busy": 1.033, "mfma_busy": 0.251,
                  "valu_insts_per_wave_tile": 214.2, "mfma_insts_per_wave_tile": 6.03,
-                 "clock_ghz_profiled": 1.945, "wave_tiles": 14493600, "waves_per_simd": 3.66,
+                 "clock_ghz_profiled": 1.924, "wave_tiles": 14493600, "waves_per_simd": 3.72,
                  "waves_per_simd_max": 4,
                  "summary": "profiles/attn_fwd_video17k_counters.md"},
 }
