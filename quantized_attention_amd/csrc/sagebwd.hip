@@ -316,14 +316,15 @@ __global__ __launch_bounds__(256, 2) void sb_fwd_kernel(FwdArgs a) {
       for (int T = 0; T < 2; T++)
 #pragma unroll
         for (int q4 = 0; q4 < 4; q4++) {
-          uint32_t t[4];
+          // e in [0, 127]: the byte conversion rounds half to even and packs byte k of the word
+          uint32_t wd = 0;
 #pragma unroll
           for (int k = 0; k < 4; k++) {
             const float e = fast_exp2(fmaf(sc[T][4 * q4 + k], mul, -base));
             esum += e;
-            t[k] = __float_as_uint(e + 12582912.0f);  // e in [0, 127]: round half to even in the low byte
+            wd = __builtin_amdgcn_cvt_pk_u8_f32(e, k, wd);
           }
-          pb[T][q4] = (int)sb_pack4(t[0], t[1], t[2], t[3]);
+          pb[T][q4] = (int)wd;
         }
       esum = pair_sum(esum);
       // s_P = exp2(rm - m) / 127 against the running max m, here against m_ref

@@ -33,8 +33,9 @@ def load():
         L.sage_probe_mfma_rate.argtypes = [i, i, i, P, P]
         L.sage_probe_valu_rate.argtypes = [i, i, i, ctypes.c_float, P, P]
         L.sage_probe_stream.argtypes = [i, P, ctypes.c_ulonglong, P, P]
+        L.sage_probe_cvt_u8.argtypes = [u, u, P, P]
         for f in (L.sage_probe_mfma_f8, L.sage_probe_mfma_i8, L.sage_probe_cvt_e4m3, L.sage_probe_mfma_rate,
-                  L.sage_probe_valu_rate, L.sage_probe_stream):
+                  L.sage_probe_valu_rate, L.sage_probe_stream, L.sage_probe_cvt_u8):
             f.restype = i
         _lib = L
     return _lib
@@ -75,6 +76,16 @@ def cvt_e4m3(start: int, count: int):
     import torch
     out = torch.empty(count, dtype=torch.uint8, device="cuda")
     _check(load().sage_probe_cvt_e4m3(start, count, out.data_ptr(), _stream()), "cvt_e4m3")
+    torch.cuda.synchronize()
+    return out
+
+
+def cvt_u8(start: int, count: int):
+    """The bytes v_cvt_pk_u8_f32 makes of the FP32 values with bit patterns start .. start + count - 1,
+    as a uint8 device tensor."""
+    import torch
+    out = torch.empty(count, dtype=torch.uint8, device="cuda")
+    _check(load().sage_probe_cvt_u8(start, count, out.data_ptr(), _stream()), "cvt_u8")
     torch.cuda.synchronize()
     return out
 

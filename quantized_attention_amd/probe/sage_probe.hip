@@ -10,6 +10,8 @@
 //   * the INT8 MFMA (v_mfma_i32_32x32x32_i8) sums exactly;
 //   * the E4M3 conversion (v_cvt_pk_fp8_f32) rounds to nearest even, and the kernels' clamp to
 //     +-448 before it gives the saturating E4M3 of the pages' "FP8 Quantization for P~V";
+//   * the unsigned-byte conversion (v_cvt_pk_u8_f32) that packs SageBwd's INT8 P codes rounds to
+//     nearest even;
 //   * the matrix-core rates behind the roofline (INT8, FP8, and block-scaled FP4);
 //   * the HBM rates behind the preprocessing's floor: streaming reads and writes, and a buffer
 //     read again after its first read (the statistics and quantization passes both read K and V).
@@ -48,6 +50,13 @@ __global__ __launch_bounds__(256) void cvt_e4m3_range(uint32_t start, uint32_t c
   const float c = fminf(fmaxf(x, -448.0f), 448.0f);
   const float y = (x == x) ? c : x;
   out[i] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0, false) & 0xff);
+}
+
+// out[i] = the byte v_cvt_pk_u8_f32 makes of the FP32 value with bits start + i (i < count).
+__global__ __launch_bounds__(256) void cvt_u8_range(uint32_t start, uint32_t count, uint8_t* out) {
+  const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+  if (i >= count) return;
+  out[i] = (uint8_t)(__builtin_amdgcn_cvt_pk_u8_f32(__uint_as_float(start + i), 0, 0) & 0xff);
 }
 
 // Matrix-core rate: every wave runs four independent accumulator chains of `iters` MFMAs each
@@ -177,6 +186,14 @@ int sage_probe_mfma_i8(const void* a, const void* b, const int* c, int* d, void*
 int sage_probe_cvt_e4m3(unsigned start, unsigned count, unsigned char* out, void* stream) {
   if (count == 0 || (unsigned long long)start + count > (1ull << 32)) return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(cvt_e4m3_range, dim3((count + 255) / 256), dim3(256), 0, (hipStream_t)stream, start, count, out);
+  return (int)hipGetLastError();
+}
+
+// out[i] = v_cvt_pk_u8_f32's byte of the FP32 value with bits start + i (i < count; start + count
+// <= 2^32).  out: count bytes.
+int sage_probe_cvt_u8(unsigned start, unsigned count, unsigned char* out, void* stream) {
+  if (count == 0 || (unsigned long long)start + count > (1ull << 32)) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(cvt_u8_range, dim3((count + 255) / 256), dim3(256), 0, (hipStream_t)stream, start, count, out);
   return (int)hipGetLastError();
 }
 

@@ -182,6 +182,25 @@ def test_e4m3_cast_matches_oracle_codec():
     assert mismatch == 0
 
 
+def test_u8_conversion_rounds_to_nearest_even():
+    """v_cvt_pk_u8_f32, which packs SageBwd's forward P codes (values 127 P / (the row's block max
+    of P), in [0, 127]), rounds to nearest with ties to even, as the oracle's rint does: every
+    FP32 value from 0 to 128 (all 1.12e9 bit patterns), against numpy's rint."""
+    start, stop = 0, int(np.float32(128.0).view(np.uint32)) + 1
+    mismatch, total = 0, 0
+    step = 2 ** 24
+    for a in range(start, stop, step):
+        n = min(step, stop - a)
+        got = probe.cvt_u8(a, n).cpu().numpy()
+        x = (np.arange(n, dtype=np.uint64) + a).astype(np.uint32).view(np.float32)
+        want = np.rint(x.astype(np.float64)).astype(np.uint8)
+        mismatch += int((got != want).sum())
+        total += n
+        del x, want, got
+    say(f"u8 conversion: {total} inputs in [0, 128], {mismatch} mismatches")
+    assert mismatch == 0
+
+
 @pytest.mark.parametrize("kind,nominal", [(0, 5000.0), (1, 5000.0), (2, 10100.0)])
 def test_mfma_rates_are_plausible(kind, nominal):
     tops = probe.mfma_rate(kind)
