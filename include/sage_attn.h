@@ -283,7 +283,7 @@ int sage_attn_varlen_fwd(const sage_attn_varlen_shape* shape, const void* q, con
  * pointers, 16-byte aligned (lse 4-byte); outputs must not overlap inputs.
  */
 #define SAGE_TRAIN_NO_SMOOTH_K 0x4000u /* ablation: K is not smoothed (training entry points) */
-/* sage_attn_train_bwd keeps each (128-query, 64-key) block pair's INT8 dS^ (9 KiB per pair,
+/* sage_attn_train_bwd keeps each (128-query, 64-key) block pair's INT8 dS^ (8.6 KiB per pair,
  * in the workspace) from its dK/dV kernel for its dQ kernel; with this bit, or when that
  * buffer would exceed 16 GiB, the dQ kernel recomputes S, P, dP and dS instead (slower, with a
  * workspace of a few bytes per token).  Both give the same dK and dV; dQ agrees to FP32

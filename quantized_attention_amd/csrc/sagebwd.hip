@@ -746,9 +746,9 @@ __global__ __launch_bounds__(256, 3) void sb_dq_kernel(BwdArgs a) {
   constexpr int NKS = D / 32;
   using TT = SbTile<D, kBK>;  // K^ transposed, keys in i8perm order
   __shared__ __attribute__((aligned(1024))) int8_t sKt[2][TT::BYTES];
-  // a 3-slot ring of the pairs' records, one kSbRec-byte record per wave: the record of pair j+2
+  // a 3-slot ring of the pairs' records, one kSbRecLds-byte slot per wave: the record of pair j+2
   // streams in while pair j is contracted (and pair j+1's, already landed, waits)
-  __shared__ __attribute__((aligned(1024))) int8_t sRec[3][4][kSbRec];
+  __shared__ __attribute__((aligned(1024))) int8_t sRec[3][4][kSbRecLds];
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, col = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   int bh, qi;
@@ -784,7 +784,7 @@ __global__ __launch_bounds__(256, 3) void sb_dq_kernel(BwdArgs a) {
   const uint32_t tail_off = lane < 32 ? 2048 + 4 * lane : 2048 + 4 * 32;
   auto fetch = [&](int jj, int r) {
     const int8_t* g = rbase + (size_t)jj * 4 * kSbRec;
-    const uint32_t l = rec0 + (uint32_t)r * 4 * kSbRec;
+    const uint32_t l = rec0 + (uint32_t)r * 4 * kSbRecLds;
     dma16(l, g, 16 * lane);
     dma16(l + 1024, g, 1024 + 16 * lane);
     dma4(l + 2048, g, tail_off);

@@ -16,8 +16,11 @@ constexpr size_t kSbPairLimit = (size_t)16 << 30;
 // The pair buffer holds one record per (pair, wave of the pair's query block): the wave's dS^
 // codes in the dQ product's B-operand order (two halves of 64 lanes x 16 bytes), the FP32 sums of
 // dS over the pair's keys for the wave's 32 queries, the pair's dQ multiplier
-// (max|dS| / 127) s_K sm_scale, and padding to 2304 bytes.
-constexpr int kSbRec = 2304;
+// (max|dS| / 127) s_K sm_scale, and padding to 2192 bytes (a multiple of 16, for the 16-byte
+// DMAs).  In the dQ kernel's LDS ring a record takes kSbRecLds bytes: its tail's DMA writes
+// 64 lanes x 4 bytes from offset 2048.
+constexpr int kSbRec = 2192;
+constexpr int kSbRecLds = 2048 + 64 * 4;
 bool sb_store_ds(const Problem& p);
 // The chunk reduction to K's mean alone, after launch_stats with v null (SageBwd takes no V
 // statistics); defined with the other preprocessing launchers.

@@ -176,13 +176,13 @@ def test_train_binding_rejects_mismatched_tensors():
 
 
 def test_train_workspace_holds_the_pair_buffer_up_to_its_limit():
-    """The backward keeps every (128-query, 64-key) block pair's dS^ in its workspace (one 2304-byte
+    """The backward keeps every (128-query, 64-key) block pair's dS^ in its workspace (one 2192-byte
     record per wave of the query block: 2048 code bytes, 32 row sums, the pair's multiplier,
     padding) unless SAGE_TRAIN_RECOMPUTE_DS asks for the recomputing dQ kernel, or the buffer
     would pass 16 GiB; the training variant bits outside the known ones are rejected."""
     def ws(B, H, N, M, d, causal, var):
         return qa.sage_attn_train_workspace_bytes(qa.SageAttnShape(B, H, H, N, M, d, causal, 0.0, var))
-    pair = 4 * 2304
+    pair = 4 * 2192
     for B, H, N, M, d in ((1, 32, 8192, 8192, 128), (2, 3, 333, 700, 64)):
         pairs = B * H * -(-N // 128) * -(-M // 64)
         stored, recomputed = ws(B, H, N, M, d, 1, 0), ws(B, H, N, M, d, 1, qa.SAGE_TRAIN_RECOMPUTE_DS)
